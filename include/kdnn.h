@@ -1,0 +1,273 @@
+/*
+ * kdnn.h -- C ABI of libkdnn.so: exact 3-D nearest-neighbour search on a
+ * CPU-built KD-tree and the ICP correspondence step, on one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method is the one described by the CUDA-KDTree ICP article
+ * (pwwt.cn, "用 CUDA-KDTree 实现 ICP"; cited below as "the article" with its
+ * section numbers):
+ *   - ICP minimises E(R, t) = sum_i || R s_i + t - m_i ||^2 over rigid
+ *     motions, where m_i is the target point nearest to the moved source
+ *     point (§2.1);
+ *   - each iteration moves the original source by the current (R, t), finds
+ *     every nearest neighbour, and solves (R, t) from the centroids and the
+ *     3x3 cross-covariance H (§2.1, §3.3);
+ *   - the target gets a KD-tree built once on the CPU, linearised into an
+ *     array and kept in device memory (§2.2, §2.3, §3.1).
+ *
+ * Conventions shared by every entry point
+ *   - Point clouds are arrays of n points, 3 consecutive fp32 values each
+ *     (x, y, z), C-contiguous, 4-byte aligned: the layout of a (n, 3) float32
+ *     tensor.  Index arrays are int32 (n < 2^31).
+ *   - R is a row-major 3x3 fp64 matrix, t a 3-vector of fp64; a point p is
+ *     moved to R p + t.
+ *   - "_dev" pointers are device memory of the current HIP device, "_host"
+ *     pointers are host memory.  Every buffer is owned by the caller, except
+ *     the memory held by a kdnn_tree (freed by kdtree_free).  No entry point
+ *     allocates device memory except kdtree_build.
+ *   - Nearest neighbour: the target point of least squared distance, the
+ *     distance evaluated in fp32 as d = (dx*dx + dy*dy) + dz*dz with no fused
+ *     multiply-add and no denormal flushing; ties go to the lowest target
+ *     index (the index into the array given to kdtree_build).  A query with a
+ *     NaN/Inf coordinate, or with every distance overflowing to +inf, gets
+ *     (idx, dist2) = (-1, +inf).
+ *   - Functions never throw and never abort.  On failure they return a
+ *     non-zero kdnn_status and kdnn_last_error() describes it.  Device faults
+ *     of asynchronous work surface as KDNN_EDEVICE from a later synchronising
+ *     call.
+ */
+#ifndef KDNN_H
+#define KDNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDNN_VERSION 1
+
+typedef enum kdnn_status {
+    KDNN_OK = 0,
+    KDNN_EINVAL = 1,      /* bad argument (size, null pointer, small workspace) */
+    KDNN_ENOMEM = 2,      /* host or device allocation failed (kdtree_build only) */
+    KDNN_EDEVICE = 3,     /* a HIP call or kernel failed */
+    KDNN_ENONFINITE = 4,  /* a target coordinate is NaN or Inf */
+    KDNN_EDEGENERATE = 5  /* fewer than 3 pairs, or H of rank < 2: rotation undetermined */
+} kdnn_status;
+
+/* Opaque tree handle.  Immutable after kdtree_build; may be shared by
+ * concurrent nn_query calls on different streams. */
+typedef struct kdnn_tree kdnn_tree;
+
+/* Build flags. */
+#define KDNN_BUILD_ROUND_ROBIN 1u /* split axis cycles x, y, z (article §4.2) instead of max variance */
+
+typedef struct kdnn_build_params {
+    int32_t leaf_size; /* 1..1024; the article recommends 8..16 (§2.2, §4.1). 0 = 16 */
+    int32_t max_depth; /* 0 = none; else the tree stops at this depth and its leaves
+                          hold every remaining point (article §5.2) */
+    uint32_t flags;    /* KDNN_BUILD_* */
+} kdnn_build_params;
+
+typedef struct kdnn_tree_info {
+    int64_t n;              /* target points */
+    int32_t depth;          /* D: every leaf sits at depth D (root = depth 0) */
+    int32_t leaf_size;      /* requested leaf size */
+    int64_t node_slots;     /* 2^(D+1): 32-byte node records in device memory */
+    int64_t leaves;         /* 2^D */
+    int32_t min_leaf;       /* fewest points in a leaf */
+    int32_t max_leaf;       /* most points in a leaf */
+    float bbox_min[3];      /* tight bounding box of the target */
+    float bbox_max[3];
+    double center[3];       /* bbox centre; the shift applied in kdnn_icp_sums */
+    double build_ms;        /* host build time (excluding the upload) */
+    double upload_ms;       /* device allocation + host-to-device copy */
+    int64_t device_bytes;   /* device memory held by the tree */
+} kdnn_tree_info;
+
+/* Correspondence sums of one ICP iteration (article §2.1).  Over the pairs
+ * (s_i, m_i) -- s_i an ORIGINAL source point, m_i its matched target point --
+ * with a fixed shift c (the target's bbox centre, for fp64 conditioning):
+ *   n      = number of pairs (source points whose query found a match)
+ *   sum_s  = sum (s_i - c),  sum_m = sum (m_i - c)
+ *   sum_sm = sum (s_i - c)(m_i - c)^T, row-major: sum_sm[3a + b] = sum (s-c)_a (m-c)_b
+ *   sum_d2 = sum of the fp32 squared distances, i.e. E(R, t) at the (R, t) used.
+ * Hence mu_s = c + sum_s/n, mu_m = c + sum_m/n and
+ * H = sum (s - mu_s)(m - mu_m)^T = sum_sm - sum_s sum_m^T / n.  All fp64. */
+typedef struct kdnn_icp_sums {
+    int64_t n;
+    double c[3];
+    double sum_s[3];
+    double sum_m[3];
+    double sum_sm[9];
+    double sum_d2;
+} kdnn_icp_sums;
+
+/* Number of doubles icp_correspond_reduce_async writes to sums_dev:
+ * [0..2] sum_s, [3..5] sum_m, [6..14] sum_sm, [15] sum_d2, [16] n. */
+#define KDNN_SUMS_DOUBLES 17
+
+/* ---------------------------------------------------------------- build */
+
+/* Build the KD-tree of a target cloud on the host and upload it (article
+ * §2.2: median split on the max-variance axis, leaves of leaf_size points;
+ * §2.3: built once on the CPU, linearised, copied to device memory once;
+ * §3.1: nodes in one array, parent before child; §5.1: storage reserved up
+ * front, in-place nth_element).
+ *   xyz_host : n x 3 fp32, host memory, read only during the call.
+ *   params   : NULL = defaults (leaf 16, no depth cap, max-variance axis).
+ *   out      : receives the handle; unchanged on failure.
+ * Every node above depth D = min{d : ceil(n / 2^d) <= leaf_size} (or
+ * max_depth) is split at its index median, so all leaves sit at depth D and
+ * hold floor(n/2^D) or ceil(n/2^D) points.
+ * Errors: EINVAL (n < 1, n >= 2^31, leaf_size or max_depth out of range,
+ * NULL pointers, D > 28), ENONFINITE (NaN/Inf coordinate), ENOMEM, EDEVICE. */
+kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_params *params,
+                         kdnn_tree **out);
+
+/* Release a tree and its device memory.  NULL is a no-op.  The caller must
+ * make sure no work using the tree is still queued. */
+void kdtree_free(kdnn_tree *tree);
+
+/* Describe a tree.  Errors: EINVAL on NULL pointers. */
+kdnn_status kdtree_info(const kdnn_tree *tree, kdnn_tree_info *out);
+
+/* Host-only build for inspection (no device, no HIP call).  Sizes first:
+ * kdtree_layout gives D and the node slot count; kdtree_build_host fills
+ *   nodes_out  : node_slots x 8 fp32 words (32-byte records, slot i = heap
+ *                node i, root = 1, children 2i and 2i+1, slot 0 unused):
+ *                [lo.x lo.y lo.z hi.x hi.y hi.z w6 w7]; internal node: w6 =
+ *                split value, w7 = axis (uint32 0/1/2); leaf (i >= 2^D):
+ *                w6 = first point slot (int32), w7 = point count (int32).
+ *   points_out : n x 4 fp32 words, points in leaf order: x, y, z and the
+ *                original index (int32 bit pattern).
+ * Same errors as kdtree_build (without ENOMEM/EDEVICE for the device). */
+kdnn_status kdtree_layout(int64_t n, const kdnn_build_params *params, int32_t *depth_out,
+                          int64_t *node_slots_out);
+kdnn_status kdtree_build_host(const float *xyz_host, int64_t n, const kdnn_build_params *params,
+                              float *nodes_out, float *points_out);
+
+/* ---------------------------------------------------------------- query */
+
+/* Query flags. */
+#define KDNN_QUERY_NO_SORT 1u /* traverse in the given order (skip the Morton ordering) */
+
+/* Bytes of device workspace nn_query needs for m queries (Morton keys,
+ * permutation, radix-sort histograms). 0 for m <= 0. */
+size_t nn_query_workspace_bytes(int64_t m);
+
+/* Exact nearest neighbour of every query (article §2.2 search with
+ * backtracking and split-plane pruning; §3.2 one query per GPU lane;
+ * §5.3 queries Morton-ordered so that neighbouring lanes walk the same
+ * branches).
+ *   q_dev      : m x 3 fp32 queries (device).
+ *   idx_dev    : m int32 out, original target index of each nearest point.
+ *   dist2_dev  : m fp32 out, its squared distance.
+ *   flags      : KDNN_QUERY_*.
+ *   ws_dev     : >= nn_query_workspace_bytes(m) bytes of device memory,
+ *                256-byte aligned; may be NULL with KDNN_QUERY_NO_SORT.
+ *   stream     : HIP stream (NULL = default stream).  Asynchronous.
+ * Results are written in the queries' own order whatever the traversal
+ * order.  m == 0 is a no-op.  Errors: EINVAL, EDEVICE (launch failure). */
+kdnn_status nn_query(const kdnn_tree *tree, const float *q_dev, int64_t m, int32_t *idx_dev,
+                     float *dist2_dev, uint32_t flags, void *ws_dev, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Instrumented nn_query: same traversal, same results, and per query the
+ * number of tree nodes loaded and of leaf points scanned (uint32 each, may be
+ * NULL).  For measurement only; slower than nn_query. */
+kdnn_status nn_query_stats(const kdnn_tree *tree, const float *q_dev, int64_t m, int32_t *idx_dev,
+                           float *dist2_dev, uint32_t *nodes_dev, uint32_t *points_dev,
+                           uint32_t flags, void *ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ transform */
+
+/* out_i = fl32( ((R_r0 x + R_r1 y) + R_r2 z) + t_r ) per row r, evaluated in
+ * fp64 in exactly that order with one round-to-nearest-even cast (article
+ * §3.3, step 1 of the main loop).  in_dev == out_dev is allowed (in place);
+ * partial overlap is not.  R_host, t_host are read during the call.
+ * Asynchronous on stream.  n == 0 is a no-op.  Errors: EINVAL, EDEVICE. */
+kdnn_status transform_points(const float *in_dev, float *out_dev, int64_t n, const double *R_host,
+                             const double *t_host, hipStream_t stream);
+
+/* ------------------------------------------------------------------ ICP */
+
+/* ICP flags. */
+#define KDNN_ICP_REUSE_ORDER 1u /* ws already holds the traversal order of this src (from a
+                                   previous call with the same src_dev and n) */
+#define KDNN_ICP_NO_SORT 2u     /* traverse source points in their given order */
+
+/* Bytes of device workspace the ICP entry points need for n source points. */
+size_t icp_workspace_bytes(int64_t n);
+
+/* One ICP correspondence step fused into one kernel (article §2.1, §3.3):
+ * move every ORIGINAL source point by (R, t) exactly as transform_points
+ * does, find its nearest target point, and reduce the pairs to the sums of
+ * kdnn_icp_sums (fp64 accumulation, deterministic order).  The article
+ * copies the per-point results back and reduces on the CPU; here only the
+ * 17 sums cross to the host.
+ *   src_dev    : n x 3 fp32 original source points (device).
+ *   R_host, t_host : current transform (host, read during the call).
+ *   out_host   : receives the sums.
+ *   idx_dev, dist2_dev : optional per-point correspondences (NULL = skip).
+ *   ws_dev     : >= icp_workspace_bytes(n) bytes, 256-byte aligned.
+ * Synchronises stream.  Calls sharing one ws must not overlap.
+ * Errors: EINVAL, EDEVICE. */
+kdnn_status icp_correspond_reduce(const kdnn_tree *tree, const float *src_dev, int64_t n,
+                                  const double *R_host, const double *t_host,
+                                  kdnn_icp_sums *out_host, int32_t *idx_dev, float *dist2_dev,
+                                  uint32_t flags, void *ws_dev, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* As icp_correspond_reduce but asynchronous: the KDNN_SUMS_DOUBLES sums are
+ * written to sums_dev (device, 8-byte aligned) when the stream reaches the
+ * kernel.  For pipelining several registrations and for timing the kernel. */
+kdnn_status icp_correspond_reduce_async(const kdnn_tree *tree, const float *src_dev, int64_t n,
+                                        const double *R_host, const double *t_host,
+                                        double *sums_dev, int32_t *idx_dev, float *dist2_dev,
+                                        uint32_t flags, void *ws_dev, size_t ws_bytes,
+                                        hipStream_t stream);
+
+/* Rigid solve from correspondence sums (article §2.1): centroids, H, its 3x3
+ * SVD H = U S V^T, R = V diag(1, 1, d) U^T with d = sign det(V U^T) so that R
+ * is a proper rotation, t = mu_m - R mu_s.  Host only, fp64.
+ * Errors: EINVAL (NULL), EDEGENERATE (n < 3 or rank(H) < 2; outputs unset). */
+kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_out);
+
+/* Whole ICP registration (article §2.1 loop, §3.3 main loop, §4.6
+ * convergence rule): from (R0, t0) (NULL = identity / zero), repeat
+ *   sums_k = correspond-and-reduce at (R_k, t_k);  E_k = sums_k.sum_d2;
+ *   (R_{k+1}, t_{k+1}) = kdnn_procrustes(sums_k)
+ * for max_iter iterations, or stop early once eps > 0 and the mean squared
+ * distance E_k / n_k changed by less than eps on two consecutive iterations.
+ *   R_out, t_out : the last solved transform (host).
+ *   E_hist       : optional [max_iter] fp64, E_k per iteration done.
+ *   Rt_hist      : optional [max_iter][12] fp64, (R_k row-major, t_k) used by
+ *                  iteration k.
+ *   iters_done   : optional, iterations completed.
+ * The traversal order is computed once, from the source moved by (R0, t0).
+ * On EDEGENERATE the outputs hold the last good transform.
+ * Errors: EINVAL, EDEVICE, EDEGENERATE. */
+kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, const double *R0_host,
+                      const double *t0_host, int32_t max_iter, double eps, double *R_out,
+                      double *t_out, double *E_hist, double *Rt_hist, int32_t *iters_done,
+                      void *ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- misc */
+
+/* Text of the last error on the calling thread ("" if none).  Valid until the
+ * next kdnn call on that thread. */
+const char *kdnn_last_error(void);
+
+/* KDNN_VERSION of the built library. */
+int32_t kdnn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDNN_H */

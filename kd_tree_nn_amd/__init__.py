@@ -1,0 +1,285 @@
+"""kd_tree_nn_amd -- exact KD-tree nearest neighbours and ICP correspondences on MI355X.
+
+A thin Python layer over libkdnn.so (C ABI: include/kdnn.h).  It only checks
+and marshals arguments: every step of the search, the transform, the
+reduction and the ICP loop runs in the library.  PyTorch provides device
+memory (CUDA/HIP tensors) and the current stream.
+
+    import kd_tree_nn_amd as kdnn
+    tree = kdnn.Tree(target_points_cpu, leaf_size=16)      # built once, on the host
+    idx, d2 = tree.query(q_gpu)                             # exact NN of every query
+    res = tree.icp(src_gpu, max_iter=30)                    # ICP registration
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    KdnnError, KDNN_QUERY_NO_SORT, KDNN_ICP_REUSE_ORDER, KDNN_ICP_NO_SORT, KDNN_SUMS_DOUBLES,
+)
+
+__all__ = ["Tree", "transform", "procrustes", "build_host", "layout", "sums_to_dict",
+           "KdnnError", "version"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def version() -> int:
+    return int(_lib.lib().kdnn_version())
+
+
+def _host_points(points) -> np.ndarray:
+    if hasattr(points, "detach"):
+        if points.is_cuda:
+            raise ValueError("target points must be host memory (build is on the CPU)")
+        points = points.detach().numpy()
+    a = np.ascontiguousarray(np.asarray(points, dtype=np.float32))
+    if a.ndim != 2 or a.shape[1] != 3:
+        raise ValueError("points must have shape (n, 3)")
+    return a
+
+
+def _dev_points(x, name):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if x.dtype != torch.float32 or x.dim() != 2 or x.shape[1] != 3:
+        raise ValueError(f"{name} must be float32 of shape (n, 3)")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return x
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(None)
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _mat(R, shape, name):
+    a = np.ascontiguousarray(np.asarray(R, dtype=np.float64).reshape(shape))
+    return a, a.ctypes.data_as(_lib.c_dp)
+
+
+def _params(leaf_size, max_depth, round_robin):
+    return _lib.BuildParams(int(leaf_size), int(max_depth),
+                            _lib.KDNN_BUILD_ROUND_ROBIN if round_robin else 0)
+
+
+def sums_to_dict(s: "_lib.IcpSums") -> dict:
+    """Correspondence sums plus the derived centroids, H and E."""
+    n = int(s.n)
+    c = np.array(s.c[:])
+    ss, sm = np.array(s.sum_s[:]), np.array(s.sum_m[:])
+    ssm = np.array(s.sum_sm[:]).reshape(3, 3)
+    out = {"n": n, "c": c, "sum_s": ss, "sum_m": sm, "sum_sm": ssm, "E": float(s.sum_d2)}
+    if n > 0:
+        out["mu_s"] = c + ss / n
+        out["mu_m"] = c + sm / n
+        out["H"] = ssm - np.outer(ss, sm) / n
+    return out
+
+
+class Tree:
+    """KD-tree of a target cloud, built on the host and resident on the device."""
+
+    def __init__(self, points, leaf_size: int = 16, max_depth: int = 0,
+                 round_robin: bool = False):
+        torch = _torch()
+        pts = _host_points(points)
+        self._h = ctypes.c_void_p(None)
+        p = _params(leaf_size, max_depth, round_robin)
+        h = ctypes.c_void_p()
+        _lib.check(_lib.lib().kdtree_build(pts.ctypes.data, len(pts), ctypes.byref(p),
+                                           ctypes.byref(h)), "kdtree_build")
+        self._h = h
+        self.n = len(pts)
+        self.device = torch.device("cuda", torch.cuda.current_device())
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.lib().kdtree_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def info(self) -> dict:
+        i = _lib.TreeInfo()
+        _lib.check(_lib.lib().kdtree_info(self._h, ctypes.byref(i)), "kdtree_info")
+        return {k: (list(getattr(i, k)) if k in ("bbox_min", "bbox_max", "center")
+                    else getattr(i, k)) for k, _ in _lib.TreeInfo._fields_}
+
+    # -------------------------------------------------------------- queries
+    def query_workspace(self, m: int):
+        torch = _torch()
+        return torch.empty(int(_lib.lib().nn_query_workspace_bytes(m)), dtype=torch.uint8,
+                           device=self.device)
+
+    def query(self, q, sort: bool = True, out=None, workspace=None, stream=None):
+        """(idx int32[m], dist2 float32[m]) of the exact nearest target point."""
+        torch = _torch()
+        q = _dev_points(q, "queries")
+        m = q.shape[0]
+        idx, d2 = out if out is not None else (
+            torch.empty(m, dtype=torch.int32, device=q.device),
+            torch.empty(m, dtype=torch.float32, device=q.device))
+        ws = None
+        if sort and m > 0:
+            ws = workspace if workspace is not None else self.query_workspace(m)
+        _lib.check(_lib.lib().nn_query(
+            self._h, _ptr(q), m, _ptr(idx), _ptr(d2), 0 if sort else KDNN_QUERY_NO_SORT,
+            _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)), "nn_query")
+        return idx, d2
+
+    def query_stats(self, q, sort: bool = True):
+        """query() plus per-query counts of nodes loaded and leaf points scanned."""
+        torch = _torch()
+        q = _dev_points(q, "queries")
+        m = q.shape[0]
+        idx = torch.empty(m, dtype=torch.int32, device=q.device)
+        d2 = torch.empty(m, dtype=torch.float32, device=q.device)
+        cn = torch.empty(m, dtype=torch.int32, device=q.device)
+        cp = torch.empty(m, dtype=torch.int32, device=q.device)
+        ws = self.query_workspace(m) if sort and m > 0 else None
+        _lib.check(_lib.lib().nn_query_stats(
+            self._h, _ptr(q), m, _ptr(idx), _ptr(d2), _ptr(cn), _ptr(cp),
+            0 if sort else KDNN_QUERY_NO_SORT, _ptr(ws), ws.numel() if ws is not None else 0,
+            _stream()), "nn_query_stats")
+        return idx, d2, cn, cp
+
+    # ------------------------------------------------------------------ ICP
+    def icp_workspace(self, n: int):
+        torch = _torch()
+        return torch.empty(int(_lib.lib().icp_workspace_bytes(n)), dtype=torch.uint8,
+                           device=self.device)
+
+    def correspond_reduce(self, src, R=None, t=None, return_pairs: bool = False,
+                          flags: int = 0, workspace=None, stream=None) -> dict:
+        """Sums of one ICP correspondence step at (R, t); optionally the pairs."""
+        torch = _torch()
+        src = _dev_points(src, "src")
+        n = src.shape[0]
+        Ra, Rp = _mat(np.eye(3) if R is None else R, (3, 3), "R")
+        ta, tp = _mat(np.zeros(3) if t is None else t, (3,), "t")
+        ws = workspace if workspace is not None else self.icp_workspace(n)
+        idx = d2 = None
+        if return_pairs:
+            idx = torch.empty(n, dtype=torch.int32, device=src.device)
+            d2 = torch.empty(n, dtype=torch.float32, device=src.device)
+        s = _lib.IcpSums()
+        _lib.check(_lib.lib().icp_correspond_reduce(
+            self._h, _ptr(src), n, Rp, tp, ctypes.byref(s), _ptr(idx), _ptr(d2), int(flags),
+            _ptr(ws), ws.numel(), _stream(stream)), "icp_correspond_reduce")
+        out = sums_to_dict(s)
+        if return_pairs:
+            out["idx"], out["d2"] = idx, d2
+        return out
+
+    def correspond_reduce_async(self, src, R, t, sums_out, workspace, flags: int = 0,
+                                idx=None, d2=None, stream=None):
+        """Enqueue one correspondence step; KDNN_SUMS_DOUBLES float64 sums go to sums_out."""
+        torch = _torch()
+        src = _dev_points(src, "src")
+        if sums_out.dtype != torch.float64 or sums_out.numel() < KDNN_SUMS_DOUBLES:
+            raise ValueError("sums_out must be float64 with >= 17 elements")
+        _, Rp = _mat(R, (3, 3), "R")
+        _, tp = _mat(t, (3,), "t")
+        _lib.check(_lib.lib().icp_correspond_reduce_async(
+            self._h, _ptr(src), src.shape[0], Rp, tp, _ptr(sums_out), _ptr(idx), _ptr(d2),
+            int(flags), _ptr(workspace), workspace.numel(), _stream(stream)),
+            "icp_correspond_reduce_async")
+
+    def icp(self, src, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
+            workspace=None, stream=None) -> dict:
+        """ICP registration of the source (device, original coordinates) onto the tree."""
+        src = _dev_points(src, "src")
+        n = src.shape[0]
+        R0a = None if R0 is None else _mat(R0, (3, 3), "R0")
+        t0a = None if t0 is None else _mat(t0, (3,), "t0")
+        R = np.zeros(9)
+        t = np.zeros(3)
+        E = np.zeros(max(max_iter, 1))
+        Rt = np.zeros((max(max_iter, 1), 12))
+        it = ctypes.c_int32(0)
+        ws = workspace if workspace is not None else self.icp_workspace(n)
+        _lib.check(_lib.lib().icp_align(
+            self._h, _ptr(src), n,
+            R0a[1] if R0a else None, t0a[1] if t0a else None, int(max_iter), float(eps),
+            R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
+            E.ctypes.data_as(_lib.c_dp), Rt.ctypes.data_as(_lib.c_dp), ctypes.byref(it),
+            _ptr(ws), ws.numel(), _stream(stream)), "icp_align")
+        k = it.value
+        return {"R": R.reshape(3, 3), "t": t, "E": E[:k], "Rt_hist": Rt[:k], "iters": k}
+
+
+def transform(x, R, t, out=None, stream=None):
+    """out = fl32(R x + t) per point, fp64 inside (in place when out is x)."""
+    torch = _torch()
+    x = _dev_points(x, "points")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        out = _dev_points(out, "out")
+    _, Rp = _mat(R, (3, 3), "R")
+    _, tp = _mat(t, (3,), "t")
+    _lib.check(_lib.lib().transform_points(_ptr(x), _ptr(out), x.shape[0], Rp, tp,
+                                           _stream(stream)), "transform_points")
+    return out
+
+
+def procrustes(sums) -> tuple:
+    """Host rigid solve from correspondence sums (an IcpSums or a dict from sums_to_dict)."""
+    if isinstance(sums, dict):
+        s = _lib.IcpSums()
+        s.n = int(sums["n"])
+        s.c[:] = list(np.asarray(sums["c"], np.float64))
+        s.sum_s[:] = list(np.asarray(sums["sum_s"], np.float64))
+        s.sum_m[:] = list(np.asarray(sums["sum_m"], np.float64))
+        s.sum_sm[:] = list(np.asarray(sums["sum_sm"], np.float64).ravel())
+        s.sum_d2 = float(sums.get("E", 0.0))
+        sums = s
+    R = np.zeros(9)
+    t = np.zeros(3)
+    _lib.check(_lib.lib().kdnn_procrustes(ctypes.byref(sums), R.ctypes.data_as(_lib.c_dp),
+                                          t.ctypes.data_as(_lib.c_dp)), "kdnn_procrustes")
+    return R.reshape(3, 3), t
+
+
+def layout(n: int, leaf_size: int = 16, max_depth: int = 0, round_robin: bool = False):
+    """(depth D, node slots 2^(D+1)) of the tree kdtree_build would make."""
+    p = _params(leaf_size, max_depth, round_robin)
+    d = ctypes.c_int32()
+    s = ctypes.c_int64()
+    _lib.check(_lib.lib().kdtree_layout(int(n), ctypes.byref(p), ctypes.byref(d),
+                                        ctypes.byref(s)), "kdtree_layout")
+    return d.value, s.value
+
+
+def build_host(points, leaf_size: int = 16, max_depth: int = 0, round_robin: bool = False) -> dict:
+    """Host-only build (no device): the node records and leaf-ordered points."""
+    pts = _host_points(points)
+    D, slots = layout(len(pts), leaf_size, max_depth, round_robin)
+    nodes = np.zeros((slots, 8), np.float32)
+    pout = np.zeros((len(pts), 4), np.float32)
+    p = _params(leaf_size, max_depth, round_robin)
+    _lib.check(_lib.lib().kdtree_build_host(pts.ctypes.data, len(pts), ctypes.byref(p),
+                                            nodes.ctypes.data, pout.ctypes.data),
+               "kdtree_build_host")
+    return {"depth": D, "nodes": nodes, "points": pout}

@@ -1,0 +1,432 @@
+// extern "C" entry points of libkdnn.so (declared and documented in kdnn.h).
+// Argument checking, error reporting, tree lifetime, and the host ICP loop
+// (CUDA-KDTree ICP article, §2.1 and §3.3: correspond, reduce, solve on the
+// host, repeat; §4.6 convergence rule).  No exception crosses the ABI.
+#include <hip/hip_runtime_api.h>
+
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kdnn_internal.hpp"
+
+using namespace kdnn;
+
+namespace {
+
+thread_local std::string g_err;
+
+kdnn_status fail(kdnn_status st, const std::string &msg)
+{
+    g_err = msg;
+    return st;
+}
+
+kdnn_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(KDNN_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define KDNN_GUARD_BEGIN try {
+#define KDNN_GUARD_END                                                     \
+    }                                                                      \
+    catch (const std::bad_alloc &) { return fail(KDNN_ENOMEM, "out of host memory"); } \
+    catch (...) { return fail(KDNN_EINVAL, "internal error"); }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+double ms_since(std::chrono::steady_clock::time_point t0)
+{
+    return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+void free_tree(kdnn_tree *t)
+{
+    if (!t) return;
+    int cur = -1;
+    if (hipGetDevice(&cur) == hipSuccess && cur != t->device) (void)hipSetDevice(t->device);
+    if (t->d_nodes) (void)hipFree(t->d_nodes);
+    if (t->d_points) (void)hipFree(t->d_points);
+    if (t->h_pinned) (void)hipHostFree(t->h_pinned);
+    if (cur >= 0 && cur != t->device) (void)hipSetDevice(cur);
+    delete t;
+}
+
+kdnn_status check_points(const void *p, int64_t n, const char *name)
+{
+    if (n < 0 || n >= (int64_t(1) << 31)) return fail(KDNN_EINVAL, std::string(name) + ": count out of range");
+    if (n > 0 && !p) return fail(KDNN_EINVAL, std::string(name) + ": null pointer");
+    if (p && !aligned(p, 4)) return fail(KDNN_EINVAL, std::string(name) + ": not 4-byte aligned");
+    return KDNN_OK;
+}
+
+kdnn_status check_ws(const void *ws, size_t have, size_t need)
+{
+    if (need == 0) return KDNN_OK;
+    if (!ws) return fail(KDNN_EINVAL, "workspace: null pointer");
+    if (!aligned(ws, 256)) return fail(KDNN_EINVAL, "workspace: not 256-byte aligned");
+    if (have < need)
+        return fail(KDNN_EINVAL, "workspace: " + std::to_string(have) + " bytes given, " +
+                                     std::to_string(need) + " needed");
+    return KDNN_OK;
+}
+
+void to_sums(const double *d, const double c[3], kdnn_icp_sums *o)
+{
+    o->n = int64_t(std::llround(d[16]));
+    for (int k = 0; k < 3; ++k) {
+        o->c[k] = c[k];
+        o->sum_s[k] = d[k];
+        o->sum_m[k] = d[3 + k];
+    }
+    for (int k = 0; k < 9; ++k) o->sum_sm[k] = d[6 + k];
+    o->sum_d2 = d[15];
+}
+
+void rt_to_f32(const double *R, const double *t, float out[12])
+{
+    for (int k = 0; k < 9; ++k) out[k] = float(R[k]);
+    for (int k = 0; k < 3; ++k) out[9 + k] = float(t[k]);
+}
+
+const double kI[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
+const double kZ[3] = {0, 0, 0};
+
+// Enqueue the traversal order (per flags) and the fused kernel.
+kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, const double *R,
+                        const double *t, double *sums_dev, int32_t *idx, float *d2,
+                        uint32_t flags, const IcpWorkspace &w, hipStream_t s)
+{
+    const int32_t *perm = nullptr;
+    hipError_t e = hipSuccess;
+    if (flags & KDNN_ICP_NO_SORT) {
+        e = launch_zero_u32(w.ticket, 1, s);
+    } else if (flags & KDNN_ICP_REUSE_ORDER) {
+        perm = w.sort.vals_a;  // ticket is clean after any completed call
+    } else {
+        float rt[12];
+        rt_to_f32(R, t, rt);
+        e = launch_icp_order(tree->dev, src, n, rt, w, &perm, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "icp: order launch");
+    e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, s);
+    if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
+    return KDNN_OK;
+}
+
+kdnn_status icp_check(const kdnn_tree *tree, const float *src, int64_t n, const double *R,
+                      const double *t, uint32_t flags, void *ws, size_t ws_bytes)
+{
+    if (!tree) return fail(KDNN_EINVAL, "icp: null tree");
+    if (n < 1) return fail(KDNN_EINVAL, "icp: n must be >= 1");
+    kdnn_status st = check_points(src, n, "icp: src");
+    if (st != KDNN_OK) return st;
+    if (!R || !t) return fail(KDNN_EINVAL, "icp: null R or t");
+    if (flags & ~(KDNN_ICP_REUSE_ORDER | KDNN_ICP_NO_SORT)) return fail(KDNN_EINVAL, "icp: unknown flag");
+    return check_ws(ws, ws_bytes, icp_ws_bytes(n));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kdnn_last_error(void) { return g_err.c_str(); }
+
+int32_t kdnn_version(void) { return KDNN_VERSION; }
+
+kdnn_status kdtree_layout(int64_t n, const kdnn_build_params *params, int32_t *depth_out,
+                          int64_t *node_slots_out)
+{
+    KDNN_GUARD_BEGIN
+    if (!depth_out || !node_slots_out) return fail(KDNN_EINVAL, "kdtree_layout: null output");
+    std::string err;
+    kdnn_status st = tree_layout(n, params, depth_out, node_slots_out, err);
+    return st == KDNN_OK ? st : fail(st, err);
+    KDNN_GUARD_END
+}
+
+kdnn_status kdtree_build_host(const float *xyz_host, int64_t n, const kdnn_build_params *params,
+                              float *nodes_out, float *points_out)
+{
+    KDNN_GUARD_BEGIN
+    if (!nodes_out || !points_out) return fail(KDNN_EINVAL, "kdtree_build_host: null output");
+    HostTree ht;
+    std::string err;
+    kdnn_status st = build_host_tree(xyz_host, n, params, ht, err);
+    if (st != KDNN_OK) return fail(st, err);
+    std::memcpy(nodes_out, ht.nodes.data(), ht.nodes.size() * sizeof(float));
+    std::memcpy(points_out, ht.points.data(), ht.points.size() * sizeof(float));
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_params *params,
+                         kdnn_tree **out)
+{
+    KDNN_GUARD_BEGIN
+    if (!out) return fail(KDNN_EINVAL, "kdtree_build: null output handle");
+    HostTree ht;
+    std::string err;
+    const auto t0 = std::chrono::steady_clock::now();
+    kdnn_status st = build_host_tree(xyz_host, n, params, ht, err);
+    if (st != KDNN_OK) return fail(st, err);
+    const double build_ms = ms_since(t0);
+
+    const auto t1 = std::chrono::steady_clock::now();
+    kdnn_tree *t = new kdnn_tree();
+    hipError_t e = hipGetDevice(&t->device);
+    if (e != hipSuccess) {
+        delete t;
+        return hip_fail(e, "kdtree_build: hipGetDevice");
+    }
+    const size_t nb = ht.nodes.size() * sizeof(float), pb = ht.points.size() * sizeof(float);
+    if ((e = hipMalloc(&t->d_nodes, nb)) != hipSuccess ||
+        (e = hipMalloc(&t->d_points, pb)) != hipSuccess) {
+        free_tree(t);
+        return fail(KDNN_ENOMEM, std::string("kdtree_build: hipMalloc: ") + hipGetErrorString(e));
+    }
+    if ((e = hipHostMalloc(reinterpret_cast<void **>(&t->h_pinned), 256, hipHostMallocDefault)) !=
+        hipSuccess) {
+        free_tree(t);
+        return fail(KDNN_ENOMEM, std::string("kdtree_build: hipHostMalloc: ") + hipGetErrorString(e));
+    }
+    if ((e = hipMemcpy(t->d_nodes, ht.nodes.data(), nb, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess) {
+        free_tree(t);
+        return hip_fail(e, "kdtree_build: upload");
+    }
+    const double upload_ms = ms_since(t1);
+
+    DeviceTree &d = t->dev;
+    d.nodes = t->d_nodes;
+    d.points = t->d_points;
+    d.first_leaf = uint32_t(1) << ht.depth;
+    for (int k = 0; k < 3; ++k) {
+        d.box_lo[k] = ht.bbox_min[k];
+        const float ext = ht.bbox_max[k] - ht.bbox_min[k];
+        d.box_inv[k] = ext > 0.0f ? 1.0f / ext : 0.0f;
+        d.center[k] = ht.center[k];
+    }
+    kdnn_tree_info &I = t->info;
+    I.n = n;
+    I.depth = ht.depth;
+    I.leaf_size = ht.leaf_size;
+    I.node_slots = int64_t(1) << (ht.depth + 1);
+    I.leaves = int64_t(1) << ht.depth;
+    I.min_leaf = ht.min_leaf;
+    I.max_leaf = ht.max_leaf;
+    for (int k = 0; k < 3; ++k) {
+        I.bbox_min[k] = ht.bbox_min[k];
+        I.bbox_max[k] = ht.bbox_max[k];
+        I.center[k] = ht.center[k];
+    }
+    I.build_ms = build_ms;
+    I.upload_ms = upload_ms;
+    I.device_bytes = int64_t(nb + pb);
+    *out = t;
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+void kdtree_free(kdnn_tree *tree)
+{
+    try {
+        free_tree(tree);
+    } catch (...) {
+    }
+}
+
+kdnn_status kdtree_info(const kdnn_tree *tree, kdnn_tree_info *out)
+{
+    if (!tree || !out) return fail(KDNN_EINVAL, "kdtree_info: null pointer");
+    *out = tree->info;
+    return KDNN_OK;
+}
+
+size_t nn_query_workspace_bytes(int64_t m) { return m > 0 ? sort_workspace_bytes(m) : 0; }
+
+static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t m, int32_t *idx,
+                                 float *d2, uint32_t *cn, uint32_t *cp, bool stats, uint32_t flags,
+                                 void *ws, size_t ws_bytes, hipStream_t s)
+{
+    if (!tree) return fail(KDNN_EINVAL, "nn_query: null tree");
+    kdnn_status st = check_points(q, m, "nn_query: queries");
+    if (st != KDNN_OK) return st;
+    if (m == 0) return KDNN_OK;
+    if (!idx || !d2) return fail(KDNN_EINVAL, "nn_query: null output");
+    if (!aligned(idx, 4) || !aligned(d2, 4)) return fail(KDNN_EINVAL, "nn_query: misaligned output");
+    if (flags & ~KDNN_QUERY_NO_SORT) return fail(KDNN_EINVAL, "nn_query: unknown flag");
+    const int32_t *perm = nullptr;
+    if (!(flags & KDNN_QUERY_NO_SORT)) {
+        st = check_ws(ws, ws_bytes, sort_workspace_bytes(m));
+        if (st != KDNN_OK) return st;
+        const SortWorkspace w = carve_sort_workspace(ws, m);
+        hipError_t e = launch_morton_order(tree->dev, q, m, nullptr, w, &perm, s);
+        if (e != hipSuccess) return hip_fail(e, "nn_query: order launch");
+    }
+    hipError_t e = launch_nn(tree->dev, q, m, perm, idx, d2, cn, cp, stats, s);
+    if (e != hipSuccess) return hip_fail(e, "nn_query: launch");
+    return KDNN_OK;
+}
+
+kdnn_status nn_query(const kdnn_tree *tree, const float *q_dev, int64_t m, int32_t *idx_dev,
+                     float *dist2_dev, uint32_t flags, void *ws_dev, size_t ws_bytes,
+                     hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    return nn_query_impl(tree, q_dev, m, idx_dev, dist2_dev, nullptr, nullptr, false, flags,
+                         ws_dev, ws_bytes, stream);
+    KDNN_GUARD_END
+}
+
+kdnn_status nn_query_stats(const kdnn_tree *tree, const float *q_dev, int64_t m, int32_t *idx_dev,
+                           float *dist2_dev, uint32_t *nodes_dev, uint32_t *points_dev,
+                           uint32_t flags, void *ws_dev, size_t ws_bytes, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    return nn_query_impl(tree, q_dev, m, idx_dev, dist2_dev, nodes_dev, points_dev, true, flags,
+                         ws_dev, ws_bytes, stream);
+    KDNN_GUARD_END
+}
+
+kdnn_status transform_points(const float *in_dev, float *out_dev, int64_t n, const double *R_host,
+                             const double *t_host, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    kdnn_status st = check_points(in_dev, n, "transform_points: in");
+    if (st != KDNN_OK) return st;
+    st = check_points(out_dev, n, "transform_points: out");
+    if (st != KDNN_OK) return st;
+    if (!R_host || !t_host) return fail(KDNN_EINVAL, "transform_points: null R or t");
+    if (n == 0) return KDNN_OK;
+    if (in_dev != out_dev) {
+        const char *a = reinterpret_cast<const char *>(in_dev);
+        const char *b = reinterpret_cast<const char *>(out_dev);
+        const size_t len = size_t(n) * 12;
+        if (a < b + len && b < a + len)
+            return fail(KDNN_EINVAL, "transform_points: in and out partially overlap");
+    }
+    hipError_t e = launch_transform(in_dev, out_dev, n, R_host, t_host, stream);
+    if (e != hipSuccess) return hip_fail(e, "transform_points: launch");
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+size_t icp_workspace_bytes(int64_t n) { return n > 0 ? icp_ws_bytes(n) : 0; }
+
+kdnn_status icp_correspond_reduce_async(const kdnn_tree *tree, const float *src_dev, int64_t n,
+                                        const double *R_host, const double *t_host,
+                                        double *sums_dev, int32_t *idx_dev, float *dist2_dev,
+                                        uint32_t flags, void *ws_dev, size_t ws_bytes,
+                                        hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    kdnn_status st = icp_check(tree, src_dev, n, R_host, t_host, flags, ws_dev, ws_bytes);
+    if (st != KDNN_OK) return st;
+    if (!sums_dev || !aligned(sums_dev, 8)) return fail(KDNN_EINVAL, "icp: bad sums_dev");
+    const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
+    return icp_enqueue(tree, src_dev, n, R_host, t_host, sums_dev, idx_dev, dist2_dev, flags, w,
+                       stream);
+    KDNN_GUARD_END
+}
+
+kdnn_status icp_correspond_reduce(const kdnn_tree *tree, const float *src_dev, int64_t n,
+                                  const double *R_host, const double *t_host,
+                                  kdnn_icp_sums *out_host, int32_t *idx_dev, float *dist2_dev,
+                                  uint32_t flags, void *ws_dev, size_t ws_bytes,
+                                  hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    kdnn_status st = icp_check(tree, src_dev, n, R_host, t_host, flags, ws_dev, ws_bytes);
+    if (st != KDNN_OK) return st;
+    if (!out_host) return fail(KDNN_EINVAL, "icp: null out_host");
+    kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
+    std::lock_guard<std::mutex> lock(mt->icp_mu);
+    const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
+    st = icp_enqueue(tree, src_dev, n, R_host, t_host, w.sums, idx_dev, dist2_dev, flags, w, stream);
+    if (st != KDNN_OK) return st;
+    hipError_t e = hipMemcpyAsync(mt->h_pinned, w.sums, KDNN_SUMS_DOUBLES * sizeof(double),
+                                  hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "icp: readback");
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "icp: synchronize");
+    to_sums(mt->h_pinned, tree->dev.center, out_host);
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_out)
+{
+    KDNN_GUARD_BEGIN
+    if (!sums || !R_out || !t_out) return fail(KDNN_EINVAL, "kdnn_procrustes: null pointer");
+    std::string err;
+    double R[9], t[3];
+    kdnn_status st = procrustes_from_sums(*sums, R, t, err);
+    if (st != KDNN_OK) return fail(st, err);
+    std::memcpy(R_out, R, sizeof R);
+    std::memcpy(t_out, t, sizeof t);
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, const double *R0_host,
+                      const double *t0_host, int32_t max_iter, double eps, double *R_out,
+                      double *t_out, double *E_hist, double *Rt_hist, int32_t *iters_done,
+                      void *ws_dev, size_t ws_bytes, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    double R[9], t[3];
+    std::memcpy(R, R0_host ? R0_host : kI, sizeof R);
+    std::memcpy(t, t0_host ? t0_host : kZ, sizeof t);
+    if (!R_out || !t_out) return fail(KDNN_EINVAL, "icp_align: null R_out or t_out");
+    if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align: max_iter < 0");
+    if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align: eps must be >= 0");
+    kdnn_status st = icp_check(tree, src_dev, n, R, t, 0, ws_dev, ws_bytes);
+    if (st != KDNN_OK) return st;
+    std::memcpy(R_out, R, sizeof R);
+    std::memcpy(t_out, t, sizeof t);
+    if (iters_done) *iters_done = 0;
+    if (max_iter == 0) return KDNN_OK;
+
+    kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
+    std::lock_guard<std::mutex> lock(mt->icp_mu);
+    const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
+    double prev_mse = 0.0;
+    int small_steps = 0;
+    for (int32_t k = 0; k < max_iter; ++k) {
+        if (Rt_hist) {
+            std::memcpy(Rt_hist + 12 * k, R, sizeof R);
+            std::memcpy(Rt_hist + 12 * k + 9, t, sizeof t);
+        }
+        st = icp_enqueue(tree, src_dev, n, R, t, w.sums, nullptr, nullptr,
+                         k == 0 ? 0u : KDNN_ICP_REUSE_ORDER, w, stream);
+        if (st != KDNN_OK) return st;
+        hipError_t e = hipMemcpyAsync(mt->h_pinned, w.sums, KDNN_SUMS_DOUBLES * sizeof(double),
+                                      hipMemcpyDeviceToHost, stream);
+        if (e != hipSuccess) return hip_fail(e, "icp_align: readback");
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "icp_align: synchronize");
+        kdnn_icp_sums sums;
+        to_sums(mt->h_pinned, tree->dev.center, &sums);
+        if (E_hist) E_hist[k] = sums.sum_d2;
+        std::string err;
+        double Rn[9], tn[3];
+        st = procrustes_from_sums(sums, Rn, tn, err);
+        if (st != KDNN_OK) return fail(st, "icp_align: iteration " + std::to_string(k) + ": " + err);
+        std::memcpy(R, Rn, sizeof R);
+        std::memcpy(t, tn, sizeof t);
+        std::memcpy(R_out, R, sizeof R);
+        std::memcpy(t_out, t, sizeof t);
+        if (iters_done) *iters_done = k + 1;
+        const double mse = sums.sum_d2 / double(sums.n);
+        if (eps > 0.0 && k > 0) {
+            small_steps = std::fabs(mse - prev_mse) < eps ? small_steps + 1 : 0;
+            if (small_steps >= 2) break;
+        }
+        prev_mse = mse;
+    }
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+}  // extern "C"

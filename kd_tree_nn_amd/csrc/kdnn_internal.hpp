@@ -1,0 +1,115 @@
+// Internal declarations shared by the host code and the HIP kernels of libkdnn.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kdnn.h"
+
+namespace kdnn {
+
+// ---------------------------------------------------------------- tree layout
+//
+// Nodes: a complete binary tree in heap order, 1-based (root = 1, children of
+// i are 2i and 2i+1, so the node index spells the path from the root).  Slot
+// 0 is unused so that every sibling pair shares one aligned 64-byte line.
+// Each node is 32 bytes = two float4:
+//   f4[2i]   = (lo.x, lo.y, lo.z, hi.x)
+//   f4[2i+1] = (hi.y, hi.z, w6, w7)
+// lo/hi: tight bounding box of the node's points (empty node: +inf / -inf).
+// Internal node (i < 2^D): w6 = split value, w7 = axis as uint32.
+// Leaf (i >= 2^D): w6 = first point slot (int32 bits), w7 = count (int32 bits).
+//
+// Points: one float4 per point in leaf order: (x, y, z, original index bits),
+// so a leaf is one contiguous run read with 16-byte loads.
+constexpr int kNodeWords = 8;
+constexpr int kMaxDepth = 28;
+constexpr int kMaxLeafSize = 1024;
+
+struct HostTree {
+    int32_t depth = 0;
+    int32_t leaf_size = 0;
+    int64_t n = 0;
+    std::vector<float> nodes;   // (2^(D+1)) * 8 words
+    std::vector<float> points;  // n * 4 words
+    float bbox_min[3] = {0, 0, 0};
+    float bbox_max[3] = {0, 0, 0};
+    double center[3] = {0, 0, 0};
+    int32_t min_leaf = 0, max_leaf = 0;
+};
+
+// Validate params and compute D and the node slot count (no allocation).
+kdnn_status tree_layout(int64_t n, const kdnn_build_params *p, int32_t *depth, int64_t *slots,
+                        std::string &err);
+// Full host build into HostTree (validates finiteness).
+kdnn_status build_host_tree(const float *xyz, int64_t n, const kdnn_build_params *p, HostTree &out,
+                            std::string &err);
+
+// Rigid solve from the 17 correspondence sums.
+kdnn_status procrustes_from_sums(const kdnn_icp_sums &s, double R[9], double t[3], std::string &err);
+
+// ---------------------------------------------------------------- device side
+
+struct DeviceTree {
+    const void *nodes = nullptr;   // float4 array, 2 per node slot
+    const void *points = nullptr;  // float4 array, 1 per point
+    uint32_t first_leaf = 1;       // 2^D
+    float box_lo[3] = {0, 0, 0};   // target bbox (Morton normalisation)
+    float box_inv[3] = {0, 0, 0};  // 1 / extent per axis (0 for a flat axis)
+    double center[3] = {0, 0, 0};
+};
+
+// Workspace carving (all offsets 256-byte aligned).
+struct SortWorkspace {
+    uint32_t *keys_a, *keys_b;
+    int32_t *vals_a, *vals_b;
+    uint32_t *hist;
+    int32_t ntiles;
+};
+size_t sort_workspace_bytes(int64_t m);
+SortWorkspace carve_sort_workspace(void *ws, int64_t m);
+
+struct IcpWorkspace {
+    SortWorkspace sort;
+    double *partials;   // KDNN_SUMS_DOUBLES * max_blocks
+    double *sums;       // KDNN_SUMS_DOUBLES
+    uint32_t *ticket;   // 1 counter, must be 0 between launches
+    int32_t max_blocks;
+};
+size_t icp_ws_bytes(int64_t n);
+IcpWorkspace carve_icp_workspace(void *ws, int64_t n);
+
+// Kernel launchers (return the hipError_t of the launch).
+// Morton-order the points moved by (R, t) (R == nullptr: not moved): on
+// return *perm points at the int32 permutation (traversal slot -> point).
+hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
+                               const SortWorkspace &ws, const int32_t **perm, hipStream_t s);
+// Same, for the ICP entry points: also clears the workspace's ticket counter.
+hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
+                            const IcpWorkspace &ws, const int32_t **perm, hipStream_t s);
+hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
+                     int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
+                     hipStream_t s);
+hipError_t launch_transform(const float *in, float *out, int64_t n, const double *R,
+                            const double *t, hipStream_t s);
+hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
+                            const double *R, const double *tv, const IcpWorkspace &ws,
+                            double *sums_out, int32_t *idx, float *d2, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
+
+}  // namespace kdnn
+
+// The opaque handle of the C ABI.
+struct kdnn_tree {
+    int device = 0;
+    kdnn::DeviceTree dev;
+    void *d_nodes = nullptr;
+    void *d_points = nullptr;
+    kdnn_tree_info info{};
+    double *h_pinned = nullptr;  // host readback slot for the ICP sums
+    std::mutex icp_mu;           // serialises users of h_pinned
+};

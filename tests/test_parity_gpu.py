@@ -1,0 +1,362 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (per the acceptance rules of the path):
+  * nn_query / the fused kernel's pairs: idx and dist2 bit-exact;
+  * transform_points: bit-exact;
+  * correspondence sums: ||H - H_o||_F <= 1e-5 ||H_o||_F and centroids within
+    1e-5 * max(||mu_o||, bbox diagonal);
+  * icp_align: ||R - R_o||_F <= 1e-4, ||t - t_o||_inf <= 1e-4.
+Every case prints its name before touching the device.
+"""
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._cases import adversarial_clouds, load_nn_cases
+
+pytestmark = pytest.mark.gpu
+
+H_RTOL = 1e-5
+MU_RTOL = 1e-5
+R_TOL = 1e-4
+T_TOL = 1e-4
+
+
+def say(*a):
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available(), "GPU tests need a HIP device"
+    return _t
+
+
+@pytest.fixture(scope="module")
+def kdnn(torch):
+    import kd_tree_nn_amd
+    from kd_tree_nn_amd import _lib
+    _lib.lib()  # fail loudly if the library is missing
+    return kd_tree_nn_amd
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def assert_nn_equal(idx, d2, oi, od, what):
+    idx = idx.cpu().numpy() if hasattr(idx, "cpu") else idx
+    d2 = d2.cpu().numpy() if hasattr(d2, "cpu") else d2
+    bad = np.nonzero((idx != oi) | (d2.view(np.uint32) != od.view(np.uint32)))[0]
+    assert len(bad) == 0, (f"{what}: {len(bad)} mismatches, first {bad[:5]}: "
+                           f"gpu {idx[bad[:5]]} {d2[bad[:5]]} oracle {oi[bad[:5]]} {od[bad[:5]]}")
+
+
+def check_sums(res, red, bbox_diag, what):
+    assert res["n"] == red["n"], what
+    Hn = np.linalg.norm(red["H"])
+    assert np.linalg.norm(res["H"] - red["H"]) <= H_RTOL * Hn, (what, res["H"], red["H"])
+    for k in ("mu_s", "mu_m"):
+        scale = max(np.linalg.norm(red[k]), bbox_diag)
+        assert np.linalg.norm(res[k] - red[k]) <= MU_RTOL * scale, (what, k, res[k], red[k])
+    assert abs(res["E"] - red["E"]) <= 1e-9 * max(red["E"], 1e-30), (what, res["E"], red["E"])
+
+
+def bbox_diag(T):
+    return float(np.linalg.norm(T.max(0).astype(np.float64) - T.min(0)))
+
+
+# ----------------------------------------------------------- cached inputs
+@functools.lru_cache(maxsize=None)
+def scene():
+    return synth.scene()
+
+
+@functools.lru_cache(maxsize=None)
+def scene_oracle_icp():
+    p = scene()
+    tr = oracle.KDTree(p.target, 16)
+    return tr, oracle.icp(p.target, p.source, p.iters, tree=tr)
+
+
+@functools.lru_cache(maxsize=None)
+def lidar():
+    return synth.lidar_pairs()
+
+
+# ======================================================== nearest neighbour
+@pytest.mark.parametrize("sort", [True, False])
+@pytest.mark.parametrize("leaf", [1, 2, 8])
+def test_golden_nn(torch, kdnn, leaf, sort):
+    for k, (T, Q, I, D) in enumerate(load_nn_cases()):
+        say("golden", k, "leaf", leaf, "sort", sort)
+        tree = kdnn.Tree(T, leaf)
+        idx, d2 = tree.query(dev(torch, Q), sort=sort)
+        assert_nn_equal(idx, d2, I, D, f"golden set {k}")
+
+
+@pytest.mark.parametrize("sort", [True, False])
+@pytest.mark.parametrize("leaf", [1, 3, 8, 16])
+def test_adversarial_nn(torch, kdnn, leaf, sort):
+    for name, T, Q in adversarial_clouds():
+        say("adversarial", name, "leaf", leaf, "sort", sort, len(T), len(Q))
+        oi, od = oracle.brute_nn(T, Q)
+        idx, d2 = kdnn.Tree(T, leaf).query(dev(torch, Q), sort=sort)
+        assert_nn_equal(idx, d2, oi, od, name)
+
+
+@pytest.mark.parametrize("m", [1, 2, 63, 64, 65, 255, 256, 257, 2047, 2048, 2049, 4097, 10007])
+def test_ragged_query_counts(torch, kdnn, m):
+    rng = np.random.Generator(np.random.PCG64(m))
+    T = rng.random((5000, 3)).astype(np.float32)
+    Q = rng.random((m, 3)).astype(np.float32) * 1.2 - 0.1
+    say("ragged m", m)
+    oi, od = oracle.brute_nn(T, Q)
+    tree = kdnn.Tree(T, 8)
+    for sort in (True, False):
+        idx, d2 = tree.query(dev(torch, Q), sort=sort)
+        assert_nn_equal(idx, d2, oi, od, f"m={m} sort={sort}")
+
+
+def test_nonfinite_and_empty(torch, kdnn):
+    say("nonfinite / empty")
+    rng = np.random.Generator(np.random.PCG64(3))
+    T = rng.random((300, 3)).astype(np.float32)
+    Q = rng.random((40, 3)).astype(np.float32)
+    Q[3, 0] = np.nan
+    Q[7, 2] = np.inf
+    Q[11, 1] = -np.inf
+    Q[20] = [1e30, 0, 0]          # every distance overflows to +inf
+    oi, od = oracle.brute_nn(T, Q)
+    assert oi[3] == -1 and oi[7] == -1 and oi[20] == -1
+    tree = kdnn.Tree(T, 8)
+    for sort in (True, False):
+        idx, d2 = tree.query(dev(torch, Q), sort=sort)
+        assert_nn_equal(idx, d2, oi, od, "nonfinite")
+    idx, d2 = tree.query(torch.empty((0, 3), dtype=torch.float32, device="cuda"))
+    assert idx.numel() == 0 and d2.numel() == 0
+
+
+def test_single_point_tree(torch, kdnn):
+    say("single point tree")
+    T = np.array([[0.5, -2.0, 7.0]], np.float32)
+    Q = np.random.Generator(np.random.PCG64(1)).normal(size=(100, 3)).astype(np.float32)
+    oi, od = oracle.brute_nn(T, Q)
+    idx, d2 = kdnn.Tree(T, 16).query(dev(torch, Q))
+    assert_nn_equal(idx, d2, oi, od, "single")
+    assert kdnn.Tree(T, 16).info["depth"] == 0
+
+
+def test_depth_cap_and_round_robin(torch, kdnn):
+    rng = np.random.Generator(np.random.PCG64(8))
+    T = np.concatenate([rng.random((3000, 3)), rng.random((3000, 3)) * [1, 0.01, 0.01]]).astype(np.float32)
+    Q = rng.random((2000, 3)).astype(np.float32)
+    oi, od = oracle.brute_nn(T, Q)
+    for kw in ({"max_depth": 4}, {"round_robin": True}, {"max_depth": 6, "round_robin": True}):
+        say("build variant", kw)
+        idx, d2 = kdnn.Tree(T, 8, **kw).query(dev(torch, Q))
+        assert_nn_equal(idx, d2, oi, od, str(kw))
+
+
+def test_query_stats_consistent(torch, kdnn):
+    say("query stats")
+    p = synth.tiny()
+    tree = kdnn.Tree(p.target, 8)
+    q = dev(torch, p.source)
+    idx, d2 = tree.query(q)
+    si, sd, cn, cp = tree.query_stats(q)
+    assert torch.equal(idx, si) and torch.equal(d2.view(torch.int32), sd.view(torch.int32))
+    D = tree.info["depth"]
+    assert int(cn.min()) >= D + 1 and int(cp.min()) >= 1
+    assert float(cn.float().mean()) < 0.25 * 2 ** (D + 1)
+
+
+# ================================================================ transform
+def test_transform_bit_exact(torch, kdnn):
+    say("transform")
+    rng = np.random.Generator(np.random.PCG64(12))
+    P = (rng.normal(size=(100_003, 3)) * 40).astype(np.float32)
+    for R, t in [(np.eye(3), np.zeros(3)),
+                 (synth.rotation_about(synth.random_unit(rng), 0.7), rng.normal(size=3) * 5),
+                 (synth.rot_z(np.pi / 2), np.array([1.0, -2.0, 0.25]))]:
+        exp = oracle.transform(P, R, t)
+        x = dev(torch, P)
+        out = kdnn.transform(x, R, t)
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), exp.view(np.uint32))
+        kdnn.transform(x, R, t, out=x)           # in place
+        np.testing.assert_array_equal(x.cpu().numpy().view(np.uint32), exp.view(np.uint32))
+    # fixed association (see the oracle pin): left-to-right fp64 sums, one cast
+    R = np.eye(3)
+    R[0] = [1.0, 2.0 ** -53, 2.0 ** -53]
+    out = kdnn.transform(dev(torch, np.ones((1, 3))), R, [2.0 ** -24, 0.0, 0.0])
+    assert out[0, 0].item() == 1.0
+    empty = torch.empty((0, 3), dtype=torch.float32, device="cuda")
+    assert kdnn.transform(empty, np.eye(3), np.zeros(3)).numel() == 0
+
+
+# ===================================================================== ICP
+def _pairs_oracle(T, S, R, t, tree=None):
+    q = oracle.transform(S, R, t)
+    oi, od = tree.query(q) if tree is not None else oracle.brute_nn(T, q)
+    ok = oi >= 0
+    return oi, od, oracle.reduce_pairs(S[ok], T[oi[ok]], od[ok])
+
+
+def test_tiny_correspond_reduce_and_icp(torch, kdnn):
+    p = synth.tiny()
+    tree = kdnn.Tree(p.target, 8)
+    src = dev(torch, p.source)
+    diag = bbox_diag(p.target)
+    for name, R, t in [("identity", np.eye(3), np.zeros(3)), ("truth", p.R_true, p.t_true)]:
+        say("tiny correspond_reduce", name)
+        oi, od, red = _pairs_oracle(p.target, p.source, R, t)
+        res = tree.correspond_reduce(src, R, t, return_pairs=True)
+        assert_nn_equal(res["idx"], res["d2"], oi, od, f"tiny pairs {name}")
+        check_sums(res, red, diag, f"tiny sums {name}")
+    say("tiny icp_align")
+    o = oracle.icp(p.target, p.source, p.iters, nn="brute")
+    g = tree.icp(src, max_iter=p.iters)
+    assert g["iters"] == p.iters
+    assert np.linalg.norm(g["R"] - o["R"]) <= R_TOL and np.max(np.abs(g["t"] - o["t"])) <= T_TOL
+    np.testing.assert_allclose(g["E"], o["E"], rtol=1e-6)
+    # recovers the generating motion within the noise
+    assert np.degrees(oracle.rot_err(g["R"], p.R_true)) < 0.1
+    # convergence rule matches the oracle's
+    say("tiny icp eps")
+    oe = oracle.icp(p.target, p.source, 50, nn="brute", eps=1e-7)
+    ge = tree.icp(src, max_iter=50, eps=1e-7)
+    assert ge["iters"] == oe["iters"]
+
+
+def test_scene_nn_full(torch, kdnn):
+    p = scene()
+    otree, o = scene_oracle_icp()
+    tree = kdnn.Tree(p.target, 16)
+    info = tree.info
+    assert info["depth"] == 13 and info["min_leaf"] == 12 and info["max_leaf"] == 13
+    for name, Q in [("iteration-0 queries", p.source),
+                    ("converged queries", oracle.transform(p.source, o["R"], o["t"]))]:
+        oi, od = otree.query(Q)
+        for sort in (True, False):
+            say("scene nn", name, "sort", sort)
+            idx, d2 = tree.query(dev(torch, Q), sort=sort)
+            assert_nn_equal(idx, d2, oi, od, f"scene {name} sort={sort}")
+
+
+def test_scene_correspond_reduce(torch, kdnn):
+    p = scene()
+    otree, o = scene_oracle_icp()
+    tree = kdnn.Tree(p.target, 16)
+    src = dev(torch, p.source)
+    diag = bbox_diag(p.target)
+    for k in (0, 1, 10, 29):
+        R = o["Rt_hist"][k, :9].reshape(3, 3)
+        t = o["Rt_hist"][k, 9:]
+        say("scene correspond_reduce iteration", k)
+        oi, od, red = _pairs_oracle(p.target, p.source, R, t, otree)
+        res = tree.correspond_reduce(src, R, t, return_pairs=True)
+        assert_nn_equal(res["idx"], res["d2"], oi, od, f"scene pairs it{k}")
+        check_sums(res, red, diag, f"scene sums it{k}")
+        assert res["E"] == pytest.approx(o["E"][k], rel=1e-12)
+
+
+def test_scene_icp_align(torch, kdnn):
+    p = scene()
+    _, o = scene_oracle_icp()
+    tree = kdnn.Tree(p.target, 16)
+    say("scene icp_align 30")
+    g = tree.icp(dev(torch, p.source), max_iter=p.iters)
+    assert g["iters"] == p.iters
+    dR = np.linalg.norm(g["R"] - o["R"])
+    dt = np.max(np.abs(g["t"] - o["t"]))
+    assert dR <= R_TOL and dt <= T_TOL, (dR, dt)
+    np.testing.assert_allclose(g["E"], o["E"], rtol=1e-6)
+    np.testing.assert_allclose(g["Rt_hist"], o["Rt_hist"], atol=1e-6)
+
+
+def test_determinism(torch, kdnn):
+    p = scene()
+    tree = kdnn.Tree(p.target, 16)
+    src = dev(torch, p.source)
+    say("determinism")
+    R = synth.rot_z(0.05)
+    a = tree.correspond_reduce(src, R, [0.1, 0.2, 0.0])
+    b = tree.correspond_reduce(src, R, [0.1, 0.2, 0.0])
+    for k in ("sum_s", "sum_m", "sum_sm"):
+        np.testing.assert_array_equal(a[k], b[k])
+    assert a["E"] == b["E"]
+    g1 = tree.icp(src, max_iter=5)
+    g2 = tree.icp(src, max_iter=5)
+    np.testing.assert_array_equal(g1["R"], g2["R"])
+    # the async entry point writes the same sums
+    import torch as T
+    ws = tree.icp_workspace(len(p.source))
+    sums = T.zeros(17, dtype=T.float64, device="cuda")
+    tree.correspond_reduce_async(src, R, [0.1, 0.2, 0.0], sums, ws)
+    tree.correspond_reduce_async(src, R, [0.1, 0.2, 0.0], sums, ws, flags=kdnn.KDNN_ICP_REUSE_ORDER)
+    s = sums.cpu().numpy()
+    np.testing.assert_array_equal(s[0:3], a["sum_s"])
+    np.testing.assert_array_equal(s[6:15].reshape(3, 3), a["sum_sm"])
+    assert s[15] == a["E"] and s[16] == a["n"]
+    # no-sort traversal gives the same pairs (sums may differ in the last bits)
+    c = tree.correspond_reduce(src, R, [0.1, 0.2, 0.0], flags=kdnn.KDNN_ICP_NO_SORT)
+    assert c["n"] == a["n"] and c["E"] == pytest.approx(a["E"], rel=1e-12)
+
+
+def test_workspace_checks(torch, kdnn):
+    say("workspace checks")
+    p = synth.tiny()
+    tree = kdnn.Tree(p.target, 8)
+    src = dev(torch, p.source)
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kdnn.KdnnError, match="EINVAL"):
+        tree.correspond_reduce(src, np.eye(3), np.zeros(3), workspace=small)
+    with pytest.raises(kdnn.KdnnError, match="EINVAL"):
+        tree.query(src, workspace=small)
+
+
+@pytest.mark.parametrize("leaf", [8, 16])
+def test_stress_nn(torch, kdnn, leaf):
+    p = synth.stress()
+    say("stress 1M x 1M leaf", leaf)
+    oi, od = oracle.KDTree(p.target, 8).query(p.source)
+    tree = kdnn.Tree(p.target, leaf)
+    assert tree.info["depth"] == (17 if leaf == 8 else 16)
+    idx, d2 = tree.query(dev(torch, p.source))
+    assert_nn_equal(idx, d2, oi, od, f"stress leaf {leaf}")
+
+
+@pytest.mark.parametrize("leaf", [8, 16])
+def test_skewed_nn(torch, kdnn, leaf):
+    p = synth.skewed()
+    say("skewed 500k leaf", leaf)
+    oi, od = oracle.KDTree(p.target, 8).query(p.source)
+    idx, d2 = kdnn.Tree(p.target, leaf).query(dev(torch, p.source))
+    assert_nn_equal(idx, d2, oi, od, f"skewed leaf {leaf}")
+
+
+def test_lidar_pairs(torch, kdnn):
+    pairs = lidar()
+    assert len(pairs) == 16
+    for k, p in enumerate(pairs):
+        say("lidar pair", k, len(p.target), len(p.source))
+        otree = oracle.KDTree(p.target, 16)
+        tree = kdnn.Tree(p.target, 16)
+        src = dev(torch, p.source)
+        oi, od, red = _pairs_oracle(p.target, p.source, np.eye(3), np.zeros(3), otree)
+        res = tree.correspond_reduce(src, np.eye(3), np.zeros(3), return_pairs=True)
+        assert_nn_equal(res["idx"], res["d2"], oi, od, f"lidar {k} pairs")
+        check_sums(res, red, bbox_diag(p.target), f"lidar {k}")
+        if k in (0, 15):
+            say("lidar icp_align pair", k)
+            o = oracle.icp(p.target, p.source, p.iters, tree=otree)
+            g = tree.icp(src, max_iter=p.iters)
+            assert np.linalg.norm(g["R"] - o["R"]) <= R_TOL
+            assert np.max(np.abs(g["t"] - o["t"])) <= T_TOL
+            assert np.degrees(oracle.rot_err(g["R"], p.R_true)) < 0.5
