@@ -156,6 +156,13 @@ kdnn_status kdtree_build_host(const float *xyz_host, int64_t n, const kdnn_build
 /* Query flags. */
 #define KDNN_QUERY_NO_SORT 1u /* traverse in the given order (skip the Morton ordering) */
 
+/* Lanes cooperating on one query (nn_query, nn_query_stats and the ICP entry
+ * points): KDNN_LANES(g) with g in {1, 2, 4, 8, 16}; without it the library
+ * picks g from the number of queries.  Results do not depend on g. */
+#define KDNN_LANES_SHIFT 8
+#define KDNN_LANES_MASK (0x1fu << KDNN_LANES_SHIFT)
+#define KDNN_LANES(g) ((uint32_t)(g) << KDNN_LANES_SHIFT)
+
 /* Bytes of device workspace nn_query needs for m queries (Morton keys,
  * permutation, radix-sort histograms). 0 for m <= 0. */
 size_t nn_query_workspace_bytes(int64_t m);
@@ -249,13 +256,14 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  *   Rt_hist      : optional [max_iter][12] fp64, (R_k row-major, t_k) used by
  *                  iteration k.
  *   iters_done   : optional, iterations completed.
+ *   flags        : KDNN_ICP_NO_SORT and/or KDNN_LANES(g).
  * The traversal order is computed once, from the source moved by (R0, t0).
  * On EDEGENERATE the outputs hold the last good transform.
  * Errors: EINVAL, EDEVICE, EDEGENERATE. */
 kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, const double *R0_host,
                       const double *t0_host, int32_t max_iter, double eps, double *R_out,
                       double *t_out, double *E_hist, double *Rt_hist, int32_t *iters_done,
-                      void *ws_dev, size_t ws_bytes, hipStream_t stream);
+                      uint32_t flags, void *ws_dev, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- misc */
 

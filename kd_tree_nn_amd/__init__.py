@@ -132,8 +132,11 @@ class Tree:
         return torch.empty(int(_lib.lib().nn_query_workspace_bytes(m)), dtype=torch.uint8,
                            device=self.device)
 
-    def query(self, q, sort: bool = True, out=None, workspace=None, stream=None):
-        """(idx int32[m], dist2 float32[m]) of the exact nearest target point."""
+    def query(self, q, sort: bool = True, out=None, workspace=None, stream=None, lanes=None):
+        """(idx int32[m], dist2 float32[m]) of the exact nearest target point.
+
+        lanes: lanes cooperating on each query (1, 2, 4, 8, 16; None = automatic).
+        """
         torch = _torch()
         q = _dev_points(q, "queries")
         m = q.shape[0]
@@ -144,11 +147,12 @@ class Tree:
         if sort and m > 0:
             ws = workspace if workspace is not None else self.query_workspace(m)
         _lib.check(_lib.lib().nn_query(
-            self._h, _ptr(q), m, _ptr(idx), _ptr(d2), 0 if sort else KDNN_QUERY_NO_SORT,
+            self._h, _ptr(q), m, _ptr(idx), _ptr(d2),
+            (0 if sort else KDNN_QUERY_NO_SORT) | _lib.lanes_flag(lanes),
             _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)), "nn_query")
         return idx, d2
 
-    def query_stats(self, q, sort: bool = True):
+    def query_stats(self, q, sort: bool = True, lanes=None):
         """query() plus per-query counts of nodes loaded and leaf points scanned."""
         torch = _torch()
         q = _dev_points(q, "queries")
@@ -160,8 +164,8 @@ class Tree:
         ws = self.query_workspace(m) if sort and m > 0 else None
         _lib.check(_lib.lib().nn_query_stats(
             self._h, _ptr(q), m, _ptr(idx), _ptr(d2), _ptr(cn), _ptr(cp),
-            0 if sort else KDNN_QUERY_NO_SORT, _ptr(ws), ws.numel() if ws is not None else 0,
-            _stream()), "nn_query_stats")
+            (0 if sort else KDNN_QUERY_NO_SORT) | _lib.lanes_flag(lanes), _ptr(ws),
+            ws.numel() if ws is not None else 0, _stream()), "nn_query_stats")
         return idx, d2, cn, cp
 
     # ------------------------------------------------------------------ ICP
@@ -207,7 +211,7 @@ class Tree:
             "icp_correspond_reduce_async")
 
     def icp(self, src, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
-            workspace=None, stream=None) -> dict:
+            workspace=None, stream=None, lanes=None, sort: bool = True) -> dict:
         """ICP registration of the source (device, original coordinates) onto the tree."""
         src = _dev_points(src, "src")
         n = src.shape[0]
@@ -224,6 +228,7 @@ class Tree:
             R0a[1] if R0a else None, t0a[1] if t0a else None, int(max_iter), float(eps),
             R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
             E.ctypes.data_as(_lib.c_dp), Rt.ctypes.data_as(_lib.c_dp), ctypes.byref(it),
+            (0 if sort else KDNN_ICP_NO_SORT) | _lib.lanes_flag(lanes),
             _ptr(ws), ws.numel(), _stream(stream)), "icp_align")
         k = it.value
         return {"R": R.reshape(3, 3), "t": t, "E": E[:k], "Rt_hist": Rt[:k], "iters": k}

@@ -16,6 +16,12 @@ KDNN_QUERY_NO_SORT = 1
 KDNN_ICP_REUSE_ORDER = 1
 KDNN_ICP_NO_SORT = 2
 KDNN_SUMS_DOUBLES = 17
+KDNN_LANES_SHIFT = 8
+
+
+def lanes_flag(lanes):
+    """KDNN_LANES(g): g lanes cooperate on a query (0 / None = library's choice)."""
+    return (int(lanes or 0) & 0x1f) << KDNN_LANES_SHIFT
 
 
 class BuildParams(ctypes.Structure):
@@ -55,7 +61,7 @@ SIGNATURES = {
                                             c_u32, c_vp, c_sz, c_vp]),
     "kdnn_procrustes": (c_i32, [ctypes.POINTER(IcpSums), c_dp, c_dp]),
     "icp_align": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, c_i32, ctypes.c_double, c_dp, c_dp,
-                          c_dp, c_dp, ctypes.POINTER(c_i32), c_vp, c_sz, c_vp]),
+                          c_dp, c_dp, ctypes.POINTER(c_i32), c_u32, c_vp, c_sz, c_vp]),
     "kdnn_last_error": (ctypes.c_char_p, []),
     "kdnn_version": (c_i32, []),
 }

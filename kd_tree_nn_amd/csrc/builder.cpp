@@ -3,11 +3,15 @@
 // the CPU; §3.1: linearised array, parent before child; §5.1: all storage
 // reserved up front, in-place std::nth_element; §5.2: optional depth cap).
 //
-// The tree is complete: every node above depth D is split at its index
-// median mid = lo + floor(cnt / 2) (left = [lo, mid), right = [mid, hi)),
-// so the node array is an implicit heap and every leaf sits at depth D with
-// floor(n / 2^D) or ceil(n / 2^D) points.  Split values are actual point
-// coordinates: left points have coordinate <= split <= right points.
+// The tree is complete: every node above depth D is split at a median, so
+// the node array is an implicit heap and every leaf sits at depth D.  Node a
+// of depth d (a = 0 .. 2^d - 1 from the left) owns the point slots
+// [floor(a n / 2^d), floor((a + 1) n / 2^d)) and splits them at
+// floor((2a + 1) n / 2^(d+1)), which is the lower or the upper median of its
+// points.  Hence leaf j owns [floor(j n / 2^D), floor((j + 1) n / 2^D)):
+// floor(n / 2^D) or ceil(n / 2^D) points, and a point range is a function
+// of the leaf index alone.  Split values are actual point coordinates: left
+// points have coordinate <= split <= right points.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -62,6 +66,7 @@ namespace {
 
 struct Builder {
     const float *P;
+    int64_t n;
     int32_t D;
     bool round_robin;
     std::vector<int32_t> perm;
@@ -93,9 +98,12 @@ struct Builder {
     {
         const int64_t a = lo[i], b = hi[i];
         const int axis = pick_axis(a, b, depth);
-        const int64_t mid = a + (b - a) / 2;
-        float split = 0.0f;
-        if (b > a) {
+        const int64_t idx_in_level = i - (int64_t(1) << depth);
+        const int64_t mid = ((2 * idx_in_level + 1) * n) >> (depth + 1);
+        // An empty right child (possible only when the node holds one point)
+        // gets split = +inf: every finite query then takes the left side.
+        float split = mid < b ? 0.0f : INFINITY;
+        if (mid < b) {
             const float *Pp = P;
             auto less = [Pp, axis](int32_t u, int32_t v) {
                 const float x = Pp[3 * int64_t(u) + axis], y = Pp[3 * int64_t(v) + axis];
@@ -147,6 +155,7 @@ kdnn_status build_host_tree(const float *xyz, int64_t n, const kdnn_build_params
 
     Builder b;
     b.P = xyz;
+    b.n = n;
     b.D = D;
     b.round_robin = p && (p->flags & KDNN_BUILD_ROUND_ROBIN);
     b.nodes = &out.nodes;

@@ -37,6 +37,12 @@ kdnn_status hip_fail(hipError_t e, const char *what)
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+bool lanes_ok(uint32_t flags)
+{
+    const uint32_t g = (flags & KDNN_LANES_MASK) >> KDNN_LANES_SHIFT;
+    return g == 0 || g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+}
+
 double ms_since(std::chrono::steady_clock::time_point t0)
 {
     return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
@@ -111,7 +117,8 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
         e = launch_icp_order(tree->dev, src, n, rt, w, &perm, s);
     }
     if (e != hipSuccess) return hip_fail(e, "icp: order launch");
-    e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, s);
+    e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2,
+                         int((flags >> KDNN_LANES_SHIFT) & 0x1f), s);
     if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
     return KDNN_OK;
 }
@@ -124,7 +131,8 @@ kdnn_status icp_check(const kdnn_tree *tree, const float *src, int64_t n, const 
     kdnn_status st = check_points(src, n, "icp: src");
     if (st != KDNN_OK) return st;
     if (!R || !t) return fail(KDNN_EINVAL, "icp: null R or t");
-    if (flags & ~(KDNN_ICP_REUSE_ORDER | KDNN_ICP_NO_SORT)) return fail(KDNN_EINVAL, "icp: unknown flag");
+    if ((flags & ~(KDNN_ICP_REUSE_ORDER | KDNN_ICP_NO_SORT | KDNN_LANES_MASK)) || !lanes_ok(flags))
+        return fail(KDNN_EINVAL, "icp: unknown flag or lane count");
     return check_ws(ws, ws_bytes, icp_ws_bytes(n));
 }
 
@@ -203,6 +211,8 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     d.nodes = t->d_nodes;
     d.points = t->d_points;
     d.first_leaf = uint32_t(1) << ht.depth;
+    d.depth = ht.depth;
+    d.n = n;
     for (int k = 0; k < 3; ++k) {
         d.box_lo[k] = ht.bbox_min[k];
         const float ext = ht.bbox_max[k] - ht.bbox_min[k];
@@ -257,7 +267,8 @@ static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t 
     if (m == 0) return KDNN_OK;
     if (!idx || !d2) return fail(KDNN_EINVAL, "nn_query: null output");
     if (!aligned(idx, 4) || !aligned(d2, 4)) return fail(KDNN_EINVAL, "nn_query: misaligned output");
-    if (flags & ~KDNN_QUERY_NO_SORT) return fail(KDNN_EINVAL, "nn_query: unknown flag");
+    if ((flags & ~(KDNN_QUERY_NO_SORT | KDNN_LANES_MASK)) || !lanes_ok(flags))
+        return fail(KDNN_EINVAL, "nn_query: unknown flag or lane count");
     const int32_t *perm = nullptr;
     if (!(flags & KDNN_QUERY_NO_SORT)) {
         st = check_ws(ws, ws_bytes, sort_workspace_bytes(m));
@@ -266,7 +277,8 @@ static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t 
         hipError_t e = launch_morton_order(tree->dev, q, m, nullptr, w, &perm, s);
         if (e != hipSuccess) return hip_fail(e, "nn_query: order launch");
     }
-    hipError_t e = launch_nn(tree->dev, q, m, perm, idx, d2, cn, cp, stats, s);
+    hipError_t e = launch_nn(tree->dev, q, m, perm, idx, d2, cn, cp, stats,
+                             int((flags >> KDNN_LANES_SHIFT) & 0x1f), s);
     if (e != hipSuccess) return hip_fail(e, "nn_query: launch");
     return KDNN_OK;
 }
@@ -373,7 +385,7 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
 kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, const double *R0_host,
                       const double *t0_host, int32_t max_iter, double eps, double *R_out,
                       double *t_out, double *E_hist, double *Rt_hist, int32_t *iters_done,
-                      void *ws_dev, size_t ws_bytes, hipStream_t stream)
+                      uint32_t flags, void *ws_dev, size_t ws_bytes, hipStream_t stream)
 {
     KDNN_GUARD_BEGIN
     double R[9], t[3];
@@ -382,7 +394,9 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     if (!R_out || !t_out) return fail(KDNN_EINVAL, "icp_align: null R_out or t_out");
     if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align: max_iter < 0");
     if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align: eps must be >= 0");
-    kdnn_status st = icp_check(tree, src_dev, n, R, t, 0, ws_dev, ws_bytes);
+    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_LANES_MASK))
+        return fail(KDNN_EINVAL, "icp_align: unknown flag");
+    kdnn_status st = icp_check(tree, src_dev, n, R, t, flags, ws_dev, ws_bytes);
     if (st != KDNN_OK) return st;
     std::memcpy(R_out, R, sizeof R);
     std::memcpy(t_out, t, sizeof t);
@@ -399,8 +413,9 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
             std::memcpy(Rt_hist + 12 * k, R, sizeof R);
             std::memcpy(Rt_hist + 12 * k + 9, t, sizeof t);
         }
-        st = icp_enqueue(tree, src_dev, n, R, t, w.sums, nullptr, nullptr,
-                         k == 0 ? 0u : KDNN_ICP_REUSE_ORDER, w, stream);
+        const uint32_t f = (flags & KDNN_ICP_NO_SORT) ? flags
+                           : (k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER));
+        st = icp_enqueue(tree, src_dev, n, R, t, w.sums, nullptr, nullptr, f, w, stream);
         if (st != KDNN_OK) return st;
         hipError_t e = hipMemcpyAsync(mt->h_pinned, w.sums, KDNN_SUMS_DOUBLES * sizeof(double),
                                       hipMemcpyDeviceToHost, stream);

@@ -58,6 +58,8 @@ struct DeviceTree {
     const void *nodes = nullptr;   // float4 array, 2 per node slot
     const void *points = nullptr;  // float4 array, 1 per point
     uint32_t first_leaf = 1;       // 2^D
+    int32_t depth = 0;             // D
+    int64_t n = 0;                 // target points
     float box_lo[3] = {0, 0, 0};   // target bbox (Morton normalisation)
     float box_inv[3] = {0, 0, 0};  // 1 / extent per axis (0 for a flat axis)
     double center[3] = {0, 0, 0};
@@ -67,7 +69,8 @@ struct DeviceTree {
 struct SortWorkspace {
     uint32_t *keys_a, *keys_b;
     int32_t *vals_a, *vals_b;
-    uint32_t *hist;
+    uint32_t *hist;    // [256][ntiles] tile counts per digit
+    uint32_t *totals;  // [256] per-digit totals
     int32_t ntiles;
 };
 size_t sort_workspace_bytes(int64_t m);
@@ -91,14 +94,17 @@ hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m,
 // Same, for the ICP entry points: also clears the workspace's ticket counter.
 hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                             const IcpWorkspace &ws, const int32_t **perm, hipStream_t s);
+// lanes: lanes per query (1, 2, 4, 8, 16); anything else = automatic.
+int lanes_for(int64_t m, int lanes);
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     hipStream_t s);
+                     int lanes, hipStream_t s);
 hipError_t launch_transform(const float *in, float *out, int64_t n, const double *R,
                             const double *t, hipStream_t s);
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
-                            double *sums_out, int32_t *idx, float *d2, hipStream_t s);
+                            double *sums_out, int32_t *idx, float *d2, int lanes,
+                            hipStream_t s);
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace kdnn

@@ -13,12 +13,19 @@
 
 namespace kdnn {
 
-constexpr int kWG = 256;                          // traversal work-group: 4 wave64
+// Compile-time tuning knobs (defaults are the shipped configuration).
+#ifndef KDNN_WG
+#define KDNN_WG 256
+#endif
+#ifndef KDNN_XCD_REMAP
+#define KDNN_XCD_REMAP 1
+#endif
+constexpr int kWG = KDNN_WG;                      // traversal work-group size
+constexpr int kLeafChunk = 16;                    // leaf points loaded per batch (one lane)
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
 constexpr int kSortTile = kSortThreads * kSortItems;  // keys per radix tile
 constexpr int kKeyBits = 16;                      // Morton prefix used for ordering
-constexpr int kScanThreads = 1024;
 constexpr int kIcpMaxBlocks = 4096;
 constexpr int kNumXcd = 8;
 constexpr int kS = KDNN_SUMS_DOUBLES;
@@ -30,6 +37,7 @@ constexpr int kS = KDNN_SUMS_DOUBLES;
 // i.e. on one spatially coherent slice of the Morton-ordered queries.
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
 {
+    if (!KDNN_XCD_REMAP) return b;
     const uint32_t x = b % kNumXcd, slot = b / kNumXcd;
     const uint32_t q = nb / kNumXcd, r = nb % kNumXcd;
     return x * q + (x < r ? x : r) + slot;
@@ -44,78 +52,342 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
 // far child lies entirely beyond the split plane, so this prunes everything
 // the plane test prunes and more.  That distance is a lower bound of every
 // fp32 point distance in the box (each rounding step is monotone), so a
-// point that could beat or tie the best is never skipped; together with the
-// (distance, index) comparison the result is the lowest-index nearest point
-// whatever the visiting order.
+// point that could beat or tie the best is never skipped.
+//
+// Candidates are ranked by the 64-bit key (fp32 distance bits, original
+// index): distances are >= 0, whose bit patterns order like their values, so
+// "closer, or as close with a lower index" is one unsigned comparison and
+// the result is the lowest-index nearest point whatever the visiting order.
+// A distance that overflows to +inf is never an answer (nothing is strictly
+// closer than the initial +inf), hence the final fix-up to index -1.
 //
 // No stack: the node index spells the path from the root, and bit d of
 // `far` records whether the path node at depth d+1 is a far child.  After a
 // subtree is done, the next subtree is the far sibling of the deepest path
-// node that is still a near child.
+// node that is still a near child.  Node steps are branch-free (selects), so
+// the two 16-byte loads of a node are in flight together and lanes of a
+// wave that disagree on the way only differ in data, not in control flow.
+//
+// Wave shape: lanes walk internal nodes until every lane of the wave has
+// reached a leaf (or finished), then all of them scan their leaves at once.
+// Leaf j owns point slots [floor(j n/2^D), floor((j+1) n/2^D)), so its points
+// are loaded together with its record.
+constexpr uint64_t kNoKey = 0x7F800000FFFFFFFFull;  // (+inf, index -1)
+constexpr uint32_t kDone = 0xFFFFFFFFu;
+
 struct Best {
     float d;
     int32_t idx;
-    float mx, my, mz;  // coordinates of the best target point
+    uint32_t slot;  // leaf-order slot of the winner (when idx >= 0)
 };
 
-template <bool STATS>
-__device__ __forceinline__ void nn_search(const float4 *__restrict__ nodes,
-                                          const float4 *__restrict__ pts, uint32_t first_leaf,
-                                          float qx, float qy, float qz, Best &b, uint32_t &cn,
-                                          uint32_t &cp)
+struct TreeView {
+    const float4 *__restrict__ nodes;
+    const float4 *__restrict__ pts;
+    uint32_t first_leaf;  // 2^D
+    int32_t depth;        // D
+    int64_t n;
+};
+
+__device__ __forceinline__ uint64_t nn_key(float d, uint32_t idx)
 {
-    b.d = INFINITY;
-    b.idx = -1;
-    b.mx = b.my = b.mz = 0.0f;
-    if (!(isfinite(qx) && isfinite(qy) && isfinite(qz))) return;
-    uint32_t i = 1, far = 0;
-    for (;;) {
-        const float4 A = nodes[2 * i];      // lo.x lo.y lo.z hi.x
-        const float4 B = nodes[2 * i + 1];  // hi.y hi.z w6 w7
-        if (STATS) ++cn;
-        const float gx = qx < A.x ? A.x - qx : (qx > A.w ? qx - A.w : 0.0f);
-        const float gy = qy < A.y ? A.y - qy : (qy > B.x ? qy - B.x : 0.0f);
-        const float gz = qz < A.z ? A.z - qz : (qz > B.y ? qz - B.y : 0.0f);
-        const float lb = (gx * gx + gy * gy) + gz * gz;
-        if (lb <= b.d && lb < INFINITY) {
-            if (i < first_leaf) {
-                const uint32_t axis = __float_as_uint(B.w);
-                const float qa = axis == 0 ? qx : (axis == 1 ? qy : qz);
-                i = 2 * i + (qa >= B.z ? 1u : 0u);
-                continue;
+    return (uint64_t(__float_as_uint(d)) << 32) | idx;
+}
+
+__device__ __forceinline__ float key_dist(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
+
+__device__ __forceinline__ void finish(uint64_t key, uint32_t slot, Best &b)
+{
+    b.d = key_dist(key);
+    b.idx = b.d < INFINITY ? int32_t(uint32_t(key)) : -1;
+    b.slot = slot;
+}
+
+// The subtree that follows the finished subtree i (kDone when none is left
+// at depth >= floor, `floor_mask` = ~(2^floor - 1)); updates `far`.
+__device__ __forceinline__ uint32_t next_subtree(uint32_t i, uint32_t &far, uint32_t floor_mask)
+{
+    const uint32_t dep = 31u - uint32_t(__clz(int(i)));
+    const uint32_t open = ~far & ((1u << dep) - 1u) & floor_mask;
+    const uint32_t h = 31u - uint32_t(__clz(int(open | 1u)));
+    const uint32_t nxt = (i >> ((dep - h - 1u) & 31u)) ^ 1u;
+    const uint32_t nfar = (far & ((1u << h) - 1u)) | (1u << h);
+    far = open ? nfar : far;
+    return open ? nxt : kDone;
+}
+
+// fp32 squared distance from q to the box (lo = A.xyz, hi = (A.w, B.x, B.y)).
+// Per axis the gap is max(lo - q, q - hi, 0): the same single fp32
+// subtraction as "lo - q if q < lo, q - hi if q > hi, else 0".
+__device__ __forceinline__ float box_lb(float qx, float qy, float qz, const float4 &A,
+                                        const float4 &B)
+{
+    const float gx = fmaxf(fmaxf(A.x - qx, qx - A.w), 0.0f);
+    const float gy = fmaxf(fmaxf(A.y - qy, qy - B.x), 0.0f);
+    const float gz = fmaxf(fmaxf(A.z - qz, qz - B.y), 0.0f);
+    return (gx * gx + gy * gy) + gz * gz;
+}
+
+__device__ __forceinline__ bool enters(float lb, float best)
+{
+    return (lb <= best) & (lb < INFINITY);
+}
+
+__device__ __forceinline__ uint32_t near_child(uint32_t i, const float4 &B, float qx, float qy,
+                                               float qz)
+{
+    const uint32_t axis = __float_as_uint(B.w);
+    const float qa = axis == 0 ? qx : (axis == 1 ? qy : qz);
+    return 2 * i + (qa >= B.z ? 1u : 0u);
+}
+
+__device__ __forceinline__ void leaf_range(const TreeView &t, uint32_t i, int32_t &begin,
+                                           int32_t &last, int32_t &end)
+{
+    const uint64_t j = uint64_t(i - t.first_leaf);
+    begin = int32_t((j * uint64_t(t.n)) >> t.depth);
+    end = int32_t(((j + 1) * uint64_t(t.n)) >> t.depth);
+    last = end > begin ? end - 1 : begin;  // a valid slot even for an empty leaf
+}
+
+// Load C points (slots first, first + S, ...; clamped to `last`), then rank
+// them.  Clamped repeats of the last point carry its own key and never
+// replace it.
+template <int C, int S>
+__device__ __forceinline__ void load_points(const TreeView &t, int32_t first, int32_t last,
+                                            float4 (&p)[C], int32_t (&sl)[C])
+{
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        sl[c] = min(first + c * S, last);
+        p[c] = t.pts[sl[c]];
+    }
+}
+
+template <int C>
+__device__ __forceinline__ void rank_points(const float4 (&p)[C], const int32_t (&sl)[C], float qx,
+                                            float qy, float qz, uint64_t &key, uint32_t &slot)
+{
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const float dx = p[c].x - qx;
+        const float dy = p[c].y - qy;
+        const float dz = p[c].z - qz;
+        const float d = (dx * dx + dy * dy) + dz * dz;
+        const uint64_t k = nn_key(d, __float_as_uint(p[c].w));
+        const bool lt = k < key;
+        key = lt ? k : key;
+        slot = lt ? uint32_t(sl[c]) : slot;
+    }
+}
+
+template <bool STATS>
+__device__ __forceinline__ void nn_search(const TreeView &t, float qx, float qy, float qz, Best &b,
+                                          uint32_t &cn, uint32_t &cp)
+{
+    uint64_t key = kNoKey;
+    uint32_t slot = 0;
+    if (isfinite(qx) && isfinite(qy) && isfinite(qz)) {
+        uint32_t i = 1, far = 0;
+        for (;;) {
+            // Phase 1: internal nodes, until a leaf or the end of the search.
+            while (i < t.first_leaf) {
+                const float4 A = t.nodes[2 * i];
+                const float4 B = t.nodes[2 * i + 1];
+                if (STATS) ++cn;
+                const bool in = enters(box_lb(qx, qy, qz, A, B), key_dist(key));
+                const uint32_t child = near_child(i, B, qx, qy, qz);
+                uint32_t f2 = far;
+                const uint32_t nx = next_subtree(i, f2, ~0u);
+                i = in ? child : nx;
+                far = in ? far : f2;
             }
-            const int32_t begin = __float_as_int(B.z);
-            const int32_t count = __float_as_int(B.w);
-            for (int32_t k = 0; k < count; ++k) {
-                const float4 p = pts[begin + k];
-                const float dx = p.x - qx;
-                const float dy = p.y - qy;
-                const float dz = p.z - qz;
-                const float d = (dx * dx + dy * dy) + dz * dz;
-                const int32_t j = __float_as_int(p.w);
-                if (d < b.d || (d == b.d && j < b.idx)) {
-                    b.d = d;
-                    b.idx = j;
-                    b.mx = p.x;
-                    b.my = p.y;
-                    b.mz = p.z;
+            if (i == kDone) break;
+            // Phase 2: leaf i -- its record and first points in flight together.
+            int32_t begin, last, end;
+            leaf_range(t, i, begin, last, end);
+            const float4 A = t.nodes[2 * i];
+            const float4 B = t.nodes[2 * i + 1];
+            float4 p[kLeafChunk];
+            int32_t sl[kLeafChunk];
+            load_points<kLeafChunk, 1>(t, begin, last, p, sl);
+            if (STATS) ++cn;
+            if (enters(box_lb(qx, qy, qz, A, B), key_dist(key))) {
+                rank_points<kLeafChunk>(p, sl, qx, qy, qz, key, slot);
+                for (int32_t k0 = begin + kLeafChunk; k0 < end; k0 += kLeafChunk) {
+                    load_points<kLeafChunk, 1>(t, k0, last, p, sl);
+                    rank_points<kLeafChunk>(p, sl, qx, qy, qz, key, slot);
+                }
+                if (STATS) cp += uint32_t(end - begin);
+            }
+            i = next_subtree(i, far, ~0u);
+        }
+    }
+    finish(key, slot, b);
+}
+
+// ------------------------------------------------ cooperative (G-lane) search
+//
+// At small query counts the GPU is mostly idle and a launch lasts as long as
+// its slowest query chain, so G consecutive lanes share one query:
+//  1. all G lanes walk the greedy root-to-leaf path of the query, keeping the
+//     fp32 squared distance from the query to each split plane on the path
+//     (lane l % G keeps depth l);
+//  2. they scan the query's own leaf together and agree on a first best;
+//  3. the shallowest path depth k whose plane distance is <= best marks the
+//     deepest ancestor v_k whose cell contains the search ball: any point
+//     outside v_k's subtree is on the other side of some split of v_0..v_k-1
+//     and therefore at fp32 distance >= that plane distance > best (rounding
+//     is monotone), so it can neither beat nor tie the best;
+//  4. the subtree of v_k is cut into min(G, 2^(D-k)) disjoint subtrees, one
+//     per lane, each searched depth-first as above with the group's best
+//     (minimum key over the G lanes) for pruning.
+// The answer is the minimum key over everything scanned: the same exact
+// lowest-index nearest point.
+constexpr int kDevMaxDepth = 28;
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off)
+{
+    const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(v)), off, 64));
+    const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(v >> 32)), off, 64));
+    return (uint64_t(hi) << 32) | lo;
+}
+
+template <int G>
+__device__ __forceinline__ uint64_t group_min_key(uint64_t k)
+{
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) {
+        const uint64_t o = shfl_xor_u64(k, off);
+        k = o < k ? o : k;
+    }
+    return k;
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) v += uint32_t(__shfl_xor(int(v), off, 64));
+    return v;
+}
+
+template <int G, bool STATS>
+__device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, float qy, float qz,
+                                                Best &b, uint32_t &cn, uint32_t &cp)
+{
+    constexpr int LOG_G = G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : G == 16 ? 4 : 5;
+    constexpr int SLOTS = (kDevMaxDepth + G - 1) / G;
+    constexpr int C = 16 / G > 1 ? 16 / G : 2;  // own-leaf points per lane per round
+    constexpr int CL = 8;                        // points per batch in a lane's own leaves
+    const int lane = threadIdx.x & 63;
+    const int gl = lane & (G - 1);
+    const int gbase = lane & ~(G - 1);
+    const uint64_t gmask = (G == 64 ? ~uint64_t(0) : ((uint64_t(1) << G) - 1)) << gbase;
+    const int D = t.depth;
+
+    uint64_t key = kNoKey;
+    uint32_t slot = 0;
+
+    // 1. greedy descent, plane distances kept round-robin over the group
+    uint32_t i = 1;
+    float pd[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) pd[s] = INFINITY;
+#pragma unroll
+    for (int l = 0; l < kDevMaxDepth; ++l) {
+        if (l < D) {
+            const float4 B = t.nodes[2 * i + 1];  // hi.y hi.z split axis
+            const uint32_t axis = __float_as_uint(B.w);
+            const float qa = axis == 0 ? qx : (axis == 1 ? qy : qz);
+            const bool right = qa >= B.z;
+            const float dl = right ? qa - B.z : B.z - qa;
+            if ((l & (G - 1)) == gl) pd[l / G] = dl * dl;
+            i = 2 * i + (right ? 1u : 0u);
+        }
+    }
+    if (STATS && gl == 0) cn += uint32_t(D);
+
+    // 2. the query's own leaf, scanned by the whole group
+    {
+        int32_t begin, last, end;
+        leaf_range(t, i, begin, last, end);
+        for (int32_t k0 = begin; k0 < end; k0 += G * C) {
+            float4 p[C];
+            int32_t sl[C];
+            load_points<C, G>(t, k0 + gl, last, p, sl);
+            rank_points<C>(p, sl, qx, qy, qz, key, slot);
+        }
+        if (STATS && gl == 0) {
+            ++cn;
+            cp += uint32_t(end - begin);
+        }
+    }
+    uint64_t gkey = group_min_key<G>(key);
+
+    // 3. shallowest path depth whose split plane is within the best distance
+    int kstar = D;
+    {
+        const float gb = key_dist(gkey);
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int l = s * G + gl;
+            const uint64_t m = __ballot(l < D && pd[s] <= gb) & gmask;
+            if (m != 0 && kstar == D) kstar = s * G + (__ffsll((unsigned long long)m) - 1 - gbase);
+        }
+    }
+
+    // 4. lanes search disjoint parts of the subtree of v_kstar
+    if (kstar < D) {
+        const int gp = LOG_G < D - kstar ? LOG_G : D - kstar;
+        const uint32_t vk = i >> (D - kstar);
+        const uint32_t floor_mask = ~((1u << uint32_t(kstar + gp)) - 1u);
+        uint32_t ci = gl < (1 << gp) ? ((vk << gp) | uint32_t(gl)) : kDone;
+        uint32_t far = 0;
+        for (;;) {
+            if (ci != kDone) {
+                const float4 A = t.nodes[2 * ci];
+                const float4 B = t.nodes[2 * ci + 1];
+                if (STATS) ++cn;
+                const bool in = enters(box_lb(qx, qy, qz, A, B), key_dist(gkey));
+                if (ci < t.first_leaf) {
+                    const uint32_t child = near_child(ci, B, qx, qy, qz);
+                    uint32_t f2 = far;
+                    const uint32_t nx = next_subtree(ci, f2, floor_mask);
+                    ci = in ? child : nx;
+                    far = in ? far : f2;
+                } else {
+                    if (in) {
+                        int32_t begin, last, end;
+                        leaf_range(t, ci, begin, last, end);
+                        for (int32_t k0 = begin; k0 < end; k0 += CL) {
+                            float4 p[CL];
+                            int32_t sl[CL];
+                            load_points<CL, 1>(t, k0, last, p, sl);
+                            rank_points<CL>(p, sl, qx, qy, qz, key, slot);
+                        }
+                        if (STATS) cp += uint32_t(end - begin);
+                    }
+                    ci = next_subtree(ci, far, floor_mask);
                 }
             }
-            if (STATS) cp += uint32_t(count);
+            gkey = group_min_key<G>(key);
+            if ((__ballot(ci != kDone) & gmask) == 0) break;
         }
-        const uint32_t dep = 31u - uint32_t(__clz(int(i)));
-        const uint32_t open = ~far & ((1u << dep) - 1u);
-        if (open == 0) break;
-        const uint32_t h = 31u - uint32_t(__clz(int(open)));
-        i = (i >> (dep - h - 1u)) ^ 1u;
-        far = (far & ((1u << h) - 1u)) | (1u << h);
+    }
+
+    // 5. the group's answer and the winning lane's slot
+    const uint64_t wm = __ballot(key == gkey) & gmask;
+    const int win = __ffsll((unsigned long long)wm) - 1;
+    finish(gkey, uint32_t(__shfl(int(slot), win, 64)), b);
+    if (STATS) {
+        cn = group_sum_u32<G>(cn);
+        cp = group_sum_u32<G>(cp);
     }
 }
 
 struct NnArgs {
-    const float4 *nodes;
-    const float4 *pts;
-    uint32_t first_leaf;
+    TreeView tree;
     const float *q;
     int64_t m;
     const int32_t *perm;
@@ -125,22 +397,46 @@ struct NnArgs {
     uint32_t *cnt_pts;
 };
 
-template <bool STATS>
+template <int G, bool STATS>
+__device__ __forceinline__ void search_query(const TreeView &t, float qx, float qy, float qz,
+                                             Best &b, uint32_t &cn, uint32_t &cp)
+{
+    if (G == 1) {
+        nn_search<STATS>(t, qx, qy, qz, b, cn, cp);
+    } else if (isfinite(qx) && isfinite(qy) && isfinite(qz)) {
+        nn_search_group<G, STATS>(t, qx, qy, qz, b, cn, cp);
+    } else {
+        b.d = INFINITY;
+        b.idx = -1;
+        b.slot = 0;
+    }
+}
+
+// G lanes per query; a block handles kWG / G queries per sweep.  The loop
+// bound is uniform over the block so a group's lanes always stay together.
+template <int G, bool STATS>
 __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
 {
+    constexpr int QPB = kWG / G;
     const uint32_t nb = gridDim.x;
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
-    for (int64_t k = int64_t(blk) * kWG + threadIdx.x; k < a.m; k += int64_t(nb) * kWG) {
-        const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
-        const float qx = a.q[3 * i], qy = a.q[3 * i + 1], qz = a.q[3 * i + 2];
-        Best b;
-        uint32_t cn = 0, cp = 0;
-        nn_search<STATS>(a.nodes, a.pts, a.first_leaf, qx, qy, qz, b, cn, cp);
-        a.idx[i] = b.idx;
-        a.d2[i] = b.d;
-        if (STATS) {
-            if (a.cnt_nodes) a.cnt_nodes[i] = cn;
-            if (a.cnt_pts) a.cnt_pts[i] = cp;
+    const int gl = threadIdx.x & (G - 1);
+    for (int64_t base = int64_t(blk) * QPB; base < a.m; base += int64_t(nb) * QPB) {
+        const int64_t k = base + threadIdx.x / G;
+        if (k < a.m) {
+            const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+            const float qx = a.q[3 * i], qy = a.q[3 * i + 1], qz = a.q[3 * i + 2];
+            Best b;
+            uint32_t cn = 0, cp = 0;
+            search_query<G, STATS>(a.tree, qx, qy, qz, b, cn, cp);
+            if (gl == 0) {
+                a.idx[i] = b.idx;
+                a.d2[i] = b.d;
+                if (STATS) {
+                    if (a.cnt_nodes) a.cnt_nodes[i] = cn;
+                    if (a.cnt_pts) a.cnt_pts[i] = cp;
+                }
+            }
         }
     }
 }
@@ -155,9 +451,7 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
 // (atomic ticket) sums the partials in a fixed order.  The result does not
 // depend on scheduling.
 struct IcpArgs {
-    const float4 *nodes;
-    const float4 *pts;
-    uint32_t first_leaf;
+    TreeView tree;
     const float *src;
     int64_t n;
     const int32_t *perm;
@@ -202,8 +496,11 @@ __device__ __forceinline__ void block_sum(double (&acc)[kS], double *red /* LDS 
     }
 }
 
+template <int G>
 __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
 {
+    constexpr int QPB = kWG / G;
+    const int gl = threadIdx.x & (G - 1);
     __shared__ double red[(kWG / 64) * kS];
     __shared__ uint32_t is_last;
     double acc[kS];
@@ -212,7 +509,9 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
 
     const uint32_t nb = gridDim.x;
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
-    for (int64_t k = int64_t(blk) * kWG + threadIdx.x; k < a.n; k += int64_t(nb) * kWG) {
+    for (int64_t base = int64_t(blk) * QPB; base < a.n; base += int64_t(nb) * QPB) {
+        const int64_t k = base + threadIdx.x / G;
+        if (k >= a.n) continue;
         const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
         const double X = a.src[3 * i], Y = a.src[3 * i + 1], Z = a.src[3 * i + 2];
         const float qx = rigid_row(a.R[0], a.R[1], a.R[2], a.t[0], X, Y, Z);
@@ -220,13 +519,15 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         const float qz = rigid_row(a.R[6], a.R[7], a.R[8], a.t[2], X, Y, Z);
         Best b;
         uint32_t cn = 0, cp = 0;
-        nn_search<false>(a.nodes, a.pts, a.first_leaf, qx, qy, qz, b, cn, cp);
+        search_query<G, false>(a.tree, qx, qy, qz, b, cn, cp);
+        if (gl != 0) continue;
         if (a.idx) a.idx[i] = b.idx;
         if (a.d2) a.d2[i] = b.d;
         if (b.idx >= 0) {
             const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
-            const double m0 = double(b.mx) - a.c[0], m1 = double(b.my) - a.c[1],
-                         m2 = double(b.mz) - a.c[2];
+            const float4 mp = a.tree.pts[b.slot];
+            const double m0 = double(mp.x) - a.c[0], m1 = double(mp.y) - a.c[1],
+                         m2 = double(mp.z) - a.c[2];
             acc[0] += s0; acc[1] += s1; acc[2] += s2;
             acc[3] += m0; acc[4] += m1; acc[5] += m2;
             acc[6] += s0 * m0; acc[7] += s0 * m1; acc[8] += s0 * m2;
@@ -344,43 +645,64 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(OrderArgs oa, 
     h[threadIdx.x] = 0u;
     __syncthreads();
     const int64_t base = int64_t(blockIdx.x) * kSortTile;
+    uint32_t key[kSortItems];
+#pragma unroll
     for (int r = 0; r < kSortItems; ++r) {
         const int64_t e = base + r * kSortThreads + threadIdx.x;
-        if (e < oa.m) {
-            const uint32_t key = FROM_POINTS ? order_key(oa, e) : keys[e];
-            atomicAdd(&h[(key >> shift) & 255u], 1u);
-        }
+        key[r] = e < oa.m ? (FROM_POINTS ? order_key(oa, e) : keys[e]) : 0u;
     }
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r)
+        if (base + r * kSortThreads + threadIdx.x < oa.m) atomicAdd(&h[(key[r] >> shift) & 255u], 1u);
     __syncthreads();
     hist[int64_t(threadIdx.x) * ntiles + blockIdx.x] = h[threadIdx.x];
 }
 
-// Exclusive scan of hist[0..total) (digit-major, so the result is each
-// (digit, tile) pair's first output slot).  One work-group.
-__global__ __launch_bounds__(kScanThreads) void radix_scan_kernel(uint32_t *hist, int64_t total,
+// Per-digit exclusive scan over tiles: work-group d scans row d of hist
+// (the tile counts of digit d, contiguous) in place and writes the row total
+// to totals[d].  The scatter kernel adds the digit bases.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wsum /* LDS [4] */,
+                                                         uint32_t &total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+#pragma unroll
+    for (int ww = 0; ww < kSortThreads / 64; ++ww) {
+        before += ww < w ? wsum[ww] : 0u;
+        total += wsum[ww];
+    }
+    __syncthreads();
+    return before + x - v;
+}
+
+__global__ __launch_bounds__(kSortThreads) void radix_scan_kernel(uint32_t *hist, int32_t ntiles,
+                                                                  uint32_t *totals,
                                                                   uint32_t *zero_me)
 {
-    __shared__ uint32_t sums[kScanThreads];
-    const int64_t per = (total + kScanThreads - 1) / kScanThreads;
-    const int64_t a = int64_t(threadIdx.x) * per;
-    const int64_t e = a + per < total ? a + per : total;
-    uint32_t s = 0;
-    for (int64_t k = a; k < e; ++k) s += hist[k];
-    sums[threadIdx.x] = s;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        const uint32_t v = threadIdx.x >= off ? sums[threadIdx.x - off] : 0u;
-        __syncthreads();
-        sums[threadIdx.x] += v;
-        __syncthreads();
+    __shared__ uint32_t wsum[kSortThreads / 64];
+    uint32_t *row = hist + int64_t(blockIdx.x) * ntiles;
+    uint32_t carry = 0;
+    for (int32_t k0 = 0; k0 < ntiles; k0 += kSortThreads) {
+        const int32_t k = k0 + threadIdx.x;
+        const uint32_t v = k < ntiles ? row[k] : 0u;
+        uint32_t total;
+        const uint32_t ex = block_exclusive_scan(v, wsum, total);
+        if (k < ntiles) row[k] = carry + ex;
+        carry += total;
     }
-    uint32_t run = threadIdx.x ? sums[threadIdx.x - 1] : 0u;
-    for (int64_t k = a; k < e; ++k) {
-        const uint32_t v = hist[k];
-        hist[k] = run;
-        run += v;
+    if (threadIdx.x == 0) {
+        totals[blockIdx.x] = carry;
+        if (zero_me && blockIdx.x == 0) *zero_me = 0u;
     }
-    if (zero_me && threadIdx.x == 0) *zero_me = 0u;
 }
 
 // Stable scatter of one tile.  Element e = tile*2048 + r*256 + tid is the
@@ -391,23 +713,36 @@ __global__ __launch_bounds__(kScanThreads) void radix_scan_kernel(uint32_t *hist
 template <bool FROM_POINTS, bool WRITE_KEYS>
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     OrderArgs oa, const uint32_t *keys_in, const int32_t *vals_in, int shift,
-    const uint32_t *hist, int32_t ntiles, uint32_t *keys_out, int32_t *vals_out)
+    const uint32_t *hist, const uint32_t *totals, int32_t ntiles, uint32_t *keys_out,
+    int32_t *vals_out)
 {
     __shared__ uint32_t base[256];
     __shared__ uint32_t wcnt[kSortThreads / 64][256];
+    __shared__ uint32_t wsum[kSortThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const uint64_t below = (uint64_t(1) << lane) - 1u;
-    base[tid] = hist[int64_t(tid) * ntiles + blockIdx.x];
+    uint32_t all;
+    const uint32_t digit_base = block_exclusive_scan(totals[tid], wsum, all);
+    base[tid] = digit_base + hist[int64_t(tid) * ntiles + blockIdx.x];
     const int64_t tbase = int64_t(blockIdx.x) * kSortTile;
+    uint32_t keys_r[kSortItems];
+    int32_t vals_r[kSortItems];
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int64_t e = tbase + r * kSortThreads + tid;
+        keys_r[r] = 0u;
+        vals_r[r] = 0;
+        if (e < oa.m) {
+            keys_r[r] = FROM_POINTS ? order_key(oa, e) : keys_in[e];
+            vals_r[r] = FROM_POINTS ? int32_t(e) : vals_in[e];
+        }
+    }
+#pragma unroll
     for (int r = 0; r < kSortItems; ++r) {
         const int64_t e = tbase + r * kSortThreads + tid;
         const bool valid = e < oa.m;
-        uint32_t key = 0u;
-        int32_t val = 0;
-        if (valid) {
-            key = FROM_POINTS ? order_key(oa, e) : keys_in[e];
-            val = FROM_POINTS ? int32_t(e) : vals_in[e];
-        }
+        const uint32_t key = keys_r[r];
+        const int32_t val = vals_r[r];
         const uint32_t dig = (key >> shift) & 255u;
 #pragma unroll
         for (int ww = 0; ww < kSortThreads / 64; ++ww) wcnt[ww][tid] = 0u;
@@ -446,7 +781,7 @@ size_t sort_workspace_bytes(int64_t m)
 {
     if (m <= 0) return 0;
     const size_t mm = size_t(m);
-    return align256(mm * 4) * 3 + align256(size_t(256) * sort_tiles(m) * 4);
+    return align256(mm * 4) * 3 + align256(size_t(256) * sort_tiles(m) * 4) + align256(256 * 4);
 }
 
 SortWorkspace carve_sort_workspace(void *ws, int64_t m)
@@ -460,12 +795,13 @@ SortWorkspace carve_sort_workspace(void *ws, int64_t m)
     w.vals_a = reinterpret_cast<int32_t *>(p + 2 * a);
     w.hist = reinterpret_cast<uint32_t *>(p + 3 * a);
     w.ntiles = sort_tiles(m);
+    w.totals = reinterpret_cast<uint32_t *>(p + 3 * a + align256(size_t(256) * w.ntiles * 4));
     return w;
 }
 
-static int32_t icp_blocks(int64_t n)
+static int32_t icp_blocks(int64_t n, int G)
 {
-    const int64_t b = (n + kWG - 1) / kWG;
+    const int64_t b = (n + kWG / G - 1) / (kWG / G);
     return int32_t(b < 1 ? 1 : (b > kIcpMaxBlocks ? kIcpMaxBlocks : b));
 }
 
@@ -493,6 +829,17 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
 
 // --------------------------------------------------------------- launchers
 
+static TreeView tree_view(const DeviceTree &t)
+{
+    TreeView v;
+    v.nodes = static_cast<const float4 *>(t.nodes);
+    v.pts = static_cast<const float4 *>(t.points);
+    v.first_leaf = t.first_leaf;
+    v.depth = t.depth;
+    v.n = t.n;
+    return v;
+}
+
 static OrderArgs make_order_args(const DeviceTree &t, const float *pts, int64_t m, const float *R12)
 {
     OrderArgs oa{};
@@ -513,15 +860,14 @@ static hipError_t morton_order_impl(const DeviceTree &t, const float *pts, int64
 {
     const OrderArgs oa = make_order_args(t, pts, m, R12);
     const int32_t nt = ws.ntiles;
-    const int64_t total = int64_t(256) * nt;
     radix_hist_kernel<true><<<nt, kSortThreads, 0, s>>>(oa, nullptr, 0, ws.hist, nt);
-    radix_scan_kernel<<<1, kScanThreads, 0, s>>>(ws.hist, total, zero_me);
-    radix_scatter_kernel<true, true><<<nt, kSortThreads, 0, s>>>(oa, nullptr, nullptr, 0, ws.hist,
-                                                                 nt, ws.keys_b, ws.vals_b);
+    radix_scan_kernel<<<256, kSortThreads, 0, s>>>(ws.hist, nt, ws.totals, zero_me);
+    radix_scatter_kernel<true, true><<<nt, kSortThreads, 0, s>>>(
+        oa, nullptr, nullptr, 0, ws.hist, ws.totals, nt, ws.keys_b, ws.vals_b);
     radix_hist_kernel<false><<<nt, kSortThreads, 0, s>>>(oa, ws.keys_b, 8, ws.hist, nt);
-    radix_scan_kernel<<<1, kScanThreads, 0, s>>>(ws.hist, total, nullptr);
+    radix_scan_kernel<<<256, kSortThreads, 0, s>>>(ws.hist, nt, ws.totals, nullptr);
     radix_scatter_kernel<false, false><<<nt, kSortThreads, 0, s>>>(
-        oa, ws.keys_b, ws.vals_b, 8, ws.hist, nt, nullptr, ws.vals_a);
+        oa, ws.keys_b, ws.vals_b, 8, ws.hist, ws.totals, nt, nullptr, ws.vals_a);
     *perm = ws.vals_a;
     return hipGetLastError();
 }
@@ -538,14 +884,30 @@ hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, co
     return morton_order_impl(t, pts, m, R12, ws.sort, ws.ticket, perm, s);
 }
 
+template <int G>
+static void launch_nn_g(const NnArgs &a, bool stats, hipStream_t s)
+{
+    int64_t blocks = (a.m + kWG / G - 1) / (kWG / G);
+    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+    if (stats)
+        nn_kernel<G, true><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
+    else
+        nn_kernel<G, false><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
+}
+
+int lanes_for(int64_t m, int lanes)
+{
+    if (lanes == 1 || lanes == 2 || lanes == 4 || lanes == 8 || lanes == 16) return lanes;
+    (void)m;
+    return 1;
+}
+
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     hipStream_t s)
+                     int lanes, hipStream_t s)
 {
     NnArgs a{};
-    a.nodes = static_cast<const float4 *>(t.nodes);
-    a.pts = static_cast<const float4 *>(t.points);
-    a.first_leaf = t.first_leaf;
+    a.tree = tree_view(t);
     a.q = q;
     a.m = m;
     a.perm = perm;
@@ -553,12 +915,13 @@ hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32
     a.d2 = d2;
     a.cnt_nodes = cnt_nodes;
     a.cnt_pts = cnt_pts;
-    int64_t blocks = (m + kWG - 1) / kWG;
-    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
-    if (stats)
-        nn_kernel<true><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
-    else
-        nn_kernel<false><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
+    switch (lanes_for(m, lanes)) {
+    case 1: launch_nn_g<1>(a, stats, s); break;
+    case 2: launch_nn_g<2>(a, stats, s); break;
+    case 4: launch_nn_g<4>(a, stats, s); break;
+    case 8: launch_nn_g<8>(a, stats, s); break;
+    default: launch_nn_g<16>(a, stats, s); break;
+    }
     return hipGetLastError();
 }
 
@@ -575,12 +938,10 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
 
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
-                            double *sums_out, int32_t *idx, float *d2, hipStream_t s)
+                            double *sums_out, int32_t *idx, float *d2, int lanes, hipStream_t s)
 {
     IcpArgs a{};
-    a.nodes = static_cast<const float4 *>(t.nodes);
-    a.pts = static_cast<const float4 *>(t.points);
-    a.first_leaf = t.first_leaf;
+    a.tree = tree_view(t);
     a.src = src;
     a.n = n;
     a.perm = perm;
@@ -594,7 +955,15 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     a.sums = sums_out;
     a.idx = idx;
     a.d2 = d2;
-    icp_fused_kernel<<<dim3(uint32_t(icp_blocks(n))), kWG, 0, s>>>(a);
+    const int G = lanes_for(n, lanes);
+    const dim3 grid(uint32_t(icp_blocks(n, G)));
+    switch (G) {
+    case 1: icp_fused_kernel<1><<<grid, kWG, 0, s>>>(a); break;
+    case 2: icp_fused_kernel<2><<<grid, kWG, 0, s>>>(a); break;
+    case 4: icp_fused_kernel<4><<<grid, kWG, 0, s>>>(a); break;
+    case 8: icp_fused_kernel<8><<<grid, kWG, 0, s>>>(a); break;
+    default: icp_fused_kernel<16><<<grid, kWG, 0, s>>>(a); break;
+    }
     return hipGetLastError();
 }
 

@@ -67,6 +67,8 @@ def _check_tree(pts, bt, leaf, max_depth=0, round_robin=False):
     begin = nodes[L0:, 6].view(np.int32)
     count = nodes[L0:, 7].view(np.int32)
     assert begin[0] == 0 and np.all(begin[1:] == begin[:-1] + count[:-1]) and count.sum() == n
+    # leaf j owns slots [floor(j n / 2^D), floor((j + 1) n / 2^D))
+    np.testing.assert_array_equal(begin, (np.arange(L0, dtype=np.int64) * n) >> D)
     assert set(np.unique(count)) <= {n // L0, -(-n // L0)}
     if max_depth == 0:
         assert count.max() <= leaf
@@ -94,10 +96,13 @@ def _check_tree(pts, bt, leaf, max_depth=0, round_robin=False):
             split = nodes[i, 6]
             la, le = box_of(2 * i)
             ra, re_ = box_of(2 * i + 1)
-            assert le == ra and (le - la) == (e - a) // 2
+            assert le == ra and (le - la) in ((e - a) // 2, (e - a + 1) // 2)
             assert np.all(P[la:le, axis] <= split) and np.all(P[ra:re_, axis] >= split)
-            if e > a:
+            if re_ > ra:
                 assert split in P[ra:re_, axis]
+            else:
+                assert split == np.inf
+            if e > a:
                 d = int(np.floor(np.log2(i)))
                 if round_robin:
                     assert axis == d % 3

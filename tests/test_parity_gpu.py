@@ -91,24 +91,26 @@ def lidar():
 
 
 # ======================================================== nearest neighbour
+@pytest.mark.parametrize("lanes", [1, 4, 16])
 @pytest.mark.parametrize("sort", [True, False])
 @pytest.mark.parametrize("leaf", [1, 2, 8])
-def test_golden_nn(torch, kdnn, leaf, sort):
+def test_golden_nn(torch, kdnn, leaf, sort, lanes):
     for k, (T, Q, I, D) in enumerate(load_nn_cases()):
-        say("golden", k, "leaf", leaf, "sort", sort)
+        say("golden", k, "leaf", leaf, "sort", sort, "lanes", lanes)
         tree = kdnn.Tree(T, leaf)
-        idx, d2 = tree.query(dev(torch, Q), sort=sort)
+        idx, d2 = tree.query(dev(torch, Q), sort=sort, lanes=lanes)
         assert_nn_equal(idx, d2, I, D, f"golden set {k}")
 
 
+@pytest.mark.parametrize("lanes", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("sort", [True, False])
 @pytest.mark.parametrize("leaf", [1, 3, 8, 16])
-def test_adversarial_nn(torch, kdnn, leaf, sort):
+def test_adversarial_nn(torch, kdnn, leaf, sort, lanes):
     for name, T, Q in adversarial_clouds():
-        say("adversarial", name, "leaf", leaf, "sort", sort, len(T), len(Q))
+        say("adversarial", name, "leaf", leaf, "sort", sort, "lanes", lanes, len(T), len(Q))
         oi, od = oracle.brute_nn(T, Q)
-        idx, d2 = kdnn.Tree(T, leaf).query(dev(torch, Q), sort=sort)
-        assert_nn_equal(idx, d2, oi, od, name)
+        idx, d2 = kdnn.Tree(T, leaf).query(dev(torch, Q), sort=sort, lanes=lanes)
+        assert_nn_equal(idx, d2, oi, od, f"{name} lanes={lanes}")
 
 
 @pytest.mark.parametrize("m", [1, 2, 63, 64, 65, 255, 256, 257, 2047, 2048, 2049, 4097, 10007])
@@ -120,8 +122,9 @@ def test_ragged_query_counts(torch, kdnn, m):
     oi, od = oracle.brute_nn(T, Q)
     tree = kdnn.Tree(T, 8)
     for sort in (True, False):
-        idx, d2 = tree.query(dev(torch, Q), sort=sort)
-        assert_nn_equal(idx, d2, oi, od, f"m={m} sort={sort}")
+        for lanes in (1, 4, 16):
+            idx, d2 = tree.query(dev(torch, Q), sort=sort, lanes=lanes)
+            assert_nn_equal(idx, d2, oi, od, f"m={m} sort={sort} lanes={lanes}")
 
 
 def test_nonfinite_and_empty(torch, kdnn):
@@ -137,8 +140,9 @@ def test_nonfinite_and_empty(torch, kdnn):
     assert oi[3] == -1 and oi[7] == -1 and oi[20] == -1
     tree = kdnn.Tree(T, 8)
     for sort in (True, False):
-        idx, d2 = tree.query(dev(torch, Q), sort=sort)
-        assert_nn_equal(idx, d2, oi, od, "nonfinite")
+        for lanes in (1, 4, 16):
+            idx, d2 = tree.query(dev(torch, Q), sort=sort, lanes=lanes)
+            assert_nn_equal(idx, d2, oi, od, f"nonfinite lanes={lanes}")
     idx, d2 = tree.query(torch.empty((0, 3), dtype=torch.float32, device="cuda"))
     assert idx.numel() == 0 and d2.numel() == 0
 
@@ -159,9 +163,10 @@ def test_depth_cap_and_round_robin(torch, kdnn):
     Q = rng.random((2000, 3)).astype(np.float32)
     oi, od = oracle.brute_nn(T, Q)
     for kw in ({"max_depth": 4}, {"round_robin": True}, {"max_depth": 6, "round_robin": True}):
-        say("build variant", kw)
-        idx, d2 = kdnn.Tree(T, 8, **kw).query(dev(torch, Q))
-        assert_nn_equal(idx, d2, oi, od, str(kw))
+        for lanes in (1, 4, 16):
+            say("build variant", kw, "lanes", lanes)
+            idx, d2 = kdnn.Tree(T, 8, **kw).query(dev(torch, Q), lanes=lanes)
+            assert_nn_equal(idx, d2, oi, od, f"{kw} lanes={lanes}")
 
 
 def test_query_stats_consistent(torch, kdnn):
@@ -170,11 +175,12 @@ def test_query_stats_consistent(torch, kdnn):
     tree = kdnn.Tree(p.target, 8)
     q = dev(torch, p.source)
     idx, d2 = tree.query(q)
-    si, sd, cn, cp = tree.query_stats(q)
-    assert torch.equal(idx, si) and torch.equal(d2.view(torch.int32), sd.view(torch.int32))
     D = tree.info["depth"]
-    assert int(cn.min()) >= D + 1 and int(cp.min()) >= 1
-    assert float(cn.float().mean()) < 0.25 * 2 ** (D + 1)
+    for lanes in (1, 4, 16):
+        si, sd, cn, cp = tree.query_stats(q, lanes=lanes)
+        assert torch.equal(idx, si) and torch.equal(d2.view(torch.int32), sd.view(torch.int32))
+        assert int(cn.min()) >= D + 1 and int(cp.min()) >= 1
+        assert float(cn.float().mean()) < 0.25 * 2 ** (D + 1)
 
 
 # ================================================================ transform
@@ -244,9 +250,10 @@ def test_scene_nn_full(torch, kdnn):
                     ("converged queries", oracle.transform(p.source, o["R"], o["t"]))]:
         oi, od = otree.query(Q)
         for sort in (True, False):
-            say("scene nn", name, "sort", sort)
-            idx, d2 = tree.query(dev(torch, Q), sort=sort)
-            assert_nn_equal(idx, d2, oi, od, f"scene {name} sort={sort}")
+            for lanes in (1, 4, 16):
+                say("scene nn", name, "sort", sort, "lanes", lanes)
+                idx, d2 = tree.query(dev(torch, Q), sort=sort, lanes=lanes)
+                assert_nn_equal(idx, d2, oi, od, f"scene {name} sort={sort} lanes={lanes}")
 
 
 def test_scene_correspond_reduce(torch, kdnn):
@@ -270,14 +277,15 @@ def test_scene_icp_align(torch, kdnn):
     p = scene()
     _, o = scene_oracle_icp()
     tree = kdnn.Tree(p.target, 16)
-    say("scene icp_align 30")
-    g = tree.icp(dev(torch, p.source), max_iter=p.iters)
-    assert g["iters"] == p.iters
-    dR = np.linalg.norm(g["R"] - o["R"])
-    dt = np.max(np.abs(g["t"] - o["t"]))
-    assert dR <= R_TOL and dt <= T_TOL, (dR, dt)
-    np.testing.assert_allclose(g["E"], o["E"], rtol=1e-6)
-    np.testing.assert_allclose(g["Rt_hist"], o["Rt_hist"], atol=1e-6)
+    for lanes in (None, 1, 4, 16):
+        say("scene icp_align 30 lanes", lanes)
+        g = tree.icp(dev(torch, p.source), max_iter=p.iters, lanes=lanes)
+        assert g["iters"] == p.iters
+        dR = np.linalg.norm(g["R"] - o["R"])
+        dt = np.max(np.abs(g["t"] - o["t"]))
+        assert dR <= R_TOL and dt <= T_TOL, (lanes, dR, dt)
+        np.testing.assert_allclose(g["E"], o["E"], rtol=1e-6)
+        np.testing.assert_allclose(g["Rt_hist"], o["Rt_hist"], atol=1e-6)
 
 
 def test_determinism(torch, kdnn):
@@ -321,24 +329,36 @@ def test_workspace_checks(torch, kdnn):
         tree.query(src, workspace=small)
 
 
-@pytest.mark.parametrize("leaf", [8, 16])
-def test_stress_nn(torch, kdnn, leaf):
+@functools.lru_cache(maxsize=None)
+def stress_oracle():
     p = synth.stress()
-    say("stress 1M x 1M leaf", leaf)
-    oi, od = oracle.KDTree(p.target, 8).query(p.source)
+    return p, oracle.KDTree(p.target, 8).query(p.source)
+
+
+@pytest.mark.parametrize("lanes", [None, 4])
+@pytest.mark.parametrize("leaf", [8, 16])
+def test_stress_nn(torch, kdnn, leaf, lanes):
+    p, (oi, od) = stress_oracle()
+    say("stress 1M x 1M leaf", leaf, "lanes", lanes)
     tree = kdnn.Tree(p.target, leaf)
     assert tree.info["depth"] == (17 if leaf == 8 else 16)
-    idx, d2 = tree.query(dev(torch, p.source))
-    assert_nn_equal(idx, d2, oi, od, f"stress leaf {leaf}")
+    idx, d2 = tree.query(dev(torch, p.source), lanes=lanes)
+    assert_nn_equal(idx, d2, oi, od, f"stress leaf {leaf} lanes {lanes}")
 
 
-@pytest.mark.parametrize("leaf", [8, 16])
-def test_skewed_nn(torch, kdnn, leaf):
+@functools.lru_cache(maxsize=None)
+def skewed_oracle():
     p = synth.skewed()
-    say("skewed 500k leaf", leaf)
-    oi, od = oracle.KDTree(p.target, 8).query(p.source)
-    idx, d2 = kdnn.Tree(p.target, leaf).query(dev(torch, p.source))
-    assert_nn_equal(idx, d2, oi, od, f"skewed leaf {leaf}")
+    return p, oracle.KDTree(p.target, 8).query(p.source)
+
+
+@pytest.mark.parametrize("lanes", [None, 1, 16])
+@pytest.mark.parametrize("leaf", [8, 16])
+def test_skewed_nn(torch, kdnn, leaf, lanes):
+    p, (oi, od) = skewed_oracle()
+    say("skewed 500k leaf", leaf, "lanes", lanes)
+    idx, d2 = kdnn.Tree(p.target, leaf).query(dev(torch, p.source), lanes=lanes)
+    assert_nn_equal(idx, d2, oi, od, f"skewed leaf {leaf} lanes {lanes}")
 
 
 def test_lidar_pairs(torch, kdnn):
