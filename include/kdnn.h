@@ -156,12 +156,18 @@ kdnn_status kdtree_build_host(const float *xyz_host, int64_t n, const kdnn_build
 /* Query flags. */
 #define KDNN_QUERY_NO_SORT 1u /* traverse in the given order (skip the Morton ordering) */
 
-/* Lanes cooperating on one query (nn_query, nn_query_stats and the ICP entry
- * points): KDNN_LANES(g) with g in {1, 2, 4, 8, 16}; without it the library
- * picks g from the number of queries.  Results do not depend on g. */
+/* Search schedule (nn_query, nn_query_stats and the ICP entry points).
+ * Default: one lane per query, one pass.  KDNN_LANES(g), g in {1, 2, 4, 8,
+ * 16}: g lanes cooperate on each query.  KDNN_BUDGET(b), b in 1..255 (without
+ * KDNN_LANES): two passes -- one lane per query with a budget of b node
+ * visits, then groups of 16 lanes complete the queries left, starting from
+ * the first pass's best.  Results never depend on the schedule. */
 #define KDNN_LANES_SHIFT 8
 #define KDNN_LANES_MASK (0x1fu << KDNN_LANES_SHIFT)
 #define KDNN_LANES(g) ((uint32_t)(g) << KDNN_LANES_SHIFT)
+#define KDNN_BUDGET_SHIFT 16
+#define KDNN_BUDGET_MASK (0xffu << KDNN_BUDGET_SHIFT)
+#define KDNN_BUDGET(b) ((uint32_t)(b) << KDNN_BUDGET_SHIFT)
 
 /* Bytes of device workspace nn_query needs for m queries (Morton keys,
  * permutation, radix-sort histograms). 0 for m <= 0. */

@@ -132,10 +132,12 @@ class Tree:
         return torch.empty(int(_lib.lib().nn_query_workspace_bytes(m)), dtype=torch.uint8,
                            device=self.device)
 
-    def query(self, q, sort: bool = True, out=None, workspace=None, stream=None, lanes=None):
+    def query(self, q, sort: bool = True, out=None, workspace=None, stream=None, lanes=None,
+              budget=None):
         """(idx int32[m], dist2 float32[m]) of the exact nearest target point.
 
-        lanes: lanes cooperating on each query (1, 2, 4, 8, 16; None = automatic).
+        lanes: single pass with this many lanes per query (1, 2, 4, 8, 16);
+        None = the default two-pass schedule (budget: its first-pass node budget).
         """
         torch = _torch()
         q = _dev_points(q, "queries")
@@ -148,11 +150,11 @@ class Tree:
             ws = workspace if workspace is not None else self.query_workspace(m)
         _lib.check(_lib.lib().nn_query(
             self._h, _ptr(q), m, _ptr(idx), _ptr(d2),
-            (0 if sort else KDNN_QUERY_NO_SORT) | _lib.lanes_flag(lanes),
+            (0 if sort else KDNN_QUERY_NO_SORT) | _lib.lanes_flag(lanes, budget),
             _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)), "nn_query")
         return idx, d2
 
-    def query_stats(self, q, sort: bool = True, lanes=None):
+    def query_stats(self, q, sort: bool = True, lanes=None, budget=None):
         """query() plus per-query counts of nodes loaded and leaf points scanned."""
         torch = _torch()
         q = _dev_points(q, "queries")
@@ -164,7 +166,7 @@ class Tree:
         ws = self.query_workspace(m) if sort and m > 0 else None
         _lib.check(_lib.lib().nn_query_stats(
             self._h, _ptr(q), m, _ptr(idx), _ptr(d2), _ptr(cn), _ptr(cp),
-            (0 if sort else KDNN_QUERY_NO_SORT) | _lib.lanes_flag(lanes), _ptr(ws),
+            (0 if sort else KDNN_QUERY_NO_SORT) | _lib.lanes_flag(lanes, budget), _ptr(ws),
             ws.numel() if ws is not None else 0, _stream()), "nn_query_stats")
         return idx, d2, cn, cp
 
@@ -211,7 +213,7 @@ class Tree:
             "icp_correspond_reduce_async")
 
     def icp(self, src, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
-            workspace=None, stream=None, lanes=None, sort: bool = True) -> dict:
+            workspace=None, stream=None, lanes=None, sort: bool = True, budget=None) -> dict:
         """ICP registration of the source (device, original coordinates) onto the tree."""
         src = _dev_points(src, "src")
         n = src.shape[0]
@@ -228,7 +230,7 @@ class Tree:
             R0a[1] if R0a else None, t0a[1] if t0a else None, int(max_iter), float(eps),
             R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
             E.ctypes.data_as(_lib.c_dp), Rt.ctypes.data_as(_lib.c_dp), ctypes.byref(it),
-            (0 if sort else KDNN_ICP_NO_SORT) | _lib.lanes_flag(lanes),
+            (0 if sort else KDNN_ICP_NO_SORT) | _lib.lanes_flag(lanes, budget),
             _ptr(ws), ws.numel(), _stream(stream)), "icp_align")
         k = it.value
         return {"R": R.reshape(3, 3), "t": t, "E": E[:k], "Rt_hist": Rt[:k], "iters": k}

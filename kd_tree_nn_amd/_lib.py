@@ -19,9 +19,13 @@ KDNN_SUMS_DOUBLES = 17
 KDNN_LANES_SHIFT = 8
 
 
-def lanes_flag(lanes):
-    """KDNN_LANES(g): g lanes cooperate on a query (0 / None = library's choice)."""
-    return (int(lanes or 0) & 0x1f) << KDNN_LANES_SHIFT
+KDNN_BUDGET_SHIFT = 16
+
+
+def lanes_flag(lanes, budget=None):
+    """KDNN_LANES(g) | KDNN_BUDGET(b): single pass with g lanes per query, or
+    (g = None) the default two-pass schedule with first-pass budget b."""
+    return ((int(lanes or 0) & 0x1f) << KDNN_LANES_SHIFT) | ((int(budget or 0) & 0xff) << KDNN_BUDGET_SHIFT)
 
 
 class BuildParams(ctypes.Structure):

@@ -118,7 +118,8 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
     }
     if (e != hipSuccess) return hip_fail(e, "icp: order launch");
     e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2,
-                         int((flags >> KDNN_LANES_SHIFT) & 0x1f), s);
+                         int((flags & KDNN_LANES_MASK) >> KDNN_LANES_SHIFT),
+                         (flags & KDNN_BUDGET_MASK) >> KDNN_BUDGET_SHIFT, s);
     if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
     return KDNN_OK;
 }
@@ -131,7 +132,8 @@ kdnn_status icp_check(const kdnn_tree *tree, const float *src, int64_t n, const 
     kdnn_status st = check_points(src, n, "icp: src");
     if (st != KDNN_OK) return st;
     if (!R || !t) return fail(KDNN_EINVAL, "icp: null R or t");
-    if ((flags & ~(KDNN_ICP_REUSE_ORDER | KDNN_ICP_NO_SORT | KDNN_LANES_MASK)) || !lanes_ok(flags))
+    if ((flags & ~(KDNN_ICP_REUSE_ORDER | KDNN_ICP_NO_SORT | KDNN_LANES_MASK | KDNN_BUDGET_MASK)) ||
+        !lanes_ok(flags))
         return fail(KDNN_EINVAL, "icp: unknown flag or lane count");
     return check_ws(ws, ws_bytes, icp_ws_bytes(n));
 }
@@ -267,7 +269,7 @@ static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t 
     if (m == 0) return KDNN_OK;
     if (!idx || !d2) return fail(KDNN_EINVAL, "nn_query: null output");
     if (!aligned(idx, 4) || !aligned(d2, 4)) return fail(KDNN_EINVAL, "nn_query: misaligned output");
-    if ((flags & ~(KDNN_QUERY_NO_SORT | KDNN_LANES_MASK)) || !lanes_ok(flags))
+    if ((flags & ~(KDNN_QUERY_NO_SORT | KDNN_LANES_MASK | KDNN_BUDGET_MASK)) || !lanes_ok(flags))
         return fail(KDNN_EINVAL, "nn_query: unknown flag or lane count");
     const int32_t *perm = nullptr;
     if (!(flags & KDNN_QUERY_NO_SORT)) {
@@ -278,7 +280,8 @@ static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t 
         if (e != hipSuccess) return hip_fail(e, "nn_query: order launch");
     }
     hipError_t e = launch_nn(tree->dev, q, m, perm, idx, d2, cn, cp, stats,
-                             int((flags >> KDNN_LANES_SHIFT) & 0x1f), s);
+                             int((flags & KDNN_LANES_MASK) >> KDNN_LANES_SHIFT),
+                             (flags & KDNN_BUDGET_MASK) >> KDNN_BUDGET_SHIFT, s);
     if (e != hipSuccess) return hip_fail(e, "nn_query: launch");
     return KDNN_OK;
 }
@@ -394,7 +397,7 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     if (!R_out || !t_out) return fail(KDNN_EINVAL, "icp_align: null R_out or t_out");
     if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align: max_iter < 0");
     if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align: eps must be >= 0");
-    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_LANES_MASK))
+    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_LANES_MASK | KDNN_BUDGET_MASK))
         return fail(KDNN_EINVAL, "icp_align: unknown flag");
     kdnn_status st = icp_check(tree, src_dev, n, R, t, flags, ws_dev, ws_bytes);
     if (st != KDNN_OK) return st;

@@ -79,6 +79,10 @@ SortWorkspace carve_sort_workspace(void *ws, int64_t m);
 struct IcpWorkspace {
     SortWorkspace sort;
     double *partials;   // KDNN_SUMS_DOUBLES * max_blocks
+    double *partials2;  // KDNN_SUMS_DOUBLES * pass-2 blocks
+    uint32_t *state;    // [n] per traversal slot
+    uint64_t *pkey;     // [n]
+    uint32_t *pslot;    // [n]
     double *sums;       // KDNN_SUMS_DOUBLES
     uint32_t *ticket;   // 1 counter, must be 0 between launches
     int32_t max_blocks;
@@ -94,17 +98,17 @@ hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m,
 // Same, for the ICP entry points: also clears the workspace's ticket counter.
 hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                             const IcpWorkspace &ws, const int32_t **perm, hipStream_t s);
-// lanes: lanes per query (1, 2, 4, 8, 16); anything else = automatic.
-int lanes_for(int64_t m, int lanes);
+// lanes: lanes per query for a single-pass search (1, 2, 4, 8, 16); 0 = the
+// default two-pass search (budgeted single lane, then cooperative groups).
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     int lanes, hipStream_t s);
+                     int lanes, uint32_t budget, hipStream_t s);
 hipError_t launch_transform(const float *in, float *out, int64_t n, const double *R,
                             const double *t, hipStream_t s);
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, int lanes,
-                            hipStream_t s);
+                            uint32_t budget, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace kdnn

@@ -181,49 +181,57 @@ __device__ __forceinline__ void rank_points(const float4 (&p)[C], const int32_t 
     }
 }
 
+// Single-lane search.  Stops after `budget` node records when the budget is
+// below kNoBudget; returns whether the search completed.  key/slot hold the
+// best candidate seen so far either way (a valid upper bound to resume from).
+constexpr uint32_t kNoBudget = 0xFFFFFFFFu;
+
 template <bool STATS>
-__device__ __forceinline__ void nn_search(const TreeView &t, float qx, float qy, float qz, Best &b,
+__device__ __forceinline__ bool nn_search(const TreeView &t, float qx, float qy, float qz,
+                                          uint32_t budget, uint64_t &key, uint32_t &slot,
                                           uint32_t &cn, uint32_t &cp)
 {
-    uint64_t key = kNoKey;
-    uint32_t slot = 0;
-    if (isfinite(qx) && isfinite(qy) && isfinite(qz)) {
-        uint32_t i = 1, far = 0;
-        for (;;) {
-            // Phase 1: internal nodes, until a leaf or the end of the search.
-            while (i < t.first_leaf) {
-                const float4 A = t.nodes[2 * i];
-                const float4 B = t.nodes[2 * i + 1];
-                if (STATS) ++cn;
-                const bool in = enters(box_lb(qx, qy, qz, A, B), key_dist(key));
-                const uint32_t child = near_child(i, B, qx, qy, qz);
-                uint32_t f2 = far;
-                const uint32_t nx = next_subtree(i, f2, ~0u);
-                i = in ? child : nx;
-                far = in ? far : f2;
-            }
-            if (i == kDone) break;
-            // Phase 2: leaf i -- its record and first points in flight together.
-            int32_t begin, last, end;
-            leaf_range(t, i, begin, last, end);
+    key = kNoKey;
+    slot = 0;
+    if (!(isfinite(qx) && isfinite(qy) && isfinite(qz))) return true;
+    uint32_t i = 1, far = 0, steps = 0;
+    for (;;) {
+        // Phase 1: internal nodes, until a leaf or the end of the search.
+        while (i < t.first_leaf) {
+            if (steps >= budget) return false;
             const float4 A = t.nodes[2 * i];
             const float4 B = t.nodes[2 * i + 1];
-            float4 p[kLeafChunk];
-            int32_t sl[kLeafChunk];
-            load_points<kLeafChunk, 1>(t, begin, last, p, sl);
+            ++steps;
             if (STATS) ++cn;
-            if (enters(box_lb(qx, qy, qz, A, B), key_dist(key))) {
-                rank_points<kLeafChunk>(p, sl, qx, qy, qz, key, slot);
-                for (int32_t k0 = begin + kLeafChunk; k0 < end; k0 += kLeafChunk) {
-                    load_points<kLeafChunk, 1>(t, k0, last, p, sl);
-                    rank_points<kLeafChunk>(p, sl, qx, qy, qz, key, slot);
-                }
-                if (STATS) cp += uint32_t(end - begin);
-            }
-            i = next_subtree(i, far, ~0u);
+            const bool in = enters(box_lb(qx, qy, qz, A, B), key_dist(key));
+            const uint32_t child = near_child(i, B, qx, qy, qz);
+            uint32_t f2 = far;
+            const uint32_t nx = next_subtree(i, f2, ~0u);
+            i = in ? child : nx;
+            far = in ? far : f2;
         }
+        if (i == kDone) return true;
+        if (steps >= budget) return false;
+        // Phase 2: leaf i -- its record and first points in flight together.
+        int32_t begin, last, end;
+        leaf_range(t, i, begin, last, end);
+        const float4 A = t.nodes[2 * i];
+        const float4 B = t.nodes[2 * i + 1];
+        float4 p[kLeafChunk];
+        int32_t sl[kLeafChunk];
+        load_points<kLeafChunk, 1>(t, begin, last, p, sl);
+        ++steps;
+        if (STATS) ++cn;
+        if (enters(box_lb(qx, qy, qz, A, B), key_dist(key))) {
+            rank_points<kLeafChunk>(p, sl, qx, qy, qz, key, slot);
+            for (int32_t k0 = begin + kLeafChunk; k0 < end; k0 += kLeafChunk) {
+                load_points<kLeafChunk, 1>(t, k0, last, p, sl);
+                rank_points<kLeafChunk>(p, sl, qx, qy, qz, key, slot);
+            }
+            if (STATS) cp += uint32_t(end - begin);
+        }
+        i = next_subtree(i, far, ~0u);
     }
-    finish(key, slot, b);
 }
 
 // ------------------------------------------------ cooperative (G-lane) search
@@ -272,9 +280,12 @@ __device__ __forceinline__ uint32_t group_sum_u32(uint32_t v)
     return v;
 }
 
+// `key`/`slot` come in as an upper bound (kNoKey: none) and go out as the
+// group's answer; with `resume` the query's own leaf is known to be scanned.
 template <int G, bool STATS>
 __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, float qy, float qz,
-                                                Best &b, uint32_t &cn, uint32_t &cp)
+                                                bool resume, uint64_t &key, uint32_t &slot,
+                                                uint32_t &cn, uint32_t &cp)
 {
     constexpr int LOG_G = G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : G == 16 ? 4 : 5;
     constexpr int SLOTS = (kDevMaxDepth + G - 1) / G;
@@ -285,9 +296,6 @@ __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, flo
     const int gbase = lane & ~(G - 1);
     const uint64_t gmask = (G == 64 ? ~uint64_t(0) : ((uint64_t(1) << G) - 1)) << gbase;
     const int D = t.depth;
-
-    uint64_t key = kNoKey;
-    uint32_t slot = 0;
 
     // 1. greedy descent, plane distances kept round-robin over the group
     uint32_t i = 1;
@@ -308,8 +316,10 @@ __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, flo
     }
     if (STATS && gl == 0) cn += uint32_t(D);
 
-    // 2. the query's own leaf, scanned by the whole group
-    {
+    // 2. the query's own leaf, scanned by the whole group (a resumed search
+    //    has scanned it already when it holds any candidate: a first pass
+    //    always reaches the greedy leaf first)
+    if (!resume || key == kNoKey) {
         int32_t begin, last, end;
         leaf_range(t, i, begin, last, end);
         for (int32_t k0 = begin; k0 < end; k0 += G * C) {
@@ -379,7 +389,8 @@ __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, flo
     // 5. the group's answer and the winning lane's slot
     const uint64_t wm = __ballot(key == gkey) & gmask;
     const int win = __ffsll((unsigned long long)wm) - 1;
-    finish(gkey, uint32_t(__shfl(int(slot), win, 64)), b);
+    slot = uint32_t(__shfl(int(slot), win, 64));
+    key = gkey;
     if (STATS) {
         cn = group_sum_u32<G>(cn);
         cp = group_sum_u32<G>(cp);
@@ -388,6 +399,7 @@ __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, flo
 
 struct NnArgs {
     TreeView tree;
+    uint32_t budget;  // pass-1 node budget (two-pass mode)
     const float *q;
     int64_t m;
     const int32_t *perm;
@@ -401,15 +413,13 @@ template <int G, bool STATS>
 __device__ __forceinline__ void search_query(const TreeView &t, float qx, float qy, float qz,
                                              Best &b, uint32_t &cn, uint32_t &cp)
 {
-    if (G == 1) {
-        nn_search<STATS>(t, qx, qy, qz, b, cn, cp);
-    } else if (isfinite(qx) && isfinite(qy) && isfinite(qz)) {
-        nn_search_group<G, STATS>(t, qx, qy, qz, b, cn, cp);
-    } else {
-        b.d = INFINITY;
-        b.idx = -1;
-        b.slot = 0;
-    }
+    uint64_t key = kNoKey;
+    uint32_t slot = 0;
+    if (G == 1)
+        nn_search<STATS>(t, qx, qy, qz, kNoBudget, key, slot, cn, cp);
+    else if (isfinite(qx) && isfinite(qy) && isfinite(qz))
+        nn_search_group<G, STATS>(t, qx, qy, qz, false, key, slot, cn, cp);
+    finish(key, slot, b);
 }
 
 // G lanes per query; a block handles kWG / G queries per sweep.  The loop
@@ -441,6 +451,73 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
     }
 }
 
+// ------------------------------------------------- two-pass search (default)
+//
+// Pass 1 gives every query one lane and a budget of kPass1Budget node
+// records; most queries finish, and a wave lasts at most about that many
+// steps.  Pass 2 sweeps all query slots with persistent groups of
+// kPass2Lanes lanes in a fixed order, skips the finished ones and completes
+// the others with the cooperative search, starting from pass 1's best.
+// nn_query keeps an unfinished query's state in its own outputs:
+// idx = -(best index + 3) (so <= -2) and dist2 = best distance so far.
+#ifndef KDNN_PASS1_BUDGET
+#define KDNN_PASS1_BUDGET 64
+#endif
+constexpr uint32_t kPass1Budget = KDNN_PASS1_BUDGET;
+constexpr int kPass2Lanes = 16;
+constexpr int kPass2MaxBlocks = 1024;
+
+template <bool STATS>
+__global__ __launch_bounds__(kWG) void nn_pass1_kernel(NnArgs a)
+{
+    const uint32_t nb = gridDim.x;
+    const uint32_t blk = xcd_remap(blockIdx.x, nb);
+    for (int64_t k = int64_t(blk) * kWG + threadIdx.x; k < a.m; k += int64_t(nb) * kWG) {
+        const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+        uint64_t key;
+        uint32_t slot, cn = 0, cp = 0;
+        const bool done = nn_search<STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2],
+                                           a.budget, key, slot, cn, cp);
+        Best b;
+        finish(key, slot, b);
+        a.idx[i] = done ? b.idx : -(int32_t(uint32_t(key)) + 3);
+        a.d2[i] = done ? b.d : key_dist(key);
+        if (STATS) {
+            if (a.cnt_nodes) a.cnt_nodes[i] = cn;
+            if (a.cnt_pts) a.cnt_pts[i] = cp;
+        }
+    }
+}
+
+template <bool STATS>
+__global__ __launch_bounds__(kWG) void nn_pass2_kernel(NnArgs a)
+{
+    constexpr int G = kPass2Lanes, QPB = kWG / G;
+    const uint32_t nb = gridDim.x;
+    const int gl = threadIdx.x & (G - 1);
+    for (int64_t base = int64_t(blockIdx.x) * QPB; base < a.m; base += int64_t(nb) * QPB) {
+        const int64_t k = base + threadIdx.x / G;
+        if (k >= a.m) continue;
+        const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+        const int32_t e = a.idx[i];
+        if (e > -2) continue;  // finished in pass 1 (the same for the whole group)
+        uint64_t key = nn_key(a.d2[i], uint32_t(-e - 3));
+        uint32_t slot = 0, cn = 0, cp = 0;
+        nn_search_group<G, STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2], true, key,
+                                  slot, cn, cp);
+        if (gl == 0) {
+            Best b;
+            finish(key, slot, b);
+            a.idx[i] = b.idx;
+            a.d2[i] = b.d;
+            if (STATS) {
+                if (a.cnt_nodes) a.cnt_nodes[i] += cn;
+                if (a.cnt_pts) a.cnt_pts[i] += cp;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------ fused ICP kernel
 //
 // Per source point: q = fl32(R s + t) evaluated in fp64 with a fixed
@@ -458,9 +535,15 @@ struct IcpArgs {
     double R[9];
     double t[3];
     double c[3];
-    double *partials;  // [kS][nb], component-major
+    double *partials;   // [kS][nb] of the kernel that reduces (single pass / pass 1)
+    double *partials2;  // [kS][nb2] of pass 2
+    int32_t nb1;        // pass-1 block count (two-pass mode)
     uint32_t *ticket;
-    double *sums;      // [kS]
+    double *sums;       // [kS]
+    uint32_t budget;    // pass-1 node budget
+    uint32_t *state;    // [n] by traversal slot: 1 = left for pass 2
+    uint64_t *pkey;     // [n] pass-1 best key of unfinished slots
+    uint32_t *pslot;    // [n] pass-1 best point slot of unfinished slots
     int32_t *idx;
     float *d2;
 };
@@ -472,8 +555,8 @@ __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, doub
 }
 
 // Sum acc[] over the work-group; thread c < kS of wave 0 gets component c
-// in *out (fixed order: lanes by xor butterfly, then waves 0..3).
-__device__ __forceinline__ void block_sum(double (&acc)[kS], double *red /* LDS [4][kS] */,
+// in *out (fixed order: lanes by xor butterfly, then waves in order).
+__device__ __forceinline__ void block_sum(double (&acc)[kS], double *red /* LDS [waves][kS] */,
                                           double *out, int64_t out_stride)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -496,65 +579,151 @@ __device__ __forceinline__ void block_sum(double (&acc)[kS], double *red /* LDS 
     }
 }
 
+// The query of source point i: q = fl32(R s + t), fp64 with a fixed association.
+__device__ __forceinline__ void icp_query(const IcpArgs &a, int64_t i, double &X, double &Y,
+                                          double &Z, float &qx, float &qy, float &qz)
+{
+    X = a.src[3 * i];
+    Y = a.src[3 * i + 1];
+    Z = a.src[3 * i + 2];
+    qx = rigid_row(a.R[0], a.R[1], a.R[2], a.t[0], X, Y, Z);
+    qy = rigid_row(a.R[3], a.R[4], a.R[5], a.t[1], X, Y, Z);
+    qz = rigid_row(a.R[6], a.R[7], a.R[8], a.t[2], X, Y, Z);
+}
+
+// Record a finished pair: optional per-point outputs, then the fp64 sums
+// (s - c), (m - c), (s - c)(m - c)^T, d2, 1.
+__device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, double X, double Y,
+                                               double Z, const Best &b, double (&acc)[kS])
+{
+    if (a.idx) a.idx[i] = b.idx;
+    if (a.d2) a.d2[i] = b.d;
+    if (b.idx < 0) return;
+    const float4 mp = a.tree.pts[b.slot];
+    const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
+    const double m0 = double(mp.x) - a.c[0], m1 = double(mp.y) - a.c[1],
+                 m2 = double(mp.z) - a.c[2];
+    acc[0] += s0; acc[1] += s1; acc[2] += s2;
+    acc[3] += m0; acc[4] += m1; acc[5] += m2;
+    acc[6] += s0 * m0; acc[7] += s0 * m1; acc[8] += s0 * m2;
+    acc[9] += s1 * m0; acc[10] += s1 * m1; acc[11] += s1 * m2;
+    acc[12] += s2 * m0; acc[13] += s2 * m1; acc[14] += s2 * m2;
+    acc[15] += double(b.d);
+    acc[16] += 1.0;
+}
+
+// After this group's partials are written: the last group to finish sums
+// p1[kS][n1] and then p2[kS][n2] in a fixed order into a.sums.
+__device__ __forceinline__ void icp_final_reduce(const IcpArgs &a, double (&acc)[kS], double *red,
+                                                 const double *p1, int32_t n1, const double *p2,
+                                                 int32_t n2)
+{
+    __shared__ uint32_t is_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    for (int32_t g = threadIdx.x; g < n1 + n2; g += kWG) {
+#pragma unroll
+        for (int c = 0; c < kS; ++c)
+            acc[c] += g < n1 ? p1[int64_t(c) * n1 + g] : p2[int64_t(c) * n2 + (g - n1)];
+    }
+    __syncthreads();  // red[] is reused
+    block_sum(acc, red, a.sums, 1);
+    if (threadIdx.x == 0) atomicExch(a.ticket, 0u);
+}
+
+// Single pass: G lanes per point, one kernel does everything.
 template <int G>
 __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
 {
     constexpr int QPB = kWG / G;
     const int gl = threadIdx.x & (G - 1);
     __shared__ double red[(kWG / 64) * kS];
-    __shared__ uint32_t is_last;
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
-
     const uint32_t nb = gridDim.x;
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
     for (int64_t base = int64_t(blk) * QPB; base < a.n; base += int64_t(nb) * QPB) {
         const int64_t k = base + threadIdx.x / G;
         if (k >= a.n) continue;
         const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
-        const double X = a.src[3 * i], Y = a.src[3 * i + 1], Z = a.src[3 * i + 2];
-        const float qx = rigid_row(a.R[0], a.R[1], a.R[2], a.t[0], X, Y, Z);
-        const float qy = rigid_row(a.R[3], a.R[4], a.R[5], a.t[1], X, Y, Z);
-        const float qz = rigid_row(a.R[6], a.R[7], a.R[8], a.t[2], X, Y, Z);
+        double X, Y, Z;
+        float qx, qy, qz;
+        icp_query(a, i, X, Y, Z, qx, qy, qz);
         Best b;
         uint32_t cn = 0, cp = 0;
         search_query<G, false>(a.tree, qx, qy, qz, b, cn, cp);
-        if (gl != 0) continue;
-        if (a.idx) a.idx[i] = b.idx;
-        if (a.d2) a.d2[i] = b.d;
-        if (b.idx >= 0) {
-            const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
-            const float4 mp = a.tree.pts[b.slot];
-            const double m0 = double(mp.x) - a.c[0], m1 = double(mp.y) - a.c[1],
-                         m2 = double(mp.z) - a.c[2];
-            acc[0] += s0; acc[1] += s1; acc[2] += s2;
-            acc[3] += m0; acc[4] += m1; acc[5] += m2;
-            acc[6] += s0 * m0; acc[7] += s0 * m1; acc[8] += s0 * m2;
-            acc[9] += s1 * m0; acc[10] += s1 * m1; acc[11] += s1 * m2;
-            acc[12] += s2 * m0; acc[13] += s2 * m1; acc[14] += s2 * m2;
-            acc[15] += double(b.d);
-            acc[16] += 1.0;
+        if (gl == 0) icp_accumulate(a, i, X, Y, Z, b, acc);
+    }
+    block_sum(acc, red, a.partials + blockIdx.x, nb);
+    icp_final_reduce(a, acc, red, a.partials, int32_t(nb), nullptr, 0);
+}
+
+// Two-pass mode, pass 1: one lane per point with a step budget.
+__global__ __launch_bounds__(kWG) void icp_pass1_kernel(IcpArgs a)
+{
+    __shared__ double red[(kWG / 64) * kS];
+    double acc[kS];
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    const uint32_t nb = gridDim.x;
+    const uint32_t blk = xcd_remap(blockIdx.x, nb);
+    for (int64_t k = int64_t(blk) * kWG + threadIdx.x; k < a.n; k += int64_t(nb) * kWG) {
+        const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+        double X, Y, Z;
+        float qx, qy, qz;
+        icp_query(a, i, X, Y, Z, qx, qy, qz);
+        uint64_t key;
+        uint32_t slot, cn = 0, cp = 0;
+        const bool done = nn_search<false>(a.tree, qx, qy, qz, a.budget, key, slot, cn, cp);
+        a.state[k] = done ? 0u : 1u;
+        if (done) {
+            Best b;
+            finish(key, slot, b);
+            icp_accumulate(a, i, X, Y, Z, b, acc);
+        } else {
+            a.pkey[k] = key;
+            a.pslot[k] = slot;
         }
     }
     block_sum(acc, red, a.partials + blockIdx.x, nb);
+}
 
-    // Publish this group's partials, then take a ticket; the last group reduces.
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) is_last = (atomicAdd(a.ticket, 1u) == nb - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
+// Two-pass mode, pass 2: groups of kPass2Lanes finish the points pass 1 left,
+// then the last group reduces both passes' partials.
+__global__ __launch_bounds__(kWG) void icp_pass2_kernel(IcpArgs a)
+{
+    constexpr int G = kPass2Lanes, QPB = kWG / G;
+    const int gl = threadIdx.x & (G - 1);
+    __shared__ double red[(kWG / 64) * kS];
+    double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
-    for (uint32_t g = threadIdx.x; g < nb; g += kWG) {
-#pragma unroll
-        for (int c = 0; c < kS; ++c) acc[c] += a.partials[int64_t(c) * nb + g];
+    const uint32_t nb = gridDim.x;
+    for (int64_t base = int64_t(blockIdx.x) * QPB; base < a.n; base += int64_t(nb) * QPB) {
+        const int64_t k = base + threadIdx.x / G;
+        if (k >= a.n || a.state[k] == 0u) continue;  // uniform over the group
+        const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+        double X, Y, Z;
+        float qx, qy, qz;
+        icp_query(a, i, X, Y, Z, qx, qy, qz);
+        uint64_t key = a.pkey[k];
+        uint32_t slot = a.pslot[k], cn = 0, cp = 0;
+        nn_search_group<G, false>(a.tree, qx, qy, qz, true, key, slot, cn, cp);
+        if (gl == 0) {
+            Best b;
+            finish(key, slot, b);
+            icp_accumulate(a, i, X, Y, Z, b, acc);
+        }
     }
-    __syncthreads();  // red[] is reused
-    block_sum(acc, red, a.sums, 1);
-    if (threadIdx.x == 0) atomicExch(a.ticket, 0u);
+    block_sum(acc, red, a.partials2 + blockIdx.x, nb);
+    icp_final_reduce(a, acc, red, a.partials, a.nb1, a.partials2, int32_t(nb));
 }
 
 // --------------------------------------------------------------- transform
@@ -808,8 +977,10 @@ static int32_t icp_blocks(int64_t n, int G)
 size_t icp_ws_bytes(int64_t n)
 {
     if (n <= 0) return 0;
+    const size_t nn = size_t(n);
     return sort_workspace_bytes(n) + align256(size_t(kS) * kIcpMaxBlocks * 8) +
-           align256(size_t(kS) * 8) + 256;
+           align256(size_t(kS) * kPass2MaxBlocks * 8) + align256(size_t(kS) * 8) + 256 +
+           align256(nn * 4) * 2 + align256(nn * 8);
 }
 
 IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
@@ -820,9 +991,17 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
     p += sort_workspace_bytes(n);
     w.partials = reinterpret_cast<double *>(p);
     p += align256(size_t(kS) * kIcpMaxBlocks * 8);
+    w.partials2 = reinterpret_cast<double *>(p);
+    p += align256(size_t(kS) * kPass2MaxBlocks * 8);
     w.sums = reinterpret_cast<double *>(p);
     p += align256(size_t(kS) * 8);
     w.ticket = reinterpret_cast<uint32_t *>(p);
+    p += 256;
+    w.state = reinterpret_cast<uint32_t *>(p);
+    p += align256(size_t(n) * 4);
+    w.pslot = reinterpret_cast<uint32_t *>(p);
+    p += align256(size_t(n) * 4);
+    w.pkey = reinterpret_cast<uint64_t *>(p);
     w.max_blocks = kIcpMaxBlocks;
     return w;
 }
@@ -895,18 +1074,31 @@ static void launch_nn_g(const NnArgs &a, bool stats, hipStream_t s)
         nn_kernel<G, false><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
 }
 
-int lanes_for(int64_t m, int lanes)
+static uint32_t pass2_blocks(int64_t m)
 {
-    if (lanes == 1 || lanes == 2 || lanes == 4 || lanes == 8 || lanes == 16) return lanes;
-    (void)m;
-    return 1;
+    const int64_t b = (m * kPass2Lanes + kWG - 1) / kWG;
+    return uint32_t(b < 1 ? 1 : (b > kPass2MaxBlocks ? kPass2MaxBlocks : b));
+}
+
+static void launch_nn_two_pass(const NnArgs &a, bool stats, hipStream_t s)
+{
+    int64_t blocks = (a.m + kWG - 1) / kWG;
+    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+    if (stats) {
+        nn_pass1_kernel<true><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
+        nn_pass2_kernel<true><<<dim3(pass2_blocks(a.m)), kWG, 0, s>>>(a);
+    } else {
+        nn_pass1_kernel<false><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
+        nn_pass2_kernel<false><<<dim3(pass2_blocks(a.m)), kWG, 0, s>>>(a);
+    }
 }
 
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     int lanes, hipStream_t s)
+                     int lanes, uint32_t budget, hipStream_t s)
 {
     NnArgs a{};
+    a.budget = budget;
     a.tree = tree_view(t);
     a.q = q;
     a.m = m;
@@ -915,12 +1107,16 @@ hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32
     a.d2 = d2;
     a.cnt_nodes = cnt_nodes;
     a.cnt_pts = cnt_pts;
-    switch (lanes_for(m, lanes)) {
-    case 1: launch_nn_g<1>(a, stats, s); break;
-    case 2: launch_nn_g<2>(a, stats, s); break;
-    case 4: launch_nn_g<4>(a, stats, s); break;
-    case 8: launch_nn_g<8>(a, stats, s); break;
-    default: launch_nn_g<16>(a, stats, s); break;
+    if (lanes == 0 && budget != 0) {
+        launch_nn_two_pass(a, stats, s);
+    } else {
+        switch (lanes) {
+        case 2: launch_nn_g<2>(a, stats, s); break;
+        case 4: launch_nn_g<4>(a, stats, s); break;
+        case 8: launch_nn_g<8>(a, stats, s); break;
+        case 16: launch_nn_g<16>(a, stats, s); break;
+        default: launch_nn_g<1>(a, stats, s); break;
+        }
     }
     return hipGetLastError();
 }
@@ -938,9 +1134,11 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
 
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
-                            double *sums_out, int32_t *idx, float *d2, int lanes, hipStream_t s)
+                            double *sums_out, int32_t *idx, float *d2, int lanes, uint32_t budget,
+                            hipStream_t s)
 {
     IcpArgs a{};
+    a.budget = budget;
     a.tree = tree_view(t);
     a.src = src;
     a.n = n;
@@ -951,18 +1149,27 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         a.c[k] = t.center[k];
     }
     a.partials = ws.partials;
+    a.partials2 = ws.partials2;
     a.ticket = ws.ticket;
     a.sums = sums_out;
+    a.state = ws.state;
+    a.pkey = ws.pkey;
+    a.pslot = ws.pslot;
     a.idx = idx;
     a.d2 = d2;
-    const int G = lanes_for(n, lanes);
-    const dim3 grid(uint32_t(icp_blocks(n, G)));
-    switch (G) {
-    case 1: icp_fused_kernel<1><<<grid, kWG, 0, s>>>(a); break;
-    case 2: icp_fused_kernel<2><<<grid, kWG, 0, s>>>(a); break;
-    case 4: icp_fused_kernel<4><<<grid, kWG, 0, s>>>(a); break;
-    case 8: icp_fused_kernel<8><<<grid, kWG, 0, s>>>(a); break;
-    default: icp_fused_kernel<16><<<grid, kWG, 0, s>>>(a); break;
+    if (!(lanes == 0 && budget != 0)) {
+        const dim3 grid(uint32_t(icp_blocks(n, lanes ? lanes : 1)));
+        switch (lanes) {
+        case 2: icp_fused_kernel<2><<<grid, kWG, 0, s>>>(a); break;
+        case 4: icp_fused_kernel<4><<<grid, kWG, 0, s>>>(a); break;
+        case 8: icp_fused_kernel<8><<<grid, kWG, 0, s>>>(a); break;
+        case 16: icp_fused_kernel<16><<<grid, kWG, 0, s>>>(a); break;
+        default: icp_fused_kernel<1><<<grid, kWG, 0, s>>>(a); break;
+        }
+    } else {
+        a.nb1 = icp_blocks(n, 1);
+        icp_pass1_kernel<<<dim3(uint32_t(a.nb1)), kWG, 0, s>>>(a);
+        icp_pass2_kernel<<<dim3(pass2_blocks(n)), kWG, 0, s>>>(a);
     }
     return hipGetLastError();
 }

@@ -21,6 +21,13 @@ from tests._cases import adversarial_clouds, load_nn_cases
 
 pytestmark = pytest.mark.gpu
 
+# search schedules: single pass with g lanes per query, or the default two-pass
+# schedule (tiny budgets push nearly every query into the second pass)
+SCHED = [{}, {"lanes": 4}, {"lanes": 16}, {"budget": 64}, {"budget": 1}, {"budget": 4}]
+SCHED_IDS = ["default", "L4", "L16", "twopass-b64", "twopass-b1", "twopass-b4"]
+SCHED_FEW = [{}, {"budget": 64}, {"budget": 2}]
+SCHED_FEW_IDS = ["default", "twopass-b64", "twopass-b2"]
+
 H_RTOL = 1e-5
 MU_RTOL = 1e-5
 R_TOL = 1e-4
@@ -91,26 +98,27 @@ def lidar():
 
 
 # ======================================================== nearest neighbour
-@pytest.mark.parametrize("lanes", [1, 4, 16])
+@pytest.mark.parametrize("sched", SCHED, ids=SCHED_IDS)
 @pytest.mark.parametrize("sort", [True, False])
 @pytest.mark.parametrize("leaf", [1, 2, 8])
-def test_golden_nn(torch, kdnn, leaf, sort, lanes):
+def test_golden_nn(torch, kdnn, leaf, sort, sched):
     for k, (T, Q, I, D) in enumerate(load_nn_cases()):
-        say("golden", k, "leaf", leaf, "sort", sort, "lanes", lanes)
+        say("golden", k, "leaf", leaf, "sort", sort, sched)
         tree = kdnn.Tree(T, leaf)
-        idx, d2 = tree.query(dev(torch, Q), sort=sort, lanes=lanes)
+        idx, d2 = tree.query(dev(torch, Q), sort=sort, **sched)
         assert_nn_equal(idx, d2, I, D, f"golden set {k}")
 
 
-@pytest.mark.parametrize("lanes", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("sched", SCHED + [{"lanes": 2}, {"lanes": 8}],
+                         ids=SCHED_IDS + ["L2", "L8"])
 @pytest.mark.parametrize("sort", [True, False])
 @pytest.mark.parametrize("leaf", [1, 3, 8, 16])
-def test_adversarial_nn(torch, kdnn, leaf, sort, lanes):
+def test_adversarial_nn(torch, kdnn, leaf, sort, sched):
     for name, T, Q in adversarial_clouds():
-        say("adversarial", name, "leaf", leaf, "sort", sort, "lanes", lanes, len(T), len(Q))
+        say("adversarial", name, "leaf", leaf, "sort", sort, sched, len(T), len(Q))
         oi, od = oracle.brute_nn(T, Q)
-        idx, d2 = kdnn.Tree(T, leaf).query(dev(torch, Q), sort=sort, lanes=lanes)
-        assert_nn_equal(idx, d2, oi, od, f"{name} lanes={lanes}")
+        idx, d2 = kdnn.Tree(T, leaf).query(dev(torch, Q), sort=sort, **sched)
+        assert_nn_equal(idx, d2, oi, od, f"{name} {sched}")
 
 
 @pytest.mark.parametrize("m", [1, 2, 63, 64, 65, 255, 256, 257, 2047, 2048, 2049, 4097, 10007])
@@ -122,9 +130,9 @@ def test_ragged_query_counts(torch, kdnn, m):
     oi, od = oracle.brute_nn(T, Q)
     tree = kdnn.Tree(T, 8)
     for sort in (True, False):
-        for lanes in (1, 4, 16):
-            idx, d2 = tree.query(dev(torch, Q), sort=sort, lanes=lanes)
-            assert_nn_equal(idx, d2, oi, od, f"m={m} sort={sort} lanes={lanes}")
+        for sched in SCHED:
+            idx, d2 = tree.query(dev(torch, Q), sort=sort, **sched)
+            assert_nn_equal(idx, d2, oi, od, f"m={m} sort={sort} {sched}")
 
 
 def test_nonfinite_and_empty(torch, kdnn):
@@ -140,9 +148,9 @@ def test_nonfinite_and_empty(torch, kdnn):
     assert oi[3] == -1 and oi[7] == -1 and oi[20] == -1
     tree = kdnn.Tree(T, 8)
     for sort in (True, False):
-        for lanes in (1, 4, 16):
-            idx, d2 = tree.query(dev(torch, Q), sort=sort, lanes=lanes)
-            assert_nn_equal(idx, d2, oi, od, f"nonfinite lanes={lanes}")
+        for sched in SCHED:
+            idx, d2 = tree.query(dev(torch, Q), sort=sort, **sched)
+            assert_nn_equal(idx, d2, oi, od, f"nonfinite {sched}")
     idx, d2 = tree.query(torch.empty((0, 3), dtype=torch.float32, device="cuda"))
     assert idx.numel() == 0 and d2.numel() == 0
 
@@ -163,10 +171,10 @@ def test_depth_cap_and_round_robin(torch, kdnn):
     Q = rng.random((2000, 3)).astype(np.float32)
     oi, od = oracle.brute_nn(T, Q)
     for kw in ({"max_depth": 4}, {"round_robin": True}, {"max_depth": 6, "round_robin": True}):
-        for lanes in (1, 4, 16):
-            say("build variant", kw, "lanes", lanes)
-            idx, d2 = kdnn.Tree(T, 8, **kw).query(dev(torch, Q), lanes=lanes)
-            assert_nn_equal(idx, d2, oi, od, f"{kw} lanes={lanes}")
+        for sched in SCHED:
+            say("build variant", kw, sched)
+            idx, d2 = kdnn.Tree(T, 8, **kw).query(dev(torch, Q), **sched)
+            assert_nn_equal(idx, d2, oi, od, f"{kw} {sched}")
 
 
 def test_query_stats_consistent(torch, kdnn):
@@ -176,11 +184,15 @@ def test_query_stats_consistent(torch, kdnn):
     q = dev(torch, p.source)
     idx, d2 = tree.query(q)
     D = tree.info["depth"]
-    for lanes in (1, 4, 16):
-        si, sd, cn, cp = tree.query_stats(q, lanes=lanes)
+    for sched in SCHED:
+        si, sd, cn, cp = tree.query_stats(q, **sched)
         assert torch.equal(idx, si) and torch.equal(d2.view(torch.int32), sd.view(torch.int32))
         assert int(cn.min()) >= D + 1 and int(cp.min()) >= 1
-        assert float(cn.float().mean()) < 0.25 * 2 ** (D + 1)
+        # a search never loads a node twice, except the greedy descent a second
+        # pass repeats; a pruning search loads far fewer than all of them
+        assert int(cn.max()) <= 2 ** (D + 1) + 2 * (D + 1)
+        if sched in ({"lanes": 1}, {}, {"budget": 64}):
+            assert float(cn.float().mean()) < 0.25 * 2 ** (D + 1)
 
 
 # ================================================================ transform
@@ -219,12 +231,15 @@ def test_tiny_correspond_reduce_and_icp(torch, kdnn):
     tree = kdnn.Tree(p.target, 8)
     src = dev(torch, p.source)
     diag = bbox_diag(p.target)
+    from kd_tree_nn_amd import _lib
     for name, R, t in [("identity", np.eye(3), np.zeros(3)), ("truth", p.R_true, p.t_true)]:
-        say("tiny correspond_reduce", name)
         oi, od, red = _pairs_oracle(p.target, p.source, R, t)
-        res = tree.correspond_reduce(src, R, t, return_pairs=True)
-        assert_nn_equal(res["idx"], res["d2"], oi, od, f"tiny pairs {name}")
-        check_sums(res, red, diag, f"tiny sums {name}")
+        for f in (0, _lib.lanes_flag(None, 1), _lib.lanes_flag(None, 5), _lib.lanes_flag(1),
+                  _lib.lanes_flag(4) | 2):
+            say("tiny correspond_reduce", name, hex(f))
+            res = tree.correspond_reduce(src, R, t, return_pairs=True, flags=f)
+            assert_nn_equal(res["idx"], res["d2"], oi, od, f"tiny pairs {name} {f:#x}")
+            check_sums(res, red, diag, f"tiny sums {name} {f:#x}")
     say("tiny icp_align")
     o = oracle.icp(p.target, p.source, p.iters, nn="brute")
     g = tree.icp(src, max_iter=p.iters)
@@ -250,10 +265,10 @@ def test_scene_nn_full(torch, kdnn):
                     ("converged queries", oracle.transform(p.source, o["R"], o["t"]))]:
         oi, od = otree.query(Q)
         for sort in (True, False):
-            for lanes in (1, 4, 16):
-                say("scene nn", name, "sort", sort, "lanes", lanes)
-                idx, d2 = tree.query(dev(torch, Q), sort=sort, lanes=lanes)
-                assert_nn_equal(idx, d2, oi, od, f"scene {name} sort={sort} lanes={lanes}")
+            for sched in SCHED:
+                say("scene nn", name, "sort", sort, sched)
+                idx, d2 = tree.query(dev(torch, Q), sort=sort, **sched)
+                assert_nn_equal(idx, d2, oi, od, f"scene {name} sort={sort} {sched}")
 
 
 def test_scene_correspond_reduce(torch, kdnn):
@@ -267,23 +282,25 @@ def test_scene_correspond_reduce(torch, kdnn):
         t = o["Rt_hist"][k, 9:]
         say("scene correspond_reduce iteration", k)
         oi, od, red = _pairs_oracle(p.target, p.source, R, t, otree)
-        res = tree.correspond_reduce(src, R, t, return_pairs=True)
-        assert_nn_equal(res["idx"], res["d2"], oi, od, f"scene pairs it{k}")
-        check_sums(res, red, diag, f"scene sums it{k}")
-        assert res["E"] == pytest.approx(o["E"][k], rel=1e-12)
+        from kd_tree_nn_amd import _lib
+        for f in (0, _lib.lanes_flag(None, 2), _lib.lanes_flag(1), _lib.lanes_flag(16)):
+            res = tree.correspond_reduce(src, R, t, return_pairs=True, flags=f)
+            assert_nn_equal(res["idx"], res["d2"], oi, od, f"scene pairs it{k} flags {f:#x}")
+            check_sums(res, red, diag, f"scene sums it{k} flags {f:#x}")
+            assert res["E"] == pytest.approx(o["E"][k], rel=1e-12)
 
 
 def test_scene_icp_align(torch, kdnn):
     p = scene()
     _, o = scene_oracle_icp()
     tree = kdnn.Tree(p.target, 16)
-    for lanes in (None, 1, 4, 16):
-        say("scene icp_align 30 lanes", lanes)
-        g = tree.icp(dev(torch, p.source), max_iter=p.iters, lanes=lanes)
+    for sched in SCHED + [{"lanes": 1}, {"sort": False}, {"sort": False, "budget": 3}]:
+        say("scene icp_align 30", sched)
+        g = tree.icp(dev(torch, p.source), max_iter=p.iters, **sched)
         assert g["iters"] == p.iters
         dR = np.linalg.norm(g["R"] - o["R"])
         dt = np.max(np.abs(g["t"] - o["t"]))
-        assert dR <= R_TOL and dt <= T_TOL, (lanes, dR, dt)
+        assert dR <= R_TOL and dt <= T_TOL, (sched, dR, dt)
         np.testing.assert_allclose(g["E"], o["E"], rtol=1e-6)
         np.testing.assert_allclose(g["Rt_hist"], o["Rt_hist"], atol=1e-6)
 
@@ -335,15 +352,15 @@ def stress_oracle():
     return p, oracle.KDTree(p.target, 8).query(p.source)
 
 
-@pytest.mark.parametrize("lanes", [None, 4])
+@pytest.mark.parametrize("sched", SCHED_FEW + [{"lanes": 4}], ids=SCHED_FEW_IDS + ["L4"])
 @pytest.mark.parametrize("leaf", [8, 16])
-def test_stress_nn(torch, kdnn, leaf, lanes):
+def test_stress_nn(torch, kdnn, leaf, sched):
     p, (oi, od) = stress_oracle()
-    say("stress 1M x 1M leaf", leaf, "lanes", lanes)
+    say("stress 1M x 1M leaf", leaf, sched)
     tree = kdnn.Tree(p.target, leaf)
     assert tree.info["depth"] == (17 if leaf == 8 else 16)
-    idx, d2 = tree.query(dev(torch, p.source), lanes=lanes)
-    assert_nn_equal(idx, d2, oi, od, f"stress leaf {leaf} lanes {lanes}")
+    idx, d2 = tree.query(dev(torch, p.source), **sched)
+    assert_nn_equal(idx, d2, oi, od, f"stress leaf {leaf} {sched}")
 
 
 @functools.lru_cache(maxsize=None)
@@ -352,13 +369,13 @@ def skewed_oracle():
     return p, oracle.KDTree(p.target, 8).query(p.source)
 
 
-@pytest.mark.parametrize("lanes", [None, 1, 16])
+@pytest.mark.parametrize("sched", SCHED_FEW + [{"lanes": 16}], ids=SCHED_FEW_IDS + ["L16"])
 @pytest.mark.parametrize("leaf", [8, 16])
-def test_skewed_nn(torch, kdnn, leaf, lanes):
+def test_skewed_nn(torch, kdnn, leaf, sched):
     p, (oi, od) = skewed_oracle()
-    say("skewed 500k leaf", leaf, "lanes", lanes)
-    idx, d2 = kdnn.Tree(p.target, leaf).query(dev(torch, p.source), lanes=lanes)
-    assert_nn_equal(idx, d2, oi, od, f"skewed leaf {leaf} lanes {lanes}")
+    say("skewed 500k leaf", leaf, sched)
+    idx, d2 = kdnn.Tree(p.target, leaf).query(dev(torch, p.source), **sched)
+    assert_nn_equal(idx, d2, oi, od, f"skewed leaf {leaf} {sched}")
 
 
 def test_lidar_pairs(torch, kdnn):
