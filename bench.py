@@ -12,11 +12,14 @@ upload are timed separately.  value = NN queries/s over the timed steps
 (30 x 100k queries per step); icp_iters_per_s is the same clock.
 
 Also reported: the fused correspondence kernel's duration (HIP events around
-each launch on the launch stream) and its roofline against algorithmic bytes
-counted by the instrumented traversal; standalone nn_query rates with and
-without the Morton ordering; and the CPU oracle on the host (one thread).
+each launch, on the stream it is launched on) and its roofline against the
+algorithmic bytes counted by the instrumented traversal; HBM traffic from the
+committed rocprofv3 counter summary when it was taken on the current kernel
+source; standalone nn_query rates with and without the Morton ordering; and
+the CPU oracle on the host (one thread, a bounded sample).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --profile-pass    # short run for rocprofv3 counter passes
 """
 
 import argparse
@@ -30,20 +33,131 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NN queries/sec and ICP iterations/sec at 100k×100k points, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "kd_tree_nn_amd", "csrc", "kernels.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "icp_fused_kernel_scene100k_traffic.txt")
+COPY_MIB = 512
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per fused launch from the counter summary, or None when the
+    summary is missing or was taken on another kernel source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            kv = dict(line.split("=", 1) for line in f.read().splitlines()
+                      if "=" in line and not line.startswith(("#", " ")))
+    except OSError:
+        return None, "no counter summary"
+    if kv.get("kernels_hip_sha256_16", "").strip() != kernel_source_hash():
+        return None, "counter summary predates the current kernel source"
+    return float(kv["traffic_bytes_per_launch"]), TRAFFIC_SUMMARY[len(ROOT) + 1:]
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench "
+             "-- python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline")
+PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} "
+           "-o pmc -- python3 -u bench.py --profile-pass")
+
+
+def summarize(trace_dir, fetch_dir, write_dir):
+    """Write the short rocprofv3 summaries under profiles/ from the CSV output of
+    the trace run and the two counter passes (commands in TRACE_CMD, PMC_CMD)."""
+    import csv
+
+    import numpy as np
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    def agent(d):
+        try:
+            for r in rows(os.path.join(d, [f for f in os.listdir(d) if f.endswith("agent_info.csv")][0])):
+                if r.get("Agent_Type", "").upper() == "GPU":
+                    return (f'{r.get("Name", "?")}, {r.get("Cu_Count", "?")} CUs, '
+                            f'{r.get("Num_Xcc", "?")} XCDs, {r.get("Max_Engine_Clk_Fcompute", "?")} MHz')
+        except (OSError, IndexError):
+            pass
+        return "?"
+
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    stats = rows(os.path.join(trace_dir, "bench_kernel_stats.csv"))
+    out = [f"# rocprofv3 kernel statistics: bench.py on the Scene 100k x 100k ICP workload",
+           f"# command: {TRACE_CMD}",
+           f"# device: {agent(trace_dir)}",
+           f"# kernels.hip sha256[:16]: {kernel_source_hash()}",
+           "",
+           f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}"]
+    for r in stats[:14]:
+        out.append(f"{r['Name'][:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                   f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                   f"{float(r['Percentage']):6.2f}")
+    with open(os.path.join(ROOT, "profiles", "icp_fused_kernel_scene100k_trace.txt"), "w") as f:
+        f.write("\n".join(out) + "\n")
+
+    def counter(d):
+        per = {}
+        for r in rows(os.path.join(d, "pmc_counter_collection.csv")):
+            per.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+        return per
+
+    copy_kib = COPY_MIB * 1024
+    res = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = counter(d)
+        fused = [v for k, vs in per.items() if "icp_fused_kernel" in k for _, v in vs]
+        copies = [v for k, vs in per.items() if "copyBuffer" in k for _, v in vs
+                  if v > 0.25 * copy_kib]
+        factor = copy_kib / float(np.mean(copies))
+        res[name] = (float(np.mean(fused)), len(fused), copies, factor)
+    traffic = sum(v * 1024 * fac for v, _, _, fac in res.values())
+    out = ["# HBM traffic of icp_fused_kernel<1> on the Scene 100k x 100k ICP workload",
+           "# two rocprofv3 counter passes, each over the same short program:",
+           "#   " + PMC_CMD.format(c="FETCH_SIZE", d="fetch"),
+           "#   " + PMC_CMD.format(c="WRITE_SIZE", d="write"),
+           f"# device: {agent(fetch_dir)}",
+           "# calibration: three device copies of a known size in the same program;",
+           "# factor = copied KiB / counter KiB of those dispatches",
+           ""]
+    for name, (avg, cnt, copies, fac) in res.items():
+        out.append(f"# {name}: fused kernel {avg:.1f} KiB/dispatch over {cnt} dispatches; "
+                   f"{COPY_MIB} MiB copies read {', '.join(f'{c:.1f}' for c in copies)} KiB "
+                   f"-> factor {fac:.5f}")
+    out += ["",
+            f"fetch_bytes_per_launch={res['FETCH_SIZE'][0] * 1024 * res['FETCH_SIZE'][3]:.0f}",
+            f"write_bytes_per_launch={res['WRITE_SIZE'][0] * 1024 * res['WRITE_SIZE'][3]:.0f}",
+            f"traffic_bytes_per_launch={traffic:.0f}",
+            f"kernels_hip_sha256_16={kernel_source_hash()}"]
+    with open(TRAFFIC_SUMMARY, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="only: 30 fused launches of the Scene ICP iterations, then a "
+                         f"{COPY_MIB} MiB device copy (calibration for HBM counters)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from rocprofv3 CSV output and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -71,6 +185,23 @@ def main():
     src = torch.from_numpy(p.source).cuda()
     ws = tree.icp_workspace(n)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sums = torch.zeros(kdnn.KDNN_SUMS_DOUBLES, dtype=torch.float64, device="cuda")
+
+    if args.profile_pass:
+        g = tree.icp(src, max_iter=ITERS, workspace=ws)
+        Rt = g["Rt_hist"]
+        for k in range(ITERS):
+            tree.correspond_reduce_async(src, Rt[k, :9], Rt[k, 9:], sums, ws)
+        a = torch.empty(COPY_MIB << 18, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("profile pass done: icp", ITERS, "iterations +", ITERS, "fused launches +",
+            f"3 copies of {COPY_MIB} MiB")
+        return
 
     # ---------------------------------------------------------------- headline
     log(f"warmup {args.warmup} registrations")
@@ -89,20 +220,30 @@ def main():
     log(f"{value / 1e9:.3f} G queries/s, {iters_per_s:.0f} ICP iterations/s")
 
     # ------------------------------------------- fused kernel: events per launch
+    # The library launches on torch's current stream; the events bracket each
+    # launch on that stream.  A spin kernel queued ahead of every 30 launches
+    # keeps the GPU from running dry while the host enqueues them, so that the
+    # events time the kernel and not the host.
     Rt = g["Rt_hist"]
-    stream = torch.cuda.current_stream()
-    sums = torch.zeros(kdnn.KDNN_SUMS_DOUBLES, dtype=torch.float64, device="cuda")
-    tree.correspond_reduce_async(src, Rt[0, :9], Rt[0, 9:], sums, ws)   # computes the order
-    evs = []
-    for _ in range(args.kernel_reps):
+    tree.correspond_reduce_async(src, Rt[0, :9], Rt[0, 9:], sums, ws)   # order, if any
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1 << 20)
+    c0.record(stream)
+    torch.cuda._sleep(1 << 24)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    spin_cycles = int((1 << 24) * 25.0 / max(c0.elapsed_time(c1), 1e-3))   # ~25 ms
+    Rts = [(Rt[k, :9].copy(), Rt[k, 9:].copy()) for k in range(ITERS)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps * ITERS)]
+    for r in range(args.kernel_reps):
+        torch.cuda._sleep(spin_cycles)
         for k in range(ITERS):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+            e0, e1 = evs[r * ITERS + k]
             e0.record(stream)
-            tree.correspond_reduce_async(src, Rt[k, :9], Rt[k, 9:], sums, ws,
+            tree.correspond_reduce_async(src, Rts[k][0], Rts[k][1], sums, ws,
                                          flags=kdnn.KDNN_ICP_REUSE_ORDER)
             e1.record(stream)
-            evs.append((e0, e1))
     torch.cuda.synchronize()
     kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
     kern_avg_ms = float(kern_ms.mean())
@@ -118,7 +259,8 @@ def main():
     nodes_avg = float(np.mean(nodes_tot)) / n
     pts_avg = float(np.mean(pts_tot)) / n
     n_blocks = min((n + 255) // 256, 4096)
-    per_query = 32 * nodes_avg + 16 * pts_avg + 12 + 4
+    # node records + leaf points + the source point (+ its slot in the order)
+    per_query = 32 * nodes_avg + 16 * pts_avg + 12 + (4 if info["auto_sort"] else 0)
     bytes_launch = n * per_query + n_blocks * 17 * 8 * 2 + 17 * 8
     achieved = bytes_launch / (kern_avg_ms * 1e-3) / 1e9
     descent_lb = 32 * (info["depth"] + 1) + 16 * (n / 2 ** info["depth"]) + 16
@@ -142,13 +284,14 @@ def main():
 
     q0 = src
     qc = kdnn.transform(src, g["R"], g["t"])
-    nnq = {}
+    nnq = {"automatic_order": "morton" if info["auto_sort"] else "unsorted"}
     for name, q in (("iteration0", q0), ("converged", qc)):
         for sort in (True, False):
             ms = time_query(q, sort)
             nnq[f"{name}_{'morton' if sort else 'unsorted'}"] = {
                 "ms": round(ms, 4), "queries_per_s": round(len(q) / (ms * 1e-3))}
     log("nn_query:", nnq)
+    traffic, traffic_src = committed_traffic()
 
     result = {
         "metric": METRIC,
@@ -182,31 +325,40 @@ def main():
         "nn_query": nnq,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "icp_fused_kernel",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "traffic_source": traffic_src,
+            "kernel": "icp_fused_kernel<1>",
+            "kernels_hip_sha256_16": kernel_source_hash(),
             "bytes_per_launch": round(bytes_launch),
             "bytes_per_query": round(per_query, 1),
             "nodes_per_query": round(nodes_avg, 2), "points_per_query": round(pts_avg, 2),
             "single_descent_bytes_per_query": round(descent_lb, 1),
-            "note": "working set (~2 MB) is L2-resident; algorithmic gather bytes vs HBM peak",
+            "tree_device_bytes": info["device_bytes"], "l2_bytes": info["l2_bytes"],
+            "note": "the tree fits one XCD's L2: algorithmic gather bytes vs HBM peak; "
+                    "traffic = HBM bytes the counters saw per launch",
         },
     }
 
     if not args.no_cpu_baseline:
         import oracle
-        log("cpu baseline: oracle ICP, 30 iterations, 1 thread")
-        t0 = time.perf_counter()
-        o = oracle.icp(p.target, p.source, ITERS, leaf_size=p.leaf_size)
-        Tc = time.perf_counter() - t0
+        log("cpu baseline: oracle ICP registrations (30 iterations each), 1 thread, >= 10 s")
+        regs, Tc = 0, 0.0
+        while Tc < 10.0 and regs < 6:
+            t0 = time.perf_counter()
+            o = oracle.icp(p.target, p.source, ITERS, leaf_size=p.leaf_size)
+            Tc += time.perf_counter() - t0
+            regs += 1
         result["cpu_baseline"] = {
-            "value": round(ITERS * n / Tc), "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": "one full Scene registration (30 ICP iterations x 100k queries) with the "
-                      "oracle's C KD-tree search and numpy fp64 reduction/Horn solve, "
-                      f"{Tc:.2f} s wall",
-            "icp_iters_per_s": round(ITERS / Tc, 2),
+            "value": round(regs * ITERS * n / Tc), "unit": "queries/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{regs} full Scene registrations (30 ICP iterations x 100k queries each) "
+                      "with the oracle's C KD-tree search and numpy fp64 reduction/Horn "
+                      f"solve, {Tc:.2f} s wall",
+            "icp_iters_per_s": round(regs * ITERS / Tc, 2),
             "R_diff_vs_gpu": float(np.linalg.norm(o["R"] - g["R"])),
         }
-        log(f"cpu baseline {ITERS * n / Tc / 1e6:.2f} M queries/s")
+        log(f"cpu baseline {regs * ITERS * n / Tc / 1e6:.2f} M queries/s")
     print(json.dumps(result), flush=True)
 
 

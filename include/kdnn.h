@@ -87,6 +87,8 @@ typedef struct kdnn_tree_info {
     double build_ms;        /* host build time (excluding the upload) */
     double upload_ms;       /* device allocation + host-to-device copy */
     int64_t device_bytes;   /* device memory held by the tree */
+    int64_t l2_bytes;       /* L2 cache size of the tree's device */
+    int32_t auto_sort;      /* 1: the automatic choice applies the Morton ordering */
 } kdnn_tree_info;
 
 /* Correspondence sums of one ICP iteration (article §2.1).  Over the pairs
@@ -155,22 +157,34 @@ kdnn_status kdtree_build_host(const float *xyz_host, int64_t n, const kdnn_build
 
 /* Query flags. */
 #define KDNN_QUERY_NO_SORT 1u /* traverse in the given order (skip the Morton ordering) */
+#define KDNN_QUERY_SORT 2u    /* always apply the Morton ordering (needs ws_dev) */
+/* Neither: the Morton ordering is applied when a workspace is given and the
+ * tree's device footprint (kdnn_tree_info.device_bytes) exceeds the device's
+ * L2 cache.  A tree that stays L2-resident gains little locality from the
+ * ordering, which also packs the queries needing wide searches into the same
+ * wavefronts.  Results never depend on the order. */
 
 /* Search schedule (nn_query, nn_query_stats and the ICP entry points).
- * Default: one lane per query, one pass.  KDNN_LANES(g), g in {1, 2, 4, 8,
- * 16}: g lanes cooperate on each query.  KDNN_BUDGET(b), b in 1..255 (without
- * KDNN_LANES): two passes -- one lane per query with a budget of b node
- * visits, then groups of 16 lanes complete the queries left, starting from
- * the first pass's best.  Results never depend on the schedule. */
+ * Default: one lane per query, one pass.
+ *   KDNN_LANES(g), g in {1, 2, 4, 8, 16}: g lanes cooperate on each query.
+ *   KDNN_BUDGET(b), b in 1..255: two passes -- one lane
+ *                   per query with a budget of b node visits, then groups of
+ *                   16 lanes complete the queries left over, starting from
+ *                   the first pass's best (nn_query: needs ws_dev).
+ *   KDNN_TOP_LDS:   one lane per query, one work-group per CU, with the top
+ *                   (up to 12) tree levels copied into LDS first.
+ * At most one of the three may be given (else EINVAL).  Results never depend
+ * on the schedule. */
 #define KDNN_LANES_SHIFT 8
 #define KDNN_LANES_MASK (0x1fu << KDNN_LANES_SHIFT)
 #define KDNN_LANES(g) ((uint32_t)(g) << KDNN_LANES_SHIFT)
 #define KDNN_BUDGET_SHIFT 16
 #define KDNN_BUDGET_MASK (0xffu << KDNN_BUDGET_SHIFT)
 #define KDNN_BUDGET(b) ((uint32_t)(b) << KDNN_BUDGET_SHIFT)
+#define KDNN_TOP_LDS (1u << 24)
 
 /* Bytes of device workspace nn_query needs for m queries (Morton keys,
- * permutation, radix-sort histograms). 0 for m <= 0. */
+ * permutation, radix-sort histograms, two-pass list). 0 for m <= 0. */
 size_t nn_query_workspace_bytes(int64_t m);
 
 /* Exact nearest neighbour of every query (article §2.2 search with
@@ -180,9 +194,10 @@ size_t nn_query_workspace_bytes(int64_t m);
  *   q_dev      : m x 3 fp32 queries (device).
  *   idx_dev    : m int32 out, original target index of each nearest point.
  *   dist2_dev  : m fp32 out, its squared distance.
- *   flags      : KDNN_QUERY_*.
+ *   flags      : KDNN_QUERY_* and the schedule flags.
  *   ws_dev     : >= nn_query_workspace_bytes(m) bytes of device memory,
- *                256-byte aligned; may be NULL with KDNN_QUERY_NO_SORT.
+ *                256-byte aligned, or NULL (then no Morton ordering and no
+ *                two-pass schedule; KDNN_QUERY_SORT with NULL is EINVAL).
  *   stream     : HIP stream (NULL = default stream).  Asynchronous.
  * Results are written in the queries' own order whatever the traversal
  * order.  m == 0 is a no-op.  Errors: EINVAL, EDEVICE (launch failure). */
@@ -210,9 +225,13 @@ kdnn_status transform_points(const float *in_dev, float *out_dev, int64_t n, con
 /* ------------------------------------------------------------------ ICP */
 
 /* ICP flags. */
-#define KDNN_ICP_REUSE_ORDER 1u /* ws already holds the traversal order of this src (from a
-                                   previous call with the same src_dev and n) */
+#define KDNN_ICP_REUSE_ORDER 1u /* ws was last used by an ICP call with the same src_dev, n
+                                   and ordering choice, stream-ordered before this one: reuse
+                                   its traversal order and skip re-initialising ws */
 #define KDNN_ICP_NO_SORT 2u     /* traverse source points in their given order */
+#define KDNN_ICP_SORT 4u        /* always traverse in Morton order of the transformed points */
+/* Neither NO_SORT nor SORT: Morton order when the tree's device footprint
+ * exceeds the device's L2 cache (as for nn_query). */
 
 /* Bytes of device workspace the ICP entry points need for n source points. */
 size_t icp_workspace_bytes(int64_t n);
@@ -262,7 +281,7 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  *   Rt_hist      : optional [max_iter][12] fp64, (R_k row-major, t_k) used by
  *                  iteration k.
  *   iters_done   : optional, iterations completed.
- *   flags        : KDNN_ICP_NO_SORT and/or KDNN_LANES(g).
+ *   flags        : KDNN_ICP_NO_SORT or KDNN_ICP_SORT, and the schedule flags.
  * The traversal order is computed once, from the source moved by (R0, t0).
  * On EDEGENERATE the outputs hold the last good transform.
  * Errors: EINVAL, EDEVICE, EDEGENERATE. */

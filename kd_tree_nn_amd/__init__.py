@@ -20,7 +20,8 @@ import numpy as np
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    KdnnError, KDNN_QUERY_NO_SORT, KDNN_ICP_REUSE_ORDER, KDNN_ICP_NO_SORT, KDNN_SUMS_DOUBLES,
+    KdnnError, KDNN_QUERY_NO_SORT, KDNN_QUERY_SORT, KDNN_ICP_REUSE_ORDER, KDNN_ICP_NO_SORT,
+    KDNN_ICP_SORT, KDNN_SUMS_DOUBLES,
 )
 
 __all__ = ["Tree", "transform", "procrustes", "build_host", "layout", "sums_to_dict",
@@ -132,12 +133,14 @@ class Tree:
         return torch.empty(int(_lib.lib().nn_query_workspace_bytes(m)), dtype=torch.uint8,
                            device=self.device)
 
-    def query(self, q, sort: bool = True, out=None, workspace=None, stream=None, lanes=None,
-              budget=None):
+    def query(self, q, sort=None, out=None, workspace=None, stream=None, lanes=None,
+              budget=None, top_lds: bool = False):
         """(idx int32[m], dist2 float32[m]) of the exact nearest target point.
 
+        sort: Morton-order the queries (None = the library's choice by tree size).
         lanes: single pass with this many lanes per query (1, 2, 4, 8, 16);
-        None = the default two-pass schedule (budget: its first-pass node budget).
+        budget: two-pass schedule with this first-pass node budget;
+        top_lds: single lane with the top tree levels staged in LDS.
         """
         torch = _torch()
         q = _dev_points(q, "queries")
@@ -146,15 +149,16 @@ class Tree:
             torch.empty(m, dtype=torch.int32, device=q.device),
             torch.empty(m, dtype=torch.float32, device=q.device))
         ws = None
-        if sort and m > 0:
+        if m > 0:
             ws = workspace if workspace is not None else self.query_workspace(m)
         _lib.check(_lib.lib().nn_query(
             self._h, _ptr(q), m, _ptr(idx), _ptr(d2),
-            (0 if sort else KDNN_QUERY_NO_SORT) | _lib.lanes_flag(lanes, budget),
+            _lib.sort_flag(sort, KDNN_QUERY_SORT, KDNN_QUERY_NO_SORT)
+            | _lib.lanes_flag(lanes, budget, top_lds),
             _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)), "nn_query")
         return idx, d2
 
-    def query_stats(self, q, sort: bool = True, lanes=None, budget=None):
+    def query_stats(self, q, sort=None, lanes=None, budget=None, top_lds: bool = False):
         """query() plus per-query counts of nodes loaded and leaf points scanned."""
         torch = _torch()
         q = _dev_points(q, "queries")
@@ -163,11 +167,11 @@ class Tree:
         d2 = torch.empty(m, dtype=torch.float32, device=q.device)
         cn = torch.empty(m, dtype=torch.int32, device=q.device)
         cp = torch.empty(m, dtype=torch.int32, device=q.device)
-        ws = self.query_workspace(m) if sort and m > 0 else None
+        ws = self.query_workspace(m) if m > 0 else None
         _lib.check(_lib.lib().nn_query_stats(
             self._h, _ptr(q), m, _ptr(idx), _ptr(d2), _ptr(cn), _ptr(cp),
-            (0 if sort else KDNN_QUERY_NO_SORT) | _lib.lanes_flag(lanes, budget), _ptr(ws),
-            ws.numel() if ws is not None else 0, _stream()), "nn_query_stats")
+            _lib.sort_flag(sort, KDNN_QUERY_SORT, KDNN_QUERY_NO_SORT)
+            | _lib.lanes_flag(lanes, budget, top_lds), _ptr(ws), ws.numel() if ws is not None else 0, _stream()), "nn_query_stats")
         return idx, d2, cn, cp
 
     # ------------------------------------------------------------------ ICP
@@ -213,7 +217,8 @@ class Tree:
             "icp_correspond_reduce_async")
 
     def icp(self, src, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
-            workspace=None, stream=None, lanes=None, sort: bool = True, budget=None) -> dict:
+            workspace=None, stream=None, lanes=None, sort=None, budget=None,
+            top_lds: bool = False) -> dict:
         """ICP registration of the source (device, original coordinates) onto the tree."""
         src = _dev_points(src, "src")
         n = src.shape[0]
@@ -230,7 +235,8 @@ class Tree:
             R0a[1] if R0a else None, t0a[1] if t0a else None, int(max_iter), float(eps),
             R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
             E.ctypes.data_as(_lib.c_dp), Rt.ctypes.data_as(_lib.c_dp), ctypes.byref(it),
-            (0 if sort else KDNN_ICP_NO_SORT) | _lib.lanes_flag(lanes, budget),
+            _lib.sort_flag(sort, KDNN_ICP_SORT, KDNN_ICP_NO_SORT)
+            | _lib.lanes_flag(lanes, budget, top_lds),
             _ptr(ws), ws.numel(), _stream(stream)), "icp_align")
         k = it.value
         return {"R": R.reshape(3, 3), "t": t, "E": E[:k], "Rt_hist": Rt[:k], "iters": k}

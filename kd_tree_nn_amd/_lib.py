@@ -13,19 +13,28 @@ KDNN_OK, KDNN_EINVAL, KDNN_ENOMEM, KDNN_EDEVICE, KDNN_ENONFINITE, KDNN_EDEGENERA
 STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ENOMEM", 3: "EDEVICE", 4: "ENONFINITE", 5: "EDEGENERATE"}
 KDNN_BUILD_ROUND_ROBIN = 1
 KDNN_QUERY_NO_SORT = 1
+KDNN_QUERY_SORT = 2
 KDNN_ICP_REUSE_ORDER = 1
 KDNN_ICP_NO_SORT = 2
+KDNN_ICP_SORT = 4
 KDNN_SUMS_DOUBLES = 17
 KDNN_LANES_SHIFT = 8
-
-
 KDNN_BUDGET_SHIFT = 16
+KDNN_TOP_LDS = 1 << 24
 
 
-def lanes_flag(lanes, budget=None):
-    """KDNN_LANES(g) | KDNN_BUDGET(b): single pass with g lanes per query, or
-    (g = None) the default two-pass schedule with first-pass budget b."""
-    return ((int(lanes or 0) & 0x1f) << KDNN_LANES_SHIFT) | ((int(budget or 0) & 0xff) << KDNN_BUDGET_SHIFT)
+def lanes_flag(lanes=None, budget=None, top_lds=False):
+    """Schedule flags: KDNN_LANES(g) (single pass, g lanes per query),
+    KDNN_BUDGET(b) (two passes, first-pass budget b), KDNN_TOP_LDS; all
+    unset = the library's automatic choice."""
+    return (((int(lanes or 0) & 0x1f) << KDNN_LANES_SHIFT)
+            | ((int(budget or 0) & 0xff) << KDNN_BUDGET_SHIFT)
+            | (KDNN_TOP_LDS if top_lds else 0))
+
+
+def sort_flag(sort, on, off):
+    """Ordering flag: None = the library's automatic choice, True/False forced."""
+    return 0 if sort is None else (on if sort else off)
 
 
 class BuildParams(ctypes.Structure):
@@ -37,7 +46,8 @@ class TreeInfo(ctypes.Structure):
                 ("leaves", c_i64), ("min_leaf", c_i32), ("max_leaf", c_i32),
                 ("bbox_min", ctypes.c_float * 3), ("bbox_max", ctypes.c_float * 3),
                 ("center", ctypes.c_double * 3), ("build_ms", ctypes.c_double),
-                ("upload_ms", ctypes.c_double), ("device_bytes", c_i64)]
+                ("upload_ms", ctypes.c_double), ("device_bytes", c_i64),
+                ("l2_bytes", c_i64), ("auto_sort", c_i32)]
 
 
 class IcpSums(ctypes.Structure):

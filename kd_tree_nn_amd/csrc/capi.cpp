@@ -37,10 +37,24 @@ kdnn_status hip_fail(hipError_t e, const char *what)
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// A valid lane count, and at most one of the lanes / budget / LDS choices.
 bool lanes_ok(uint32_t flags)
 {
     const uint32_t g = (flags & KDNN_LANES_MASK) >> KDNN_LANES_SHIFT;
-    return g == 0 || g == 1 || g == 2 || g == 4 || g == 8 || g == 16;
+    const int chosen = int(g != 0) + int((flags & KDNN_BUDGET_MASK) != 0) +
+                       int((flags & KDNN_TOP_LDS) != 0);
+    return (g == 0 || g == 1 || g == 2 || g == 4 || g == 8 || g == 16) && chosen <= 1;
+}
+
+constexpr uint32_t kSchedMask = KDNN_LANES_MASK | KDNN_BUDGET_MASK | KDNN_TOP_LDS;
+
+Schedule schedule_of(uint32_t flags)
+{
+    Schedule sc;
+    sc.lanes = int((flags & KDNN_LANES_MASK) >> KDNN_LANES_SHIFT);
+    sc.budget = (flags & KDNN_BUDGET_MASK) >> KDNN_BUDGET_SHIFT;
+    sc.top_lds = (flags & KDNN_TOP_LDS) != 0;
+    return sc;
 }
 
 double ms_since(std::chrono::steady_clock::time_point t0)
@@ -100,6 +114,16 @@ void rt_to_f32(const double *R, const double *t, float out[12])
 const double kI[9] = {1, 0, 0, 0, 1, 0, 0, 0, 1};
 const double kZ[3] = {0, 0, 0};
 
+// Resolve the ordering choice of ICP flags to KDNN_ICP_NO_SORT set or clear
+// (KDNN_ICP_SORT cleared).
+uint32_t icp_resolve_sort(const kdnn_tree *tree, uint32_t flags)
+{
+    const bool sort = (flags & KDNN_ICP_SORT) ||
+                      (!(flags & KDNN_ICP_NO_SORT) && tree->auto_sort);
+    flags &= ~(KDNN_ICP_SORT | KDNN_ICP_NO_SORT);
+    return sort ? flags : (flags | KDNN_ICP_NO_SORT);
+}
+
 // Enqueue the traversal order (per flags) and the fused kernel.
 kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, const double *R,
                         const double *t, double *sums_dev, int32_t *idx, float *d2,
@@ -107,19 +131,19 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
 {
     const int32_t *perm = nullptr;
     hipError_t e = hipSuccess;
+    // Every fused launch leaves the ticket at zero; a workspace coming from a
+    // call ordered before this one on the stream needs no clearing.
     if (flags & KDNN_ICP_NO_SORT) {
-        e = launch_zero_u32(w.ticket, 1, s);
+        if (!(flags & KDNN_ICP_REUSE_ORDER)) e = launch_zero_u32(w.ticket, 1, s);
     } else if (flags & KDNN_ICP_REUSE_ORDER) {
-        perm = w.sort.vals_a;  // ticket is clean after any completed call
+        perm = w.sort.vals_a;
     } else {
         float rt[12];
         rt_to_f32(R, t, rt);
         e = launch_icp_order(tree->dev, src, n, rt, w, &perm, s);
     }
     if (e != hipSuccess) return hip_fail(e, "icp: order launch");
-    e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2,
-                         int((flags & KDNN_LANES_MASK) >> KDNN_LANES_SHIFT),
-                         (flags & KDNN_BUDGET_MASK) >> KDNN_BUDGET_SHIFT, s);
+    e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, schedule_of(flags), s);
     if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
     return KDNN_OK;
 }
@@ -132,9 +156,11 @@ kdnn_status icp_check(const kdnn_tree *tree, const float *src, int64_t n, const 
     kdnn_status st = check_points(src, n, "icp: src");
     if (st != KDNN_OK) return st;
     if (!R || !t) return fail(KDNN_EINVAL, "icp: null R or t");
-    if ((flags & ~(KDNN_ICP_REUSE_ORDER | KDNN_ICP_NO_SORT | KDNN_LANES_MASK | KDNN_BUDGET_MASK)) ||
+    if ((flags & ~(KDNN_ICP_REUSE_ORDER | KDNN_ICP_NO_SORT | KDNN_ICP_SORT | kSchedMask)) ||
         !lanes_ok(flags))
         return fail(KDNN_EINVAL, "icp: unknown flag or lane count");
+    if ((flags & KDNN_ICP_SORT) && (flags & KDNN_ICP_NO_SORT))
+        return fail(KDNN_EINVAL, "icp: KDNN_ICP_SORT and KDNN_ICP_NO_SORT together");
     return check_ws(ws, ws_bytes, icp_ws_bytes(n));
 }
 
@@ -237,6 +263,14 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     I.build_ms = build_ms;
     I.upload_ms = upload_ms;
     I.device_bytes = int64_t(nb + pb);
+    int l2 = 0;
+    if ((e = hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, t->device)) != hipSuccess) {
+        free_tree(t);
+        return hip_fail(e, "kdtree_build: L2 size query");
+    }
+    t->auto_sort = nb + pb > size_t(l2 > 0 ? l2 : 0);
+    I.l2_bytes = l2;
+    I.auto_sort = t->auto_sort ? 1 : 0;
     *out = t;
     return KDNN_OK;
     KDNN_GUARD_END
@@ -257,7 +291,7 @@ kdnn_status kdtree_info(const kdnn_tree *tree, kdnn_tree_info *out)
     return KDNN_OK;
 }
 
-size_t nn_query_workspace_bytes(int64_t m) { return m > 0 ? sort_workspace_bytes(m) : 0; }
+size_t nn_query_workspace_bytes(int64_t m) { return query_ws_bytes(m); }
 
 static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t m, int32_t *idx,
                                  float *d2, uint32_t *cn, uint32_t *cp, bool stats, uint32_t flags,
@@ -269,19 +303,30 @@ static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t 
     if (m == 0) return KDNN_OK;
     if (!idx || !d2) return fail(KDNN_EINVAL, "nn_query: null output");
     if (!aligned(idx, 4) || !aligned(d2, 4)) return fail(KDNN_EINVAL, "nn_query: misaligned output");
-    if ((flags & ~(KDNN_QUERY_NO_SORT | KDNN_LANES_MASK | KDNN_BUDGET_MASK)) || !lanes_ok(flags))
+    if ((flags & ~(KDNN_QUERY_NO_SORT | KDNN_QUERY_SORT | kSchedMask)) || !lanes_ok(flags))
         return fail(KDNN_EINVAL, "nn_query: unknown flag or lane count");
+    if ((flags & KDNN_QUERY_SORT) && (flags & KDNN_QUERY_NO_SORT))
+        return fail(KDNN_EINVAL, "nn_query: KDNN_QUERY_SORT and KDNN_QUERY_NO_SORT together");
+    if ((flags & KDNN_QUERY_SORT) && !ws)
+        return fail(KDNN_EINVAL, "nn_query: the Morton ordering needs a workspace");
+    if ((flags & KDNN_BUDGET_MASK) && !ws)
+        return fail(KDNN_EINVAL, "nn_query: the two-pass schedule needs a workspace");
+    const bool sort = (flags & KDNN_QUERY_SORT) ||
+                      (!(flags & KDNN_QUERY_NO_SORT) && tree->auto_sort && ws);
     const int32_t *perm = nullptr;
-    if (!(flags & KDNN_QUERY_NO_SORT)) {
-        st = check_ws(ws, ws_bytes, sort_workspace_bytes(m));
+    void *twopass = nullptr;
+    if (ws) {
+        st = check_ws(ws, ws_bytes, query_ws_bytes(m));
         if (st != KDNN_OK) return st;
-        const SortWorkspace w = carve_sort_workspace(ws, m);
-        hipError_t e = launch_morton_order(tree->dev, q, m, nullptr, w, &perm, s);
-        if (e != hipSuccess) return hip_fail(e, "nn_query: order launch");
+        const QueryWorkspace w = carve_query_workspace(ws, m);
+        twopass = w.twopass;
+        if (sort) {
+            hipError_t e = launch_morton_order(tree->dev, q, m, nullptr, w.sort, &perm, s);
+            if (e != hipSuccess) return hip_fail(e, "nn_query: order launch");
+        }
     }
-    hipError_t e = launch_nn(tree->dev, q, m, perm, idx, d2, cn, cp, stats,
-                             int((flags & KDNN_LANES_MASK) >> KDNN_LANES_SHIFT),
-                             (flags & KDNN_BUDGET_MASK) >> KDNN_BUDGET_SHIFT, s);
+    hipError_t e = launch_nn(tree->dev, q, m, perm, idx, d2, cn, cp, stats, schedule_of(flags),
+                             twopass, s);
     if (e != hipSuccess) return hip_fail(e, "nn_query: launch");
     return KDNN_OK;
 }
@@ -342,7 +387,8 @@ kdnn_status icp_correspond_reduce_async(const kdnn_tree *tree, const float *src_
     if (st != KDNN_OK) return st;
     if (!sums_dev || !aligned(sums_dev, 8)) return fail(KDNN_EINVAL, "icp: bad sums_dev");
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
-    return icp_enqueue(tree, src_dev, n, R_host, t_host, sums_dev, idx_dev, dist2_dev, flags, w,
+    return icp_enqueue(tree, src_dev, n, R_host, t_host, sums_dev, idx_dev, dist2_dev,
+                       icp_resolve_sort(tree, flags), w,
                        stream);
     KDNN_GUARD_END
 }
@@ -360,7 +406,8 @@ kdnn_status icp_correspond_reduce(const kdnn_tree *tree, const float *src_dev, i
     kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
     std::lock_guard<std::mutex> lock(mt->icp_mu);
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
-    st = icp_enqueue(tree, src_dev, n, R_host, t_host, w.sums, idx_dev, dist2_dev, flags, w, stream);
+    st = icp_enqueue(tree, src_dev, n, R_host, t_host, w.sums, idx_dev, dist2_dev,
+                     icp_resolve_sort(tree, flags), w, stream);
     if (st != KDNN_OK) return st;
     hipError_t e = hipMemcpyAsync(mt->h_pinned, w.sums, KDNN_SUMS_DOUBLES * sizeof(double),
                                   hipMemcpyDeviceToHost, stream);
@@ -397,10 +444,11 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     if (!R_out || !t_out) return fail(KDNN_EINVAL, "icp_align: null R_out or t_out");
     if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align: max_iter < 0");
     if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align: eps must be >= 0");
-    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_LANES_MASK | KDNN_BUDGET_MASK))
+    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_ICP_SORT | kSchedMask))
         return fail(KDNN_EINVAL, "icp_align: unknown flag");
     kdnn_status st = icp_check(tree, src_dev, n, R, t, flags, ws_dev, ws_bytes);
     if (st != KDNN_OK) return st;
+    flags = icp_resolve_sort(tree, flags);
     std::memcpy(R_out, R, sizeof R);
     std::memcpy(t_out, t, sizeof t);
     if (iters_done) *iters_done = 0;
@@ -416,8 +464,7 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
             std::memcpy(Rt_hist + 12 * k, R, sizeof R);
             std::memcpy(Rt_hist + 12 * k + 9, t, sizeof t);
         }
-        const uint32_t f = (flags & KDNN_ICP_NO_SORT) ? flags
-                           : (k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER));
+        const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
         st = icp_enqueue(tree, src_dev, n, R, t, w.sums, nullptr, nullptr, f, w, stream);
         if (st != KDNN_OK) return st;
         hipError_t e = hipMemcpyAsync(mt->h_pinned, w.sums, KDNN_SUMS_DOUBLES * sizeof(double),

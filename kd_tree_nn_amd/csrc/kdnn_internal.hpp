@@ -76,13 +76,20 @@ struct SortWorkspace {
 size_t sort_workspace_bytes(int64_t m);
 SortWorkspace carve_sort_workspace(void *ws, int64_t m);
 
+struct QueryWorkspace {
+    SortWorkspace sort;
+    void *twopass;  // two-pass list + per-group counts
+};
+size_t query_ws_bytes(int64_t m);
+QueryWorkspace carve_query_workspace(void *ws, int64_t m);
+
 struct IcpWorkspace {
     SortWorkspace sort;
     double *partials;   // KDNN_SUMS_DOUBLES * max_blocks
     double *partials2;  // KDNN_SUMS_DOUBLES * pass-2 blocks
-    uint32_t *state;    // [n] per traversal slot
-    uint64_t *pkey;     // [n]
+    uint64_t *pkey;     // [n] pass-1 best key per traversal slot
     uint32_t *pslot;    // [n]
+    void *twopass;      // two-pass list + per-group counts
     double *sums;       // KDNN_SUMS_DOUBLES
     uint32_t *ticket;   // 1 counter, must be 0 between launches
     int32_t max_blocks;
@@ -98,17 +105,22 @@ hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m,
 // Same, for the ICP entry points: also clears the workspace's ticket counter.
 hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                             const IcpWorkspace &ws, const int32_t **perm, hipStream_t s);
-// lanes: lanes per query for a single-pass search (1, 2, 4, 8, 16); 0 = the
-// default two-pass search (budgeted single lane, then cooperative groups).
+// Search schedule decoded from the KDNN_LANES / KDNN_BUDGET / KDNN_TOP_LDS
+// flag fields (see kdnn.h).
+struct Schedule {
+    int lanes = 0;        // 0 = automatic, else single pass with this many lanes
+    uint32_t budget = 0;  // 0 = default two-pass budget / automatic choice
+    bool top_lds = false;
+};
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     int lanes, uint32_t budget, hipStream_t s);
+                     const Schedule &sc, void *twopass, hipStream_t s);
 hipError_t launch_transform(const float *in, float *out, int64_t n, const double *R,
                             const double *t, hipStream_t s);
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
-                            double *sums_out, int32_t *idx, float *d2, int lanes,
-                            uint32_t budget, hipStream_t s);
+                            double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
+                            hipStream_t s);
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace kdnn
@@ -121,5 +133,6 @@ struct kdnn_tree {
     void *d_points = nullptr;
     kdnn_tree_info info{};
     double *h_pinned = nullptr;  // host readback slot for the ICP sums
+    bool auto_sort = false;      // footprint exceeds L2: order queries unless told otherwise
     std::mutex icp_mu;           // serialises users of h_pinned
 };

@@ -186,10 +186,24 @@ __device__ __forceinline__ void rank_points(const float4 (&p)[C], const int32_t 
 // best candidate seen so far either way (a valid upper bound to resume from).
 constexpr uint32_t kNoBudget = 0xFFFFFFFFu;
 
+// Node record i: from the LDS copy of the top levels when i < lds_first.
+__device__ __forceinline__ void fetch_node(const TreeView &t, const float4 *lds, uint32_t lds_first,
+                                           uint32_t i, float4 &A, float4 &B)
+{
+    if (i < lds_first) {
+        A = lds[2 * i];
+        B = lds[2 * i + 1];
+    } else {
+        A = t.nodes[2 * i];
+        B = t.nodes[2 * i + 1];
+    }
+}
+
 template <bool STATS>
 __device__ __forceinline__ bool nn_search(const TreeView &t, float qx, float qy, float qz,
                                           uint32_t budget, uint64_t &key, uint32_t &slot,
-                                          uint32_t &cn, uint32_t &cp)
+                                          uint32_t &cn, uint32_t &cp,
+                                          const float4 *lds = nullptr, uint32_t lds_first = 0)
 {
     key = kNoKey;
     slot = 0;
@@ -199,8 +213,8 @@ __device__ __forceinline__ bool nn_search(const TreeView &t, float qx, float qy,
         // Phase 1: internal nodes, until a leaf or the end of the search.
         while (i < t.first_leaf) {
             if (steps >= budget) return false;
-            const float4 A = t.nodes[2 * i];
-            const float4 B = t.nodes[2 * i + 1];
+            float4 A, B;
+            fetch_node(t, lds, lds_first, i, A, B);
             ++steps;
             if (STATS) ++cn;
             const bool in = enters(box_lb(qx, qy, qz, A, B), key_dist(key));
@@ -451,37 +465,40 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
     }
 }
 
-// ------------------------------------------------- two-pass search (default)
+// ---------------------------------------- persistent search, top levels in LDS
 //
-// Pass 1 gives every query one lane and a budget of kPass1Budget node
-// records; most queries finish, and a wave lasts at most about that many
-// steps.  Pass 2 sweeps all query slots with persistent groups of
-// kPass2Lanes lanes in a fixed order, skips the finished ones and completes
-// the others with the cooperative search, starting from pass 1's best.
-// nn_query keeps an unfinished query's state in its own outputs:
-// idx = -(best index + 3) (so <= -2) and dist2 = best distance so far.
-#ifndef KDNN_PASS1_BUDGET
-#define KDNN_PASS1_BUDGET 64
-#endif
-constexpr uint32_t kPass1Budget = KDNN_PASS1_BUDGET;
-constexpr int kPass2Lanes = 16;
-constexpr int kPass2MaxBlocks = 1024;
+// One work-group of kPWG lanes per CU.  It first copies the node records of
+// the top L levels (heap indices 1 .. 2^L - 1, 32 bytes each, L <= 12 so at
+// most 128 KB) into LDS, then walks a contiguous slice of the (Morton
+// ordered) queries, one lane per query; node fetches above depth L hit LDS
+// instead of L2, which removes most of the descent's memory round trips.
+constexpr int kPWG = 512;
+constexpr int kLdsMaxLevels = 12;
+
+__device__ __forceinline__ void stage_top_levels(const TreeView &t, float4 *lds, uint32_t lds_first)
+{
+    for (uint32_t j = 2 + threadIdx.x; j < 2 * lds_first; j += blockDim.x) lds[j] = t.nodes[j];
+    __syncthreads();
+}
 
 template <bool STATS>
-__global__ __launch_bounds__(kWG) void nn_pass1_kernel(NnArgs a)
+__global__ __launch_bounds__(kPWG) void nn_persist_kernel(NnArgs a, uint32_t lds_first)
 {
-    const uint32_t nb = gridDim.x;
-    const uint32_t blk = xcd_remap(blockIdx.x, nb);
-    for (int64_t k = int64_t(blk) * kWG + threadIdx.x; k < a.m; k += int64_t(nb) * kWG) {
+    extern __shared__ float4 lds_nodes[];
+    stage_top_levels(a.tree, lds_nodes, lds_first);
+    const int64_t chunk = (a.m + gridDim.x - 1) / gridDim.x;
+    const int64_t k0 = int64_t(blockIdx.x) * chunk;
+    const int64_t k1 = k0 + chunk < a.m ? k0 + chunk : a.m;
+    for (int64_t k = k0 + threadIdx.x; k < k1; k += kPWG) {
         const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
         uint64_t key;
         uint32_t slot, cn = 0, cp = 0;
-        const bool done = nn_search<STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2],
-                                           a.budget, key, slot, cn, cp);
+        nn_search<STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2], kNoBudget, key, slot,
+                         cn, cp, lds_nodes, lds_first);
         Best b;
         finish(key, slot, b);
-        a.idx[i] = done ? b.idx : -(int32_t(uint32_t(key)) + 3);
-        a.d2[i] = done ? b.d : key_dist(key);
+        a.idx[i] = b.idx;
+        a.d2[i] = b.d;
         if (STATS) {
             if (a.cnt_nodes) a.cnt_nodes[i] = cn;
             if (a.cnt_pts) a.cnt_pts[i] = cp;
@@ -489,27 +506,149 @@ __global__ __launch_bounds__(kWG) void nn_pass1_kernel(NnArgs a)
     }
 }
 
-template <bool STATS>
-__global__ __launch_bounds__(kWG) void nn_pass2_kernel(NnArgs a)
+// ------------------------------------------------------------ two-pass search
+//
+// Opt-in schedule (a node budget in the flags).  A launch lasts as long as
+// its slowest waves, the ones holding queries that need a wide search.
+// Pass 1 gives every query one lane and a budget of node records; most
+// queries finish.  The slots left unfinished are compacted, per work-group
+// and in lane order, into a list.  Pass 2 hands list entry e to group
+// e mod (number of groups) of kPass2Lanes lanes, which completes the query
+// with the cooperative search starting from pass 1's best.  Every step is a
+// fixed function of the input, so the ICP sums are reproducible.
+// nn_query keeps an unfinished query's state in its own outputs:
+// idx = -(best index + 3) (so <= -2) and dist2 = best distance so far.
+constexpr int kPass2Lanes = 16;
+constexpr int kPass1MaxBlocks = 4096;
+constexpr int kPass2Blocks = 256;
+
+// Rank of this lane among the lanes of the work-group whose flag is set,
+// in lane order; *total = number of flagged lanes.  Whole group must call.
+__device__ __forceinline__ uint32_t block_rank(bool flag, uint32_t *wcount, uint32_t &total)
 {
-    constexpr int G = kPass2Lanes, QPB = kWG / G;
-    const uint32_t nb = gridDim.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t bal = __ballot(flag);
+    const uint32_t in_wave = uint32_t(__popcll(bal & ((uint64_t(1) << lane) - 1u)));
+    if (lane == 0) wcount[w] = uint32_t(__popcll(bal));
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+    for (int ww = 0; ww < kWG / 64; ++ww) {
+        before += ww < w ? wcount[ww] : 0u;
+        total += wcount[ww];
+    }
+    __syncthreads();
+    return before + in_wave;
+}
+
+// pre[0..nb] = exclusive prefix sums of counts[0..nb) (pre[nb] = total).
+__device__ __forceinline__ void load_prefix(const uint32_t *counts, int32_t nb, uint32_t *pre)
+{
+    __shared__ uint32_t wsum[kWG / 64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t carry = 0;
+    for (int32_t b0 = 0; b0 < nb; b0 += kWG) {
+        const int32_t b = b0 + threadIdx.x;
+        const uint32_t v = b < nb ? counts[b] : 0u;
+        uint32_t x = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wsum[w] = x;
+        __syncthreads();
+        uint32_t before = 0, tot = 0;
+        for (int ww = 0; ww < kWG / 64; ++ww) {
+            before += ww < w ? wsum[ww] : 0u;
+            tot += wsum[ww];
+        }
+        if (b < nb) pre[b] = carry + before + x - v;
+        carry += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) pre[nb] = carry;
+    __syncthreads();
+}
+
+// The work-group b holding list entry e: largest b with pre[b] <= e.
+__device__ __forceinline__ int32_t entry_block(const uint32_t *pre, int32_t nb, uint32_t e)
+{
+    int32_t lo = 0, hi = nb - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= e)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+struct TwoPass {
+    int32_t *list;     // [nb1 * cap] slots left by pass 1, per work-group segment
+    uint32_t *counts;  // [nb1]
+    int32_t nb1;       // pass-1 work-groups
+    int32_t cap;       // slots per work-group segment
+};
+
+template <bool STATS>
+__global__ __launch_bounds__(kWG) void nn_pass1_kernel(NnArgs a, TwoPass tp)
+{
+    __shared__ uint32_t wcount[kWG / 64];
+    int32_t *seg = tp.list + int64_t(blockIdx.x) * tp.cap;
+    uint32_t run = 0;
+    const int64_t stride = int64_t(gridDim.x) * kWG;
+    for (int64_t base = int64_t(blockIdx.x) * kWG; base < a.m; base += stride) {
+        const int64_t k = base + threadIdx.x;
+        bool hard = false;
+        if (k < a.m) {
+            const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+            uint64_t key;
+            uint32_t slot, cn = 0, cp = 0;
+            const bool done = nn_search<STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2],
+                                               a.budget, key, slot, cn, cp);
+            Best b;
+            finish(key, slot, b);
+            a.idx[i] = done ? b.idx : -(int32_t(uint32_t(key)) + 3);
+            a.d2[i] = done ? b.d : key_dist(key);
+            if (STATS) {
+                if (a.cnt_nodes) a.cnt_nodes[i] = cn;
+                if (a.cnt_pts) a.cnt_pts[i] = cp;
+            }
+            hard = !done;
+        }
+        uint32_t tot;
+        const uint32_t r = block_rank(hard, wcount, tot);
+        if (hard) seg[run + r] = int32_t(k);
+        run += tot;
+    }
+    if (threadIdx.x == 0) tp.counts[blockIdx.x] = run;
+}
+
+template <bool STATS>
+__global__ __launch_bounds__(kWG) void nn_pass2_kernel(NnArgs a, TwoPass tp)
+{
+    constexpr int G = kPass2Lanes;
+    __shared__ uint32_t pre[kPass1MaxBlocks + 1];
+    load_prefix(tp.counts, tp.nb1, pre);
+    const uint32_t H = pre[tp.nb1];
+    const uint32_t ng = gridDim.x * (kWG / G);
     const int gl = threadIdx.x & (G - 1);
-    for (int64_t base = int64_t(blockIdx.x) * QPB; base < a.m; base += int64_t(nb) * QPB) {
-        const int64_t k = base + threadIdx.x / G;
-        if (k >= a.m) continue;
+    for (uint32_t e = blockIdx.x * (kWG / G) + threadIdx.x / G; e < H; e += ng) {
+        const int32_t b = entry_block(pre, tp.nb1, e);
+        const int64_t k = tp.list[int64_t(b) * tp.cap + (e - pre[b])];
         const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
-        const int32_t e = a.idx[i];
-        if (e > -2) continue;  // finished in pass 1 (the same for the whole group)
-        uint64_t key = nn_key(a.d2[i], uint32_t(-e - 3));
+        const int32_t enc = a.idx[i];
+        uint64_t key = nn_key(a.d2[i], uint32_t(-enc - 3));
         uint32_t slot = 0, cn = 0, cp = 0;
         nn_search_group<G, STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2], true, key,
                                   slot, cn, cp);
         if (gl == 0) {
-            Best b;
-            finish(key, slot, b);
-            a.idx[i] = b.idx;
-            a.d2[i] = b.d;
+            Best bb;
+            finish(key, slot, bb);
+            a.idx[i] = bb.idx;
+            a.d2[i] = bb.d;
             if (STATS) {
                 if (a.cnt_nodes) a.cnt_nodes[i] += cn;
                 if (a.cnt_pts) a.cnt_pts[i] += cp;
@@ -541,7 +680,6 @@ struct IcpArgs {
     uint32_t *ticket;
     double *sums;       // [kS]
     uint32_t budget;    // pass-1 node budget
-    uint32_t *state;    // [n] by traversal slot: 1 = left for pass 2
     uint64_t *pkey;     // [n] pass-1 best key of unfinished slots
     uint32_t *pslot;    // [n] pass-1 best point slot of unfinished slots
     int32_t *idx;
@@ -554,10 +692,11 @@ __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, doub
     return float(((r0 * x + r1 * y) + r2 * z) + tr);
 }
 
-// Sum acc[] over the work-group; thread c < kS of wave 0 gets component c
+// Sum acc[] over a work-group of WG lanes; thread c < kS gets component c
 // in *out (fixed order: lanes by xor butterfly, then waves in order).
-__device__ __forceinline__ void block_sum(double (&acc)[kS], double *red /* LDS [waves][kS] */,
-                                          double *out, int64_t out_stride)
+template <int WG>
+__device__ __forceinline__ void block_sum_n(double (&acc)[kS], double *red /* LDS [waves][kS] */,
+                                            double *out, int64_t out_stride)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -574,9 +713,15 @@ __device__ __forceinline__ void block_sum(double (&acc)[kS], double *red /* LDS 
     __syncthreads();
     if (threadIdx.x < kS) {
         double s = 0.0;
-        for (int ww = 0; ww < kWG / 64; ++ww) s += red[ww * kS + threadIdx.x];
+        for (int ww = 0; ww < WG / 64; ++ww) s += red[ww * kS + threadIdx.x];
         out[threadIdx.x * out_stride] = s;
     }
+}
+
+__device__ __forceinline__ void block_sum(double (&acc)[kS], double *red, double *out,
+                                          int64_t out_stride)
+{
+    block_sum_n<kWG>(acc, red, out, out_stride);
 }
 
 // The query of source point i: q = fl32(R s + t), fp64 with a fixed association.
@@ -614,9 +759,10 @@ __device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, doub
 
 // After this group's partials are written: the last group to finish sums
 // p1[kS][n1] and then p2[kS][n2] in a fixed order into a.sums.
-__device__ __forceinline__ void icp_final_reduce(const IcpArgs &a, double (&acc)[kS], double *red,
-                                                 const double *p1, int32_t n1, const double *p2,
-                                                 int32_t n2)
+template <int WG>
+__device__ __forceinline__ void icp_final_reduce_n(const IcpArgs &a, double (&acc)[kS],
+                                                   double *red, const double *p1, int32_t n1,
+                                                   const double *p2, int32_t n2)
 {
     __shared__ uint32_t is_last;
     __threadfence();
@@ -627,14 +773,21 @@ __device__ __forceinline__ void icp_final_reduce(const IcpArgs &a, double (&acc)
     __threadfence();
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
-    for (int32_t g = threadIdx.x; g < n1 + n2; g += kWG) {
+    for (int32_t g = threadIdx.x; g < n1 + n2; g += WG) {
 #pragma unroll
         for (int c = 0; c < kS; ++c)
             acc[c] += g < n1 ? p1[int64_t(c) * n1 + g] : p2[int64_t(c) * n2 + (g - n1)];
     }
     __syncthreads();  // red[] is reused
-    block_sum(acc, red, a.sums, 1);
+    block_sum_n<WG>(acc, red, a.sums, 1);
     if (threadIdx.x == 0) atomicExch(a.ticket, 0u);
+}
+
+__device__ __forceinline__ void icp_final_reduce(const IcpArgs &a, double (&acc)[kS], double *red,
+                                                 const double *p1, int32_t n1, const double *p2,
+                                                 int32_t n2)
+{
+    icp_final_reduce_n<kWG>(a, acc, red, p1, n1, p2, n2);
 }
 
 // Single pass: G lanes per point, one kernel does everything.
@@ -665,50 +818,65 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
     icp_final_reduce(a, acc, red, a.partials, int32_t(nb), nullptr, 0);
 }
 
-// Two-pass mode, pass 1: one lane per point with a step budget.
-__global__ __launch_bounds__(kWG) void icp_pass1_kernel(IcpArgs a)
+// Two-pass mode, pass 1: one lane per point with a node budget; unfinished
+// slots keep their best so far and are compacted into the pass-2 list.
+__global__ __launch_bounds__(kWG) void icp_pass1_kernel(IcpArgs a, TwoPass tp)
 {
     __shared__ double red[(kWG / 64) * kS];
+    __shared__ uint32_t wcount[kWG / 64];
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
-    const uint32_t nb = gridDim.x;
-    const uint32_t blk = xcd_remap(blockIdx.x, nb);
-    for (int64_t k = int64_t(blk) * kWG + threadIdx.x; k < a.n; k += int64_t(nb) * kWG) {
-        const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
-        double X, Y, Z;
-        float qx, qy, qz;
-        icp_query(a, i, X, Y, Z, qx, qy, qz);
-        uint64_t key;
-        uint32_t slot, cn = 0, cp = 0;
-        const bool done = nn_search<false>(a.tree, qx, qy, qz, a.budget, key, slot, cn, cp);
-        a.state[k] = done ? 0u : 1u;
-        if (done) {
-            Best b;
-            finish(key, slot, b);
-            icp_accumulate(a, i, X, Y, Z, b, acc);
-        } else {
-            a.pkey[k] = key;
-            a.pslot[k] = slot;
+    int32_t *seg = tp.list + int64_t(blockIdx.x) * tp.cap;
+    uint32_t run = 0;
+    const int64_t stride = int64_t(gridDim.x) * kWG;
+    for (int64_t base = int64_t(blockIdx.x) * kWG; base < a.n; base += stride) {
+        const int64_t k = base + threadIdx.x;
+        bool hard = false;
+        if (k < a.n) {
+            const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+            double X, Y, Z;
+            float qx, qy, qz;
+            icp_query(a, i, X, Y, Z, qx, qy, qz);
+            uint64_t key;
+            uint32_t slot, cn = 0, cp = 0;
+            const bool done = nn_search<false>(a.tree, qx, qy, qz, a.budget, key, slot, cn, cp);
+            if (done) {
+                Best b;
+                finish(key, slot, b);
+                icp_accumulate(a, i, X, Y, Z, b, acc);
+            } else {
+                a.pkey[k] = key;
+                a.pslot[k] = slot;
+            }
+            hard = !done;
         }
+        uint32_t tot;
+        const uint32_t r = block_rank(hard, wcount, tot);
+        if (hard) seg[run + r] = int32_t(k);
+        run += tot;
     }
-    block_sum(acc, red, a.partials + blockIdx.x, nb);
+    if (threadIdx.x == 0) tp.counts[blockIdx.x] = run;
+    block_sum(acc, red, a.partials + blockIdx.x, gridDim.x);
 }
 
-// Two-pass mode, pass 2: groups of kPass2Lanes finish the points pass 1 left,
+// Two-pass mode, pass 2: groups of kPass2Lanes complete the listed points,
 // then the last group reduces both passes' partials.
-__global__ __launch_bounds__(kWG) void icp_pass2_kernel(IcpArgs a)
+__global__ __launch_bounds__(kWG) void icp_pass2_kernel(IcpArgs a, TwoPass tp)
 {
-    constexpr int G = kPass2Lanes, QPB = kWG / G;
-    const int gl = threadIdx.x & (G - 1);
+    constexpr int G = kPass2Lanes;
     __shared__ double red[(kWG / 64) * kS];
+    __shared__ uint32_t pre[kPass1MaxBlocks + 1];
+    load_prefix(tp.counts, tp.nb1, pre);
+    const uint32_t H = pre[tp.nb1];
+    const uint32_t ng = gridDim.x * (kWG / G);
+    const int gl = threadIdx.x & (G - 1);
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
-    const uint32_t nb = gridDim.x;
-    for (int64_t base = int64_t(blockIdx.x) * QPB; base < a.n; base += int64_t(nb) * QPB) {
-        const int64_t k = base + threadIdx.x / G;
-        if (k >= a.n || a.state[k] == 0u) continue;  // uniform over the group
+    for (uint32_t e = blockIdx.x * (kWG / G) + threadIdx.x / G; e < H; e += ng) {
+        const int32_t b = entry_block(pre, tp.nb1, e);
+        const int64_t k = tp.list[int64_t(b) * tp.cap + (e - pre[b])];
         const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
         double X, Y, Z;
         float qx, qy, qz;
@@ -717,13 +885,41 @@ __global__ __launch_bounds__(kWG) void icp_pass2_kernel(IcpArgs a)
         uint32_t slot = a.pslot[k], cn = 0, cp = 0;
         nn_search_group<G, false>(a.tree, qx, qy, qz, true, key, slot, cn, cp);
         if (gl == 0) {
-            Best b;
-            finish(key, slot, b);
-            icp_accumulate(a, i, X, Y, Z, b, acc);
+            Best bb;
+            finish(key, slot, bb);
+            icp_accumulate(a, i, X, Y, Z, bb, acc);
         }
     }
-    block_sum(acc, red, a.partials2 + blockIdx.x, nb);
-    icp_final_reduce(a, acc, red, a.partials, a.nb1, a.partials2, int32_t(nb));
+    block_sum(acc, red, a.partials2 + blockIdx.x, gridDim.x);
+    icp_final_reduce(a, acc, red, a.partials, tp.nb1, a.partials2, int32_t(gridDim.x));
+}
+
+// Persistent single-lane correspondence kernel with the top levels in LDS.
+__global__ __launch_bounds__(kPWG) void icp_persist_kernel(IcpArgs a, uint32_t lds_first)
+{
+    extern __shared__ float4 lds_nodes[];
+    __shared__ double red[(kPWG / 64) * kS];
+    stage_top_levels(a.tree, lds_nodes, lds_first);
+    double acc[kS];
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    const int64_t chunk = (a.n + gridDim.x - 1) / gridDim.x;
+    const int64_t k0 = int64_t(blockIdx.x) * chunk;
+    const int64_t k1 = k0 + chunk < a.n ? k0 + chunk : a.n;
+    for (int64_t k = k0 + threadIdx.x; k < k1; k += kPWG) {
+        const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+        double X, Y, Z;
+        float qx, qy, qz;
+        icp_query(a, i, X, Y, Z, qx, qy, qz);
+        uint64_t key;
+        uint32_t slot, cn = 0, cp = 0;
+        nn_search<false>(a.tree, qx, qy, qz, kNoBudget, key, slot, cn, cp, lds_nodes, lds_first);
+        Best b;
+        finish(key, slot, b);
+        icp_accumulate(a, i, X, Y, Z, b, acc);
+    }
+    block_sum_n<kPWG>(acc, red, a.partials + blockIdx.x, gridDim.x);
+    icp_final_reduce_n<kPWG>(a, acc, red, a.partials, int32_t(gridDim.x), nullptr, 0);
 }
 
 // --------------------------------------------------------------- transform
@@ -968,6 +1164,46 @@ SortWorkspace carve_sort_workspace(void *ws, int64_t m)
     return w;
 }
 
+// Pass-1 grid and per-work-group list segment of the two-pass search.
+static void twopass_shape(int64_t m, int32_t &nb1, int32_t &cap)
+{
+    int64_t b = (m + kWG - 1) / kWG;
+    nb1 = int32_t(b < 1 ? 1 : (b > kPass1MaxBlocks ? kPass1MaxBlocks : b));
+    const int64_t sweeps = (m + int64_t(nb1) * kWG - 1) / (int64_t(nb1) * kWG);
+    cap = int32_t((sweeps < 1 ? 1 : sweeps) * kWG);
+}
+
+size_t twopass_bytes(int64_t m)
+{
+    if (m <= 0) return 0;
+    int32_t nb1, cap;
+    twopass_shape(m, nb1, cap);
+    return align256(size_t(nb1) * cap * 4) + align256(size_t(kPass1MaxBlocks) * 4);
+}
+
+static TwoPass carve_twopass(void *p, int64_t m)
+{
+    TwoPass tp{};
+    twopass_shape(m, tp.nb1, tp.cap);
+    char *c = static_cast<char *>(p);
+    tp.list = reinterpret_cast<int32_t *>(c);
+    tp.counts = reinterpret_cast<uint32_t *>(c + align256(size_t(tp.nb1) * tp.cap * 4));
+    return tp;
+}
+
+size_t query_ws_bytes(int64_t m)
+{
+    return m > 0 ? sort_workspace_bytes(m) + twopass_bytes(m) : 0;
+}
+
+QueryWorkspace carve_query_workspace(void *ws, int64_t m)
+{
+    QueryWorkspace w{};
+    w.sort = carve_sort_workspace(ws, m);
+    w.twopass = static_cast<char *>(ws) + sort_workspace_bytes(m);
+    return w;
+}
+
 static int32_t icp_blocks(int64_t n, int G)
 {
     const int64_t b = (n + kWG / G - 1) / (kWG / G);
@@ -979,8 +1215,8 @@ size_t icp_ws_bytes(int64_t n)
     if (n <= 0) return 0;
     const size_t nn = size_t(n);
     return sort_workspace_bytes(n) + align256(size_t(kS) * kIcpMaxBlocks * 8) +
-           align256(size_t(kS) * kPass2MaxBlocks * 8) + align256(size_t(kS) * 8) + 256 +
-           align256(nn * 4) * 2 + align256(nn * 8);
+           align256(size_t(kS) * kPass2Blocks * 8) + align256(size_t(kS) * 8) + 256 +
+           align256(nn * 4) + align256(nn * 8) + twopass_bytes(n);
 }
 
 IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
@@ -992,16 +1228,16 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
     w.partials = reinterpret_cast<double *>(p);
     p += align256(size_t(kS) * kIcpMaxBlocks * 8);
     w.partials2 = reinterpret_cast<double *>(p);
-    p += align256(size_t(kS) * kPass2MaxBlocks * 8);
+    p += align256(size_t(kS) * kPass2Blocks * 8);
     w.sums = reinterpret_cast<double *>(p);
     p += align256(size_t(kS) * 8);
     w.ticket = reinterpret_cast<uint32_t *>(p);
     p += 256;
-    w.state = reinterpret_cast<uint32_t *>(p);
-    p += align256(size_t(n) * 4);
     w.pslot = reinterpret_cast<uint32_t *>(p);
     p += align256(size_t(n) * 4);
     w.pkey = reinterpret_cast<uint64_t *>(p);
+    p += align256(size_t(n) * 8);
+    w.twopass = p;
     w.max_blocks = kIcpMaxBlocks;
     return w;
 }
@@ -1074,31 +1310,62 @@ static void launch_nn_g(const NnArgs &a, bool stats, hipStream_t s)
         nn_kernel<G, false><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
 }
 
-static uint32_t pass2_blocks(int64_t m)
+// Persistent LDS launch shape for this device: one work-group per CU and
+// the deepest L <= min(12, D) whose node records fit the LDS limit.
+struct PersistShape {
+    uint32_t blocks;
+    uint32_t lds_first;  // 2^L
+    size_t lds_bytes;
+};
+
+static bool persist_shape(const TreeView &t, int64_t m, PersistShape &ps)
 {
-    const int64_t b = (m * kPass2Lanes + kWG - 1) / kWG;
-    return uint32_t(b < 1 ? 1 : (b > kPass2MaxBlocks ? kPass2MaxBlocks : b));
+    static int cached_dev = -1;
+    static int cus = 0;
+    static size_t lds_max = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (dev != cached_dev) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+        cus = prop.multiProcessorCount;
+        lds_max = prop.sharedMemPerBlock;
+        cached_dev = dev;
+    }
+    if (m < int64_t(cus) * 64) return false;  // too few queries to amortise the copy
+    int L = t.depth < kLdsMaxLevels ? t.depth : kLdsMaxLevels;
+    while (L > 0 && (size_t(32) << L) + 2048 > lds_max) --L;
+    if (L < 4) return false;
+    ps.lds_first = 1u << L;
+    ps.lds_bytes = size_t(32) << L;
+    ps.blocks = uint32_t(cus);
+    return true;
 }
 
-static void launch_nn_two_pass(const NnArgs &a, bool stats, hipStream_t s)
+template <typename K>
+static void allow_lds(K kernel, size_t bytes)
 {
-    int64_t blocks = (a.m + kWG - 1) / kWG;
-    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
+
+static void launch_nn_two_pass(const NnArgs &a, bool stats, void *twopass, hipStream_t s)
+{
+    const TwoPass tp = carve_twopass(twopass, a.m);
     if (stats) {
-        nn_pass1_kernel<true><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
-        nn_pass2_kernel<true><<<dim3(pass2_blocks(a.m)), kWG, 0, s>>>(a);
+        nn_pass1_kernel<true><<<dim3(uint32_t(tp.nb1)), kWG, 0, s>>>(a, tp);
+        nn_pass2_kernel<true><<<dim3(kPass2Blocks), kWG, 0, s>>>(a, tp);
     } else {
-        nn_pass1_kernel<false><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
-        nn_pass2_kernel<false><<<dim3(pass2_blocks(a.m)), kWG, 0, s>>>(a);
+        nn_pass1_kernel<false><<<dim3(uint32_t(tp.nb1)), kWG, 0, s>>>(a, tp);
+        nn_pass2_kernel<false><<<dim3(kPass2Blocks), kWG, 0, s>>>(a, tp);
     }
 }
 
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     int lanes, uint32_t budget, hipStream_t s)
+                     const Schedule &sc, void *twopass, hipStream_t s)
 {
     NnArgs a{};
-    a.budget = budget;
     a.tree = tree_view(t);
     a.q = q;
     a.m = m;
@@ -1107,10 +1374,20 @@ hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32
     a.d2 = d2;
     a.cnt_nodes = cnt_nodes;
     a.cnt_pts = cnt_pts;
-    if (lanes == 0 && budget != 0) {
-        launch_nn_two_pass(a, stats, s);
+    a.budget = sc.budget;
+    PersistShape ps;
+    if (sc.lanes == 0 && sc.top_lds && persist_shape(a.tree, m, ps)) {
+        if (stats) {
+            allow_lds(nn_persist_kernel<true>, ps.lds_bytes);
+            nn_persist_kernel<true><<<ps.blocks, kPWG, ps.lds_bytes, s>>>(a, ps.lds_first);
+        } else {
+            allow_lds(nn_persist_kernel<false>, ps.lds_bytes);
+            nn_persist_kernel<false><<<ps.blocks, kPWG, ps.lds_bytes, s>>>(a, ps.lds_first);
+        }
+    } else if (sc.lanes == 0 && sc.budget != 0 && twopass) {
+        launch_nn_two_pass(a, stats, twopass, s);
     } else {
-        switch (lanes) {
+        switch (sc.lanes) {
         case 2: launch_nn_g<2>(a, stats, s); break;
         case 4: launch_nn_g<4>(a, stats, s); break;
         case 8: launch_nn_g<8>(a, stats, s); break;
@@ -1134,11 +1411,10 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
 
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
-                            double *sums_out, int32_t *idx, float *d2, int lanes, uint32_t budget,
+                            double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
                             hipStream_t s)
 {
     IcpArgs a{};
-    a.budget = budget;
     a.tree = tree_view(t);
     a.src = src;
     a.n = n;
@@ -1152,24 +1428,28 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     a.partials2 = ws.partials2;
     a.ticket = ws.ticket;
     a.sums = sums_out;
-    a.state = ws.state;
     a.pkey = ws.pkey;
     a.pslot = ws.pslot;
     a.idx = idx;
     a.d2 = d2;
-    if (!(lanes == 0 && budget != 0)) {
-        const dim3 grid(uint32_t(icp_blocks(n, lanes ? lanes : 1)));
-        switch (lanes) {
+    a.budget = sc.budget;
+    PersistShape ps;
+    if (sc.lanes == 0 && sc.top_lds && persist_shape(a.tree, n, ps)) {
+        allow_lds(icp_persist_kernel, ps.lds_bytes);
+        icp_persist_kernel<<<ps.blocks, kPWG, ps.lds_bytes, s>>>(a, ps.lds_first);
+    } else if (sc.lanes == 0 && sc.budget != 0) {
+        const TwoPass tp = carve_twopass(ws.twopass, n);
+        icp_pass1_kernel<<<dim3(uint32_t(tp.nb1)), kWG, 0, s>>>(a, tp);
+        icp_pass2_kernel<<<dim3(kPass2Blocks), kWG, 0, s>>>(a, tp);
+    } else {
+        const dim3 grid(uint32_t(icp_blocks(n, sc.lanes ? sc.lanes : 1)));
+        switch (sc.lanes) {
         case 2: icp_fused_kernel<2><<<grid, kWG, 0, s>>>(a); break;
         case 4: icp_fused_kernel<4><<<grid, kWG, 0, s>>>(a); break;
         case 8: icp_fused_kernel<8><<<grid, kWG, 0, s>>>(a); break;
         case 16: icp_fused_kernel<16><<<grid, kWG, 0, s>>>(a); break;
         default: icp_fused_kernel<1><<<grid, kWG, 0, s>>>(a); break;
         }
-    } else {
-        a.nb1 = icp_blocks(n, 1);
-        icp_pass1_kernel<<<dim3(uint32_t(a.nb1)), kWG, 0, s>>>(a);
-        icp_pass2_kernel<<<dim3(pass2_blocks(n)), kWG, 0, s>>>(a);
     }
     return hipGetLastError();
 }

@@ -23,10 +23,11 @@ pytestmark = pytest.mark.gpu
 
 # search schedules: single pass with g lanes per query, or the default two-pass
 # schedule (tiny budgets push nearly every query into the second pass)
-SCHED = [{}, {"lanes": 4}, {"lanes": 16}, {"budget": 64}, {"budget": 1}, {"budget": 4}]
-SCHED_IDS = ["default", "L4", "L16", "twopass-b64", "twopass-b1", "twopass-b4"]
-SCHED_FEW = [{}, {"budget": 64}, {"budget": 2}]
-SCHED_FEW_IDS = ["default", "twopass-b64", "twopass-b2"]
+SCHED = [{}, {"lanes": 4}, {"lanes": 16}, {"budget": 64}, {"budget": 1}, {"budget": 4},
+         {"top_lds": True}]
+SCHED_IDS = ["default", "L4", "L16", "twopass-b64", "twopass-b1", "twopass-b4", "toplds"]
+SCHED_FEW = [{}, {"budget": 64}, {"budget": 2}, {"top_lds": True}]
+SCHED_FEW_IDS = ["default", "twopass-b64", "twopass-b2", "toplds"]
 
 H_RTOL = 1e-5
 MU_RTOL = 1e-5
@@ -235,7 +236,7 @@ def test_tiny_correspond_reduce_and_icp(torch, kdnn):
     for name, R, t in [("identity", np.eye(3), np.zeros(3)), ("truth", p.R_true, p.t_true)]:
         oi, od, red = _pairs_oracle(p.target, p.source, R, t)
         for f in (0, _lib.lanes_flag(None, 1), _lib.lanes_flag(None, 5), _lib.lanes_flag(1),
-                  _lib.lanes_flag(4) | 2):
+                  _lib.lanes_flag(4) | 2, _lib.KDNN_ICP_SORT, _lib.KDNN_ICP_SORT | _lib.lanes_flag(None, 3)):
             say("tiny correspond_reduce", name, hex(f))
             res = tree.correspond_reduce(src, R, t, return_pairs=True, flags=f)
             assert_nn_equal(res["idx"], res["d2"], oi, od, f"tiny pairs {name} {f:#x}")
@@ -283,7 +284,9 @@ def test_scene_correspond_reduce(torch, kdnn):
         say("scene correspond_reduce iteration", k)
         oi, od, red = _pairs_oracle(p.target, p.source, R, t, otree)
         from kd_tree_nn_amd import _lib
-        for f in (0, _lib.lanes_flag(None, 2), _lib.lanes_flag(1), _lib.lanes_flag(16)):
+        for f in (0, _lib.lanes_flag(None, 2), _lib.lanes_flag(1), _lib.lanes_flag(16),
+                  _lib.lanes_flag(top_lds=True), _lib.KDNN_ICP_SORT, _lib.KDNN_ICP_NO_SORT,
+                  _lib.KDNN_ICP_SORT | _lib.lanes_flag(None, 2)):
             res = tree.correspond_reduce(src, R, t, return_pairs=True, flags=f)
             assert_nn_equal(res["idx"], res["d2"], oi, od, f"scene pairs it{k} flags {f:#x}")
             check_sums(res, red, diag, f"scene sums it{k} flags {f:#x}")
@@ -294,7 +297,8 @@ def test_scene_icp_align(torch, kdnn):
     p = scene()
     _, o = scene_oracle_icp()
     tree = kdnn.Tree(p.target, 16)
-    for sched in SCHED + [{"lanes": 1}, {"sort": False}, {"sort": False, "budget": 3}]:
+    for sched in SCHED + [{"lanes": 1}, {"sort": False}, {"sort": False, "budget": 3},
+                          {"sort": True}, {"sort": True, "budget": 3}]:
         say("scene icp_align 30", sched)
         g = tree.icp(dev(torch, p.source), max_iter=p.iters, **sched)
         assert g["iters"] == p.iters
@@ -344,6 +348,30 @@ def test_workspace_checks(torch, kdnn):
         tree.correspond_reduce(src, np.eye(3), np.zeros(3), workspace=small)
     with pytest.raises(kdnn.KdnnError, match="EINVAL"):
         tree.query(src, workspace=small)
+    from kd_tree_nn_amd import _lib
+    with pytest.raises(kdnn.KdnnError, match="EINVAL"):
+        tree.correspond_reduce(src, np.eye(3), np.zeros(3),
+                               flags=_lib.KDNN_ICP_SORT | _lib.KDNN_ICP_NO_SORT)
+    m = src.shape[0]
+    idx = torch.empty(m, dtype=torch.int32, device="cuda")
+    d2 = torch.empty(m, dtype=torch.float32, device="cuda")
+    ws = tree.query_workspace(m)
+    L = _lib.lib()
+    args = (tree._h, src.data_ptr(), m, idx.data_ptr(), d2.data_ptr())
+    # the ordering and the two-pass schedule need a workspace; conflicting
+    # order flags are rejected
+    assert L.nn_query(*args, _lib.KDNN_QUERY_SORT, None, 0, None) == _lib.KDNN_EINVAL
+    assert L.nn_query(*args, _lib.KDNN_QUERY_SORT | _lib.KDNN_QUERY_NO_SORT, ws.data_ptr(),
+                      ws.numel(), None) == _lib.KDNN_EINVAL
+    assert L.nn_query(*args, _lib.lanes_flag(None, 8), None, 0, None) == _lib.KDNN_EINVAL
+    # automatic mode without a workspace: single pass in the given order
+    assert L.nn_query(*args, 0, None, 0, None) == _lib.KDNN_OK
+    for bad in (_lib.lanes_flag(4, 8), _lib.lanes_flag(1, None, True), _lib.lanes_flag(None, 8, True),
+                _lib.lanes_flag(3)):
+        assert L.nn_query(*args, bad, ws.data_ptr(), ws.numel(), None) == _lib.KDNN_EINVAL
+    torch.cuda.synchronize()
+    ri, rd = tree.query(src, sort=True)
+    assert torch.equal(idx, ri) and torch.equal(d2.view(torch.int32), rd.view(torch.int32))
 
 
 @functools.lru_cache(maxsize=None)
