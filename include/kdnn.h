@@ -124,8 +124,10 @@ typedef struct kdnn_icp_sums {
  *   params   : NULL = defaults (leaf 16, no depth cap, max-variance axis).
  *   out      : receives the handle; unchanged on failure.
  * Every node above depth D = min{d : ceil(n / 2^d) <= leaf_size} (or
- * max_depth) is split at its index median, so all leaves sit at depth D and
- * hold floor(n/2^D) or ceil(n/2^D) points.
+ * max_depth) is split, so all leaves sit at depth D.  Node a of depth d owns
+ * the leaf-order slots [floor(a n / 2^d), floor((a+1) n / 2^d)) and splits at
+ * slot floor((2a+1) n / 2^(d+1)), a median of its range; leaves hold
+ * floor(n/2^D) or ceil(n/2^D) points.
  * Errors: EINVAL (n < 1, n >= 2^31, leaf_size or max_depth out of range,
  * NULL pointers, D > 28), ENONFINITE (NaN/Inf coordinate), ENOMEM, EDEVICE. */
 kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_params *params,
