@@ -228,6 +228,13 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         free_tree(t);
         return fail(KDNN_ENOMEM, std::string("kdtree_build: hipHostMalloc: ") + hipGetErrorString(e));
     }
+    // The fused kernel of the synchronous ICP calls writes its sums straight
+    // into this slot (no separate copy launch per iteration).
+    if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&t->d_pinned), t->h_pinned, 0)) !=
+        hipSuccess) {
+        free_tree(t);
+        return hip_fail(e, "kdtree_build: hipHostGetDevicePointer");
+    }
     if ((e = hipMemcpy(t->d_nodes, ht.nodes.data(), nb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess) {
         free_tree(t);
@@ -406,13 +413,11 @@ kdnn_status icp_correspond_reduce(const kdnn_tree *tree, const float *src_dev, i
     kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
     std::lock_guard<std::mutex> lock(mt->icp_mu);
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
-    st = icp_enqueue(tree, src_dev, n, R_host, t_host, w.sums, idx_dev, dist2_dev,
+    st = icp_enqueue(tree, src_dev, n, R_host, t_host, mt->d_pinned, idx_dev, dist2_dev,
                      icp_resolve_sort(tree, flags), w, stream);
     if (st != KDNN_OK) return st;
-    hipError_t e = hipMemcpyAsync(mt->h_pinned, w.sums, KDNN_SUMS_DOUBLES * sizeof(double),
-                                  hipMemcpyDeviceToHost, stream);
-    if (e != hipSuccess) return hip_fail(e, "icp: readback");
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "icp: synchronize");
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "icp: synchronize");
     to_sums(mt->h_pinned, tree->dev.center, out_host);
     return KDNN_OK;
     KDNN_GUARD_END
@@ -465,12 +470,10 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
             std::memcpy(Rt_hist + 12 * k + 9, t, sizeof t);
         }
         const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
-        st = icp_enqueue(tree, src_dev, n, R, t, w.sums, nullptr, nullptr, f, w, stream);
+        st = icp_enqueue(tree, src_dev, n, R, t, mt->d_pinned, nullptr, nullptr, f, w, stream);
         if (st != KDNN_OK) return st;
-        hipError_t e = hipMemcpyAsync(mt->h_pinned, w.sums, KDNN_SUMS_DOUBLES * sizeof(double),
-                                      hipMemcpyDeviceToHost, stream);
-        if (e != hipSuccess) return hip_fail(e, "icp_align: readback");
-        if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "icp_align: synchronize");
+        hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "icp_align: synchronize");
         kdnn_icp_sums sums;
         to_sums(mt->h_pinned, tree->dev.center, &sums);
         if (E_hist) E_hist[k] = sums.sum_d2;
