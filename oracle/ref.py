@@ -206,6 +206,55 @@ def solve_rigid(red: dict, method: str = "horn"):
 
 
 # ---------------------------------------------------------------------------
+# O8: correspondence rejection (§4.4)
+# ---------------------------------------------------------------------------
+def max_dist_bound(max_dist) -> np.float32:
+    """The fp32 squared-distance bound of a distance threshold (§4.4, first way).
+
+    Pairs whose fp32 squared distance exceeds fl32(max_dist * max_dist) (the
+    product in float64, one rounding) are dropped.  None, <= 0 or non-finite
+    means no threshold (+inf).
+    """
+    if max_dist is None or not np.isfinite(max_dist) or max_dist <= 0:
+        return np.float32(np.inf)
+    md = float(max_dist)
+    return np.float32(md * md)
+
+
+def residual_sq(src, matched, R, t) -> np.ndarray:
+    """r_i^2 = ||R s_i + t - m_i||^2 in float64 (§4.4, second way: residuals
+    after the solve).
+
+    Per axis e_a = (((R_a0 x + R_a1 y) + R_a2 z) + t_a) - m_a, every product and
+    sum a separate float64 operation (the moved point is not rounded to
+    float32), then r^2 = (e_0 e_0 + e_1 e_1) + e_2 e_2.
+    """
+    S = np.asarray(src, np.float32).reshape(-1, 3).astype(np.float64)
+    M = np.asarray(matched, np.float32).reshape(-1, 3).astype(np.float64)
+    R = np.asarray(R, np.float64).reshape(3, 3)
+    t = np.asarray(t, np.float64).reshape(3)
+    e = np.empty_like(S)
+    for a in range(3):
+        e[:, a] = (((R[a, 0] * S[:, 0] + R[a, 1] * S[:, 1]) + R[a, 2] * S[:, 2]) + t[a]) - M[:, a]
+    return (e[:, 0] * e[:, 0] + e[:, 1] * e[:, 1]) + e[:, 2] * e[:, 2]
+
+
+def reject_sigma(src, matched, R, t, k: float):
+    """§4.4 residual rejection with the 3-sigma rule (k = 3).
+
+    Residuals are taken under the first solve (R, t).  sigma^2 is the mean
+    squared residual over the pairs (the residual vectors of a least-squares
+    fit have zero mean, so this is their variance); a pair is kept iff
+    r_i^2 <= (k * k) * sigma^2.  Returns (keep mask, sigma^2, threshold).
+    """
+    r2 = residual_sq(src, matched, R, t)
+    n = len(r2)
+    sigma2 = float(r2.sum()) / n if n else 0.0
+    thr = (float(k) * float(k)) * sigma2
+    return r2 <= thr, sigma2, thr
+
+
+# ---------------------------------------------------------------------------
 # O6: the ICP iteration
 # ---------------------------------------------------------------------------
 def mse_converged(E_hist, n_hist, eps: float) -> bool:
@@ -218,15 +267,20 @@ def mse_converged(E_hist, n_hist, eps: float) -> bool:
 
 
 def icp(target, source, iters: int, R0=None, t0=None, leaf_size: int = 8,
-        eps: float = 0.0, nn: str = "kd", tree: Optional[KDTree] = None) -> dict:
-    """ICP as the article describes it (§2.1, §3.3).
+        eps: float = 0.0, nn: str = "kd", tree: Optional[KDTree] = None,
+        max_dist=None, reject_k: float = 0.0) -> dict:
+    """ICP as the article describes it (§2.1, §3.3), with the optional
+    correspondence rejection of §4.4.
 
     Each iteration k: q = transform(original source; R_k, t_k); find every
-    q's nearest target point; E_k = sum of squared distances; solve the rigid
-    (R_{k+1}, t_{k+1}) mapping original source points onto their matches.
-    Stops after ``iters`` iterations, or earlier under :func:`mse_converged`.
-    Source points whose query has no match (idx = -1, non-finite) are dropped
-    from the pairs.
+    q's nearest target point; drop pairs beyond ``max_dist``
+    (:func:`max_dist_bound`); E_k = sum of the kept squared distances; solve
+    the rigid motion mapping original source points onto their matches.  With
+    ``reject_k`` > 0, the pairs are then filtered by :func:`reject_sigma`
+    under that first solve and the motion is solved again from the pairs
+    left (§4.4, the two ways combined).  Stops after ``iters`` iterations, or
+    earlier under :func:`mse_converged`.  Source points whose query has no
+    match (idx = -1, non-finite) are dropped from the pairs.
     """
     T = _pts(target)
     S = _pts(source)
@@ -235,22 +289,28 @@ def icp(target, source, iters: int, R0=None, t0=None, leaf_size: int = 8,
     if nn == "kd" and tree is None:
         tree = KDTree(T, leaf_size)
     find = tree.query if nn == "kd" else (lambda q: brute_nn(T, q))
-    E_hist, n_hist, Rt_hist = [], [], []
+    tau = max_dist_bound(max_dist)
+    E_hist, n_hist, Rt_hist, kept_hist = [], [], [], []
     done = 0
     for _ in range(iters):
         Rt_hist.append(np.concatenate([R.ravel(), t]))
         q = transform(S, R, t)
         idx, d2 = find(q)
-        ok = idx >= 0
-        red = reduce_pairs(S[ok], T[idx[ok]], d2[ok])
+        ok = (idx >= 0) & (d2 <= tau)
+        Sp, Mp, dp = S[ok], T[idx[ok]], d2[ok]
+        red = reduce_pairs(Sp, Mp, dp)
         E_hist.append(red["E"])
         n_hist.append(red["n"])
         R, t = solve_rigid(red)
+        if reject_k > 0:
+            keep, _, _ = reject_sigma(Sp, Mp, R, t, reject_k)
+            R, t = solve_rigid(reduce_pairs(Sp[keep], Mp[keep], dp[keep]))
+            kept_hist.append(int(keep.sum()))
         done += 1
         if mse_converged(E_hist, n_hist, eps):
             break
     return {"R": R, "t": t, "E": np.array(E_hist), "n": np.array(n_hist),
-            "Rt_hist": np.array(Rt_hist), "iters": done}
+            "Rt_hist": np.array(Rt_hist), "iters": done, "kept": np.array(kept_hist)}
 
 
 # ---------------------------------------------------------------------------
