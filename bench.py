@@ -219,6 +219,25 @@ def main():
     iters_per_s = args.steps * ITERS / T
     log(f"{value / 1e9:.3f} G queries/s, {iters_per_s:.0f} ICP iterations/s")
 
+    # ---------------------------------- the same registration with rejection
+    # (article §4.4: max_dist fused into the search, then 3-sigma residual
+    # rejection and a second solve per iteration)
+    REJ = {"max_dist": 1.0, "reject_k": 3.0}
+    for _ in range(2):
+        tree.icp(src, max_iter=ITERS, workspace=ws, **REJ)
+    torch.cuda.synchronize()
+    rsteps = max(args.steps // 2, 1)
+    t0 = time.perf_counter()
+    for _ in range(rsteps):
+        gr = tree.icp(src, max_iter=ITERS, workspace=ws, **REJ)
+    torch.cuda.synchronize()
+    Tr = time.perf_counter() - t0
+    rej = {"max_dist_m": REJ["max_dist"], "reject_k": REJ["reject_k"], "steps": rsteps,
+           "icp_iters_per_s": round(rsteps * ITERS / Tr, 1),
+           "icp_iter_us": round(Tr / (rsteps * ITERS) * 1e6, 2),
+           "queries_per_s": round(rsteps * ITERS * n / Tr)}
+    log(f"with rejection: {rej['icp_iters_per_s']:.0f} ICP iterations/s")
+
     # ------------------------------------------- fused kernel: events per launch
     # The library launches on torch's current stream; the events bracket each
     # launch on that stream.  A spin kernel queued ahead of every 30 launches
@@ -313,6 +332,7 @@ def main():
             "step": "one 30-iteration ICP registration, tree and clouds resident",
         },
         "icp_iters_per_s": round(iters_per_s, 1),
+        "icp_with_rejection": rej,
         "icp_iter_us": round(T / (args.steps * ITERS) * 1e6, 2),
         "build": {"host_build_ms": round(info["build_ms"], 3),
                   "upload_ms": round(info["upload_ms"], 3),

@@ -207,6 +207,17 @@ kdnn_status nn_query(const kdnn_tree *tree, const float *q_dev, int64_t m, int32
                      float *dist2_dev, uint32_t flags, void *ws_dev, size_t ws_bytes,
                      hipStream_t stream);
 
+/* nn_query restricted to target points within max_dist (article §4.4: the
+ * distance threshold applied at correspondence time, fused into the search,
+ * where it also serves as the initial pruning bound).  The result is the
+ * lowest-index nearest point among those whose fp32 squared distance is
+ * <= fl32(max_dist * max_dist) (product in fp64, one rounding), else
+ * (idx -1, dist2 +inf).  max_dist <= 0 or +inf: no bound (as nn_query).
+ * Arguments and errors as nn_query; EINVAL also for a NaN max_dist. */
+kdnn_status nn_query_radius(const kdnn_tree *tree, const float *q_dev, int64_t m, double max_dist,
+                            int32_t *idx_dev, float *dist2_dev, uint32_t flags, void *ws_dev,
+                            size_t ws_bytes, hipStream_t stream);
+
 /* Instrumented nn_query: same traversal, same results, and per query the
  * number of tree nodes loaded and of leaf points scanned (uint32 each, may be
  * NULL).  For measurement only; slower than nn_query. */
@@ -235,6 +246,21 @@ kdnn_status transform_points(const float *in_dev, float *out_dev, int64_t n, con
 /* Neither NO_SORT nor SORT: Morton order when the tree's device footprint
  * exceeds the device's L2 cache (as for nn_query). */
 
+/* Correspondence rejection (article §4.4, both ways combined).
+ *   max_dist : finite and > 0: a pair takes part only if its fp32 squared
+ *              distance is <= fl32(max_dist * max_dist); the search itself is
+ *              bounded by it (as nn_query_radius).  Otherwise no threshold.
+ *   reject_k : > 0: after the rigid solve (R1, t1) of an iteration, residuals
+ *              r_i^2 = ||R1 s_i + t1 - m_i||^2 are taken in fp64 over the
+ *              pairs (the moved point not rounded), sigma^2 = mean r_i^2, and
+ *              only pairs with r_i^2 <= (k k) sigma^2 enter a second solve
+ *              (k = 3: the 3-sigma rule).  0: off.  Must be finite, >= 0.
+ * A NULL pointer means neither. */
+typedef struct {
+    double max_dist;
+    double reject_k;
+} kdnn_icp_reject;
+
 /* Bytes of device workspace the ICP entry points need for n source points. */
 size_t icp_workspace_bytes(int64_t n);
 
@@ -248,14 +274,17 @@ size_t icp_workspace_bytes(int64_t n);
  *   R_host, t_host : current transform (host, read during the call).
  *   out_host   : receives the sums.
  *   idx_dev, dist2_dev : optional per-point correspondences (NULL = skip).
+ *   reject     : optional; max_dist drops far pairs (idx -1 in idx_dev).  With
+ *                reject_k > 0 the matches are also kept in ws for a following
+ *                icp_reject_reduce.
  *   ws_dev     : >= icp_workspace_bytes(n) bytes, 256-byte aligned.
  * Synchronises stream.  Calls sharing one ws must not overlap.
  * Errors: EINVAL, EDEVICE. */
 kdnn_status icp_correspond_reduce(const kdnn_tree *tree, const float *src_dev, int64_t n,
                                   const double *R_host, const double *t_host,
                                   kdnn_icp_sums *out_host, int32_t *idx_dev, float *dist2_dev,
-                                  uint32_t flags, void *ws_dev, size_t ws_bytes,
-                                  hipStream_t stream);
+                                  uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /* As icp_correspond_reduce but asynchronous: the KDNN_SUMS_DOUBLES sums are
  * written to sums_dev (device, 8-byte aligned) when the stream reaches the
@@ -263,8 +292,25 @@ kdnn_status icp_correspond_reduce(const kdnn_tree *tree, const float *src_dev, i
 kdnn_status icp_correspond_reduce_async(const kdnn_tree *tree, const float *src_dev, int64_t n,
                                         const double *R_host, const double *t_host,
                                         double *sums_dev, int32_t *idx_dev, float *dist2_dev,
-                                        uint32_t flags, void *ws_dev, size_t ws_bytes,
-                                        hipStream_t stream);
+                                        uint32_t flags, const kdnn_icp_reject *reject,
+                                        void *ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* The residual rejection step of kdnn_icp_reject.reject_k (article §4.4,
+ * second way; 3-sigma rule for reject_k = 3) on the matches that the last
+ * icp_correspond_reduce(_async) call with reject_k > 0 kept in ws (same src,
+ * n, stream-ordered before this call): residuals under (R_host, t_host) --
+ * normally the solve of that call's sums -- then the sums of the pairs with
+ * r_i^2 <= (reject_k^2) * mean r_i^2.  sum_d2 is the kept pairs' match
+ * distances.
+ *   out_host   : the kept pairs' sums.   sigma2_out : optional, mean r_i^2.
+ *   kept_dev   : optional n uint8 out, 1 where the pair is kept.
+ * A ws without such matches gives unspecified sums (the stored slots are
+ * bounds-checked, so it is safe).  Synchronises stream.
+ * Errors: EINVAL (also reject_k <= 0 or non-finite), EDEVICE. */
+kdnn_status icp_reject_reduce(const kdnn_tree *tree, const float *src_dev, int64_t n,
+                              const double *R_host, const double *t_host, double reject_k,
+                              kdnn_icp_sums *out_host, double *sigma2_out, uint8_t *kept_dev,
+                              void *ws_dev, size_t ws_bytes, hipStream_t stream);
 
 /* Rigid solve from correspondence sums (article §2.1): centroids, H, its 3x3
  * SVD H = U S V^T, R = V diag(1, 1, d) U^T with d = sign det(V U^T) so that R
@@ -284,13 +330,18 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  *                  iteration k.
  *   iters_done   : optional, iterations completed.
  *   flags        : KDNN_ICP_NO_SORT or KDNN_ICP_SORT, and the schedule flags.
+ *   reject       : optional correspondence rejection (kdnn_icp_reject): the
+ *                  pairs of iteration k are those within max_dist, E_k and
+ *                  n_k count them; with reject_k > 0 each iteration solves,
+ *                  rejects by residual (icp_reject_reduce) and solves again.
  * The traversal order is computed once, from the source moved by (R0, t0).
  * On EDEGENERATE the outputs hold the last good transform.
  * Errors: EINVAL, EDEVICE, EDEGENERATE. */
 kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, const double *R0_host,
                       const double *t0_host, int32_t max_iter, double eps, double *R_out,
                       double *t_out, double *E_hist, double *Rt_hist, int32_t *iters_done,
-                      uint32_t flags, void *ws_dev, size_t ws_bytes, hipStream_t stream);
+                      uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
+                      size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- misc */
 

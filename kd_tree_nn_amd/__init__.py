@@ -74,6 +74,14 @@ def _mat(R, shape, name):
     return a, a.ctypes.data_as(_lib.c_dp)
 
 
+def _reject(max_dist, reject_k):
+    """kdnn_icp_reject pointer, or NULL when neither rejection is asked for."""
+    if max_dist is None and not reject_k:
+        return None
+    md = float("inf") if max_dist is None else float(max_dist)
+    return ctypes.byref(_lib.IcpReject(md, float(reject_k or 0.0)))
+
+
 def _params(leaf_size, max_depth, round_robin):
     return _lib.BuildParams(int(leaf_size), int(max_depth),
                             _lib.KDNN_BUILD_ROUND_ROBIN if round_robin else 0)
@@ -134,13 +142,14 @@ class Tree:
                            device=self.device)
 
     def query(self, q, sort=None, out=None, workspace=None, stream=None, lanes=None,
-              budget=None, top_lds: bool = False):
+              budget=None, top_lds: bool = False, max_dist=None):
         """(idx int32[m], dist2 float32[m]) of the exact nearest target point.
 
         sort: Morton-order the queries (None = the library's choice by tree size).
         lanes: single pass with this many lanes per query (1, 2, 4, 8, 16);
         budget: two-pass schedule with this first-pass node budget;
         top_lds: single lane with the top tree levels staged in LDS.
+        max_dist: only target points within this distance (else idx -1, +inf).
         """
         torch = _torch()
         q = _dev_points(q, "queries")
@@ -151,11 +160,16 @@ class Tree:
         ws = None
         if m > 0:
             ws = workspace if workspace is not None else self.query_workspace(m)
-        _lib.check(_lib.lib().nn_query(
-            self._h, _ptr(q), m, _ptr(idx), _ptr(d2),
-            _lib.sort_flag(sort, KDNN_QUERY_SORT, KDNN_QUERY_NO_SORT)
-            | _lib.lanes_flag(lanes, budget, top_lds),
-            _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)), "nn_query")
+        flags = (_lib.sort_flag(sort, KDNN_QUERY_SORT, KDNN_QUERY_NO_SORT)
+                 | _lib.lanes_flag(lanes, budget, top_lds))
+        wp, wn = _ptr(ws), ws.numel() if ws is not None else 0
+        if max_dist is None:
+            _lib.check(_lib.lib().nn_query(self._h, _ptr(q), m, _ptr(idx), _ptr(d2), flags,
+                                           wp, wn, _stream(stream)), "nn_query")
+        else:
+            _lib.check(_lib.lib().nn_query_radius(self._h, _ptr(q), m, float(max_dist), _ptr(idx),
+                                                  _ptr(d2), flags, wp, wn, _stream(stream)),
+                       "nn_query_radius")
         return idx, d2
 
     def query_stats(self, q, sort=None, lanes=None, budget=None, top_lds: bool = False):
@@ -181,8 +195,13 @@ class Tree:
                            device=self.device)
 
     def correspond_reduce(self, src, R=None, t=None, return_pairs: bool = False,
-                          flags: int = 0, workspace=None, stream=None) -> dict:
-        """Sums of one ICP correspondence step at (R, t); optionally the pairs."""
+                          flags: int = 0, workspace=None, stream=None, max_dist=None,
+                          reject_k: float = 0.0) -> dict:
+        """Sums of one ICP correspondence step at (R, t); optionally the pairs.
+
+        max_dist drops pairs farther than it; reject_k > 0 also keeps the
+        matches in the workspace for a following :meth:`reject_reduce`.
+        """
         torch = _torch()
         src = _dev_points(src, "src")
         n = src.shape[0]
@@ -196,30 +215,56 @@ class Tree:
         s = _lib.IcpSums()
         _lib.check(_lib.lib().icp_correspond_reduce(
             self._h, _ptr(src), n, Rp, tp, ctypes.byref(s), _ptr(idx), _ptr(d2), int(flags),
-            _ptr(ws), ws.numel(), _stream(stream)), "icp_correspond_reduce")
+            _reject(max_dist, reject_k), _ptr(ws), ws.numel(), _stream(stream)),
+            "icp_correspond_reduce")
         out = sums_to_dict(s)
         if return_pairs:
             out["idx"], out["d2"] = idx, d2
         return out
 
     def correspond_reduce_async(self, src, R, t, sums_out, workspace, flags: int = 0,
-                                idx=None, d2=None, stream=None):
+                                idx=None, d2=None, stream=None, max_dist=None,
+                                reject_k: float = 0.0):
         """Enqueue one correspondence step; KDNN_SUMS_DOUBLES float64 sums go to sums_out."""
         torch = _torch()
         src = _dev_points(src, "src")
         if sums_out.dtype != torch.float64 or sums_out.numel() < KDNN_SUMS_DOUBLES:
             raise ValueError("sums_out must be float64 with >= 17 elements")
-        _, Rp = _mat(R, (3, 3), "R")
-        _, tp = _mat(t, (3,), "t")
+        Ra, Rp = _mat(R, (3, 3), "R")
+        ta, tp = _mat(t, (3,), "t")
         _lib.check(_lib.lib().icp_correspond_reduce_async(
             self._h, _ptr(src), src.shape[0], Rp, tp, _ptr(sums_out), _ptr(idx), _ptr(d2),
-            int(flags), _ptr(workspace), workspace.numel(), _stream(stream)),
-            "icp_correspond_reduce_async")
+            int(flags), _reject(max_dist, reject_k), _ptr(workspace), workspace.numel(),
+            _stream(stream)), "icp_correspond_reduce_async")
+
+    def reject_reduce(self, src, R, t, reject_k: float, workspace, return_kept: bool = False,
+                      stream=None) -> dict:
+        """Residual rejection of the matches a previous :meth:`correspond_reduce`
+        (with reject_k > 0, same workspace) kept: sums of the pairs whose
+        residual under (R, t) is within reject_k sigma, plus sigma^2."""
+        torch = _torch()
+        src = _dev_points(src, "src")
+        n = src.shape[0]
+        Ra, Rp = _mat(R, (3, 3), "R")
+        ta, tp = _mat(t, (3,), "t")
+        kept = torch.empty(n, dtype=torch.uint8, device=src.device) if return_kept else None
+        s = _lib.IcpSums()
+        sigma2 = ctypes.c_double(0.0)
+        _lib.check(_lib.lib().icp_reject_reduce(
+            self._h, _ptr(src), n, Rp, tp, float(reject_k), ctypes.byref(s),
+            ctypes.byref(sigma2), _ptr(kept), _ptr(workspace), workspace.numel(),
+            _stream(stream)), "icp_reject_reduce")
+        out = sums_to_dict(s)
+        out["sigma2"] = sigma2.value
+        if return_kept:
+            out["kept"] = kept
+        return out
 
     def icp(self, src, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
             workspace=None, stream=None, lanes=None, sort=None, budget=None,
-            top_lds: bool = False) -> dict:
-        """ICP registration of the source (device, original coordinates) onto the tree."""
+            top_lds: bool = False, max_dist=None, reject_k: float = 0.0) -> dict:
+        """ICP registration of the source (device, original coordinates) onto the
+        tree; max_dist / reject_k: correspondence rejection (kdnn_icp_reject)."""
         src = _dev_points(src, "src")
         n = src.shape[0]
         R0a = None if R0 is None else _mat(R0, (3, 3), "R0")
@@ -236,7 +281,7 @@ class Tree:
             R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
             E.ctypes.data_as(_lib.c_dp), Rt.ctypes.data_as(_lib.c_dp), ctypes.byref(it),
             _lib.sort_flag(sort, KDNN_ICP_SORT, KDNN_ICP_NO_SORT)
-            | _lib.lanes_flag(lanes, budget, top_lds),
+            | _lib.lanes_flag(lanes, budget, top_lds), _reject(max_dist, reject_k),
             _ptr(ws), ws.numel(), _stream(stream)), "icp_align")
         k = it.value
         return {"R": R.reshape(3, 3), "t": t, "E": E[:k], "Rt_hist": Rt[:k], "iters": k}
@@ -250,8 +295,8 @@ def transform(x, R, t, out=None, stream=None):
         out = torch.empty_like(x)
     else:
         out = _dev_points(out, "out")
-    _, Rp = _mat(R, (3, 3), "R")
-    _, tp = _mat(t, (3,), "t")
+    Ra, Rp = _mat(R, (3, 3), "R")
+    ta, tp = _mat(t, (3,), "t")
     _lib.check(_lib.lib().transform_points(_ptr(x), _ptr(out), x.shape[0], Rp, tp,
                                            _stream(stream)), "transform_points")
     return out

@@ -50,6 +50,10 @@ class TreeInfo(ctypes.Structure):
                 ("l2_bytes", c_i64), ("auto_sort", c_i32)]
 
 
+class IcpReject(ctypes.Structure):
+    _fields_ = [("max_dist", ctypes.c_double), ("reject_k", ctypes.c_double)]
+
+
 class IcpSums(ctypes.Structure):
     _fields_ = [("n", c_i64), ("c", ctypes.c_double * 3), ("sum_s", ctypes.c_double * 3),
                 ("sum_m", ctypes.c_double * 3), ("sum_sm", ctypes.c_double * 9),
@@ -66,16 +70,22 @@ SIGNATURES = {
     "kdtree_build_host": (c_i32, [c_vp, c_i64, ctypes.POINTER(BuildParams), c_vp, c_vp]),
     "nn_query_workspace_bytes": (c_sz, [c_i64]),
     "nn_query": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_u32, c_vp, c_sz, c_vp]),
+    "nn_query_radius": (c_i32, [c_vp, c_vp, c_i64, ctypes.c_double, c_vp, c_vp, c_u32, c_vp, c_sz,
+                                c_vp]),
     "nn_query_stats": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_u32, c_vp, c_sz, c_vp]),
     "transform_points": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, c_vp]),
     "icp_workspace_bytes": (c_sz, [c_i64]),
     "icp_correspond_reduce": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, ctypes.POINTER(IcpSums),
-                                      c_vp, c_vp, c_u32, c_vp, c_sz, c_vp]),
+                                      c_vp, c_vp, c_u32, ctypes.POINTER(IcpReject), c_vp, c_sz,
+                                      c_vp]),
     "icp_correspond_reduce_async": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, c_vp, c_vp, c_vp,
-                                            c_u32, c_vp, c_sz, c_vp]),
+                                            c_u32, ctypes.POINTER(IcpReject), c_vp, c_sz, c_vp]),
+    "icp_reject_reduce": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, ctypes.c_double,
+                                  ctypes.POINTER(IcpSums), c_dp, c_vp, c_vp, c_sz, c_vp]),
     "kdnn_procrustes": (c_i32, [ctypes.POINTER(IcpSums), c_dp, c_dp]),
     "icp_align": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, c_i32, ctypes.c_double, c_dp, c_dp,
-                          c_dp, c_dp, ctypes.POINTER(c_i32), c_u32, c_vp, c_sz, c_vp]),
+                          c_dp, c_dp, ctypes.POINTER(c_i32), c_u32, ctypes.POINTER(IcpReject),
+                          c_vp, c_sz, c_vp]),
     "kdnn_last_error": (ctypes.c_char_p, []),
     "kdnn_version": (c_i32, []),
 }

@@ -124,11 +124,28 @@ uint32_t icp_resolve_sort(const kdnn_tree *tree, uint32_t flags)
     return sort ? flags : (flags | KDNN_ICP_NO_SORT);
 }
 
+// The fp32 squared-distance bound of a distance threshold: fl32(max_dist^2)
+// (product in fp64, one rounding); no bound unless max_dist is finite and > 0.
+float bound_of(double max_dist)
+{
+    return (max_dist > 0.0 && std::isfinite(max_dist)) ? float(max_dist * max_dist) : INFINITY;
+}
+
+kdnn_status check_reject(const kdnn_icp_reject *r, const char *where)
+{
+    if (r && !(r->reject_k >= 0.0 && std::isfinite(r->reject_k)))
+        return fail(KDNN_EINVAL, std::string(where) + ": reject_k must be finite and >= 0");
+    return KDNN_OK;
+}
+
 // Enqueue the traversal order (per flags) and the fused kernel.
 kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, const double *R,
                         const double *t, double *sums_dev, int32_t *idx, float *d2,
-                        uint32_t flags, const IcpWorkspace &w, hipStream_t s)
+                        uint32_t flags, const kdnn_icp_reject *rej, const IcpWorkspace &w,
+                        hipStream_t s)
 {
+    const float bound2 = rej ? bound_of(rej->max_dist) : INFINITY;
+    const bool keep = rej && rej->reject_k > 0.0;
     const int32_t *perm = nullptr;
     hipError_t e = hipSuccess;
     // Every fused launch leaves the ticket at zero; a workspace coming from a
@@ -143,7 +160,8 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
         e = launch_icp_order(tree->dev, src, n, rt, w, &perm, s);
     }
     if (e != hipSuccess) return hip_fail(e, "icp: order launch");
-    e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, schedule_of(flags), s);
+    e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, schedule_of(flags),
+                         bound2, keep, s);
     if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
     return KDNN_OK;
 }
@@ -302,7 +320,7 @@ size_t nn_query_workspace_bytes(int64_t m) { return query_ws_bytes(m); }
 
 static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t m, int32_t *idx,
                                  float *d2, uint32_t *cn, uint32_t *cp, bool stats, uint32_t flags,
-                                 void *ws, size_t ws_bytes, hipStream_t s)
+                                 float bound2, void *ws, size_t ws_bytes, hipStream_t s)
 {
     if (!tree) return fail(KDNN_EINVAL, "nn_query: null tree");
     kdnn_status st = check_points(q, m, "nn_query: queries");
@@ -333,7 +351,7 @@ static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t 
         }
     }
     hipError_t e = launch_nn(tree->dev, q, m, perm, idx, d2, cn, cp, stats, schedule_of(flags),
-                             twopass, s);
+                             bound2, twopass, s);
     if (e != hipSuccess) return hip_fail(e, "nn_query: launch");
     return KDNN_OK;
 }
@@ -344,7 +362,18 @@ kdnn_status nn_query(const kdnn_tree *tree, const float *q_dev, int64_t m, int32
 {
     KDNN_GUARD_BEGIN
     return nn_query_impl(tree, q_dev, m, idx_dev, dist2_dev, nullptr, nullptr, false, flags,
-                         ws_dev, ws_bytes, stream);
+                         INFINITY, ws_dev, ws_bytes, stream);
+    KDNN_GUARD_END
+}
+
+kdnn_status nn_query_radius(const kdnn_tree *tree, const float *q_dev, int64_t m, double max_dist,
+                            int32_t *idx_dev, float *dist2_dev, uint32_t flags, void *ws_dev,
+                            size_t ws_bytes, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    if (std::isnan(max_dist)) return fail(KDNN_EINVAL, "nn_query_radius: max_dist is NaN");
+    return nn_query_impl(tree, q_dev, m, idx_dev, dist2_dev, nullptr, nullptr, false, flags,
+                         bound_of(max_dist), ws_dev, ws_bytes, stream);
     KDNN_GUARD_END
 }
 
@@ -354,7 +383,7 @@ kdnn_status nn_query_stats(const kdnn_tree *tree, const float *q_dev, int64_t m,
 {
     KDNN_GUARD_BEGIN
     return nn_query_impl(tree, q_dev, m, idx_dev, dist2_dev, nodes_dev, points_dev, true, flags,
-                         ws_dev, ws_bytes, stream);
+                         INFINITY, ws_dev, ws_bytes, stream);
     KDNN_GUARD_END
 }
 
@@ -386,39 +415,67 @@ size_t icp_workspace_bytes(int64_t n) { return n > 0 ? icp_ws_bytes(n) : 0; }
 kdnn_status icp_correspond_reduce_async(const kdnn_tree *tree, const float *src_dev, int64_t n,
                                         const double *R_host, const double *t_host,
                                         double *sums_dev, int32_t *idx_dev, float *dist2_dev,
-                                        uint32_t flags, void *ws_dev, size_t ws_bytes,
-                                        hipStream_t stream)
+                                        uint32_t flags, const kdnn_icp_reject *reject,
+                                        void *ws_dev, size_t ws_bytes, hipStream_t stream)
 {
     KDNN_GUARD_BEGIN
     kdnn_status st = icp_check(tree, src_dev, n, R_host, t_host, flags, ws_dev, ws_bytes);
     if (st != KDNN_OK) return st;
+    if ((st = check_reject(reject, "icp_correspond_reduce_async")) != KDNN_OK) return st;
     if (!sums_dev || !aligned(sums_dev, 8)) return fail(KDNN_EINVAL, "icp: bad sums_dev");
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
     return icp_enqueue(tree, src_dev, n, R_host, t_host, sums_dev, idx_dev, dist2_dev,
-                       icp_resolve_sort(tree, flags), w,
-                       stream);
+                       icp_resolve_sort(tree, flags), reject, w, stream);
     KDNN_GUARD_END
 }
 
 kdnn_status icp_correspond_reduce(const kdnn_tree *tree, const float *src_dev, int64_t n,
                                   const double *R_host, const double *t_host,
                                   kdnn_icp_sums *out_host, int32_t *idx_dev, float *dist2_dev,
-                                  uint32_t flags, void *ws_dev, size_t ws_bytes,
-                                  hipStream_t stream)
+                                  uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
+                                  size_t ws_bytes, hipStream_t stream)
 {
     KDNN_GUARD_BEGIN
     kdnn_status st = icp_check(tree, src_dev, n, R_host, t_host, flags, ws_dev, ws_bytes);
     if (st != KDNN_OK) return st;
+    if ((st = check_reject(reject, "icp_correspond_reduce")) != KDNN_OK) return st;
     if (!out_host) return fail(KDNN_EINVAL, "icp: null out_host");
     kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
     std::lock_guard<std::mutex> lock(mt->icp_mu);
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
     st = icp_enqueue(tree, src_dev, n, R_host, t_host, mt->d_pinned, idx_dev, dist2_dev,
-                     icp_resolve_sort(tree, flags), w, stream);
+                     icp_resolve_sort(tree, flags), reject, w, stream);
     if (st != KDNN_OK) return st;
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "icp: synchronize");
     to_sums(mt->h_pinned, tree->dev.center, out_host);
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+kdnn_status icp_reject_reduce(const kdnn_tree *tree, const float *src_dev, int64_t n,
+                              const double *R_host, const double *t_host, double reject_k,
+                              kdnn_icp_sums *out_host, double *sigma2_out, uint8_t *kept_dev,
+                              void *ws_dev, size_t ws_bytes, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    kdnn_status st = icp_check(tree, src_dev, n, R_host, t_host, 0, ws_dev, ws_bytes);
+    if (st != KDNN_OK) return st;
+    if (!(reject_k > 0.0 && std::isfinite(reject_k)))
+        return fail(KDNN_EINVAL, "icp_reject_reduce: reject_k must be finite and > 0");
+    if (!out_host) return fail(KDNN_EINVAL, "icp_reject_reduce: null out_host");
+    kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
+    std::lock_guard<std::mutex> lock(mt->icp_mu);
+    const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
+    hipError_t e = launch_zero_u32(w.ticket, 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "icp_reject_reduce: launch");
+    e = launch_icp_reject(tree->dev, src_dev, n, R_host, t_host, reject_k * reject_k, w,
+                          mt->d_pinned, mt->d_pinned + KDNN_SUMS_DOUBLES, kept_dev, stream);
+    if (e != hipSuccess) return hip_fail(e, "icp_reject_reduce: launch");
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+        return hip_fail(e, "icp_reject_reduce: synchronize");
+    to_sums(mt->h_pinned, tree->dev.center, out_host);
+    if (sigma2_out) *sigma2_out = mt->h_pinned[KDNN_SUMS_DOUBLES];
     return KDNN_OK;
     KDNN_GUARD_END
 }
@@ -440,7 +497,8 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
 kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, const double *R0_host,
                       const double *t0_host, int32_t max_iter, double eps, double *R_out,
                       double *t_out, double *E_hist, double *Rt_hist, int32_t *iters_done,
-                      uint32_t flags, void *ws_dev, size_t ws_bytes, hipStream_t stream)
+                      uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
+                      size_t ws_bytes, hipStream_t stream)
 {
     KDNN_GUARD_BEGIN
     double R[9], t[3];
@@ -453,7 +511,9 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
         return fail(KDNN_EINVAL, "icp_align: unknown flag");
     kdnn_status st = icp_check(tree, src_dev, n, R, t, flags, ws_dev, ws_bytes);
     if (st != KDNN_OK) return st;
+    if ((st = check_reject(reject, "icp_align")) != KDNN_OK) return st;
     flags = icp_resolve_sort(tree, flags);
+    const double reject_k = reject ? reject->reject_k : 0.0;
     std::memcpy(R_out, R, sizeof R);
     std::memcpy(t_out, t, sizeof t);
     if (iters_done) *iters_done = 0;
@@ -470,7 +530,8 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
             std::memcpy(Rt_hist + 12 * k + 9, t, sizeof t);
         }
         const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
-        st = icp_enqueue(tree, src_dev, n, R, t, mt->d_pinned, nullptr, nullptr, f, w, stream);
+        st = icp_enqueue(tree, src_dev, n, R, t, mt->d_pinned, nullptr, nullptr, f, reject, w,
+                         stream);
         if (st != KDNN_OK) return st;
         hipError_t e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return hip_fail(e, "icp_align: synchronize");
@@ -481,6 +542,19 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
         double Rn[9], tn[3];
         st = procrustes_from_sums(sums, Rn, tn, err);
         if (st != KDNN_OK) return fail(st, "icp_align: iteration " + std::to_string(k) + ": " + err);
+        if (reject_k > 0.0) {
+            // residual rejection under the first solve, then solve again
+            e = launch_icp_reject(tree->dev, src_dev, n, Rn, tn, reject_k * reject_k, w,
+                                  mt->d_pinned, nullptr, nullptr, stream);
+            if (e != hipSuccess) return hip_fail(e, "icp_align: rejection launch");
+            if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+                return hip_fail(e, "icp_align: synchronize");
+            kdnn_icp_sums kept;
+            to_sums(mt->h_pinned, tree->dev.center, &kept);
+            st = procrustes_from_sums(kept, Rn, tn, err);
+            if (st != KDNN_OK)
+                return fail(st, "icp_align: iteration " + std::to_string(k) + " after rejection: " + err);
+        }
         std::memcpy(R, Rn, sizeof R);
         std::memcpy(t, tn, sizeof t);
         std::memcpy(R_out, R, sizeof R);

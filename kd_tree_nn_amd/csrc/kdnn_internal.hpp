@@ -90,6 +90,9 @@ struct IcpWorkspace {
     uint64_t *pkey;     // [n] pass-1 best key per traversal slot
     uint32_t *pslot;    // [n]
     void *twopass;      // two-pass list + per-group counts
+    int32_t *mslot;     // [n] match slot per source point (rejection)
+    float *md2;         // [n] its squared distance
+    double *stat;       // residual statistics of the rejection step
     double *sums;       // KDNN_SUMS_DOUBLES
     uint32_t *ticket;   // 1 counter, must be 0 between launches
     int32_t max_blocks;
@@ -114,13 +117,18 @@ struct Schedule {
 };
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     const Schedule &sc, void *twopass, hipStream_t s);
+                     const Schedule &sc, float bound2, void *twopass, hipStream_t s);
 hipError_t launch_transform(const float *in, float *out, int64_t n, const double *R,
                             const double *t, hipStream_t s);
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
-                            hipStream_t s);
+                            float bound2, bool keep_matches, hipStream_t s);
+// Residual rejection of the pairs the last fused launch stored (keep_matches):
+// sums of the pairs with r^2 <= kk * mean r^2 under (R, t).
+hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
+                             const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,
+                             double *stat_out, uint8_t *kept, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace kdnn

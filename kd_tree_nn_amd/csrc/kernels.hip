@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "kdnn_internal.hpp"
 
@@ -72,7 +73,6 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
 // reached a leaf (or finished), then all of them scan their leaves at once.
 // Leaf j owns point slots [floor(j n/2^D), floor((j+1) n/2^D)), so its points
 // are loaded together with its record.
-constexpr uint64_t kNoKey = 0x7F800000FFFFFFFFull;  // (+inf, index -1)
 constexpr uint32_t kDone = 0xFFFFFFFFu;
 
 struct Best {
@@ -96,10 +96,17 @@ __device__ __forceinline__ uint64_t nn_key(float d, uint32_t idx)
 
 __device__ __forceinline__ float key_dist(uint64_t k) { return __uint_as_float(uint32_t(k >> 32)); }
 
+// A search starts from a bound key (d_max bits, index 0xFFFFFFFF): no real
+// point has that index, so a point at exactly d_max still ranks below it,
+// and a key still carrying the index field 0xFFFFFFFF at the end is a miss.
+__device__ __forceinline__ uint64_t bound_key(float dmax2) { return nn_key(dmax2, 0xFFFFFFFFu); }
+
 __device__ __forceinline__ void finish(uint64_t key, uint32_t slot, Best &b)
 {
-    b.d = key_dist(key);
-    b.idx = b.d < INFINITY ? int32_t(uint32_t(key)) : -1;
+    const float d = key_dist(key);
+    const bool hit = uint32_t(key) != 0xFFFFFFFFu && d < INFINITY;
+    b.d = hit ? d : INFINITY;
+    b.idx = hit ? int32_t(uint32_t(key)) : -1;
     b.slot = slot;
 }
 
@@ -181,9 +188,10 @@ __device__ __forceinline__ void rank_points(const float4 (&p)[C], const int32_t 
     }
 }
 
-// Single-lane search.  Stops after `budget` node records when the budget is
-// below kNoBudget; returns whether the search completed.  key/slot hold the
-// best candidate seen so far either way (a valid upper bound to resume from).
+// Single-lane search from the bound key `init` (bound +inf: none).  Stops
+// after `budget` node records when the budget is below kNoBudget; returns
+// whether the search completed.  key/slot hold the best candidate seen so far
+// either way (a valid upper bound to resume from).
 constexpr uint32_t kNoBudget = 0xFFFFFFFFu;
 
 // Node record i: from the LDS copy of the top levels when i < lds_first.
@@ -201,11 +209,11 @@ __device__ __forceinline__ void fetch_node(const TreeView &t, const float4 *lds,
 
 template <bool STATS>
 __device__ __forceinline__ bool nn_search(const TreeView &t, float qx, float qy, float qz,
-                                          uint32_t budget, uint64_t &key, uint32_t &slot,
-                                          uint32_t &cn, uint32_t &cp,
+                                          uint64_t init, uint32_t budget, uint64_t &key,
+                                          uint32_t &slot, uint32_t &cn, uint32_t &cp,
                                           const float4 *lds = nullptr, uint32_t lds_first = 0)
 {
-    key = kNoKey;
+    key = init;
     slot = 0;
     if (!(isfinite(qx) && isfinite(qy) && isfinite(qz))) return true;
     uint32_t i = 1, far = 0, steps = 0;
@@ -294,7 +302,7 @@ __device__ __forceinline__ uint32_t group_sum_u32(uint32_t v)
     return v;
 }
 
-// `key`/`slot` come in as an upper bound (kNoKey: none) and go out as the
+// `key`/`slot` come in as an upper bound (a bound key when nothing is found yet) and go out as the
 // group's answer; with `resume` the query's own leaf is known to be scanned.
 template <int G, bool STATS>
 __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, float qy, float qz,
@@ -332,8 +340,8 @@ __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, flo
 
     // 2. the query's own leaf, scanned by the whole group (a resumed search
     //    has scanned it already when it holds any candidate: a first pass
-    //    always reaches the greedy leaf first)
-    if (!resume || key == kNoKey) {
+    //    always reaches the greedy leaf first unless a bound prunes it)
+    if (!resume || uint32_t(key) == 0xFFFFFFFFu) {
         int32_t begin, last, end;
         leaf_range(t, i, begin, last, end);
         for (int32_t k0 = begin; k0 < end; k0 += G * C) {
@@ -413,6 +421,7 @@ __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, flo
 
 struct NnArgs {
     TreeView tree;
+    uint64_t init;    // bound key (bound +inf: none)
     uint32_t budget;  // pass-1 node budget (two-pass mode)
     const float *q;
     int64_t m;
@@ -425,12 +434,12 @@ struct NnArgs {
 
 template <int G, bool STATS>
 __device__ __forceinline__ void search_query(const TreeView &t, float qx, float qy, float qz,
-                                             Best &b, uint32_t &cn, uint32_t &cp)
+                                             uint64_t init, Best &b, uint32_t &cn, uint32_t &cp)
 {
-    uint64_t key = kNoKey;
+    uint64_t key = init;
     uint32_t slot = 0;
     if (G == 1)
-        nn_search<STATS>(t, qx, qy, qz, kNoBudget, key, slot, cn, cp);
+        nn_search<STATS>(t, qx, qy, qz, init, kNoBudget, key, slot, cn, cp);
     else if (isfinite(qx) && isfinite(qy) && isfinite(qz))
         nn_search_group<G, STATS>(t, qx, qy, qz, false, key, slot, cn, cp);
     finish(key, slot, b);
@@ -452,7 +461,7 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             const float qx = a.q[3 * i], qy = a.q[3 * i + 1], qz = a.q[3 * i + 2];
             Best b;
             uint32_t cn = 0, cp = 0;
-            search_query<G, STATS>(a.tree, qx, qy, qz, b, cn, cp);
+            search_query<G, STATS>(a.tree, qx, qy, qz, a.init, b, cn, cp);
             if (gl == 0) {
                 a.idx[i] = b.idx;
                 a.d2[i] = b.d;
@@ -493,8 +502,8 @@ __global__ __launch_bounds__(kPWG) void nn_persist_kernel(NnArgs a, uint32_t lds
         const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
         uint64_t key;
         uint32_t slot, cn = 0, cp = 0;
-        nn_search<STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2], kNoBudget, key, slot,
-                         cn, cp, lds_nodes, lds_first);
+        nn_search<STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2], a.init, kNoBudget,
+                         key, slot, cn, cp, lds_nodes, lds_first);
         Best b;
         finish(key, slot, b);
         a.idx[i] = b.idx;
@@ -607,7 +616,7 @@ __global__ __launch_bounds__(kWG) void nn_pass1_kernel(NnArgs a, TwoPass tp)
             uint64_t key;
             uint32_t slot, cn = 0, cp = 0;
             const bool done = nn_search<STATS>(a.tree, a.q[3 * i], a.q[3 * i + 1], a.q[3 * i + 2],
-                                               a.budget, key, slot, cn, cp);
+                                               a.init, a.budget, key, slot, cn, cp);
             Best b;
             finish(key, slot, b);
             a.idx[i] = done ? b.idx : -(int32_t(uint32_t(key)) + 3);
@@ -684,6 +693,9 @@ struct IcpArgs {
     uint32_t *pslot;    // [n] pass-1 best point slot of unfinished slots
     int32_t *idx;
     float *d2;
+    uint64_t init;      // bound key (bound +inf: none)
+    int32_t *mslot;     // [n] or null: leaf-order slot of each source point's match, -1 if none
+    float *md2;         // [n] or null: its squared distance
 };
 
 __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, double tr, double x,
@@ -743,6 +755,10 @@ __device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, doub
 {
     if (a.idx) a.idx[i] = b.idx;
     if (a.d2) a.d2[i] = b.d;
+    if (a.mslot) {
+        a.mslot[i] = b.idx >= 0 ? int32_t(b.slot) : -1;
+        a.md2[i] = b.d;
+    }
     if (b.idx < 0) return;
     const float4 mp = a.tree.pts[b.slot];
     const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
@@ -759,18 +775,26 @@ __device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, doub
 
 // After this group's partials are written: the last group to finish sums
 // p1[kS][n1] and then p2[kS][n2] in a fixed order into a.sums.
-template <int WG>
-__device__ __forceinline__ void icp_final_reduce_n(const IcpArgs &a, double (&acc)[kS],
-                                                   double *red, const double *p1, int32_t n1,
-                                                   const double *p2, int32_t n2)
+// True in the last work-group of the grid to get here (atomic ticket); that
+// group sees every other group's partials.  The ticket is reset by it.
+__device__ __forceinline__ bool last_group(uint32_t *ticket)
 {
     __shared__ uint32_t is_last;
     __threadfence();
     __syncthreads();
-    if (threadIdx.x == 0) is_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+    if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
     __syncthreads();
-    if (!is_last) return;
+    if (!is_last) return false;
     __threadfence();
+    return true;
+}
+
+template <int WG>
+__device__ __forceinline__ void final_reduce_n(uint32_t *ticket, double *sums, double (&acc)[kS],
+                                               double *red, const double *p1, int32_t n1,
+                                               const double *p2, int32_t n2)
+{
+    if (!last_group(ticket)) return;
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     for (int32_t g = threadIdx.x; g < n1 + n2; g += WG) {
@@ -779,8 +803,16 @@ __device__ __forceinline__ void icp_final_reduce_n(const IcpArgs &a, double (&ac
             acc[c] += g < n1 ? p1[int64_t(c) * n1 + g] : p2[int64_t(c) * n2 + (g - n1)];
     }
     __syncthreads();  // red[] is reused
-    block_sum_n<WG>(acc, red, a.sums, 1);
-    if (threadIdx.x == 0) atomicExch(a.ticket, 0u);
+    block_sum_n<WG>(acc, red, sums, 1);
+    if (threadIdx.x == 0) atomicExch(ticket, 0u);
+}
+
+template <int WG>
+__device__ __forceinline__ void icp_final_reduce_n(const IcpArgs &a, double (&acc)[kS],
+                                                   double *red, const double *p1, int32_t n1,
+                                                   const double *p2, int32_t n2)
+{
+    final_reduce_n<WG>(a.ticket, a.sums, acc, red, p1, n1, p2, n2);
 }
 
 __device__ __forceinline__ void icp_final_reduce(const IcpArgs &a, double (&acc)[kS], double *red,
@@ -811,7 +843,7 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         icp_query(a, i, X, Y, Z, qx, qy, qz);
         Best b;
         uint32_t cn = 0, cp = 0;
-        search_query<G, false>(a.tree, qx, qy, qz, b, cn, cp);
+        search_query<G, false>(a.tree, qx, qy, qz, a.init, b, cn, cp);
         if (gl == 0) icp_accumulate(a, i, X, Y, Z, b, acc);
     }
     block_sum(acc, red, a.partials + blockIdx.x, nb);
@@ -840,7 +872,8 @@ __global__ __launch_bounds__(kWG) void icp_pass1_kernel(IcpArgs a, TwoPass tp)
             icp_query(a, i, X, Y, Z, qx, qy, qz);
             uint64_t key;
             uint32_t slot, cn = 0, cp = 0;
-            const bool done = nn_search<false>(a.tree, qx, qy, qz, a.budget, key, slot, cn, cp);
+            const bool done =
+                nn_search<false>(a.tree, qx, qy, qz, a.init, a.budget, key, slot, cn, cp);
             if (done) {
                 Best b;
                 finish(key, slot, b);
@@ -913,13 +946,146 @@ __global__ __launch_bounds__(kPWG) void icp_persist_kernel(IcpArgs a, uint32_t l
         icp_query(a, i, X, Y, Z, qx, qy, qz);
         uint64_t key;
         uint32_t slot, cn = 0, cp = 0;
-        nn_search<false>(a.tree, qx, qy, qz, kNoBudget, key, slot, cn, cp, lds_nodes, lds_first);
+        nn_search<false>(a.tree, qx, qy, qz, a.init, kNoBudget, key, slot, cn, cp, lds_nodes,
+                         lds_first);
         Best b;
         finish(key, slot, b);
         icp_accumulate(a, i, X, Y, Z, b, acc);
     }
     block_sum_n<kPWG>(acc, red, a.partials + blockIdx.x, gridDim.x);
     icp_final_reduce_n<kPWG>(a, acc, red, a.partials, int32_t(gridDim.x), nullptr, 0);
+}
+
+// ------------------------------------------- residual rejection (3 sigma)
+//
+// After the first solve (R1, t1) of an iteration, with the matches the fused
+// kernel stored per source point:
+//   icp_residual_kernel: r_i^2 = ||R1 s_i + t1 - m_i||^2 in fp64 (the moved
+//     point is not rounded), summed over the pairs with their count; the last
+//     work-group turns them into sigma^2 = sum / count and the threshold
+//     (k k) sigma^2, kept in device memory for the next kernel;
+//   icp_reject_kernel: the 17 sums of the pairs with r_i^2 <= threshold.
+// Both reduce in a fixed order.  A stored slot outside the tree is treated as
+// "no match", so any content of the match buffer is safe to read.
+struct RejArgs {
+    TreeView tree;
+    const float *src;
+    int64_t n;
+    double R[9];
+    double t[3];
+    double c[3];
+    double kk;             // k * k
+    const int32_t *mslot;  // [n]
+    const float *md2;      // [n]
+    double *partials;      // [kS][gridDim.x]
+    uint32_t *ticket;
+    double *stat;          // device: sum r^2, pairs, threshold
+    double *sums;          // [kS] output of icp_reject_kernel
+    double *stat_out;      // [2] or null: sigma^2, threshold (written by icp_reject_kernel)
+    uint8_t *kept;         // [n] or null: 1 where the pair is kept
+};
+
+__device__ __forceinline__ bool rej_pair(const RejArgs &a, int64_t i, uint32_t &slot)
+{
+    const int32_t sl = a.mslot[i];
+    slot = uint32_t(sl);
+    return sl >= 0 && int64_t(sl) < a.tree.n;
+}
+
+__device__ __forceinline__ double rej_residual_sq(const RejArgs &a, double X, double Y, double Z,
+                                                  const float4 &m)
+{
+    const double e0 = (((a.R[0] * X + a.R[1] * Y) + a.R[2] * Z) + a.t[0]) - double(m.x);
+    const double e1 = (((a.R[3] * X + a.R[4] * Y) + a.R[5] * Z) + a.t[1]) - double(m.y);
+    const double e2 = (((a.R[6] * X + a.R[7] * Y) + a.R[8] * Z) + a.t[2]) - double(m.z);
+    return (e0 * e0 + e1 * e1) + e2 * e2;
+}
+
+__global__ __launch_bounds__(kWG) void icp_residual_kernel(RejArgs a)
+{
+    __shared__ double red[(kWG / 64) * kS];
+    __shared__ double tot[kS];
+    double acc[kS];
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    for (int64_t i = int64_t(blockIdx.x) * kWG + threadIdx.x; i < a.n;
+         i += int64_t(gridDim.x) * kWG) {
+        uint32_t slot;
+        if (!rej_pair(a, i, slot)) continue;
+        const float4 m = a.tree.pts[slot];
+        acc[0] += rej_residual_sq(a, a.src[3 * i], a.src[3 * i + 1], a.src[3 * i + 2], m);
+        acc[1] += 1.0;
+    }
+    block_sum(acc, red, a.partials + blockIdx.x, gridDim.x);
+    if (!last_group(a.ticket)) return;
+    const int32_t nb = int32_t(gridDim.x);
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    for (int32_t g = threadIdx.x; g < nb; g += kWG) {
+        acc[0] += a.partials[g];
+        acc[1] += a.partials[int64_t(nb) + g];
+    }
+    __syncthreads();  // red[] is reused
+    block_sum(acc, red, tot, 1);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double sum = tot[0];
+        const double cnt = tot[1];
+        a.stat[0] = sum;
+        a.stat[1] = cnt;
+        a.stat[2] = a.kk * (sum / cnt);
+        atomicExch(a.ticket, 0u);
+    }
+}
+
+__global__ __launch_bounds__(kWG) void icp_reject_kernel(RejArgs a)
+{
+    __shared__ double red[(kWG / 64) * kS];
+    double acc[kS];
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    const double thr = a.stat[2];
+    for (int64_t i = int64_t(blockIdx.x) * kWG + threadIdx.x; i < a.n;
+         i += int64_t(gridDim.x) * kWG) {
+        uint32_t slot;
+        bool keep = false;
+        if (rej_pair(a, i, slot)) {
+            const double X = a.src[3 * i], Y = a.src[3 * i + 1], Z = a.src[3 * i + 2];
+            const float4 mp = a.tree.pts[slot];
+            keep = rej_residual_sq(a, X, Y, Z, mp) <= thr;
+            if (keep) {
+                const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
+                const double m0 = double(mp.x) - a.c[0], m1 = double(mp.y) - a.c[1],
+                             m2 = double(mp.z) - a.c[2];
+                acc[0] += s0; acc[1] += s1; acc[2] += s2;
+                acc[3] += m0; acc[4] += m1; acc[5] += m2;
+                acc[6] += s0 * m0; acc[7] += s0 * m1; acc[8] += s0 * m2;
+                acc[9] += s1 * m0; acc[10] += s1 * m1; acc[11] += s1 * m2;
+                acc[12] += s2 * m0; acc[13] += s2 * m1; acc[14] += s2 * m2;
+                acc[15] += double(a.md2[i]);
+                acc[16] += 1.0;
+            }
+        }
+        if (a.kept) a.kept[i] = keep ? 1 : 0;
+    }
+    block_sum(acc, red, a.partials + blockIdx.x, gridDim.x);
+    if (!last_group(a.ticket)) return;
+    const int32_t nb = int32_t(gridDim.x);
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    for (int32_t g = threadIdx.x; g < nb; g += kWG) {
+#pragma unroll
+        for (int c = 0; c < kS; ++c) acc[c] += a.partials[int64_t(c) * nb + g];
+    }
+    __syncthreads();  // red[] is reused
+    block_sum(acc, red, a.sums, 1);
+    if (threadIdx.x == 0) {
+        if (a.stat_out) {
+            a.stat_out[0] = a.stat[0] / a.stat[1];
+            a.stat_out[1] = thr;
+        }
+        atomicExch(a.ticket, 0u);
+    }
 }
 
 // --------------------------------------------------------------- transform
@@ -1216,7 +1382,7 @@ size_t icp_ws_bytes(int64_t n)
     const size_t nn = size_t(n);
     return sort_workspace_bytes(n) + align256(size_t(kS) * kIcpMaxBlocks * 8) +
            align256(size_t(kS) * kPass2Blocks * 8) + align256(size_t(kS) * 8) + 256 +
-           align256(nn * 4) + align256(nn * 8) + twopass_bytes(n);
+           align256(nn * 4) + align256(nn * 8) + twopass_bytes(n) + 2 * align256(nn * 4) + 256;
 }
 
 IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
@@ -1238,6 +1404,12 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
     w.pkey = reinterpret_cast<uint64_t *>(p);
     p += align256(size_t(n) * 8);
     w.twopass = p;
+    p += twopass_bytes(n);
+    w.mslot = reinterpret_cast<int32_t *>(p);
+    p += align256(size_t(n) * 4);
+    w.md2 = reinterpret_cast<float *>(p);
+    p += align256(size_t(n) * 4);
+    w.stat = reinterpret_cast<double *>(p);
     w.max_blocks = kIcpMaxBlocks;
     return w;
 }
@@ -1361,12 +1533,20 @@ static void launch_nn_two_pass(const NnArgs &a, bool stats, void *twopass, hipSt
     }
 }
 
+static uint64_t host_bound_key(float bound2)
+{
+    uint32_t bits;
+    std::memcpy(&bits, &bound2, 4);
+    return (uint64_t(bits) << 32) | 0xFFFFFFFFull;
+}
+
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     const Schedule &sc, void *twopass, hipStream_t s)
+                     const Schedule &sc, float bound2, void *twopass, hipStream_t s)
 {
     NnArgs a{};
     a.tree = tree_view(t);
+    a.init = host_bound_key(bound2);
     a.q = q;
     a.m = m;
     a.perm = perm;
@@ -1412,10 +1592,13 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
-                            hipStream_t s)
+                            float bound2, bool keep_matches, hipStream_t s)
 {
     IcpArgs a{};
     a.tree = tree_view(t);
+    a.init = host_bound_key(bound2);
+    a.mslot = keep_matches ? ws.mslot : nullptr;
+    a.md2 = keep_matches ? ws.md2 : nullptr;
     a.src = src;
     a.n = n;
     a.perm = perm;
@@ -1451,6 +1634,34 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         default: icp_fused_kernel<1><<<grid, kWG, 0, s>>>(a); break;
         }
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
+                             const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,
+                             double *stat_out, uint8_t *kept, hipStream_t s)
+{
+    RejArgs a{};
+    a.tree = tree_view(t);
+    a.src = src;
+    a.n = n;
+    for (int k = 0; k < 9; ++k) a.R[k] = R[k];
+    for (int k = 0; k < 3; ++k) {
+        a.t[k] = tv[k];
+        a.c[k] = t.center[k];
+    }
+    a.kk = kk;
+    a.mslot = ws.mslot;
+    a.md2 = ws.md2;
+    a.partials = ws.partials;
+    a.ticket = ws.ticket;
+    a.stat = ws.stat;
+    a.sums = sums_out;
+    a.stat_out = stat_out;
+    a.kept = kept;
+    const dim3 grid(uint32_t(icp_blocks(n, 1)));
+    icp_residual_kernel<<<grid, kWG, 0, s>>>(a);
+    icp_reject_kernel<<<grid, kWG, 0, s>>>(a);
     return hipGetLastError();
 }
 
