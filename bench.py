@@ -238,6 +238,41 @@ def main():
            "queries_per_s": round(rsteps * ITERS * n / Tr)}
     log(f"with rejection: {rej['icp_iters_per_s']:.0f} ICP iterations/s")
 
+    # ----------------------- LiDAR frame pairs: batched vs one after another
+    # (article §3.4: consecutive frames in flight together)
+    log("LiDAR: 16 frame pairs, 30 iterations each")
+    lp = synth.lidar_pairs()
+    ltrees = [kdnn.Tree(q.target, q.leaf_size) for q in lp]
+    lsrc = [torch.from_numpy(np.ascontiguousarray(q.source)).cuda() for q in lp]
+    bws = kdnn.icp_batch_workspace([len(x) for x in lsrc])
+    lws = [t_.icp_workspace(len(x)) for t_, x in zip(ltrees, lsrc)]
+
+    def run_batch():
+        return kdnn.icp_batch(ltrees, lsrc, max_iter=ITERS, workspace=bws)
+
+    def run_seq():
+        return [t_.icp(x, max_iter=ITERS, workspace=w_, sort=False)
+                for t_, x, w_ in zip(ltrees, lsrc, lws)]
+
+    lid = {"pairs": len(lp), "points_per_frame": int(np.mean([len(x) for x in lsrc])),
+           "iterations": ITERS}
+    for name, fn in (("batched", run_batch), ("sequential", run_seq)):
+        fn()
+        torch.cuda.synchronize()
+        reps = 5
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        T_ = (time.perf_counter() - t0) / reps
+        q_ = sum(len(x) for x in lsrc) * ITERS
+        lid[name] = {"ms_per_16_pairs": round(T_ * 1e3, 3), "pairs_per_s": round(len(lp) / T_, 1),
+                     "icp_iters_per_s": round(len(lp) * ITERS / T_, 1),
+                     "queries_per_s": round(q_ / T_)}
+    lid["speedup"] = round(lid["sequential"]["ms_per_16_pairs"] / lid["batched"]["ms_per_16_pairs"], 2)
+    log(f"LiDAR batched {lid['batched']['pairs_per_s']} pairs/s, "
+        f"sequential {lid['sequential']['pairs_per_s']} pairs/s")
+
     # ------------------------------------------- fused kernel: events per launch
     # The library launches on torch's current stream; the events bracket each
     # launch on that stream.  A spin kernel queued ahead of every 30 launches
@@ -333,6 +368,7 @@ def main():
         },
         "icp_iters_per_s": round(iters_per_s, 1),
         "icp_with_rejection": rej,
+        "lidar_pairs": lid,
         "icp_iter_us": round(T / (args.steps * ITERS) * 1e6, 2),
         "build": {"host_build_ms": round(info["build_ms"], 3),
                   "upload_ms": round(info["upload_ms"], 3),

@@ -343,6 +343,35 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
                       uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
                       size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of device workspace icp_align_batch needs for B pairs of n[p] source
+ * points.  0 if B < 1, n is NULL or some n[p] < 1. */
+size_t icp_batch_workspace_bytes(int32_t B, const int64_t *n);
+
+/* B independent registrations advanced together (article §3.4: consecutive
+ * frames kept in flight at once so the GPU stays busy and one host round trip
+ * per iteration serves all of them).  Pair p registers src_dev[p] (n[p]
+ * points) onto trees[p] exactly as icp_align does with flags
+ * KDNN_ICP_NO_SORT and one lane per query: same iteration, same convergence
+ * rule per pair, and the same max_dist bound.  Each launch carries up to 8
+ * pairs, each pair on its own XCDs so that its tree stays in their L2.
+ *   trees, src_dev, n : [B] (all trees on the current device).
+ *   R0_host, t0_host  : optional [B][9] / [B][3] (NULL = identity / zero).
+ *   R_out, t_out      : [B][9] / [B][3], the last solved transforms.
+ *   E_hist            : optional [B][max_iter], E_k of each pair.
+ *   iters_done        : optional [B].      status_out : optional [B].
+ *   flags             : 0 or KDNN_ICP_NO_SORT.
+ *   reject            : optional; max_dist only (reject_k > 0 is EINVAL).
+ *   ws_dev            : >= icp_batch_workspace_bytes(B, n), 256-byte aligned.
+ * A pair whose solve degenerates stops with its last good transform and its
+ * status_out entry set; the others go on, and the call returns EDEGENERATE.
+ * Synchronises stream.  Errors: EINVAL, ENOMEM, EDEVICE, EDEGENERATE. */
+kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const float *const *src_dev,
+                            const int64_t *n, const double *R0_host, const double *t0_host,
+                            int32_t max_iter, double eps, double *R_out, double *t_out,
+                            double *E_hist, int32_t *iters_done, kdnn_status *status_out,
+                            uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
+                            size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- misc */
 
 /* Text of the last error on the calling thread ("" if none).  Valid until the

@@ -25,7 +25,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["Tree", "transform", "procrustes", "build_host", "layout", "sums_to_dict",
-           "KdnnError", "version"]
+           "icp_batch", "icp_batch_workspace", "KdnnError", "version"]
 
 
 def _torch():
@@ -300,6 +300,51 @@ def transform(x, R, t, out=None, stream=None):
     _lib.check(_lib.lib().transform_points(_ptr(x), _ptr(out), x.shape[0], Rp, tp,
                                            _stream(stream)), "transform_points")
     return out
+
+
+def icp_batch_workspace(sources_n, device=None):
+    """Device workspace for :func:`icp_batch` over pairs of these sizes."""
+    torch = _torch()
+    n = np.ascontiguousarray(np.asarray(sources_n, np.int64))
+    nb = int(_lib.lib().icp_batch_workspace_bytes(len(n), n.ctypes.data_as(
+        ctypes.POINTER(_lib.c_i64))))
+    return torch.empty(nb, dtype=torch.uint8, device=device or "cuda")
+
+
+def icp_batch(trees, sources, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
+              workspace=None, stream=None, max_dist=None) -> list:
+    """Register sources[p] onto trees[p] for every p together (icp_align_batch).
+
+    Returns one dict per pair: R, t, E (per iteration), iters and status
+    (0 = OK; a degenerate pair keeps its last good transform).
+    """
+    B = len(trees)
+    if B != len(sources) or B < 1:
+        raise ValueError("trees and sources must be non-empty and of equal length")
+    srcs = [_dev_points(x, "src") for x in sources]
+    n = np.ascontiguousarray([x.shape[0] for x in srcs], dtype=np.int64)
+    th = (ctypes.c_void_p * B)(*[tr._h.value for tr in trees])
+    sp = (ctypes.c_void_p * B)(*[x.data_ptr() for x in srcs])
+    R0a = None if R0 is None else np.ascontiguousarray(np.asarray(R0, np.float64).reshape(B, 9))
+    t0a = None if t0 is None else np.ascontiguousarray(np.asarray(t0, np.float64).reshape(B, 3))
+    R = np.zeros((B, 9))
+    t = np.zeros((B, 3))
+    E = np.zeros((B, max(max_iter, 1)))
+    it = np.zeros(B, np.int32)
+    st = np.zeros(B, np.int32)
+    ws = workspace if workspace is not None else icp_batch_workspace(n, srcs[0].device)
+    status = _lib.lib().icp_align_batch(
+        B, th, sp, n.ctypes.data_as(ctypes.POINTER(_lib.c_i64)),
+        R0a.ctypes.data_as(_lib.c_dp) if R0a is not None else None,
+        t0a.ctypes.data_as(_lib.c_dp) if t0a is not None else None,
+        int(max_iter), float(eps), R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
+        E.ctypes.data_as(_lib.c_dp), it.ctypes.data_as(ctypes.POINTER(_lib.c_i32)),
+        st.ctypes.data_as(ctypes.POINTER(_lib.c_i32)), 0, _reject(max_dist, 0.0),
+        _ptr(ws), ws.numel(), _stream(stream))
+    if status not in (_lib.KDNN_OK, _lib.KDNN_EDEGENERATE):
+        _lib.check(status, "icp_align_batch")
+    return [{"R": R[p].reshape(3, 3), "t": t[p], "E": E[p, :it[p]], "iters": int(it[p]),
+             "status": int(st[p])} for p in range(B)]
 
 
 def procrustes(sums) -> tuple:

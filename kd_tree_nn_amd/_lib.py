@@ -86,6 +86,11 @@ SIGNATURES = {
     "icp_align": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, c_i32, ctypes.c_double, c_dp, c_dp,
                           c_dp, c_dp, ctypes.POINTER(c_i32), c_u32, ctypes.POINTER(IcpReject),
                           c_vp, c_sz, c_vp]),
+    "icp_batch_workspace_bytes": (c_sz, [c_i32, ctypes.POINTER(c_i64)]),
+    "icp_align_batch": (c_i32, [c_i32, c_vp, c_vp, ctypes.POINTER(c_i64), c_dp, c_dp, c_i32,
+                                ctypes.c_double, c_dp, c_dp, c_dp, ctypes.POINTER(c_i32),
+                                ctypes.POINTER(c_i32), c_u32, ctypes.POINTER(IcpReject), c_vp,
+                                c_sz, c_vp]),
     "kdnn_last_error": (ctypes.c_char_p, []),
     "kdnn_version": (c_i32, []),
 }

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "kdnn_internal.hpp"
 
@@ -567,6 +568,137 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
         }
         prev_mse = mse;
     }
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+size_t icp_batch_workspace_bytes(int32_t B, const int64_t *n)
+{
+    if (B < 1 || !n) return 0;
+    for (int32_t p = 0; p < B; ++p)
+        if (n[p] < 1) return 0;
+    return icp_batch_ws_bytes(B, n);
+}
+
+kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const float *const *src_dev,
+                            const int64_t *n, const double *R0_host, const double *t0_host,
+                            int32_t max_iter, double eps, double *R_out, double *t_out,
+                            double *E_hist, int32_t *iters_done, kdnn_status *status_out,
+                            uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
+                            size_t ws_bytes, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    if (B < 1 || !trees || !src_dev || !n || !R_out || !t_out)
+        return fail(KDNN_EINVAL, "icp_align_batch: B < 1 or a null array");
+    if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align_batch: max_iter < 0");
+    if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align_batch: eps must be >= 0");
+    if (flags & ~KDNN_ICP_NO_SORT)
+        return fail(KDNN_EINVAL, "icp_align_batch: only KDNN_ICP_NO_SORT is accepted "
+                                 "(pairs are traversed in their given order, one lane each)");
+    kdnn_status st = check_reject(reject, "icp_align_batch");
+    if (st != KDNN_OK) return st;
+    if (reject && reject->reject_k > 0.0)
+        return fail(KDNN_EINVAL, "icp_align_batch: residual rejection is not available in the "
+                                 "batched call (max_dist is)");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "icp_align_batch: hipGetDevice");
+    for (int32_t p = 0; p < B; ++p) {
+        if (!trees[p]) return fail(KDNN_EINVAL, "icp_align_batch: null tree");
+        if (trees[p]->device != dev)
+            return fail(KDNN_EINVAL, "icp_align_batch: a tree lives on another device");
+        if (n[p] < 1) return fail(KDNN_EINVAL, "icp_align_batch: n must be >= 1");
+        if ((st = check_points(src_dev[p], n[p], "icp_align_batch: src")) != KDNN_OK) return st;
+    }
+    if ((st = check_ws(ws_dev, ws_bytes, icp_batch_ws_bytes(B, n))) != KDNN_OK) return st;
+
+    std::vector<double> R(size_t(9) * B), t(size_t(3) * B);
+    for (int32_t p = 0; p < B; ++p) {
+        std::memcpy(&R[9 * size_t(p)], R0_host ? R0_host + 9 * size_t(p) : kI, 9 * sizeof(double));
+        std::memcpy(&t[3 * size_t(p)], t0_host ? t0_host + 3 * size_t(p) : kZ, 3 * sizeof(double));
+        if (iters_done) iters_done[p] = 0;
+        if (status_out) status_out[p] = KDNN_OK;
+    }
+    auto copy_out = [&]() {
+        std::memcpy(R_out, R.data(), R.size() * sizeof(double));
+        std::memcpy(t_out, t.data(), t.size() * sizeof(double));
+    };
+    copy_out();
+    if (max_iter == 0) return KDNN_OK;
+
+    // one partial column per work-group of every pair, a ticket per pair
+    std::vector<int32_t> part(B);
+    int32_t total = 0;
+    for (int32_t p = 0; p < B; ++p) {
+        part[p] = total;
+        total += batch_groups(n[p]);
+    }
+    uint32_t *tickets = batch_tickets(ws_dev, total);
+    // host slot the kernels write the sums into
+    struct Pinned {
+        double *h = nullptr;
+        ~Pinned() { if (h) (void)hipHostFree(h); }
+    } pin;
+    if ((e = hipHostMalloc(reinterpret_cast<void **>(&pin.h),
+                           size_t(KDNN_SUMS_DOUBLES) * 8 * size_t(B), hipHostMallocDefault)) !=
+        hipSuccess)
+        return fail(KDNN_ENOMEM, std::string("icp_align_batch: hipHostMalloc: ") + hipGetErrorString(e));
+    double *d_sums = nullptr;
+    if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&d_sums), pin.h, 0)) != hipSuccess)
+        return hip_fail(e, "icp_align_batch: hipHostGetDevicePointer");
+    if ((e = launch_zero_u32(tickets, B, stream)) != hipSuccess)
+        return hip_fail(e, "icp_align_batch: launch");
+
+    const float bound2 = reject ? bound_of(reject->max_dist) : INFINITY;
+    std::vector<char> done(B, 0);
+    std::vector<double> prev_mse(B, 0.0);
+    std::vector<int> small_steps(B, 0);
+    std::vector<BatchJob> jobs;
+    bool any_failed = false;
+    for (int32_t k = 0; k < max_iter; ++k) {
+        std::vector<int32_t> active;
+        for (int32_t p = 0; p < B; ++p)
+            if (!done[p]) active.push_back(p);
+        if (active.empty()) break;
+        for (size_t c0 = 0; c0 < active.size(); c0 += size_t(batch_max_pairs())) {
+            jobs.clear();
+            for (size_t c = c0; c < active.size() && c < c0 + size_t(batch_max_pairs()); ++c) {
+                const int32_t p = active[c];
+                jobs.push_back(BatchJob{&trees[p]->dev, src_dev[p], n[p], &R[9 * size_t(p)],
+                                        &t[3 * size_t(p)], part[p], tickets + p,
+                                        d_sums + size_t(KDNN_SUMS_DOUBLES) * p});
+            }
+            e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream);
+            if (e != hipSuccess) return hip_fail(e, "icp_align_batch: launch");
+        }
+        if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+            return hip_fail(e, "icp_align_batch: synchronize");
+        for (const int32_t p : active) {
+            kdnn_icp_sums sums;
+            to_sums(pin.h + size_t(KDNN_SUMS_DOUBLES) * p, trees[p]->dev.center, &sums);
+            if (E_hist) E_hist[size_t(p) * max_iter + k] = sums.sum_d2;
+            std::string err;
+            double Rn[9], tn[3];
+            const kdnn_status ps = procrustes_from_sums(sums, Rn, tn, err);
+            if (ps != KDNN_OK) {
+                if (status_out) status_out[p] = ps;
+                done[p] = 1;
+                any_failed = true;
+                continue;
+            }
+            std::memcpy(&R[9 * size_t(p)], Rn, sizeof Rn);
+            std::memcpy(&t[3 * size_t(p)], tn, sizeof tn);
+            if (iters_done) iters_done[p] = k + 1;
+            const double mse = sums.sum_d2 / double(sums.n);
+            if (eps > 0.0 && k > 0) {
+                small_steps[p] = std::fabs(mse - prev_mse[p]) < eps ? small_steps[p] + 1 : 0;
+                if (small_steps[p] >= 2) done[p] = 1;
+            }
+            prev_mse[p] = mse;
+        }
+    }
+    copy_out();
+    if (any_failed) return fail(KDNN_EDEGENERATE, "icp_align_batch: a pair degenerated (status_out)");
     return KDNN_OK;
     KDNN_GUARD_END
 }

@@ -124,6 +124,26 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
                             float bound2, bool keep_matches, hipStream_t s);
+// Batched correspondence steps: up to batch_max_pairs() (tree, source) pairs
+// per launch, one pair per group of XCDs.  ws: icp_batch_ws_bytes layout
+// (partials of `total` work-group columns, then one ticket per pair).
+struct BatchJob {
+    const DeviceTree *tree;
+    const float *src;
+    int64_t n;
+    const double *R;  // [9]
+    const double *t;  // [3]
+    int32_t part;     // first partial column
+    uint32_t *ticket;
+    double *sums;     // [KDNN_SUMS_DOUBLES] out (device-visible)
+};
+int batch_max_pairs();
+int32_t batch_groups(int64_t n);  // work-groups (partial columns) of an n-point pair
+size_t icp_batch_ws_bytes(int32_t B, const int64_t *n);
+uint32_t *batch_tickets(void *ws, int32_t total);
+hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void *ws, int32_t total,
+                            hipStream_t s);
+
 // Residual rejection of the pairs the last fused launch stored (keep_matches):
 // sums of the pairs with r^2 <= kk * mean r^2 under (R, t).
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,

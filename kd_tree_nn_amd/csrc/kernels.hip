@@ -775,18 +775,23 @@ __device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, doub
 
 // After this group's partials are written: the last group to finish sums
 // p1[kS][n1] and then p2[kS][n2] in a fixed order into a.sums.
-// True in the last work-group of the grid to get here (atomic ticket); that
-// group sees every other group's partials.  The ticket is reset by it.
-__device__ __forceinline__ bool last_group(uint32_t *ticket)
+// True in the last of `groups` work-groups to get here (atomic ticket); that
+// group sees every other group's partials.  The caller resets the ticket.
+__device__ __forceinline__ bool last_group_of(uint32_t *ticket, uint32_t groups)
 {
     __shared__ uint32_t is_last;
     __threadfence();
     __syncthreads();
-    if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == gridDim.x - 1) ? 1u : 0u;
+    if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == groups - 1) ? 1u : 0u;
     __syncthreads();
     if (!is_last) return false;
     __threadfence();
     return true;
+}
+
+__device__ __forceinline__ bool last_group(uint32_t *ticket)
+{
+    return last_group_of(ticket, gridDim.x);
 }
 
 template <int WG>
@@ -954,6 +959,89 @@ __global__ __launch_bounds__(kPWG) void icp_persist_kernel(IcpArgs a, uint32_t l
     }
     block_sum_n<kPWG>(acc, red, a.partials + blockIdx.x, gridDim.x);
     icp_final_reduce_n<kPWG>(a, acc, red, a.partials, int32_t(gridDim.x), nullptr, 0);
+}
+
+// ------------------------------------------------- batched ICP (frame pairs)
+//
+// Several registrations advance in lock-step: one launch runs the fused
+// correspondence step of up to kBatchMax (source, tree) pairs.  Work-groups
+// are dealt round-robin to the 8 XCDs, so work-group b runs on XCD b % 8;
+// pair p of a launch with B pairs gets the XCDs x with x % B == p.  Every XCD
+// then walks a single tree, which stays in its own L2 (a 131k-point frame
+// tree is ~2.6 MB of the 4 MB), instead of all of them thrashing it.  Each
+// pair reduces its work-groups' partials with its own ticket, in a fixed
+// order, into its 17 sums.
+constexpr int kBatchMax = 8;
+
+struct BatchPair {
+    TreeView tree;
+    const float *src;
+    int64_t n;
+    double R[9];
+    double t[3];
+    double c[3];
+    int32_t nb;       // work-groups of this pair: ceil(n / kWG)
+    int32_t part;     // first partial column of this pair
+    uint32_t *ticket;
+    double *sums;     // [kS] out
+};
+
+struct BatchArgs {
+    BatchPair p[kBatchMax];
+    int32_t B;
+    int32_t total;    // partial columns (stride of one component)
+    uint64_t init;    // bound key
+    double *partials; // [kS][total]
+};
+
+__global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
+{
+    __shared__ double red[(kWG / 64) * kS];
+    const int x = int(blockIdx.x % uint32_t(kNumXcd));
+    const int pi = x % a.B;
+    const BatchPair &P = a.p[pi];
+    const int kx = (kNumXcd - pi + a.B - 1) / a.B;  // XCDs serving this pair
+    const int32_t j = int32_t(blockIdx.x / uint32_t(kNumXcd)) * kx + x / a.B;
+    if (j >= P.nb) return;  // uniform over the work-group
+    double acc[kS];
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    const int64_t i = int64_t(j) * kWG + threadIdx.x;
+    if (i < P.n) {
+        const double X = P.src[3 * i], Y = P.src[3 * i + 1], Z = P.src[3 * i + 2];
+        const float qx = rigid_row(P.R[0], P.R[1], P.R[2], P.t[0], X, Y, Z);
+        const float qy = rigid_row(P.R[3], P.R[4], P.R[5], P.t[1], X, Y, Z);
+        const float qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
+        uint64_t key;
+        uint32_t slot, cn = 0, cp = 0;
+        nn_search<false>(P.tree, qx, qy, qz, a.init, kNoBudget, key, slot, cn, cp);
+        Best b;
+        finish(key, slot, b);
+        if (b.idx >= 0) {
+            const float4 mp = P.tree.pts[b.slot];
+            const double s0 = X - P.c[0], s1 = Y - P.c[1], s2 = Z - P.c[2];
+            const double m0 = double(mp.x) - P.c[0], m1 = double(mp.y) - P.c[1],
+                         m2 = double(mp.z) - P.c[2];
+            acc[0] = s0; acc[1] = s1; acc[2] = s2;
+            acc[3] = m0; acc[4] = m1; acc[5] = m2;
+            acc[6] = s0 * m0; acc[7] = s0 * m1; acc[8] = s0 * m2;
+            acc[9] = s1 * m0; acc[10] = s1 * m1; acc[11] = s1 * m2;
+            acc[12] = s2 * m0; acc[13] = s2 * m1; acc[14] = s2 * m2;
+            acc[15] = double(b.d);
+            acc[16] = 1.0;
+        }
+    }
+    block_sum(acc, red, a.partials + P.part + j, a.total);
+    if (!last_group_of(P.ticket, uint32_t(P.nb))) return;
+#pragma unroll
+    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    for (int32_t g = threadIdx.x; g < P.nb; g += kWG) {
+#pragma unroll
+        for (int c = 0; c < kS; ++c) acc[c] += a.partials[int64_t(c) * a.total + P.part + g];
+    }
+    __syncthreads();  // red[] is reused
+    block_sum(acc, red, P.sums, 1);
+    if (threadIdx.x == 0) atomicExch(P.ticket, 0u);
 }
 
 // ------------------------------------------- residual rejection (3 sigma)
@@ -1663,6 +1751,55 @@ hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, c
     icp_residual_kernel<<<grid, kWG, 0, s>>>(a);
     icp_reject_kernel<<<grid, kWG, 0, s>>>(a);
     return hipGetLastError();
+}
+
+int batch_max_pairs() { return kBatchMax; }
+
+int32_t batch_groups(int64_t n) { return int32_t((n + kWG - 1) / kWG); }
+
+size_t icp_batch_ws_bytes(int32_t B, const int64_t *n)
+{
+    int64_t total = 0;
+    for (int32_t p = 0; p < B; ++p) total += batch_groups(n[p]);
+    return align256(size_t(kS) * size_t(total) * 8) + align256(size_t(B) * 4);
+}
+
+hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void *ws, int32_t total,
+                            hipStream_t s)
+{
+    BatchArgs a{};
+    a.B = B;
+    a.total = total;
+    a.init = host_bound_key(bound2);
+    a.partials = static_cast<double *>(ws);
+    int64_t slots = 0;
+    for (int32_t p = 0; p < B; ++p) {
+        const BatchJob &J = jobs[p];
+        BatchPair &P = a.p[p];
+        P.tree = tree_view(*J.tree);
+        P.src = J.src;
+        P.n = J.n;
+        for (int k = 0; k < 9; ++k) P.R[k] = J.R[k];
+        for (int k = 0; k < 3; ++k) {
+            P.t[k] = J.t[k];
+            P.c[k] = J.tree->center[k];
+        }
+        P.nb = batch_groups(J.n);
+        P.part = J.part;
+        P.ticket = J.ticket;
+        P.sums = J.sums;
+        const int kx = (kNumXcd - p + B - 1) / B;
+        const int64_t per_xcd = (P.nb + kx - 1) / kx;
+        slots = per_xcd > slots ? per_xcd : slots;
+    }
+    icp_batch_kernel<<<dim3(uint32_t(slots * kNumXcd)), kWG, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+uint32_t *batch_tickets(void *ws, int32_t total)
+{
+    return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
+                                        align256(size_t(kS) * size_t(total) * 8));
 }
 
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s)

@@ -1,0 +1,119 @@
+"""GPU parity of the batched registration (icp_align_batch; CUDA-KDTree ICP
+article §3.4: consecutive frames in flight together): every pair of a batch
+must give the single-pair result and the oracle's, to the ICP bar."""
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.test_parity_gpu import (  # noqa: F401  (fixtures)
+    R_TOL, T_TOL, dev, kdnn, lidar, say, scene, torch,
+)
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=None)
+def lidar_oracle(k):
+    p = lidar()[k]
+    return oracle.icp(p.target, p.source, p.iters, leaf_size=16)
+
+
+def _single(kdnn, torch, tree, src, iters, **kw):
+    return tree.icp(dev(torch, src), max_iter=iters, sort=False, **kw)
+
+
+def _close_to_single(b, s, what):
+    assert b["iters"] == s["iters"], what
+    np.testing.assert_allclose(b["E"], s["E"], rtol=1e-9, err_msg=what)
+    assert np.linalg.norm(b["R"] - s["R"]) <= 1e-9, what
+    assert np.max(np.abs(b["t"] - s["t"])) <= 1e-9, what
+
+
+def test_lidar_16_pairs_batch(torch, kdnn):
+    pairs = lidar()
+    trees = [kdnn.Tree(p.target, 16) for p in pairs]
+    say("lidar batch of 16")
+    res = kdnn.icp_batch(trees, [dev(torch, p.source) for p in pairs], max_iter=30)
+    for k, (p, tr, b) in enumerate(zip(pairs, trees, res)):
+        assert b["status"] == 0
+        s = _single(kdnn, torch, tr, p.source, 30)
+        _close_to_single(b, s, f"lidar pair {k}")
+    for k in (0, 15):
+        o = lidar_oracle(k)
+        assert np.linalg.norm(res[k]["R"] - o["R"]) <= R_TOL
+        assert np.max(np.abs(res[k]["t"] - o["t"])) <= T_TOL
+        np.testing.assert_allclose(res[k]["E"], o["E"], rtol=1e-9)
+
+
+def test_mixed_sizes_and_chunks(torch, kdnn):
+    """B = 3 pairs of different sizes (XCD groups of 3/3/2), then B = 9 (a launch
+    of 8 and a launch of 1), with initial transforms and early stopping."""
+    tiny = synth.tiny()
+    sc = scene()
+    pairs = [(tiny.target, tiny.source, 8, 20), (sc.target, sc.source, 16, 30),
+             (lidar()[2].target, lidar()[2].source, 16, 30)]
+    trees = [kdnn.Tree(T, leaf) for T, _, leaf, _ in pairs]
+    say("batch of 3 mixed sizes")
+    res = kdnn.icp_batch(trees, [dev(torch, S) for _, S, _, _ in pairs], max_iter=30)
+    for k, ((T, S, leaf, _), tr, b) in enumerate(zip(pairs, trees, res)):
+        _close_to_single(b, _single(kdnn, torch, tr, S, 30), f"mixed pair {k}")
+
+    rng = np.random.Generator(np.random.PCG64(9))
+    R0 = np.stack([synth.rotation_about(synth.random_unit(rng), 0.01 * k) for k in range(9)])
+    t0 = rng.normal(size=(9, 3)) * 0.01
+    lp = lidar()[:9]
+    trees9 = [kdnn.Tree(p.target, 16) for p in lp]
+    say("batch of 9 with R0, t0, eps")
+    res = kdnn.icp_batch(trees9, [dev(torch, p.source) for p in lp], R0=R0, t0=t0,
+                         max_iter=40, eps=1e-5)
+    for k, (p, tr, b) in enumerate(zip(lp, trees9, res)):
+        s = tr.icp(dev(torch, p.source), R0=R0[k], t0=t0[k], max_iter=40, eps=1e-5, sort=False)
+        _close_to_single(b, s, f"pair {k} of 9")
+
+
+def test_batch_max_dist(torch, kdnn):
+    lp = lidar()[4:7]
+    trees = [kdnn.Tree(p.target, 16) for p in lp]
+    say("batch max_dist")
+    res = kdnn.icp_batch(trees, [dev(torch, p.source) for p in lp], max_iter=30, max_dist=1.0)
+    for k, (p, tr, b) in enumerate(zip(lp, trees, res)):
+        s = _single(kdnn, torch, tr, p.source, 30, max_dist=1.0)
+        _close_to_single(b, s, f"max_dist pair {k}")
+    o = oracle.icp(lp[0].target, lp[0].source, 30, leaf_size=16, max_dist=1.0)
+    assert np.linalg.norm(res[0]["R"] - o["R"]) <= R_TOL
+    assert np.max(np.abs(res[0]["t"] - o["t"])) <= T_TOL
+
+
+def test_batch_degenerate_pair_and_errors(torch, kdnn):
+    tiny = synth.tiny()
+    far = (tiny.source + np.float32(100.0)).astype(np.float32)
+    trees = [kdnn.Tree(tiny.target, 8), kdnn.Tree(tiny.target, 8)]
+    say("batch degenerate pair")
+    res = kdnn.icp_batch(trees, [dev(torch, tiny.source), dev(torch, far)], max_iter=5,
+                         max_dist=0.5)
+    assert res[0]["status"] == 0 and res[0]["iters"] == 5
+    assert res[1]["status"] == 5 and res[1]["iters"] == 0           # EDEGENERATE
+    np.testing.assert_array_equal(res[1]["R"], np.eye(3))
+    s = trees[0].icp(dev(torch, tiny.source), max_iter=5, max_dist=0.5, sort=False)
+    _close_to_single(res[0], s, "healthy pair next to a degenerate one")
+    from kd_tree_nn_amd import _lib
+    import ctypes
+    n = np.array([len(tiny.source)], np.int64)
+    ws = kdnn.icp_batch_workspace(n)
+    R = np.zeros(9)
+    t = np.zeros(3)
+    th = (ctypes.c_void_p * 1)(trees[0]._h.value)
+    sp = (ctypes.c_void_p * 1)(dev(torch, tiny.source).data_ptr())
+    L = _lib.lib()
+    args = lambda flags, rej, wsz: L.icp_align_batch(  # noqa: E731
+        1, th, sp, n.ctypes.data_as(ctypes.POINTER(_lib.c_i64)), None, None, 3, 0.0,
+        R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp), None, None, None, flags,
+        rej, ws.data_ptr(), wsz, None)
+    assert args(_lib.lanes_flag(4), None, ws.numel()) == _lib.KDNN_EINVAL  # a schedule flag
+    assert args(0, ctypes.byref(_lib.IcpReject(1.0, 3.0)), ws.numel()) == _lib.KDNN_EINVAL
+    assert args(0, None, 16) == _lib.KDNN_EINVAL                           # workspace too small
+    assert args(0, None, ws.numel()) == _lib.KDNN_OK
