@@ -10,4 +10,5 @@ fp64 solve (see ``ref.py`` for each function's citation and its pins).
 from .ref import (  # noqa: F401
     brute_nn, KDTree, transform, reduce_pairs, horn, kabsch_svd, icp,
     rot_err, trans_err, mse_converged, max_dist_bound, residual_sq, reject_sigma, solve_rigid,
+    voxel_downsample,
 )

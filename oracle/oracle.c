@@ -227,3 +227,79 @@ void okd_query(const void *h, const float *Q, int64_t m, int32_t *idx, float *d2
         if (visits_or_null) visits_or_null[i] = s.visits;
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* O9: voxel-grid down-sampling (article §4.3: voxel filter before the     */
+/* tree is built).  The plain definition:                                  */
+/*   voxel of p = (floor(p_x / leaf), floor(p_y / leaf), floor(p_z / leaf))*/
+/*   with each quotient in fp64 (the fp32 coordinate promoted exactly);    */
+/*   points with a non-finite coordinate belong to no voxel;               */
+/*   every occupied voxel gives one point, the mean of its points: fp64    */
+/*   sums taken in ascending original index, divided by the count, one     */
+/*   round-to-nearest cast to fp32;                                        */
+/*   voxels are listed by ascending linear key                             */
+/*   (vx - min vx) + Nx ((vy - min vy) + Ny (vz - min vz)) over the grid   */
+/*   spanned by the occupied voxels.                                       */
+/* Returns the number of voxels M; out (>= M x 3) and counts (>= M).       */
+/* ---------------------------------------------------------------------- */
+typedef struct {
+    int64_t key;
+    int64_t idx;
+} vox_item;
+
+static int cmp_vox(const void *a, const void *b)
+{
+    const vox_item *x = (const vox_item *)a, *y = (const vox_item *)b;
+    if (x->key != y->key) return x->key < y->key ? -1 : 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+int64_t oracle_voxel(const float *P, int64_t n, double leaf, float *out, int32_t *counts)
+{
+    int64_t *v = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * 3 * sizeof(int64_t));
+    vox_item *it = (vox_item *)malloc((size_t)(n > 0 ? n : 1) * sizeof(vox_item));
+    int64_t lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0}, nf = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const float *p = P + 3 * i;
+        if (!(isfinite(p[0]) && isfinite(p[1]) && isfinite(p[2]))) continue;
+        for (int a = 0; a < 3; ++a) {
+            const int64_t c = (int64_t)floor((double)p[a] / leaf);
+            v[3 * i + a] = c;
+            if (nf == 0 || c < lo[a]) lo[a] = c;
+            if (nf == 0 || c > hi[a]) hi[a] = c;
+        }
+        ++nf;
+    }
+    const int64_t nx = hi[0] - lo[0] + 1, ny = hi[1] - lo[1] + 1;
+    int64_t k = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const float *p = P + 3 * i;
+        if (!(isfinite(p[0]) && isfinite(p[1]) && isfinite(p[2]))) continue;
+        it[k].key = (v[3 * i] - lo[0]) + nx * ((v[3 * i + 1] - lo[1]) + ny * (v[3 * i + 2] - lo[2]));
+        it[k].idx = i;
+        ++k;
+    }
+    qsort(it, (size_t)nf, sizeof(vox_item), cmp_vox);
+    int64_t m = 0;
+    for (int64_t s = 0; s < nf;) {
+        int64_t e = s;
+        double sx = 0.0, sy = 0.0, sz = 0.0;
+        while (e < nf && it[e].key == it[s].key) {
+            const float *p = P + 3 * it[e].idx;
+            sx += (double)p[0];
+            sy += (double)p[1];
+            sz += (double)p[2];
+            ++e;
+        }
+        const double c = (double)(e - s);
+        out[3 * m] = (float)(sx / c);
+        out[3 * m + 1] = (float)(sy / c);
+        out[3 * m + 2] = (float)(sz / c);
+        counts[m] = (int32_t)(e - s);
+        ++m;
+        s = e;
+    }
+    free(v);
+    free(it);
+    return m;
+}

@@ -15,6 +15,9 @@ reduce_pairs    (O4)          §2.1 centroids, de-centring, H, and E   closed fo
 horn / kabsch   (O5)          §2.1 rigid solve from H                 known-motion recovery, Horn == SVD, det = +1
 icp             (O6)          §2.1 loop, §3.3 main loop, §4.6 rule    known-motion recovery, E non-increasing
 rot_err, trans_err (O7)       §6 regression metrics                   known rotation angles
+max_dist_bound, residual_sq,  §4.4 correspondence rejection           hand values, inclusive bound, outlier recovery
+reject_sigma (O8)
+voxel_downsample (O9)         §4.3 voxel filter before the tree       hand voxels, dict-based grouping, idempotence
 """
 
 from __future__ import annotations
@@ -54,6 +57,8 @@ def _load():
     lib.okd_node_count.restype = i64
     lib.okd_query.argtypes = [ctypes.c_void_p, _f32p, i64, _i32p, _f32p, ctypes.c_void_p]
     lib.okd_query.restype = None
+    lib.oracle_voxel.argtypes = [_f32p, i64, ctypes.c_double, _f32p, _i32p]
+    lib.oracle_voxel.restype = i64
     _lib = lib
     return lib
 
@@ -252,6 +257,27 @@ def reject_sigma(src, matched, R, t, k: float):
     sigma2 = float(r2.sum()) / n if n else 0.0
     thr = (float(k) * float(k)) * sigma2
     return r2 <= thr, sigma2, thr
+
+
+# ---------------------------------------------------------------------------
+# O9: voxel-grid down-sampling (§4.3)
+# ---------------------------------------------------------------------------
+def voxel_downsample(points, leaf: float):
+    """One point per occupied voxel of side ``leaf`` (§4.3 voxel filter).
+
+    Voxel of p: floor(p_a / leaf) per axis in float64.  Each voxel yields the
+    mean of its points (float64 sums in ascending point index, one cast to
+    float32), listed by ascending linear key over the occupied voxels' grid
+    (x fastest, z slowest).  Non-finite points are dropped.  Returns
+    (centroids float32 (M, 3), counts int32 (M,)).  Plain C in ``oracle.c``.
+    """
+    P = _pts(points)
+    if not (leaf > 0 and np.isfinite(leaf)):
+        raise ValueError("leaf must be finite and > 0")
+    out = np.empty((max(len(P), 1), 3), np.float32)
+    cnt = np.empty(max(len(P), 1), np.int32)
+    m = int(_load().oracle_voxel(P, len(P), float(leaf), out, cnt))
+    return out[:m].copy(), cnt[:m].copy()
 
 
 # ---------------------------------------------------------------------------
