@@ -372,6 +372,33 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
                             uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
                             size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------- preprocessing */
+
+/* Bytes of device workspace voxel_downsample needs for n points. */
+size_t voxel_downsample_workspace_bytes(int64_t n);
+
+/* Voxel-grid down-sampling (article §4.3: filter the cloud with a voxel grid
+ * before building the tree; leaf 0.05-0.1 m indoors, 0.2-0.5 m outdoors).
+ * The voxel of p is (floor(p_x / leaf), floor(p_y / leaf), floor(p_z / leaf)),
+ * each quotient in fp64.  Every occupied voxel yields one point, the mean of
+ * its points (fp64 sums in ascending point index, one round-to-nearest cast
+ * to fp32).  Voxels come out by ascending linear key
+ * (vx - min vx) + Nx ((vy - min vy) + Ny (vz - min vz)) over the grid spanned
+ * by the occupied voxels (x fastest).  Points with a non-finite coordinate
+ * belong to no voxel.
+ *   xyz_dev    : n x 3 fp32 points (device).
+ *   leaf       : voxel side, finite and > 0.
+ *   out_dev    : room for n x 3 fp32 (device); the first *m_out rows are set.
+ *   m_out      : host, number of voxels.
+ *   counts_dev : optional, room for n int32: points per voxel.
+ *   ws_dev     : >= voxel_downsample_workspace_bytes(n), 256-byte aligned.
+ * Synchronises stream.  n == 0 gives *m_out = 0.
+ * Errors: EINVAL (also when the grid over the cloud's extent would need
+ * 2^32 cells or more), EDEVICE. */
+kdnn_status voxel_downsample(const float *xyz_dev, int64_t n, double leaf, float *out_dev,
+                             int64_t *m_out, int32_t *counts_dev, void *ws_dev, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* ---------------------------------------------------------------- misc */
 
 /* Text of the last error on the calling thread ("" if none).  Valid until the

@@ -25,7 +25,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["Tree", "transform", "procrustes", "build_host", "layout", "sums_to_dict",
-           "icp_batch", "icp_batch_workspace", "KdnnError", "version"]
+           "icp_batch", "icp_batch_workspace", "voxel_downsample", "KdnnError", "version"]
 
 
 def _torch():
@@ -345,6 +345,27 @@ def icp_batch(trees, sources, R0=None, t0=None, max_iter: int = 30, eps: float =
         _lib.check(status, "icp_align_batch")
     return [{"R": R[p].reshape(3, 3), "t": t[p], "E": E[p, :it[p]], "iters": int(it[p]),
              "status": int(st[p])} for p in range(B)]
+
+
+def voxel_downsample(points, leaf: float, return_counts: bool = False, workspace=None,
+                     stream=None):
+    """One point per occupied voxel of side ``leaf`` (the mean of its points),
+    ordered by linear voxel key; device in, device out (voxel_downsample)."""
+    torch = _torch()
+    x = _dev_points(points, "points")
+    n = x.shape[0]
+    out = torch.empty((max(n, 1), 3), dtype=torch.float32, device=x.device)
+    cnt = torch.empty(max(n, 1), dtype=torch.int32, device=x.device) if return_counts else None
+    ws = workspace
+    if ws is None and n > 0:
+        ws = torch.empty(int(_lib.lib().voxel_downsample_workspace_bytes(n)), dtype=torch.uint8,
+                         device=x.device)
+    m = ctypes.c_int64(0)
+    _lib.check(_lib.lib().voxel_downsample(
+        _ptr(x), n, float(leaf), _ptr(out), ctypes.byref(m), _ptr(cnt), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)), "voxel_downsample")
+    k = m.value
+    return (out[:k], cnt[:k]) if return_counts else out[:k]
 
 
 def procrustes(sums) -> tuple:

@@ -91,6 +91,9 @@ SIGNATURES = {
                                 ctypes.c_double, c_dp, c_dp, c_dp, ctypes.POINTER(c_i32),
                                 ctypes.POINTER(c_i32), c_u32, ctypes.POINTER(IcpReject), c_vp,
                                 c_sz, c_vp]),
+    "voxel_downsample_workspace_bytes": (c_sz, [c_i64]),
+    "voxel_downsample": (c_i32, [c_vp, c_i64, ctypes.c_double, c_vp, ctypes.POINTER(c_i64), c_vp,
+                                 c_vp, c_sz, c_vp]),
     "kdnn_last_error": (ctypes.c_char_p, []),
     "kdnn_version": (c_i32, []),
 }

@@ -124,6 +124,36 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
                             float bound2, bool keep_matches, hipStream_t s);
+// One stable LSD radix pass (8-bit digit at `shift`) of (key, value) pairs;
+// hist: 256 x radix_tiles(m) words, totals: 256 words.
+int32_t radix_tiles(int64_t m);
+hipError_t launch_radix_pass(const uint32_t *keys_in, const int32_t *vals_in, int shift,
+                             uint32_t *keys_out, int32_t *vals_out, int64_t m, uint32_t *hist,
+                             uint32_t *totals, hipStream_t s);
+// In-place exclusive scan of row[0..len); *total = the sum.  One work-group.
+hipError_t launch_scan_row(uint32_t *row, int32_t len, uint32_t *total, hipStream_t s);
+
+// Voxel-grid filter (voxel.hip).
+struct VoxelWorkspace {
+    uint32_t *keys_a, *keys_b;
+    int32_t *vals_a, *vals_b;
+    uint32_t *hist, *totals;
+    uint32_t *tile_heads;   // [tiles]
+    int32_t *starts;        // [n] first sorted position of each voxel
+    float *bbox_part;       // [7][kVoxBlocks]: min xyz, max xyz, finite count
+    float *bbox;            // [8]: min xyz, max xyz, finite count (as float bits), pad
+    uint32_t *nvox;         // [1]
+};
+size_t voxel_ws_bytes(int64_t n);
+VoxelWorkspace carve_voxel_workspace(void *ws, int64_t n);
+hipError_t launch_voxel_bbox(const float *xyz, int64_t n, const VoxelWorkspace &w, hipStream_t s);
+// key grid: voxel v = floor(p / leaf) - vmin, key = vx + dims[0] (vy + dims[1] vz);
+// non-finite points get key `sentinel` (= dims product); passes = radix passes.
+hipError_t launch_voxel_filter(const float *xyz, int64_t n, double leaf, const int64_t *vmin,
+                               const uint32_t *dims, uint32_t sentinel, int passes,
+                               int64_t n_finite, const VoxelWorkspace &w, float *out,
+                               int32_t *counts, hipStream_t s);
+
 // Batched correspondence steps: up to batch_max_pairs() (tree, source) pairs
 // per launch, one pair per group of XCDs.  ws: icp_batch_ws_bytes layout
 // (partials of `total` work-group columns, then one ticket per pair).
