@@ -63,7 +63,7 @@ def log(*a):
 
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench "
-             "-- python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline")
+             "-- python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline --headline-only")
 PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} "
            "-o pmc -- python3 -u bench.py --profile-pass")
 
@@ -149,6 +149,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the rejection, leaf/axis sweep, LiDAR batch and voxel sections "
+                         "(the kernel trace of the Scene workload alone)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="only: 30 fused launches of the Scene ICP iterations, then a "
                          f"{COPY_MIB} MiB device copy (calibration for HBM counters)")
@@ -219,79 +222,122 @@ def main():
     iters_per_s = args.steps * ITERS / T
     log(f"{value / 1e9:.3f} G queries/s, {iters_per_s:.0f} ICP iterations/s")
 
-    # ---------------------------------- the same registration with rejection
-    # (article §4.4: max_dist fused into the search, then 3-sigma residual
-    # rejection and a second solve per iteration)
-    REJ = {"max_dist": 1.0, "reject_k": 3.0}
-    for _ in range(2):
-        tree.icp(src, max_iter=ITERS, workspace=ws, **REJ)
-    torch.cuda.synchronize()
-    rsteps = max(args.steps // 2, 1)
-    t0 = time.perf_counter()
-    for _ in range(rsteps):
-        gr = tree.icp(src, max_iter=ITERS, workspace=ws, **REJ)
-    torch.cuda.synchronize()
-    Tr = time.perf_counter() - t0
-    rej = {"max_dist_m": REJ["max_dist"], "reject_k": REJ["reject_k"], "steps": rsteps,
-           "icp_iters_per_s": round(rsteps * ITERS / Tr, 1),
-           "icp_iter_us": round(Tr / (rsteps * ITERS) * 1e6, 2),
-           "queries_per_s": round(rsteps * ITERS * n / Tr)}
-    log(f"with rejection: {rej['icp_iters_per_s']:.0f} ICP iterations/s")
-
-    # ----------------------- LiDAR frame pairs: batched vs one after another
-    # (article §3.4: consecutive frames in flight together)
-    log("LiDAR: 16 frame pairs, 30 iterations each")
-    lp = synth.lidar_pairs()
-    ltrees = [kdnn.Tree(q.target, q.leaf_size) for q in lp]
-    lsrc = [torch.from_numpy(np.ascontiguousarray(q.source)).cuda() for q in lp]
-    bws = kdnn.icp_batch_workspace([len(x) for x in lsrc])
-    lws = [t_.icp_workspace(len(x)) for t_, x in zip(ltrees, lsrc)]
-
-    def run_batch():
-        return kdnn.icp_batch(ltrees, lsrc, max_iter=ITERS, workspace=bws)
-
-    def run_seq():
-        return [t_.icp(x, max_iter=ITERS, workspace=w_, sort=False)
-                for t_, x, w_ in zip(ltrees, lsrc, lws)]
-
-    lid = {"pairs": len(lp), "points_per_frame": int(np.mean([len(x) for x in lsrc])),
-           "iterations": ITERS}
-    for name, fn in (("batched", run_batch), ("sequential", run_seq)):
-        fn()
+    rej, sweep, lid, vox = None, None, None, None
+    if not args.headline_only:
+        # ---------------------------------- the same registration with rejection
+        # (article §4.4: max_dist fused into the search, then 3-sigma residual
+        # rejection and a second solve per iteration)
+        REJ = {"max_dist": 1.0, "reject_k": 3.0}
+        for _ in range(2):
+            tree.icp(src, max_iter=ITERS, workspace=ws, **REJ)
         torch.cuda.synchronize()
-        reps = 5
+        rsteps = max(args.steps // 2, 1)
+        t0 = time.perf_counter()
+        for _ in range(rsteps):
+            gr = tree.icp(src, max_iter=ITERS, workspace=ws, **REJ)
+        torch.cuda.synchronize()
+        Tr = time.perf_counter() - t0
+        rej = {"max_dist_m": REJ["max_dist"], "reject_k": REJ["reject_k"], "steps": rsteps,
+               "icp_iters_per_s": round(rsteps * ITERS / Tr, 1),
+               "icp_iter_us": round(Tr / (rsteps * ITERS) * 1e6, 2),
+               "queries_per_s": round(rsteps * ITERS * n / Tr)}
+        log(f"with rejection: {rej['icp_iters_per_s']:.0f} ICP iterations/s")
+
+        # ------------------ builder variants: leaf size and split-axis rule sweep
+        # (article §4.1 leaf table, §4.2 max-variance vs round-robin axis)
+        log("leaf / axis sweep on the Scene target")
+        q_it0 = src
+        sweep = []
+        for rr in (False, True):
+            for leaf in (1, 4, 8, 16, 32, 64):
+                tr = kdnn.Tree(p.target, leaf, round_robin=rr)
+                inf_ = tr.info
+                out_ = (torch.empty(n, dtype=torch.int32, device="cuda"),
+                        torch.empty(n, dtype=torch.float32, device="cuda"))
+                qw = tr.query_workspace(n)
+                tr.query(q_it0, out=out_, workspace=qw)
+                ts = []
+                for _ in range(10):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    tr.query(q_it0, out=out_, workspace=qw)
+                    e1.record(stream)
+                    ts.append((e0, e1))
+                _, _, cn_, cp_ = tr.query_stats(q_it0)
+                torch.cuda.synchronize()
+                iw = tr.icp_workspace(n)
+                tr.icp(src, max_iter=ITERS, workspace=iw)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(3):
+                    tr.icp(src, max_iter=ITERS, workspace=iw)
+                torch.cuda.synchronize()
+                sweep.append({
+                    "axis": "round_robin" if rr else "max_variance", "leaf": leaf,
+                    "depth": inf_["depth"], "host_build_ms": round(inf_["build_ms"], 2),
+                    "device_mb": round(inf_["device_bytes"] / 2**20, 2),
+                    "nn_query_us": round(float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3, 1),
+                    "nodes_per_query": round(float(cn_.float().mean()), 2),
+                    "points_per_query": round(float(cp_.float().mean()), 2),
+                    "icp_iter_us": round((time.perf_counter() - t0) / (3 * ITERS) * 1e6, 1)})
+                del tr
+        log("sweep:", [(r["axis"][0], r["leaf"], r["nn_query_us"]) for r in sweep])
+
+        # ----------------------- LiDAR frame pairs: batched vs one after another
+        # (article §3.4: consecutive frames in flight together)
+        log("LiDAR: 16 frame pairs, 30 iterations each")
+        lp = synth.lidar_pairs()
+        ltrees = [kdnn.Tree(q.target, q.leaf_size) for q in lp]
+        lsrc = [torch.from_numpy(np.ascontiguousarray(q.source)).cuda() for q in lp]
+        bws = kdnn.icp_batch_workspace([len(x) for x in lsrc])
+        lws = [t_.icp_workspace(len(x)) for t_, x in zip(ltrees, lsrc)]
+
+        def run_batch():
+            return kdnn.icp_batch(ltrees, lsrc, max_iter=ITERS, workspace=bws)
+
+        def run_seq():
+            return [t_.icp(x, max_iter=ITERS, workspace=w_, sort=False)
+                    for t_, x, w_ in zip(ltrees, lsrc, lws)]
+
+        lid = {"pairs": len(lp), "points_per_frame": int(np.mean([len(x) for x in lsrc])),
+               "iterations": ITERS}
+        for name, fn in (("batched", run_batch), ("sequential", run_seq)):
+            fn()
+            torch.cuda.synchronize()
+            reps = 5
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+            T_ = (time.perf_counter() - t0) / reps
+            q_ = sum(len(x) for x in lsrc) * ITERS
+            lid[name] = {"ms_per_16_pairs": round(T_ * 1e3, 3), "pairs_per_s": round(len(lp) / T_, 1),
+                         "icp_iters_per_s": round(len(lp) * ITERS / T_, 1),
+                         "queries_per_s": round(q_ / T_)}
+        lid["speedup"] = round(lid["sequential"]["ms_per_16_pairs"] / lid["batched"]["ms_per_16_pairs"], 2)
+        log(f"LiDAR batched {lid['batched']['pairs_per_s']} pairs/s, "
+            f"sequential {lid['sequential']['pairs_per_s']} pairs/s")
+
+        # ------------------------------- voxel-grid down-sampling (article §4.3)
+        # ~1M points: the first 8 LiDAR frames stacked (each in its own sensor
+        # frame), filtered at 0.2 m (the article's outdoor range 0.2-0.5 m)
+        vox_in = torch.cat(lsrc[:8]).contiguous()
+        vws = torch.empty(int(kdnn._lib.lib().voxel_downsample_workspace_bytes(len(vox_in))),
+                          dtype=torch.uint8, device="cuda")
+        vox = {"input_points": int(len(vox_in)), "leaf_m": 0.2}
+        vout = kdnn.voxel_downsample(vox_in, 0.2, workspace=vws)
+        torch.cuda.synchronize()
+        reps = 10
         t0 = time.perf_counter()
         for _ in range(reps):
-            fn()
+            vout = kdnn.voxel_downsample(vox_in, 0.2, workspace=vws)
         torch.cuda.synchronize()
-        T_ = (time.perf_counter() - t0) / reps
-        q_ = sum(len(x) for x in lsrc) * ITERS
-        lid[name] = {"ms_per_16_pairs": round(T_ * 1e3, 3), "pairs_per_s": round(len(lp) / T_, 1),
-                     "icp_iters_per_s": round(len(lp) * ITERS / T_, 1),
-                     "queries_per_s": round(q_ / T_)}
-    lid["speedup"] = round(lid["sequential"]["ms_per_16_pairs"] / lid["batched"]["ms_per_16_pairs"], 2)
-    log(f"LiDAR batched {lid['batched']['pairs_per_s']} pairs/s, "
-        f"sequential {lid['sequential']['pairs_per_s']} pairs/s")
-
-    # ------------------------------- voxel-grid down-sampling (article §4.3)
-    # ~1M points: the first 8 LiDAR frames stacked (each in its own sensor
-    # frame), filtered at 0.2 m (the article's outdoor range 0.2-0.5 m)
-    vox_in = torch.cat(lsrc[:8]).contiguous()
-    vws = torch.empty(int(kdnn._lib.lib().voxel_downsample_workspace_bytes(len(vox_in))),
-                      dtype=torch.uint8, device="cuda")
-    vox = {"input_points": int(len(vox_in)), "leaf_m": 0.2}
-    vout = kdnn.voxel_downsample(vox_in, 0.2, workspace=vws)
-    torch.cuda.synchronize()
-    reps = 10
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        vout = kdnn.voxel_downsample(vox_in, 0.2, workspace=vws)
-    torch.cuda.synchronize()
-    Tv = (time.perf_counter() - t0) / reps
-    vox.update({"voxels": int(len(vout)), "ms": round(Tv * 1e3, 3),
-                "points_per_s": round(len(vox_in) / Tv),
-                "note": "wall time of the synchronous call (two host round trips included)"})
-    log(f"voxel filter: {vox['input_points']} -> {vox['voxels']} in {vox['ms']} ms")
+        Tv = (time.perf_counter() - t0) / reps
+        vox.update({"voxels": int(len(vout)), "ms": round(Tv * 1e3, 3),
+                    "points_per_s": round(len(vox_in) / Tv),
+                    "note": "wall time of the synchronous call (two host round trips included)"})
+        log(f"voxel filter: {vox['input_points']} -> {vox['voxels']} in {vox['ms']} ms")
 
     # ------------------------------------------- fused kernel: events per launch
     # The library launches on torch's current stream; the events bracket each
@@ -389,6 +435,7 @@ def main():
         "icp_iters_per_s": round(iters_per_s, 1),
         "icp_with_rejection": rej,
         "lidar_pairs": lid,
+        "leaf_axis_sweep": sweep,
         "voxel_downsample": vox,
         "icp_iter_us": round(T / (args.steps * ITERS) * 1e6, 2),
         "build": {"host_build_ms": round(info["build_ms"], 3),

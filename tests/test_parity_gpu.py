@@ -425,3 +425,29 @@ def test_lidar_pairs(torch, kdnn):
             assert np.linalg.norm(g["R"] - o["R"]) <= R_TOL
             assert np.max(np.abs(g["t"] - o["t"])) <= T_TOL
             assert np.degrees(oracle.rot_err(g["R"], p.R_true)) < 0.5
+
+
+# ------------------------------------------------ builder variants (leaf sweep)
+@pytest.mark.parametrize("leaf", [1, 4, 32, 64])
+@pytest.mark.parametrize("round_robin", [False, True], ids=["maxvar", "roundrobin"])
+def test_scene_builder_variants(torch, kdnn, leaf, round_robin):
+    """The tree's shape (leaf size, split-axis rule) never changes a result:
+    same pairs as the oracle, and the same registration."""
+    p = scene()
+    otree, o = scene_oracle_icp()
+    tree = kdnn.Tree(p.target, leaf, round_robin=round_robin)
+    n = len(p.target)
+    D = tree.info["depth"]
+    assert 2 ** D * leaf >= n and (D == 0 or 2 ** (D - 1) * leaf < n)
+    src = dev(torch, p.source)
+    for k in (0, p.iters - 1):
+        R = o["Rt_hist"][k, :9].reshape(3, 3)
+        t = o["Rt_hist"][k, 9:]
+        say("builder variant", leaf, round_robin, "iteration", k)
+        oi, od, red = _pairs_oracle(p.target, p.source, R, t, otree)
+        res = tree.correspond_reduce(src, R, t, return_pairs=True)
+        assert_nn_equal(res["idx"], res["d2"], oi, od, f"leaf {leaf} rr {round_robin} it{k}")
+        check_sums(res, red, bbox_diag(p.target), f"leaf {leaf} rr {round_robin} it{k}")
+    g = tree.icp(src, max_iter=p.iters)
+    assert np.linalg.norm(g["R"] - o["R"]) <= R_TOL
+    assert np.max(np.abs(g["t"] - o["t"])) <= T_TOL
