@@ -419,6 +419,92 @@ __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, flo
     }
 }
 
+// ------------------------------------------------ pair-load search (one lane)
+//
+// The default single-lane search.  Entering an internal node loads the
+// records of both its children together (one aligned 64-byte line); their
+// box bounds set the visiting order (smaller bound first) and tell at once
+// whether the other child can be dropped -- for good, since the best
+// distance only shrinks.  The other child's bound is kept per path level in
+// LDS (one float per level and lane) and a bit of `pend` marks it as still
+// pending, so coming back to it costs an LDS read instead of a memory round
+// trip, and a node is never fetched twice.  Exactness is as above: a child is
+// skipped only when its box bound exceeds the best distance at that moment.
+//
+// Path levels: bit d of `pend` and lbs[d * kWG] belong to depth d + 1.
+
+// The node to enter after the subtree of i is finished: the pending second
+// child at the deepest path level whose bound is still <= best; kDone if none.
+__device__ __forceinline__ uint32_t pair_next(uint32_t i, uint32_t &pend, const float *lbs,
+                                              float best)
+{
+    const uint32_t dep = 31u - uint32_t(__clz(int(i)));
+    uint32_t cand = pend & ((1u << dep) - 1u);
+    while (cand != 0u) {
+        const uint32_t h = 31u - uint32_t(__clz(int(cand)));
+        if (enters(lbs[h * kWG], best)) {
+            pend &= (1u << h) - 1u;  // level h + 1 now holds its second child
+            return (i >> (dep - h - 1u)) ^ 1u;
+        }
+        cand &= ~(1u << h);
+    }
+    return kDone;
+}
+
+// lbs: this lane's column of an LDS array [kDevMaxDepth][kWG].
+template <bool STATS>
+__device__ __forceinline__ void nn_search_pair(const TreeView &t, float qx, float qy, float qz,
+                                               uint64_t init, float *lbs, uint64_t &key,
+                                               uint32_t &slot, uint32_t &cn, uint32_t &cp)
+{
+    key = init;
+    slot = 0;
+    if (!(isfinite(qx) && isfinite(qy) && isfinite(qz))) return;
+    uint32_t i;
+    {
+        const float4 A = t.nodes[2];
+        const float4 B = t.nodes[3];
+        if (STATS) ++cn;
+        i = enters(box_lb(qx, qy, qz, A, B), key_dist(key)) ? 1u : kDone;
+    }
+    uint32_t pend = 0;
+    for (;;) {
+        // Phase 1: internal nodes (entered), until a leaf or the end.
+        while (i < t.first_leaf) {
+            const float4 A0 = t.nodes[4 * i];
+            const float4 B0 = t.nodes[4 * i + 1];
+            const float4 A1 = t.nodes[4 * i + 2];
+            const float4 B1 = t.nodes[4 * i + 3];
+            if (STATS) cn += 2;
+            const float l0 = box_lb(qx, qy, qz, A0, B0);
+            const float l1 = box_lb(qx, qy, qz, A1, B1);
+            const bool swap = l1 < l0;
+            const float lf = swap ? l1 : l0, ls = swap ? l0 : l1;
+            const float best = key_dist(key);
+            const uint32_t d = 31u - uint32_t(__clz(int(i)));  // children's level bit
+            if (enters(lf, best)) {
+                lbs[d * kWG] = ls;
+                pend = enters(ls, best) ? (pend | (1u << d)) : (pend & ~(1u << d));
+                i = 2 * i + (swap ? 1u : 0u);
+            } else {
+                i = pair_next(i, pend, lbs, best);
+            }
+        }
+        if (i == kDone) return;
+        // Phase 2: leaf i (entered) -- its points, in batches of kLeafChunk.
+        int32_t begin, last, end;
+        leaf_range(t, i, begin, last, end);
+        for (int32_t k0 = begin; k0 < end; k0 += kLeafChunk) {
+            float4 p[kLeafChunk];
+            int32_t sl[kLeafChunk];
+            load_points<kLeafChunk, 1>(t, k0, last, p, sl);
+            rank_points<kLeafChunk>(p, sl, qx, qy, qz, key, slot);
+        }
+        if (STATS) cp += uint32_t(end - begin);
+        i = pair_next(i, pend, lbs, key_dist(key));
+    }
+}
+
 struct NnArgs {
     TreeView tree;
     uint64_t init;    // bound key (bound +inf: none)
@@ -434,12 +520,13 @@ struct NnArgs {
 
 template <int G, bool STATS>
 __device__ __forceinline__ void search_query(const TreeView &t, float qx, float qy, float qz,
-                                             uint64_t init, Best &b, uint32_t &cn, uint32_t &cp)
+                                             uint64_t init, float *lbs, Best &b, uint32_t &cn,
+                                             uint32_t &cp)
 {
     uint64_t key = init;
     uint32_t slot = 0;
     if (G == 1)
-        nn_search<STATS>(t, qx, qy, qz, init, kNoBudget, key, slot, cn, cp);
+        nn_search_pair<STATS>(t, qx, qy, qz, init, lbs, key, slot, cn, cp);
     else if (isfinite(qx) && isfinite(qy) && isfinite(qz))
         nn_search_group<G, STATS>(t, qx, qy, qz, false, key, slot, cn, cp);
     finish(key, slot, b);
@@ -451,6 +538,7 @@ template <int G, bool STATS>
 __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
 {
     constexpr int QPB = kWG / G;
+    __shared__ float lbs[G == 1 ? kDevMaxDepth * kWG : 1];
     const uint32_t nb = gridDim.x;
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
     const int gl = threadIdx.x & (G - 1);
@@ -461,7 +549,7 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             const float qx = a.q[3 * i], qy = a.q[3 * i + 1], qz = a.q[3 * i + 2];
             Best b;
             uint32_t cn = 0, cp = 0;
-            search_query<G, STATS>(a.tree, qx, qy, qz, a.init, b, cn, cp);
+            search_query<G, STATS>(a.tree, qx, qy, qz, a.init, lbs + threadIdx.x, b, cn, cp);
             if (gl == 0) {
                 a.idx[i] = b.idx;
                 a.d2[i] = b.d;
@@ -834,6 +922,7 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
     constexpr int QPB = kWG / G;
     const int gl = threadIdx.x & (G - 1);
     __shared__ double red[(kWG / 64) * kS];
+    __shared__ float lbs[G == 1 ? kDevMaxDepth * kWG : 1];
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
@@ -848,7 +937,7 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         icp_query(a, i, X, Y, Z, qx, qy, qz);
         Best b;
         uint32_t cn = 0, cp = 0;
-        search_query<G, false>(a.tree, qx, qy, qz, a.init, b, cn, cp);
+        search_query<G, false>(a.tree, qx, qy, qz, a.init, lbs + threadIdx.x, b, cn, cp);
         if (gl == 0) icp_accumulate(a, i, X, Y, Z, b, acc);
     }
     block_sum(acc, red, a.partials + blockIdx.x, nb);
@@ -997,6 +1086,7 @@ struct BatchArgs {
 __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
+    __shared__ float lbs[kDevMaxDepth * kWG];
     const int x = int(blockIdx.x % uint32_t(kNumXcd));
     const int pi = x % a.B;
     const BatchPair &P = a.p[pi];
@@ -1014,7 +1104,7 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
         const float qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
         uint64_t key;
         uint32_t slot, cn = 0, cp = 0;
-        nn_search<false>(P.tree, qx, qy, qz, a.init, kNoBudget, key, slot, cn, cp);
+        nn_search_pair<false>(P.tree, qx, qy, qz, a.init, lbs + threadIdx.x, key, slot, cn, cp);
         Best b;
         finish(key, slot, b);
         if (b.idx >= 0) {
