@@ -142,6 +142,65 @@ def summarize(trace_dir, fetch_dir, write_dir):
     print("\n".join(out))
 
 
+PMC_SETS = {
+    "sq1": "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+           "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INST_LEVEL_VMEM",
+    "mem": "TCC_HIT_sum TCC_MISS_sum TCC_REQ_sum TCP_PENDING_STALL_CYCLES_sum "
+           "TCP_READ_TAGCONFLICT_STALL_CYCLES_sum TCP_TCC_READ_REQ_sum "
+           "TCP_TOTAL_CACHE_ACCESSES_sum TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum "
+           "GRBM_GUI_ACTIVE",
+    "sq2": "SQ_THREAD_CYCLES_VALU SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VMEM SQ_INST_CYCLES_VMEM_RD "
+           "SQ_WAIT_ANY SQ_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT",
+}
+
+
+def summarize_counters(root):
+    """profiles/ summary of the three counter passes (PMC_SETS) over
+    `bench.py --profile-pass`, per dispatch of the fused kernel."""
+    import csv
+
+    import numpy as np
+    val = {}
+    for name in PMC_SETS:
+        per = {}
+        with open(os.path.join(root, f"pmc_{name}", "pmc_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if "icp_fused_kernel" in r["Kernel_Name"]:
+                    per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+                    per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for c, d in per.items():
+            val[c] = float(np.mean(list(d.values())))
+    waves = val["SQ_WAVES"]
+    derived = [
+        ("L2 hit rate", val["TCC_HIT_sum"] / max(val["TCC_REQ_sum"], 1)),
+        ("L1 hit rate (1 - L1->L2 reads / L1 accesses)",
+         1 - val["TCP_TCC_READ_REQ_sum"] / max(val["TCP_TOTAL_CACHE_ACCESSES_sum"], 1)),
+        ("VALU lane utilisation (thread-cycles / (64 x VALU cycles))",
+         val["SQ_THREAD_CYCLES_VALU"] / max(64 * val["SQ_ACTIVE_INST_VALU"], 1)),
+        ("VALU instructions per wave", val["SQ_INSTS_VALU"] / waves),
+        ("vector-memory read instructions per wave", val["SQ_INSTS_VMEM_RD"] / waves),
+        ("LDS instructions per wave", val["SQ_INSTS_LDS"] / waves),
+        ("LDS bank conflicts per dispatch", val["SQ_LDS_BANK_CONFLICT"]),
+        ("address unit busy (TA busy / (CUs x GPU-active cycles per XCD))",
+         val["TA_TA_BUSY_sum"] / (256 * val["GRBM_GUI_ACTIVE"] / 8)),
+    ]
+    out = ["# rocprofv3 counters of icp_fused_kernel<1>, Scene 100k x 100k, mean per dispatch",
+           "# three passes, each: timeout -s KILL 120 rocprofv3 --pmc <set> --output-format csv "
+           "-d gpurun_out/pmc_<name> -o pmc -- python3 -u bench.py --profile-pass",
+           f"# kernels.hip sha256[:16]: {kernel_source_hash()}", ""]
+    for name, cs in PMC_SETS.items():
+        out.append(f"# set {name}: {cs}")
+    out.append("")
+    for c in sorted(val):
+        out.append(f"{c:44s} {val[c]:14.6g}")
+    out.append("")
+    for k, v in derived:
+        out.append(f"{k:64s} {v:10.4g}")
+    with open(os.path.join(ROOT, "profiles", "icp_fused_kernel_scene100k_counters.txt"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,7 +216,12 @@ def main():
                          f"{COPY_MIB} MiB device copy (calibration for HBM counters)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 CSV output and exit")
+    ap.add_argument("--summarize-counters", metavar="OUT_DIR",
+                    help="write the profiles/ counter summary from gpurun_out/pmc_<set> and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.summarize:
         summarize(*args.summarize)
         return
