@@ -70,6 +70,7 @@ void free_tree(kdnn_tree *t)
     if (hipGetDevice(&cur) == hipSuccess && cur != t->device) (void)hipSetDevice(t->device);
     if (t->d_nodes) (void)hipFree(t->d_nodes);
     if (t->d_points) (void)hipFree(t->d_points);
+    if (t->d_orig) (void)hipFree(t->d_orig);
     if (t->h_pinned) (void)hipHostFree(t->h_pinned);
     if (cur >= 0 && cur != t->device) (void)hipSetDevice(cur);
     delete t;
@@ -236,9 +237,20 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         delete t;
         return hip_fail(e, "kdtree_build: hipGetDevice");
     }
+    // kPointPad sentinel points after the last one: +inf coordinates and index
+    // 0xFFFFFFFF (never a hit), so a search may read whole chunks past a leaf.
+    constexpr size_t kPointPad = 16;
     const size_t nb = ht.nodes.size() * sizeof(float), pb = ht.points.size() * sizeof(float);
+    const size_t pad_bytes = kPointPad * 4 * sizeof(float);
+    std::vector<float> pad(kPointPad * 4, INFINITY);
+    for (size_t k = 0; k < kPointPad; ++k) {
+        const uint32_t none = 0xFFFFFFFFu;
+        std::memcpy(&pad[4 * k + 3], &none, 4);
+    }
+    const size_t ob = size_t(n) * 3 * sizeof(float);
     if ((e = hipMalloc(&t->d_nodes, nb)) != hipSuccess ||
-        (e = hipMalloc(&t->d_points, pb)) != hipSuccess) {
+        (e = hipMalloc(&t->d_points, pb + pad_bytes)) != hipSuccess ||
+        (e = hipMalloc(&t->d_orig, ob)) != hipSuccess) {
         free_tree(t);
         return fail(KDNN_ENOMEM, std::string("kdtree_build: hipMalloc: ") + hipGetErrorString(e));
     }
@@ -255,7 +267,10 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         return hip_fail(e, "kdtree_build: hipHostGetDevicePointer");
     }
     if ((e = hipMemcpy(t->d_nodes, ht.nodes.data(), nb, hipMemcpyHostToDevice)) != hipSuccess ||
-        (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess) {
+        (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(static_cast<char *>(t->d_points) + pb, pad.data(), pad_bytes,
+                       hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(t->d_orig, xyz_host, ob, hipMemcpyHostToDevice)) != hipSuccess) {
         free_tree(t);
         return hip_fail(e, "kdtree_build: upload");
     }
@@ -264,6 +279,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     DeviceTree &d = t->dev;
     d.nodes = t->d_nodes;
     d.points = t->d_points;
+    d.orig = t->d_orig;
     d.first_leaf = uint32_t(1) << ht.depth;
     d.depth = ht.depth;
     d.n = n;
@@ -288,7 +304,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     }
     I.build_ms = build_ms;
     I.upload_ms = upload_ms;
-    I.device_bytes = int64_t(nb + pb);
+    I.device_bytes = int64_t(nb + pb + pad_bytes + ob);
     int l2 = 0;
     if ((e = hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, t->device)) != hipSuccess) {
         free_tree(t);

@@ -84,6 +84,7 @@ struct Best {
 struct TreeView {
     const float4 *__restrict__ nodes;
     const float4 *__restrict__ pts;
+    const float *__restrict__ orig;  // target points in their original order (xyz)
     uint32_t first_leaf;  // 2^D
     int32_t depth;        // D
     int64_t n;
@@ -491,17 +492,192 @@ __device__ __forceinline__ void nn_search_pair(const TreeView &t, float qx, floa
             }
         }
         if (i == kDone) return;
-        // Phase 2: leaf i (entered) -- its points, in batches of kLeafChunk.
+        // Phase 2: leaf i (entered) -- its points in whole chunks of
+        // kLeafChunk from one base address.  A chunk may run into the next
+        // leaf (real points: ranking them cannot change the exact answer) or
+        // into the kLeafChunk sentinel slots after the last point (+inf
+        // distance, index 0xFFFFFFFF: never a hit).
         int32_t begin, last, end;
         leaf_range(t, i, begin, last, end);
-        for (int32_t k0 = begin; k0 < end; k0 += kLeafChunk) {
+        uint32_t k0 = uint32_t(begin);
+        do {
+            const float4 *pc = t.pts + k0;
             float4 p[kLeafChunk];
-            int32_t sl[kLeafChunk];
-            load_points<kLeafChunk, 1>(t, k0, last, p, sl);
-            rank_points<kLeafChunk>(p, sl, qx, qy, qz, key, slot);
-        }
+#pragma unroll
+            for (int c = 0; c < kLeafChunk; ++c) p[c] = pc[c];
+#pragma unroll
+            for (int c = 0; c < kLeafChunk; ++c) {
+                const float dx = p[c].x - qx;
+                const float dy = p[c].y - qy;
+                const float dz = p[c].z - qz;
+                const float dd = (dx * dx + dy * dy) + dz * dz;
+                const uint64_t k = nn_key(dd, __float_as_uint(p[c].w));
+                const bool lt = k < key;
+                key = lt ? k : key;
+                slot = lt ? k0 + uint32_t(c) : slot;
+            }
+            k0 += kLeafChunk;
+        } while (k0 < uint32_t(end));
         if (STATS) cp += uint32_t(end - begin);
         i = pair_next(i, pend, lbs, key_dist(key));
+    }
+}
+
+// --------------------------------------- in-wave load balancing of the search
+//
+// A wave's 64 queries need very different amounts of work, and a wave lives
+// as long as its busiest lane.  Here every lane owns one query but works on a
+// task: its own query, or a subtree of another lane's query taken over when
+// it has nothing left to do.  After each round of leaf scans the idle lanes
+// are paired (by rank, via wave ballots) with lanes that still hold pending
+// second children, and each such donor hands over its shallowest pending
+// subtree (root node, box bound, query, owner) through lane shuffles.  The
+// best key of each query lives in LDS (okey); workers merge into it with a
+// 64-bit atomic minimum and prune with it, so every worker of a query
+// shares the best found so far.  The answer is the minimum key over a
+// superset of the leaves the single-lane search must scan, hence the same
+// exact, unique result.  Everything is wave-synchronous: lanes never wait on
+// each other, and the loop ends once no lane holds a task.
+constexpr uint32_t kNoOwner = 0xFFFFFFFFu;
+
+// Position of the r-th (0-based) set bit of m (m has more than r set bits).
+__device__ __forceinline__ uint32_t nth_set_bit(uint64_t m, uint32_t r)
+{
+    uint32_t pos = 0;
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {
+        const uint32_t c = uint32_t(__popcll(m & ((uint64_t(1) << w) - 1u)));
+        if (r >= c) {
+            r -= c;
+            m >>= w;
+            pos += uint32_t(w);
+        }
+    }
+    return pos;
+}
+
+// All lanes of the wave must call this together.  okey / ocn / ocp: the
+// work-group's LDS arrays [kWG], slot threadIdx.x = this lane's own query.
+// On return okey[threadIdx.x] holds the answer key of this lane's query (the
+// bound key when there is none), ocn / ocp its node / point counts (STATS).
+template <bool STATS>
+__device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
+                                            float oqz, uint64_t init, float *lbs,
+                                            unsigned long long *okey, uint32_t *ocn,
+                                            uint32_t *ocp)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t below = (uint64_t(1) << lane) - 1u;
+    okey[threadIdx.x] = init;
+    if (STATS) {
+        ocn[threadIdx.x] = 0u;
+        ocp[threadIdx.x] = 0u;
+    }
+    uint32_t owner = own ? threadIdx.x : kNoOwner;
+    float qx = oqx, qy = oqy, qz = oqz;
+    uint64_t key = init;
+    uint32_t i = kDone, pend = 0, cn = 0, cp = 0;
+    if (own && isfinite(qx) && isfinite(qy) && isfinite(qz)) {
+        const float4 A = t.nodes[2];
+        const float4 B = t.nodes[3];
+        if (STATS) ++cn;
+        i = enters(box_lb(qx, qy, qz, A, B), key_dist(key)) ? 1u : kDone;
+    }
+    for (;;) {
+        // Phase 1: internal nodes, as in the single-lane pair search.
+        while (i < t.first_leaf) {
+            const float4 A0 = t.nodes[4 * i];
+            const float4 B0 = t.nodes[4 * i + 1];
+            const float4 A1 = t.nodes[4 * i + 2];
+            const float4 B1 = t.nodes[4 * i + 3];
+            if (STATS) cn += 2;
+            const float l0 = box_lb(qx, qy, qz, A0, B0);
+            const float l1 = box_lb(qx, qy, qz, A1, B1);
+            const bool swap = l1 < l0;
+            const float lf = swap ? l1 : l0, ls = swap ? l0 : l1;
+            const float best = key_dist(key);
+            const uint32_t d = 31u - uint32_t(__clz(int(i)));
+            if (enters(lf, best)) {
+                lbs[d * kWG] = ls;
+                pend = enters(ls, best) ? (pend | (1u << d)) : (pend & ~(1u << d));
+                i = 2 * i + (swap ? 1u : 0u);
+            } else {
+                i = pair_next(i, pend, lbs, best);
+            }
+        }
+        // Phase 2: leaves, then share the improved best of the query.
+        if (i != kDone) {
+            int32_t begin, last, end;
+            leaf_range(t, i, begin, last, end);
+            uint32_t k0 = uint32_t(begin);
+            do {
+                const float4 *pc = t.pts + k0;
+                float4 p[kLeafChunk];
+#pragma unroll
+                for (int c = 0; c < kLeafChunk; ++c) p[c] = pc[c];
+#pragma unroll
+                for (int c = 0; c < kLeafChunk; ++c) {
+                    const float dx = p[c].x - qx;
+                    const float dy = p[c].y - qy;
+                    const float dz = p[c].z - qz;
+                    const float dd = (dx * dx + dy * dy) + dz * dz;
+                    const uint64_t k = nn_key(dd, __float_as_uint(p[c].w));
+                    key = k < key ? k : key;
+                }
+                k0 += kLeafChunk;
+            } while (k0 < uint32_t(end));
+            if (STATS) cp += uint32_t(end - begin);
+            const uint64_t seen = atomicMin(&okey[owner], (unsigned long long)key);
+            key = seen < key ? seen : key;
+            i = pair_next(i, pend, lbs, key_dist(key));
+        }
+        if (i == kDone && owner != kNoOwner) {
+            atomicMin(&okey[owner], (unsigned long long)key);
+            if (STATS) {
+                atomicAdd(&ocn[owner], cn);
+                atomicAdd(&ocp[owner], cp);
+                cn = 0u;
+                cp = 0u;
+            }
+            owner = kNoOwner;
+        }
+        // Hand-over round (every lane reaches it).
+        const bool idle = owner == kNoOwner;
+        const uint32_t dep = idle ? 0u : 31u - uint32_t(__clz(int(i)));
+        const uint32_t avail = idle ? 0u : (pend & ((1u << dep) - 1u));
+        const uint64_t busy_m = __ballot(!idle);
+        if (busy_m == 0) break;
+        const uint64_t idle_m = __ballot(idle), don_m = __ballot(avail != 0u);
+        if (idle_m == 0 || don_m == 0) continue;
+        const uint32_t nidle = uint32_t(__popcll(idle_m)), ndon = uint32_t(__popcll(don_m));
+        const uint32_t np = nidle < ndon ? nidle : ndon;
+        const bool gives = avail != 0u && uint32_t(__popcll(don_m & below)) < np;
+        uint32_t gv = 0u;
+        float glb = 0.0f;
+        if (gives) {
+            const uint32_t h = uint32_t(__ffs(int(avail))) - 1u;  // shallowest pending level
+            glb = lbs[h * kWG];
+            gv = (i >> (dep - h - 1u)) ^ 1u;
+            pend &= ~(1u << h);
+        }
+        const uint32_t trank = uint32_t(__popcll(idle_m & below));
+        const bool takes = idle && trank < np;
+        const int src = takes ? int(nth_set_bit(don_m, trank)) : int(lane);
+        const uint32_t tv = uint32_t(__shfl(int(gv), src, 64));
+        const float tlb = __shfl(glb, src, 64);
+        const float tqx = __shfl(qx, src, 64);
+        const float tqy = __shfl(qy, src, 64);
+        const float tqz = __shfl(qz, src, 64);
+        const uint32_t town = uint32_t(__shfl(int(owner), src, 64));
+        if (takes) {
+            owner = town;
+            qx = tqx;
+            qy = tqy;
+            qz = tqz;
+            pend = 0u;
+            key = okey[town];
+            i = enters(tlb, key_dist(key)) ? tv : kDone;
+        }
     }
 }
 
@@ -538,9 +714,34 @@ template <int G, bool STATS>
 __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
 {
     constexpr int QPB = kWG / G;
-    __shared__ float lbs[G == 1 ? kDevMaxDepth * kWG : 1];
     const uint32_t nb = gridDim.x;
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
+    if constexpr (G == 1) {
+        __shared__ float lbs[kDevMaxDepth * kWG];
+        __shared__ unsigned long long okey[kWG];
+        __shared__ uint32_t ocn[STATS ? kWG : 1], ocp[STATS ? kWG : 1];
+        for (int64_t base = int64_t(blk) * kWG; base < a.m; base += int64_t(nb) * kWG) {
+            const int64_t k = base + threadIdx.x;
+            const bool own = k < a.m;
+            const int64_t i = own ? (a.perm ? int64_t(a.perm[k]) : k) : 0;
+            const float qx = own ? a.q[3 * i] : 0.0f;
+            const float qy = own ? a.q[3 * i + 1] : 0.0f;
+            const float qz = own ? a.q[3 * i + 2] : 0.0f;
+            wave_search<STATS>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, ocn, ocp);
+            if (own) {
+                Best b;
+                finish(okey[threadIdx.x], 0u, b);
+                a.idx[i] = b.idx;
+                a.d2[i] = b.d;
+                if (STATS) {
+                    if (a.cnt_nodes) a.cnt_nodes[i] = ocn[threadIdx.x];
+                    if (a.cnt_pts) a.cnt_pts[i] = ocp[threadIdx.x];
+                }
+            }
+        }
+        return;
+    }
+    __shared__ float lbs[1];
     const int gl = threadIdx.x & (G - 1);
     for (int64_t base = int64_t(blk) * QPB; base < a.m; base += int64_t(nb) * QPB) {
         const int64_t k = base + threadIdx.x / G;
@@ -782,7 +983,7 @@ struct IcpArgs {
     int32_t *idx;
     float *d2;
     uint64_t init;      // bound key (bound +inf: none)
-    int32_t *mslot;     // [n] or null: leaf-order slot of each source point's match, -1 if none
+    int32_t *mslot;     // [n] or null: original index of each source point's match, -1 if none
     float *md2;         // [n] or null: its squared distance
 };
 
@@ -844,11 +1045,12 @@ __device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, doub
     if (a.idx) a.idx[i] = b.idx;
     if (a.d2) a.d2[i] = b.d;
     if (a.mslot) {
-        a.mslot[i] = b.idx >= 0 ? int32_t(b.slot) : -1;
+        a.mslot[i] = b.idx;
         a.md2[i] = b.d;
     }
     if (b.idx < 0) return;
-    const float4 mp = a.tree.pts[b.slot];
+    const float *mo = a.tree.orig + 3 * int64_t(b.idx);
+    const float4 mp = make_float4(mo[0], mo[1], mo[2], 0.0f);
     const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
     const double m0 = double(mp.x) - a.c[0], m1 = double(mp.y) - a.c[1],
                  m2 = double(mp.z) - a.c[2];
@@ -928,6 +1130,28 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     const uint32_t nb = gridDim.x;
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
+    if constexpr (G == 1) {
+        // one lane owns each source point; the wave balances the searches
+        __shared__ unsigned long long okey[kWG];
+        for (int64_t base = int64_t(blk) * kWG; base < a.n; base += int64_t(nb) * kWG) {
+            const int64_t k = base + threadIdx.x;
+            const bool own = k < a.n;
+            const int64_t i = own ? (a.perm ? int64_t(a.perm[k]) : k) : 0;
+            double X = 0.0, Y = 0.0, Z = 0.0;
+            float qx = 0.0f, qy = 0.0f, qz = 0.0f;
+            if (own) icp_query(a, i, X, Y, Z, qx, qy, qz);
+            wave_search<false>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, nullptr,
+                               nullptr);
+            if (own) {
+                Best b;
+                finish(okey[threadIdx.x], 0u, b);
+                icp_accumulate(a, i, X, Y, Z, b, acc);
+            }
+        }
+        block_sum(acc, red, a.partials + blockIdx.x, nb);
+        icp_final_reduce(a, acc, red, a.partials, int32_t(nb), nullptr, 0);
+        return;
+    }
     for (int64_t base = int64_t(blk) * QPB; base < a.n; base += int64_t(nb) * QPB) {
         const int64_t k = base + threadIdx.x / G;
         if (k >= a.n) continue;
@@ -1096,19 +1320,26 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    __shared__ unsigned long long okey[kWG];
     const int64_t i = int64_t(j) * kWG + threadIdx.x;
-    if (i < P.n) {
-        const double X = P.src[3 * i], Y = P.src[3 * i + 1], Z = P.src[3 * i + 2];
-        const float qx = rigid_row(P.R[0], P.R[1], P.R[2], P.t[0], X, Y, Z);
-        const float qy = rigid_row(P.R[3], P.R[4], P.R[5], P.t[1], X, Y, Z);
-        const float qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
-        uint64_t key;
-        uint32_t slot, cn = 0, cp = 0;
-        nn_search_pair<false>(P.tree, qx, qy, qz, a.init, lbs + threadIdx.x, key, slot, cn, cp);
+    const bool own = i < P.n;
+    double X = 0.0, Y = 0.0, Z = 0.0;
+    float qx = 0.0f, qy = 0.0f, qz = 0.0f;
+    if (own) {
+        X = P.src[3 * i];
+        Y = P.src[3 * i + 1];
+        Z = P.src[3 * i + 2];
+        qx = rigid_row(P.R[0], P.R[1], P.R[2], P.t[0], X, Y, Z);
+        qy = rigid_row(P.R[3], P.R[4], P.R[5], P.t[1], X, Y, Z);
+        qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
+    }
+    wave_search<false>(P.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, nullptr, nullptr);
+    if (own) {
         Best b;
-        finish(key, slot, b);
+        finish(okey[threadIdx.x], 0u, b);
         if (b.idx >= 0) {
-            const float4 mp = P.tree.pts[b.slot];
+            const float *mo = P.tree.orig + 3 * int64_t(b.idx);
+            const float4 mp = make_float4(mo[0], mo[1], mo[2], 0.0f);
             const double s0 = X - P.c[0], s1 = Y - P.c[1], s2 = Z - P.c[2];
             const double m0 = double(mp.x) - P.c[0], m1 = double(mp.y) - P.c[1],
                          m2 = double(mp.z) - P.c[2];
@@ -1153,7 +1384,7 @@ struct RejArgs {
     double t[3];
     double c[3];
     double kk;             // k * k
-    const int32_t *mslot;  // [n]
+    const int32_t *mslot;  // [n] original index of the match, -1 if none
     const float *md2;      // [n]
     double *partials;      // [kS][gridDim.x]
     uint32_t *ticket;
@@ -1163,11 +1394,15 @@ struct RejArgs {
     uint8_t *kept;         // [n] or null: 1 where the pair is kept
 };
 
-__device__ __forceinline__ bool rej_pair(const RejArgs &a, int64_t i, uint32_t &slot)
+// The matched target point of source point i, if any (a stored index outside
+// the tree counts as none, so any buffer content is safe to read).
+__device__ __forceinline__ bool rej_pair(const RejArgs &a, int64_t i, float4 &m)
 {
-    const int32_t sl = a.mslot[i];
-    slot = uint32_t(sl);
-    return sl >= 0 && int64_t(sl) < a.tree.n;
+    const int32_t j = a.mslot[i];
+    if (!(j >= 0 && int64_t(j) < a.tree.n)) return false;
+    const float *mo = a.tree.orig + 3 * int64_t(j);
+    m = make_float4(mo[0], mo[1], mo[2], 0.0f);
+    return true;
 }
 
 __device__ __forceinline__ double rej_residual_sq(const RejArgs &a, double X, double Y, double Z,
@@ -1188,9 +1423,8 @@ __global__ __launch_bounds__(kWG) void icp_residual_kernel(RejArgs a)
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     for (int64_t i = int64_t(blockIdx.x) * kWG + threadIdx.x; i < a.n;
          i += int64_t(gridDim.x) * kWG) {
-        uint32_t slot;
-        if (!rej_pair(a, i, slot)) continue;
-        const float4 m = a.tree.pts[slot];
+        float4 m;
+        if (!rej_pair(a, i, m)) continue;
         acc[0] += rej_residual_sq(a, a.src[3 * i], a.src[3 * i + 1], a.src[3 * i + 2], m);
         acc[1] += 1.0;
     }
@@ -1225,11 +1459,10 @@ __global__ __launch_bounds__(kWG) void icp_reject_kernel(RejArgs a)
     const double thr = a.stat[2];
     for (int64_t i = int64_t(blockIdx.x) * kWG + threadIdx.x; i < a.n;
          i += int64_t(gridDim.x) * kWG) {
-        uint32_t slot;
+        float4 mp;
         bool keep = false;
-        if (rej_pair(a, i, slot)) {
+        if (rej_pair(a, i, mp)) {
             const double X = a.src[3 * i], Y = a.src[3 * i + 1], Z = a.src[3 * i + 2];
-            const float4 mp = a.tree.pts[slot];
             keep = rej_residual_sq(a, X, Y, Z, mp) <= thr;
             if (keep) {
                 const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
@@ -1598,6 +1831,7 @@ static TreeView tree_view(const DeviceTree &t)
 {
     TreeView v;
     v.nodes = static_cast<const float4 *>(t.nodes);
+    v.orig = static_cast<const float *>(t.orig);
     v.pts = static_cast<const float4 *>(t.points);
     v.first_leaf = t.first_leaf;
     v.depth = t.depth;
