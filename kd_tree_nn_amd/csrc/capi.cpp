@@ -70,7 +70,7 @@ void free_tree(kdnn_tree *t)
     if (hipGetDevice(&cur) == hipSuccess && cur != t->device) (void)hipSetDevice(t->device);
     if (t->d_nodes) (void)hipFree(t->d_nodes);
     if (t->d_points) (void)hipFree(t->d_points);
-    if (t->d_orig) (void)hipFree(t->d_orig);
+    if (t->d_slot_of) (void)hipFree(t->d_slot_of);
     if (t->h_pinned) (void)hipHostFree(t->h_pinned);
     if (cur >= 0 && cur != t->device) (void)hipSetDevice(cur);
     delete t;
@@ -247,10 +247,16 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         const uint32_t none = 0xFFFFFFFFu;
         std::memcpy(&pad[4 * k + 3], &none, 4);
     }
-    const size_t ob = size_t(n) * 3 * sizeof(float);
+    std::vector<int32_t> slot_of(static_cast<size_t>(n));
+    for (int64_t k = 0; k < n; ++k) {
+        uint32_t j;
+        std::memcpy(&j, &ht.points[4 * size_t(k) + 3], 4);
+        slot_of[j] = int32_t(k);
+    }
+    const size_t ob = size_t(n) * sizeof(int32_t);
     if ((e = hipMalloc(&t->d_nodes, nb)) != hipSuccess ||
         (e = hipMalloc(&t->d_points, pb + pad_bytes)) != hipSuccess ||
-        (e = hipMalloc(&t->d_orig, ob)) != hipSuccess) {
+        (e = hipMalloc(&t->d_slot_of, ob)) != hipSuccess) {
         free_tree(t);
         return fail(KDNN_ENOMEM, std::string("kdtree_build: hipMalloc: ") + hipGetErrorString(e));
     }
@@ -270,7 +276,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(static_cast<char *>(t->d_points) + pb, pad.data(), pad_bytes,
                        hipMemcpyHostToDevice)) != hipSuccess ||
-        (e = hipMemcpy(t->d_orig, xyz_host, ob, hipMemcpyHostToDevice)) != hipSuccess) {
+        (e = hipMemcpy(t->d_slot_of, slot_of.data(), ob, hipMemcpyHostToDevice)) != hipSuccess) {
         free_tree(t);
         return hip_fail(e, "kdtree_build: upload");
     }
@@ -279,7 +285,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     DeviceTree &d = t->dev;
     d.nodes = t->d_nodes;
     d.points = t->d_points;
-    d.orig = t->d_orig;
+    d.slot_of = t->d_slot_of;
     d.first_leaf = uint32_t(1) << ht.depth;
     d.depth = ht.depth;
     d.n = n;

@@ -57,7 +57,7 @@ kdnn_status procrustes_from_sums(const kdnn_icp_sums &s, double R[9], double t[3
 struct DeviceTree {
     const void *nodes = nullptr;   // float4 array, 2 per node slot
     const void *points = nullptr;  // float4 array, 1 per point
-    const void *orig = nullptr;    // n x 3 floats, the target in its original order
+    const void *slot_of = nullptr; // n int32: leaf-order slot of each original index
     uint32_t first_leaf = 1;       // 2^D
     int32_t depth = 0;             // D
     int64_t n = 0;                 // target points
@@ -190,7 +190,7 @@ struct kdnn_tree {
     kdnn::DeviceTree dev;
     void *d_nodes = nullptr;
     void *d_points = nullptr;
-    void *d_orig = nullptr;
+    void *d_slot_of = nullptr;
     kdnn_tree_info info{};
     double *h_pinned = nullptr;  // host readback slot for the ICP sums
     double *d_pinned = nullptr;  // the same slot as the device addresses it

@@ -84,7 +84,7 @@ struct Best {
 struct TreeView {
     const float4 *__restrict__ nodes;
     const float4 *__restrict__ pts;
-    const float *__restrict__ orig;  // target points in their original order (xyz)
+    const int32_t *__restrict__ slot_of;  // original index -> leaf-order slot
     uint32_t first_leaf;  // 2^D
     int32_t depth;        // D
     int64_t n;
@@ -1049,8 +1049,7 @@ __device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, doub
         a.md2[i] = b.d;
     }
     if (b.idx < 0) return;
-    const float *mo = a.tree.orig + 3 * int64_t(b.idx);
-    const float4 mp = make_float4(mo[0], mo[1], mo[2], 0.0f);
+    const float4 mp = a.tree.pts[a.tree.slot_of[b.idx]];
     const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
     const double m0 = double(mp.x) - a.c[0], m1 = double(mp.y) - a.c[1],
                  m2 = double(mp.z) - a.c[2];
@@ -1338,8 +1337,7 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
         Best b;
         finish(okey[threadIdx.x], 0u, b);
         if (b.idx >= 0) {
-            const float *mo = P.tree.orig + 3 * int64_t(b.idx);
-            const float4 mp = make_float4(mo[0], mo[1], mo[2], 0.0f);
+            const float4 mp = P.tree.pts[P.tree.slot_of[b.idx]];
             const double s0 = X - P.c[0], s1 = Y - P.c[1], s2 = Z - P.c[2];
             const double m0 = double(mp.x) - P.c[0], m1 = double(mp.y) - P.c[1],
                          m2 = double(mp.z) - P.c[2];
@@ -1400,8 +1398,7 @@ __device__ __forceinline__ bool rej_pair(const RejArgs &a, int64_t i, float4 &m)
 {
     const int32_t j = a.mslot[i];
     if (!(j >= 0 && int64_t(j) < a.tree.n)) return false;
-    const float *mo = a.tree.orig + 3 * int64_t(j);
-    m = make_float4(mo[0], mo[1], mo[2], 0.0f);
+    m = a.tree.pts[a.tree.slot_of[j]];
     return true;
 }
 
@@ -1831,7 +1828,7 @@ static TreeView tree_view(const DeviceTree &t)
 {
     TreeView v;
     v.nodes = static_cast<const float4 *>(t.nodes);
-    v.orig = static_cast<const float *>(t.orig);
+    v.slot_of = static_cast<const int32_t *>(t.slot_of);
     v.pts = static_cast<const float4 *>(t.points);
     v.first_leaf = t.first_leaf;
     v.depth = t.depth;
