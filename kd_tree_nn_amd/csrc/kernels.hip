@@ -539,6 +539,15 @@ __device__ __forceinline__ void nn_search_pair(const TreeView &t, float qx, floa
 // exact, unique result.  Everything is wave-synchronous: lanes never wait on
 // each other, and the loop ends once no lane holds a task.
 constexpr uint32_t kNoOwner = 0xFFFFFFFFu;
+#ifndef KDNN_DONATE_DEEPEST
+#define KDNN_DONATE_DEEPEST 0
+#endif
+#ifndef KDNN_P1_HANDOVER
+#define KDNN_P1_HANDOVER 1
+#endif
+#ifndef KDNN_P1_MIN_IDLE
+#define KDNN_P1_MIN_IDLE 16
+#endif
 
 // Position of the r-th (0-based) set bit of m (m has more than r set bits).
 __device__ __forceinline__ uint32_t nth_set_bit(uint64_t m, uint32_t r)
@@ -556,6 +565,83 @@ __device__ __forceinline__ uint32_t nth_set_bit(uint64_t m, uint32_t r)
     return pos;
 }
 
+// Per-lane state of the balanced search.
+struct WaveTask {
+    uint32_t owner;  // slot of the query this lane works for (kNoOwner: idle)
+    float qx, qy, qz;
+    uint64_t key;    // best key seen by this lane for that query
+    uint32_t i;      // node being processed (kDone: task finished)
+    uint32_t pend;   // pending second children, per path level
+    uint32_t cn, cp;
+};
+
+// A finished task publishes its best (and counts) to the owner's slot.
+template <bool STATS>
+__device__ __forceinline__ void task_finish(WaveTask &w, unsigned long long *okey, uint32_t *ocn,
+                                            uint32_t *ocp)
+{
+    if (w.i == kDone && w.owner != kNoOwner) {
+        atomicMin(&okey[w.owner], (unsigned long long)w.key);
+        if (STATS) {
+            atomicAdd(&ocn[w.owner], w.cn);
+            atomicAdd(&ocp[w.owner], w.cp);
+            w.cn = 0u;
+            w.cp = 0u;
+        }
+        w.owner = kNoOwner;
+    }
+}
+
+// Hand-over round: idle lanes take the shallowest pending subtree of busy
+// lanes, paired by rank.  Every lane of the wave must call it together.
+__device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
+                                              const unsigned long long *okey,
+                                              uint32_t min_idle = 1u)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t below = (uint64_t(1) << lane) - 1u;
+    const bool idle = w.owner == kNoOwner;
+    const uint64_t idle_m = __ballot(idle);
+    if (idle_m == 0 || uint32_t(__popcll(idle_m)) < min_idle) return;
+    const uint32_t dep = idle ? 0u : 31u - uint32_t(__clz(int(w.i)));
+    const uint32_t avail = idle ? 0u : (w.pend & ((1u << dep) - 1u));
+    const uint64_t don_m = __ballot(avail != 0u);
+    if (don_m == 0) return;
+    const uint32_t nidle = uint32_t(__popcll(idle_m)), ndon = uint32_t(__popcll(don_m));
+    const uint32_t np = nidle < ndon ? nidle : ndon;
+    const bool gives = avail != 0u && uint32_t(__popcll(don_m & below)) < np;
+    uint32_t gv = 0u;
+    float glb = 0.0f;
+    if (gives) {
+#if KDNN_DONATE_DEEPEST
+        const uint32_t h = 31u - uint32_t(__clz(int(avail)));  // deepest pending level
+#else
+        const uint32_t h = uint32_t(__ffs(int(avail))) - 1u;  // shallowest pending level
+#endif
+        glb = lbs[h * kWG];
+        gv = (w.i >> (dep - h - 1u)) ^ 1u;
+        w.pend &= ~(1u << h);
+    }
+    const uint32_t trank = uint32_t(__popcll(idle_m & below));
+    const bool takes = idle && trank < np;
+    const int src = takes ? int(nth_set_bit(don_m, trank)) : int(lane);
+    const uint32_t tv = uint32_t(__shfl(int(gv), src, 64));
+    const float tlb = __shfl(glb, src, 64);
+    const float tqx = __shfl(w.qx, src, 64);
+    const float tqy = __shfl(w.qy, src, 64);
+    const float tqz = __shfl(w.qz, src, 64);
+    const uint32_t town = uint32_t(__shfl(int(w.owner), src, 64));
+    if (takes) {
+        w.owner = town;
+        w.qx = tqx;
+        w.qy = tqy;
+        w.qz = tqz;
+        w.pend = 0u;
+        w.key = okey[town];
+        w.i = enters(tlb, key_dist(w.key)) ? tv : kDone;
+    }
+}
+
 // All lanes of the wave must call this together.  okey / ocn / ocp: the
 // work-group's LDS arrays [kWG], slot threadIdx.x = this lane's own query.
 // On return okey[threadIdx.x] holds the answer key of this lane's query (the
@@ -566,50 +652,61 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                                             unsigned long long *okey, uint32_t *ocn,
                                             uint32_t *ocp)
 {
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint64_t below = (uint64_t(1) << lane) - 1u;
     okey[threadIdx.x] = init;
     if (STATS) {
         ocn[threadIdx.x] = 0u;
         ocp[threadIdx.x] = 0u;
     }
-    uint32_t owner = own ? threadIdx.x : kNoOwner;
-    float qx = oqx, qy = oqy, qz = oqz;
-    uint64_t key = init;
-    uint32_t i = kDone, pend = 0, cn = 0, cp = 0;
-    if (own && isfinite(qx) && isfinite(qy) && isfinite(qz)) {
+    WaveTask w;
+    w.owner = own ? threadIdx.x : kNoOwner;
+    w.qx = oqx;
+    w.qy = oqy;
+    w.qz = oqz;
+    w.key = init;
+    w.i = kDone;
+    w.pend = 0u;
+    w.cn = 0u;
+    w.cp = 0u;
+    if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
         const float4 A = t.nodes[2];
         const float4 B = t.nodes[3];
-        if (STATS) ++cn;
-        i = enters(box_lb(qx, qy, qz, A, B), key_dist(key)) ? 1u : kDone;
+        if (STATS) ++w.cn;
+        w.i = enters(box_lb(oqx, oqy, oqz, A, B), key_dist(w.key)) ? 1u : kDone;
     }
     for (;;) {
-        // Phase 1: internal nodes, as in the single-lane pair search.
-        while (i < t.first_leaf) {
-            const float4 A0 = t.nodes[4 * i];
-            const float4 B0 = t.nodes[4 * i + 1];
-            const float4 A1 = t.nodes[4 * i + 2];
-            const float4 B1 = t.nodes[4 * i + 3];
-            if (STATS) cn += 2;
-            const float l0 = box_lb(qx, qy, qz, A0, B0);
-            const float l1 = box_lb(qx, qy, qz, A1, B1);
-            const bool swap = l1 < l0;
-            const float lf = swap ? l1 : l0, ls = swap ? l0 : l1;
-            const float best = key_dist(key);
-            const uint32_t d = 31u - uint32_t(__clz(int(i)));
-            if (enters(lf, best)) {
-                lbs[d * kWG] = ls;
-                pend = enters(ls, best) ? (pend | (1u << d)) : (pend & ~(1u << d));
-                i = 2 * i + (swap ? 1u : 0u);
-            } else {
-                i = pair_next(i, pend, lbs, best);
+        // Phase 1: internal nodes, as in the single-lane pair search; lanes
+        // that run out of work take some over on every pass.
+        while (__ballot(w.i < t.first_leaf) != 0) {
+            if (w.i < t.first_leaf) {
+                const uint32_t i = w.i;
+                const float4 A0 = t.nodes[4 * i];
+                const float4 B0 = t.nodes[4 * i + 1];
+                const float4 A1 = t.nodes[4 * i + 2];
+                const float4 B1 = t.nodes[4 * i + 3];
+                if (STATS) w.cn += 2;
+                const float l0 = box_lb(w.qx, w.qy, w.qz, A0, B0);
+                const float l1 = box_lb(w.qx, w.qy, w.qz, A1, B1);
+                const bool swap = l1 < l0;
+                const float lf = swap ? l1 : l0, ls = swap ? l0 : l1;
+                const float best = key_dist(w.key);
+                const uint32_t d = 31u - uint32_t(__clz(int(i)));
+                if (enters(lf, best)) {
+                    lbs[d * kWG] = ls;
+                    w.pend = enters(ls, best) ? (w.pend | (1u << d)) : (w.pend & ~(1u << d));
+                    w.i = 2 * i + (swap ? 1u : 0u);
+                } else {
+                    w.i = pair_next(i, w.pend, lbs, best);
+                }
             }
+            task_finish<STATS>(w, okey, ocn, ocp);
+            if (KDNN_P1_HANDOVER) task_handover(w, lbs, okey, KDNN_P1_MIN_IDLE);
         }
         // Phase 2: leaves, then share the improved best of the query.
-        if (i != kDone) {
+        if (w.i != kDone) {
             int32_t begin, last, end;
-            leaf_range(t, i, begin, last, end);
+            leaf_range(t, w.i, begin, last, end);
             uint32_t k0 = uint32_t(begin);
+            uint64_t key = w.key;
             do {
                 const float4 *pc = t.pts + k0;
                 float4 p[kLeafChunk];
@@ -617,67 +714,23 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                 for (int c = 0; c < kLeafChunk; ++c) p[c] = pc[c];
 #pragma unroll
                 for (int c = 0; c < kLeafChunk; ++c) {
-                    const float dx = p[c].x - qx;
-                    const float dy = p[c].y - qy;
-                    const float dz = p[c].z - qz;
+                    const float dx = p[c].x - w.qx;
+                    const float dy = p[c].y - w.qy;
+                    const float dz = p[c].z - w.qz;
                     const float dd = (dx * dx + dy * dy) + dz * dz;
                     const uint64_t k = nn_key(dd, __float_as_uint(p[c].w));
                     key = k < key ? k : key;
                 }
                 k0 += kLeafChunk;
             } while (k0 < uint32_t(end));
-            if (STATS) cp += uint32_t(end - begin);
-            const uint64_t seen = atomicMin(&okey[owner], (unsigned long long)key);
-            key = seen < key ? seen : key;
-            i = pair_next(i, pend, lbs, key_dist(key));
+            if (STATS) w.cp += uint32_t(end - begin);
+            const uint64_t seen = atomicMin(&okey[w.owner], (unsigned long long)key);
+            w.key = seen < key ? seen : key;
+            w.i = pair_next(w.i, w.pend, lbs, key_dist(w.key));
         }
-        if (i == kDone && owner != kNoOwner) {
-            atomicMin(&okey[owner], (unsigned long long)key);
-            if (STATS) {
-                atomicAdd(&ocn[owner], cn);
-                atomicAdd(&ocp[owner], cp);
-                cn = 0u;
-                cp = 0u;
-            }
-            owner = kNoOwner;
-        }
-        // Hand-over round (every lane reaches it).
-        const bool idle = owner == kNoOwner;
-        const uint32_t dep = idle ? 0u : 31u - uint32_t(__clz(int(i)));
-        const uint32_t avail = idle ? 0u : (pend & ((1u << dep) - 1u));
-        const uint64_t busy_m = __ballot(!idle);
-        if (busy_m == 0) break;
-        const uint64_t idle_m = __ballot(idle), don_m = __ballot(avail != 0u);
-        if (idle_m == 0 || don_m == 0) continue;
-        const uint32_t nidle = uint32_t(__popcll(idle_m)), ndon = uint32_t(__popcll(don_m));
-        const uint32_t np = nidle < ndon ? nidle : ndon;
-        const bool gives = avail != 0u && uint32_t(__popcll(don_m & below)) < np;
-        uint32_t gv = 0u;
-        float glb = 0.0f;
-        if (gives) {
-            const uint32_t h = uint32_t(__ffs(int(avail))) - 1u;  // shallowest pending level
-            glb = lbs[h * kWG];
-            gv = (i >> (dep - h - 1u)) ^ 1u;
-            pend &= ~(1u << h);
-        }
-        const uint32_t trank = uint32_t(__popcll(idle_m & below));
-        const bool takes = idle && trank < np;
-        const int src = takes ? int(nth_set_bit(don_m, trank)) : int(lane);
-        const uint32_t tv = uint32_t(__shfl(int(gv), src, 64));
-        const float tlb = __shfl(glb, src, 64);
-        const float tqx = __shfl(qx, src, 64);
-        const float tqy = __shfl(qy, src, 64);
-        const float tqz = __shfl(qz, src, 64);
-        const uint32_t town = uint32_t(__shfl(int(owner), src, 64));
-        if (takes) {
-            owner = town;
-            qx = tqx;
-            qy = tqy;
-            qz = tqz;
-            pend = 0u;
-            key = okey[town];
-            i = enters(tlb, key_dist(key)) ? tv : kDone;
-        }
+        task_finish<STATS>(w, okey, ocn, ocp);
+        if (__ballot(w.owner != kNoOwner) == 0) break;
+        task_handover(w, lbs, okey);
     }
 }
 
