@@ -433,6 +433,13 @@ def main():
     kern_avg_ms = float(kern_ms.mean())
     log(f"fused kernel: mean {kern_avg_ms * 1e3:.1f} us, median {np.median(kern_ms) * 1e3:.1f} us")
 
+    # host rigid solve alone (what each iteration does between two launches)
+    sd = tree.correspond_reduce(src, Rt[0, :9], Rt[0, 9:], workspace=ws)
+    t0 = time.perf_counter()
+    for _ in range(200):
+        kdnn.procrustes(sd)
+    solve_us = (time.perf_counter() - t0) / 200 * 1e6
+
     # algorithmic bytes of one launch, per iteration's transform
     nodes_tot, pts_tot = [], []
     for k in range(ITERS):
@@ -450,31 +457,53 @@ def main():
     descent_lb = 32 * (info["depth"] + 1) + 16 * (n / 2 ** info["depth"]) + 16
 
     # ------------------------------------------------------ standalone nn_query
-    def time_query(q, sort, reps=20):
-        qws = tree.query_workspace(len(q))
+    def time_query(tr, q, sort, reps=100, warm=10):
+        """Device time of nn_query (events on the launch stream): median, p25, p75 in ms."""
+        qws = tr.query_workspace(len(q))
         out = (torch.empty(len(q), dtype=torch.int32, device="cuda"),
                torch.empty(len(q), dtype=torch.float32, device="cuda"))
-        tree.query(q, sort=sort, out=out, workspace=qws)
-        ts = []
-        for _ in range(reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(warm):
+            tr.query(q, sort=sort, out=out, workspace=qws)
+        evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(reps)]
+        torch.cuda._sleep(spin_cycles)
+        for e0, e1 in evs_:
             e0.record(stream)
-            tree.query(q, sort=sort, out=out, workspace=qws)
+            tr.query(q, sort=sort, out=out, workspace=qws)
             e1.record(stream)
-            ts.append((e0, e1))
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in ts]))
+        t_ = np.array([a.elapsed_time(b) for a, b in evs_])
+        return float(np.median(t_)), float(np.percentile(t_, 25)), float(np.percentile(t_, 75))
+
+    def nn_entry(m_, ms):
+        return {"ms": round(ms[0], 4), "p25_ms": round(ms[1], 4), "p75_ms": round(ms[2], 4),
+                "queries_per_s": round(m_ / (ms[0] * 1e-3))}
 
     q0 = src
     qc = kdnn.transform(src, g["R"], g["t"])
-    nnq = {"automatic_order": "morton" if info["auto_sort"] else "unsorted"}
+    nnq = {"automatic_order": "morton" if info["auto_sort"] else "unsorted",
+           "runs": "median and quartiles of 100 launches after 10 warm-ups"}
     for name, q in (("iteration0", q0), ("converged", qc)):
         for sort in (True, False):
-            ms = time_query(q, sort)
-            nnq[f"{name}_{'morton' if sort else 'unsorted'}"] = {
-                "ms": round(ms, 4), "queries_per_s": round(len(q) / (ms * 1e-3))}
+            nnq[f"{name}_{'morton' if sort else 'unsorted'}"] = nn_entry(
+                len(q), time_query(tree, q, sort))
     log("nn_query:", nnq)
+
+    # the other query workloads (one nn_query pass each, the library's automatic order)
+    other = {}
+    if not args.headline_only:
+        for wname, gen, leaf in (("stress_1M_leaf8", synth.stress, 8),
+                                 ("stress_1M_leaf16", synth.stress, 16),
+                                 ("skewed_500k_leaf8", synth.skewed, 8),
+                                 ("skewed_500k_leaf16", synth.skewed, 16)):
+            pw = gen()
+            tw = kdnn.Tree(pw.target, leaf)
+            qw = torch.from_numpy(np.ascontiguousarray(pw.source)).cuda()
+            other[wname] = dict(nn_entry(len(qw), time_query(tw, qw, None, reps=20, warm=3)),
+                                automatic_order="morton" if tw.info["auto_sort"] else "unsorted",
+                                build_ms=round(tw.info["build_ms"], 1))
+            del tw, qw
+        log("other workloads:", other)
     traffic, traffic_src = committed_traffic()
 
     result = {
@@ -508,9 +537,21 @@ def main():
                   "registration_incl_build_ms": round(build_wall_ms + T / args.steps * 1e3, 3)},
         "fused_kernel": {"name": "icp_fused_kernel", "mean_us": round(kern_avg_ms * 1e3, 2),
                          "median_us": round(float(np.median(kern_ms)) * 1e3, 2),
+                         "p25_us": round(float(np.percentile(kern_ms, 25)) * 1e3, 2),
+                         "p75_us": round(float(np.percentile(kern_ms, 75)) * 1e3, 2),
                          "launches": len(kern_ms),
                          "queries_per_s": round(n / (kern_avg_ms * 1e-3))},
+        "icp_iteration_breakdown_us": {
+            "iteration": round(T / (args.steps * ITERS) * 1e6, 2),
+            "fused_kernel_events": round(kern_avg_ms * 1e3, 2),
+            "host_and_launch": round(T / (args.steps * ITERS) * 1e6 - kern_avg_ms * 1e3, 2),
+            "host_solve_through_python": round(solve_us, 2),
+            "note": "host_and_launch = readback wait, host SVD solve, convergence check, "
+                    "next launch; the sums are written by the kernel into pinned memory. "
+                    "host_solve_through_python times kdnn_procrustes called from Python "
+                    "(ctypes marshalling included): an upper bound of the C++ call"},
         "nn_query": nnq,
+        "other_workloads_nn_query": other,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
