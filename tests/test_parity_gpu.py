@@ -451,3 +451,30 @@ def test_scene_builder_variants(torch, kdnn, leaf, round_robin):
     g = tree.icp(src, max_iter=p.iters)
     assert np.linalg.norm(g["R"] - o["R"]) <= R_TOL
     assert np.max(np.abs(g["t"] - o["t"])) <= T_TOL
+
+
+def test_fused_kernel_several_chunks_per_work_group(torch, kdnn):
+    """More than 4096 x 256 source points: the fused kernel's work-groups each
+    take several 256-point chunks in turn (its grid is capped at 4096)."""
+    p = synth.stress()
+    rng = np.random.Generator(np.random.PCG64(77))
+    S = rng.uniform(-50, 50, size=(1_100_000, 3)).astype(np.float32)
+    tree = kdnn.Tree(p.target, 8)
+    R = synth.rotation_about(synth.random_unit(rng), 0.01)
+    t = np.array([0.05, -0.02, 0.01])
+    say("fused kernel, 1.1M source points")
+    oi, od, red = _pairs_oracle(p.target, S, R, t, stress_oracle_tree())
+    for f in (0, _lib_flags().KDNN_ICP_NO_SORT, _lib_flags().KDNN_ICP_SORT):
+        res = tree.correspond_reduce(dev(torch, S), R, t, return_pairs=True, flags=f)
+        assert_nn_equal(res["idx"], res["d2"], oi, od, f"1.1M pairs flags {f}")
+        check_sums(res, red, bbox_diag(p.target), f"1.1M sums flags {f}")
+
+
+def _lib_flags():
+    from kd_tree_nn_amd import _lib
+    return _lib
+
+
+@functools.lru_cache(maxsize=None)
+def stress_oracle_tree():
+    return oracle.KDTree(synth.stress().target, 8)
