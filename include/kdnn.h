@@ -167,8 +167,10 @@ kdnn_status kdtree_build_host(const float *xyz_host, int64_t n, const kdnn_build
  * wavefronts.  Results never depend on the order. */
 
 /* Search schedule (nn_query, nn_query_stats and the ICP entry points).
- * Default: one lane per query, one pass.
- *   KDNN_LANES(g), g in {1, 2, 4, 8, 16}: g lanes cooperate on each query.
+ * Default: one lane owns each query, and the 64 lanes of a wavefront share
+ * the work (lanes that finish take over pending subtrees of busy ones).
+ *   KDNN_LANES(g), g in {2, 4, 8, 16}: g lanes cooperate on each query (g = 1
+ *                   is the default).
  *   KDNN_BUDGET(b), b in 1..255: two passes -- one lane
  *                   per query with a budget of b node visits, then groups of
  *                   16 lanes complete the queries left over, starting from

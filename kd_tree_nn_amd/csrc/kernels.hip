@@ -452,77 +452,6 @@ __device__ __forceinline__ uint32_t pair_next(uint32_t i, uint32_t &pend, const 
     return kDone;
 }
 
-// lbs: this lane's column of an LDS array [kDevMaxDepth][kWG].
-template <bool STATS>
-__device__ __forceinline__ void nn_search_pair(const TreeView &t, float qx, float qy, float qz,
-                                               uint64_t init, float *lbs, uint64_t &key,
-                                               uint32_t &slot, uint32_t &cn, uint32_t &cp)
-{
-    key = init;
-    slot = 0;
-    if (!(isfinite(qx) && isfinite(qy) && isfinite(qz))) return;
-    uint32_t i;
-    {
-        const float4 A = t.nodes[2];
-        const float4 B = t.nodes[3];
-        if (STATS) ++cn;
-        i = enters(box_lb(qx, qy, qz, A, B), key_dist(key)) ? 1u : kDone;
-    }
-    uint32_t pend = 0;
-    for (;;) {
-        // Phase 1: internal nodes (entered), until a leaf or the end.
-        while (i < t.first_leaf) {
-            const float4 A0 = t.nodes[4 * i];
-            const float4 B0 = t.nodes[4 * i + 1];
-            const float4 A1 = t.nodes[4 * i + 2];
-            const float4 B1 = t.nodes[4 * i + 3];
-            if (STATS) cn += 2;
-            const float l0 = box_lb(qx, qy, qz, A0, B0);
-            const float l1 = box_lb(qx, qy, qz, A1, B1);
-            const bool swap = l1 < l0;
-            const float lf = swap ? l1 : l0, ls = swap ? l0 : l1;
-            const float best = key_dist(key);
-            const uint32_t d = 31u - uint32_t(__clz(int(i)));  // children's level bit
-            if (enters(lf, best)) {
-                lbs[d * kWG] = ls;
-                pend = enters(ls, best) ? (pend | (1u << d)) : (pend & ~(1u << d));
-                i = 2 * i + (swap ? 1u : 0u);
-            } else {
-                i = pair_next(i, pend, lbs, best);
-            }
-        }
-        if (i == kDone) return;
-        // Phase 2: leaf i (entered) -- its points in whole chunks of
-        // kLeafChunk from one base address.  A chunk may run into the next
-        // leaf (real points: ranking them cannot change the exact answer) or
-        // into the kLeafChunk sentinel slots after the last point (+inf
-        // distance, index 0xFFFFFFFF: never a hit).
-        int32_t begin, last, end;
-        leaf_range(t, i, begin, last, end);
-        uint32_t k0 = uint32_t(begin);
-        do {
-            const float4 *pc = t.pts + k0;
-            float4 p[kLeafChunk];
-#pragma unroll
-            for (int c = 0; c < kLeafChunk; ++c) p[c] = pc[c];
-#pragma unroll
-            for (int c = 0; c < kLeafChunk; ++c) {
-                const float dx = p[c].x - qx;
-                const float dy = p[c].y - qy;
-                const float dz = p[c].z - qz;
-                const float dd = (dx * dx + dy * dy) + dz * dz;
-                const uint64_t k = nn_key(dd, __float_as_uint(p[c].w));
-                const bool lt = k < key;
-                key = lt ? k : key;
-                slot = lt ? k0 + uint32_t(c) : slot;
-            }
-            k0 += kLeafChunk;
-        } while (k0 < uint32_t(end));
-        if (STATS) cp += uint32_t(end - begin);
-        i = pair_next(i, pend, lbs, key_dist(key));
-    }
-}
-
 // --------------------------------------- in-wave load balancing of the search
 //
 // A wave's 64 queries need very different amounts of work, and a wave lives
@@ -747,22 +676,21 @@ struct NnArgs {
     uint32_t *cnt_pts;
 };
 
+// Cooperative search of one query by G >= 2 lanes.
 template <int G, bool STATS>
 __device__ __forceinline__ void search_query(const TreeView &t, float qx, float qy, float qz,
-                                             uint64_t init, float *lbs, Best &b, uint32_t &cn,
-                                             uint32_t &cp)
+                                             uint64_t init, Best &b, uint32_t &cn, uint32_t &cp)
 {
     uint64_t key = init;
     uint32_t slot = 0;
-    if (G == 1)
-        nn_search_pair<STATS>(t, qx, qy, qz, init, lbs, key, slot, cn, cp);
-    else if (isfinite(qx) && isfinite(qy) && isfinite(qz))
+    if (isfinite(qx) && isfinite(qy) && isfinite(qz))
         nn_search_group<G, STATS>(t, qx, qy, qz, false, key, slot, cn, cp);
     finish(key, slot, b);
 }
 
-// G lanes per query; a block handles kWG / G queries per sweep.  The loop
-// bound is uniform over the block so a group's lanes always stay together.
+// One query per lane (G = 1: the balanced wave search) or G lanes per query.
+// A block handles kWG / G queries per sweep; the loop bound is uniform over the
+// block so a wave's (or group's) lanes always stay together.
 template <int G, bool STATS>
 __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
 {
@@ -792,24 +720,23 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
                 }
             }
         }
-        return;
-    }
-    __shared__ float lbs[1];
-    const int gl = threadIdx.x & (G - 1);
-    for (int64_t base = int64_t(blk) * QPB; base < a.m; base += int64_t(nb) * QPB) {
-        const int64_t k = base + threadIdx.x / G;
-        if (k < a.m) {
-            const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
-            const float qx = a.q[3 * i], qy = a.q[3 * i + 1], qz = a.q[3 * i + 2];
-            Best b;
-            uint32_t cn = 0, cp = 0;
-            search_query<G, STATS>(a.tree, qx, qy, qz, a.init, lbs + threadIdx.x, b, cn, cp);
-            if (gl == 0) {
-                a.idx[i] = b.idx;
-                a.d2[i] = b.d;
-                if (STATS) {
-                    if (a.cnt_nodes) a.cnt_nodes[i] = cn;
-                    if (a.cnt_pts) a.cnt_pts[i] = cp;
+    } else {
+        const int gl = threadIdx.x & (G - 1);
+        for (int64_t base = int64_t(blk) * QPB; base < a.m; base += int64_t(nb) * QPB) {
+            const int64_t k = base + threadIdx.x / G;
+            if (k < a.m) {
+                const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+                const float qx = a.q[3 * i], qy = a.q[3 * i + 1], qz = a.q[3 * i + 2];
+                Best b;
+                uint32_t cn = 0, cp = 0;
+                search_query<G, STATS>(a.tree, qx, qy, qz, a.init, b, cn, cp);
+                if (gl == 0) {
+                    a.idx[i] = b.idx;
+                    a.d2[i] = b.d;
+                    if (STATS) {
+                        if (a.cnt_nodes) a.cnt_nodes[i] = cn;
+                        if (a.cnt_pts) a.cnt_pts[i] = cp;
+                    }
                 }
             }
         }
@@ -1169,14 +1096,12 @@ __device__ __forceinline__ void icp_final_reduce(const IcpArgs &a, double (&acc)
     icp_final_reduce_n<kWG>(a, acc, red, p1, n1, p2, n2);
 }
 
-// Single pass: G lanes per point, one kernel does everything.
+// Single pass, one kernel: transform, search (balanced wave search for G = 1,
+// G lanes per point otherwise) and the fp64 reduction.
 template <int G>
 __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
 {
-    constexpr int QPB = kWG / G;
-    const int gl = threadIdx.x & (G - 1);
     __shared__ double red[(kWG / 64) * kS];
-    __shared__ float lbs[G == 1 ? kDevMaxDepth * kWG : 1];
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
@@ -1184,6 +1109,7 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
     if constexpr (G == 1) {
         // one lane owns each source point; the wave balances the searches
+        __shared__ float lbs[kDevMaxDepth * kWG];
         __shared__ unsigned long long okey[kWG];
         for (int64_t base = int64_t(blk) * kWG; base < a.n; base += int64_t(nb) * kWG) {
             const int64_t k = base + threadIdx.x;
@@ -1200,21 +1126,21 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
                 icp_accumulate(a, i, X, Y, Z, b, acc);
             }
         }
-        block_sum(acc, red, a.partials + blockIdx.x, nb);
-        icp_final_reduce(a, acc, red, a.partials, int32_t(nb), nullptr, 0);
-        return;
-    }
-    for (int64_t base = int64_t(blk) * QPB; base < a.n; base += int64_t(nb) * QPB) {
-        const int64_t k = base + threadIdx.x / G;
-        if (k >= a.n) continue;
-        const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
-        double X, Y, Z;
-        float qx, qy, qz;
-        icp_query(a, i, X, Y, Z, qx, qy, qz);
-        Best b;
-        uint32_t cn = 0, cp = 0;
-        search_query<G, false>(a.tree, qx, qy, qz, a.init, lbs + threadIdx.x, b, cn, cp);
-        if (gl == 0) icp_accumulate(a, i, X, Y, Z, b, acc);
+    } else {
+        constexpr int QPB = kWG / G;
+        const int gl = threadIdx.x & (G - 1);
+        for (int64_t base = int64_t(blk) * QPB; base < a.n; base += int64_t(nb) * QPB) {
+            const int64_t k = base + threadIdx.x / G;
+            if (k >= a.n) continue;
+            const int64_t i = a.perm ? int64_t(a.perm[k]) : k;
+            double X, Y, Z;
+            float qx, qy, qz;
+            icp_query(a, i, X, Y, Z, qx, qy, qz);
+            Best b;
+            uint32_t cn = 0, cp = 0;
+            search_query<G, false>(a.tree, qx, qy, qz, a.init, b, cn, cp);
+            if (gl == 0) icp_accumulate(a, i, X, Y, Z, b, acc);
+        }
     }
     block_sum(acc, red, a.partials + blockIdx.x, nb);
     icp_final_reduce(a, acc, red, a.partials, int32_t(nb), nullptr, 0);
