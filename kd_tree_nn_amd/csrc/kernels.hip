@@ -973,21 +973,43 @@ __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, doub
     return float(((r0 * x + r1 * y) + r2 * z) + tr);
 }
 
-// Sum acc[] over a work-group of WG lanes; thread c < kS gets component c
-// in *out (fixed order: lanes by xor butterfly, then waves in order).
+// v + (v of the lane DPP control CTRL selects; +0 where there is none).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add(double v)
+{
+    const uint64_t b = uint64_t(__double_as_longlong(v));
+    const uint32_t lo = uint32_t(
+        __builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, ROW_MASK, 0xF, false));
+    const uint32_t hi = uint32_t(
+        __builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, ROW_MASK, 0xF, false));
+    return v + __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
+// Sum of v over the 64 lanes of a full wave, in lane 63: an inclusive scan by
+// DPP row shifts 1, 2, 4, 8 within rows of 16, then row broadcasts of lanes 15
+// and 31 -- register moves instead of LDS-crossbar shuffles, in a fixed order.
+__device__ __forceinline__ double wave_total(double v)
+{
+    v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// Sum acc[] over a work-group of WG lanes (all active); thread c < kS gets
+// component c in out[c * out_stride] (fixed order: lanes by wave_total, then
+// waves in order).  acc[] is left holding partial sums.
 template <int WG>
 __device__ __forceinline__ void block_sum_n(double (&acc)[kS], double *red /* LDS [waves][kS] */,
                                             double *out, int64_t out_stride)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int c = 0; c < kS; ++c) {
-        double v = acc[c];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-        acc[c] = v;
-    }
-    if (lane == 0) {
+    for (int c = 0; c < kS; ++c) acc[c] = wave_total(acc[c]);
+    if (lane == 63) {
 #pragma unroll
         for (int c = 0; c < kS; ++c) red[w * kS + c] = acc[c];
     }
