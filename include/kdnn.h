@@ -242,7 +242,7 @@ kdnn_status transform_points(const float *in_dev, float *out_dev, int64_t n, con
 /* ICP flags. */
 #define KDNN_ICP_REUSE_ORDER 1u /* ws was last used by an ICP call with the same src_dev, n
                                    and ordering choice, stream-ordered before this one: reuse
-                                   its traversal order and skip re-initialising ws */
+                                   its traversal order instead of sorting again */
 #define KDNN_ICP_NO_SORT 2u     /* traverse source points in their given order */
 #define KDNN_ICP_SORT 4u        /* always traverse in Morton order of the transformed points */
 /* Neither NO_SORT nor SORT: Morton order when the tree's device footprint

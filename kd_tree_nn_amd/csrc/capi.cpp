@@ -150,10 +150,8 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
     const bool keep = rej && rej->reject_k > 0.0;
     const int32_t *perm = nullptr;
     hipError_t e = hipSuccess;
-    // Every fused launch leaves the ticket at zero; a workspace coming from a
-    // call ordered before this one on the stream needs no clearing.
     if (flags & KDNN_ICP_NO_SORT) {
-        if (!(flags & KDNN_ICP_REUSE_ORDER)) e = launch_zero_u32(w.ticket, 1, s);
+        // points in caller order
     } else if (flags & KDNN_ICP_REUSE_ORDER) {
         perm = w.sort.vals_a;
     } else {
@@ -490,9 +488,7 @@ kdnn_status icp_reject_reduce(const kdnn_tree *tree, const float *src_dev, int64
     kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
     std::lock_guard<std::mutex> lock(mt->icp_mu);
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
-    hipError_t e = launch_zero_u32(w.ticket, 1, stream);
-    if (e != hipSuccess) return hip_fail(e, "icp_reject_reduce: launch");
-    e = launch_icp_reject(tree->dev, src_dev, n, R_host, t_host, reject_k * reject_k, w,
+    hipError_t e = launch_icp_reject(tree->dev, src_dev, n, R_host, t_host, reject_k * reject_k, w,
                           mt->d_pinned, mt->d_pinned + KDNN_SUMS_DOUBLES, kept_dev, stream);
     if (e != hipSuccess) return hip_fail(e, "icp_reject_reduce: launch");
     if ((e = hipStreamSynchronize(stream)) != hipSuccess)
@@ -709,14 +705,13 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
     copy_out();
     if (max_iter == 0) return KDNN_OK;
 
-    // one partial column per work-group of every pair, a ticket per pair
+    // one partial column per work-group of every pair
     std::vector<int32_t> part(B);
     int32_t total = 0;
     for (int32_t p = 0; p < B; ++p) {
         part[p] = total;
         total += batch_groups(n[p]);
     }
-    uint32_t *tickets = batch_tickets(ws_dev, total);
     // host slot the kernels write the sums into
     struct Pinned {
         double *h = nullptr;
@@ -729,8 +724,6 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
     double *d_sums = nullptr;
     if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&d_sums), pin.h, 0)) != hipSuccess)
         return hip_fail(e, "icp_align_batch: hipHostGetDevicePointer");
-    if ((e = launch_zero_u32(tickets, B, stream)) != hipSuccess)
-        return hip_fail(e, "icp_align_batch: launch");
 
     const float bound2 = reject ? bound_of(reject->max_dist) : INFINITY;
     std::vector<char> done(B, 0);
@@ -748,7 +741,7 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
             for (size_t c = c0; c < active.size() && c < c0 + size_t(batch_max_pairs()); ++c) {
                 const int32_t p = active[c];
                 jobs.push_back(BatchJob{&trees[p]->dev, src_dev[p], n[p], &R[9 * size_t(p)],
-                                        &t[3 * size_t(p)], part[p], tickets + p,
+                                        &t[3 * size_t(p)], part[p],
                                         d_sums + size_t(KDNN_SUMS_DOUBLES) * p});
             }
             e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream);

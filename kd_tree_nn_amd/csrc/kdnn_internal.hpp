@@ -95,7 +95,6 @@ struct IcpWorkspace {
     float *md2;         // [n] its squared distance
     double *stat;       // residual statistics of the rejection step
     double *sums;       // KDNN_SUMS_DOUBLES
-    uint32_t *ticket;   // 1 counter, must be 0 between launches
     int32_t max_blocks;
 };
 size_t icp_ws_bytes(int64_t n);
@@ -106,7 +105,7 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n);
 // return *perm points at the int32 permutation (traversal slot -> point).
 hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                                const SortWorkspace &ws, const int32_t **perm, hipStream_t s);
-// Same, for the ICP entry points: also clears the workspace's ticket counter.
+// Same, for the ICP entry points (sort buffers carved from the ICP workspace).
 hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                             const IcpWorkspace &ws, const int32_t **perm, hipStream_t s);
 // Search schedule decoded from the KDNN_LANES / KDNN_BUDGET / KDNN_TOP_LDS
@@ -157,7 +156,7 @@ hipError_t launch_voxel_filter(const float *xyz, int64_t n, double leaf, const i
 
 // Batched correspondence steps: up to batch_max_pairs() (tree, source) pairs
 // per launch, one pair per group of XCDs.  ws: icp_batch_ws_bytes layout
-// (partials of `total` work-group columns, then one ticket per pair).
+// (partials of `total` work-group columns).
 struct BatchJob {
     const DeviceTree *tree;
     const float *src;
@@ -165,13 +164,11 @@ struct BatchJob {
     const double *R;  // [9]
     const double *t;  // [3]
     int32_t part;     // first partial column
-    uint32_t *ticket;
     double *sums;     // [KDNN_SUMS_DOUBLES] out (device-visible)
 };
 int batch_max_pairs();
 int32_t batch_groups(int64_t n);  // work-groups (partial columns) of an n-point pair
 size_t icp_batch_ws_bytes(int32_t B, const int64_t *n);
-uint32_t *batch_tickets(void *ws, int32_t total);
 hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void *ws, int32_t total,
                             hipStream_t s);
 
@@ -180,7 +177,6 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
                              const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,
                              double *stat_out, uint8_t *kept, hipStream_t s);
-hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace kdnn
 

@@ -940,10 +940,9 @@ __global__ __launch_bounds__(kWG) void nn_pass2_kernel(NnArgs a, TwoPass tp)
 // Per source point: q = fl32(R s + t) evaluated in fp64 with a fixed
 // association; nearest target point m; accumulate in fp64, shifted by c,
 //   (s-c), (m-c), (s-c)(m-c)^T, d2, 1.
-// Per lane -> wave (xor butterfly, lane 0 keeps the total) -> work-group
-// (waves summed in order) -> per-group partials; the last group to finish
-// (atomic ticket) sums the partials in a fixed order.  The result does not
-// depend on scheduling.
+// Per lane -> wave (DPP scan, lane 63 keeps the total) -> work-group (waves
+// summed in order) -> per-group partials; reduce_partials_kernel then sums
+// the partials in a fixed order.  The result does not depend on scheduling.
 struct IcpArgs {
     TreeView tree;
     const float *src;
@@ -955,7 +954,6 @@ struct IcpArgs {
     double *partials;   // [kS][nb] of the kernel that reduces (single pass / pass 1)
     double *partials2;  // [kS][nb2] of pass 2
     int32_t nb1;        // pass-1 block count (two-pass mode)
-    uint32_t *ticket;
     double *sums;       // [kS]
     uint32_t budget;    // pass-1 node budget
     uint64_t *pkey;     // [n] pass-1 best key of unfinished slots
@@ -1064,58 +1062,32 @@ __device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, doub
     acc[16] += 1.0;
 }
 
-// After this group's partials are written: the last group to finish sums
-// p1[kS][n1] and then p2[kS][n2] in a fixed order into a.sums.
-// True in the last of `groups` work-groups to get here (atomic ticket); that
-// group sees every other group's partials.  The caller resets the ticket.
-__device__ __forceinline__ bool last_group_of(uint32_t *ticket, uint32_t groups)
+// Sums of per-work-group partials, in a separate launch: one work-group adds
+// the columns of p1 (n1 of them) and then of p2 (n2) in a fixed order and
+// writes the KDNN_SUMS_DOUBLES totals to out.  The kernel boundary makes the
+// partials visible; a last-work-group ticket inside the producing kernel
+// would need a device-scope release in every work-group, which on MI355X
+// writes back the L2 of its XCD (the L2s are not coherent with each other).
+// With stat (residual rejection): stat_out = (stat[0] / stat[1], stat[2]).
+__global__ __launch_bounds__(kWG) void reduce_partials_kernel(const double *p1, int32_t n1,
+                                                              const double *p2, int32_t n2,
+                                                              double *out, const double *stat,
+                                                              double *stat_out)
 {
-    __shared__ uint32_t is_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == groups - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!is_last) return false;
-    __threadfence();
-    return true;
-}
-
-__device__ __forceinline__ bool last_group(uint32_t *ticket)
-{
-    return last_group_of(ticket, gridDim.x);
-}
-
-template <int WG>
-__device__ __forceinline__ void final_reduce_n(uint32_t *ticket, double *sums, double (&acc)[kS],
-                                               double *red, const double *p1, int32_t n1,
-                                               const double *p2, int32_t n2)
-{
-    if (!last_group(ticket)) return;
+    __shared__ double red[(kWG / 64) * kS];
+    double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
-    for (int32_t g = threadIdx.x; g < n1 + n2; g += WG) {
+    for (int32_t g = threadIdx.x; g < n1 + n2; g += kWG) {
 #pragma unroll
         for (int c = 0; c < kS; ++c)
             acc[c] += g < n1 ? p1[int64_t(c) * n1 + g] : p2[int64_t(c) * n2 + (g - n1)];
     }
-    __syncthreads();  // red[] is reused
-    block_sum_n<WG>(acc, red, sums, 1);
-    if (threadIdx.x == 0) atomicExch(ticket, 0u);
-}
-
-template <int WG>
-__device__ __forceinline__ void icp_final_reduce_n(const IcpArgs &a, double (&acc)[kS],
-                                                   double *red, const double *p1, int32_t n1,
-                                                   const double *p2, int32_t n2)
-{
-    final_reduce_n<WG>(a.ticket, a.sums, acc, red, p1, n1, p2, n2);
-}
-
-__device__ __forceinline__ void icp_final_reduce(const IcpArgs &a, double (&acc)[kS], double *red,
-                                                 const double *p1, int32_t n1, const double *p2,
-                                                 int32_t n2)
-{
-    icp_final_reduce_n<kWG>(a, acc, red, p1, n1, p2, n2);
+    block_sum_n<kWG>(acc, red, out, 1);
+    if (stat && stat_out && threadIdx.x == 0) {
+        stat_out[0] = stat[0] / stat[1];
+        stat_out[1] = stat[2];
+    }
 }
 
 // Single pass, one kernel: transform, search (balanced wave search for G = 1,
@@ -1165,7 +1137,6 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         }
     }
     block_sum(acc, red, a.partials + blockIdx.x, nb);
-    icp_final_reduce(a, acc, red, a.partials, int32_t(nb), nullptr, 0);
 }
 
 // Two-pass mode, pass 1: one lane per point with a node budget; unfinished
@@ -1211,8 +1182,8 @@ __global__ __launch_bounds__(kWG) void icp_pass1_kernel(IcpArgs a, TwoPass tp)
     block_sum(acc, red, a.partials + blockIdx.x, gridDim.x);
 }
 
-// Two-pass mode, pass 2: groups of kPass2Lanes complete the listed points,
-// then the last group reduces both passes' partials.
+// Two-pass mode, pass 2: groups of kPass2Lanes complete the listed points
+// and write their partials after pass 1's.
 __global__ __launch_bounds__(kWG) void icp_pass2_kernel(IcpArgs a, TwoPass tp)
 {
     constexpr int G = kPass2Lanes;
@@ -1242,7 +1213,6 @@ __global__ __launch_bounds__(kWG) void icp_pass2_kernel(IcpArgs a, TwoPass tp)
         }
     }
     block_sum(acc, red, a.partials2 + blockIdx.x, gridDim.x);
-    icp_final_reduce(a, acc, red, a.partials, tp.nb1, a.partials2, int32_t(gridDim.x));
 }
 
 // Persistent single-lane correspondence kernel with the top levels in LDS.
@@ -1271,7 +1241,6 @@ __global__ __launch_bounds__(kPWG) void icp_persist_kernel(IcpArgs a, uint32_t l
         icp_accumulate(a, i, X, Y, Z, b, acc);
     }
     block_sum_n<kPWG>(acc, red, a.partials + blockIdx.x, gridDim.x);
-    icp_final_reduce_n<kPWG>(a, acc, red, a.partials, int32_t(gridDim.x), nullptr, 0);
 }
 
 // ------------------------------------------------- batched ICP (frame pairs)
@@ -1282,8 +1251,8 @@ __global__ __launch_bounds__(kPWG) void icp_persist_kernel(IcpArgs a, uint32_t l
 // pair p of a launch with B pairs gets the XCDs x with x % B == p.  Every XCD
 // then walks a single tree, which stays in its own L2 (a 131k-point frame
 // tree is ~2.6 MB of the 4 MB), instead of all of them thrashing it.  Each
-// pair reduces its work-groups' partials with its own ticket, in a fixed
-// order, into its 17 sums.
+// pair's work-group partials are then summed in a fixed order into its 17
+// sums (batch_reduce_kernel, one work-group per pair).
 constexpr int kBatchMax = 8;
 
 struct BatchPair {
@@ -1295,7 +1264,6 @@ struct BatchPair {
     double c[3];
     int32_t nb;       // work-groups of this pair: ceil(n / kWG)
     int32_t part;     // first partial column of this pair
-    uint32_t *ticket;
     double *sums;     // [kS] out
 };
 
@@ -1352,16 +1320,21 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
         }
     }
     block_sum(acc, red, a.partials + P.part + j, a.total);
-    if (!last_group_of(P.ticket, uint32_t(P.nb))) return;
+}
+
+// Work-group p: the sums of pair p from its work-groups' partial columns.
+__global__ __launch_bounds__(kWG) void batch_reduce_kernel(BatchArgs a)
+{
+    __shared__ double red[(kWG / 64) * kS];
+    const BatchPair &P = a.p[blockIdx.x];
+    double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     for (int32_t g = threadIdx.x; g < P.nb; g += kWG) {
 #pragma unroll
         for (int c = 0; c < kS; ++c) acc[c] += a.partials[int64_t(c) * a.total + P.part + g];
     }
-    __syncthreads();  // red[] is reused
     block_sum(acc, red, P.sums, 1);
-    if (threadIdx.x == 0) atomicExch(P.ticket, 0u);
 }
 
 // ------------------------------------------- residual rejection (3 sigma)
@@ -1386,10 +1359,7 @@ struct RejArgs {
     const int32_t *mslot;  // [n] original index of the match, -1 if none
     const float *md2;      // [n]
     double *partials;      // [kS][gridDim.x]
-    uint32_t *ticket;
     double *stat;          // device: sum r^2, pairs, threshold
-    double *sums;          // [kS] output of icp_reject_kernel
-    double *stat_out;      // [2] or null: sigma^2, threshold (written by icp_reject_kernel)
     uint8_t *kept;         // [n] or null: 1 where the pair is kept
 };
 
@@ -1415,7 +1385,6 @@ __device__ __forceinline__ double rej_residual_sq(const RejArgs &a, double X, do
 __global__ __launch_bounds__(kWG) void icp_residual_kernel(RejArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
-    __shared__ double tot[kS];
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
@@ -1427,24 +1396,29 @@ __global__ __launch_bounds__(kWG) void icp_residual_kernel(RejArgs a)
         acc[1] += 1.0;
     }
     block_sum(acc, red, a.partials + blockIdx.x, gridDim.x);
-    if (!last_group(a.ticket)) return;
-    const int32_t nb = int32_t(gridDim.x);
+}
+
+// sigma^2 and the threshold from the residual kernel's partials (one group).
+__global__ __launch_bounds__(kWG) void residual_stat_kernel(const double *p, int32_t nb, double kk,
+                                                            double *stat)
+{
+    __shared__ double red[(kWG / 64) * kS];
+    __shared__ double tot[kS];
+    double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     for (int32_t g = threadIdx.x; g < nb; g += kWG) {
-        acc[0] += a.partials[g];
-        acc[1] += a.partials[int64_t(nb) + g];
+        acc[0] += p[g];
+        acc[1] += p[int64_t(nb) + g];
     }
-    __syncthreads();  // red[] is reused
     block_sum(acc, red, tot, 1);
     __syncthreads();
     if (threadIdx.x == 0) {
         const double sum = tot[0];
         const double cnt = tot[1];
-        a.stat[0] = sum;
-        a.stat[1] = cnt;
-        a.stat[2] = a.kk * (sum / cnt);
-        atomicExch(a.ticket, 0u);
+        stat[0] = sum;
+        stat[1] = cnt;
+        stat[2] = kk * (sum / cnt);
     }
 }
 
@@ -1478,23 +1452,6 @@ __global__ __launch_bounds__(kWG) void icp_reject_kernel(RejArgs a)
         if (a.kept) a.kept[i] = keep ? 1 : 0;
     }
     block_sum(acc, red, a.partials + blockIdx.x, gridDim.x);
-    if (!last_group(a.ticket)) return;
-    const int32_t nb = int32_t(gridDim.x);
-#pragma unroll
-    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
-    for (int32_t g = threadIdx.x; g < nb; g += kWG) {
-#pragma unroll
-        for (int c = 0; c < kS; ++c) acc[c] += a.partials[int64_t(c) * nb + g];
-    }
-    __syncthreads();  // red[] is reused
-    block_sum(acc, red, a.sums, 1);
-    if (threadIdx.x == 0) {
-        if (a.stat_out) {
-            a.stat_out[0] = a.stat[0] / a.stat[1];
-            a.stat_out[1] = thr;
-        }
-        atomicExch(a.ticket, 0u);
-    }
 }
 
 // --------------------------------------------------------------- transform
@@ -1515,13 +1472,6 @@ __global__ __launch_bounds__(256) void transform_kernel(const float *in, float *
         out[3 * i + 1] = b;
         out[3 * i + 2] = c;
     }
-}
-
-__global__ void zero_u32_kernel(uint32_t *p, int64_t n)
-{
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += int64_t(gridDim.x) * blockDim.x)
-        p[i] = 0u;
 }
 
 // ------------------------------------------------------- Morton ordering
@@ -1790,7 +1740,7 @@ size_t icp_ws_bytes(int64_t n)
     if (n <= 0) return 0;
     const size_t nn = size_t(n);
     return sort_workspace_bytes(n) + align256(size_t(kS) * kIcpMaxBlocks * 8) +
-           align256(size_t(kS) * kPass2Blocks * 8) + align256(size_t(kS) * 8) + 256 +
+           align256(size_t(kS) * kPass2Blocks * 8) + align256(size_t(kS) * 8) +
            align256(nn * 4) + align256(nn * 8) + twopass_bytes(n) + 2 * align256(nn * 4) + 256;
 }
 
@@ -1806,8 +1756,6 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
     p += align256(size_t(kS) * kPass2Blocks * 8);
     w.sums = reinterpret_cast<double *>(p);
     p += align256(size_t(kS) * 8);
-    w.ticket = reinterpret_cast<uint32_t *>(p);
-    p += 256;
     w.pslot = reinterpret_cast<uint32_t *>(p);
     p += align256(size_t(n) * 4);
     w.pkey = reinterpret_cast<uint64_t *>(p);
@@ -1900,7 +1848,7 @@ hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m,
 hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                             const IcpWorkspace &ws, const int32_t **perm, hipStream_t s)
 {
-    return morton_order_impl(t, pts, m, R12, ws.sort, ws.ticket, perm, s);
+    return morton_order_impl(t, pts, m, R12, ws.sort, nullptr, perm, s);
 }
 
 template <int G>
@@ -2041,7 +1989,6 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     }
     a.partials = ws.partials;
     a.partials2 = ws.partials2;
-    a.ticket = ws.ticket;
     a.sums = sums_out;
     a.pkey = ws.pkey;
     a.pslot = ws.pslot;
@@ -2052,10 +1999,14 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     if (sc.lanes == 0 && sc.top_lds && persist_shape(a.tree, n, ps)) {
         allow_lds(icp_persist_kernel, ps.lds_bytes);
         icp_persist_kernel<<<ps.blocks, kPWG, ps.lds_bytes, s>>>(a, ps.lds_first);
+        reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, int32_t(ps.blocks), nullptr, 0,
+                                                 sums_out, nullptr, nullptr);
     } else if (sc.lanes == 0 && sc.budget != 0) {
         const TwoPass tp = carve_twopass(ws.twopass, n);
         icp_pass1_kernel<<<dim3(uint32_t(tp.nb1)), kWG, 0, s>>>(a, tp);
         icp_pass2_kernel<<<dim3(kPass2Blocks), kWG, 0, s>>>(a, tp);
+        reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, tp.nb1, a.partials2, kPass2Blocks,
+                                                 sums_out, nullptr, nullptr);
     } else {
         const dim3 grid(uint32_t(icp_blocks(n, sc.lanes ? sc.lanes : 1)));
         switch (sc.lanes) {
@@ -2065,6 +2016,8 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         case 16: icp_fused_kernel<16><<<grid, kWG, 0, s>>>(a); break;
         default: icp_fused_kernel<1><<<grid, kWG, 0, s>>>(a); break;
         }
+        reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, int32_t(grid.x), nullptr, 0,
+                                                 sums_out, nullptr, nullptr);
     }
     return hipGetLastError();
 }
@@ -2086,14 +2039,14 @@ hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, c
     a.mslot = ws.mslot;
     a.md2 = ws.md2;
     a.partials = ws.partials;
-    a.ticket = ws.ticket;
     a.stat = ws.stat;
-    a.sums = sums_out;
-    a.stat_out = stat_out;
     a.kept = kept;
-    const dim3 grid(uint32_t(icp_blocks(n, 1)));
-    icp_residual_kernel<<<grid, kWG, 0, s>>>(a);
-    icp_reject_kernel<<<grid, kWG, 0, s>>>(a);
+    const int32_t nb = icp_blocks(n, 1);
+    icp_residual_kernel<<<dim3(uint32_t(nb)), kWG, 0, s>>>(a);
+    residual_stat_kernel<<<1, kWG, 0, s>>>(a.partials, nb, kk, a.stat);
+    icp_reject_kernel<<<dim3(uint32_t(nb)), kWG, 0, s>>>(a);
+    reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, nb, nullptr, 0, sums_out, a.stat,
+                                             stat_out);
     return hipGetLastError();
 }
 
@@ -2105,7 +2058,7 @@ size_t icp_batch_ws_bytes(int32_t B, const int64_t *n)
 {
     int64_t total = 0;
     for (int32_t p = 0; p < B; ++p) total += batch_groups(n[p]);
-    return align256(size_t(kS) * size_t(total) * 8) + align256(size_t(B) * 4);
+    return align256(size_t(kS) * size_t(total) * 8);
 }
 
 hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void *ws, int32_t total,
@@ -2130,25 +2083,13 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
         }
         P.nb = batch_groups(J.n);
         P.part = J.part;
-        P.ticket = J.ticket;
         P.sums = J.sums;
         const int kx = (kNumXcd - p + B - 1) / B;
         const int64_t per_xcd = (P.nb + kx - 1) / kx;
         slots = per_xcd > slots ? per_xcd : slots;
     }
     icp_batch_kernel<<<dim3(uint32_t(slots * kNumXcd)), kWG, 0, s>>>(a);
-    return hipGetLastError();
-}
-
-uint32_t *batch_tickets(void *ws, int32_t total)
-{
-    return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
-                                        align256(size_t(kS) * size_t(total) * 8));
-}
-
-hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s)
-{
-    zero_u32_kernel<<<1, 64, 0, s>>>(p, n);
+    batch_reduce_kernel<<<dim3(uint32_t(B)), kWG, 0, s>>>(a);
     return hipGetLastError();
 }
 
