@@ -407,6 +407,22 @@ kdnn_status voxel_downsample(const float *xyz_dev, int64_t n, double leaf, float
  * next kdnn call on that thread. */
 const char *kdnn_last_error(void);
 
+/* Kernel timing, a profiling aid.  After kdnn_timing_begin(cap), each of the
+ * calling thread's next `cap` correspondence launches (icp_correspond_reduce,
+ * icp_correspond_reduce_async and each iteration of icp_align) has its search
+ * kernel's dispatch stamp a pair of HIP events with its start and end time
+ * (hipExtLaunchKernel; the traversal-order sort before it and the reduction
+ * after it fall outside; the two-pass schedule spans both passes); later
+ * launches are not timed.  kdnn_timing_end waits for the recorded events,
+ * writes the launch count to *count_out (optional) and, when ms_out is not
+ * null, the search kernel's duration in milliseconds of launch k to
+ * ms_out[k] (cap_out entries available, at least the count), and ends timing.
+ * cap: 1 .. KDNN_TIMING_MAX.  Errors: EINVAL (cap out of range, timing not
+ * started, cap_out too small: timing ends anyway), EDEVICE. */
+#define KDNN_TIMING_MAX 65536
+kdnn_status kdnn_timing_begin(int32_t cap);
+kdnn_status kdnn_timing_end(float *ms_out, int32_t cap_out, int32_t *count_out);
+
 /* KDNN_VERSION of the built library. */
 int32_t kdnn_version(void);
 

@@ -386,6 +386,23 @@ def procrustes(sums) -> tuple:
     return R.reshape(3, 3), t
 
 
+KDNN_TIMING_MAX = 65536
+
+
+def timing_begin(cap: int) -> None:
+    """Time the search kernel of this thread's next `cap` correspondence launches."""
+    _lib.check(_lib.lib().kdnn_timing_begin(int(cap)), "kdnn_timing_begin")
+
+
+def timing_end() -> np.ndarray:
+    """Wait for the timed launches; their search-kernel durations in ms (float32)."""
+    cnt = _lib.c_i32()
+    ms = np.zeros(KDNN_TIMING_MAX, np.float32)
+    _lib.check(_lib.lib().kdnn_timing_end(ms.ctypes.data_as(_lib.c_fp),
+                                          KDNN_TIMING_MAX, ctypes.byref(cnt)), "kdnn_timing_end")
+    return ms[:cnt.value].copy()
+
+
 def layout(n: int, leaf_size: int = 16, max_depth: int = 0, round_robin: bool = False):
     """(depth D, node slots 2^(D+1)) of the tree kdtree_build would make."""
     p = _params(leaf_size, max_depth, round_robin)

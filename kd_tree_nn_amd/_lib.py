@@ -94,6 +94,8 @@ SIGNATURES = {
     "voxel_downsample_workspace_bytes": (c_sz, [c_i64]),
     "voxel_downsample": (c_i32, [c_vp, c_i64, ctypes.c_double, c_vp, ctypes.POINTER(c_i64), c_vp,
                                  c_vp, c_sz, c_vp]),
+    "kdnn_timing_begin": (c_i32, [c_i32]),
+    "kdnn_timing_end": (c_i32, [c_fp, c_i32, ctypes.POINTER(c_i32)]),
     "kdnn_last_error": (ctypes.c_char_p, []),
     "kdnn_version": (c_i32, []),
 }

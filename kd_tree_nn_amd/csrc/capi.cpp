@@ -19,6 +19,29 @@ namespace {
 
 thread_local std::string g_err;
 
+// Kernel timing (kdnn_timing_begin / kdnn_timing_end): event pairs for the
+// next `cap` correspondence launches of this thread.
+struct Timing {
+    std::vector<hipEvent_t> ev;  // 2 per launch
+    int32_t used = 0;
+    bool on = false;
+    void release()
+    {
+        for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+        ev.clear();
+        used = 0;
+        on = false;
+    }
+    ~Timing() { release(); }
+    // next free pair, or null (off, or all used)
+    const hipEvent_t *next()
+    {
+        if (!on || 2 * size_t(used) >= ev.size()) return nullptr;
+        return &ev[2 * size_t(used++)];
+    }
+};
+thread_local Timing g_timing;
+
 kdnn_status fail(kdnn_status st, const std::string &msg)
 {
     g_err = msg;
@@ -161,7 +184,7 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
     }
     if (e != hipSuccess) return hip_fail(e, "icp: order launch");
     e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, schedule_of(flags),
-                         bound2, keep, s);
+                         bound2, keep, s, g_timing.next());
     if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
     return KDNN_OK;
 }
@@ -187,6 +210,51 @@ kdnn_status icp_check(const kdnn_tree *tree, const float *src, int64_t n, const 
 extern "C" {
 
 const char *kdnn_last_error(void) { return g_err.c_str(); }
+
+kdnn_status kdnn_timing_begin(int32_t cap)
+{
+    KDNN_GUARD_BEGIN
+    if (cap < 1 || cap > KDNN_TIMING_MAX)
+        return fail(KDNN_EINVAL, "kdnn_timing_begin: cap out of range");
+    g_timing.release();
+    g_timing.ev.reserve(2 * size_t(cap));
+    for (int32_t k = 0; k < 2 * cap; ++k) {
+        hipEvent_t e;
+        const hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            g_timing.release();
+            return hip_fail(r, "kdnn_timing_begin: hipEventCreate");
+        }
+        g_timing.ev.push_back(e);
+    }
+    g_timing.on = true;
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+kdnn_status kdnn_timing_end(float *ms_out, int32_t cap_out, int32_t *count_out)
+{
+    KDNN_GUARD_BEGIN
+    if (!g_timing.on) return fail(KDNN_EINVAL, "kdnn_timing_end: timing not started");
+    const int32_t used = g_timing.used;
+    if (count_out) *count_out = used;
+    if (ms_out && cap_out < used) {
+        g_timing.release();
+        return fail(KDNN_EINVAL, "kdnn_timing_end: cap_out smaller than the launch count");
+    }
+    for (int32_t k = 0; ms_out && k < used; ++k) {
+        hipEvent_t a = g_timing.ev[2 * size_t(k)], b = g_timing.ev[2 * size_t(k) + 1];
+        hipError_t r = hipEventSynchronize(b);
+        if (r == hipSuccess) r = hipEventElapsedTime(&ms_out[k], a, b);
+        if (r != hipSuccess) {
+            g_timing.release();
+            return hip_fail(r, "kdnn_timing_end: event");
+        }
+    }
+    g_timing.release();
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
 
 int32_t kdnn_version(void) { return KDNN_VERSION; }
 

@@ -120,10 +120,14 @@ hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32
                      const Schedule &sc, float bound2, void *twopass, hipStream_t s);
 hipError_t launch_transform(const float *in, float *out, int64_t n, const double *R,
                             const double *t, hipStream_t s);
+// Correspondence search + per-work-group partials, then the one-group
+// reduction into sums_out.  timing: null, or two events the search
+// kernel(s) stamp with their start and end.
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
-                            float bound2, bool keep_matches, hipStream_t s);
+                            float bound2, bool keep_matches, hipStream_t s,
+                            const hipEvent_t *timing = nullptr);
 // One stable LSD radix pass (8-bit digit at `shift`) of (key, value) pairs;
 // hist: 256 x radix_tiles(m) words, totals: 256 words.
 int32_t radix_tiles(int64_t m);

@@ -4,6 +4,7 @@
 // transform.  Built with -ffp-contract=off: every fp32 product and sum of
 // the distance code is rounded on its own, exactly as the host-side
 // definition writes it.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -1969,10 +1970,28 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
     return hipGetLastError();
 }
 
+template <typename T>
+struct same_type {
+    using type = T;
+};
+
+// Launch through hipExtLaunchKernel: a non-null e0 / e1 is stamped by the
+// dispatch itself at its start / end (no marker packets between kernels);
+// with both null it is a plain launch.
+template <typename... P>
+static hipError_t launch_k(void (*k)(P...), dim3 grid, uint32_t block, size_t lds, hipStream_t s,
+                           hipEvent_t e0, hipEvent_t e1, typename same_type<P>::type... args)
+{
+    void *pa[] = {static_cast<void *>(&args)...};
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(k), grid, dim3(block), pa, lds, s, e0,
+                              e1, 0);
+}
+
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
-                            float bound2, bool keep_matches, hipStream_t s)
+                            float bound2, bool keep_matches, hipStream_t s,
+                            const hipEvent_t *timing)
 {
     IcpArgs a{};
     a.tree = tree_view(t);
@@ -1995,27 +2014,37 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     a.idx = idx;
     a.d2 = d2;
     a.budget = sc.budget;
+    // the timing events bracket the search kernel(s), not the reduction
+    const hipEvent_t e0 = timing ? timing[0] : nullptr, e1 = timing ? timing[1] : nullptr;
+    hipError_t e;
     PersistShape ps;
     if (sc.lanes == 0 && sc.top_lds && persist_shape(a.tree, n, ps)) {
         allow_lds(icp_persist_kernel, ps.lds_bytes);
-        icp_persist_kernel<<<ps.blocks, kPWG, ps.lds_bytes, s>>>(a, ps.lds_first);
+        e = launch_k(icp_persist_kernel, dim3(ps.blocks), kPWG, ps.lds_bytes, s, e0, e1, a,
+                     ps.lds_first);
+        if (e != hipSuccess) return e;
         reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, int32_t(ps.blocks), nullptr, 0,
                                                  sums_out, nullptr, nullptr);
     } else if (sc.lanes == 0 && sc.budget != 0) {
         const TwoPass tp = carve_twopass(ws.twopass, n);
-        icp_pass1_kernel<<<dim3(uint32_t(tp.nb1)), kWG, 0, s>>>(a, tp);
-        icp_pass2_kernel<<<dim3(kPass2Blocks), kWG, 0, s>>>(a, tp);
+        e = launch_k(icp_pass1_kernel, dim3(uint32_t(tp.nb1)), kWG, 0, s, e0, nullptr, a, tp);
+        if (e == hipSuccess)
+            e = launch_k(icp_pass2_kernel, dim3(kPass2Blocks), kWG, 0, s, nullptr, e1, a, tp);
+        if (e != hipSuccess) return e;
         reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, tp.nb1, a.partials2, kPass2Blocks,
                                                  sums_out, nullptr, nullptr);
     } else {
         const dim3 grid(uint32_t(icp_blocks(n, sc.lanes ? sc.lanes : 1)));
+        void (*k)(IcpArgs);
         switch (sc.lanes) {
-        case 2: icp_fused_kernel<2><<<grid, kWG, 0, s>>>(a); break;
-        case 4: icp_fused_kernel<4><<<grid, kWG, 0, s>>>(a); break;
-        case 8: icp_fused_kernel<8><<<grid, kWG, 0, s>>>(a); break;
-        case 16: icp_fused_kernel<16><<<grid, kWG, 0, s>>>(a); break;
-        default: icp_fused_kernel<1><<<grid, kWG, 0, s>>>(a); break;
+        case 2: k = icp_fused_kernel<2>; break;
+        case 4: k = icp_fused_kernel<4>; break;
+        case 8: k = icp_fused_kernel<8>; break;
+        case 16: k = icp_fused_kernel<16>; break;
+        default: k = icp_fused_kernel<1>; break;
         }
+        e = launch_k(k, grid, kWG, 0, s, e0, e1, a);
+        if (e != hipSuccess) return e;
         reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, int32_t(grid.x), nullptr, 0,
                                                  sums_out, nullptr, nullptr);
     }

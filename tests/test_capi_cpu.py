@@ -241,3 +241,15 @@ def test_kdtree_build_rejects_before_device(kdnn):
     assert st == _lib.KDNN_ENONFINITE
     assert _lib.lib().nn_query_workspace_bytes(0) == 0
     assert _lib.lib().icp_workspace_bytes(100_000) > 100_000 * 12
+
+
+def test_timing_argument_errors(kdnn):
+    """kdnn_timing_begin / _end reject bad arguments before any event exists."""
+    from kd_tree_nn_amd import _lib
+    from kd_tree_nn_amd._lib import KdnnError
+    L = _lib.lib()
+    assert L.kdnn_timing_begin(0) == _lib.KDNN_EINVAL
+    assert L.kdnn_timing_begin(kdnn.KDNN_TIMING_MAX + 1) == _lib.KDNN_EINVAL
+    assert b"cap" in L.kdnn_last_error()
+    with pytest.raises(KdnnError, match="not started"):
+        kdnn.timing_end()

@@ -470,6 +470,31 @@ def test_fused_kernel_several_chunks_per_work_group(torch, kdnn):
         check_sums(res, red, bbox_diag(p.target), f"1.1M sums flags {f}")
 
 
+def test_kernel_timing(torch, kdnn):
+    """The timing facility records one positive duration per correspondence
+    launch, up to its cap, and leaves the results unchanged."""
+    p = scene()
+    tree = kdnn.Tree(p.target, 16)
+    src = dev(torch, p.source)
+    R, t = np.eye(3), np.zeros(3)
+    say("kernel timing, scene")
+    ref = tree.correspond_reduce(src, R, t, return_pairs=True)
+    ref_idx, ref_d2 = ref["idx"].cpu().numpy(), ref["d2"].cpu().numpy()
+    kdnn.timing_begin(3)
+    for _ in range(5):
+        res = tree.correspond_reduce(src, R, t, return_pairs=True)
+    ms = kdnn.timing_end()
+    assert len(ms) == 3 and np.all(ms > 0) and np.all(ms < 1e3)
+    assert np.array_equal(res["idx"].cpu().numpy(), ref_idx)
+    assert np.array_equal(res["d2"].cpu().numpy(), ref_d2)
+    assert res["E"] == ref["E"]
+    kdnn.timing_begin(2)
+    tree.correspond_reduce(src, R, t)
+    assert len(kdnn.timing_end()) == 1
+    with pytest.raises(Exception, match="not started"):
+        kdnn.timing_end()
+
+
 def _lib_flags():
     from kd_tree_nn_amd import _lib
     return _lib
