@@ -337,6 +337,7 @@ def main():
                 for _ in range(3):
                     tr.icp(src, max_iter=ITERS, workspace=iw)
                 torch.cuda.synchronize()
+                icp_us = (time.perf_counter() - t0) / (3 * ITERS) * 1e6
                 sweep.append({
                     "axis": "round_robin" if rr else "max_variance", "leaf": leaf,
                     "depth": inf_["depth"], "host_build_ms": round(inf_["build_ms"], 2),
@@ -344,7 +345,7 @@ def main():
                     "nn_query_us": round(float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3, 1),
                     "nodes_per_query": round(float(cn_.float().mean()), 2),
                     "points_per_query": round(float(cp_.float().mean()), 2),
-                    "icp_iter_us": round((time.perf_counter() - t0) / (3 * ITERS) * 1e6, 1)})
+                    "icp_iter_us": round(icp_us, 1)})
                 del tr
         log("sweep:", [(r["axis"][0], r["leaf"], r["nn_query_us"]) for r in sweep])
 
@@ -465,7 +466,7 @@ def main():
     pts_avg = float(np.mean(pts_tot)) / n
     n_blocks = min((n + 255) // 256, 4096)
     # node records + leaf points + the source point (+ its slot in the order)
-    per_query = 32 * nodes_avg + 16 * pts_avg + 12 + (4 if info["auto_sort"] else 0)
+    per_query = 32 * nodes_avg + 16 * pts_avg + 12 + (4 if info["auto_sort_icp"] else 0)
     bytes_launch = n * per_query + n_blocks * 17 * 8          # + the partials it writes
     achieved = bytes_launch / (kern_avg_ms * 1e-3) / 1e9
     descent_lb = 32 * (info["depth"] + 1) + 16 * (n / 2 ** info["depth"]) + 16

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDNN_VERSION 1
+#define KDNN_VERSION 2
 
 typedef enum kdnn_status {
     KDNN_OK = 0,
@@ -88,7 +88,8 @@ typedef struct kdnn_tree_info {
     double upload_ms;       /* device allocation + host-to-device copy */
     int64_t device_bytes;   /* device memory held by the tree */
     int64_t l2_bytes;       /* L2 cache size of the tree's device */
-    int32_t auto_sort;      /* 1: the automatic choice applies the Morton ordering */
+    int32_t auto_sort;      /* 1: nn_query's automatic choice applies the Morton ordering */
+    int32_t auto_sort_icp;  /* 1: the ICP entry points' automatic choice applies it */
 } kdnn_tree_info;
 
 /* Correspondence sums of one ICP iteration (article §2.1).  Over the pairs
@@ -161,10 +162,10 @@ kdnn_status kdtree_build_host(const float *xyz_host, int64_t n, const kdnn_build
 #define KDNN_QUERY_NO_SORT 1u /* traverse in the given order (skip the Morton ordering) */
 #define KDNN_QUERY_SORT 2u    /* always apply the Morton ordering (needs ws_dev) */
 /* Neither: the Morton ordering is applied when a workspace is given and the
- * tree's device footprint (kdnn_tree_info.device_bytes) exceeds the device's
- * L2 cache.  A tree that stays L2-resident gains little locality from the
- * ordering, which also packs the queries needing wide searches into the same
- * wavefronts.  Results never depend on the order. */
+ * tree's node records and points take more than 4 times the device's L2
+ * cache (kdnn_tree_info.auto_sort).  The ordering costs a sort on every
+ * call, and the search gains L2 locality from it only for trees well beyond
+ * the L2.  Results never depend on the order. */
 
 /* Search schedule (nn_query, nn_query_stats and the ICP entry points).
  * Default: one lane owns each query, and the 64 lanes of a wavefront share
@@ -245,8 +246,9 @@ kdnn_status transform_points(const float *in_dev, float *out_dev, int64_t n, con
                                    its traversal order instead of sorting again */
 #define KDNN_ICP_NO_SORT 2u     /* traverse source points in their given order */
 #define KDNN_ICP_SORT 4u        /* always traverse in Morton order of the transformed points */
-/* Neither NO_SORT nor SORT: Morton order when the tree's device footprint
- * exceeds the device's L2 cache (as for nn_query). */
+/* Neither NO_SORT nor SORT: Morton order when the tree's node records and
+ * points exceed the device's L2 cache (kdnn_tree_info.auto_sort_icp); the
+ * order is computed once per registration. */
 
 /* Correspondence rejection (article §4.4, both ways combined).
  *   max_dist : finite and > 0: a pair takes part only if its fp32 squared

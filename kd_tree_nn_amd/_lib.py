@@ -47,7 +47,8 @@ class TreeInfo(ctypes.Structure):
                 ("bbox_min", ctypes.c_float * 3), ("bbox_max", ctypes.c_float * 3),
                 ("center", ctypes.c_double * 3), ("build_ms", ctypes.c_double),
                 ("upload_ms", ctypes.c_double), ("device_bytes", c_i64),
-                ("l2_bytes", c_i64), ("auto_sort", c_i32)]
+                ("l2_bytes", c_i64), ("auto_sort", c_i32),
+                ("auto_sort_icp", c_i32)]
 
 
 class IcpReject(ctypes.Structure):

@@ -19,6 +19,12 @@ namespace {
 
 thread_local std::string g_err;
 
+// nn_query's automatic Morton ordering: tree footprint above this many L2s.
+// The ordering costs a radix sort per call (30-55 us at 0.1-1M queries); with
+// each wave's queries spread over its XCD's segment, the search gains about
+// that much only once the tree is several times the L2.
+constexpr size_t kQuerySortL2Multiple = 4;
+
 // Kernel timing (kdnn_timing_begin / kdnn_timing_end): event pairs for the
 // next `cap` correspondence launches of this thread.
 struct Timing {
@@ -144,7 +150,7 @@ const double kZ[3] = {0, 0, 0};
 uint32_t icp_resolve_sort(const kdnn_tree *tree, uint32_t flags)
 {
     const bool sort = (flags & KDNN_ICP_SORT) ||
-                      (!(flags & KDNN_ICP_NO_SORT) && tree->auto_sort);
+                      (!(flags & KDNN_ICP_NO_SORT) && tree->auto_sort_icp);
     flags &= ~(KDNN_ICP_SORT | KDNN_ICP_NO_SORT);
     return sort ? flags : (flags | KDNN_ICP_NO_SORT);
 }
@@ -382,9 +388,13 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         free_tree(t);
         return hip_fail(e, "kdtree_build: L2 size query");
     }
-    t->auto_sort = nb + pb > size_t(l2 > 0 ? l2 : 0);
+    // nn_query pays the ordering on every call, ICP once per registration
+    const size_t l2b = size_t(l2 > 0 ? l2 : 0);
+    t->auto_sort = nb + pb > kQuerySortL2Multiple * l2b;
+    t->auto_sort_icp = nb + pb > l2b;
     I.l2_bytes = l2;
     I.auto_sort = t->auto_sort ? 1 : 0;
+    I.auto_sort_icp = t->auto_sort_icp ? 1 : 0;
     *out = t;
     return KDNN_OK;
     KDNN_GUARD_END

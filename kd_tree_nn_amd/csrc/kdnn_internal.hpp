@@ -194,6 +194,7 @@ struct kdnn_tree {
     kdnn_tree_info info{};
     double *h_pinned = nullptr;  // host readback slot for the ICP sums
     double *d_pinned = nullptr;  // the same slot as the device addresses it
-    bool auto_sort = false;      // footprint exceeds L2: order queries unless told otherwise
+    bool auto_sort = false;      // nn_query orders queries unless told otherwise
+    bool auto_sort_icp = false;  // the ICP entry points order the source unless told otherwise
     std::mutex icp_mu;           // serialises users of h_pinned
 };

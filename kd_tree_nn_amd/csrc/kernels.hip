@@ -34,6 +34,7 @@ constexpr int kS = KDNN_SUMS_DOUBLES;
 
 // ------------------------------------------------------------------ helpers
 
+
 // Work-groups are dealt round-robin to the 8 XCDs (each with its own L2).
 // Map them so that every XCD works on one contiguous run of logical blocks,
 // i.e. on one spatially coherent slice of the Morton-ordered queries.
@@ -43,6 +44,43 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
     const uint32_t x = b % kNumXcd, slot = b / kNumXcd;
     const uint32_t q = nb / kNumXcd, r = nb % kNumXcd;
     return x * q + (x < r ? x : r) + slot;
+}
+
+// Which queries share a wave in the one-lane-per-query kernels.  The lanes
+// of a wave balance their searches among themselves, which only helps when a
+// wave mixes easy and hard queries; hard queries (sparse regions, points far
+// from the target) sit close together in space, hence in a Morton order or a
+// scan order, and 64 of them in one wave leave no lane idle to help: that
+// wave runs long.  So the kernels deal the positions of the order to lanes
+// through a bijection that spreads every wave's 64 queries evenly over the
+// segment of the order its XCD works on.  In each sweep of nb * kWG slots
+// the logical blocks of XCD x (xcd_remap) cover one contiguous segment
+// [s0, s0 + L), so every XCD still works on one run of the order (one region
+// of space for a Morton order: L2 locality).  Inside the segment (W =
+// ceil(L / 64) waves, the last one d = 64 W - L lanes short), lane l of the
+// segment's wave w takes position s0 + start(l) + w, where start(l) = l W -
+// max(0, l - (64 - d)) lays the 64 lanes' rows end to end.
+__device__ __forceinline__ int64_t spread_in(int64_t j, int64_t L)
+{
+    const int64_t W = (L + 63) >> 6;
+    const int l = int(j & 63);
+    const int d = int(64 * W - L);
+    const int64_t start = int64_t(l) * W - (l > 64 - d ? l - (64 - d) : 0);
+    return start + (j >> 6);
+}
+
+// Position for slot k < m (blk = xcd_remap(blockIdx.x, nb); base = the
+// sweep's first slot of this block).
+__device__ __forceinline__ int64_t spread_pos(int64_t k, int64_t blk, int64_t base, uint32_t nb,
+                                              int64_t m)
+{
+    if (!KDNN_XCD_REMAP) return k;
+    const int64_t sweep = base - blk * kWG;
+    const uint32_t x = blockIdx.x % kNumXcd;
+    const uint32_t q = nb / kNumXcd, r = nb % kNumXcd;
+    const int64_t s0 = sweep + (int64_t(x) * q + (x < r ? x : r)) * kWG;
+    const int64_t e = s0 + (int64_t(q) + (x < r ? 1 : 0)) * kWG;
+    return s0 + spread_in(k - s0, (e < m ? e : m) - s0);
 }
 
 // ----------------------------------------------------------- NN traversal
@@ -705,7 +743,8 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
         for (int64_t base = int64_t(blk) * kWG; base < a.m; base += int64_t(nb) * kWG) {
             const int64_t k = base + threadIdx.x;
             const bool own = k < a.m;
-            const int64_t i = own ? (a.perm ? int64_t(a.perm[k]) : k) : 0;
+            const int64_t pos = own ? spread_pos(k, blk, base, nb, a.m) : k;
+            const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
             const float qx = own ? a.q[3 * i] : 0.0f;
             const float qy = own ? a.q[3 * i + 1] : 0.0f;
             const float qz = own ? a.q[3 * i + 2] : 0.0f;
@@ -1109,7 +1148,8 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         for (int64_t base = int64_t(blk) * kWG; base < a.n; base += int64_t(nb) * kWG) {
             const int64_t k = base + threadIdx.x;
             const bool own = k < a.n;
-            const int64_t i = own ? (a.perm ? int64_t(a.perm[k]) : k) : 0;
+            const int64_t pos = own ? spread_pos(k, blk, base, nb, a.n) : k;
+            const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
             double X = 0.0, Y = 0.0, Z = 0.0;
             float qx = 0.0f, qy = 0.0f, qz = 0.0f;
             if (own) icp_query(a, i, X, Y, Z, qx, qy, qz);

@@ -470,6 +470,22 @@ def test_fused_kernel_several_chunks_per_work_group(torch, kdnn):
         check_sums(res, red, bbox_diag(p.target), f"1.1M sums flags {f}")
 
 
+def test_automatic_order_rule(torch, kdnn):
+    """nn_query orders its queries by default only for trees (node records +
+    points) above 4 L2s, the ICP entry points above one L2; Scene stays
+    unordered, Skewed 500k (leaf 8) is ordered for ICP only, Stress 1M both."""
+    for name, gen, leaf, want in (("scene", scene, 16, (0, 0)),
+                                  ("skewed", synth.skewed, 8, (0, 1)),
+                                  ("stress", synth.stress, 8, (1, 1))):
+        say("automatic order rule", name)
+        info = kdnn.Tree(gen().target, leaf).info
+        fp = info["node_slots"] * 32 + info["n"] * 16
+        l2 = info["l2_bytes"]
+        assert (info["auto_sort"], info["auto_sort_icp"]) == (int(fp > 4 * l2), int(fp > l2))
+        if l2 == 4 * 2**20:
+            assert (info["auto_sort"], info["auto_sort_icp"]) == want, name
+
+
 def test_kernel_timing(torch, kdnn):
     """The timing facility records one positive duration per correspondence
     launch, up to its cap, and leaves the results unchanged."""
