@@ -7,6 +7,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -70,11 +71,11 @@ __device__ __forceinline__ int64_t spread_in(int64_t j, int64_t L)
 }
 
 // Position for slot k < m (blk = xcd_remap(blockIdx.x, nb); base = the
-// sweep's first slot of this block).
-__device__ __forceinline__ int64_t spread_pos(int64_t k, int64_t blk, int64_t base, uint32_t nb,
-                                              int64_t m)
+// sweep's first slot of this block).  spread == false: position k.
+__device__ __forceinline__ int64_t spread_pos(bool spread, int64_t k, int64_t blk, int64_t base,
+                                              uint32_t nb, int64_t m)
 {
-    if (!KDNN_XCD_REMAP) return k;
+    if (!KDNN_XCD_REMAP || !spread) return k;
     const int64_t sweep = base - blk * kWG;
     const uint32_t x = blockIdx.x % kNumXcd;
     const uint32_t q = nb / kNumXcd, r = nb % kNumXcd;
@@ -713,6 +714,7 @@ struct NnArgs {
     float *d2;
     uint32_t *cnt_nodes;
     uint32_t *cnt_pts;
+    bool spread;  // one-lane-per-query kernel: spread_pos
 };
 
 // Cooperative search of one query by G >= 2 lanes.
@@ -743,7 +745,7 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
         for (int64_t base = int64_t(blk) * kWG; base < a.m; base += int64_t(nb) * kWG) {
             const int64_t k = base + threadIdx.x;
             const bool own = k < a.m;
-            const int64_t pos = own ? spread_pos(k, blk, base, nb, a.m) : k;
+            const int64_t pos = own ? spread_pos(a.spread, k, blk, base, nb, a.m) : k;
             const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
             const float qx = own ? a.q[3 * i] : 0.0f;
             const float qy = own ? a.q[3 * i + 1] : 0.0f;
@@ -1003,6 +1005,7 @@ struct IcpArgs {
     uint64_t init;      // bound key (bound +inf: none)
     int32_t *mslot;     // [n] or null: original index of each source point's match, -1 if none
     float *md2;         // [n] or null: its squared distance
+    bool spread;        // one-lane-per-query kernel: spread_pos
 };
 
 __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, double tr, double x,
@@ -1148,7 +1151,7 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         for (int64_t base = int64_t(blk) * kWG; base < a.n; base += int64_t(nb) * kWG) {
             const int64_t k = base + threadIdx.x;
             const bool own = k < a.n;
-            const int64_t pos = own ? spread_pos(k, blk, base, nb, a.n) : k;
+            const int64_t pos = own ? spread_pos(a.spread, k, blk, base, nb, a.n) : k;
             const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
             double X = 0.0, Y = 0.0, Z = 0.0;
             float qx = 0.0f, qy = 0.0f, qz = 0.0f;
@@ -1892,11 +1895,47 @@ hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, co
     return morton_order_impl(t, pts, m, R12, ws.sort, nullptr, perm, s);
 }
 
+// Work-groups of `kernel` (kWG lanes) the current device holds at once:
+// CUs x resident groups per CU; cached per device and slot (0 on failure).
+template <typename K>
+static int64_t resident_groups(K kernel, int slot)
+{
+    static std::atomic<int64_t> cache[64][2];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int64_t v = cache[dev][slot].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWG, 0) != hipSuccess)
+        return 0;
+    v = int64_t(cus) * per_cu;
+    cache[dev][slot].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// Spread the queries of a one-lane-per-query launch (spread_pos)?  Always for
+// the given order.  For a Morton order only while the launch fills at most
+// kSpreadMaxRounds rounds of resident work-groups: such a launch lasts as
+// long as its longest wave, so mixing easy and hard queries in every wave
+// pays; a longer launch overlaps its long waves with others, and keeping
+// each wave's queries side by side (fewer distinct cache lines per load)
+// pays more.
+constexpr int64_t kSpreadMaxRounds = 3;
+template <typename K>
+static bool spread_wanted(K kernel, int slot, int64_t m, bool ordered)
+{
+    if (!ordered) return true;
+    const int64_t groups = (m + kWG - 1) / kWG, res = resident_groups(kernel, slot);
+    return res > 0 && groups <= kSpreadMaxRounds * res;
+}
+
 template <int G>
-static void launch_nn_g(const NnArgs &a, bool stats, hipStream_t s)
+static void launch_nn_g(NnArgs a, bool stats, hipStream_t s)
 {
     int64_t blocks = (a.m + kWG / G - 1) / (kWG / G);
     if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+    if (G == 1) a.spread = spread_wanted(nn_kernel<1, false>, 0, a.m, a.perm != nullptr);
     if (stats)
         nn_kernel<G, true><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
     else
@@ -2054,6 +2093,7 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     a.idx = idx;
     a.d2 = d2;
     a.budget = sc.budget;
+    a.spread = spread_wanted(icp_fused_kernel<1>, 1, n, perm != nullptr);
     // the timing events bracket the search kernel(s), not the reduction
     const hipEvent_t e0 = timing ? timing[0] : nullptr, e1 = timing ? timing[1] : nullptr;
     hipError_t e;
