@@ -7,6 +7,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -24,6 +25,10 @@ namespace kdnn {
 #define KDNN_XCD_REMAP 1
 #endif
 constexpr int kWG = KDNN_WG;                      // traversal work-group size
+// Queries owned per wave in the one-lane-per-query kernels: 2^qs, qs = 5 or
+// 6 per launch (with 32, the other lanes start idle and take over pending
+// subtrees); (kWG / 64) 2^qs per work-group and sweep.
+constexpr uint32_t kQsSmall = 5, kQsFull = 6;
 constexpr int kLeafChunk = 16;                    // leaf points loaded per batch (one lane)
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
@@ -61,27 +66,29 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
 // ceil(L / 64) waves, the last one d = 64 W - L lanes short), lane l of the
 // segment's wave w takes position s0 + start(l) + w, where start(l) = l W -
 // max(0, l - (64 - d)) lays the 64 lanes' rows end to end.
-__device__ __forceinline__ int64_t spread_in(int64_t j, int64_t L)
+__device__ __forceinline__ int64_t spread_in(int64_t j, int64_t L, uint32_t qs)
 {
-    const int64_t W = (L + 63) >> 6;
-    const int l = int(j & 63);
-    const int d = int(64 * W - L);
-    const int64_t start = int64_t(l) * W - (l > 64 - d ? l - (64 - d) : 0);
-    return start + (j >> 6);
+    const int Q = 1 << qs;
+    const int64_t W = (L + Q - 1) >> qs;
+    const int l = int(j & (Q - 1));
+    const int d = int(int64_t(Q) * W - L);
+    const int64_t start = int64_t(l) * W - (l > Q - d ? l - (Q - d) : 0);
+    return start + (j >> qs);
 }
 
 // Position for slot k < m (blk = xcd_remap(blockIdx.x, nb); base = the
 // sweep's first slot of this block).  spread == false: position k.
-__device__ __forceinline__ int64_t spread_pos(bool spread, int64_t k, int64_t blk, int64_t base,
-                                              uint32_t nb, int64_t m)
+__device__ __forceinline__ int64_t spread_pos(bool spread, uint32_t qs, int64_t k, int64_t blk,
+                                              int64_t base, uint32_t nb, int64_t m)
 {
     if (!KDNN_XCD_REMAP || !spread) return k;
-    const int64_t sweep = base - blk * kWG;
+    const int64_t QB = int64_t(kWG / 64) << qs;
+    const int64_t sweep = base - blk * QB;
     const uint32_t x = blockIdx.x % kNumXcd;
     const uint32_t q = nb / kNumXcd, r = nb % kNumXcd;
-    const int64_t s0 = sweep + (int64_t(x) * q + (x < r ? x : r)) * kWG;
-    const int64_t e = s0 + (int64_t(q) + (x < r ? 1 : 0)) * kWG;
-    return s0 + spread_in(k - s0, (e < m ? e : m) - s0);
+    const int64_t s0 = sweep + (int64_t(x) * q + (x < r ? x : r)) * QB;
+    const int64_t e = s0 + (int64_t(q) + (x < r ? 1 : 0)) * QB;
+    return s0 + spread_in(k - s0, (e < m ? e : m) - s0, qs);
 }
 
 // ----------------------------------------------------------- NN traversal
@@ -715,6 +722,7 @@ struct NnArgs {
     uint32_t *cnt_nodes;
     uint32_t *cnt_pts;
     bool spread;  // one-lane-per-query kernel: spread_pos
+    uint32_t qs;  // one-lane-per-query kernel: 2^qs queries per wave
 };
 
 // Cooperative search of one query by G >= 2 lanes.
@@ -742,10 +750,13 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
         __shared__ float lbs[kDevMaxDepth * kWG];
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t ocn[STATS ? kWG : 1], ocp[STATS ? kWG : 1];
-        for (int64_t base = int64_t(blk) * kWG; base < a.m; base += int64_t(nb) * kWG) {
-            const int64_t k = base + threadIdx.x;
-            const bool own = k < a.m;
-            const int64_t pos = own ? spread_pos(a.spread, k, blk, base, nb, a.m) : k;
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const uint32_t qs = a.qs;
+        const int64_t QB = int64_t(kWG / 64) << qs;
+        for (int64_t base = int64_t(blk) * QB; base < a.m; base += int64_t(nb) * QB) {
+            const int64_t k = base + (int64_t(wv) << qs) + lane;
+            const bool own = lane < (1 << qs) && k < a.m;
+            const int64_t pos = own ? spread_pos(a.spread, qs, k, blk, base, nb, a.m) : k;
             const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
             const float qx = own ? a.q[3 * i] : 0.0f;
             const float qy = own ? a.q[3 * i + 1] : 0.0f;
@@ -1006,6 +1017,7 @@ struct IcpArgs {
     int32_t *mslot;     // [n] or null: original index of each source point's match, -1 if none
     float *md2;         // [n] or null: its squared distance
     bool spread;        // one-lane-per-query kernel: spread_pos
+    uint32_t qs;        // one-lane-per-query kernel: 2^qs queries per wave
 };
 
 __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, double tr, double x,
@@ -1139,32 +1151,61 @@ template <int G>
 __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
-    double acc[kS];
-#pragma unroll
-    for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     const uint32_t nb = gridDim.x;
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
     if constexpr (G == 1) {
-        // one lane owns each source point; the wave balances the searches
+        // One lane owns each source point; the wave balances the searches.
+        // Each sweep's pairs are summed over the wave at once and added to the
+        // wave's row of red (lane 63), so no sums stay live in registers
+        // across the next search.
         __shared__ float lbs[kDevMaxDepth * kWG];
         __shared__ unsigned long long okey[kWG];
-        for (int64_t base = int64_t(blk) * kWG; base < a.n; base += int64_t(nb) * kWG) {
-            const int64_t k = base + threadIdx.x;
-            const bool own = k < a.n;
-            const int64_t pos = own ? spread_pos(a.spread, k, blk, base, nb, a.n) : k;
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        if (lane == 63) {
+#pragma unroll
+            for (int c = 0; c < kS; ++c) red[wv * kS + c] = 0.0;
+        }
+        const uint32_t qs = a.qs;
+        const int64_t QB = int64_t(kWG / 64) << qs;
+        for (int64_t base = int64_t(blk) * QB; base < a.n; base += int64_t(nb) * QB) {
+            const int64_t k = base + (int64_t(wv) << qs) + lane;
+            const bool own = lane < (1 << qs) && k < a.n;
+            const int64_t pos = own ? spread_pos(a.spread, qs, k, blk, base, nb, a.n) : k;
             const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
-            double X = 0.0, Y = 0.0, Z = 0.0;
             float qx = 0.0f, qy = 0.0f, qz = 0.0f;
-            if (own) icp_query(a, i, X, Y, Z, qx, qy, qz);
+            if (own) {
+                double X, Y, Z;
+                icp_query(a, i, X, Y, Z, qx, qy, qz);
+            }
             wave_search<false>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, nullptr,
                                nullptr);
+            double acc[kS];
+#pragma unroll
+            for (int c = 0; c < kS; ++c) acc[c] = 0.0;
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
+                // the source point again (cheaper than keeping it in registers)
+                const double X = a.src[3 * i], Y = a.src[3 * i + 1], Z = a.src[3 * i + 2];
                 icp_accumulate(a, i, X, Y, Z, b, acc);
             }
+#pragma unroll
+            for (int c = 0; c < kS; ++c) acc[c] = wave_total(acc[c]);
+            if (lane == 63) {
+#pragma unroll
+                for (int c = 0; c < kS; ++c) red[wv * kS + c] += acc[c];
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < kS) {
+            double s = 0.0;
+            for (int ww = 0; ww < kWG / 64; ++ww) s += red[ww * kS + threadIdx.x];
+            a.partials[int64_t(threadIdx.x) * nb + blockIdx.x] = s;
         }
     } else {
+        double acc[kS];
+#pragma unroll
+        for (int c = 0; c < kS; ++c) acc[c] = 0.0;
         constexpr int QPB = kWG / G;
         const int gl = threadIdx.x & (G - 1);
         for (int64_t base = int64_t(blk) * QPB; base < a.n; base += int64_t(nb) * QPB) {
@@ -1179,8 +1220,8 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
             search_query<G, false>(a.tree, qx, qy, qz, a.init, b, cn, cp);
             if (gl == 0) icp_accumulate(a, i, X, Y, Z, b, acc);
         }
+        block_sum(acc, red, a.partials + blockIdx.x, nb);
     }
-    block_sum(acc, red, a.partials + blockIdx.x, nb);
 }
 
 // Two-pass mode, pass 1: one lane per point with a node budget; unfinished
@@ -1773,9 +1814,10 @@ QueryWorkspace carve_query_workspace(void *ws, int64_t m)
     return w;
 }
 
-static int32_t icp_blocks(int64_t n, int G)
+static int32_t icp_blocks(int64_t n, int G, uint32_t qs = kQsFull)
 {
-    const int64_t b = (n + kWG / G - 1) / (kWG / G);
+    const int64_t per = G == 1 ? (int64_t(kWG / 64) << qs) : kWG / G;  // per group and sweep
+    const int64_t b = (n + per - 1) / per;
     return int32_t(b < 1 ? 1 : (b > kIcpMaxBlocks ? kIcpMaxBlocks : b));
 }
 
@@ -1930,12 +1972,28 @@ static bool spread_wanted(K kernel, int slot, int64_t m, bool ordered)
     return res > 0 && groups <= kSpreadMaxRounds * res;
 }
 
+// Queries per wave (log2) of a one-lane-per-query launch of m queries: 32
+// while 64 per wave would not fill one round of resident work-groups (the
+// launch lasts as long as its longest wave, and idle lanes help shorten it
+// at no cost in occupancy), else 64 (the extra lanes would only add
+// redundant subtree work to a machine that is already full).
+template <typename K>
+static uint32_t wave_shift(K kernel, int slot, int64_t m)
+{
+    const int64_t groups = (m + kWG - 1) / kWG, res = resident_groups(kernel, slot);
+    return (res > 0 && groups <= res) ? kQsSmall : kQsFull;
+}
+
 template <int G>
 static void launch_nn_g(NnArgs a, bool stats, hipStream_t s)
 {
-    int64_t blocks = (a.m + kWG / G - 1) / (kWG / G);
+    if (G == 1) {
+        a.spread = spread_wanted(nn_kernel<1, false>, 0, a.m, a.perm != nullptr);
+        a.qs = wave_shift(nn_kernel<1, false>, 0, a.m);
+    }
+    const int64_t per = G == 1 ? (int64_t(kWG / 64) << a.qs) : kWG / G;  // per group and sweep
+    int64_t blocks = (a.m + per - 1) / per;
     if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
-    if (G == 1) a.spread = spread_wanted(nn_kernel<1, false>, 0, a.m, a.perm != nullptr);
     if (stats)
         nn_kernel<G, true><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
     else
@@ -2094,6 +2152,7 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     a.d2 = d2;
     a.budget = sc.budget;
     a.spread = spread_wanted(icp_fused_kernel<1>, 1, n, perm != nullptr);
+    a.qs = wave_shift(icp_fused_kernel<1>, 1, n);
     // the timing events bracket the search kernel(s), not the reduction
     const hipEvent_t e0 = timing ? timing[0] : nullptr, e1 = timing ? timing[1] : nullptr;
     hipError_t e;
@@ -2114,7 +2173,7 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, tp.nb1, a.partials2, kPass2Blocks,
                                                  sums_out, nullptr, nullptr);
     } else {
-        const dim3 grid(uint32_t(icp_blocks(n, sc.lanes ? sc.lanes : 1)));
+        const dim3 grid(uint32_t(icp_blocks(n, sc.lanes ? sc.lanes : 1, a.qs)));
         void (*k)(IcpArgs);
         switch (sc.lanes) {
         case 2: k = icp_fused_kernel<2>; break;
@@ -2150,7 +2209,8 @@ hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, c
     a.partials = ws.partials;
     a.stat = ws.stat;
     a.kept = kept;
-    const int32_t nb = icp_blocks(n, 1);
+    const int32_t nb = int32_t(std::min<int64_t>(std::max<int64_t>((n + kWG - 1) / kWG, 1),
+                                                 kIcpMaxBlocks));
     icp_residual_kernel<<<dim3(uint32_t(nb)), kWG, 0, s>>>(a);
     residual_stat_kernel<<<1, kWG, 0, s>>>(a.partials, nb, kk, a.stat);
     icp_reject_kernel<<<dim3(uint32_t(nb)), kWG, 0, s>>>(a);
