@@ -221,9 +221,14 @@ kdnn_status nn_query_radius(const kdnn_tree *tree, const float *q_dev, int64_t m
                             int32_t *idx_dev, float *dist2_dev, uint32_t flags, void *ws_dev,
                             size_t ws_bytes, hipStream_t stream);
 
-/* Instrumented nn_query: same traversal, same results, and per query the
- * number of tree nodes loaded and of leaf points scanned (uint32 each, may be
- * NULL).  For measurement only; slower than nn_query. */
+/* Instrumented nn_query: same results, and per query the number of tree node
+ * records loaded and of leaf points scanned (uint32 each, may be NULL).  With
+ * the default schedule the counts are those of the exact single-lane search
+ * of that query (lanes do not share work in this mode, so the counts do not
+ * depend on which queries share a wavefront; the balanced search of nn_query
+ * loads these plus the extra visits of subtrees handed over).  With
+ * KDNN_LANES / KDNN_BUDGET / KDNN_TOP_LDS: the counts of that schedule's
+ * traversal.  For measurement only; slower than nn_query. */
 kdnn_status nn_query_stats(const kdnn_tree *tree, const float *q_dev, int64_t m, int32_t *idx_dev,
                            float *dist2_dev, uint32_t *nodes_dev, uint32_t *points_dev,
                            uint32_t flags, void *ws_dev, size_t ws_bytes, hipStream_t stream);

@@ -28,7 +28,10 @@ constexpr int kWG = KDNN_WG;                      // traversal work-group size
 // Queries owned per wave in the one-lane-per-query kernels: 2^qs, qs = 5 or
 // 6 per launch (with 32, the other lanes start idle and take over pending
 // subtrees); (kWG / 64) 2^qs per work-group and sweep.
-constexpr uint32_t kQsSmall = 5, kQsFull = 6;
+#ifndef KDNN_QS_SMALL
+#define KDNN_QS_SMALL 5
+#endif
+constexpr uint32_t kQsSmall = KDNN_QS_SMALL, kQsFull = 6;
 constexpr int kLeafChunk = 16;                    // leaf points loaded per batch (one lane)
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
@@ -622,7 +625,10 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
 // work-group's LDS arrays [kWG], slot threadIdx.x = this lane's own query.
 // On return okey[threadIdx.x] holds the answer key of this lane's query (the
 // bound key when there is none), ocn / ocp its node / point counts (STATS).
-template <bool STATS>
+// BALANCE == false: no hand-over, every lane searches its own query alone
+// (the plain single-lane pair search; its counts are the method's own work,
+// independent of which queries share a wave).
+template <bool STATS, bool BALANCE = true>
 __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
                                             float oqz, uint64_t init, float *lbs,
                                             unsigned long long *okey, uint32_t *ocn,
@@ -675,7 +681,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                 }
             }
             task_finish<STATS>(w, okey, ocn, ocp);
-            if (KDNN_P1_HANDOVER) task_handover(w, lbs, okey, KDNN_P1_MIN_IDLE);
+            if (BALANCE && KDNN_P1_HANDOVER) task_handover(w, lbs, okey, KDNN_P1_MIN_IDLE);
         }
         // Phase 2: leaves, then share the improved best of the query.
         if (w.i != kDone) {
@@ -706,7 +712,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
         }
         task_finish<STATS>(w, okey, ocn, ocp);
         if (__ballot(w.owner != kNoOwner) == 0) break;
-        task_handover(w, lbs, okey);
+        if (BALANCE) task_handover(w, lbs, okey);
     }
 }
 
@@ -761,7 +767,9 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             const float qx = own ? a.q[3 * i] : 0.0f;
             const float qy = own ? a.q[3 * i + 1] : 0.0f;
             const float qz = own ? a.q[3 * i + 2] : 0.0f;
-            wave_search<STATS>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, ocn, ocp);
+            // the instrumented kernel counts the single-lane search of each query
+            wave_search<STATS, !STATS>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
+                                       ocn, ocp);
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
@@ -1973,23 +1981,26 @@ static bool spread_wanted(K kernel, int slot, int64_t m, bool ordered)
 }
 
 // Queries per wave (log2) of a one-lane-per-query launch of m queries: 32
-// while 64 per wave would not fill one round of resident work-groups (the
-// launch lasts as long as its longest wave, and idle lanes help shorten it
-// at no cost in occupancy), else 64 (the extra lanes would only add
-// redundant subtree work to a machine that is already full).
+// for an unbounded search while 64 per wave would not fill one round of
+// resident work-groups (the launch lasts as long as its longest wave, and the
+// idle lanes shorten it by taking pending far subtrees, at no cost in
+// occupancy), else 64: on a full machine the extra lanes would only add
+// redundant subtree work, and under a distance bound few far subtrees are
+// pending to be taken (measured: 57 vs 52 us per Scene ICP iteration).
 template <typename K>
-static uint32_t wave_shift(K kernel, int slot, int64_t m)
+static uint32_t wave_shift(K kernel, int slot, int64_t m, float bound2)
 {
+    if (!(bound2 == INFINITY)) return kQsFull;
     const int64_t groups = (m + kWG - 1) / kWG, res = resident_groups(kernel, slot);
     return (res > 0 && groups <= res) ? kQsSmall : kQsFull;
 }
 
 template <int G>
-static void launch_nn_g(NnArgs a, bool stats, hipStream_t s)
+static void launch_nn_g(NnArgs a, bool stats, float bound2, hipStream_t s)
 {
     if (G == 1) {
         a.spread = spread_wanted(nn_kernel<1, false>, 0, a.m, a.perm != nullptr);
-        a.qs = wave_shift(nn_kernel<1, false>, 0, a.m);
+        a.qs = stats ? kQsFull : wave_shift(nn_kernel<1, false>, 0, a.m, bound2);
     }
     const int64_t per = G == 1 ? (int64_t(kWG / 64) << a.qs) : kWG / G;  // per group and sweep
     int64_t blocks = (a.m + per - 1) / per;
@@ -2086,11 +2097,11 @@ hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32
         launch_nn_two_pass(a, stats, twopass, s);
     } else {
         switch (sc.lanes) {
-        case 2: launch_nn_g<2>(a, stats, s); break;
-        case 4: launch_nn_g<4>(a, stats, s); break;
-        case 8: launch_nn_g<8>(a, stats, s); break;
-        case 16: launch_nn_g<16>(a, stats, s); break;
-        default: launch_nn_g<1>(a, stats, s); break;
+        case 2: launch_nn_g<2>(a, stats, bound2, s); break;
+        case 4: launch_nn_g<4>(a, stats, bound2, s); break;
+        case 8: launch_nn_g<8>(a, stats, bound2, s); break;
+        case 16: launch_nn_g<16>(a, stats, bound2, s); break;
+        default: launch_nn_g<1>(a, stats, bound2, s); break;
         }
     }
     return hipGetLastError();
@@ -2152,7 +2163,7 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     a.d2 = d2;
     a.budget = sc.budget;
     a.spread = spread_wanted(icp_fused_kernel<1>, 1, n, perm != nullptr);
-    a.qs = wave_shift(icp_fused_kernel<1>, 1, n);
+    a.qs = wave_shift(icp_fused_kernel<1>, 1, n, bound2);
     // the timing events bracket the search kernel(s), not the reduction
     const hipEvent_t e0 = timing ? timing[0] : nullptr, e1 = timing ? timing[1] : nullptr;
     hipError_t e;

@@ -194,6 +194,14 @@ def test_query_stats_consistent(torch, kdnn):
         assert int(cn.max()) <= 2 ** (D + 1) + 2 * (D + 1)
         if sched in ({"lanes": 1}, {}, {"budget": 64}):
             assert float(cn.float().mean()) < 0.25 * 2 ** (D + 1)
+    # default schedule: each query's own single-lane counts, whichever queries
+    # share its wavefront (given order, a permutation, the Morton order)
+    perm = torch.randperm(len(q), generator=torch.Generator().manual_seed(3)).cuda()
+    _, _, cn1, cp1 = tree.query_stats(q)
+    _, _, cn2, cp2 = tree.query_stats(q[perm].contiguous())
+    assert torch.equal(cn1[perm], cn2) and torch.equal(cp1[perm], cp2)
+    _, _, cn3, cp3 = tree.query_stats(q, sort=True)
+    assert torch.equal(cn1, cn3) and torch.equal(cp1, cp3)
 
 
 # ================================================================ transform
