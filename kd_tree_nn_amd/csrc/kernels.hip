@@ -25,13 +25,16 @@ namespace kdnn {
 #define KDNN_XCD_REMAP 1
 #endif
 constexpr int kWG = KDNN_WG;                      // traversal work-group size
-// Queries owned per wave in the one-lane-per-query kernels: 2^qs, qs = 5 or
-// 6 per launch (with 32, the other lanes start idle and take over pending
-// subtrees); (kWG / 64) 2^qs per work-group and sweep.
-#ifndef KDNN_QS_SMALL
-#define KDNN_QS_SMALL 5
+// Queries owned per wave in the one-lane-per-query kernels: q <= 64, chosen
+// per launch (wave_plan); with q < 64 the other lanes start idle and take
+// over pending subtrees.  (kWG / 64) q queries per work-group and sweep.
+#ifndef KDNN_Q_TARGET_NN
+#define KDNN_Q_TARGET_NN 33
 #endif
-constexpr uint32_t kQsSmall = KDNN_QS_SMALL, kQsFull = 6;
+#ifndef KDNN_Q_TARGET_ICP
+#define KDNN_Q_TARGET_ICP 43
+#endif
+constexpr uint32_t kQFull = 64;
 constexpr int kLeafChunk = 16;                    // leaf points loaded per batch (one lane)
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
@@ -69,29 +72,30 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
 // ceil(L / 64) waves, the last one d = 64 W - L lanes short), lane l of the
 // segment's wave w takes position s0 + start(l) + w, where start(l) = l W -
 // max(0, l - (64 - d)) lays the 64 lanes' rows end to end.
-__device__ __forceinline__ int64_t spread_in(int64_t j, int64_t L, uint32_t qs)
+__device__ __forceinline__ int64_t spread_in(int64_t j, int64_t L, uint32_t q)
 {
-    const int Q = 1 << qs;
-    const int64_t W = (L + Q - 1) >> qs;
-    const int l = int(j & (Q - 1));
+    const int Q = int(q);
+    const int64_t W = (L + Q - 1) / Q;
+    const int64_t w = j / Q;
+    const int l = int(j - w * Q);
     const int d = int(int64_t(Q) * W - L);
     const int64_t start = int64_t(l) * W - (l > Q - d ? l - (Q - d) : 0);
-    return start + (j >> qs);
+    return start + w;
 }
 
 // Position for slot k < m (blk = xcd_remap(blockIdx.x, nb); base = the
 // sweep's first slot of this block).  spread == false: position k.
-__device__ __forceinline__ int64_t spread_pos(bool spread, uint32_t qs, int64_t k, int64_t blk,
+__device__ __forceinline__ int64_t spread_pos(bool spread, uint32_t wq, int64_t k, int64_t blk,
                                               int64_t base, uint32_t nb, int64_t m)
 {
     if (!KDNN_XCD_REMAP || !spread) return k;
-    const int64_t QB = int64_t(kWG / 64) << qs;
+    const int64_t QB = int64_t(kWG / 64) * wq;
     const int64_t sweep = base - blk * QB;
     const uint32_t x = blockIdx.x % kNumXcd;
     const uint32_t q = nb / kNumXcd, r = nb % kNumXcd;
     const int64_t s0 = sweep + (int64_t(x) * q + (x < r ? x : r)) * QB;
     const int64_t e = s0 + (int64_t(q) + (x < r ? 1 : 0)) * QB;
-    return s0 + spread_in(k - s0, (e < m ? e : m) - s0, qs);
+    return s0 + spread_in(k - s0, (e < m ? e : m) - s0, wq);
 }
 
 // ----------------------------------------------------------- NN traversal
@@ -728,7 +732,7 @@ struct NnArgs {
     uint32_t *cnt_nodes;
     uint32_t *cnt_pts;
     bool spread;  // one-lane-per-query kernel: spread_pos
-    uint32_t qs;  // one-lane-per-query kernel: 2^qs queries per wave
+    uint32_t wq;  // one-lane-per-query kernel: queries per wave (1..64)
 };
 
 // Cooperative search of one query by G >= 2 lanes.
@@ -757,12 +761,12 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t ocn[STATS ? kWG : 1], ocp[STATS ? kWG : 1];
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-        const uint32_t qs = a.qs;
-        const int64_t QB = int64_t(kWG / 64) << qs;
+        const uint32_t wq = a.wq;
+        const int64_t QB = int64_t(kWG / 64) * wq;
         for (int64_t base = int64_t(blk) * QB; base < a.m; base += int64_t(nb) * QB) {
-            const int64_t k = base + (int64_t(wv) << qs) + lane;
-            const bool own = lane < (1 << qs) && k < a.m;
-            const int64_t pos = own ? spread_pos(a.spread, qs, k, blk, base, nb, a.m) : k;
+            const int64_t k = base + int64_t(wv) * wq + lane;
+            const bool own = uint32_t(lane) < wq && k < a.m;
+            const int64_t pos = own ? spread_pos(a.spread, wq, k, blk, base, nb, a.m) : k;
             const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
             const float qx = own ? a.q[3 * i] : 0.0f;
             const float qy = own ? a.q[3 * i + 1] : 0.0f;
@@ -1025,7 +1029,7 @@ struct IcpArgs {
     int32_t *mslot;     // [n] or null: original index of each source point's match, -1 if none
     float *md2;         // [n] or null: its squared distance
     bool spread;        // one-lane-per-query kernel: spread_pos
-    uint32_t qs;        // one-lane-per-query kernel: 2^qs queries per wave
+    uint32_t wq;        // one-lane-per-query kernel: queries per wave (1..64)
 };
 
 __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, double tr, double x,
@@ -1173,12 +1177,12 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
 #pragma unroll
             for (int c = 0; c < kS; ++c) red[wv * kS + c] = 0.0;
         }
-        const uint32_t qs = a.qs;
-        const int64_t QB = int64_t(kWG / 64) << qs;
+        const uint32_t wq = a.wq;
+        const int64_t QB = int64_t(kWG / 64) * wq;
         for (int64_t base = int64_t(blk) * QB; base < a.n; base += int64_t(nb) * QB) {
-            const int64_t k = base + (int64_t(wv) << qs) + lane;
-            const bool own = lane < (1 << qs) && k < a.n;
-            const int64_t pos = own ? spread_pos(a.spread, qs, k, blk, base, nb, a.n) : k;
+            const int64_t k = base + int64_t(wv) * wq + lane;
+            const bool own = uint32_t(lane) < wq && k < a.n;
+            const int64_t pos = own ? spread_pos(a.spread, wq, k, blk, base, nb, a.n) : k;
             const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
             float qx = 0.0f, qy = 0.0f, qz = 0.0f;
             if (own) {
@@ -1822,9 +1826,10 @@ QueryWorkspace carve_query_workspace(void *ws, int64_t m)
     return w;
 }
 
-static int32_t icp_blocks(int64_t n, int G, uint32_t qs = kQsFull)
+// Work-groups of a fused launch: `per` points per group and sweep (G lanes per
+// point: kWG / G), at most kIcpMaxBlocks (the partials' columns).
+static int32_t icp_blocks(int64_t n, int64_t per)
 {
-    const int64_t per = G == 1 ? (int64_t(kWG / 64) << qs) : kWG / G;  // per group and sweep
     const int64_t b = (n + per - 1) / per;
     return int32_t(b < 1 ? 1 : (b > kIcpMaxBlocks ? kIcpMaxBlocks : b));
 }
@@ -1946,22 +1951,26 @@ hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, co
 }
 
 // Work-groups of `kernel` (kWG lanes) the current device holds at once:
-// CUs x resident groups per CU; cached per device and slot (0 on failure).
+// CUs x resident groups per CU (0 on failure; *cus_out = CUs when given);
+// cached per device and slot.
 template <typename K>
-static int64_t resident_groups(K kernel, int slot)
+static int64_t resident_groups(K kernel, int slot, int64_t *cus_out = nullptr)
 {
     static std::atomic<int64_t> cache[64][2];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     int64_t v = cache[dev][slot].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWG, 0) != hipSuccess)
-        return 0;
-    v = int64_t(cus) * per_cu;
-    cache[dev][slot].store(v, std::memory_order_relaxed);
-    return v;
+    if (v <= 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWG, 0) != hipSuccess ||
+            cus <= 0 || per_cu <= 0)
+            return 0;
+        v = (int64_t(cus) << 8) | per_cu;  // per_cu < 256
+        cache[dev][slot].store(v, std::memory_order_relaxed);
+    }
+    if (cus_out) *cus_out = v >> 8;
+    return (v >> 8) * (v & 0xFF);
 }
 
 // Spread the queries of a one-lane-per-query launch (spread_pos)?  Always for
@@ -1980,30 +1989,71 @@ static bool spread_wanted(K kernel, int slot, int64_t m, bool ordered)
     return res > 0 && groups <= kSpreadMaxRounds * res;
 }
 
-// Queries per wave (log2) of a one-lane-per-query launch of m queries: 32
-// for an unbounded search while 64 per wave would not fill one round of
-// resident work-groups (the launch lasts as long as its longest wave, and the
-// idle lanes shorten it by taking pending far subtrees, at no cost in
-// occupancy), else 64: on a full machine the extra lanes would only add
-// redundant subtree work, and under a distance bound few far subtrees are
-// pending to be taken (measured: 57 vs 52 us per Scene ICP iteration).
-template <typename K>
-static uint32_t wave_shift(K kernel, int slot, int64_t m, float bound2)
+// Queries per wave and work-groups of a one-lane-per-query launch of m
+// queries.  64 per wave (and as many groups as that takes) when 64 per wave
+// would fill more than one round of resident work-groups, or under a
+// distance bound: on a full machine extra idle lanes would only add redundant
+// subtree work, and under a bound few far subtrees are pending to be taken
+// (measured: 57 vs 52 us per Scene ICP iteration).  Otherwise the launch
+// lasts as long as its longest wave, and the idle lanes shorten it by taking
+// pending subtrees at no cost in occupancy: the launch gets c work-groups on
+// every CU (the fewest that leave at most `target` queries to a wave) and
+// q = ceil(m / waves) queries per wave.  Whole groups per CU give every SIMD
+// the same number of waves; with a remainder of groups, the CUs holding one
+// more run longer and set the launch time (Scene 100k: 782 groups of 32
+// queries per wave, 46.2 us; 768 groups of 33, 41.8 us; 1,024 of 25, 44.7 us;
+// 512 of 49, 42.9 us).  Small launches keep at least KDNN_Q_MIN queries per
+// wave and fewer groups.
+#ifndef KDNN_Q_MIN
+#define KDNN_Q_MIN 8
+#endif
+struct WavePlan {
+    uint32_t q;
+    int64_t blocks;
+};
+static WavePlan full_wave_plan(int64_t m)
 {
-    if (!(bound2 == INFINITY)) return kQsFull;
-    const int64_t groups = (m + kWG - 1) / kWG, res = resident_groups(kernel, slot);
-    return (res > 0 && groups <= res) ? kQsSmall : kQsFull;
+    constexpr int64_t per = int64_t(kWG / 64) * kQFull;
+    const int64_t b = (m + per - 1) / per;
+    return WavePlan{kQFull, b < 1 ? 1 : b};
+}
+template <typename K>
+static WavePlan wave_plan(K kernel, int slot, int64_t m, float bound2, int64_t target)
+{
+    constexpr int64_t wpg = kWG / 64;  // waves per group
+    WavePlan p = full_wave_plan(m);
+    if (!(bound2 == INFINITY)) return p;
+    int64_t cus = 0;
+    const int64_t res = resident_groups(kernel, slot, &cus);
+    if (res <= 0 || p.blocks > res) return p;
+    const int64_t per_cu = res / cus, tq = target;
+    int64_t c = (m + wpg * cus * tq - 1) / (wpg * cus * tq);
+    c = c < 1 ? 1 : (c > per_cu ? per_cu : c);
+    int64_t blocks = c * cus;
+    int64_t q = (m + wpg * blocks - 1) / (wpg * blocks);
+    if (q < KDNN_Q_MIN) {
+        blocks = (m + wpg * KDNN_Q_MIN - 1) / (wpg * KDNN_Q_MIN);
+        if (blocks < 1) blocks = 1;
+        q = (m + wpg * blocks - 1) / (wpg * blocks);
+    }
+    p.q = uint32_t(q);
+    p.blocks = blocks;
+    return p;
 }
 
 template <int G>
 static void launch_nn_g(NnArgs a, bool stats, float bound2, hipStream_t s)
 {
+    int64_t blocks = (a.m + kWG / G - 1) / (kWG / G);  // G lanes per query
     if (G == 1) {
         a.spread = spread_wanted(nn_kernel<1, false>, 0, a.m, a.perm != nullptr);
-        a.qs = stats ? kQsFull : wave_shift(nn_kernel<1, false>, 0, a.m, bound2);
+        // the instrumented kernel searches each query alone, 64 per wave
+        const WavePlan wp = stats ? full_wave_plan(a.m)
+                                  : wave_plan(nn_kernel<1, false>, 0, a.m, bound2,
+                                              KDNN_Q_TARGET_NN);
+        a.wq = wp.q;
+        blocks = wp.blocks;
     }
-    const int64_t per = G == 1 ? (int64_t(kWG / 64) << a.qs) : kWG / G;  // per group and sweep
-    int64_t blocks = (a.m + per - 1) / per;
     if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
     if (stats)
         nn_kernel<G, true><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
@@ -2163,7 +2213,8 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     a.d2 = d2;
     a.budget = sc.budget;
     a.spread = spread_wanted(icp_fused_kernel<1>, 1, n, perm != nullptr);
-    a.qs = wave_shift(icp_fused_kernel<1>, 1, n, bound2);
+    const WavePlan wp = wave_plan(icp_fused_kernel<1>, 1, n, bound2, KDNN_Q_TARGET_ICP);
+    a.wq = wp.q;
     // the timing events bracket the search kernel(s), not the reduction
     const hipEvent_t e0 = timing ? timing[0] : nullptr, e1 = timing ? timing[1] : nullptr;
     hipError_t e;
@@ -2184,7 +2235,9 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         reduce_partials_kernel<<<1, kWG, 0, s>>>(a.partials, tp.nb1, a.partials2, kPass2Blocks,
                                                  sums_out, nullptr, nullptr);
     } else {
-        const dim3 grid(uint32_t(icp_blocks(n, sc.lanes ? sc.lanes : 1, a.qs)));
+        const dim3 grid(uint32_t(sc.lanes > 1 ? icp_blocks(n, kWG / sc.lanes)
+                                              : (wp.blocks < kIcpMaxBlocks ? wp.blocks
+                                                                           : kIcpMaxBlocks)));
         void (*k)(IcpArgs);
         switch (sc.lanes) {
         case 2: k = icp_fused_kernel<2>; break;

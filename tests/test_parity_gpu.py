@@ -527,3 +527,38 @@ def _lib_flags():
 @functools.lru_cache(maxsize=None)
 def stress_oracle_tree():
     return oracle.KDTree(synth.stress().target, 8)
+
+
+@functools.lru_cache(maxsize=None)
+def shapes_target():
+    rng = np.random.Generator(np.random.PCG64(4242))
+    T = rng.uniform(-10, 10, size=(50_000, 3)).astype(np.float32)
+    return T, oracle.KDTree(T, 16)
+
+
+# Source sizes that reach each launch shape of the one-lane-per-point kernels:
+# a few points (fewer work-groups than CUs), one round with 1 to 5 groups per
+# CU and a non-power-of-two number of points per wave, the full machine, and
+# more than one round (64 points per wave, several sweeps).
+SHAPE_SIZES = [1, 5, 31, 257, 4097, 33_793, 50_001, 131_065, 163_841, 300_001, 330_001]
+
+
+@pytest.mark.parametrize("n", SHAPE_SIZES)
+def test_fused_kernel_launch_shapes(torch, kdnn, n):
+    T, otree = shapes_target()
+    rng = np.random.Generator(np.random.PCG64(n))
+    S = rng.uniform(-11, 11, size=(n, 3)).astype(np.float32)
+    R = synth.rotation_about(synth.random_unit(rng), 0.02)
+    t = np.array([0.1, -0.05, 0.02])
+    say("fused kernel launch shape, n", n)
+    oi, od, red = _pairs_oracle(T, S, R, t, otree)
+    tree = kdnn.Tree(T, 16)
+    src = dev(torch, S)
+    for f in (0, _lib_flags().KDNN_ICP_NO_SORT, _lib_flags().KDNN_ICP_SORT):
+        res = tree.correspond_reduce(src, R, t, return_pairs=True, flags=f)
+        assert_nn_equal(res["idx"], res["d2"], oi, od, f"n={n} flags {f}")
+        check_sums(res, red, bbox_diag(T), f"n={n} flags {f}")
+    q = dev(torch, oracle.transform(S, R, t))
+    for sort in (True, False):
+        idx, d2 = tree.query(q, sort=sort)
+        assert_nn_equal(idx, d2, oi, od, f"nn_query n={n} sort={sort}")
