@@ -4,6 +4,7 @@
 // host, repeat; §4.6 convergence rule).  No exception crosses the ABI.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstring>
@@ -169,11 +170,42 @@ kdnn_status check_reject(const kdnn_icp_reject *r, const char *where)
     return KDNN_OK;
 }
 
-// Enqueue the traversal order (per flags) and the fused kernel.
+// The word of the tree's pinned slot that the reduction sets to the sequence
+// number of the launch once its sums are there (the sums take words 0 .. 18).
+constexpr int kDoneWord = 31;
+
+// Wait until the reduction launched with sequence number seq has published its
+// sums in the tree's pinned slot: poll that word, and ask the stream every
+// ~20 us, so that a failed or finished stream ends the wait either way.
+hipError_t wait_sums(const kdnn_tree *t, uint64_t seq, hipStream_t s)
+{
+    const volatile uint64_t *w = reinterpret_cast<const volatile uint64_t *>(t->h_pinned + kDoneWord);
+    auto last = std::chrono::steady_clock::now();
+    for (;;) {
+        if (*w == seq) {
+            std::atomic_thread_fence(std::memory_order_acquire);
+            return hipSuccess;
+        }
+        const auto now = std::chrono::steady_clock::now();
+        if (now - last < std::chrono::microseconds(20)) continue;
+        last = now;
+        const hipError_t e = hipStreamQuery(s);
+        if (e == hipErrorNotReady) continue;
+        if (e != hipSuccess) return e;
+        if (*w == seq) {  // the stream is idle: the word must be there now
+            std::atomic_thread_fence(std::memory_order_acquire);
+            return hipSuccess;
+        }
+        return hipErrorLaunchFailure;
+    }
+}
+
+// Enqueue the traversal order (per flags) and the fused kernel.  done / seq:
+// the reduction's completion word (device address) and value, or null.
 kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, const double *R,
                         const double *t, double *sums_dev, int32_t *idx, float *d2,
                         uint32_t flags, const kdnn_icp_reject *rej, const IcpWorkspace &w,
-                        hipStream_t s)
+                        hipStream_t s, uint64_t *done = nullptr, uint64_t seq = 0)
 {
     const float bound2 = rej ? bound_of(rej->max_dist) : INFINITY;
     const bool keep = rej && rej->reject_k > 0.0;
@@ -190,7 +222,7 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
     }
     if (e != hipSuccess) return hip_fail(e, "icp: order launch");
     e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, schedule_of(flags),
-                         bound2, keep, s, g_timing.next());
+                         bound2, keep, s, g_timing.next(), done, seq);
     if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
     return KDNN_OK;
 }
@@ -325,8 +357,19 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         std::memcpy(&j, &ht.points[4 * size_t(k) + 3], 4);
         slot_of[j] = int32_t(k);
     }
+    // kNodePad empty records (box +inf / -inf) after the last slot: a search
+    // step one level above the leaves reads four records from 2i, the last
+    // two of which lie past the heap for the last node of that level.
+    constexpr size_t kNodePad = 2;
+    const size_t node_pad_bytes = kNodePad * kNodeWords * sizeof(float);
+    std::vector<float> node_pad(kNodePad * kNodeWords, 0.0f);
+    for (size_t k = 0; k < kNodePad; ++k)
+        for (int ax = 0; ax < 3; ++ax) {
+            node_pad[k * kNodeWords + ax] = INFINITY;
+            node_pad[k * kNodeWords + 3 + ax] = -INFINITY;
+        }
     const size_t ob = size_t(n) * sizeof(int32_t);
-    if ((e = hipMalloc(&t->d_nodes, nb)) != hipSuccess ||
+    if ((e = hipMalloc(&t->d_nodes, nb + node_pad_bytes)) != hipSuccess ||
         (e = hipMalloc(&t->d_points, pb + pad_bytes)) != hipSuccess ||
         (e = hipMalloc(&t->d_slot_of, ob)) != hipSuccess) {
         free_tree(t);
@@ -337,6 +380,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         free_tree(t);
         return fail(KDNN_ENOMEM, std::string("kdtree_build: hipHostMalloc: ") + hipGetErrorString(e));
     }
+    std::memset(t->h_pinned, 0, 256);  // completion word 0: no launch yet
     // The fused kernel of the synchronous ICP calls writes its sums straight
     // into this slot (no separate copy launch per iteration).
     if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&t->d_pinned), t->h_pinned, 0)) !=
@@ -345,6 +389,8 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         return hip_fail(e, "kdtree_build: hipHostGetDevicePointer");
     }
     if ((e = hipMemcpy(t->d_nodes, ht.nodes.data(), nb, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(static_cast<char *>(t->d_nodes) + nb, node_pad.data(), node_pad_bytes,
+                       hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(static_cast<char *>(t->d_points) + pb, pad.data(), pad_bytes,
                        hipMemcpyHostToDevice)) != hipSuccess ||
@@ -382,7 +428,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     }
     I.build_ms = build_ms;
     I.upload_ms = upload_ms;
-    I.device_bytes = int64_t(nb + pb + pad_bytes + ob);
+    I.device_bytes = int64_t(nb + node_pad_bytes + pb + pad_bytes + ob);
     int l2 = 0;
     if ((e = hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, t->device)) != hipSuccess) {
         free_tree(t);
@@ -627,11 +673,12 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
             std::memcpy(Rt_hist + 12 * k + 9, t, sizeof t);
         }
         const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
+        const uint64_t seq = ++mt->seq;
         st = icp_enqueue(tree, src_dev, n, R, t, mt->d_pinned, nullptr, nullptr, f, reject, w,
-                         stream);
+                         stream, reinterpret_cast<uint64_t *>(mt->d_pinned + kDoneWord), seq);
         if (st != KDNN_OK) return st;
-        hipError_t e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return hip_fail(e, "icp_align: synchronize");
+        hipError_t e = wait_sums(mt, seq, stream);
+        if (e != hipSuccess) return hip_fail(e, "icp_align: wait for the sums");
         kdnn_icp_sums sums;
         to_sums(mt->h_pinned, tree->dev.center, &sums);
         if (E_hist) E_hist[k] = sums.sum_d2;
@@ -664,6 +711,9 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
         }
         prev_mse = mse;
     }
+    // the loop waited for the sums only; leave the stream idle, as documented
+    const hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "icp_align: synchronize");
     return KDNN_OK;
     KDNN_GUARD_END
 }

@@ -122,12 +122,14 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
                             const double *t, hipStream_t s);
 // Correspondence search + per-work-group partials, then the one-group
 // reduction into sums_out.  timing: null, or two events the search
-// kernel(s) stamp with their start and end.
+// kernel(s) stamp with their start and end.  done: null, or a word the
+// reduction sets to seq (system-scope release) once the sums are written.
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
                             float bound2, bool keep_matches, hipStream_t s,
-                            const hipEvent_t *timing = nullptr);
+                            const hipEvent_t *timing = nullptr, uint64_t *done = nullptr,
+                            uint64_t seq = 0);
 // One stable LSD radix pass (8-bit digit at `shift`) of (key, value) pairs;
 // hist: 256 x radix_tiles(m) words, totals: 256 words.
 int32_t radix_tiles(int64_t m);
@@ -192,7 +194,9 @@ struct kdnn_tree {
     void *d_points = nullptr;
     void *d_slot_of = nullptr;
     kdnn_tree_info info{};
-    double *h_pinned = nullptr;  // host readback slot for the ICP sums
+    double *h_pinned = nullptr;  // host readback slot for the ICP sums (32 doubles;
+                                 // the last word: completion sequence number)
+    uint64_t seq = 0;            // last sequence number handed to the reduction
     double *d_pinned = nullptr;  // the same slot as the device addresses it
     bool auto_sort = false;      // nn_query orders queries unless told otherwise
     bool auto_sort_icp = false;  // the ICP entry points order the source unless told otherwise
