@@ -99,6 +99,7 @@ void free_tree(kdnn_tree *t)
     int cur = -1;
     if (hipGetDevice(&cur) == hipSuccess && cur != t->device) (void)hipSetDevice(t->device);
     if (t->d_nodes) (void)hipFree(t->d_nodes);
+    if (t->d_boxes) (void)hipFree(t->d_boxes);
     if (t->d_points) (void)hipFree(t->d_points);
     if (t->d_slot_of) (void)hipFree(t->d_slot_of);
     if (t->h_pinned) (void)hipHostFree(t->h_pinned);
@@ -357,19 +358,16 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         std::memcpy(&j, &ht.points[4 * size_t(k) + 3], 4);
         slot_of[j] = int32_t(k);
     }
-    // kNodePad empty records (box +inf / -inf) after the last slot: a search
-    // step one level above the leaves reads four records from 2i, the last
-    // two of which lie past the heap for the last node of that level.
-    constexpr size_t kNodePad = 2;
-    const size_t node_pad_bytes = kNodePad * kNodeWords * sizeof(float);
-    std::vector<float> node_pad(kNodePad * kNodeWords, 0.0f);
-    for (size_t k = 0; k < kNodePad; ++k)
-        for (int ax = 0; ax < 3; ++ax) {
-            node_pad[k * kNodeWords + ax] = INFINITY;
-            node_pad[k * kNodeWords + 3 + ax] = -INFINITY;
-        }
+    // The boxes alone, 24 bytes per node slot, so that the two children of
+    // node i are one 48-byte run (three 16-byte loads) for the search.
+    const size_t slots = ht.nodes.size() / kNodeWords;
+    std::vector<float> boxes(6 * slots);
+    for (size_t r = 0; r < slots; ++r)
+        std::memcpy(&boxes[6 * r], &ht.nodes[r * kNodeWords], 6 * sizeof(float));
+    const size_t bb = boxes.size() * sizeof(float);
     const size_t ob = size_t(n) * sizeof(int32_t);
-    if ((e = hipMalloc(&t->d_nodes, nb + node_pad_bytes)) != hipSuccess ||
+    if ((e = hipMalloc(&t->d_nodes, nb)) != hipSuccess ||
+        (e = hipMalloc(&t->d_boxes, bb)) != hipSuccess ||
         (e = hipMalloc(&t->d_points, pb + pad_bytes)) != hipSuccess ||
         (e = hipMalloc(&t->d_slot_of, ob)) != hipSuccess) {
         free_tree(t);
@@ -389,8 +387,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         return hip_fail(e, "kdtree_build: hipHostGetDevicePointer");
     }
     if ((e = hipMemcpy(t->d_nodes, ht.nodes.data(), nb, hipMemcpyHostToDevice)) != hipSuccess ||
-        (e = hipMemcpy(static_cast<char *>(t->d_nodes) + nb, node_pad.data(), node_pad_bytes,
-                       hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(t->d_boxes, boxes.data(), bb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(static_cast<char *>(t->d_points) + pb, pad.data(), pad_bytes,
                        hipMemcpyHostToDevice)) != hipSuccess ||
@@ -402,6 +399,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
 
     DeviceTree &d = t->dev;
     d.nodes = t->d_nodes;
+    d.boxes = t->d_boxes;
     d.points = t->d_points;
     d.slot_of = t->d_slot_of;
     d.first_leaf = uint32_t(1) << ht.depth;
@@ -428,7 +426,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     }
     I.build_ms = build_ms;
     I.upload_ms = upload_ms;
-    I.device_bytes = int64_t(nb + node_pad_bytes + pb + pad_bytes + ob);
+    I.device_bytes = int64_t(nb + bb + pb + pad_bytes + ob);
     int l2 = 0;
     if ((e = hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, t->device)) != hipSuccess) {
         free_tree(t);

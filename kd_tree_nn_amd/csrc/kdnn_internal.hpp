@@ -56,6 +56,7 @@ kdnn_status procrustes_from_sums(const kdnn_icp_sums &s, double R[9], double t[3
 
 struct DeviceTree {
     const void *nodes = nullptr;   // float4 array, 2 per node slot
+    const void *boxes = nullptr;   // 6 floats per node slot: lo.xyz, hi.xyz (pairs 48 B)
     const void *points = nullptr;  // float4 array, 1 per point
     const void *slot_of = nullptr; // n int32: leaf-order slot of each original index
     uint32_t first_leaf = 1;       // 2^D
@@ -191,6 +192,7 @@ struct kdnn_tree {
     int device = 0;
     kdnn::DeviceTree dev;
     void *d_nodes = nullptr;
+    void *d_boxes = nullptr;
     void *d_points = nullptr;
     void *d_slot_of = nullptr;
     kdnn_tree_info info{};

@@ -137,6 +137,7 @@ struct Best {
 
 struct TreeView {
     const float4 *__restrict__ nodes;
+    const float4 *__restrict__ boxes;     // children of i: boxes[3i .. 3i+2] (48 B)
     const float4 *__restrict__ pts;
     const int32_t *__restrict__ slot_of;  // original index -> leaf-order slot
     uint32_t first_leaf;  // 2^D
@@ -625,81 +626,6 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
     }
 }
 
-// One search step from internal node i at depth d.  With d + 2 <= D it covers
-// two levels: it loads the records of the four grandchildren 4i .. 4i+3 (one
-// aligned 128-byte line) and skips the children's own records.  A child's
-// bound is the smaller of its two grandchildren's box bounds: every point of
-// the child lies in one of them, so that is a valid lower bound, never looser
-// than the child's own box.  The nearer child's nearer grandchild is
-// entered; the farther child stays pending at depth d + 1 and the other
-// grandchild at depth d + 2, each with its bound -- the same one-per-depth
-// pending state as a step per level, reached in one dependent load instead
-// of two, for the same record bytes (two one-level steps read 2 + 2 records).
-// One level above the leaves (d = D - 1) the step covers one level: it reads
-// the same four-record shape from 2i (the children of i and of i + 1; the
-// node array carries two empty records past its end for the last i) and
-// uses the first two.  Both cases run the same instructions, so lanes of a
-// wave at different depths do not split into two code paths.
-#ifndef KDNN_QUAD
-#define KDNN_QUAD 0
-#endif
-template <bool STATS>
-__device__ __forceinline__ void quad_step(const TreeView &t, WaveTask &w, float *lbs)
-{
-    const uint32_t i = w.i;
-    const uint32_t d = 31u - uint32_t(__clz(int(i)));
-    const bool two = d + 2u <= uint32_t(t.depth);
-    const float4 *g = t.nodes + (two ? 8 * i : 4 * i);
-    const float4 A0 = g[0], B0 = g[1], A1 = g[2], B1 = g[3];
-    const float4 A2 = g[4], B2 = g[5], A3 = g[6], B3 = g[7];
-    if (STATS) w.cn += two ? 4 : 2;
-    const float l0 = box_lb(w.qx, w.qy, w.qz, A0, B0);
-    const float l1 = box_lb(w.qx, w.qy, w.qz, A1, B1);
-    const float l2 = box_lb(w.qx, w.qy, w.qz, A2, B2);
-    const float l3 = box_lb(w.qx, w.qy, w.qz, A3, B3);
-    const float c0 = two ? fminf(l0, l1) : l0, c1 = two ? fminf(l2, l3) : l1;
-    const bool sc = c1 < c0;                 // nearer child: 2i + sc
-    const float cn = sc ? c1 : c0, cf = sc ? c0 : c1;
-    const float ga = sc ? l2 : l0, gb = sc ? l3 : l1;
-    const bool sg = gb < ga;                 // nearer grandchild within it
-    const float go = sg ? ga : gb;
-    const float best = key_dist(w.key);
-    if (enters(cn, best)) {
-        lbs[d * kWG] = cf;
-        uint32_t pend = enters(cf, best) ? (w.pend | (1u << d)) : (w.pend & ~(1u << d));
-        if (two) {
-            lbs[(d + 1) * kWG] = go;
-            pend = enters(go, best) ? (pend | (2u << d)) : (pend & ~(2u << d));
-        }
-        w.pend = pend;
-        w.i = two ? 4 * i + (sc ? 2u : 0u) + (sg ? 1u : 0u) : 2 * i + (sc ? 1u : 0u);
-    } else {
-        w.i = pair_next(i, w.pend, lbs, best);
-    }
-}
-
-// Top levels of the tree in LDS: the node records 0 .. kTopRecs - 1 (depths
-// 0 .. KDNN_TOP_LEVELS - 1; every descent starts through them) are copied into
-// each work-group's LDS once per launch, and a step whose child pair lies
-// there reads LDS instead of issuing vector-memory loads.
-#ifndef KDNN_TOP_LEVELS
-#define KDNN_TOP_LEVELS 0
-#endif
-constexpr uint32_t kTopRecs = KDNN_TOP_LEVELS ? (1u << KDNN_TOP_LEVELS) : 1u;
-__device__ __forceinline__ uint32_t top_records(const TreeView &t)
-{
-    if (!KDNN_TOP_LEVELS) return 0u;
-    return kTopRecs < 2u * t.first_leaf ? kTopRecs : 2u * t.first_leaf;
-}
-// All lanes of the work-group: copy the records, then a barrier.
-__device__ __forceinline__ void stage_top(const TreeView &t, float4 *top)
-{
-    if (!KDNN_TOP_LEVELS) return;
-    const uint32_t n4 = 2u * top_records(t);
-    for (uint32_t r = threadIdx.x; r < n4; r += kWG) top[r] = t.nodes[r];
-    __syncthreads();
-}
-
 // All lanes of the wave must call this together.  okey / ocn / ocp: the
 // work-group's LDS arrays [kWG], slot threadIdx.x = this lane's own query.
 // On return okey[threadIdx.x] holds the answer key of this lane's query (the
@@ -711,9 +637,8 @@ template <bool STATS, bool BALANCE = true>
 __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
                                             float oqz, uint64_t init, float *lbs,
                                             unsigned long long *okey, uint32_t *ocn,
-                                            uint32_t *ocp, const float4 *top = nullptr)
+                                            uint32_t *ocp)
 {
-    const uint32_t top_recs = top ? top_records(t) : 0u;
     okey[threadIdx.x] = init;
     if (STATS) {
         ocn[threadIdx.x] = 0u;
@@ -739,22 +664,16 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
         // Phase 1: internal nodes, as in the single-lane pair search; lanes
         // that run out of work take some over on every pass.
         while (__ballot(w.i < t.first_leaf) != 0) {
-            if (KDNN_QUAD && w.i < t.first_leaf) {
-                quad_step<STATS>(t, w, lbs);
-            } else if (w.i < t.first_leaf) {
+            if (w.i < t.first_leaf) {
+                // the two children's boxes: one 48-byte run, three loads
                 const uint32_t i = w.i;
-                float4 A0, B0, A1, B1;
-                if (2 * i + 1 < top_recs) {
-                    A0 = top[4 * i];
-                    B0 = top[4 * i + 1];
-                    A1 = top[4 * i + 2];
-                    B1 = top[4 * i + 3];
-                } else {
-                    A0 = t.nodes[4 * i];
-                    B0 = t.nodes[4 * i + 1];
-                    A1 = t.nodes[4 * i + 2];
-                    B1 = t.nodes[4 * i + 3];
-                }
+                const float4 P0 = t.boxes[3 * i];
+                const float4 P1 = t.boxes[3 * i + 1];
+                const float4 P2 = t.boxes[3 * i + 2];
+                const float4 A0 = P0;
+                const float4 B0 = make_float4(P1.x, P1.y, 0.0f, 0.0f);
+                const float4 A1 = make_float4(P1.z, P1.w, P2.x, P2.y);
+                const float4 B1 = make_float4(P2.z, P2.w, 0.0f, 0.0f);
                 if (STATS) w.cn += 2;
                 const float l0 = box_lb(w.qx, w.qy, w.qz, A0, B0);
                 const float l1 = box_lb(w.qx, w.qy, w.qz, A1, B1);
@@ -846,8 +765,6 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
         __shared__ float lbs[kDevMaxDepth * kWG];
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t ocn[STATS ? kWG : 1], ocp[STATS ? kWG : 1];
-        __shared__ float4 top[2 * kTopRecs];
-        stage_top(a.tree, top);
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         const uint32_t wq = a.wq;
         const int64_t QB = int64_t(kWG / 64) * wq;
@@ -861,7 +778,7 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             const float qz = own ? a.q[3 * i + 2] : 0.0f;
             // the instrumented kernel counts the single-lane search of each query
             wave_search<STATS, !STATS>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
-                                       ocn, ocp, top);
+                                       ocn, ocp);
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
@@ -1285,8 +1202,6 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         // across the next search.
         __shared__ float lbs[kDevMaxDepth * kWG];
         __shared__ unsigned long long okey[kWG];
-        __shared__ float4 top[2 * kTopRecs];
-        stage_top(a.tree, top);
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         if (lane == 63) {
 #pragma unroll
@@ -1305,7 +1220,7 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
                 icp_query(a, i, X, Y, Z, qx, qy, qz);
             }
             wave_search<false>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, nullptr,
-                               nullptr, top);
+                               nullptr);
             double acc[kS];
 #pragma unroll
             for (int c = 0; c < kS; ++c) acc[c] = 0.0;
@@ -1991,6 +1906,7 @@ static TreeView tree_view(const DeviceTree &t)
 {
     TreeView v;
     v.nodes = static_cast<const float4 *>(t.nodes);
+    v.boxes = static_cast<const float4 *>(t.boxes);
     v.slot_of = static_cast<const int32_t *>(t.slot_of);
     v.pts = static_cast<const float4 *>(t.points);
     v.first_leaf = t.first_leaf;
