@@ -1175,16 +1175,19 @@ __global__ __launch_bounds__(WG) void reduce_partials_kernel(const double *p1, i
     }
 }
 
+#ifndef KDNN_RED_WG
+#define KDNN_RED_WG 512
+#endif
 static void launch_reduce_partials(const double *p1, int32_t n1, const double *p2, int32_t n2,
                                    double *out, const double *stat, double *stat_out,
                                    uint64_t *done, uint64_t seq, hipStream_t s)
 {
-    if (n1 + n2 <= kWG)
+    if (n1 + n2 <= kWG || KDNN_RED_WG == kWG)
         reduce_partials_kernel<kWG><<<1, kWG, 0, s>>>(p1, n1, p2, n2, out, stat, stat_out, done,
                                                       seq);
     else
-        reduce_partials_kernel<1024><<<1, 1024, 0, s>>>(p1, n1, p2, n2, out, stat, stat_out, done,
-                                                        seq);
+        reduce_partials_kernel<KDNN_RED_WG><<<1, KDNN_RED_WG, 0, s>>>(p1, n1, p2, n2, out, stat,
+                                                                      stat_out, done, seq);
 }
 
 // Single pass, one kernel: transform, search (balanced wave search for G = 1,
