@@ -464,12 +464,18 @@ def main():
         pts_tot.append(int(cp.sum()))
     nodes_avg = float(np.mean(nodes_tot)) / n
     pts_avg = float(np.mean(pts_tot)) / n
-    n_blocks = min((n + 255) // 256, 4096)
-    # node records + leaf points + the source point (+ its slot in the order)
-    per_query = 32 * nodes_avg + 16 * pts_avg + 12 + (4 if info["auto_sort_icp"] else 0)
-    bytes_launch = n * per_query + n_blocks * 17 * 8          # + the partials it writes
+    # per source point: the box of every node record the search reads (24 B),
+    # every leaf point scanned (16 B: x, y, z, original index), the source point
+    # (12 B), its matched target point and that point's slot (16 + 4 B), and its
+    # slot in the traversal order when ordered (4 B).  The 136 B of partial sums
+    # each work-group writes are left out (< 0.1%).
+    per_query = (24 * nodes_avg + 16 * pts_avg + 12 + 20
+                 + (4 if info["auto_sort_icp"] else 0))
+    bytes_launch = n * per_query
     achieved = bytes_launch / (kern_avg_ms * 1e-3) / 1e9
-    descent_lb = 32 * (info["depth"] + 1) + 16 * (n / 2 ** info["depth"]) + 16
+    # one descent to a leaf and nothing else: the root box, both children's
+    # boxes at each of D levels, one leaf's points, the source and its match
+    descent_lb = 24 * (2 * info["depth"] + 1) + 16 * (n / 2 ** info["depth"]) + 32
 
     # ------------------------------------------------------ standalone nn_query
     def time_query(tr, q, sort, reps=100, warm=10):
