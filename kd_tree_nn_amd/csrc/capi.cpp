@@ -175,12 +175,11 @@ kdnn_status check_reject(const kdnn_icp_reject *r, const char *where)
 // number of the launch once its sums are there (the sums take words 0 .. 18).
 constexpr int kDoneWord = 31;
 
-// Wait until the reduction launched with sequence number seq has published its
-// sums in the tree's pinned slot: poll that word, and ask the stream every
-// ~20 us, so that a failed or finished stream ends the wait either way.
-hipError_t wait_sums(const kdnn_tree *t, uint64_t seq, hipStream_t s)
+// Wait until a reduction launched with sequence number seq has published its
+// sums, i.e. set the pinned word w to seq: poll that word, and ask the stream
+// every ~20 us, so that a failed or finished stream ends the wait either way.
+hipError_t wait_word(const volatile uint64_t *w, uint64_t seq, hipStream_t s)
 {
-    const volatile uint64_t *w = reinterpret_cast<const volatile uint64_t *>(t->h_pinned + kDoneWord);
     auto last = std::chrono::steady_clock::now();
     for (;;) {
         if (*w == seq) {
@@ -199,6 +198,12 @@ hipError_t wait_sums(const kdnn_tree *t, uint64_t seq, hipStream_t s)
         }
         return hipErrorLaunchFailure;
     }
+}
+
+// The same for the tree's own pinned slot.
+hipError_t wait_sums(const kdnn_tree *t, uint64_t seq, hipStream_t s)
+{
+    return wait_word(reinterpret_cast<const volatile uint64_t *>(t->h_pinned + kDoneWord), seq, s);
 }
 
 // Enqueue the traversal order (per flags) and the fused kernel.  done / seq:
@@ -686,11 +691,13 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
         if (st != KDNN_OK) return fail(st, "icp_align: iteration " + std::to_string(k) + ": " + err);
         if (reject_k > 0.0) {
             // residual rejection under the first solve, then solve again
+            const uint64_t rseq = ++mt->seq;
             e = launch_icp_reject(tree->dev, src_dev, n, Rn, tn, reject_k * reject_k, w,
-                                  mt->d_pinned, nullptr, nullptr, stream);
+                                  mt->d_pinned, nullptr, nullptr, stream,
+                                  reinterpret_cast<uint64_t *>(mt->d_pinned + kDoneWord), rseq);
             if (e != hipSuccess) return hip_fail(e, "icp_align: rejection launch");
-            if ((e = hipStreamSynchronize(stream)) != hipSuccess)
-                return hip_fail(e, "icp_align: synchronize");
+            if ((e = wait_sums(mt, rseq, stream)) != hipSuccess)
+                return hip_fail(e, "icp_align: wait for the kept sums");
             kdnn_icp_sums kept;
             to_sums(mt->h_pinned, tree->dev.center, &kept);
             st = procrustes_from_sums(kept, Rn, tn, err);
@@ -839,17 +846,30 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         total += batch_groups(n[p]);
     }
     // host slot the kernels write the sums into
+    // (on every return the stream is drained first: launches of the current
+    // iteration may still be writing into the buffer)
     struct Pinned {
         double *h = nullptr;
-        ~Pinned() { if (h) (void)hipHostFree(h); }
+        hipStream_t s = nullptr;
+        ~Pinned()
+        {
+            if (h) {
+                (void)hipStreamSynchronize(s);
+                (void)hipHostFree(h);
+            }
+        }
     } pin;
-    if ((e = hipHostMalloc(reinterpret_cast<void **>(&pin.h),
-                           size_t(KDNN_SUMS_DOUBLES) * 8 * size_t(B), hipHostMallocDefault)) !=
-        hipSuccess)
+    pin.s = stream;
+    // B x 17 sums, then one completion word per pair
+    const size_t pin_words = size_t(KDNN_SUMS_DOUBLES + 1) * size_t(B);
+    if ((e = hipHostMalloc(reinterpret_cast<void **>(&pin.h), pin_words * 8,
+                           hipHostMallocDefault)) != hipSuccess)
         return fail(KDNN_ENOMEM, std::string("icp_align_batch: hipHostMalloc: ") + hipGetErrorString(e));
+    std::memset(pin.h, 0, pin_words * 8);
     double *d_sums = nullptr;
     if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&d_sums), pin.h, 0)) != hipSuccess)
         return hip_fail(e, "icp_align_batch: hipHostGetDevicePointer");
+    const size_t done0 = size_t(KDNN_SUMS_DOUBLES) * size_t(B);
 
     const float bound2 = reject ? bound_of(reject->max_dist) : INFINITY;
     std::vector<char> done(B, 0);
@@ -868,13 +888,17 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
                 const int32_t p = active[c];
                 jobs.push_back(BatchJob{&trees[p]->dev, src_dev[p], n[p], &R[9 * size_t(p)],
                                         &t[3 * size_t(p)], part[p],
-                                        d_sums + size_t(KDNN_SUMS_DOUBLES) * p});
+                                        d_sums + size_t(KDNN_SUMS_DOUBLES) * p,
+                                        reinterpret_cast<uint64_t *>(d_sums + done0 + p)});
             }
-            e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream);
+            e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream,
+                                 uint64_t(k) + 1);
             if (e != hipSuccess) return hip_fail(e, "icp_align_batch: launch");
         }
-        if ((e = hipStreamSynchronize(stream)) != hipSuccess)
-            return hip_fail(e, "icp_align_batch: synchronize");
+        for (const int32_t p : active)
+            if ((e = wait_word(reinterpret_cast<const volatile uint64_t *>(pin.h + done0 + p),
+                               uint64_t(k) + 1, stream)) != hipSuccess)
+                return hip_fail(e, "icp_align_batch: wait for the sums");
         for (const int32_t p : active) {
             kdnn_icp_sums sums;
             to_sums(pin.h + size_t(KDNN_SUMS_DOUBLES) * p, trees[p]->dev.center, &sums);
@@ -900,6 +924,10 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         }
     }
     copy_out();
+    // the loop waited for the sums only; leave the stream idle (and the pinned
+    // buffer unused by the device) before returning
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+        return hip_fail(e, "icp_align_batch: synchronize");
     if (any_failed) return fail(KDNN_EDEGENERATE, "icp_align_batch: a pair degenerated (status_out)");
     return KDNN_OK;
     KDNN_GUARD_END

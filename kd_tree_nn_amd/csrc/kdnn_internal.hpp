@@ -172,18 +172,20 @@ struct BatchJob {
     const double *t;  // [3]
     int32_t part;     // first partial column
     double *sums;     // [KDNN_SUMS_DOUBLES] out (device-visible)
+    uint64_t *done;   // null, or a device-visible word the reduction sets to seq
 };
 int batch_max_pairs();
 int32_t batch_groups(int64_t n);  // work-groups (partial columns) of an n-point pair
 size_t icp_batch_ws_bytes(int32_t B, const int64_t *n);
 hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void *ws, int32_t total,
-                            hipStream_t s);
+                            hipStream_t s, uint64_t seq = 0);
 
 // Residual rejection of the pairs the last fused launch stored (keep_matches):
 // sums of the pairs with r^2 <= kk * mean r^2 under (R, t).
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
                              const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,
-                             double *stat_out, uint8_t *kept, hipStream_t s);
+                             double *stat_out, uint8_t *kept, hipStream_t s,
+                             uint64_t *done = nullptr, uint64_t seq = 0);
 
 }  // namespace kdnn
 

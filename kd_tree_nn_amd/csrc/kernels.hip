@@ -1395,6 +1395,7 @@ struct BatchPair {
     int32_t nb;       // work-groups of this pair: ceil(n / kWG)
     int32_t part;     // first partial column of this pair
     double *sums;     // [kS] out
+    uint64_t *done;   // null, or a word set to the launch's sequence number after the sums
 };
 
 struct BatchArgs {
@@ -1403,6 +1404,7 @@ struct BatchArgs {
     int32_t total;    // partial columns (stride of one component)
     uint64_t init;    // bound key
     double *partials; // [kS][total]
+    uint64_t seq;     // value stored into each pair's done word
 };
 
 __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
@@ -1465,6 +1467,12 @@ __global__ __launch_bounds__(kWG) void batch_reduce_kernel(BatchArgs a)
         for (int c = 0; c < kS; ++c) acc[c] += a.partials[int64_t(c) * a.total + P.part + g];
     }
     block_sum(acc, red, P.sums, 1);
+    if (P.done) {  // sums visible at system scope first (polled from the host)
+        if (threadIdx.x < kS) __threadfence_system();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(P.done, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
 }
 
 // ------------------------------------------- residual rejection (3 sigma)
@@ -2290,7 +2298,8 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
 
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
                              const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,
-                             double *stat_out, uint8_t *kept, hipStream_t s)
+                             double *stat_out, uint8_t *kept, hipStream_t s, uint64_t *done,
+                             uint64_t seq)
 {
     RejArgs a{};
     a.tree = tree_view(t);
@@ -2312,7 +2321,7 @@ hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, c
     icp_residual_kernel<<<dim3(uint32_t(nb)), kWG, 0, s>>>(a);
     residual_stat_kernel<<<1, kWG, 0, s>>>(a.partials, nb, kk, a.stat);
     icp_reject_kernel<<<dim3(uint32_t(nb)), kWG, 0, s>>>(a);
-    launch_reduce_partials(a.partials, nb, nullptr, 0, sums_out, a.stat, stat_out, nullptr, 0, s);
+    launch_reduce_partials(a.partials, nb, nullptr, 0, sums_out, a.stat, stat_out, done, seq, s);
     return hipGetLastError();
 }
 
@@ -2328,9 +2337,10 @@ size_t icp_batch_ws_bytes(int32_t B, const int64_t *n)
 }
 
 hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void *ws, int32_t total,
-                            hipStream_t s)
+                            hipStream_t s, uint64_t seq)
 {
     BatchArgs a{};
+    a.seq = seq;
     a.B = B;
     a.total = total;
     a.init = host_bound_key(bound2);
@@ -2350,6 +2360,7 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
         P.nb = batch_groups(J.n);
         P.part = J.part;
         P.sums = J.sums;
+        P.done = J.done;
         const int kx = (kNumXcd - p + B - 1) / B;
         const int64_t per_xcd = (P.nb + kx - 1) / kx;
         slots = per_xcd > slots ? per_xcd : slots;
