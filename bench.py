@@ -39,9 +39,17 @@ COPY_MIB = 512
 
 
 def kernel_source_hash():
+    """SHA-256 (first 16 hex digits) of the kernel source's code: comments and
+    whitespace are dropped first, so an edited comment does not invalidate a
+    counter summary taken on the same code."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)   # block comments
+    src = re.sub(r"//[^\n]*", " ", src)                 # line comments
+    code = " ".join(src.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def committed_traffic():
@@ -94,7 +102,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     out = [f"# rocprofv3 kernel statistics: bench.py on the Scene 100k x 100k ICP workload",
            f"# command: {TRACE_CMD}",
            f"# device: {agent(trace_dir)}",
-           f"# kernels.hip sha256[:16]: {kernel_source_hash()}",
+           f"# kernels.hip code sha256[:16] (comments, whitespace dropped): {kernel_source_hash()}",
            "",
            f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}"]
     for r in stats[:14]:
@@ -187,7 +195,7 @@ def summarize_counters(root):
     out = ["# rocprofv3 counters of icp_fused_kernel<1>, Scene 100k x 100k, mean per dispatch",
            "# three passes, each: timeout -s KILL 120 rocprofv3 --pmc <set> --output-format csv "
            "-d gpurun_out/pmc_<name> -o pmc -- python3 -u bench.py --profile-pass",
-           f"# kernels.hip sha256[:16]: {kernel_source_hash()}", ""]
+           f"# kernels.hip code sha256[:16] (comments, whitespace dropped): {kernel_source_hash()}", ""]
     for name, cs in PMC_SETS.items():
         out.append(f"# set {name}: {cs}")
     out.append("")

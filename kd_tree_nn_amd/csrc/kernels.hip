@@ -62,16 +62,16 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb)
 // of a wave balance their searches among themselves, which only helps when a
 // wave mixes easy and hard queries; hard queries (sparse regions, points far
 // from the target) sit close together in space, hence in a Morton order or a
-// scan order, and 64 of them in one wave leave no lane idle to help: that
+// scan order, and a wave full of them leaves no lane idle to help: that
 // wave runs long.  So the kernels deal the positions of the order to lanes
-// through a bijection that spreads every wave's 64 queries evenly over the
-// segment of the order its XCD works on.  In each sweep of nb * kWG slots
-// the logical blocks of XCD x (xcd_remap) cover one contiguous segment
+// through a bijection that spreads every wave's q queries evenly over the
+// segment of the order its XCD works on.  In each sweep of nb * (kWG / 64) q
+// slots the logical blocks of XCD x (xcd_remap) cover one contiguous segment
 // [s0, s0 + L), so every XCD still works on one run of the order (one region
 // of space for a Morton order: L2 locality).  Inside the segment (W =
-// ceil(L / 64) waves, the last one d = 64 W - L lanes short), lane l of the
-// segment's wave w takes position s0 + start(l) + w, where start(l) = l W -
-// max(0, l - (64 - d)) lays the 64 lanes' rows end to end.
+// ceil(L / q) waves, the last one d = q W - L queries short), query lane l of
+// the segment's wave w takes position s0 + start(l) + w, where start(l) =
+// l W - max(0, l - (q - d)) lays the q lanes' rows end to end.
 __device__ __forceinline__ int64_t spread_in(int64_t j, int64_t L, uint32_t q)
 {
     const int Q = int(q);
@@ -477,8 +477,9 @@ __device__ __forceinline__ void nn_search_group(const TreeView &t, float qx, flo
 
 // ------------------------------------------------ pair-load search (one lane)
 //
-// The default single-lane search.  Entering an internal node loads the
-// records of both its children together (one aligned 64-byte line); their
+// The single-lane search of the default schedule.  Entering an internal node
+// loads the boxes of both its children together (one 48-byte run of the box
+// array, three 16-byte loads); their
 // box bounds set the visiting order (smaller bound first) and tell at once
 // whether the other child can be dropped -- for good, since the best
 // distance only shrinks.  The other child's bound is kept per path level in
@@ -509,7 +510,7 @@ __device__ __forceinline__ uint32_t pair_next(uint32_t i, uint32_t &pend, const 
 
 // --------------------------------------- in-wave load balancing of the search
 //
-// A wave's 64 queries need very different amounts of work, and a wave lives
+// A wave's queries need very different amounts of work, and a wave lives
 // as long as its busiest lane.  Here every lane owns one query but works on a
 // task: its own query, or a subtree of another lane's query taken over when
 // it has nothing left to do.  After each round of leaf scans the idle lanes
