@@ -209,6 +209,46 @@ def summarize_counters(root):
     print("\n".join(out))
 
 
+def roofline_micro(torch, kdnn, work_bytes, n, nodes_avg, pts_avg, kern_ms):
+    """The library's micro-benchmarks at three working-set sizes: the fused
+    kernel's own (box array + points + index map: one XCD's L2), 64 MiB (the
+    Infinity Cache) and 512 MiB (HBM).  Random-gather GB/s for records of 16 B
+    (a point), 48 B (a child-pair box load) and 256 B (a leaf chunk), 2^20
+    lanes x 16 records, best of three seeds; dependent-load latency per hop
+    for 64 lanes chasing a random cycle of 64-byte records.  Then the fused
+    kernel's floor at its own level: its box-pair, leaf and per-point bytes
+    each at the L2 rate for that record shape."""
+    sizes = {"l2_working_set": int(work_bytes), "infinity_cache": 64 << 20, "hbm": 512 << 20}
+    lanes, rounds = 1 << 20, 16
+    out = {}
+    for lvl, size in sizes.items():
+        size -= size % 4096
+        buf = torch.empty(size // 4, dtype=torch.int32, device="cuda")
+        e = {"mib": round(size / 2 ** 20, 2)}
+        for words in (1, 3, 16):
+            kdnn.gather_bench(buf, words, lanes, rounds)
+            ms = min(kdnn.gather_bench(buf, words, lanes, rounds, seed=s_) for s_ in (1, 2, 3))
+            e[f"gather_gbs_{16 * words}B"] = round(lanes * rounds * words * 16 / (ms * 1e-3) / 1e9, 1)
+        nrec = size // 64
+        perm = torch.randperm(nrec, device="cuda", dtype=torch.int64)
+        nxt = torch.zeros(nrec * 16, dtype=torch.int32, device="cuda")
+        nxt[perm * 16] = torch.roll(perm, -1).to(torch.int32)
+        steps = 4000
+        kdnn.chase_bench(nxt, 1, 200)
+        e["latency_ns"] = round(kdnn.chase_bench(nxt, 1, steps) * 1e6 / steps, 1)
+        out[lvl] = e
+        del buf, perm, nxt
+    l2 = out["l2_working_set"]
+    t_min = n * (24 * nodes_avg / l2["gather_gbs_48B"] + 16 * pts_avg / l2["gather_gbs_256B"]
+                 + 32 / l2["gather_gbs_16B"]) / 1e9
+    out["fused_kernel_at_l2"] = {
+        "floor_us": round(t_min * 1e6, 2), "measured_us": round(kern_ms * 1e3, 2),
+        "frac": round(t_min / (kern_ms * 1e-3), 4),
+        "note": "floor = box-pair bytes at the 48 B rate + leaf bytes at the 256 B rate + "
+                "source/match bytes at the 16 B rate, all for this working set"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -533,6 +573,11 @@ def main():
                                 build_ms=round(tw.info["build_ms"], 1))
             del tw, qw
         log("other workloads:", other)
+    micro = None
+    if not args.headline_only:
+        work = 24 * 2 ** (info["depth"] + 1) + 16 * (len(p.target) + 16) + 4 * len(p.target)
+        micro = roofline_micro(torch, kdnn, work, n, nodes_avg, pts_avg, kern_avg_ms)
+        log("roofline micro-benchmarks:", micro)
     traffic, traffic_src = committed_traffic()
 
     result = {
@@ -600,6 +645,7 @@ def main():
             "tree_device_bytes": info["device_bytes"], "l2_bytes": info["l2_bytes"],
             "note": "the tree fits one XCD's L2: algorithmic gather bytes vs HBM peak; "
                     "traffic = HBM bytes the counters saw per launch",
+            "measured_levels": micro,
         },
     }
 

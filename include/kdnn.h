@@ -430,6 +430,35 @@ const char *kdnn_last_error(void);
 kdnn_status kdnn_timing_begin(int32_t cap);
 kdnn_status kdnn_timing_end(float *ms_out, int32_t cap_out, int32_t *count_out);
 
+/* Roofline micro-benchmarks, a measurement aid: the ceilings of the memory
+ * level a working set of a given size lives in (L2, Infinity Cache, HBM) for
+ * the access shapes of the search.  Not used by any search.
+ *
+ * kdnn_gather_bench: `lanes` lanes (a positive multiple of 256) each read
+ * `rounds` records (a positive multiple of 4) at pseudo-random indices in
+ * [0, n_records), four at a time; a record is `words` consecutive 16-byte
+ * words (1: one point; 3: a child-pair box load; 16: a leaf chunk).
+ *   buf_dev  : n_records * words * 16 bytes of device memory, 16-byte aligned,
+ *              any contents; read only.
+ *   sink_dev : one device word the kernel may write (keeps its loads alive).
+ *   seed     : varies the index stream.
+ *   ms_out   : host; kernel time measured with events on stream (waits).
+ * Useful bytes per launch: lanes * rounds * words * 16.
+ *
+ * kdnn_chase_bench: `waves` waves of 64 lanes each follow a chain of `steps`
+ * dependent loads: record i (64 bytes) holds the index of the next record in
+ * its first uint32; an index >= n_records is read as n_records - 1.
+ *   next_dev : n_records * 64 bytes, 64-byte aligned (e.g. a random cyclic
+ *              permutation written by the caller).
+ *   ms_out   : host; kernel time (waits).  Latency per hop = ms / steps.
+ * Errors (both): EINVAL (arguments out of range, null or misaligned
+ * pointers), EDEVICE. */
+kdnn_status kdnn_gather_bench(const void *buf_dev, int64_t n_records, int32_t words, int64_t lanes,
+                              int32_t rounds, uint32_t seed, uint32_t *sink_dev, float *ms_out,
+                              hipStream_t stream);
+kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_t waves,
+                             int32_t steps, uint32_t *sink_dev, float *ms_out, hipStream_t stream);
+
 /* KDNN_VERSION of the built library. */
 int32_t kdnn_version(void);
 

@@ -25,7 +25,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["Tree", "transform", "procrustes", "build_host", "layout", "sums_to_dict",
-           "icp_batch", "icp_batch_workspace", "voxel_downsample", "KdnnError", "version"]
+           "icp_batch", "icp_batch_workspace", "voxel_downsample", "KdnnError", "version",
+           "gather_bench", "chase_bench"]
 
 
 def _torch():
@@ -401,6 +402,40 @@ def timing_end() -> np.ndarray:
     _lib.check(_lib.lib().kdnn_timing_end(ms.ctypes.data_as(_lib.c_fp),
                                           KDNN_TIMING_MAX, ctypes.byref(cnt)), "kdnn_timing_end")
     return ms[:cnt.value].copy()
+
+
+def gather_bench(buf, words: int, lanes: int, rounds: int, seed: int = 1, stream=None) -> float:
+    """Random-gather micro-benchmark (kdnn_gather_bench): `lanes` lanes each read
+    `rounds` records of `words` 16-byte words at pseudo-random indices of the
+    device buffer `buf` (its bytes are taken as n_records * words * 16).
+    Returns the kernel time in ms; useful bytes = lanes * rounds * words * 16."""
+    torch = _torch()
+    if not (hasattr(buf, "is_cuda") and buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    n_rec = nbytes // (16 * int(words))
+    sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    ms = ctypes.c_float()
+    _lib.check(_lib.lib().kdnn_gather_bench(_ptr(buf), n_rec, int(words), int(lanes), int(rounds),
+                                            int(seed) & 0xFFFFFFFF, _ptr(sink), ctypes.byref(ms),
+                                            _stream(stream)), "kdnn_gather_bench")
+    return float(ms.value)
+
+
+def chase_bench(next_idx, waves: int, steps: int, stream=None) -> float:
+    """Dependent-load micro-benchmark (kdnn_chase_bench).  `next_idx`: a device
+    int32 tensor of n_records * 16 words (64-byte records) whose word 16 k holds
+    the record after record k.  Returns the kernel time in ms (ms / steps per hop)."""
+    torch = _torch()
+    if not (hasattr(next_idx, "is_cuda") and next_idx.is_cuda and next_idx.is_contiguous()
+            and next_idx.dtype == torch.int32 and next_idx.numel() % 16 == 0):
+        raise ValueError("next_idx must be a contiguous int32 device tensor of 16-word records")
+    sink = torch.zeros(1, dtype=torch.int32, device=next_idx.device)
+    ms = ctypes.c_float()
+    _lib.check(_lib.lib().kdnn_chase_bench(_ptr(next_idx), next_idx.numel() // 16, int(waves),
+                                           int(steps), _ptr(sink), ctypes.byref(ms),
+                                           _stream(stream)), "kdnn_chase_bench")
+    return float(ms.value)
 
 
 def layout(n: int, leaf_size: int = 16, max_depth: int = 0, round_robin: bool = False):

@@ -96,6 +96,8 @@ SIGNATURES = {
     "voxel_downsample": (c_i32, [c_vp, c_i64, ctypes.c_double, c_vp, ctypes.POINTER(c_i64), c_vp,
                                  c_vp, c_sz, c_vp]),
     "kdnn_timing_begin": (c_i32, [c_i32]),
+    "kdnn_gather_bench": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_i32, c_u32, c_vp, c_fp, c_vp]),
+    "kdnn_chase_bench": (c_i32, [c_vp, c_i64, c_i32, c_i32, c_vp, c_fp, c_vp]),
     "kdnn_timing_end": (c_i32, [c_fp, c_i32, ctypes.POINTER(c_i32)]),
     "kdnn_last_error": (ctypes.c_char_p, []),
     "kdnn_version": (c_i32, []),

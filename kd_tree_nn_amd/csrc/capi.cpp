@@ -300,6 +300,43 @@ kdnn_status kdnn_timing_end(float *ms_out, int32_t cap_out, int32_t *count_out)
     KDNN_GUARD_END
 }
 
+kdnn_status kdnn_gather_bench(const void *buf_dev, int64_t n_records, int32_t words, int64_t lanes,
+                              int32_t rounds, uint32_t seed, uint32_t *sink_dev, float *ms_out,
+                              hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    if (!buf_dev || !aligned(buf_dev, 16) || !sink_dev || !aligned(sink_dev, 4) || !ms_out)
+        return fail(KDNN_EINVAL, "kdnn_gather_bench: null or misaligned pointer");
+    if (!(words == 1 || words == 3 || words == 16))
+        return fail(KDNN_EINVAL, "kdnn_gather_bench: words must be 1, 3 or 16");
+    if (n_records < 1 || n_records > int64_t(UINT32_MAX))
+        return fail(KDNN_EINVAL, "kdnn_gather_bench: n_records out of range");
+    if (lanes < 256 || lanes % 256 != 0 || lanes / 256 > int64_t(INT32_MAX))
+        return fail(KDNN_EINVAL, "kdnn_gather_bench: lanes must be a positive multiple of 256");
+    if (rounds < 4 || rounds % 4 != 0)
+        return fail(KDNN_EINVAL, "kdnn_gather_bench: rounds must be a positive multiple of 4");
+    if (!run_gather_bench(buf_dev, n_records, words, lanes, rounds, seed, sink_dev, ms_out, stream))
+        return hip_fail(hipGetLastError(), "kdnn_gather_bench");
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
+kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_t waves,
+                             int32_t steps, uint32_t *sink_dev, float *ms_out, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    if (!next_dev || !aligned(next_dev, 64) || !sink_dev || !aligned(sink_dev, 4) || !ms_out)
+        return fail(KDNN_EINVAL, "kdnn_chase_bench: null or misaligned pointer");
+    if (n_records < 1 || n_records > int64_t(UINT32_MAX))
+        return fail(KDNN_EINVAL, "kdnn_chase_bench: n_records out of range");
+    if (waves < 1 || steps < 1)
+        return fail(KDNN_EINVAL, "kdnn_chase_bench: waves and steps must be >= 1");
+    if (!run_chase_bench(next_dev, n_records, waves, steps, sink_dev, ms_out, stream))
+        return hip_fail(hipGetLastError(), "kdnn_chase_bench");
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
 int32_t kdnn_version(void) { return KDNN_VERSION; }
 
 kdnn_status kdtree_layout(int64_t n, const kdnn_build_params *params, int32_t *depth_out,

@@ -49,6 +49,13 @@ kdnn_status tree_layout(int64_t n, const kdnn_build_params *p, int32_t *depth, i
 kdnn_status build_host_tree(const float *xyz, int64_t n, const kdnn_build_params *p, HostTree &out,
                             std::string &err);
 
+// Roofline micro-benchmarks (roofline.hip); each times one launch with events
+// on s.  false on a HIP error.
+bool run_gather_bench(const void *buf, int64_t n_records, int32_t words, int64_t lanes,
+                      int32_t rounds, uint32_t seed, uint32_t *sink, float *ms, hipStream_t s);
+bool run_chase_bench(const uint32_t *next, int64_t n_records, int32_t waves, int32_t steps,
+                     uint32_t *sink, float *ms, hipStream_t s);
+
 // Rigid solve from the 17 correspondence sums.
 kdnn_status procrustes_from_sums(const kdnn_icp_sums &s, double R[9], double t[3], std::string &err);
 
