@@ -540,6 +540,9 @@ constexpr uint32_t kNoOwner = 0xFFFFFFFFu;
 #ifndef KDNN_LEAF_QUORUM_FULL
 #define KDNN_LEAF_QUORUM_FULL 48
 #endif
+#ifndef KDNN_XFER_LDS
+#define KDNN_XFER_LDS 1
+#endif
 #ifndef KDNN_P1_MIN_IDLE
 #define KDNN_P1_MIN_IDLE 16
 #endif
@@ -589,8 +592,9 @@ __device__ __forceinline__ void task_finish(WaveTask &w, unsigned long long *oke
 
 // Hand-over round: idle lanes take the shallowest pending subtree of busy
 // lanes, paired by rank.  Every lane of the wave must call it together.
+// xfer: this wave's 64-entry LDS table (donor rank -> donor lane).
 __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
-                                              const unsigned long long *okey,
+                                              const unsigned long long *okey, uint32_t *xfer,
                                               uint32_t min_idle = 1u)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -619,7 +623,14 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
     }
     const uint32_t trank = uint32_t(__popcll(idle_m & below));
     const bool takes = idle && trank < np;
+#if KDNN_XFER_LDS
+    // the donor of rank r publishes its lane in slot r; the taker of rank r reads it
+    if (gives) xfer[__popcll(don_m & below)] = lane;
+    __builtin_amdgcn_wave_barrier();
+    const int src = takes ? int(xfer[trank]) : int(lane);
+#else
     const int src = takes ? int(nth_set_bit(don_m, trank)) : int(lane);
+#endif
     const uint32_t tv = uint32_t(__shfl(int(gv), src, 64));
     const float tlb = __shfl(glb, src, 64);
     const float tqx = __shfl(w.qx, src, 64);
@@ -648,7 +659,7 @@ template <bool STATS, bool BALANCE = true>
 __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
                                             float oqz, uint64_t init, float *lbs,
                                             unsigned long long *okey, uint32_t *ocn,
-                                            uint32_t *ocp, uint32_t quorum = 64u)
+                                            uint32_t *ocp, uint32_t *xfer, uint32_t quorum = 64u)
 {
     okey[threadIdx.x] = init;
     if (STATS) {
@@ -708,7 +719,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                 }
             }
             task_finish<STATS>(w, okey, ocn, ocp);
-            if (BALANCE && KDNN_P1_HANDOVER) task_handover(w, lbs, okey, KDNN_P1_MIN_IDLE);
+            if (BALANCE && KDNN_P1_HANDOVER) task_handover(w, lbs, okey, xfer, KDNN_P1_MIN_IDLE);
         }
         // Phase 2: leaves, then share the improved best of the query.
         if (w.i != kDone && w.i >= t.first_leaf) {
@@ -739,7 +750,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
         }
         task_finish<STATS>(w, okey, ocn, ocp);
         if (__ballot(w.owner != kNoOwner) == 0) break;
-        if (BALANCE) task_handover(w, lbs, okey);
+        if (BALANCE) task_handover(w, lbs, okey, xfer);
     }
 }
 
@@ -783,6 +794,7 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
         __shared__ float lbs[kDevMaxDepth * kWG];
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t ocn[STATS ? kWG : 1], ocp[STATS ? kWG : 1];
+        __shared__ uint32_t xfer[kWG];
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         const uint32_t wq = a.wq;
         const int64_t QB = int64_t(kWG / 64) * wq;
@@ -796,7 +808,8 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             const float qz = own ? a.q[3 * i + 2] : 0.0f;
             // the instrumented kernel counts the single-lane search of each query
             wave_search<STATS, !STATS>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
-                                       ocn, ocp, wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u);
+                                       ocn, ocp, xfer + (threadIdx.x & ~63u),
+                                       wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u);
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
@@ -1223,6 +1236,7 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         // across the next search.
         __shared__ float lbs[kDevMaxDepth * kWG];
         __shared__ unsigned long long okey[kWG];
+        __shared__ uint32_t xfer[kWG];
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         if (lane == 63) {
 #pragma unroll
@@ -1241,7 +1255,8 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
                 icp_query(a, i, X, Y, Z, qx, qy, qz);
             }
             wave_search<false>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, nullptr,
-                               nullptr, wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u);
+                               nullptr, xfer + (threadIdx.x & ~63u),
+                               wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u);
             double acc[kS];
 #pragma unroll
             for (int c = 0; c < kS; ++c) acc[c] = 0.0;
@@ -1442,6 +1457,7 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     __shared__ unsigned long long okey[kWG];
+    __shared__ uint32_t xfer[kWG];
     const int64_t i = int64_t(j) * kWG + threadIdx.x;
     const bool own = i < P.n;
     double X = 0.0, Y = 0.0, Z = 0.0;
@@ -1455,7 +1471,7 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
         qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
     }
     wave_search<false>(P.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, nullptr, nullptr,
-                       KDNN_BATCH_QUORUM);
+                       xfer + (threadIdx.x & ~63u), KDNN_BATCH_QUORUM);
     if (own) {
         Best b;
         finish(okey[threadIdx.x], 0u, b);
