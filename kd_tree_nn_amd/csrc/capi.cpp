@@ -446,6 +446,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     d.slot_of = t->d_slot_of;
     d.first_leaf = uint32_t(1) << ht.depth;
     d.depth = ht.depth;
+    d.max_leaf = ht.max_leaf;
     d.n = n;
     for (int k = 0; k < 3; ++k) {
         d.box_lo[k] = ht.bbox_min[k];

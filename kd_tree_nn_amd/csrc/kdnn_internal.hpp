@@ -68,6 +68,7 @@ struct DeviceTree {
     const void *slot_of = nullptr; // n int32: leaf-order slot of each original index
     uint32_t first_leaf = 1;       // 2^D
     int32_t depth = 0;             // D
+    int32_t max_leaf = 0;          // points in the largest leaf
     int64_t n = 0;                 // target points
     float box_lo[3] = {0, 0, 0};   // target bbox (Morton normalisation)
     float box_inv[3] = {0, 0, 0};  // 1 / extent per axis (0 for a flat axis)

@@ -36,6 +36,7 @@ constexpr int kWG = KDNN_WG;                      // traversal work-group size
 #endif
 constexpr uint32_t kQFull = 64;
 constexpr int kLeafChunk = 16;                    // leaf points loaded per batch (one lane)
+constexpr int kLeafChunkSmall = 8;                // the same for trees whose leaves hold <= 8
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
 constexpr int kSortTile = kSortThreads * kSortItems;  // keys per radix tile
@@ -648,6 +649,24 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
     }
 }
 
+// The pending-bound array of a balanced-search work-group (one float per path
+// level and lane): a static array of kDevMaxDepth levels, or (DYN) dynamic LDS
+// of lbs_bytes(D) sized to the tree, which leaves room for more resident
+// groups where registers allow them (the 8-point leaf batches, the batched
+// kernel).  The 16-point kernels keep the static array: their occupancy is
+// set by registers, and they measured faster in that form.
+template <bool DYN>
+__device__ __forceinline__ float *lbs_array()
+{
+    if constexpr (DYN) {
+        extern __shared__ float lbs_dyn[];
+        return lbs_dyn;
+    } else {
+        __shared__ float lbs_static[kDevMaxDepth * kWG];
+        return lbs_static;
+    }
+}
+
 // All lanes of the wave must call this together.  okey / ocn / ocp: the
 // work-group's LDS arrays [kWG], slot threadIdx.x = this lane's own query.
 // On return okey[threadIdx.x] holds the answer key of this lane's query (the
@@ -655,7 +674,9 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
 // BALANCE == false: no hand-over, every lane searches its own query alone
 // (the plain single-lane pair search; its counts are the method's own work,
 // independent of which queries share a wave).
-template <bool STATS, bool BALANCE = true>
+// CH: leaf points loaded per batch (kLeafChunk, or kLeafChunkSmall for a tree
+// whose leaves hold at most that many: fewer registers, more resident waves).
+template <bool STATS, bool BALANCE = true, int CH = kLeafChunk>
 __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
                                             float oqz, uint64_t init, float *lbs,
                                             unsigned long long *okey, uint32_t *ocn,
@@ -729,11 +750,11 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
             uint64_t key = w.key;
             do {
                 const float4 *pc = t.pts + k0;
-                float4 p[kLeafChunk];
+                float4 p[CH];
 #pragma unroll
-                for (int c = 0; c < kLeafChunk; ++c) p[c] = pc[c];
+                for (int c = 0; c < CH; ++c) p[c] = pc[c];
 #pragma unroll
-                for (int c = 0; c < kLeafChunk; ++c) {
+                for (int c = 0; c < CH; ++c) {
                     const float dx = p[c].x - w.qx;
                     const float dy = p[c].y - w.qy;
                     const float dz = p[c].z - w.qz;
@@ -741,7 +762,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                     const uint64_t k = nn_key(dd, __float_as_uint(p[c].w));
                     key = k < key ? k : key;
                 }
-                k0 += kLeafChunk;
+                k0 += CH;
             } while (k0 < uint32_t(end));
             if (STATS) w.cp += uint32_t(end - begin);
             const uint64_t seen = atomicMin(&okey[w.owner], (unsigned long long)key);
@@ -784,14 +805,14 @@ __device__ __forceinline__ void search_query(const TreeView &t, float qx, float 
 // One query per lane (G = 1: the balanced wave search) or G lanes per query.
 // A block handles kWG / G queries per sweep; the loop bound is uniform over the
 // block so a wave's (or group's) lanes always stay together.
-template <int G, bool STATS>
+template <int G, bool STATS, int CH = kLeafChunk>
 __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
 {
     constexpr int QPB = kWG / G;
     const uint32_t nb = gridDim.x;
     const uint32_t blk = xcd_remap(blockIdx.x, nb);
     if constexpr (G == 1) {
-        __shared__ float lbs[kDevMaxDepth * kWG];
+        float *const lbs = lbs_array<CH == kLeafChunkSmall>();
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t ocn[STATS ? kWG : 1], ocp[STATS ? kWG : 1];
         __shared__ uint32_t xfer[kWG];
@@ -807,7 +828,7 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             const float qy = own ? a.q[3 * i + 1] : 0.0f;
             const float qz = own ? a.q[3 * i + 2] : 0.0f;
             // the instrumented kernel counts the single-lane search of each query
-            wave_search<STATS, !STATS>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
+            wave_search<STATS, !STATS, CH>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
                                        ocn, ocp, xfer + (threadIdx.x & ~63u),
                                        wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u);
             if (own) {
@@ -1223,7 +1244,7 @@ static void launch_reduce_partials(const double *p1, int32_t n1, const double *p
 
 // Single pass, one kernel: transform, search (balanced wave search for G = 1,
 // G lanes per point otherwise) and the fp64 reduction.
-template <int G>
+template <int G, int CH = kLeafChunk>
 __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
@@ -1234,7 +1255,7 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
         // Each sweep's pairs are summed over the wave at once and added to the
         // wave's row of red (lane 63), so no sums stay live in registers
         // across the next search.
-        __shared__ float lbs[kDevMaxDepth * kWG];
+        float *const lbs = lbs_array<CH == kLeafChunkSmall>();
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t xfer[kWG];
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -1254,8 +1275,8 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
                 double X, Y, Z;
                 icp_query(a, i, X, Y, Z, qx, qy, qz);
             }
-            wave_search<false>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, nullptr,
-                               nullptr, xfer + (threadIdx.x & ~63u),
+            wave_search<false, true, CH>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
+                                         nullptr, nullptr, xfer + (threadIdx.x & ~63u),
                                wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u);
             double acc[kS];
 #pragma unroll
@@ -1443,10 +1464,11 @@ struct BatchArgs {
 #ifndef KDNN_BATCH_QUORUM
 #define KDNN_BATCH_QUORUM KDNN_LEAF_QUORUM_FULL
 #endif
+template <int CH>
 __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
-    __shared__ float lbs[kDevMaxDepth * kWG];
+    float *const lbs = lbs_array<true>();
     const int x = int(blockIdx.x % uint32_t(kNumXcd));
     const int pi = x % a.B;
     const BatchPair &P = a.p[pi];
@@ -1470,8 +1492,9 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
         qy = rigid_row(P.R[3], P.R[4], P.R[5], P.t[1], X, Y, Z);
         qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
     }
-    wave_search<false>(P.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey, nullptr, nullptr,
-                       xfer + (threadIdx.x & ~63u), KDNN_BATCH_QUORUM);
+    wave_search<false, true, CH>(P.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
+                                 nullptr, nullptr, xfer + (threadIdx.x & ~63u),
+                                 KDNN_BATCH_QUORUM);
     if (own) {
         Best b;
         finish(okey[threadIdx.x], 0u, b);
@@ -2030,24 +2053,36 @@ hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, co
     return morton_order_impl(t, pts, m, R12, ws.sort, nullptr, perm, s);
 }
 
-// Work-groups of `kernel` (kWG lanes) the current device holds at once:
-// CUs x resident groups per CU (0 on failure; *cus_out = CUs when given);
-// cached per device and slot.
-template <typename K>
-static int64_t resident_groups(K kernel, int slot, int64_t *cus_out = nullptr)
+// Dynamic LDS of the balanced search kernels: the pending bound of every path
+// level of a depth-D tree, for each lane (D x 1 KB per work-group), so a
+// shallow tree leaves room for more resident work-groups.
+static size_t lbs_bytes(int32_t depth)
 {
-    static std::atomic<int64_t> cache[64][2];
+    return size_t(depth < 1 ? 1 : depth) * kWG * sizeof(float);
+}
+
+// Work-groups of `kernel` (kWG lanes, lbs_bytes(depth) of dynamic LDS) the
+// current device holds at once: CUs x resident groups per CU (0 on failure;
+// *cus_out = CUs when given); cached per device, slot and depth.
+template <typename K>
+static int64_t resident_groups(K kernel, int slot, int32_t depth, int64_t *cus_out = nullptr)
+{
+    // slots 2, 3: the 8-point kernels, with dynamic LDS
+    const size_t dyn = slot >= 2 ? lbs_bytes(depth) : 0;
+    static std::atomic<int64_t> cache[64][4][kDevMaxDepth + 1];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int64_t v = cache[dev][slot].load(std::memory_order_relaxed);
+    const int d = depth < 0 ? 0 : (depth > kDevMaxDepth ? kDevMaxDepth : depth);
+    int64_t v = cache[dev][slot][d].load(std::memory_order_relaxed);
     if (v <= 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWG, 0) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWG, dyn) !=
+                hipSuccess ||
             cus <= 0 || per_cu <= 0)
             return 0;
         v = (int64_t(cus) << 8) | per_cu;  // per_cu < 256
-        cache[dev][slot].store(v, std::memory_order_relaxed);
+        cache[dev][slot][d].store(v, std::memory_order_relaxed);
     }
     if (cus_out) *cus_out = v >> 8;
     return (v >> 8) * (v & 0xFF);
@@ -2062,10 +2097,10 @@ static int64_t resident_groups(K kernel, int slot, int64_t *cus_out = nullptr)
 // pays more.
 constexpr int64_t kSpreadMaxRounds = 3;
 template <typename K>
-static bool spread_wanted(K kernel, int slot, int64_t m, bool ordered)
+static bool spread_wanted(K kernel, int slot, int32_t depth, int64_t m, bool ordered)
 {
     if (!ordered) return true;
-    const int64_t groups = (m + kWG - 1) / kWG, res = resident_groups(kernel, slot);
+    const int64_t groups = (m + kWG - 1) / kWG, res = resident_groups(kernel, slot, depth);
     return res > 0 && groups <= kSpreadMaxRounds * res;
 }
 
@@ -2098,13 +2133,14 @@ static WavePlan full_wave_plan(int64_t m)
     return WavePlan{kQFull, b < 1 ? 1 : b};
 }
 template <typename K>
-static WavePlan wave_plan(K kernel, int slot, int64_t m, float bound2, int64_t target)
+static WavePlan wave_plan(K kernel, int slot, int32_t depth, int64_t m, float bound2,
+                          int64_t target)
 {
     constexpr int64_t wpg = kWG / 64;  // waves per group
     WavePlan p = full_wave_plan(m);
     if (!(bound2 == INFINITY)) return p;
     int64_t cus = 0;
-    const int64_t res = resident_groups(kernel, slot, &cus);
+    const int64_t res = resident_groups(kernel, slot, depth, &cus);
     if (res <= 0 || p.blocks > res) return p;
     const int64_t per_cu = res / cus, tq = target;
     int64_t c = (m + wpg * cus * tq - 1) / (wpg * cus * tq);
@@ -2121,24 +2157,27 @@ static WavePlan wave_plan(K kernel, int slot, int64_t m, float bound2, int64_t t
     return p;
 }
 
-template <int G>
+template <int G, int CH = kLeafChunk>
 static void launch_nn_g(NnArgs a, bool stats, float bound2, hipStream_t s)
 {
     int64_t blocks = (a.m + kWG / G - 1) / (kWG / G);  // G lanes per query
     if (G == 1) {
-        a.spread = spread_wanted(nn_kernel<1, false>, 0, a.m, a.perm != nullptr);
+        const int slot = CH == kLeafChunk ? 0 : 2;
+        a.spread = spread_wanted(nn_kernel<1, false, CH>, slot, a.tree.depth, a.m,
+                                 a.perm != nullptr);
         // the instrumented kernel searches each query alone, 64 per wave
         const WavePlan wp = stats ? full_wave_plan(a.m)
-                                  : wave_plan(nn_kernel<1, false>, 0, a.m, bound2,
-                                              KDNN_Q_TARGET_NN);
+                                  : wave_plan(nn_kernel<1, false, CH>, slot, a.tree.depth, a.m,
+                                              bound2, KDNN_Q_TARGET_NN);
         a.wq = wp.q;
         blocks = wp.blocks;
     }
     if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+    const size_t lds = G == 1 && CH == kLeafChunkSmall ? lbs_bytes(a.tree.depth) : 0;
     if (stats)
-        nn_kernel<G, true><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
+        nn_kernel<G, true, CH><<<dim3(uint32_t(blocks)), kWG, lds, s>>>(a);
     else
-        nn_kernel<G, false><<<dim3(uint32_t(blocks)), kWG, 0, s>>>(a);
+        nn_kernel<G, false, CH><<<dim3(uint32_t(blocks)), kWG, lds, s>>>(a);
 }
 
 // Persistent LDS launch shape for this device: one work-group per CU and
@@ -2231,7 +2270,12 @@ hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32
         case 4: launch_nn_g<4>(a, stats, bound2, s); break;
         case 8: launch_nn_g<8>(a, stats, bound2, s); break;
         case 16: launch_nn_g<16>(a, stats, bound2, s); break;
-        default: launch_nn_g<1>(a, stats, bound2, s); break;
+        default:
+            if (t.max_leaf <= kLeafChunkSmall)
+                launch_nn_g<1, kLeafChunkSmall>(a, stats, bound2, s);
+            else
+                launch_nn_g<1>(a, stats, bound2, s);
+            break;
         }
     }
     return hipGetLastError();
@@ -2292,8 +2336,10 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
     a.idx = idx;
     a.d2 = d2;
     a.budget = sc.budget;
-    a.spread = spread_wanted(icp_fused_kernel<1>, 1, n, perm != nullptr);
-    const WavePlan wp = wave_plan(icp_fused_kernel<1>, 1, n, bound2, KDNN_Q_TARGET_ICP);
+    const bool small = t.max_leaf <= kLeafChunkSmall;
+    void (*k1)(IcpArgs) = small ? icp_fused_kernel<1, kLeafChunkSmall> : icp_fused_kernel<1>;
+    a.spread = spread_wanted(k1, small ? 3 : 1, t.depth, n, perm != nullptr);
+    const WavePlan wp = wave_plan(k1, small ? 3 : 1, t.depth, n, bound2, KDNN_Q_TARGET_ICP);
     a.wq = wp.q;
     // the timing events bracket the search kernel(s), not the reduction
     const hipEvent_t e0 = timing ? timing[0] : nullptr, e1 = timing ? timing[1] : nullptr;
@@ -2324,9 +2370,10 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         case 4: k = icp_fused_kernel<4>; break;
         case 8: k = icp_fused_kernel<8>; break;
         case 16: k = icp_fused_kernel<16>; break;
-        default: k = icp_fused_kernel<1>; break;
+        default: k = k1; break;
         }
-        e = launch_k(k, grid, kWG, 0, s, e0, e1, a);
+        e = launch_k(k, grid, kWG, sc.lanes <= 1 && small ? lbs_bytes(t.depth) : 0, s, e0, e1,
+                     a);
         if (e != hipSuccess) return e;
         launch_reduce_partials(a.partials, int32_t(grid.x), nullptr, 0, sums_out, nullptr, nullptr,
                                done, seq, s);
@@ -2384,10 +2431,14 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
     a.init = host_bound_key(bound2);
     a.partials = static_cast<double *>(ws);
     int64_t slots = 0;
+    int32_t depth = 0;     // the deepest tree sets the launch's LDS
+    int32_t max_leaf = 0;  // the largest leaf, the leaf batch
     for (int32_t p = 0; p < B; ++p) {
         const BatchJob &J = jobs[p];
         BatchPair &P = a.p[p];
         P.tree = tree_view(*J.tree);
+        depth = J.tree->depth > depth ? J.tree->depth : depth;
+        max_leaf = J.tree->max_leaf > max_leaf ? J.tree->max_leaf : max_leaf;
         P.src = J.src;
         P.n = J.n;
         for (int k = 0; k < 9; ++k) P.R[k] = J.R[k];
@@ -2403,7 +2454,12 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
         const int64_t per_xcd = (P.nb + kx - 1) / kx;
         slots = per_xcd > slots ? per_xcd : slots;
     }
-    icp_batch_kernel<<<dim3(uint32_t(slots * kNumXcd)), kWG, 0, s>>>(a);
+    if (max_leaf <= kLeafChunkSmall)
+        icp_batch_kernel<kLeafChunkSmall><<<dim3(uint32_t(slots * kNumXcd)), kWG, lbs_bytes(depth),
+                                            s>>>(a);
+    else
+        icp_batch_kernel<kLeafChunk><<<dim3(uint32_t(slots * kNumXcd)), kWG, lbs_bytes(depth),
+                                       s>>>(a);
     batch_reduce_kernel<<<dim3(uint32_t(B)), kWG, 0, s>>>(a);
     return hipGetLastError();
 }
