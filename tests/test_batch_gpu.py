@@ -117,3 +117,15 @@ def test_batch_degenerate_pair_and_errors(torch, kdnn):
     assert args(0, ctypes.byref(_lib.IcpReject(1.0, 3.0)), ws.numel()) == _lib.KDNN_EINVAL
     assert args(0, None, 16) == _lib.KDNN_EINVAL                           # workspace too small
     assert args(0, None, ws.numel()) == _lib.KDNN_OK
+
+
+def test_batch_leaf8_trees(torch, kdnn):
+    """Trees whose leaves hold at most 8 points take the batched kernel's 8-point
+    leaf batches and depth-sized LDS; each pair must match its single-pair ICP."""
+    lp = lidar()[:3]
+    trees = [kdnn.Tree(p.target, 8) for p in lp]
+    assert all(tr.info["max_leaf"] <= 8 for tr in trees)
+    say("batch of 3 LiDAR pairs, leaf 8")
+    res = kdnn.icp_batch(trees, [dev(torch, p.source) for p in lp], max_iter=10)
+    for k, (p, tr, b) in enumerate(zip(lp, trees, res)):
+        _close_to_single(b, _single(kdnn, torch, tr, p.source, 10), f"leaf-8 pair {k}")
