@@ -1062,7 +1062,7 @@ __global__ __launch_bounds__(kWG) void nn_pass2_kernel(NnArgs a, TwoPass tp)
 // Per source point: q = fl32(R s + t) evaluated in fp64 with a fixed
 // association; nearest target point m; accumulate in fp64, shifted by c,
 //   (s-c), (m-c), (s-c)(m-c)^T, d2, 1.
-// Per lane -> wave (DPP scan, lane 63 keeps the total) -> work-group (waves
+// Per lane -> wave (reduce-scatter, one component per lane pair) -> work-group (waves
 // summed in order) -> per-group partials; reduce_partials_kernel then sums
 // the partials in a fixed order.  The result does not depend on scheduling.
 struct IcpArgs {
@@ -1095,46 +1095,101 @@ __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, doub
     return float(((r0 * x + r1 * y) + r2 * z) + tr);
 }
 
-// v + (v of the lane DPP control CTRL selects; +0 where there is none).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_add(double v)
+// ---- wave sums of the kS fp64 components: a reduce-scatter over the lanes
+//
+// Summing each of the kS components over the wave by its own log2(64)-step
+// butterfly moves every component through every step (~500 VALU instructions
+// per wave).  A reduce-scatter halves the number of values a lane carries at
+// each step: at a step, a lane pairs with a partner lane in the other half of
+// its group, keeps one of two components (its half decides which), receives
+// the partner's copy of that same component and adds it.  Steps: the upper
+// and lower 32 lanes (permlane32 swap), the odd and even rows of 16 lanes
+// (permlane16 swap), then within a row the mirror pairs l <-> 15 - l, the
+// half-row mirror pairs l <-> 7 - l, and lanes l <-> l ^ 2, l <-> l ^ 1 (DPP).
+// kS = 17 values -> 9 -> 5 -> 3 -> 2 -> 1: ~90 instructions.  Each output is
+// a fixed sum tree over the 64 lanes, the same in every run.
+
+// (a, b) -> (half of the lanes: a + partner's a, the rest: b + partner's b)
+// through a permlane swap; `tag` says which (0: a, 1: b) this lane now holds.
+template <bool ROWS16>
+__device__ __forceinline__ double swap_step(double a, double b, uint32_t &tag)
 {
-    const uint64_t b = uint64_t(__double_as_longlong(v));
-    const uint32_t lo = uint32_t(
-        __builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, ROW_MASK, 0xF, false));
-    const uint32_t hi = uint32_t(
-        __builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, ROW_MASK, 0xF, false));
-    return v + __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+    const uint64_t ba = uint64_t(__double_as_longlong(a)), bb = uint64_t(__double_as_longlong(b));
+    uint32_t alo = uint32_t(ba), ahi = uint32_t(ba >> 32), blo = uint32_t(bb), bhi = uint32_t(bb >> 32);
+    uint32_t ta = 0u, tb = 1u;
+    if constexpr (ROWS16) {
+        const auto l = __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
+        const auto h = __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
+        const auto t = __builtin_amdgcn_permlane16_swap(ta, tb, false, false);
+        alo = l[0]; blo = l[1]; ahi = h[0]; bhi = h[1]; ta = t[0];
+    } else {
+        const auto l = __builtin_amdgcn_permlane32_swap(alo, blo, false, false);
+        const auto h = __builtin_amdgcn_permlane32_swap(ahi, bhi, false, false);
+        const auto t = __builtin_amdgcn_permlane32_swap(ta, tb, false, false);
+        alo = l[0]; blo = l[1]; ahi = h[0]; bhi = h[1]; ta = t[0];
+    }
+    tag = ta;  // both registers now hold parts of the same component
+    return __longlong_as_double((long long)((uint64_t(ahi) << 32) | alo)) +
+           __longlong_as_double((long long)((uint64_t(bhi) << 32) | blo));
 }
 
-// Sum of v over the 64 lanes of a full wave, in lane 63: an inclusive scan by
-// DPP row shifts 1, 2, 4, 8 within rows of 16, then row broadcasts of lanes 15
-// and 31 -- register moves instead of LDS-crossbar shuffles, in a fixed order.
-__device__ __forceinline__ double wave_total(double v)
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov(double v)
 {
-    v = dpp_add<0x111, 0xF>(v);  // row_shr:1
-    v = dpp_add<0x112, 0xF>(v);  // row_shr:2
-    v = dpp_add<0x114, 0xF>(v);  // row_shr:4
-    v = dpp_add<0x118, 0xF>(v);  // row_shr:8
-    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
-    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
-    return v;
+    const uint64_t b = uint64_t(__double_as_longlong(v));
+    const uint32_t lo = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(b)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false));
+    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
+// Within-row step with a symmetric DPP pairing that crosses lane bit `hi`:
+// the lower lane keeps a (+ partner's a), the upper one b (+ partner's b).
+template <int CTRL>
+__device__ __forceinline__ double row_step(double a, double b, bool hi)
+{
+    const double send = hi ? a : b;
+    const double keep = hi ? b : a;
+    return keep + dpp_mov<CTRL>(send);
+}
+
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+constexpr int kDppXor2 = 0x4E, kDppXor1 = 0xB1;  // quad_perm [2,3,0,1], [1,0,3,2]
+
+// On return v = the sum over the 64 lanes of component c (the return value;
+// c >= kS: padding, no component).  Lanes l and l ^ 1 return the same c and
+// v.  Every lane of the wave must call it together.
+__device__ __forceinline__ int wave_scatter_sums(const double (&acc)[kS], double &v)
+{
+    static_assert(kS == 17, "the step sequence below is laid out for 17 components");
+    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t t32 = 0u, t16 = 0u;
+    double v1[9], v2[5], v3[3], v4[2];
+#pragma unroll
+    for (int j = 0; j < 9; ++j) v1[j] = swap_step<false>(acc[2 * j], 2 * j + 1 < kS ? acc[2 * j + 1] : 0.0, t32);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) v2[k] = swap_step<true>(v1[2 * k], 2 * k + 1 < 9 ? v1[2 * k + 1] : 0.0, t16);
+    const bool b3 = lane & 8u, b2 = lane & 4u, b1 = lane & 2u;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) v3[k] = row_step<kDppRowMirror>(v2[2 * k], 2 * k + 1 < 5 ? v2[2 * k + 1] : 0.0, b3);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) v4[k] = row_step<kDppRowHalfMirror>(v3[2 * k], 2 * k + 1 < 3 ? v3[2 * k + 1] : 0.0, b2);
+    const double v5 = row_step<kDppXor2>(v4[0], v4[1], b1);
+    v = v5 + dpp_mov<kDppXor1>(v5);
+    // v1[j] holds component 2j + t32, v2[k] = v1[2k + t16], v3[k] = v2[2k + b3], ...
+    return 16 * int(b1) + 8 * int(b2) + 4 * int(b3) + 2 * int(t16) + int(t32);
 }
 
 // Sum acc[] over a work-group of WG lanes (all active); thread c < kS gets
-// component c in out[c * out_stride] (fixed order: lanes by wave_total, then
-// waves in order).  acc[] is left holding partial sums.
+// component c in out[c * out_stride] (fixed order: lanes by wave_scatter_sums,
+// then waves in order).  acc[] is left holding partial sums.
 template <int WG>
 __device__ __forceinline__ void block_sum_n(double (&acc)[kS], double *red /* LDS [waves][kS] */,
                                             double *out, int64_t out_stride)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int c = 0; c < kS; ++c) acc[c] = wave_total(acc[c]);
-    if (lane == 63) {
-#pragma unroll
-        for (int c = 0; c < kS; ++c) red[w * kS + c] = acc[c];
-    }
+    double v;
+    const int cw = wave_scatter_sums(acc, v);
+    if (cw < kS && !(lane & 1)) red[w * kS + cw] = v;
     __syncthreads();
     if (threadIdx.x < kS) {
         double s = 0.0;
@@ -1244,8 +1299,14 @@ static void launch_reduce_partials(const double *p1, int32_t n1, const double *p
 
 // Single pass, one kernel: transform, search (balanced wave search for G = 1,
 // G lanes per point otherwise) and the fp64 reduction.
+// Registers: the reduce-scatter's 17 live sums would take the 16-point kernel
+// to 97 VGPRs (4 waves per SIMD); held to 5 waves, as the search alone allows.
+#ifndef KDNN_FUSED_WPE
+#define KDNN_FUSED_WPE 5
+#endif
 template <int G, int CH = kLeafChunk>
-__global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(KDNN_FUSED_WPE))) void
+icp_fused_kernel(IcpArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
     const uint32_t nb = gridDim.x;
@@ -1253,8 +1314,8 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
     if constexpr (G == 1) {
         // One lane owns each source point; the wave balances the searches.
         // Each sweep's pairs are summed over the wave at once and added to the
-        // wave's row of red (lane 63), so no sums stay live in registers
-        // across the next search.
+        // wave's row of red (by the lanes the reduce-scatter leaves a component
+        // in), so no sums stay live in registers across the next search.
         float *const lbs = lbs_array<CH == kLeafChunkSmall>();
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t xfer[kWG];
@@ -1288,12 +1349,9 @@ __global__ __launch_bounds__(kWG) void icp_fused_kernel(IcpArgs a)
                 const double X = a.src[3 * i], Y = a.src[3 * i + 1], Z = a.src[3 * i + 2];
                 icp_accumulate(a, i, X, Y, Z, b, acc);
             }
-#pragma unroll
-            for (int c = 0; c < kS; ++c) acc[c] = wave_total(acc[c]);
-            if (lane == 63) {
-#pragma unroll
-                for (int c = 0; c < kS; ++c) red[wv * kS + c] += acc[c];
-            }
+            double v;
+            const int cw = wave_scatter_sums(acc, v);
+            if (cw < kS && !(lane & 1)) red[wv * kS + cw] += v;
         }
         __syncthreads();
         if (threadIdx.x < kS) {
