@@ -251,6 +251,9 @@ kdnn_status transform_points(const float *in_dev, float *out_dev, int64_t n, con
                                    its traversal order instead of sorting again */
 #define KDNN_ICP_NO_SORT 2u     /* traverse source points in their given order */
 #define KDNN_ICP_SORT 4u        /* always traverse in Morton order of the transformed points */
+#define KDNN_ICP_HOST_LOOP 8u   /* icp_align only: solve each iteration on the host (a
+                                   readback of the sums per iteration) instead of keeping
+                                   the iterations on the device */
 /* Neither NO_SORT nor SORT: Morton order when the tree's node records and
  * points exceed the device's L2 cache (kdnn_tree_info.auto_sort_icp); the
  * order is computed once per registration. */
@@ -321,9 +324,14 @@ kdnn_status icp_reject_reduce(const kdnn_tree *tree, const float *src_dev, int64
                               kdnn_icp_sums *out_host, double *sigma2_out, uint8_t *kept_dev,
                               void *ws_dev, size_t ws_bytes, hipStream_t stream);
 
-/* Rigid solve from correspondence sums (article §2.1): centroids, H, its 3x3
- * SVD H = U S V^T, R = V diag(1, 1, d) U^T with d = sign det(V U^T) so that R
- * is a proper rotation, t = mu_m - R mu_s.  Host only, fp64.
+/* Rigid solve from correspondence sums (article §2.1): centroids, H, and the
+ * proper rotation R minimising sum |R (s - mu_s) - (m - mu_m)|^2 -- the
+ * article takes it from the SVD H = U S V^T as V diag(1, 1, d) U^T with
+ * d = sign det(V U^T); here from Horn's unit-quaternion form (the largest
+ * eigenvalue of a 4x4 symmetric matrix by Newton's method on its
+ * characteristic polynomial, the vector from the adjugate), with the SVD
+ * route taken when the two largest eigenvalues are close -- then
+ * t = mu_m - R mu_s.  Host, fp64; the device-side ICP loop runs the same code.
  * Errors: EINVAL (NULL), EDEGENERATE (n < 3 or rank(H) < 2; outputs unset). */
 kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_out);
 
@@ -344,6 +352,13 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  *                  n_k count them; with reject_k > 0 each iteration solves,
  *                  rejects by residual (icp_reject_reduce) and solves again.
  * The traversal order is computed once, from the source moved by (R0, t0).
+ * With one lane per query (no schedule flag or KDNN_LANES(1)), no reject_k,
+ * max_iter <= 512 and no KDNN_ICP_HOST_LOOP, the iterations stay on the
+ * device: each one's sums are reduced and solved (the same arithmetic as
+ * kdnn_procrustes) by a one-group kernel that leaves the next transform for
+ * the next search, so all iterations are enqueued at once (in chunks of 4
+ * when eps > 0, to stop soon after convergence) and the host waits once.
+ * Otherwise each iteration's sums come back to the host, which solves.
  * On EDEGENERATE the outputs hold the last good transform.
  * Errors: EINVAL, EDEVICE, EDEGENERATE. */
 kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, const double *R0_host,

@@ -263,9 +263,11 @@ class Tree:
 
     def icp(self, src, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
             workspace=None, stream=None, lanes=None, sort=None, budget=None,
-            top_lds: bool = False, max_dist=None, reject_k: float = 0.0) -> dict:
+            top_lds: bool = False, max_dist=None, reject_k: float = 0.0,
+            host_loop: bool = False) -> dict:
         """ICP registration of the source (device, original coordinates) onto the
-        tree; max_dist / reject_k: correspondence rejection (kdnn_icp_reject)."""
+        tree; max_dist / reject_k: correspondence rejection (kdnn_icp_reject);
+        host_loop: solve each iteration on the host (KDNN_ICP_HOST_LOOP)."""
         src = _dev_points(src, "src")
         n = src.shape[0]
         R0a = None if R0 is None else _mat(R0, (3, 3), "R0")
@@ -282,7 +284,8 @@ class Tree:
             R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
             E.ctypes.data_as(_lib.c_dp), Rt.ctypes.data_as(_lib.c_dp), ctypes.byref(it),
             _lib.sort_flag(sort, KDNN_ICP_SORT, KDNN_ICP_NO_SORT)
-            | _lib.lanes_flag(lanes, budget, top_lds), _reject(max_dist, reject_k),
+            | _lib.lanes_flag(lanes, budget, top_lds)
+            | (_lib.KDNN_ICP_HOST_LOOP if host_loop else 0), _reject(max_dist, reject_k),
             _ptr(ws), ws.numel(), _stream(stream)), "icp_align")
         k = it.value
         return {"R": R.reshape(3, 3), "t": t, "E": E[:k], "Rt_hist": Rt[:k], "iters": k}

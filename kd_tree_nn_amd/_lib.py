@@ -17,6 +17,7 @@ KDNN_QUERY_SORT = 2
 KDNN_ICP_REUSE_ORDER = 1
 KDNN_ICP_NO_SORT = 2
 KDNN_ICP_SORT = 4
+KDNN_ICP_HOST_LOOP = 8
 KDNN_SUMS_DOUBLES = 17
 KDNN_LANES_SHIFT = 8
 KDNN_BUDGET_SHIFT = 16

@@ -103,6 +103,7 @@ void free_tree(kdnn_tree *t)
     if (t->d_points) (void)hipFree(t->d_points);
     if (t->d_slot_of) (void)hipFree(t->d_slot_of);
     if (t->h_pinned) (void)hipHostFree(t->h_pinned);
+    if (t->h_loop) (void)hipHostFree(t->h_loop);
     if (cur >= 0 && cur != t->device) (void)hipSetDevice(cur);
     delete t;
 }
@@ -211,7 +212,8 @@ hipError_t wait_sums(const kdnn_tree *t, uint64_t seq, hipStream_t s)
 kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, const double *R,
                         const double *t, double *sums_dev, int32_t *idx, float *d2,
                         uint32_t flags, const kdnn_icp_reject *rej, const IcpWorkspace &w,
-                        hipStream_t s, uint64_t *done = nullptr, uint64_t seq = 0)
+                        hipStream_t s, uint64_t *done = nullptr, uint64_t seq = 0,
+                        const IcpLoop *loop = nullptr)
 {
     const float bound2 = rej ? bound_of(rej->max_dist) : INFINITY;
     const bool keep = rej && rej->reject_k > 0.0;
@@ -228,7 +230,7 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
     }
     if (e != hipSuccess) return hip_fail(e, "icp: order launch");
     e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, schedule_of(flags),
-                         bound2, keep, s, g_timing.next(), done, seq);
+                         bound2, keep, s, g_timing.next(), done, seq, loop);
     if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
     return KDNN_OK;
 }
@@ -247,6 +249,54 @@ kdnn_status icp_check(const kdnn_tree *tree, const float *src, int64_t n, const 
     if ((flags & KDNN_ICP_SORT) && (flags & KDNN_ICP_NO_SORT))
         return fail(KDNN_EINVAL, "icp: KDNN_ICP_SORT and KDNN_ICP_NO_SORT together");
     return check_ws(ws, ws_bytes, icp_ws_bytes(n));
+}
+
+// icp_align with the iterations kept on the device: the host enqueues the
+// initial state, then per iteration the fused kernel and the step kernel
+// (rigid solve, convergence rule, next transform on the device), and waits
+// once -- after every 4 iterations when eps > 0, so that a converged
+// registration stops soon.  The record the step kernels write into the tree's
+// pinned slot gives the outputs.  Caller holds the tree's ICP lock.
+kdnn_status icp_align_on_device(kdnn_tree *mt, const float *src_dev, int64_t n, const double *R,
+                                const double *t, int32_t max_iter, double eps, double *R_out,
+                                double *t_out, double *E_hist, double *Rt_hist,
+                                int32_t *iters_done, uint32_t flags, const kdnn_icp_reject *reject,
+                                const IcpWorkspace &w, hipStream_t stream)
+{
+    constexpr int32_t kChunk = 4;
+    hipError_t e = launch_icp_loop_init(w.loop, mt->d_loop, R, t, stream);
+    if (e != hipSuccess) return hip_fail(e, "icp_align: loop start");
+    IcpLoop L{w.loop, mt->d_loop, 0, eps};
+    const volatile IcpLoopOut *out = mt->h_loop;
+    for (int32_t k = 0; k < max_iter; ++k) {
+        L.iter = k;
+        const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
+        const kdnn_status st = icp_enqueue(mt, src_dev, n, R, t, nullptr, nullptr, nullptr, f,
+                                           reject, w, stream, nullptr, 0, &L);
+        if (st != KDNN_OK) return st;
+        if (eps > 0.0 && (k + 1) % kChunk == 0 && k + 1 < max_iter) {
+            if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+                return hip_fail(e, "icp_align: synchronize");
+            if (out->stopped) break;
+        }
+    }
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+        return hip_fail(e, "icp_align: synchronize");
+    const int32_t done = int32_t(out->iters);
+    const int32_t failed = int32_t(out->fail_iter);
+    const int32_t recorded = failed >= 0 ? failed + 1 : done;
+    for (int32_t k = 0; k < recorded && k < max_iter; ++k) {
+        if (E_hist) E_hist[k] = out->E[k];
+        if (Rt_hist)
+            for (int j = 0; j < 12; ++j) Rt_hist[12 * k + j] = out->rt_hist[k][j];
+    }
+    for (int j = 0; j < 9; ++j) R_out[j] = out->rt[j];
+    for (int j = 0; j < 3; ++j) t_out[j] = out->rt[9 + j];
+    if (iters_done) *iters_done = done;
+    if (failed >= 0)
+        return fail(KDNN_EDEGENERATE, "icp_align: iteration " + std::to_string(failed) + ": " +
+                                          rigid_status_text(int32_t(out->status)));
+    return KDNN_OK;
 }
 
 }  // namespace
@@ -424,6 +474,18 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     // The fused kernel of the synchronous ICP calls writes its sums straight
     // into this slot (no separate copy launch per iteration).
     if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&t->d_pinned), t->h_pinned, 0)) !=
+        hipSuccess) {
+        free_tree(t);
+        return hip_fail(e, "kdtree_build: hipHostGetDevicePointer");
+    }
+    // the record the device-side ICP loop writes (per-iteration E and transform)
+    if ((e = hipHostMalloc(reinterpret_cast<void **>(&t->h_loop), sizeof(kdnn::IcpLoopOut),
+                           hipHostMallocDefault)) != hipSuccess) {
+        free_tree(t);
+        return fail(KDNN_ENOMEM, std::string("kdtree_build: hipHostMalloc: ") + hipGetErrorString(e));
+    }
+    std::memset(static_cast<void *>(t->h_loop), 0, sizeof(kdnn::IcpLoopOut));
+    if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&t->d_loop), t->h_loop, 0)) !=
         hipSuccess) {
         free_tree(t);
         return hip_fail(e, "kdtree_build: hipHostGetDevicePointer");
@@ -691,8 +753,10 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     if (!R_out || !t_out) return fail(KDNN_EINVAL, "icp_align: null R_out or t_out");
     if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align: max_iter < 0");
     if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align: eps must be >= 0");
-    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_ICP_SORT | kSchedMask))
+    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_ICP_SORT | KDNN_ICP_HOST_LOOP | kSchedMask))
         return fail(KDNN_EINVAL, "icp_align: unknown flag");
+    const bool host_loop = (flags & KDNN_ICP_HOST_LOOP) != 0;
+    flags &= ~KDNN_ICP_HOST_LOOP;
     kdnn_status st = icp_check(tree, src_dev, n, R, t, flags, ws_dev, ws_bytes);
     if (st != KDNN_OK) return st;
     if ((st = check_reject(reject, "icp_align")) != KDNN_OK) return st;
@@ -706,6 +770,11 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
     std::lock_guard<std::mutex> lock(mt->icp_mu);
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
+    const Schedule sc = schedule_of(flags);
+    if (!host_loop && reject_k == 0.0 && sc.lanes <= 1 && !sc.top_lds && sc.budget == 0 &&
+        max_iter <= kLoopMaxIter)
+        return icp_align_on_device(mt, src_dev, n, R, t, max_iter, eps, R_out, t_out, E_hist,
+                                   Rt_hist, iters_done, flags, reject, w, stream);
     double prev_mse = 0.0;
     int small_steps = 0;
     for (int32_t k = 0; k < max_iter; ++k) {

@@ -58,6 +58,8 @@ bool run_chase_bench(const uint32_t *next, int64_t n_records, int32_t waves, int
 
 // Rigid solve from the 17 correspondence sums.
 kdnn_status procrustes_from_sums(const kdnn_icp_sums &s, double R[9], double t[3], std::string &err);
+// Message of a rigid_solve.hpp status code.
+const char *rigid_status_text(int32_t st);
 
 // ---------------------------------------------------------------- device side
 
@@ -93,6 +95,34 @@ struct QueryWorkspace {
 size_t query_ws_bytes(int64_t m);
 QueryWorkspace carve_query_workspace(void *ws, int64_t m);
 
+// ICP iterations kept on the device (icp_align's default path): each
+// iteration is the fused kernel followed by a one-group step kernel that sums
+// the partials, solves the rigid transform (rigid_solve.hpp), applies the
+// convergence rule and leaves the next transform here for the next fused
+// kernel, so the host enqueues all iterations and waits once.
+struct IcpLoopState {  // device memory (ICP workspace)
+    double rt[12];     // (R row-major, t) of the next iteration
+    double prev_mse;   // mean squared distance of the last iteration
+    int32_t small;     // consecutive iterations whose MSE changed by < eps
+    uint32_t stop;     // nonzero: converged or failed, later iterations do nothing
+};
+constexpr int32_t kLoopMaxIter = 512;  // iterations the output record holds
+struct IcpLoopOut {    // pinned host memory, written by the step kernels
+    double rt[12];     // last solved transform (the initial one until a solve)
+    int64_t iters;     // iterations completed
+    int64_t status;    // rigid_solve status of the failed iteration, 0 if none
+    int64_t fail_iter; // that iteration, -1 if none
+    int64_t stopped;   // nonzero once state.stop is set
+    double E[kLoopMaxIter];
+    double rt_hist[kLoopMaxIter][12];  // transform used by each iteration
+};
+struct IcpLoop {
+    IcpLoopState *state;  // device
+    IcpLoopOut *out;      // device address of the pinned record
+    int32_t iter;         // iteration index of this launch
+    double eps;
+};
+
 struct IcpWorkspace {
     SortWorkspace sort;
     double *partials;   // KDNN_SUMS_DOUBLES * max_blocks
@@ -104,6 +134,7 @@ struct IcpWorkspace {
     float *md2;         // [n] its squared distance
     double *stat;       // residual statistics of the rejection step
     double *sums;       // KDNN_SUMS_DOUBLES
+    IcpLoopState *loop; // device-side ICP loop state
     int32_t max_blocks;
 };
 size_t icp_ws_bytes(int64_t n);
@@ -133,12 +164,19 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
 // reduction into sums_out.  timing: null, or two events the search
 // kernel(s) stamp with their start and end.  done: null, or a word the
 // reduction sets to seq (system-scope release) once the sums are written.
+// loop: null, or one iteration of a device-side loop (one lane per query
+// schedule only): the search takes its transform from loop->state (R, tv
+// unused) and the step kernel replaces the reduction (sums_out unused).
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
                             float bound2, bool keep_matches, hipStream_t s,
                             const hipEvent_t *timing = nullptr, uint64_t *done = nullptr,
-                            uint64_t seq = 0);
+                            uint64_t seq = 0, const IcpLoop *loop = nullptr);
+// Start a device-side ICP loop: state <- (R0, t0), counters cleared; the
+// output record's transform <- (R0, t0), no iterations, no failure.
+hipError_t launch_icp_loop_init(IcpLoopState *state, IcpLoopOut *out, const double *R0,
+                                const double *t0, hipStream_t s);
 // One stable LSD radix pass (8-bit digit at `shift`) of (key, value) pairs;
 // hist: 256 x radix_tiles(m) words, totals: 256 words.
 int32_t radix_tiles(int64_t m);
@@ -210,6 +248,8 @@ struct kdnn_tree {
                                  // the last word: completion sequence number)
     uint64_t seq = 0;            // last sequence number handed to the reduction
     double *d_pinned = nullptr;  // the same slot as the device addresses it
+    kdnn::IcpLoopOut *h_loop = nullptr;  // device-side ICP loop record (pinned)
+    kdnn::IcpLoopOut *d_loop = nullptr;  // the same, as the device addresses it
     bool auto_sort = false;      // nn_query orders queries unless told otherwise
     bool auto_sort_icp = false;  // the ICP entry points order the source unless told otherwise
     std::mutex icp_mu;           // serialises users of h_pinned

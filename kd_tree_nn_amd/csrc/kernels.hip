@@ -14,6 +14,7 @@
 #include <cstring>
 
 #include "kdnn_internal.hpp"
+#include "rigid_solve.hpp"
 
 namespace kdnn {
 
@@ -1065,6 +1066,10 @@ __global__ __launch_bounds__(kWG) void nn_pass2_kernel(NnArgs a, TwoPass tp)
 // Per lane -> wave (reduce-scatter, one component per lane pair) -> work-group (waves
 // summed in order) -> per-group partials; reduce_partials_kernel then sums
 // the partials in a fixed order.  The result does not depend on scheduling.
+struct Rt12 {  // 12 doubles by value (kernel argument)
+    double v[12];
+};
+
 struct IcpArgs {
     TreeView tree;
     const float *src;
@@ -1087,6 +1092,8 @@ struct IcpArgs {
     float *md2;         // [n] or null: its squared distance
     bool spread;        // one-lane-per-query kernel: spread_pos
     uint32_t wq;        // one-lane-per-query kernel: queries per wave (1..64)
+    const double *rt_dev;  // one-lane-per-query kernel, device loop: (R, t) here, not in R / t
+    const uint32_t *stop;  // the same: nonzero = the loop has stopped, do nothing
 };
 
 __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, double tr, double x,
@@ -1216,6 +1223,20 @@ __device__ __forceinline__ void icp_query(const IcpArgs &a, int64_t i, double &X
     qz = rigid_row(a.R[6], a.R[7], a.R[8], a.t[2], X, Y, Z);
 }
 
+// The same with (R, t) read from device memory (the device-side ICP loop).
+__device__ __forceinline__ void icp_query_dev(const double *__restrict__ rt,
+                                              const float *__restrict__ src, int64_t i, double &X,
+                                              double &Y, double &Z, float &qx, float &qy,
+                                              float &qz)
+{
+    X = src[3 * i];
+    Y = src[3 * i + 1];
+    Z = src[3 * i + 2];
+    qx = rigid_row(rt[0], rt[1], rt[2], rt[9], X, Y, Z);
+    qy = rigid_row(rt[3], rt[4], rt[5], rt[10], X, Y, Z);
+    qz = rigid_row(rt[6], rt[7], rt[8], rt[11], X, Y, Z);
+}
+
 // Record a finished pair: optional per-point outputs, then the fp64 sums
 // (s - c), (m - c), (s - c)(m - c)^T, d2, 1.
 __device__ __forceinline__ void icp_accumulate(const IcpArgs &a, int64_t i, double X, double Y,
@@ -1297,6 +1318,108 @@ static void launch_reduce_partials(const double *p1, int32_t n1, const double *p
                                                                       stat_out, done, seq);
 }
 
+// ------------------------------------------- ICP iterations on the device
+//
+// One iteration = the fused kernel (transform from st->rt, search, partials)
+// + icp_loop_step_kernel (one work-group): the partials summed in the same
+// fixed order as reduce_partials_kernel, then on one lane the rigid solve,
+// the convergence rule (|MSE_k - MSE_{k-1}| < eps on two consecutive
+// iterations, as the host loop applies it) and the next transform.  A failed
+// solve keeps the last good transform and sets stop; so does convergence.
+// Once stop is set the remaining launches of the queue return at once.
+// The per-iteration record (E_k, the transform used) goes to pinned host
+// memory, read by the host after it synchronises the stream.
+__global__ __launch_bounds__(64) void icp_loop_init_kernel(IcpLoopState *st, IcpLoopOut *out,
+                                                           Rt12 rt0)
+{
+    if (threadIdx.x != 0) return;
+    for (int k = 0; k < 12; ++k) {
+        st->rt[k] = rt0.v[k];
+        out->rt[k] = rt0.v[k];
+    }
+    st->prev_mse = 0.0;
+    st->small = 0;
+    st->stop = 0u;
+    out->iters = 0;
+    out->status = 0;
+    out->fail_iter = -1;
+    out->stopped = 0;
+}
+
+template <int WG>
+__global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int32_t np,
+                                                           IcpLoopState *st, IcpLoopOut *out,
+                                                           int32_t k, double eps, Rt12 c)
+{
+    __shared__ double red[(WG / 64) * kS];
+    __shared__ double tot[kS];
+    if (st->stop) return;  // uniform: every lane reads the same word
+    double acc[kS];
+#pragma unroll
+    for (int j = 0; j < kS; ++j) acc[j] = 0.0;
+    for (int32_t g = threadIdx.x; g < np; g += WG) {
+#pragma unroll
+        for (int j = 0; j < kS; ++j) acc[j] += p[int64_t(j) * np + g];
+    }
+    block_sum_n<WG>(acc, red, tot, 1);
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    const double n = tot[16], E = tot[15];
+    if (k >= 0 && k < kLoopMaxIter) {  // the host never launches beyond the record
+        out->E[k] = E;
+        for (int j = 0; j < 12; ++j) out->rt_hist[k][j] = st->rt[j];
+    }
+    double R[9], t[3];
+    const int32_t rs = rigid_from_sums(&tot[0], &tot[3], &tot[6], n, c.v, R, t);
+    if (rs != kRigidOk) {
+        out->status = rs;
+        out->fail_iter = k;
+        out->stopped = 1;
+        st->stop = 1u;
+        return;
+    }
+    for (int j = 0; j < 9; ++j) {
+        st->rt[j] = R[j];
+        out->rt[j] = R[j];
+    }
+    for (int j = 0; j < 3; ++j) {
+        st->rt[9 + j] = t[j];
+        out->rt[9 + j] = t[j];
+    }
+    out->iters = k + 1;
+    const double mse = E / n;
+    if (eps > 0.0 && k > 0) {
+        st->small = fabs(mse - st->prev_mse) < eps ? st->small + 1 : 0;
+        if (st->small >= 2) {
+            st->stop = 1u;
+            out->stopped = 1;
+        }
+    }
+    st->prev_mse = mse;
+}
+
+hipError_t launch_icp_loop_init(IcpLoopState *state, IcpLoopOut *out, const double *R0,
+                                const double *t0, hipStream_t s)
+{
+    Rt12 rt0;
+    for (int k = 0; k < 9; ++k) rt0.v[k] = R0[k];
+    for (int k = 0; k < 3; ++k) rt0.v[9 + k] = t0[k];
+    icp_loop_init_kernel<<<1, 64, 0, s>>>(state, out, rt0);
+    return hipGetLastError();
+}
+
+static void launch_icp_loop_step(const double *p, int32_t np, const IcpLoop &L,
+                                 const double *center, hipStream_t s)
+{
+    Rt12 c{};
+    for (int k = 0; k < 3; ++k) c.v[k] = center[k];
+    if (np <= kWG || KDNN_RED_WG == kWG)
+        icp_loop_step_kernel<kWG><<<1, kWG, 0, s>>>(p, np, L.state, L.out, L.iter, L.eps, c);
+    else
+        icp_loop_step_kernel<KDNN_RED_WG><<<1, KDNN_RED_WG, 0, s>>>(p, np, L.state, L.out,
+                                                                     L.iter, L.eps, c);
+}
+
 // Single pass, one kernel: transform, search (balanced wave search for G = 1,
 // G lanes per point otherwise) and the fp64 reduction.
 // Registers: the reduce-scatter's 17 live sums would take the 16-point kernel
@@ -1320,6 +1443,7 @@ icp_fused_kernel(IcpArgs a)
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t xfer[kWG];
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        if (a.stop && *a.stop) return;  // device loop already stopped (uniform)
         if (lane == 63) {
 #pragma unroll
             for (int c = 0; c < kS; ++c) red[wv * kS + c] = 0.0;
@@ -1334,7 +1458,10 @@ icp_fused_kernel(IcpArgs a)
             float qx = 0.0f, qy = 0.0f, qz = 0.0f;
             if (own) {
                 double X, Y, Z;
-                icp_query(a, i, X, Y, Z, qx, qy, qz);
+                if (a.rt_dev)
+                    icp_query_dev(a.rt_dev, a.src, i, X, Y, Z, qx, qy, qz);
+                else
+                    icp_query(a, i, X, Y, Z, qx, qy, qz);
             }
             wave_search<false, true, CH>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
                                          nullptr, nullptr, xfer + (threadIdx.x & ~63u),
@@ -2000,7 +2127,8 @@ size_t icp_ws_bytes(int64_t n)
     const size_t nn = size_t(n);
     return sort_workspace_bytes(n) + align256(size_t(kS) * kIcpMaxBlocks * 8) +
            align256(size_t(kS) * kPass2Blocks * 8) + align256(size_t(kS) * 8) +
-           align256(nn * 4) + align256(nn * 8) + twopass_bytes(n) + 2 * align256(nn * 4) + 256;
+           align256(nn * 4) + align256(nn * 8) + twopass_bytes(n) + 2 * align256(nn * 4) + 256 +
+           align256(sizeof(IcpLoopState));
 }
 
 IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
@@ -2026,6 +2154,8 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
     w.md2 = reinterpret_cast<float *>(p);
     p += align256(size_t(n) * 4);
     w.stat = reinterpret_cast<double *>(p);
+    p += 256;
+    w.loop = reinterpret_cast<IcpLoopState *>(p);
     w.max_blocks = kIcpMaxBlocks;
     return w;
 }
@@ -2371,9 +2501,16 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
                             float bound2, bool keep_matches, hipStream_t s,
-                            const hipEvent_t *timing, uint64_t *done, uint64_t seq)
+                            const hipEvent_t *timing, uint64_t *done, uint64_t seq,
+                            const IcpLoop *loop)
 {
+    if (loop && (sc.lanes > 1 || sc.top_lds || sc.budget != 0 || keep_matches))
+        return hipErrorInvalidValue;  // the device loop runs the one-lane-per-query kernel only
     IcpArgs a{};
+    if (loop) {
+        a.rt_dev = loop->state->rt;
+        a.stop = &loop->state->stop;
+    }
     a.tree = tree_view(t);
     a.init = host_bound_key(bound2);
     a.mslot = keep_matches ? ws.mslot : nullptr;
@@ -2433,8 +2570,11 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         e = launch_k(k, grid, kWG, sc.lanes <= 1 && small ? lbs_bytes(t.depth) : 0, s, e0, e1,
                      a);
         if (e != hipSuccess) return e;
-        launch_reduce_partials(a.partials, int32_t(grid.x), nullptr, 0, sums_out, nullptr, nullptr,
-                               done, seq, s);
+        if (loop)
+            launch_icp_loop_step(a.partials, int32_t(grid.x), *loop, t.center, s);
+        else
+            launch_reduce_partials(a.partials, int32_t(grid.x), nullptr, 0, sums_out, nullptr,
+                                   nullptr, done, seq, s);
     }
     return hipGetLastError();
 }

@@ -306,7 +306,7 @@ def test_scene_icp_align(torch, kdnn):
     _, o = scene_oracle_icp()
     tree = kdnn.Tree(p.target, 16)
     for sched in SCHED + [{"lanes": 1}, {"sort": False}, {"sort": False, "budget": 3},
-                          {"sort": True}, {"sort": True, "budget": 3}]:
+                          {"sort": True}, {"sort": True, "budget": 3}, {"host_loop": True}]:
         say("scene icp_align 30", sched)
         g = tree.icp(dev(torch, p.source), max_iter=p.iters, **sched)
         assert g["iters"] == p.iters
@@ -315,6 +315,66 @@ def test_scene_icp_align(torch, kdnn):
         assert dR <= R_TOL and dt <= T_TOL, (sched, dR, dt)
         np.testing.assert_allclose(g["E"], o["E"], rtol=1e-6)
         np.testing.assert_allclose(g["Rt_hist"], o["Rt_hist"], atol=1e-6)
+
+
+def test_device_loop_matches_host_loop(torch, kdnn):
+    """icp_align keeps the iterations on the device (the step kernel solves with
+    the same code as kdnn_procrustes on the same sums, summed in the same order)
+    unless asked to solve on the host: both must follow the same iterates."""
+    for name, p, leaf in [("tiny", synth.tiny(), 8), ("scene", scene(), 16),
+                          ("lidar 5", lidar()[5], 16)]:
+        tree = kdnn.Tree(p.target, leaf)
+        src = dev(torch, p.source)
+        for kw in ({}, {"sort": True}, {"max_dist": 1.0}):
+            say("device vs host loop", name, kw)
+            d = tree.icp(src, max_iter=p.iters, **kw)
+            h = tree.icp(src, max_iter=p.iters, host_loop=True, **kw)
+            assert d["iters"] == h["iters"] == p.iters, (name, kw)
+            np.testing.assert_allclose(d["E"], h["E"], rtol=1e-12, err_msg=f"{name} {kw}")
+            np.testing.assert_allclose(d["Rt_hist"], h["Rt_hist"], rtol=0, atol=1e-12)
+            assert np.linalg.norm(d["R"] - h["R"]) <= 1e-12 and np.max(np.abs(d["t"] - h["t"])) <= 1e-12
+            say("  bit-identical:", bool(np.array_equal(d["Rt_hist"], h["Rt_hist"])))
+
+
+def test_device_loop_eps_and_limits(torch, kdnn):
+    """Convergence stop at every phase of the 4-iteration chunks, the host
+    fallback beyond the record's 512 iterations, and a degenerate first
+    iteration (no pair within max_dist): EDEGENERATE, transform unchanged."""
+    p = synth.tiny()
+    tree = kdnn.Tree(p.target, 8)
+    src = dev(torch, p.source)
+    for eps in (1e-5, 1e-6, 1e-7, 1e-8, 1e-9):
+        say("device loop eps", eps)
+        o = oracle.icp(p.target, p.source, 60, nn="brute", eps=eps)
+        d = tree.icp(src, max_iter=60, eps=eps)
+        h = tree.icp(src, max_iter=60, eps=eps, host_loop=True)
+        assert d["iters"] == h["iters"] == o["iters"], (eps, d["iters"], h["iters"], o["iters"])
+        np.testing.assert_allclose(d["E"], o["E"], rtol=1e-6)
+    say("device loop beyond the record")
+    g = tree.icp(src, max_iter=520)
+    assert g["iters"] == 520 and len(g["E"]) == 520
+    from kd_tree_nn_amd import _lib
+    import ctypes
+    far = dev(torch, (p.source + np.float32(100.0)).astype(np.float32))
+    ws = tree.icp_workspace(len(p.source))
+    R0 = synth.rotation_about([0, 0, 1], 0.1)
+    t0 = np.array([0.5, -0.25, 2.0])
+    for flags in (0, _lib.KDNN_ICP_HOST_LOOP):
+        say("device loop degenerate, flags", flags)
+        R, t, E = np.zeros(9), np.zeros(3), np.zeros(5)
+        it = ctypes.c_int32(-1)
+        st = _lib.lib().icp_align(
+            tree._h, ctypes.c_void_p(far.data_ptr()), len(p.source),
+            np.ascontiguousarray(R0).ctypes.data_as(_lib.c_dp), t0.ctypes.data_as(_lib.c_dp), 5, 0.0,
+            R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp), E.ctypes.data_as(_lib.c_dp),
+            None, ctypes.byref(it), flags, ctypes.byref(_lib.IcpReject(0.5, 0.0)),
+            ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+        assert st == _lib.KDNN_EDEGENERATE, st
+        assert b"iteration 0" in _lib.lib().kdnn_last_error()
+        assert it.value == 0
+        np.testing.assert_array_equal(R.reshape(3, 3), R0)
+        np.testing.assert_array_equal(t, t0)
+        assert E[0] == 0.0  # no pair: the iteration's sum of squared distances
 
 
 def test_determinism(torch, kdnn):
