@@ -1353,7 +1353,12 @@ __global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int3
 {
     __shared__ double red[(WG / 64) * kS];
     __shared__ double tot[kS];
-    if (st->stop) return;  // uniform: every lane reads the same word
+    // the state's words are read up front, in the shadow of the partials'
+    // loads (a stopped loop sums stale partials and then discards them)
+    const uint32_t stopped = st->stop;
+    double rt_used[12];
+    if (threadIdx.x == 0)
+        for (int j = 0; j < 12; ++j) rt_used[j] = st->rt[j];
     double acc[kS];
 #pragma unroll
     for (int j = 0; j < kS; ++j) acc[j] = 0.0;
@@ -1363,11 +1368,11 @@ __global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int3
     }
     block_sum_n<WG>(acc, red, tot, 1);
     __syncthreads();
-    if (threadIdx.x != 0) return;
+    if (threadIdx.x != 0 || stopped) return;
     const double n = tot[16], E = tot[15];
     if (k >= 0 && k < kLoopMaxIter) {  // the host never launches beyond the record
         out->E[k] = E;
-        for (int j = 0; j < 12; ++j) out->rt_hist[k][j] = st->rt[j];
+        for (int j = 0; j < 12; ++j) out->rt_hist[k][j] = rt_used[j];
     }
     double R[9], t[3];
     const int32_t rs = rigid_from_sums(&tot[0], &tot[3], &tot[6], n, c.v, R, t);

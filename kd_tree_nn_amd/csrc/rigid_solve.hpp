@@ -214,8 +214,10 @@ KDNN_HD inline int32_t rotation_by_svd(const double H[9], double R[9])
 // the cross-covariance H[3a + b] = sum (s - mu_s)_a (m - mu_m)_b.
 KDNN_HD inline int32_t rigid_rotation(const double H[9], double R[9])
 {
-    double F = 0.0;
-    for (int k = 0; k < 9; ++k) F += H[k] * H[k];
+    // sums as balanced trees: short dependency chains on one GPU lane
+    const double F = (((H[0] * H[0] + H[1] * H[1]) + (H[2] * H[2] + H[3] * H[3])) +
+                      ((H[4] * H[4] + H[5] * H[5]) + (H[6] * H[6] + H[7] * H[7]))) +
+                     H[8] * H[8];
     if (!(F > 0.0) || !(F < INFINITY)) return kRigidRankLow;
     // cofactors of H (the 2x2 minors, signed)
     const double C[9] = {H[4] * H[8] - H[5] * H[7], H[5] * H[6] - H[3] * H[8],
@@ -223,8 +225,9 @@ KDNN_HD inline int32_t rigid_rotation(const double H[9], double R[9])
                          H[0] * H[8] - H[2] * H[6], H[1] * H[6] - H[0] * H[7],
                          H[1] * H[5] - H[2] * H[4], H[2] * H[3] - H[0] * H[5],
                          H[0] * H[4] - H[1] * H[3]};
-    double K = 0.0;
-    for (int k = 0; k < 9; ++k) K += C[k] * C[k];
+    const double K = (((C[0] * C[0] + C[1] * C[1]) + (C[2] * C[2] + C[3] * C[3])) +
+                      ((C[4] * C[4] + C[5] * C[5]) + (C[6] * C[6] + C[7] * C[7]))) +
+                     C[8] * C[8];
     if (!(K > 1e-24 * (F * F))) return kRigidRankLow;
     const double detH = (H[0] * C[0] + H[1] * C[1]) + H[2] * C[2];
     const double Sxx = H[0], Sxy = H[1], Sxz = H[2], Syx = H[3], Syy = H[4], Syz = H[5],
@@ -234,7 +237,20 @@ KDNN_HD inline int32_t rigid_rotation(const double H[9], double R[9])
                           Szx - Sxz,         Sxy + Syx,         (Syy - Sxx) - Szz,  Syz + Szy,
                           Sxy - Syx,         Szx + Sxz,         Syz + Szy,          (Szz - Sxx) - Syy};
     const double c2 = -2.0 * F, c1 = -8.0 * detH, c0 = det4(minors4(N));
-    double x = std::sqrt(3.0 * F);
+    // start: the smaller of two upper bounds of the largest eigenvalue,
+    // sqrt(3) |H|_F and Gershgorin's max_i (N_ii + sum_j!=i |N_ij|) -- the
+    // latter is within a fraction of a percent of it when the rotation is
+    // small (N is then nearly diagonal in its first row), which saves about
+    // half of the Newton steps
+    double gersh = -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+        const double r = N[5 * i] + ((std::fabs(N[4 * i + (i + 1) % 4]) +
+                                      std::fabs(N[4 * i + (i + 2) % 4])) +
+                                     std::fabs(N[4 * i + (i + 3) % 4]));
+        gersh = r > gersh ? r : gersh;
+    }
+    const double root3F = std::sqrt(3.0 * F);
+    double x = gersh < root3F ? gersh : root3F;
     for (int it = 0; it < 100; ++it) {
         const double x2 = x * x;
         const double p = ((x2 + c2) * x2 + c1 * x) + c0;
