@@ -7,6 +7,7 @@
 #include <atomic>
 #include <chrono>
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <new>
 #include <string>
@@ -104,6 +105,7 @@ void free_tree(kdnn_tree *t)
     if (t->d_slot_of) (void)hipFree(t->d_slot_of);
     if (t->h_pinned) (void)hipHostFree(t->h_pinned);
     if (t->h_loop) (void)hipHostFree(t->h_loop);
+    if (t->d_loop) (void)hipFree(t->d_loop);
     if (cur >= 0 && cur != t->device) (void)hipSetDevice(cur);
     delete t;
 }
@@ -255,8 +257,9 @@ kdnn_status icp_check(const kdnn_tree *tree, const float *src, int64_t n, const 
 // initial state, then per iteration the fused kernel and the step kernel
 // (rigid solve, convergence rule, next transform on the device), and waits
 // once -- after every 4 iterations when eps > 0, so that a converged
-// registration stops soon.  The record the step kernels write into the tree's
-// pinned slot gives the outputs.  Caller holds the tree's ICP lock.
+// registration stops soon.  The record the step kernels write (device memory,
+// copied into the tree's pinned slot at the end) gives the outputs.  Caller
+// holds the tree's ICP lock.
 kdnn_status icp_align_on_device(kdnn_tree *mt, const float *src_dev, int64_t n, const double *R,
                                 const double *t, int32_t max_iter, double eps, double *R_out,
                                 double *t_out, double *E_hist, double *Rt_hist,
@@ -267,7 +270,8 @@ kdnn_status icp_align_on_device(kdnn_tree *mt, const float *src_dev, int64_t n, 
     hipError_t e = launch_icp_loop_init(w.loop, mt->d_loop, R, t, stream);
     if (e != hipSuccess) return hip_fail(e, "icp_align: loop start");
     IcpLoop L{w.loop, mt->d_loop, 0, eps};
-    const volatile IcpLoopOut *out = mt->h_loop;
+    const IcpLoopOut *out = mt->h_loop;
+    constexpr size_t kHead = offsetof(IcpLoopOut, E);
     for (int32_t k = 0; k < max_iter; ++k) {
         L.iter = k;
         const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
@@ -275,12 +279,21 @@ kdnn_status icp_align_on_device(kdnn_tree *mt, const float *src_dev, int64_t n, 
                                            reject, w, stream, nullptr, 0, &L);
         if (st != KDNN_OK) return st;
         if (eps > 0.0 && (k + 1) % kChunk == 0 && k + 1 < max_iter) {
-            if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+            if ((e = hipMemcpyAsync(mt->h_loop, mt->d_loop, kHead, hipMemcpyDeviceToHost,
+                                    stream)) != hipSuccess ||
+                (e = hipStreamSynchronize(stream)) != hipSuccess)
                 return hip_fail(e, "icp_align: synchronize");
             if (out->stopped) break;
         }
     }
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess)
+    // the record: header and E_0.. always, the transforms used when asked for
+    const size_t nrec = size_t(max_iter);
+    if ((e = hipMemcpyAsync(mt->h_loop, mt->d_loop, kHead + nrec * sizeof(double),
+                            hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+        (Rt_hist && (e = hipMemcpyAsync(mt->h_loop->rt_hist, mt->d_loop->rt_hist,
+                                        nrec * sizeof(out->rt_hist[0]), hipMemcpyDeviceToHost,
+                                        stream)) != hipSuccess) ||
+        (e = hipStreamSynchronize(stream)) != hipSuccess)
         return hip_fail(e, "icp_align: synchronize");
     const int32_t done = int32_t(out->iters);
     const int32_t failed = int32_t(out->fail_iter);
@@ -478,18 +491,18 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         free_tree(t);
         return hip_fail(e, "kdtree_build: hipHostGetDevicePointer");
     }
-    // the record the device-side ICP loop writes (per-iteration E and transform)
-    if ((e = hipHostMalloc(reinterpret_cast<void **>(&t->h_loop), sizeof(kdnn::IcpLoopOut),
+    // the record the device-side ICP loop writes (per-iteration E and transform):
+    // in device memory, copied once into pinned memory at the end of a
+    // registration (writes to host memory would hold up every step kernel's
+    // completion by a PCIe round trip)
+    if ((e = hipMalloc(reinterpret_cast<void **>(&t->d_loop), sizeof(kdnn::IcpLoopOut))) !=
+            hipSuccess ||
+        (e = hipHostMalloc(reinterpret_cast<void **>(&t->h_loop), sizeof(kdnn::IcpLoopOut),
                            hipHostMallocDefault)) != hipSuccess) {
         free_tree(t);
-        return fail(KDNN_ENOMEM, std::string("kdtree_build: hipHostMalloc: ") + hipGetErrorString(e));
+        return fail(KDNN_ENOMEM, std::string("kdtree_build: loop record: ") + hipGetErrorString(e));
     }
     std::memset(static_cast<void *>(t->h_loop), 0, sizeof(kdnn::IcpLoopOut));
-    if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&t->d_loop), t->h_loop, 0)) !=
-        hipSuccess) {
-        free_tree(t);
-        return hip_fail(e, "kdtree_build: hipHostGetDevicePointer");
-    }
     if ((e = hipMemcpy(t->d_nodes, ht.nodes.data(), nb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(t->d_boxes, boxes.data(), bb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess ||

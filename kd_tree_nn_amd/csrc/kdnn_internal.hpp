@@ -107,7 +107,7 @@ struct IcpLoopState {  // device memory (ICP workspace)
     uint32_t stop;     // nonzero: converged or failed, later iterations do nothing
 };
 constexpr int32_t kLoopMaxIter = 512;  // iterations the output record holds
-struct IcpLoopOut {    // pinned host memory, written by the step kernels
+struct IcpLoopOut {    // device memory, written by the step kernels (copied to the host at the end)
     double rt[12];     // last solved transform (the initial one until a solve)
     int64_t iters;     // iterations completed
     int64_t status;    // rigid_solve status of the failed iteration, 0 if none
@@ -248,8 +248,8 @@ struct kdnn_tree {
                                  // the last word: completion sequence number)
     uint64_t seq = 0;            // last sequence number handed to the reduction
     double *d_pinned = nullptr;  // the same slot as the device addresses it
-    kdnn::IcpLoopOut *h_loop = nullptr;  // device-side ICP loop record (pinned)
-    kdnn::IcpLoopOut *d_loop = nullptr;  // the same, as the device addresses it
+    kdnn::IcpLoopOut *d_loop = nullptr;  // device-side ICP loop record (device memory)
+    kdnn::IcpLoopOut *h_loop = nullptr;  // its pinned copy, read after a registration
     bool auto_sort = false;      // nn_query orders queries unless told otherwise
     bool auto_sort_icp = false;  // the ICP entry points order the source unless told otherwise
     std::mutex icp_mu;           // serialises users of h_pinned

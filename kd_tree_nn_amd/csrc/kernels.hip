@@ -1327,8 +1327,9 @@ static void launch_reduce_partials(const double *p1, int32_t n1, const double *p
 // iterations, as the host loop applies it) and the next transform.  A failed
 // solve keeps the last good transform and sets stop; so does convergence.
 // Once stop is set the remaining launches of the queue return at once.
-// The per-iteration record (E_k, the transform used) goes to pinned host
-// memory, read by the host after it synchronises the stream.
+// The per-iteration record (E_k, the transform used) stays in device memory;
+// the host copies it once the registration has run (a store to host memory
+// would hold up each step kernel's completion by a PCIe round trip).
 __global__ __launch_bounds__(64) void icp_loop_init_kernel(IcpLoopState *st, IcpLoopOut *out,
                                                            Rt12 rt0)
 {
