@@ -352,12 +352,13 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  *                  n_k count them; with reject_k > 0 each iteration solves,
  *                  rejects by residual (icp_reject_reduce) and solves again.
  * The traversal order is computed once, from the source moved by (R0, t0).
- * With one lane per query (no schedule flag or KDNN_LANES(1)), no reject_k,
- * max_iter <= 512 and no KDNN_ICP_HOST_LOOP, the iterations stay on the
- * device: each one's sums are reduced and solved (the same arithmetic as
- * kdnn_procrustes) by a one-group kernel that leaves the next transform for
- * the next search, so all iterations are enqueued at once (in chunks of 4
- * when eps > 0, to stop soon after convergence) and the host waits once.
+ * With one lane per query (no schedule flag or KDNN_LANES(1)), max_iter <= 512
+ * and no KDNN_ICP_HOST_LOOP, the iterations stay on the device: each one's
+ * sums are reduced and solved (the same arithmetic as kdnn_procrustes) by a
+ * one-group kernel that leaves the next transform for the next search (with
+ * reject_k > 0: the first solve for the residual pass, then the kept pairs'),
+ * so all iterations are enqueued at once (in chunks of 4 when eps > 0, to
+ * stop soon after convergence) and the host waits once.
  * Otherwise each iteration's sums come back to the host, which solves.
  * On EDEGENERATE the outputs hold the last good transform.
  * Errors: EINVAL, EDEVICE, EDEGENERATE. */

@@ -269,15 +269,24 @@ kdnn_status icp_align_on_device(kdnn_tree *mt, const float *src_dev, int64_t n, 
     constexpr int32_t kChunk = 4;
     hipError_t e = launch_icp_loop_init(w.loop, mt->d_loop, R, t, stream);
     if (e != hipSuccess) return hip_fail(e, "icp_align: loop start");
-    IcpLoop L{w.loop, mt->d_loop, 0, eps};
+    const double reject_k = reject ? reject->reject_k : 0.0;
+    IcpLoop L{w.loop, mt->d_loop, 0, eps, reject_k > 0.0 ? 1 : 0};
     const IcpLoopOut *out = mt->h_loop;
     constexpr size_t kHead = offsetof(IcpLoopOut, E);
     for (int32_t k = 0; k < max_iter; ++k) {
         L.iter = k;
         const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
+        L.mode = reject_k > 0.0 ? 1 : 0;
         const kdnn_status st = icp_enqueue(mt, src_dev, n, R, t, nullptr, nullptr, nullptr, f,
                                            reject, w, stream, nullptr, 0, &L);
         if (st != KDNN_OK) return st;
+        if (reject_k > 0.0) {
+            // residuals under the first solve, then the solve of the kept pairs
+            L.mode = 2;
+            e = launch_icp_reject(mt->dev, src_dev, n, R, t, reject_k * reject_k, w, nullptr,
+                                  nullptr, nullptr, stream, nullptr, 0, &L);
+            if (e != hipSuccess) return hip_fail(e, "icp_align: rejection launch");
+        }
         if (eps > 0.0 && (k + 1) % kChunk == 0 && k + 1 < max_iter) {
             if ((e = hipMemcpyAsync(mt->h_loop, mt->d_loop, kHead, hipMemcpyDeviceToHost,
                                     stream)) != hipSuccess ||
@@ -307,7 +316,8 @@ kdnn_status icp_align_on_device(kdnn_tree *mt, const float *src_dev, int64_t n, 
     for (int j = 0; j < 3; ++j) t_out[j] = out->rt[9 + j];
     if (iters_done) *iters_done = done;
     if (failed >= 0)
-        return fail(KDNN_EDEGENERATE, "icp_align: iteration " + std::to_string(failed) + ": " +
+        return fail(KDNN_EDEGENERATE, "icp_align: iteration " + std::to_string(failed) +
+                                          (out->fail_phase ? " after rejection: " : ": ") +
                                           rigid_status_text(int32_t(out->status)));
     return KDNN_OK;
 }
@@ -784,8 +794,7 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     std::lock_guard<std::mutex> lock(mt->icp_mu);
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
     const Schedule sc = schedule_of(flags);
-    if (!host_loop && reject_k == 0.0 && sc.lanes <= 1 && !sc.top_lds && sc.budget == 0 &&
-        max_iter <= kLoopMaxIter)
+    if (!host_loop && sc.lanes <= 1 && !sc.top_lds && sc.budget == 0 && max_iter <= kLoopMaxIter)
         return icp_align_on_device(mt, src_dev, n, R, t, max_iter, eps, R_out, t_out, E_hist,
                                    Rt_hist, iters_done, flags, reject, w, stream);
     double prev_mse = 0.0;

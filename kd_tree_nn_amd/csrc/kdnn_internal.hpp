@@ -102,7 +102,9 @@ QueryWorkspace carve_query_workspace(void *ws, int64_t m);
 // kernel, so the host enqueues all iterations and waits once.
 struct IcpLoopState {  // device memory (ICP workspace)
     double rt[12];     // (R row-major, t) of the next iteration
+    double rt1[12];    // residual rejection: the iteration's first solve
     double prev_mse;   // mean squared distance of the last iteration
+    double mse;        // residual rejection: this iteration's (first pass)
     int32_t small;     // consecutive iterations whose MSE changed by < eps
     uint32_t stop;     // nonzero: converged or failed, later iterations do nothing
 };
@@ -112,15 +114,20 @@ struct IcpLoopOut {    // device memory, written by the step kernels (copied to 
     int64_t iters;     // iterations completed
     int64_t status;    // rigid_solve status of the failed iteration, 0 if none
     int64_t fail_iter; // that iteration, -1 if none
+    int64_t fail_phase;// 1: the solve after residual rejection failed
     int64_t stopped;   // nonzero once state.stop is set
     double E[kLoopMaxIter];
     double rt_hist[kLoopMaxIter][12];  // transform used by each iteration
 };
 struct IcpLoop {
     IcpLoopState *state;  // device
-    IcpLoopOut *out;      // device address of the pinned record
+    IcpLoopOut *out;      // device record
     int32_t iter;         // iteration index of this launch
     double eps;
+    // 0: the iteration's only solve; with residual rejection, 1: the first
+    // solve (into state.rt1, iteration not yet done), 2: the solve of the
+    // kept pairs (ends the iteration)
+    int32_t mode;
 };
 
 struct IcpWorkspace {
@@ -231,7 +238,8 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
                              const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,
                              double *stat_out, uint8_t *kept, hipStream_t s,
-                             uint64_t *done = nullptr, uint64_t seq = 0);
+                             uint64_t *done = nullptr, uint64_t seq = 0,
+                             const IcpLoop *loop = nullptr);
 
 }  // namespace kdnn
 

@@ -1344,13 +1344,16 @@ __global__ __launch_bounds__(64) void icp_loop_init_kernel(IcpLoopState *st, Icp
     out->iters = 0;
     out->status = 0;
     out->fail_iter = -1;
+    out->fail_phase = 0;
     out->stopped = 0;
+    st->mse = 0.0;
 }
 
 template <int WG>
 __global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int32_t np,
                                                            IcpLoopState *st, IcpLoopOut *out,
-                                                           int32_t k, double eps, Rt12 c)
+                                                           int32_t k, double eps, Rt12 c,
+                                                           int32_t mode)
 {
     __shared__ double red[(WG / 64) * kS];
     __shared__ double tot[kS];
@@ -1371,7 +1374,7 @@ __global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int3
     __syncthreads();
     if (threadIdx.x != 0 || stopped) return;
     const double n = tot[16], E = tot[15];
-    if (k >= 0 && k < kLoopMaxIter) {  // the host never launches beyond the record
+    if (mode != 2 && k >= 0 && k < kLoopMaxIter) {  // the host never launches beyond the record
         out->E[k] = E;
         for (int j = 0; j < 12; ++j) out->rt_hist[k][j] = rt_used[j];
     }
@@ -1380,8 +1383,15 @@ __global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int3
     if (rs != kRigidOk) {
         out->status = rs;
         out->fail_iter = k;
+        out->fail_phase = mode == 2 ? 1 : 0;
         out->stopped = 1;
         st->stop = 1u;
+        return;
+    }
+    if (mode == 1) {  // first solve of a rejection iteration: the residuals use it
+        for (int j = 0; j < 9; ++j) st->rt1[j] = R[j];
+        for (int j = 0; j < 3; ++j) st->rt1[9 + j] = t[j];
+        st->mse = E / n;
         return;
     }
     for (int j = 0; j < 9; ++j) {
@@ -1393,7 +1403,7 @@ __global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int3
         out->rt[9 + j] = t[j];
     }
     out->iters = k + 1;
-    const double mse = E / n;
+    const double mse = mode == 2 ? st->mse : E / n;  // the first pass's, as the host loop
     if (eps > 0.0 && k > 0) {
         st->small = fabs(mse - st->prev_mse) < eps ? st->small + 1 : 0;
         if (st->small >= 2) {
@@ -1420,10 +1430,11 @@ static void launch_icp_loop_step(const double *p, int32_t np, const IcpLoop &L,
     Rt12 c{};
     for (int k = 0; k < 3; ++k) c.v[k] = center[k];
     if (np <= kWG || KDNN_RED_WG == kWG)
-        icp_loop_step_kernel<kWG><<<1, kWG, 0, s>>>(p, np, L.state, L.out, L.iter, L.eps, c);
+        icp_loop_step_kernel<kWG><<<1, kWG, 0, s>>>(p, np, L.state, L.out, L.iter, L.eps, c,
+                                                    L.mode);
     else
         icp_loop_step_kernel<KDNN_RED_WG><<<1, KDNN_RED_WG, 0, s>>>(p, np, L.state, L.out,
-                                                                     L.iter, L.eps, c);
+                                                                     L.iter, L.eps, c, L.mode);
 }
 
 // Single pass, one kernel: transform, search (balanced wave search for G = 1,
@@ -1751,6 +1762,7 @@ struct RejArgs {
     double *partials;      // [kS][gridDim.x]
     double *stat;          // device: sum r^2, pairs, threshold
     uint8_t *kept;         // [n] or null: 1 where the pair is kept
+    const double *rt_dev;  // device loop: (R, t) here (its first solve), not in R / t
 };
 
 // The matched target point of source point i, if any (a stored index outside
@@ -1763,13 +1775,20 @@ __device__ __forceinline__ bool rej_pair(const RejArgs &a, int64_t i, float4 &m)
     return true;
 }
 
-__device__ __forceinline__ double rej_residual_sq(const RejArgs &a, double X, double Y, double Z,
-                                                  const float4 &m)
+__device__ __forceinline__ double rej_residual_sq(const double (&T)[12], double X, double Y,
+                                                  double Z, const float4 &m)
 {
-    const double e0 = (((a.R[0] * X + a.R[1] * Y) + a.R[2] * Z) + a.t[0]) - double(m.x);
-    const double e1 = (((a.R[3] * X + a.R[4] * Y) + a.R[5] * Z) + a.t[1]) - double(m.y);
-    const double e2 = (((a.R[6] * X + a.R[7] * Y) + a.R[8] * Z) + a.t[2]) - double(m.z);
+    const double e0 = (((T[0] * X + T[1] * Y) + T[2] * Z) + T[9]) - double(m.x);
+    const double e1 = (((T[3] * X + T[4] * Y) + T[5] * Z) + T[10]) - double(m.y);
+    const double e2 = (((T[6] * X + T[7] * Y) + T[8] * Z) + T[11]) - double(m.z);
     return (e0 * e0 + e1 * e1) + e2 * e2;
+}
+
+// (R, t) of a rejection kernel: the arguments, or the device loop's state.
+__device__ __forceinline__ void rej_transform(const RejArgs &a, double (&T)[12])
+{
+#pragma unroll
+    for (int k = 0; k < 12; ++k) T[k] = a.rt_dev ? a.rt_dev[k] : (k < 9 ? a.R[k] : a.t[k - 9]);
 }
 
 __global__ __launch_bounds__(kWG) void icp_residual_kernel(RejArgs a)
@@ -1778,11 +1797,13 @@ __global__ __launch_bounds__(kWG) void icp_residual_kernel(RejArgs a)
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
+    double T[12];
+    rej_transform(a, T);
     for (int64_t i = int64_t(blockIdx.x) * kWG + threadIdx.x; i < a.n;
          i += int64_t(gridDim.x) * kWG) {
         float4 m;
         if (!rej_pair(a, i, m)) continue;
-        acc[0] += rej_residual_sq(a, a.src[3 * i], a.src[3 * i + 1], a.src[3 * i + 2], m);
+        acc[0] += rej_residual_sq(T, a.src[3 * i], a.src[3 * i + 1], a.src[3 * i + 2], m);
         acc[1] += 1.0;
     }
     block_sum(acc, red, a.partials + blockIdx.x, gridDim.x);
@@ -1819,13 +1840,15 @@ __global__ __launch_bounds__(kWG) void icp_reject_kernel(RejArgs a)
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     const double thr = a.stat[2];
+    double T[12];
+    rej_transform(a, T);
     for (int64_t i = int64_t(blockIdx.x) * kWG + threadIdx.x; i < a.n;
          i += int64_t(gridDim.x) * kWG) {
         float4 mp;
         bool keep = false;
         if (rej_pair(a, i, mp)) {
             const double X = a.src[3 * i], Y = a.src[3 * i + 1], Z = a.src[3 * i + 2];
-            keep = rej_residual_sq(a, X, Y, Z, mp) <= thr;
+            keep = rej_residual_sq(T, X, Y, Z, mp) <= thr;
             if (keep) {
                 const double s0 = X - a.c[0], s1 = Y - a.c[1], s2 = Z - a.c[2];
                 const double m0 = double(mp.x) - a.c[0], m1 = double(mp.y) - a.c[1],
@@ -2510,7 +2533,7 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
                             const hipEvent_t *timing, uint64_t *done, uint64_t seq,
                             const IcpLoop *loop)
 {
-    if (loop && (sc.lanes > 1 || sc.top_lds || sc.budget != 0 || keep_matches))
+    if (loop && (sc.lanes > 1 || sc.top_lds || sc.budget != 0))
         return hipErrorInvalidValue;  // the device loop runs the one-lane-per-query kernel only
     IcpArgs a{};
     if (loop) {
@@ -2588,9 +2611,10 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
                              const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,
                              double *stat_out, uint8_t *kept, hipStream_t s, uint64_t *done,
-                             uint64_t seq)
+                             uint64_t seq, const IcpLoop *loop)
 {
     RejArgs a{};
+    if (loop) a.rt_dev = loop->state->rt1;
     a.tree = tree_view(t);
     a.src = src;
     a.n = n;
@@ -2610,7 +2634,11 @@ hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, c
     icp_residual_kernel<<<dim3(uint32_t(nb)), kWG, 0, s>>>(a);
     residual_stat_kernel<<<1, kWG, 0, s>>>(a.partials, nb, kk, a.stat);
     icp_reject_kernel<<<dim3(uint32_t(nb)), kWG, 0, s>>>(a);
-    launch_reduce_partials(a.partials, nb, nullptr, 0, sums_out, a.stat, stat_out, done, seq, s);
+    if (loop)
+        launch_icp_loop_step(a.partials, nb, *loop, t.center, s);
+    else
+        launch_reduce_partials(a.partials, nb, nullptr, 0, sums_out, a.stat, stat_out, done, seq,
+                               s);
     return hipGetLastError();
 }
 

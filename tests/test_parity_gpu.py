@@ -319,13 +319,15 @@ def test_scene_icp_align(torch, kdnn):
 
 def test_device_loop_matches_host_loop(torch, kdnn):
     """icp_align keeps the iterations on the device (the step kernel solves with
-    the same code as kdnn_procrustes on the same sums, summed in the same order)
-    unless asked to solve on the host: both must follow the same iterates."""
+    the same code as kdnn_procrustes on the same sums, summed in the same order;
+    with residual rejection both solves of an iteration) unless asked to solve
+    on the host: both must follow the same iterates."""
     for name, p, leaf in [("tiny", synth.tiny(), 8), ("scene", scene(), 16),
                           ("lidar 5", lidar()[5], 16)]:
         tree = kdnn.Tree(p.target, leaf)
         src = dev(torch, p.source)
-        for kw in ({}, {"sort": True}, {"max_dist": 1.0}):
+        for kw in ({}, {"sort": True}, {"max_dist": 1.0}, {"max_dist": 1.0, "reject_k": 3.0},
+                   {"reject_k": 2.5}):
             say("device vs host loop", name, kw)
             d = tree.icp(src, max_iter=p.iters, **kw)
             h = tree.icp(src, max_iter=p.iters, host_loop=True, **kw)
