@@ -384,7 +384,10 @@ size_t icp_batch_workspace_bytes(int32_t B, const int64_t *n);
  *   R_out, t_out      : [B][9] / [B][3], the last solved transforms.
  *   E_hist            : optional [B][max_iter], E_k of each pair.
  *   iters_done        : optional [B].      status_out : optional [B].
- *   flags             : 0 or KDNN_ICP_NO_SORT.
+ *   flags             : 0 or KDNN_ICP_NO_SORT, and KDNN_ICP_HOST_LOOP (solve on the
+ *                       host each iteration; otherwise, for max_iter <= 512, each
+ *                       pair's reduction group solves and advances its loop on the
+ *                       device and the host waits once).
  *   reject            : optional; max_dist only (reject_k > 0 is EINVAL).
  *   ws_dev            : >= icp_batch_workspace_bytes(B, n), 256-byte aligned.
  * A pair whose solve degenerates stops with its last good transform and its

@@ -316,11 +316,12 @@ def icp_batch_workspace(sources_n, device=None):
 
 
 def icp_batch(trees, sources, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
-              workspace=None, stream=None, max_dist=None) -> list:
+              workspace=None, stream=None, max_dist=None, host_loop: bool = False) -> list:
     """Register sources[p] onto trees[p] for every p together (icp_align_batch).
 
     Returns one dict per pair: R, t, E (per iteration), iters and status
-    (0 = OK; a degenerate pair keeps its last good transform).
+    (0 = OK; a degenerate pair keeps its last good transform).  host_loop:
+    solve each iteration on the host (KDNN_ICP_HOST_LOOP).
     """
     B = len(trees)
     if B != len(sources) or B < 1:
@@ -343,7 +344,8 @@ def icp_batch(trees, sources, R0=None, t0=None, max_iter: int = 30, eps: float =
         t0a.ctypes.data_as(_lib.c_dp) if t0a is not None else None,
         int(max_iter), float(eps), R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
         E.ctypes.data_as(_lib.c_dp), it.ctypes.data_as(ctypes.POINTER(_lib.c_i32)),
-        st.ctypes.data_as(ctypes.POINTER(_lib.c_i32)), 0, _reject(max_dist, 0.0),
+        st.ctypes.data_as(ctypes.POINTER(_lib.c_i32)),
+        _lib.KDNN_ICP_HOST_LOOP if host_loop else 0, _reject(max_dist, 0.0),
         _ptr(ws), ws.numel(), _stream(stream))
     if status not in (_lib.KDNN_OK, _lib.KDNN_EDEGENERATE):
         _lib.check(status, "icp_align_batch")

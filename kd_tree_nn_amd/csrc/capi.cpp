@@ -322,6 +322,103 @@ kdnn_status icp_align_on_device(kdnn_tree *mt, const float *src_dev, int64_t n, 
     return KDNN_OK;
 }
 
+// icp_align_batch with the iterations kept on the device: each pair's state
+// and record live in the workspace; per iteration the batched search and, per
+// pair, a one-group step that reduces, solves and advances that pair's loop
+// (converged or failed pairs' work-groups return at once).  The host waits
+// once (every 4 iterations when eps > 0, stopping when every pair has).
+kdnn_status batch_on_device(int32_t B, const kdnn_tree *const *trees, const float *const *src_dev,
+                            const int64_t *n, const std::vector<double> &R,
+                            const std::vector<double> &t, int32_t max_iter, double eps,
+                            double *R_out, double *t_out, double *E_hist, int32_t *iters_done,
+                            kdnn_status *status_out, const kdnn_icp_reject *reject, void *ws_dev,
+                            int32_t total, const std::vector<int32_t> &part, hipStream_t stream)
+{
+    constexpr int32_t kChunk = 4;
+    constexpr size_t kHead = offsetof(IcpLoopOut, E);
+    // strides of the workspace's state and record arrays (256-byte aligned)
+    const size_t sb = (sizeof(IcpLoopState) + 255) & ~size_t(255);
+    const size_t rb = (sizeof(IcpLoopOut) + 255) & ~size_t(255);
+    const size_t row = kHead + size_t(max_iter) * sizeof(double);
+    // pinned staging: B states, then B record rows
+    struct Pinned {
+        char *h = nullptr;
+        hipStream_t s = nullptr;
+        ~Pinned()
+        {
+            if (h) {
+                (void)hipStreamSynchronize(s);
+                (void)hipHostFree(h);
+            }
+        }
+    } pin;
+    pin.s = stream;
+    hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&pin.h), size_t(B) * (sb + row),
+                                 hipHostMallocDefault);
+    if (e != hipSuccess)
+        return fail(KDNN_ENOMEM, std::string("icp_align_batch: hipHostMalloc: ") + hipGetErrorString(e));
+    std::memset(pin.h, 0, size_t(B) * (sb + row));
+    for (int32_t p = 0; p < B; ++p) {
+        IcpLoopState *st = reinterpret_cast<IcpLoopState *>(pin.h + size_t(p) * sb);
+        std::memcpy(st->rt, &R[9 * size_t(p)], 9 * sizeof(double));
+        std::memcpy(st->rt + 9, &t[3 * size_t(p)], 3 * sizeof(double));
+    }
+    if ((e = hipMemcpyAsync(batch_loop_state(ws_dev, total, 0), pin.h, size_t(B) * sb,
+                            hipMemcpyHostToDevice, stream)) != hipSuccess ||
+        (e = launch_batch_loop_init(B, ws_dev, total, stream)) != hipSuccess)
+        return hip_fail(e, "icp_align_batch: loop start");
+    const float bound2 = reject ? bound_of(reject->max_dist) : INFINITY;
+    std::vector<BatchJob> jobs;
+    for (int32_t k = 0; k < max_iter; ++k) {
+        for (int32_t c0 = 0; c0 < B; c0 += batch_max_pairs()) {
+            jobs.clear();
+            for (int32_t p = c0; p < B && p < c0 + batch_max_pairs(); ++p) {
+                BatchJob J{&trees[p]->dev, src_dev[p], n[p], &R[9 * size_t(p)],
+                           &t[3 * size_t(p)], part[p], nullptr, nullptr};
+                J.st = batch_loop_state(ws_dev, total, p);
+                J.out = batch_loop_out(ws_dev, total, B, p);
+                jobs.push_back(J);
+            }
+            if ((e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total,
+                                      stream, 0, k, eps)) != hipSuccess)
+                return hip_fail(e, "icp_align_batch: launch");
+        }
+        if (eps > 0.0 && (k + 1) % kChunk == 0 && k + 1 < max_iter) {
+            if ((e = hipMemcpyAsync(pin.h, batch_loop_state(ws_dev, total, 0), size_t(B) * sb,
+                                    hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+                (e = hipStreamSynchronize(stream)) != hipSuccess)
+                return hip_fail(e, "icp_align_batch: synchronize");
+            bool all = true;
+            for (int32_t p = 0; p < B; ++p)
+                all = all && reinterpret_cast<const IcpLoopState *>(pin.h + size_t(p) * sb)->stop;
+            if (all) break;
+        }
+    }
+    char *rec = pin.h + size_t(B) * sb;
+    if ((e = hipMemcpy2DAsync(rec, row, batch_loop_out(ws_dev, total, B, 0), rb, row, size_t(B),
+                              hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+        (e = hipStreamSynchronize(stream)) != hipSuccess)
+        return hip_fail(e, "icp_align_batch: synchronize");
+    bool any_failed = false;
+    for (int32_t p = 0; p < B; ++p) {
+        const IcpLoopOut *out = reinterpret_cast<const IcpLoopOut *>(rec + size_t(p) * row);
+        std::memcpy(R_out + 9 * size_t(p), out->rt, 9 * sizeof(double));
+        std::memcpy(t_out + 3 * size_t(p), out->rt + 9, 3 * sizeof(double));
+        if (iters_done) iters_done[p] = int32_t(out->iters);
+        const int64_t failed = out->fail_iter;
+        const int64_t recorded = failed >= 0 ? failed + 1 : out->iters;
+        if (E_hist)
+            for (int64_t k = 0; k < recorded && k < max_iter; ++k)
+                E_hist[size_t(p) * max_iter + size_t(k)] = out->E[k];
+        if (failed >= 0) {
+            if (status_out) status_out[p] = KDNN_EDEGENERATE;
+            any_failed = true;
+        }
+    }
+    if (any_failed) return fail(KDNN_EDEGENERATE, "icp_align_batch: a pair degenerated (status_out)");
+    return KDNN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -933,9 +1030,10 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         return fail(KDNN_EINVAL, "icp_align_batch: B < 1 or a null array");
     if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align_batch: max_iter < 0");
     if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align_batch: eps must be >= 0");
-    if (flags & ~KDNN_ICP_NO_SORT)
-        return fail(KDNN_EINVAL, "icp_align_batch: only KDNN_ICP_NO_SORT is accepted "
-                                 "(pairs are traversed in their given order, one lane each)");
+    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_ICP_HOST_LOOP))
+        return fail(KDNN_EINVAL, "icp_align_batch: only KDNN_ICP_NO_SORT and KDNN_ICP_HOST_LOOP "
+                                 "are accepted (pairs are traversed in their given order, one "
+                                 "lane each)");
     kdnn_status st = check_reject(reject, "icp_align_batch");
     if (st != KDNN_OK) return st;
     if (reject && reject->reject_k > 0.0)
@@ -974,6 +1072,10 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         part[p] = total;
         total += batch_groups(n[p]);
     }
+    if (!(flags & KDNN_ICP_HOST_LOOP) && max_iter <= kLoopMaxIter)
+        return batch_on_device(B, trees, src_dev, n, R, t, max_iter, eps, R_out, t_out, E_hist,
+                               iters_done, status_out, reject, ws_dev, total, part, stream);
+
     // host slot the kernels write the sums into
     // (on every return the stream is drained first: launches of the current
     // iteration may still be writing into the buffer)

@@ -226,12 +226,21 @@ struct BatchJob {
     int32_t part;     // first partial column
     double *sums;     // [KDNN_SUMS_DOUBLES] out (device-visible)
     uint64_t *done;   // null, or a device-visible word the reduction sets to seq
+    IcpLoopState *st = nullptr;  // device loop: the pair's state (R, t unused), else null
+    IcpLoopOut *out = nullptr;   // device loop: the pair's record
 };
 int batch_max_pairs();
 int32_t batch_groups(int64_t n);  // work-groups (partial columns) of an n-point pair
+// Workspace: the partial columns, then B loop states, then B loop records.
 size_t icp_batch_ws_bytes(int32_t B, const int64_t *n);
+size_t batch_loop_bytes(int32_t B);
+IcpLoopState *batch_loop_state(void *ws, int32_t total, int32_t p);
+IcpLoopOut *batch_loop_out(void *ws, int32_t total, int32_t B, int32_t p);
+// Each pair's record header from its state (states written by the host first).
+hipError_t launch_batch_loop_init(int32_t B, void *ws, int32_t total, hipStream_t s);
+// iter / eps: the device loop's (jobs with st set: the reduction also solves).
 hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void *ws, int32_t total,
-                            hipStream_t s, uint64_t seq = 0);
+                            hipStream_t s, uint64_t seq = 0, int32_t iter = 0, double eps = 0.0);
 
 // Residual rejection of the pairs the last fused launch stored (keep_matches):
 // sums of the pairs with r^2 <= kk * mean r^2 under (R, t).

@@ -1349,37 +1349,20 @@ __global__ __launch_bounds__(64) void icp_loop_init_kernel(IcpLoopState *st, Icp
     st->mse = 0.0;
 }
 
-template <int WG>
-__global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int32_t np,
-                                                           IcpLoopState *st, IcpLoopOut *out,
-                                                           int32_t k, double eps, Rt12 c,
-                                                           int32_t mode)
+// One lane: record E_k and the transform used, solve, and advance the loop
+// state (mode as IcpLoop::mode).  tot: the iteration's (or the kept pairs')
+// 17 sums; rt_used: the transform this iteration searched with.
+__device__ __forceinline__ void loop_finish(const double *tot, IcpLoopState *st, IcpLoopOut *out,
+                                            int32_t k, double eps, const double *c, int32_t mode,
+                                            const double (&rt_used)[12])
 {
-    __shared__ double red[(WG / 64) * kS];
-    __shared__ double tot[kS];
-    // the state's words are read up front, in the shadow of the partials'
-    // loads (a stopped loop sums stale partials and then discards them)
-    const uint32_t stopped = st->stop;
-    double rt_used[12];
-    if (threadIdx.x == 0)
-        for (int j = 0; j < 12; ++j) rt_used[j] = st->rt[j];
-    double acc[kS];
-#pragma unroll
-    for (int j = 0; j < kS; ++j) acc[j] = 0.0;
-    for (int32_t g = threadIdx.x; g < np; g += WG) {
-#pragma unroll
-        for (int j = 0; j < kS; ++j) acc[j] += p[int64_t(j) * np + g];
-    }
-    block_sum_n<WG>(acc, red, tot, 1);
-    __syncthreads();
-    if (threadIdx.x != 0 || stopped) return;
     const double n = tot[16], E = tot[15];
     if (mode != 2 && k >= 0 && k < kLoopMaxIter) {  // the host never launches beyond the record
         out->E[k] = E;
         for (int j = 0; j < 12; ++j) out->rt_hist[k][j] = rt_used[j];
     }
     double R[9], t[3];
-    const int32_t rs = rigid_from_sums(&tot[0], &tot[3], &tot[6], n, c.v, R, t);
+    const int32_t rs = rigid_from_sums(&tot[0], &tot[3], &tot[6], n, c, R, t);
     if (rs != kRigidOk) {
         out->status = rs;
         out->fail_iter = k;
@@ -1412,6 +1395,33 @@ __global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int3
         }
     }
     st->prev_mse = mse;
+}
+
+template <int WG>
+__global__ __launch_bounds__(WG) void icp_loop_step_kernel(const double *p, int32_t np,
+                                                           IcpLoopState *st, IcpLoopOut *out,
+                                                           int32_t k, double eps, Rt12 c,
+                                                           int32_t mode)
+{
+    __shared__ double red[(WG / 64) * kS];
+    __shared__ double tot[kS];
+    // the state's words are read up front, in the shadow of the partials'
+    // loads (a stopped loop sums stale partials and then discards them)
+    const uint32_t stopped = st->stop;
+    double rt_used[12];
+    if (threadIdx.x == 0)
+        for (int j = 0; j < 12; ++j) rt_used[j] = st->rt[j];
+    double acc[kS];
+#pragma unroll
+    for (int j = 0; j < kS; ++j) acc[j] = 0.0;
+    for (int32_t g = threadIdx.x; g < np; g += WG) {
+#pragma unroll
+        for (int j = 0; j < kS; ++j) acc[j] += p[int64_t(j) * np + g];
+    }
+    block_sum_n<WG>(acc, red, tot, 1);
+    __syncthreads();
+    if (threadIdx.x != 0 || stopped) return;
+    loop_finish(tot, st, out, k, eps, c.v, mode, rt_used);
 }
 
 hipError_t launch_icp_loop_init(IcpLoopState *state, IcpLoopOut *out, const double *R0,
@@ -1652,6 +1662,8 @@ struct BatchPair {
     int32_t part;     // first partial column of this pair
     double *sums;     // [kS] out
     uint64_t *done;   // null, or a word set to the launch's sequence number after the sums
+    IcpLoopState *st; // device loop: the pair's state ((R, t) from here), else null
+    IcpLoopOut *out;  // device loop: the pair's record
 };
 
 struct BatchArgs {
@@ -1661,6 +1673,8 @@ struct BatchArgs {
     uint64_t init;    // bound key
     double *partials; // [kS][total]
     uint64_t seq;     // value stored into each pair's done word
+    int32_t iter;     // device loop: iteration index
+    double eps;       // device loop: convergence threshold
 };
 
 #ifndef KDNN_BATCH_QUORUM
@@ -1677,6 +1691,7 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
     const int kx = (kNumXcd - pi + a.B - 1) / a.B;  // XCDs serving this pair
     const int32_t j = int32_t(blockIdx.x / uint32_t(kNumXcd)) * kx + x / a.B;
     if (j >= P.nb) return;  // uniform over the work-group
+    if (P.st && P.st->stop) return;  // the pair's device loop has stopped (uniform)
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
@@ -1687,12 +1702,16 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
     double X = 0.0, Y = 0.0, Z = 0.0;
     float qx = 0.0f, qy = 0.0f, qz = 0.0f;
     if (own) {
-        X = P.src[3 * i];
-        Y = P.src[3 * i + 1];
-        Z = P.src[3 * i + 2];
-        qx = rigid_row(P.R[0], P.R[1], P.R[2], P.t[0], X, Y, Z);
-        qy = rigid_row(P.R[3], P.R[4], P.R[5], P.t[1], X, Y, Z);
-        qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
+        if (P.st) {
+            icp_query_dev(P.st->rt, P.src, i, X, Y, Z, qx, qy, qz);
+        } else {
+            X = P.src[3 * i];
+            Y = P.src[3 * i + 1];
+            Z = P.src[3 * i + 2];
+            qx = rigid_row(P.R[0], P.R[1], P.R[2], P.t[0], X, Y, Z);
+            qy = rigid_row(P.R[3], P.R[4], P.R[5], P.t[1], X, Y, Z);
+            qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
+        }
     }
     wave_search<false, true, CH>(P.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
                                  nullptr, nullptr, xfer + (threadIdx.x & ~63u),
@@ -1718,16 +1737,30 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
 }
 
 // Work-group p: the sums of pair p from its work-groups' partial columns.
+// Device loop (P.st set): the pair's step instead -- sums into LDS, then the
+// rigid solve and the loop state on one lane, as icp_loop_step_kernel.
 __global__ __launch_bounds__(kWG) void batch_reduce_kernel(BatchArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
+    __shared__ double tot[kS];
     const BatchPair &P = a.p[blockIdx.x];
+    const uint32_t stopped = P.st ? P.st->stop : 0u;
+    double rt_used[12];
+    if (P.st && threadIdx.x == 0)
+        for (int j = 0; j < 12; ++j) rt_used[j] = P.st->rt[j];
     double acc[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) acc[c] = 0.0;
     for (int32_t g = threadIdx.x; g < P.nb; g += kWG) {
 #pragma unroll
         for (int c = 0; c < kS; ++c) acc[c] += a.partials[int64_t(c) * a.total + P.part + g];
+    }
+    if (P.st) {
+        block_sum(acc, red, tot, 1);
+        __syncthreads();
+        if (threadIdx.x == 0 && !stopped)
+            loop_finish(tot, P.st, P.out, a.iter, a.eps, P.c, 0, rt_used);
+        return;
     }
     block_sum(acc, red, P.sums, 1);
     if (P.done) {  // sums visible at system scope first (polled from the host)
@@ -2650,14 +2683,63 @@ size_t icp_batch_ws_bytes(int32_t B, const int64_t *n)
 {
     int64_t total = 0;
     for (int32_t p = 0; p < B; ++p) total += batch_groups(n[p]);
-    return align256(size_t(kS) * size_t(total) * 8);
+    return align256(size_t(kS) * size_t(total) * 8) + batch_loop_bytes(B);
+}
+
+size_t batch_loop_bytes(int32_t B)
+{
+    return size_t(B) * (align256(sizeof(IcpLoopState)) + align256(sizeof(IcpLoopOut)));
+}
+
+IcpLoopState *batch_loop_state(void *ws, int32_t total, int32_t p)
+{
+    return reinterpret_cast<IcpLoopState *>(static_cast<char *>(ws) +
+                                            align256(size_t(kS) * size_t(total) * 8) +
+                                            size_t(p) * align256(sizeof(IcpLoopState)));
+}
+
+IcpLoopOut *batch_loop_out(void *ws, int32_t total, int32_t B, int32_t p)
+{
+    return reinterpret_cast<IcpLoopOut *>(static_cast<char *>(ws) +
+                                          align256(size_t(kS) * size_t(total) * 8) +
+                                          size_t(B) * align256(sizeof(IcpLoopState)) +
+                                          size_t(p) * align256(sizeof(IcpLoopOut)));
+}
+
+// One lane per pair: each record's header from its state (set by the host).
+__global__ __launch_bounds__(64) void batch_loop_init_kernel(int32_t B, IcpLoopState *st0,
+                                                             IcpLoopOut *out0, size_t st_stride,
+                                                             size_t out_stride)
+{
+    const int32_t p = int32_t(blockIdx.x * 64 + threadIdx.x);
+    if (p >= B) return;
+    const IcpLoopState *st = reinterpret_cast<const IcpLoopState *>(
+        reinterpret_cast<const char *>(st0) + size_t(p) * st_stride);
+    IcpLoopOut *out = reinterpret_cast<IcpLoopOut *>(reinterpret_cast<char *>(out0) +
+                                                     size_t(p) * out_stride);
+    for (int k = 0; k < 12; ++k) out->rt[k] = st->rt[k];
+    out->iters = 0;
+    out->status = 0;
+    out->fail_iter = -1;
+    out->fail_phase = 0;
+    out->stopped = 0;
+}
+
+hipError_t launch_batch_loop_init(int32_t B, void *ws, int32_t total, hipStream_t s)
+{
+    batch_loop_init_kernel<<<dim3(uint32_t((B + 63) / 64)), 64, 0, s>>>(
+        B, batch_loop_state(ws, total, 0), batch_loop_out(ws, total, B, 0),
+        align256(sizeof(IcpLoopState)), align256(sizeof(IcpLoopOut)));
+    return hipGetLastError();
 }
 
 hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void *ws, int32_t total,
-                            hipStream_t s, uint64_t seq)
+                            hipStream_t s, uint64_t seq, int32_t iter, double eps)
 {
     BatchArgs a{};
     a.seq = seq;
+    a.iter = iter;
+    a.eps = eps;
     a.B = B;
     a.total = total;
     a.init = host_bound_key(bound2);
@@ -2682,6 +2764,8 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
         P.part = J.part;
         P.sums = J.sums;
         P.done = J.done;
+        P.st = J.st;
+        P.out = J.out;
         const int kx = (kNumXcd - p + B - 1) / B;
         const int64_t per_xcd = (P.nb + kx - 1) / kx;
         slots = per_xcd > slots ? per_xcd : slots;

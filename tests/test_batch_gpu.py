@@ -114,6 +114,7 @@ def test_batch_degenerate_pair_and_errors(torch, kdnn):
         R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp), None, None, None, flags,
         rej, ws.data_ptr(), wsz, None)
     assert args(_lib.lanes_flag(4), None, ws.numel()) == _lib.KDNN_EINVAL  # a schedule flag
+    assert args(0, None, ws.numel() - 256) == _lib.KDNN_EINVAL              # no room for the loop
     assert args(0, ctypes.byref(_lib.IcpReject(1.0, 3.0)), ws.numel()) == _lib.KDNN_EINVAL
     assert args(0, None, 16) == _lib.KDNN_EINVAL                           # workspace too small
     assert args(0, None, ws.numel()) == _lib.KDNN_OK
@@ -129,3 +130,22 @@ def test_batch_leaf8_trees(torch, kdnn):
     res = kdnn.icp_batch(trees, [dev(torch, p.source) for p in lp], max_iter=10)
     for k, (p, tr, b) in enumerate(zip(lp, trees, res)):
         _close_to_single(b, _single(kdnn, torch, tr, p.source, 10), f"leaf-8 pair {k}")
+
+
+def test_batch_device_loop_matches_host_loop(torch, kdnn):
+    """The batched call keeps its iterations on the device (per pair: reduction,
+    solve and loop state in one group) unless asked to solve on the host; same
+    kernels, same sums, same solve code: the same iterates."""
+    lp = lidar()[:5]
+    tiny = synth.tiny()
+    trees = [kdnn.Tree(p.target, 16) for p in lp] + [kdnn.Tree(tiny.target, 8)]
+    srcs = [dev(torch, p.source) for p in lp] + [dev(torch, tiny.source)]
+    for kw in ({"max_iter": 30}, {"max_iter": 40, "eps": 1e-6}, {"max_iter": 12, "max_dist": 1.0}):
+        say("batch device vs host loop", kw)
+        d = kdnn.icp_batch(trees, srcs, **kw)
+        h = kdnn.icp_batch(trees, srcs, host_loop=True, **kw)
+        for k, (a, b) in enumerate(zip(d, h)):
+            assert a["status"] == b["status"] == 0 and a["iters"] == b["iters"], (kw, k)
+            np.testing.assert_allclose(a["E"], b["E"], rtol=1e-12, err_msg=f"{kw} pair {k}")
+            assert np.linalg.norm(a["R"] - b["R"]) <= 1e-12, (kw, k)
+            assert np.max(np.abs(a["t"] - b["t"])) <= 1e-12, (kw, k)
