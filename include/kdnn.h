@@ -369,12 +369,13 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
                       size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace icp_align_batch needs for B pairs of n[p] source
- * points.  0 if B < 1, n is NULL or some n[p] < 1. */
+ * points (partial sums, and each pair's loop state and record, ~54 KB).
+ * 0 if B < 1, n is NULL or some n[p] < 1. */
 size_t icp_batch_workspace_bytes(int32_t B, const int64_t *n);
 
 /* B independent registrations advanced together (article §3.4: consecutive
- * frames kept in flight at once so the GPU stays busy and one host round trip
- * per iteration serves all of them).  Pair p registers src_dev[p] (n[p]
+ * frames kept in flight at once so the GPU stays busy; here no host round trip
+ * per iteration at all, unless KDNN_ICP_HOST_LOOP).  Pair p registers src_dev[p] (n[p]
  * points) onto trees[p] exactly as icp_align does with flags
  * KDNN_ICP_NO_SORT and one lane per query: same iteration, same convergence
  * rule per pair, and the same max_dist bound.  Each launch carries up to 8
