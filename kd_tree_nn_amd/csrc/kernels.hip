@@ -718,9 +718,11 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
             if (w.i < t.first_leaf) {
                 // the two children's boxes: one 48-byte run, three loads
                 const uint32_t i = w.i;
-                const float4 P0 = t.boxes[3 * i];
-                const float4 P1 = t.boxes[3 * i + 1];
-                const float4 P2 = t.boxes[3 * i + 2];
+                // one address, the three loads at immediate offsets 0, 16, 32
+                const float4 *const pb = t.boxes + 3 * size_t(i);
+                const float4 P0 = pb[0];
+                const float4 P1 = pb[1];
+                const float4 P2 = pb[2];
                 const float4 A0 = P0;
                 const float4 B0 = make_float4(P1.x, P1.y, 0.0f, 0.0f);
                 const float4 A1 = make_float4(P1.z, P1.w, P2.x, P2.y);
