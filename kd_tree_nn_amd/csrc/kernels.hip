@@ -595,6 +595,7 @@ __device__ __forceinline__ void task_finish(WaveTask &w, unsigned long long *oke
 // Hand-over round: idle lanes take the shallowest pending subtree of busy
 // lanes, paired by rank.  Every lane of the wave must call it together.
 // xfer: this wave's 64-entry LDS table (donor rank -> donor lane).
+template <bool QL = false>
 __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
                                               const unsigned long long *okey, uint32_t *xfer,
                                               uint32_t min_idle = 1u)
@@ -635,15 +636,19 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
 #endif
     const uint32_t tv = uint32_t(__shfl(int(gv), src, 64));
     const float tlb = __shfl(glb, src, 64);
-    const float tqx = __shfl(w.qx, src, 64);
-    const float tqy = __shfl(w.qy, src, 64);
-    const float tqz = __shfl(w.qz, src, 64);
     const uint32_t town = uint32_t(__shfl(int(w.owner), src, 64));
+    if constexpr (!QL) {  // QL: the query's coordinates are read from LDS by owner
+        const float tqx = __shfl(w.qx, src, 64);
+        const float tqy = __shfl(w.qy, src, 64);
+        const float tqz = __shfl(w.qz, src, 64);
+        if (takes) {
+            w.qx = tqx;
+            w.qy = tqy;
+            w.qz = tqz;
+        }
+    }
     if (takes) {
         w.owner = town;
-        w.qx = tqx;
-        w.qy = tqy;
-        w.qz = tqz;
         w.pend = 0u;
         w.key = okey[town];
         w.i = enters(tlb, key_dist(w.key)) ? tv : kDone;
@@ -677,13 +682,19 @@ __device__ __forceinline__ float *lbs_array()
 // independent of which queries share a wave).
 // CH: leaf points loaded per batch (kLeafChunk, or kLeafChunkSmall for a tree
 // whose leaves hold at most that many: fewer registers, more resident waves).
-template <bool STATS, bool BALANCE = true, int CH = kLeafChunk>
+// QL: the queries' coordinates live in qpool (LDS, one float4 per owner slot)
+// and each step reads its task's from there, instead of every task carrying
+// them in registers: a hand-over moves the owner only, and the loop carries
+// three registers fewer (which the compiler otherwise merges by copies).
+template <bool STATS, bool BALANCE = true, int CH = kLeafChunk, bool QL = false>
 __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
                                             float oqz, uint64_t init, float *lbs,
                                             unsigned long long *okey, uint32_t *ocn,
-                                            uint32_t *ocp, uint32_t *xfer, uint32_t quorum = 64u)
+                                            uint32_t *ocp, uint32_t *xfer, uint32_t quorum = 64u,
+                                            float4 *qpool = nullptr)
 {
     okey[threadIdx.x] = init;
+    if constexpr (QL) qpool[threadIdx.x] = make_float4(oqx, oqy, oqz, 0.0f);
     if (STATS) {
         ocn[threadIdx.x] = 0u;
         ocp[threadIdx.x] = 0u;
@@ -728,8 +739,15 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                 const float4 A1 = make_float4(P1.z, P1.w, P2.x, P2.y);
                 const float4 B1 = make_float4(P2.z, P2.w, 0.0f, 0.0f);
                 if (STATS) w.cn += 2;
-                const float l0 = box_lb(w.qx, w.qy, w.qz, A0, B0);
-                const float l1 = box_lb(w.qx, w.qy, w.qz, A1, B1);
+                float qx = w.qx, qy = w.qy, qz = w.qz;
+                if constexpr (QL) {
+                    const float4 q = qpool[w.owner];
+                    qx = q.x;
+                    qy = q.y;
+                    qz = q.z;
+                }
+                const float l0 = box_lb(qx, qy, qz, A0, B0);
+                const float l1 = box_lb(qx, qy, qz, A1, B1);
                 const bool swap = l1 < l0;
                 const float lf = swap ? l1 : l0, ls = swap ? l0 : l1;
                 const float best = key_dist(w.key);
@@ -743,7 +761,8 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                 }
             }
             task_finish<STATS>(w, okey, ocn, ocp);
-            if (BALANCE && KDNN_P1_HANDOVER) task_handover(w, lbs, okey, xfer, KDNN_P1_MIN_IDLE);
+            if (BALANCE && KDNN_P1_HANDOVER)
+                task_handover<QL>(w, lbs, okey, xfer, KDNN_P1_MIN_IDLE);
         }
         // Phase 2: leaves, then share the improved best of the query.
         if (w.i != kDone && w.i >= t.first_leaf) {
@@ -751,6 +770,13 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
             leaf_range(t, w.i, begin, last, end);
             uint32_t k0 = uint32_t(begin);
             uint64_t key = w.key;
+            float qx = w.qx, qy = w.qy, qz = w.qz;
+            if constexpr (QL) {
+                const float4 q = qpool[w.owner];
+                qx = q.x;
+                qy = q.y;
+                qz = q.z;
+            }
             do {
                 const float4 *pc = t.pts + k0;
                 float4 p[CH];
@@ -758,9 +784,9 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                 for (int c = 0; c < CH; ++c) p[c] = pc[c];
 #pragma unroll
                 for (int c = 0; c < CH; ++c) {
-                    const float dx = p[c].x - w.qx;
-                    const float dy = p[c].y - w.qy;
-                    const float dz = p[c].z - w.qz;
+                    const float dx = p[c].x - qx;
+                    const float dy = p[c].y - qy;
+                    const float dz = p[c].z - qz;
                     const float dd = (dx * dx + dy * dy) + dz * dz;
                     const uint64_t k = nn_key(dd, __float_as_uint(p[c].w));
                     key = k < key ? k : key;
@@ -774,7 +800,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
         }
         task_finish<STATS>(w, okey, ocn, ocp);
         if (__ballot(w.owner != kNoOwner) == 0) break;
-        if (BALANCE) task_handover(w, lbs, okey, xfer);
+        if (BALANCE) task_handover<QL>(w, lbs, okey, xfer);
     }
 }
 
@@ -1451,13 +1477,21 @@ static void launch_icp_loop_step(const double *p, int32_t np, const IcpLoop &L,
 
 // Single pass, one kernel: transform, search (balanced wave search for G = 1,
 // G lanes per point otherwise) and the fp64 reduction.
-// Registers: the reduce-scatter's 17 live sums would take the 16-point kernel
-// to 97 VGPRs (4 waves per SIMD); held to 5 waves, as the search alone allows.
+// Occupancy: the one-lane-per-query kernels hold the queries' coordinates in
+// LDS (wave_search QL), 36 KB per group with the 16-point kernel's static
+// bound array, so 4 groups per CU (one-round launches use at most 3); the
+// registers are held to what that occupancy allows.  The 8-point kernels
+// (bound array sized to the tree) keep 5 waves per SIMD: the reduce-scatter's
+// 17 live sums would otherwise take them past the register budget of 5.
+#ifndef KDNN_QLDS
+#define KDNN_QLDS 1
+#endif
 #ifndef KDNN_FUSED_WPE
 #define KDNN_FUSED_WPE 5
 #endif
 template <int G, int CH = kLeafChunk>
-__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(KDNN_FUSED_WPE))) void
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(
+    G == 1 && CH == kLeafChunk && KDNN_QLDS ? 4 : KDNN_FUSED_WPE))) void
 icp_fused_kernel(IcpArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
@@ -1471,6 +1505,7 @@ icp_fused_kernel(IcpArgs a)
         float *const lbs = lbs_array<CH == kLeafChunkSmall>();
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t xfer[kWG];
+        __shared__ float4 qpool[KDNN_QLDS ? kWG : 1];
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         if (a.stop && *a.stop) return;  // device loop already stopped (uniform)
         if (lane == 63) {
@@ -1492,9 +1527,11 @@ icp_fused_kernel(IcpArgs a)
                 else
                     icp_query(a, i, X, Y, Z, qx, qy, qz);
             }
-            wave_search<false, true, CH>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
-                                         nullptr, nullptr, xfer + (threadIdx.x & ~63u),
-                               wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u);
+            wave_search<false, true, CH, KDNN_QLDS>(a.tree, own, qx, qy, qz, a.init,
+                                                    lbs + threadIdx.x, okey, nullptr, nullptr,
+                                                    xfer + (threadIdx.x & ~63u),
+                                                    wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u,
+                                                    qpool);
             double acc[kS];
 #pragma unroll
             for (int c = 0; c < kS; ++c) acc[c] = 0.0;
