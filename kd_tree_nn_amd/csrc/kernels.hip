@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -193,10 +194,12 @@ __device__ __forceinline__ float box_lb(float qx, float qy, float qz, const floa
     return (gx * gx + gy * gy) + gz * gz;
 }
 
-__device__ __forceinline__ bool enters(float lb, float best)
-{
-    return (lb <= best) & (lb < INFINITY);
-}
+// A search's best distance starts finite (the largest float when there is no
+// bound, see host_bound_key), so a subtree whose bound overflowed to +inf is
+// never entered; that is exact: every fp32 point distance in such a box is
+// +inf as well (the rounding is monotone), and a point at +inf is never a
+// match.
+__device__ __forceinline__ bool enters(float lb, float best) { return lb <= best; }
 
 __device__ __forceinline__ uint32_t near_child(uint32_t i, const float4 &B, float qx, float qy,
                                                float qz)
@@ -2520,10 +2523,15 @@ static void launch_nn_two_pass(const NnArgs &a, bool stats, void *twopass, hipSt
     }
 }
 
+// The start key of a search under the squared-distance bound bound2: no bound
+// (+inf) starts from the largest float instead, which accepts every finite
+// distance as +inf would (a point at +inf is no match either way) and lets
+// enters() drop its own +inf test.
 static uint64_t host_bound_key(float bound2)
 {
+    const float b = bound2 < FLT_MAX ? bound2 : FLT_MAX;
     uint32_t bits;
-    std::memcpy(&bits, &bound2, 4);
+    std::memcpy(&bits, &b, 4);
     return (uint64_t(bits) << 32) | 0xFFFFFFFFull;
 }
 
