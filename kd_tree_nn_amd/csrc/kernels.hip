@@ -548,6 +548,9 @@ constexpr uint32_t kNoOwner = 0xFFFFFFFFu;
 #ifndef KDNN_XFER_LDS
 #define KDNN_XFER_LDS 1
 #endif
+#ifndef KDNN_QLDS
+#define KDNN_QLDS 1  // query coordinates in LDS (wave_search QL) where the kernel allows
+#endif
 #ifndef KDNN_P1_MIN_IDLE
 #define KDNN_P1_MIN_IDLE 16
 #endif
@@ -837,7 +840,9 @@ __device__ __forceinline__ void search_query(const TreeView &t, float qx, float 
 // One query per lane (G = 1: the balanced wave search) or G lanes per query.
 // A block handles kWG / G queries per sweep; the loop bound is uniform over the
 // block so a wave's (or group's) lanes always stay together.
-template <int G, bool STATS, int CH = kLeafChunk>
+// QL: the query coordinates in LDS (wave_search QL); more LDS per group, so
+// used for one-round launches only, where the groups fit anyway.
+template <int G, bool STATS, int CH = kLeafChunk, bool QL = false>
 __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
 {
     constexpr int QPB = kWG / G;
@@ -848,6 +853,7 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t ocn[STATS ? kWG : 1], ocp[STATS ? kWG : 1];
         __shared__ uint32_t xfer[kWG];
+        __shared__ float4 qpool[QL ? kWG : 1];
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         const uint32_t wq = a.wq;
         const int64_t QB = int64_t(kWG / 64) * wq;
@@ -860,9 +866,10 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             const float qy = own ? a.q[3 * i + 1] : 0.0f;
             const float qz = own ? a.q[3 * i + 2] : 0.0f;
             // the instrumented kernel counts the single-lane search of each query
-            wave_search<STATS, !STATS, CH>(a.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
-                                       ocn, ocp, xfer + (threadIdx.x & ~63u),
-                                       wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u);
+            wave_search<STATS, !STATS, CH, QL>(a.tree, own, qx, qy, qz, a.init,
+                                               lbs + threadIdx.x, okey, ocn, ocp,
+                                               xfer + (threadIdx.x & ~63u),
+                                               wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u, qpool);
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
@@ -1486,9 +1493,6 @@ static void launch_icp_loop_step(const double *p, int32_t np, const IcpLoop &L,
 // registers are held to what that occupancy allows.  The 8-point kernels
 // (bound array sized to the tree) keep 5 waves per SIMD: the reduce-scatter's
 // 17 live sums would otherwise take them past the register budget of 5.
-#ifndef KDNN_QLDS
-#define KDNN_QLDS 1
-#endif
 #ifndef KDNN_FUSED_WPE
 #define KDNN_FUSED_WPE 5
 #endif
@@ -2359,9 +2363,9 @@ static size_t lbs_bytes(int32_t depth)
 template <typename K>
 static int64_t resident_groups(K kernel, int slot, int32_t depth, int64_t *cus_out = nullptr)
 {
-    // slots 2, 3: the 8-point kernels, with dynamic LDS
-    const size_t dyn = slot >= 2 ? lbs_bytes(depth) : 0;
-    static std::atomic<int64_t> cache[64][4][kDevMaxDepth + 1];
+    // slots 2, 3, 5: the 8-point kernels, with dynamic LDS (4, 5: nn_kernel QL)
+    const size_t dyn = (slot == 2 || slot == 3 || slot == 5) ? lbs_bytes(depth) : 0;
+    static std::atomic<int64_t> cache[64][6][kDevMaxDepth + 1];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     const int d = depth < 0 ? 0 : (depth > kDevMaxDepth ? kDevMaxDepth : depth);
@@ -2466,10 +2470,16 @@ static void launch_nn_g(NnArgs a, bool stats, float bound2, hipStream_t s)
     }
     if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
     const size_t lds = G == 1 && CH == kLeafChunkSmall ? lbs_bytes(a.tree.depth) : 0;
-    if (stats)
+    if (stats) {
         nn_kernel<G, true, CH><<<dim3(uint32_t(blocks)), kWG, lds, s>>>(a);
-    else
+    } else if (G == 1 && KDNN_QLDS && a.wq < kQFull &&
+               blocks <= resident_groups(nn_kernel<1, false, CH, true>,
+                                         CH == kLeafChunk ? 4 : 5, a.tree.depth)) {
+        // a one-round launch, still resident at once with the larger LDS
+        nn_kernel<1, false, CH, true><<<dim3(uint32_t(blocks)), kWG, lds, s>>>(a);
+    } else {
         nn_kernel<G, false, CH><<<dim3(uint32_t(blocks)), kWG, lds, s>>>(a);
+    }
 }
 
 // Persistent LDS launch shape for this device: one work-group per CU and
