@@ -551,6 +551,17 @@ constexpr uint32_t kNoOwner = 0xFFFFFFFFu;
 #ifndef KDNN_QLDS
 #define KDNN_QLDS 1  // query coordinates in LDS (wave_search QL) where the kernel allows
 #endif
+// Idle lanes that trigger a hand-over inside the internal-node phase: 16 when
+// a wave starts with many idle lanes (fewer than KDNN_P1_Q_SPLIT queries per
+// wave), 24 when it starts (nearly) full.  Measured: Scene ICP (33 per wave)
+// best at 16; the 131k LiDAR frame's fused kernel (43 per wave) 39.9 -> 38.2 us
+// at 24, Skewed 500k (64 per wave) -2.5%, uniform Stress 1M -1.5%.
+#ifndef KDNN_P1_MIN_IDLE_FULL
+#define KDNN_P1_MIN_IDLE_FULL 24
+#endif
+#ifndef KDNN_P1_Q_SPLIT
+#define KDNN_P1_Q_SPLIT 40
+#endif
 #ifndef KDNN_P1_MIN_IDLE
 #define KDNN_P1_MIN_IDLE 16
 #endif
@@ -697,8 +708,9 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                                             float oqz, uint64_t init, float *lbs,
                                             unsigned long long *okey, uint32_t *ocn,
                                             uint32_t *ocp, uint32_t *xfer, uint32_t quorum = 64u,
-                                            float4 *qpool = nullptr)
+                                            float4 *qpool = nullptr, uint32_t wq = 64u)
 {
+    const uint32_t p1_idle = wq < KDNN_P1_Q_SPLIT ? KDNN_P1_MIN_IDLE : KDNN_P1_MIN_IDLE_FULL;
     okey[threadIdx.x] = init;
     if constexpr (QL) qpool[threadIdx.x] = make_float4(oqx, oqy, oqz, 0.0f);
     if (STATS) {
@@ -768,7 +780,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
             }
             task_finish<STATS>(w, okey, ocn, ocp);
             if (BALANCE && KDNN_P1_HANDOVER)
-                task_handover<QL>(w, lbs, okey, xfer, KDNN_P1_MIN_IDLE);
+                task_handover<QL>(w, lbs, okey, xfer, p1_idle);
         }
         // Phase 2: leaves, then share the improved best of the query.
         if (w.i != kDone && w.i >= t.first_leaf) {
@@ -869,7 +881,8 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             wave_search<STATS, !STATS, CH, QL>(a.tree, own, qx, qy, qz, a.init,
                                                lbs + threadIdx.x, okey, ocn, ocp,
                                                xfer + (threadIdx.x & ~63u),
-                                               wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u, qpool);
+                                               wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u, qpool,
+                                               wq);
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
@@ -1538,7 +1551,7 @@ icp_fused_kernel(IcpArgs a)
                                                     lbs + threadIdx.x, okey, nullptr, nullptr,
                                                     xfer + (threadIdx.x & ~63u),
                                                     wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u,
-                                                    qpool);
+                                                    qpool, wq);
             double acc[kS];
 #pragma unroll
             for (int c = 0; c < kS; ++c) acc[c] = 0.0;
