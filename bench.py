@@ -686,6 +686,36 @@ def main():
             "R_diff_vs_gpu": float(np.linalg.norm(o["R"] - g["R"])),
         }
         log(f"cpu baseline {regs * ITERS * n / Tc / 1e6:.2f} M queries/s")
+        # context: the oracle's KD-tree query of one iteration's queries on every
+        # host core (threads over query chunks; the C query holds no global
+        # state and ctypes releases the GIL), and its brute force on a sample
+        import concurrent.futures as cf
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        otree = oracle.KDTree(p.target, p.leaf_size)
+        chunks = np.array_split(p.source, threads * 4)
+        t0 = time.perf_counter()
+        otree.query(p.source)
+        Tq1 = time.perf_counter() - t0
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(otree.query, chunks[:threads]))  # warm
+            t0 = time.perf_counter()
+            list(ex.map(otree.query, chunks))
+            Tq = time.perf_counter() - t0
+        ns = 2000
+        t0 = time.perf_counter()
+        oracle.brute_nn(p.target, p.source[:ns])
+        Tb = time.perf_counter() - t0
+        result["cpu_context"] = {
+            "oracle_kd_nn_queries_per_s_all_cores": round(n / Tq),
+            "threads": threads,
+            "oracle_kd_nn_queries_per_s_1_thread": round(n / Tq1),
+            "brute_force_pairs_per_s_1_thread": round(ns * len(p.target) / Tb),
+            "brute_force_one_scene_iteration_s": round(Tb * n / ns, 1),
+            "note": "context only: the oracle's own KD search of one Scene iteration's "
+                    "100k queries split over host threads; brute force timed on 2,000 "
+                    "queries and scaled to 100k x 100k pairs"}
+        log(f"cpu context: {n / Tq / 1e6:.2f} M queries/s on {threads} threads, brute force "
+            f"{Tb * n / ns:.1f} s per Scene iteration")
     print(json.dumps(result), flush=True)
 
 
