@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDNN_VERSION 2
+#define KDNN_VERSION 3  /* 3: KDNN_ICP_HOST_LOOP; icp_align and icp_align_batch iterate on the device */
 
 typedef enum kdnn_status {
     KDNN_OK = 0,
