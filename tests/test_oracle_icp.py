@@ -167,6 +167,7 @@ def test_icp_kd_and_brute_agree():
 
 
 def test_icp_convergence_rule_stops_early():
+    """The stop is at the FIRST iteration where the rule holds, never later."""
     p = synth.tiny()
     full = oracle.icp(p.target, p.source, iters=50, nn="brute")
     early = oracle.icp(p.target, p.source, iters=50, nn="brute", eps=1e-7)
@@ -174,7 +175,76 @@ def test_icp_convergence_rule_stops_early():
     mse = full["E"] / full["n"]
     k = early["iters"] - 1
     assert abs(mse[k] - mse[k - 1]) < 1e-7 and abs(mse[k - 1] - mse[k - 2]) < 1e-7
+    for j in range(2, k):   # no earlier iteration satisfies it
+        assert not (abs(mse[j] - mse[j - 1]) < 1e-7 and abs(mse[j - 1] - mse[j - 2]) < 1e-7), j
     np.testing.assert_array_equal(early["E"], full["E"][:early["iters"]])
+
+
+class _ScriptedTree:
+    """Stands in for the oracle's KD-tree inside oracle.icp: every source point
+    i is matched to target point i at a scripted squared distance, so the mean
+    squared distance of iteration k is exactly script[k] (all values below are
+    exact in fp32, and E / n is exact for n a power of two)."""
+
+    def __init__(self, script):
+        self.script = [np.float32(v) for v in script]
+        self.k = 0
+
+    def query(self, q):
+        d = self.script[self.k]
+        self.k += 1
+        return np.arange(len(q), dtype=np.int32), np.full(len(q), d, np.float32)
+
+
+# 8 non-coplanar points: source == target, so every solve is the identity
+_CUBE = np.array([[x, y, z] for x in (0, 1) for y in (0, 2) for z in (0, 3)], np.float32)
+_D = 2.0 ** -12      # a "small" change
+_EPS = 2.0 ** -10    # eps of the scripted cases
+
+
+def _scripted_icp(script, eps, iters=None):
+    tree = _ScriptedTree(script)
+    res = oracle.icp(_CUBE, _CUBE, iters or len(script), nn="kd", tree=tree, eps=eps)
+    assert tree.k == res["iters"]
+    np.testing.assert_array_equal(res["E"] / res["n"], np.asarray(script[:res["iters"]], np.float32))
+    return res["iters"]
+
+
+@pytest.mark.parametrize("script, expect", [
+    # two small changes in a row at iterations 1 and 2: stop after iteration 2
+    ([1.0, 1.0 - _D, 1.0 - 2 * _D, 0.5, 0.25, 0.125], 3),
+    # a single small change (iteration 2), then a large one (3): no stop there;
+    # two small changes at 4 and 5: stop after iteration 5 and not later
+    ([1.0, 0.5, 0.5 - _D, 0.25, 0.25 - _D, 0.25 - 2 * _D, 0.25 - 3 * _D, 0.25 - 4 * _D], 6),
+    # small, large, small, large ...: never two in a row, runs to the cap
+    ([1.0, 1.0 - _D, 0.5, 0.5 - _D, 0.25, 0.25 - _D, 0.125, 0.125 - _D], 8),
+    # a change of exactly eps is not "below eps" (strict): continues
+    ([1.0, 1.0 - _EPS, 1.0 - 2 * _EPS, 1.0 - 2 * _EPS - _D, 1.0 - 2 * _EPS - 2 * _D, 0.5], 5),
+    # the MSE rising counts by its magnitude too
+    ([1.0, 0.5, 0.5 + _D, 0.5, 0.125], 4),
+])
+def test_icp_convergence_stop_on_scripted_mse(script, expect):
+    """§4.6: stop once the MSE changed by less than eps on two consecutive
+    iterations -- the literal iteration counts are worked out by hand."""
+    assert _scripted_icp(script, _EPS) == expect
+
+
+def test_icp_convergence_off_without_eps():
+    script = [1.0, 1.0, 1.0, 1.0, 1.0, 1.0]
+    assert _scripted_icp(script, 0.0) == 6
+    assert _scripted_icp(script, _EPS) == 3
+
+
+def test_mse_converged_hand_cases():
+    """mse_converged over prefixes, as the loop calls it."""
+    first = lambda m, eps: next((k for k in range(len(m))
+                                 if oracle.mse_converged(m[:k + 1], [1] * (k + 1), eps)), None)
+    assert first([1.0, 0.9, 0.89, 0.5, 0.49, 0.48, 0.47], 0.02) == 5
+    assert first([1.0, 0.99, 0.98], 0.02) == 2
+    assert first([1.0, 0.99, 0.5, 0.49, 0.2], 0.02) is None
+    # MSE = E / n with n varying (rejection changes the pair count)
+    assert oracle.mse_converged([10.0, 9.0, 8.0], [10, 9, 8], 1e-12)
+    assert not oracle.mse_converged([10.0, 9.0, 8.0], [10, 10, 10], 0.05)
 
 
 # ---------------------------------------------------------------- O7 metrics
