@@ -333,17 +333,17 @@ def main():
     value = args.steps * ITERS * n / T
     iters_per_s = args.steps * ITERS / T
     log(f"{value / 1e9:.3f} G queries/s, {iters_per_s:.0f} ICP iterations/s")
-    # the same registrations with the solve on the host (one readback per iteration)
+    # the same registrations with the iterations kept on the device
     for _ in range(max(args.warmup, 1)):
-        gh = tree.icp(src, max_iter=ITERS, workspace=ws, host_loop=True)
+        gh = tree.icp(src, max_iter=ITERS, workspace=ws, device_loop=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        gh = tree.icp(src, max_iter=ITERS, workspace=ws, host_loop=True)
+        gh = tree.icp(src, max_iter=ITERS, workspace=ws, device_loop=True)
     torch.cuda.synchronize()
     T_host = time.perf_counter() - t0
     assert gh["iters"] == ITERS
-    log(f"host-driven loop: {args.steps * ITERS / T_host:.0f} ICP iterations/s")
+    log(f"device loop: {args.steps * ITERS / T_host:.0f} ICP iterations/s")
 
     rej, sweep, lid, vox = None, None, None, None
     if not args.headline_only:

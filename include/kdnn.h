@@ -48,7 +48,8 @@
 extern "C" {
 #endif
 
-#define KDNN_VERSION 3  /* 3: KDNN_ICP_HOST_LOOP; icp_align and icp_align_batch iterate on the device */
+#define KDNN_VERSION 4  /* 4: kdnn_moments; icp_align solves on the host unless
+                           KDNN_ICP_DEVICE_LOOP; kdnn_procrustes takes the SVD route */
 
 typedef enum kdnn_status {
     KDNN_OK = 0,
@@ -109,6 +110,17 @@ typedef struct kdnn_icp_sums {
     double sum_sm[9];
     double sum_d2;
 } kdnn_icp_sums;
+
+/* What the article's solve takes from one iteration's pairs (§2.1: the
+ * centroids, the de-centred pairs' cross-covariance H, and the error E). */
+typedef struct kdnn_icp_moments {
+    int64_t n;        /* pairs */
+    double mu_s[3];   /* source centroid  c + sum_s / n */
+    double mu_m[3];   /* matched-target centroid  c + sum_m / n */
+    double H[9];      /* sum (s - mu_s)(m - mu_m)^T = sum_sm - sum_s sum_m^T / n, row-major */
+    double E;         /* sum of squared distances (sum_d2) */
+    double mse;       /* E / n */
+} kdnn_icp_moments;
 
 /* Number of doubles icp_correspond_reduce_async writes to sums_dev:
  * [0..2] sum_s, [3..5] sum_m, [6..14] sum_sm, [15] sum_d2, [16] n. */
@@ -251,9 +263,12 @@ kdnn_status transform_points(const float *in_dev, float *out_dev, int64_t n, con
                                    its traversal order instead of sorting again */
 #define KDNN_ICP_NO_SORT 2u     /* traverse source points in their given order */
 #define KDNN_ICP_SORT 4u        /* always traverse in Morton order of the transformed points */
-#define KDNN_ICP_HOST_LOOP 8u   /* icp_align only: solve each iteration on the host (a
-                                   readback of the sums per iteration) instead of keeping
-                                   the iterations on the device */
+#define KDNN_ICP_HOST_LOOP 8u   /* icp_align, icp_align_batch: each iteration's sums come
+                                   back to the host, which solves (SVD) and applies the
+                                   convergence rule; icp_align's default */
+#define KDNN_ICP_DEVICE_LOOP 16u /* icp_align, icp_align_batch: the iterations stay on the
+                                    device (a one-group kernel reduces, solves and applies
+                                    the convergence rule); icp_align_batch's default */
 /* Neither NO_SORT nor SORT: Morton order when the tree's node records and
  * points exceed the device's L2 cache (kdnn_tree_info.auto_sort_icp); the
  * order is computed once per registration. */
@@ -324,14 +339,22 @@ kdnn_status icp_reject_reduce(const kdnn_tree *tree, const float *src_dev, int64
                               kdnn_icp_sums *out_host, double *sigma2_out, uint8_t *kept_dev,
                               void *ws_dev, size_t ws_bytes, hipStream_t stream);
 
-/* Rigid solve from correspondence sums (article §2.1): centroids, H, and the
- * proper rotation R minimising sum |R (s - mu_s) - (m - mu_m)|^2 -- the
- * article takes it from the SVD H = U S V^T as V diag(1, 1, d) U^T with
- * d = sign det(V U^T); here from Horn's unit-quaternion form (the largest
- * eigenvalue of a 4x4 symmetric matrix by Newton's method on its
- * characteristic polynomial, the vector from the adjugate), with the SVD
- * route taken when the two largest eigenvalues are close -- then
- * t = mu_m - R mu_s.  Host, fp64; the device-side ICP loop runs the same code.
+/* Centroids, cross-covariance and error of one iteration's pairs from their
+ * shifted sums (article §2.1: the centroids, then H over the de-centred
+ * pairs, which the SVD of the solve takes).  Host, fp64:
+ *   mu_s = c + sum_s / n,  mu_m = c + sum_m / n,
+ *   H = sum_sm - sum_s sum_m^T / n  (= sum (s - mu_s)(m - mu_m)^T),
+ *   E = sum_d2,  mse = E / n.
+ * n <= 0: out->n = n, E copied, every other field zero.
+ * Errors: EINVAL (NULL pointer). */
+kdnn_status kdnn_moments(const kdnn_icp_sums *sums, kdnn_icp_moments *out);
+
+/* Rigid solve from correspondence sums (article §2.1): centroids and H as
+ * kdnn_moments gives them, the SVD H = U S V^T (one-sided Jacobi, fp64),
+ * the proper rotation R = V diag(1, 1, d) U^T with d = sign det(V U^T) --
+ * the rotation minimising sum |R (s - mu_s) - (m - mu_m)|^2 -- then
+ * t = mu_m - R mu_s.  Host.  (The device-side ICP loop reaches the same
+ * rotation through Horn's unit-quaternion form.)
  * Errors: EINVAL (NULL), EDEGENERATE (n < 3 or rank(H) < 2; outputs unset). */
 kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_out);
 
@@ -352,14 +375,18 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  *                  n_k count them; with reject_k > 0 each iteration solves,
  *                  rejects by residual (icp_reject_reduce) and solves again.
  * The traversal order is computed once, from the source moved by (R0, t0).
- * With one lane per query (no schedule flag or KDNN_LANES(1)), max_iter <= 512
- * and no KDNN_ICP_HOST_LOOP, the iterations stay on the device: each one's
- * sums are reduced and solved (the same arithmetic as kdnn_procrustes) by a
- * one-group kernel that leaves the next transform for the next search (with
- * reject_k > 0: the first solve for the residual pass, then the kept pairs'),
- * so all iterations are enqueued at once (in chunks of 4 when eps > 0, to
- * stop soon after convergence) and the host waits once.
- * Otherwise each iteration's sums come back to the host, which solves.
+ * Default (and KDNN_ICP_HOST_LOOP): the article's loop (§3.3) -- each
+ * iteration's 17 sums come back to the host (a pinned readback), which solves
+ * with kdnn_procrustes (SVD, det sign fix) and applies the convergence rule
+ * before launching the next iteration.
+ * KDNN_ICP_DEVICE_LOOP (one lane per query: no schedule flag or
+ * KDNN_LANES(1); max_iter <= 512): the iterations stay on the device -- each
+ * one's sums are reduced and solved (Horn's quaternion form) by a one-group
+ * kernel that applies the convergence rule and leaves the next transform for
+ * the next search (with reject_k > 0: the first solve for the residual pass,
+ * then the kept pairs'), so all iterations are enqueued at once (in chunks of
+ * 4 when eps > 0, to stop soon after convergence) and the host waits once.
+ * KDNN_ICP_DEVICE_LOOP with another schedule or max_iter > 512 is EINVAL.
  * On EDEGENERATE the outputs hold the last good transform.
  * Errors: EINVAL, EDEVICE, EDEGENERATE. */
 kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, const double *R0_host,
@@ -375,7 +402,8 @@ size_t icp_batch_workspace_bytes(int32_t B, const int64_t *n);
 
 /* B independent registrations advanced together (article §3.4: consecutive
  * frames kept in flight at once so the GPU stays busy; here no host round trip
- * per iteration at all, unless KDNN_ICP_HOST_LOOP).  Pair p registers src_dev[p] (n[p]
+ * per iteration at all, unless KDNN_ICP_HOST_LOOP).  No allocation: every
+ * buffer is the caller's workspace or host arrays of this call.  Pair p registers src_dev[p] (n[p]
  * points) onto trees[p] exactly as icp_align does with flags
  * KDNN_ICP_NO_SORT and one lane per query: same iteration, same convergence
  * rule per pair, and the same max_dist bound.  Each launch carries up to 8
@@ -385,15 +413,18 @@ size_t icp_batch_workspace_bytes(int32_t B, const int64_t *n);
  *   R_out, t_out      : [B][9] / [B][3], the last solved transforms.
  *   E_hist            : optional [B][max_iter], E_k of each pair.
  *   iters_done        : optional [B].      status_out : optional [B].
- *   flags             : 0 or KDNN_ICP_NO_SORT, and KDNN_ICP_HOST_LOOP (solve on the
- *                       host each iteration; otherwise, for max_iter <= 512, each
- *                       pair's reduction group solves and advances its loop on the
- *                       device and the host waits once).
+ *   flags             : 0 or KDNN_ICP_NO_SORT, and one of KDNN_ICP_HOST_LOOP (each
+ *                       iteration's sums come back and the host solves) or
+ *                       KDNN_ICP_DEVICE_LOOP (the default for max_iter <= 512:
+ *                       each pair's reduction group solves and advances its loop
+ *                       on the device and the host waits once -- the frames stay
+ *                       in flight with no host round trip, §3.4; beyond 512
+ *                       iterations the host loop).
  *   reject            : optional; max_dist only (reject_k > 0 is EINVAL).
  *   ws_dev            : >= icp_batch_workspace_bytes(B, n), 256-byte aligned.
  * A pair whose solve degenerates stops with its last good transform and its
  * status_out entry set; the others go on, and the call returns EDEGENERATE.
- * Synchronises stream.  Errors: EINVAL, ENOMEM, EDEVICE, EDEGENERATE. */
+ * Synchronises stream.  Errors: EINVAL, EDEVICE, EDEGENERATE. */
 kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const float *const *src_dev,
                             const int64_t *n, const double *R0_host, const double *t0_host,
                             int32_t max_iter, double eps, double *R_out, double *t_out,

@@ -21,7 +21,7 @@ import numpy as np
 from . import _lib
 from ._lib import (  # noqa: F401
     KdnnError, KDNN_QUERY_NO_SORT, KDNN_QUERY_SORT, KDNN_ICP_REUSE_ORDER, KDNN_ICP_NO_SORT,
-    KDNN_ICP_SORT, KDNN_SUMS_DOUBLES,
+    KDNN_ICP_SORT, KDNN_ICP_HOST_LOOP, KDNN_ICP_DEVICE_LOOP, KDNN_SUMS_DOUBLES,
 )
 
 __all__ = ["Tree", "transform", "procrustes", "build_host", "layout", "sums_to_dict",
@@ -89,16 +89,19 @@ def _params(leaf_size, max_depth, round_robin):
 
 
 def sums_to_dict(s: "_lib.IcpSums") -> dict:
-    """Correspondence sums plus the derived centroids, H and E."""
+    """Correspondence sums plus the centroids, H and E the library derives from
+    them (kdnn_moments); copies only."""
+    m = _lib.IcpMoments()
+    _lib.check(_lib.lib().kdnn_moments(ctypes.byref(s), ctypes.byref(m)), "kdnn_moments")
     n = int(s.n)
-    c = np.array(s.c[:])
-    ss, sm = np.array(s.sum_s[:]), np.array(s.sum_m[:])
-    ssm = np.array(s.sum_sm[:]).reshape(3, 3)
-    out = {"n": n, "c": c, "sum_s": ss, "sum_m": sm, "sum_sm": ssm, "E": float(s.sum_d2)}
+    out = {"n": n, "c": np.array(s.c[:]), "sum_s": np.array(s.sum_s[:]),
+           "sum_m": np.array(s.sum_m[:]), "sum_sm": np.array(s.sum_sm[:]).reshape(3, 3),
+           "E": float(s.sum_d2)}
     if n > 0:
-        out["mu_s"] = c + ss / n
-        out["mu_m"] = c + sm / n
-        out["H"] = ssm - np.outer(ss, sm) / n
+        out["mu_s"] = np.array(m.mu_s[:])
+        out["mu_m"] = np.array(m.mu_m[:])
+        out["H"] = np.array(m.H[:]).reshape(3, 3)
+        out["mse"] = float(m.mse)
     return out
 
 
@@ -155,12 +158,15 @@ class Tree:
         torch = _torch()
         q = _dev_points(q, "queries")
         m = q.shape[0]
-        idx, d2 = out if out is not None else (
-            torch.empty(m, dtype=torch.int32, device=q.device),
-            torch.empty(m, dtype=torch.float32, device=q.device))
-        ws = None
-        if m > 0:
-            ws = workspace if workspace is not None else self.query_workspace(m)
+        # buffers made here belong to the stream the search runs on, so the
+        # caching allocator cannot hand them out again before it is done
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+            idx, d2 = out if out is not None else (
+                torch.empty(m, dtype=torch.int32, device=q.device),
+                torch.empty(m, dtype=torch.float32, device=q.device))
+            ws = None
+            if m > 0:
+                ws = workspace if workspace is not None else self.query_workspace(m)
         flags = (_lib.sort_flag(sort, KDNN_QUERY_SORT, KDNN_QUERY_NO_SORT)
                  | _lib.lanes_flag(lanes, budget, top_lds))
         wp, wn = _ptr(ws), ws.numel() if ws is not None else 0
@@ -264,10 +270,12 @@ class Tree:
     def icp(self, src, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
             workspace=None, stream=None, lanes=None, sort=None, budget=None,
             top_lds: bool = False, max_dist=None, reject_k: float = 0.0,
-            host_loop: bool = False) -> dict:
+            device_loop: Optional[bool] = None) -> dict:
         """ICP registration of the source (device, original coordinates) onto the
-        tree; max_dist / reject_k: correspondence rejection (kdnn_icp_reject);
-        host_loop: solve each iteration on the host (KDNN_ICP_HOST_LOOP)."""
+        tree; max_dist / reject_k: correspondence rejection (kdnn_icp_reject).
+        device_loop: None or False = a host solve per iteration (the default;
+        KDNN_ICP_HOST_LOOP); True = the iterations stay on the device
+        (KDNN_ICP_DEVICE_LOOP)."""
         src = _dev_points(src, "src")
         n = src.shape[0]
         R0a = None if R0 is None else _mat(R0, (3, 3), "R0")
@@ -285,7 +293,7 @@ class Tree:
             E.ctypes.data_as(_lib.c_dp), Rt.ctypes.data_as(_lib.c_dp), ctypes.byref(it),
             _lib.sort_flag(sort, KDNN_ICP_SORT, KDNN_ICP_NO_SORT)
             | _lib.lanes_flag(lanes, budget, top_lds)
-            | (_lib.KDNN_ICP_HOST_LOOP if host_loop else 0), _reject(max_dist, reject_k),
+            | _lib.loop_flag(device_loop), _reject(max_dist, reject_k),
             _ptr(ws), ws.numel(), _stream(stream)), "icp_align")
         k = it.value
         return {"R": R.reshape(3, 3), "t": t, "E": E[:k], "Rt_hist": Rt[:k], "iters": k}
@@ -316,12 +324,15 @@ def icp_batch_workspace(sources_n, device=None):
 
 
 def icp_batch(trees, sources, R0=None, t0=None, max_iter: int = 30, eps: float = 0.0,
-              workspace=None, stream=None, max_dist=None, host_loop: bool = False) -> list:
+              workspace=None, stream=None, max_dist=None,
+              device_loop: Optional[bool] = None) -> list:
     """Register sources[p] onto trees[p] for every p together (icp_align_batch).
 
     Returns one dict per pair: R, t, E (per iteration), iters and status
-    (0 = OK; a degenerate pair keeps its last good transform).  host_loop:
-    solve each iteration on the host (KDNN_ICP_HOST_LOOP).
+    (0 = OK; a degenerate pair keeps its last good transform).  device_loop:
+    None or True = the iterations stay on the device (the default;
+    KDNN_ICP_DEVICE_LOOP); False = a host solve per iteration
+    (KDNN_ICP_HOST_LOOP).
     """
     B = len(trees)
     if B != len(sources) or B < 1:
@@ -345,7 +356,7 @@ def icp_batch(trees, sources, R0=None, t0=None, max_iter: int = 30, eps: float =
         int(max_iter), float(eps), R.ctypes.data_as(_lib.c_dp), t.ctypes.data_as(_lib.c_dp),
         E.ctypes.data_as(_lib.c_dp), it.ctypes.data_as(ctypes.POINTER(_lib.c_i32)),
         st.ctypes.data_as(ctypes.POINTER(_lib.c_i32)),
-        _lib.KDNN_ICP_HOST_LOOP if host_loop else 0, _reject(max_dist, 0.0),
+        _lib.loop_flag(device_loop), _reject(max_dist, 0.0),
         _ptr(ws), ws.numel(), _stream(stream))
     if status not in (_lib.KDNN_OK, _lib.KDNN_EDEGENERATE):
         _lib.check(status, "icp_align_batch")

@@ -18,6 +18,7 @@ KDNN_ICP_REUSE_ORDER = 1
 KDNN_ICP_NO_SORT = 2
 KDNN_ICP_SORT = 4
 KDNN_ICP_HOST_LOOP = 8
+KDNN_ICP_DEVICE_LOOP = 16
 KDNN_SUMS_DOUBLES = 17
 KDNN_LANES_SHIFT = 8
 KDNN_BUDGET_SHIFT = 16
@@ -62,6 +63,17 @@ class IcpSums(ctypes.Structure):
                 ("sum_d2", ctypes.c_double)]
 
 
+class IcpMoments(ctypes.Structure):
+    _fields_ = [("n", c_i64), ("mu_s", ctypes.c_double * 3), ("mu_m", ctypes.c_double * 3),
+                ("H", ctypes.c_double * 9), ("E", ctypes.c_double), ("mse", ctypes.c_double)]
+
+
+def loop_flag(device_loop):
+    """ICP loop flag: None = the entry point's default, True = iterations on the
+    device (KDNN_ICP_DEVICE_LOOP), False = a host solve per iteration."""
+    return 0 if device_loop is None else (KDNN_ICP_DEVICE_LOOP if device_loop else KDNN_ICP_HOST_LOOP)
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "kdtree_build": (c_i32, [c_vp, c_i64, ctypes.POINTER(BuildParams), ctypes.POINTER(c_vp)]),
@@ -85,6 +97,7 @@ SIGNATURES = {
     "icp_reject_reduce": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, ctypes.c_double,
                                   ctypes.POINTER(IcpSums), c_dp, c_vp, c_vp, c_sz, c_vp]),
     "kdnn_procrustes": (c_i32, [ctypes.POINTER(IcpSums), c_dp, c_dp]),
+    "kdnn_moments": (c_i32, [ctypes.POINTER(IcpSums), ctypes.POINTER(IcpMoments)]),
     "icp_align": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, c_i32, ctypes.c_double, c_dp, c_dp,
                           c_dp, c_dp, ctypes.POINTER(c_i32), c_u32, ctypes.POINTER(IcpReject),
                           c_vp, c_sz, c_vp]),

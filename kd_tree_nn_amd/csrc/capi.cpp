@@ -340,30 +340,23 @@ kdnn_status batch_on_device(int32_t B, const kdnn_tree *const *trees, const floa
     const size_t sb = (sizeof(IcpLoopState) + 255) & ~size_t(255);
     const size_t rb = (sizeof(IcpLoopOut) + 255) & ~size_t(255);
     const size_t row = kHead + size_t(max_iter) * sizeof(double);
-    // pinned staging: B states, then B record rows
-    struct Pinned {
-        char *h = nullptr;
+    // host staging (ordinary host memory; every copy below is followed by a
+    // stream synchronisation before the buffer is read or released): B
+    // states, then B record rows
+    struct Staging {
+        std::vector<char> h;
         hipStream_t s = nullptr;
-        ~Pinned()
-        {
-            if (h) {
-                (void)hipStreamSynchronize(s);
-                (void)hipHostFree(h);
-            }
-        }
+        ~Staging() { (void)hipStreamSynchronize(s); }  // no copy outlives the buffer
     } pin;
     pin.s = stream;
-    hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&pin.h), size_t(B) * (sb + row),
-                                 hipHostMallocDefault);
-    if (e != hipSuccess)
-        return fail(KDNN_ENOMEM, std::string("icp_align_batch: hipHostMalloc: ") + hipGetErrorString(e));
-    std::memset(pin.h, 0, size_t(B) * (sb + row));
+    pin.h.assign(size_t(B) * (sb + row), 0);
     for (int32_t p = 0; p < B; ++p) {
-        IcpLoopState *st = reinterpret_cast<IcpLoopState *>(pin.h + size_t(p) * sb);
+        IcpLoopState *st = reinterpret_cast<IcpLoopState *>(pin.h.data() + size_t(p) * sb);
         std::memcpy(st->rt, &R[9 * size_t(p)], 9 * sizeof(double));
         std::memcpy(st->rt + 9, &t[3 * size_t(p)], 3 * sizeof(double));
     }
-    if ((e = hipMemcpyAsync(batch_loop_state(ws_dev, total, 0), pin.h, size_t(B) * sb,
+    hipError_t e;
+    if ((e = hipMemcpyAsync(batch_loop_state(ws_dev, total, 0), pin.h.data(), size_t(B) * sb,
                             hipMemcpyHostToDevice, stream)) != hipSuccess ||
         (e = launch_batch_loop_init(B, ws_dev, total, stream)) != hipSuccess)
         return hip_fail(e, "icp_align_batch: loop start");
@@ -384,17 +377,18 @@ kdnn_status batch_on_device(int32_t B, const kdnn_tree *const *trees, const floa
                 return hip_fail(e, "icp_align_batch: launch");
         }
         if (eps > 0.0 && (k + 1) % kChunk == 0 && k + 1 < max_iter) {
-            if ((e = hipMemcpyAsync(pin.h, batch_loop_state(ws_dev, total, 0), size_t(B) * sb,
-                                    hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+            if ((e = hipMemcpyAsync(pin.h.data(), batch_loop_state(ws_dev, total, 0),
+                                    size_t(B) * sb, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
                 (e = hipStreamSynchronize(stream)) != hipSuccess)
                 return hip_fail(e, "icp_align_batch: synchronize");
             bool all = true;
             for (int32_t p = 0; p < B; ++p)
-                all = all && reinterpret_cast<const IcpLoopState *>(pin.h + size_t(p) * sb)->stop;
+                all = all &&
+                      reinterpret_cast<const IcpLoopState *>(pin.h.data() + size_t(p) * sb)->stop;
             if (all) break;
         }
     }
-    char *rec = pin.h + size_t(B) * sb;
+    char *rec = pin.h.data() + size_t(B) * sb;
     if ((e = hipMemcpy2DAsync(rec, row, batch_loop_out(ws_dev, total, B, 0), rb, row, size_t(B),
                               hipMemcpyDeviceToHost, stream)) != hipSuccess ||
         (e = hipStreamSynchronize(stream)) != hipSuccess)
@@ -846,6 +840,15 @@ kdnn_status icp_reject_reduce(const kdnn_tree *tree, const float *src_dev, int64
     KDNN_GUARD_END
 }
 
+kdnn_status kdnn_moments(const kdnn_icp_sums *sums, kdnn_icp_moments *out)
+{
+    KDNN_GUARD_BEGIN
+    if (!sums || !out) return fail(KDNN_EINVAL, "kdnn_moments: null pointer");
+    moments_of_sums(*sums, *out);
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
 kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_out)
 {
     KDNN_GUARD_BEGIN
@@ -873,10 +876,22 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     if (!R_out || !t_out) return fail(KDNN_EINVAL, "icp_align: null R_out or t_out");
     if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align: max_iter < 0");
     if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align: eps must be >= 0");
-    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_ICP_SORT | KDNN_ICP_HOST_LOOP | kSchedMask))
+    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_ICP_SORT | KDNN_ICP_HOST_LOOP | KDNN_ICP_DEVICE_LOOP |
+                  kSchedMask))
         return fail(KDNN_EINVAL, "icp_align: unknown flag");
-    const bool host_loop = (flags & KDNN_ICP_HOST_LOOP) != 0;
-    flags &= ~KDNN_ICP_HOST_LOOP;
+    if ((flags & KDNN_ICP_HOST_LOOP) && (flags & KDNN_ICP_DEVICE_LOOP))
+        return fail(KDNN_EINVAL, "icp_align: KDNN_ICP_HOST_LOOP and KDNN_ICP_DEVICE_LOOP together");
+    const bool device_loop = (flags & KDNN_ICP_DEVICE_LOOP) != 0;
+    flags &= ~(KDNN_ICP_HOST_LOOP | KDNN_ICP_DEVICE_LOOP);
+    if (device_loop) {
+        const Schedule sc0 = schedule_of(flags);
+        if (sc0.lanes > 1 || sc0.top_lds || sc0.budget != 0)
+            return fail(KDNN_EINVAL, "icp_align: KDNN_ICP_DEVICE_LOOP needs one lane per query "
+                                     "(no schedule flag or KDNN_LANES(1))");
+        if (max_iter > kLoopMaxIter)
+            return fail(KDNN_EINVAL, "icp_align: KDNN_ICP_DEVICE_LOOP records at most " +
+                                         std::to_string(kLoopMaxIter) + " iterations");
+    }
     kdnn_status st = icp_check(tree, src_dev, n, R, t, flags, ws_dev, ws_bytes);
     if (st != KDNN_OK) return st;
     if ((st = check_reject(reject, "icp_align")) != KDNN_OK) return st;
@@ -890,8 +905,7 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     kdnn_tree *mt = const_cast<kdnn_tree *>(tree);
     std::lock_guard<std::mutex> lock(mt->icp_mu);
     const IcpWorkspace w = carve_icp_workspace(ws_dev, n);
-    const Schedule sc = schedule_of(flags);
-    if (!host_loop && sc.lanes <= 1 && !sc.top_lds && sc.budget == 0 && max_iter <= kLoopMaxIter)
+    if (device_loop)
         return icp_align_on_device(mt, src_dev, n, R, t, max_iter, eps, R_out, t_out, E_hist,
                                    Rt_hist, iters_done, flags, reject, w, stream);
     double prev_mse = 0.0;
@@ -1030,10 +1044,16 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         return fail(KDNN_EINVAL, "icp_align_batch: B < 1 or a null array");
     if (max_iter < 0) return fail(KDNN_EINVAL, "icp_align_batch: max_iter < 0");
     if (!(eps >= 0.0)) return fail(KDNN_EINVAL, "icp_align_batch: eps must be >= 0");
-    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_ICP_HOST_LOOP))
-        return fail(KDNN_EINVAL, "icp_align_batch: only KDNN_ICP_NO_SORT and KDNN_ICP_HOST_LOOP "
-                                 "are accepted (pairs are traversed in their given order, one "
-                                 "lane each)");
+    if (flags & ~(KDNN_ICP_NO_SORT | KDNN_ICP_HOST_LOOP | KDNN_ICP_DEVICE_LOOP))
+        return fail(KDNN_EINVAL, "icp_align_batch: only KDNN_ICP_NO_SORT, KDNN_ICP_HOST_LOOP and "
+                                 "KDNN_ICP_DEVICE_LOOP are accepted (pairs are traversed in their "
+                                 "given order, one lane each)");
+    if ((flags & KDNN_ICP_HOST_LOOP) && (flags & KDNN_ICP_DEVICE_LOOP))
+        return fail(KDNN_EINVAL,
+                    "icp_align_batch: KDNN_ICP_HOST_LOOP and KDNN_ICP_DEVICE_LOOP together");
+    if ((flags & KDNN_ICP_DEVICE_LOOP) && max_iter > kLoopMaxIter)
+        return fail(KDNN_EINVAL, "icp_align_batch: KDNN_ICP_DEVICE_LOOP records at most " +
+                                     std::to_string(kLoopMaxIter) + " iterations");
     kdnn_status st = check_reject(reject, "icp_align_batch");
     if (st != KDNN_OK) return st;
     if (reject && reject->reject_k > 0.0)
@@ -1076,31 +1096,23 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         return batch_on_device(B, trees, src_dev, n, R, t, max_iter, eps, R_out, t_out, E_hist,
                                iters_done, status_out, reject, ws_dev, total, part, stream);
 
-    // host slot the kernels write the sums into
-    // (on every return the stream is drained first: launches of the current
-    // iteration may still be writing into the buffer)
-    struct Pinned {
-        double *h = nullptr;
+    // Each pair's 17 sums go to its loop-state slot of the workspace (unused
+    // by this path) and come back with one copy per iteration into ordinary
+    // host memory; on every return the stream is drained first, since a copy
+    // of the current iteration may still be in flight.
+    const size_t sb = (sizeof(IcpLoopState) + 255) & ~size_t(255);
+    static_assert(sizeof(IcpLoopState) >= KDNN_SUMS_DOUBLES * sizeof(double),
+                  "a loop-state slot holds one pair's sums");
+    struct Staging {
+        std::vector<double> h;
         hipStream_t s = nullptr;
-        ~Pinned()
-        {
-            if (h) {
-                (void)hipStreamSynchronize(s);
-                (void)hipHostFree(h);
-            }
-        }
+        ~Staging() { (void)hipStreamSynchronize(s); }
     } pin;
     pin.s = stream;
-    // B x 17 sums, then one completion word per pair
-    const size_t pin_words = size_t(KDNN_SUMS_DOUBLES + 1) * size_t(B);
-    if ((e = hipHostMalloc(reinterpret_cast<void **>(&pin.h), pin_words * 8,
-                           hipHostMallocDefault)) != hipSuccess)
-        return fail(KDNN_ENOMEM, std::string("icp_align_batch: hipHostMalloc: ") + hipGetErrorString(e));
-    std::memset(pin.h, 0, pin_words * 8);
-    double *d_sums = nullptr;
-    if ((e = hipHostGetDevicePointer(reinterpret_cast<void **>(&d_sums), pin.h, 0)) != hipSuccess)
-        return hip_fail(e, "icp_align_batch: hipHostGetDevicePointer");
-    const size_t done0 = size_t(KDNN_SUMS_DOUBLES) * size_t(B);
+    pin.h.assign(size_t(B) * (sb / sizeof(double)), 0.0);
+    auto dev_sums = [&](int32_t p) {
+        return reinterpret_cast<double *>(batch_loop_state(ws_dev, total, p));
+    };
 
     const float bound2 = reject ? bound_of(reject->max_dist) : INFINITY;
     std::vector<char> done(B, 0);
@@ -1118,21 +1130,20 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
             for (size_t c = c0; c < active.size() && c < c0 + size_t(batch_max_pairs()); ++c) {
                 const int32_t p = active[c];
                 jobs.push_back(BatchJob{&trees[p]->dev, src_dev[p], n[p], &R[9 * size_t(p)],
-                                        &t[3 * size_t(p)], part[p],
-                                        d_sums + size_t(KDNN_SUMS_DOUBLES) * p,
-                                        reinterpret_cast<uint64_t *>(d_sums + done0 + p)});
+                                        &t[3 * size_t(p)], part[p], dev_sums(p), nullptr});
             }
-            e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream,
-                                 uint64_t(k) + 1);
+            e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream);
             if (e != hipSuccess) return hip_fail(e, "icp_align_batch: launch");
         }
-        for (const int32_t p : active)
-            if ((e = wait_word(reinterpret_cast<const volatile uint64_t *>(pin.h + done0 + p),
-                               uint64_t(k) + 1, stream)) != hipSuccess)
-                return hip_fail(e, "icp_align_batch: wait for the sums");
+        // every pair's slot, active or not (one strided copy), then wait
+        if ((e = hipMemcpy2DAsync(pin.h.data(), sb, dev_sums(0), sb,
+                                  KDNN_SUMS_DOUBLES * sizeof(double), size_t(B),
+                                  hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+            (e = hipStreamSynchronize(stream)) != hipSuccess)
+            return hip_fail(e, "icp_align_batch: read back the sums");
         for (const int32_t p : active) {
             kdnn_icp_sums sums;
-            to_sums(pin.h + size_t(KDNN_SUMS_DOUBLES) * p, trees[p]->dev.center, &sums);
+            to_sums(pin.h.data() + size_t(p) * (sb / sizeof(double)), trees[p]->dev.center, &sums);
             if (E_hist) E_hist[size_t(p) * max_iter + k] = sums.sum_d2;
             std::string err;
             double Rn[9], tn[3];

@@ -58,6 +58,8 @@ bool run_chase_bench(const uint32_t *next, int64_t n_records, int32_t waves, int
 
 // Rigid solve from the 17 correspondence sums.
 kdnn_status procrustes_from_sums(const kdnn_icp_sums &s, double R[9], double t[3], std::string &err);
+// Centroids, H, E and E / n from the 17 correspondence sums (zero for n <= 0).
+void moments_of_sums(const kdnn_icp_sums &s, kdnn_icp_moments &m);
 // Message of a rigid_solve.hpp status code.
 const char *rigid_status_text(int32_t st);
 

@@ -2,10 +2,12 @@
 // (CUDA-KDTree ICP article, §2.1: the rotation that best maps the centred
 // source points onto their centred matches, then the translation between the
 // centroids).  Compiled for the host (kdnn_procrustes, the host-driven loops)
-// and for the device (the loop that keeps every ICP iteration on the GPU), so
-// both take the same arithmetic.
+// and for the device (the loop that keeps every ICP iteration on the GPU).
+// The host takes the article's route: the 3x3 SVD of H with the det sign fix
+// (rigid_rotation_svd).  One GPU lane takes the quaternion form below, which
+// reaches the same rotation with far fewer dependent operations.
 //
-// Method: Horn's closed form with unit quaternions (B. K. P. Horn, "Closed-form
+// Method on the device: Horn's closed form with unit quaternions (B. K. P. Horn, "Closed-form
 // solution of absolute orientation using unit quaternions", JOSA A 4(4), 1987):
 // the optimal rotation is the quaternion of the largest eigenvalue of a
 // symmetric, trace-free 4x4 matrix N built from the cross-covariance H.  A
@@ -284,29 +286,63 @@ KDNN_HD inline int32_t rigid_rotation(const double H[9], double R[9])
     return kRigidOk;
 }
 
-// (R, t) from the sums shifted by c: S_s = sum (s - c), S_m = sum (m - c),
-// S_sm[3a + b] = sum (s - c)_a (m - c)_b over n pairs.  H = S_sm - (S_s / n) S_m^T
-// is the same cross-covariance (the shift cancels), t = mu_m - R mu_s.
-KDNN_HD inline int32_t rigid_from_sums(const double S_s[3], const double S_m[3],
-                                       const double S_sm[9], double n, const double c[3],
-                                       double R[9], double t[3])
+// The same rotation by the article's SVD route for every H: H = U S V^T by
+// one-sided Jacobi, R = V diag(1, 1, d) U^T with d = sign det(V U^T).  Same
+// degeneracy test as rigid_rotation, so both report the same cases.
+KDNN_HD inline int32_t rigid_rotation_svd(const double H[9], double R[9])
 {
-    if (!(n >= 3.0)) return kRigidFewPairs;
+    double F = 0.0, K = 0.0;
+    for (int k = 0; k < 9; ++k) F += H[k] * H[k];
+    if (!(F > 0.0) || !(F < INFINITY)) return kRigidRankLow;
+    const double C[9] = {H[4] * H[8] - H[5] * H[7], H[5] * H[6] - H[3] * H[8],
+                         H[3] * H[7] - H[4] * H[6], H[2] * H[7] - H[1] * H[8],
+                         H[0] * H[8] - H[2] * H[6], H[1] * H[6] - H[0] * H[7],
+                         H[1] * H[5] - H[2] * H[4], H[2] * H[3] - H[0] * H[5],
+                         H[0] * H[4] - H[1] * H[3]};
+    for (int k = 0; k < 9; ++k) K += C[k] * C[k];
+    if (!(K > 1e-24 * (F * F))) return kRigidRankLow;
+    return rotation_by_svd(H, R);
+}
+
+// Centroids and cross-covariance from the sums shifted by c (article §2.1:
+// centroids, then de-centred pairs, then H): with S_s = sum (s - c),
+// S_m = sum (m - c), S_sm[3a + b] = sum (s - c)_a (m - c)_b over n > 0 pairs,
+// mu_s = c + S_s / n, mu_m = c + S_m / n and
+// H = sum (s - mu_s)(m - mu_m)^T = S_sm - (S_s / n) S_m^T (the shift cancels).
+KDNN_HD inline void moments_from_sums(const double S_s[3], const double S_m[3],
+                                      const double S_sm[9], double n, const double c[3],
+                                      double mu_s[3], double mu_m[3], double H[9])
+{
     const double inv_n = 1.0 / n;  // one division (each costs ~65 cycles on a GPU lane)
-    double ms[3], mm[3], H[9];
+    double ms[3], mm[3];
     for (int a = 0; a < 3; ++a) {
         ms[a] = S_s[a] * inv_n;
         mm[a] = S_m[a] * inv_n;
     }
     for (int a = 0; a < 3; ++a)
         for (int b = 0; b < 3; ++b) H[3 * a + b] = S_sm[3 * a + b] - ms[a] * S_m[b];
-    const int32_t st = rigid_rotation(H, R);
-    if (st != kRigidOk) return st;
-    double mus[3], mum[3];
     for (int a = 0; a < 3; ++a) {
-        mus[a] = c[a] + ms[a];
-        mum[a] = c[a] + mm[a];
+        mu_s[a] = c[a] + ms[a];
+        mu_m[a] = c[a] + mm[a];
     }
+}
+
+enum RigidMethod : int32_t {
+    kRigidHorn = 0,  // quaternion form (one GPU lane: the device-side loop)
+    kRigidSvd = 1,   // the article's SVD with the det sign fix (the host)
+};
+
+// (R, t) from the shifted sums: the rotation from H (by `method`), then
+// t = mu_m - R mu_s.
+KDNN_HD inline int32_t rigid_from_sums(const double S_s[3], const double S_m[3],
+                                       const double S_sm[9], double n, const double c[3],
+                                       double R[9], double t[3], int32_t method = kRigidHorn)
+{
+    if (!(n >= 3.0)) return kRigidFewPairs;
+    double mus[3], mum[3], H[9];
+    moments_from_sums(S_s, S_m, S_sm, n, c, mus, mum, H);
+    const int32_t st = method == kRigidSvd ? rigid_rotation_svd(H, R) : rigid_rotation(H, R);
+    if (st != kRigidOk) return st;
     for (int i = 0; i < 3; ++i)
         t[i] = mum[i] - ((R[3 * i] * mus[0] + R[3 * i + 1] * mus[1]) + R[3 * i + 2] * mus[2]);
     return kRigidOk;

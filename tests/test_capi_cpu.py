@@ -39,7 +39,7 @@ def test_header_symbols_exported(kdnn):
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdnn.h but not exported"
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
-    assert kdnn.version() == 3
+    assert kdnn.version() == 4
 
 
 @pytest.mark.parametrize("n,leaf,D", [(1, 16, 0), (16, 16, 0), (17, 16, 1), (1024, 8, 7),
@@ -311,3 +311,56 @@ def test_timing_argument_errors(kdnn):
     assert b"cap" in L.kdnn_last_error()
     with pytest.raises(KdnnError, match="not started"):
         kdnn.timing_end()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_moments_match_oracle_reduction(kdnn, seed):
+    """kdnn_moments: centroids and H from the shifted sums equal the oracle's
+    two-pass reduction of the same pairs (§2.1), whatever the shift c."""
+    rng = np.random.Generator(np.random.PCG64(300 + seed))
+    n = int(rng.integers(3, 5000))
+    s = (rng.normal(size=(n, 3)) * [20, 5, 1] + [40, -10, 3]).astype(np.float32)
+    m = (s @ synth.rot_z(0.2).T + [1.0, 2.0, 0.5] + rng.normal(scale=0.1, size=s.shape)).astype(np.float32)
+    d2 = rng.random(n).astype(np.float32)
+    c = rng.normal(size=3) * 30
+    got = kdnn.sums_to_dict(_ctypes_sums(_sums_from_pairs(s, m, d2.astype(np.float64), c)))
+    red = oracle.reduce_pairs(s, m, d2)
+    assert got["n"] == red["n"] == n
+    np.testing.assert_allclose(got["mu_s"], red["mu_s"], rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(got["mu_m"], red["mu_m"], rtol=1e-12, atol=1e-9)
+    assert np.linalg.norm(got["H"] - red["H"]) <= 1e-10 * np.linalg.norm(red["H"])
+    assert got["E"] == pytest.approx(red["E"], rel=1e-12)
+    assert got["mse"] == pytest.approx(red["E"] / n, rel=1e-12)
+
+
+def test_moments_hand_example_and_empty(kdnn):
+    """Unit tetrahedron corners matched to 2 s (H worked by hand: diagonal 3/2,
+    off-diagonal -1/2), with the sums shifted by c = (1, -1, 2); n = 0 gives
+    zero centroids and H."""
+    s = np.array([[0, 0, 0], [1, 0, 0], [0, 1, 0], [0, 0, 1]], np.float64)
+    got = kdnn.sums_to_dict(_ctypes_sums(_sums_from_pairs(s, 2 * s, [0, 1, 1, 1], [1.0, -1.0, 2.0])))
+    np.testing.assert_allclose(got["mu_s"], [0.25] * 3, atol=1e-15)
+    np.testing.assert_allclose(got["mu_m"], [0.5] * 3, atol=1e-15)
+    H = np.full((3, 3), -0.5) + np.eye(3) * 2.0
+    np.testing.assert_allclose(got["H"], H, atol=1e-14)
+    assert got["E"] == 3.0 and got["mse"] == 0.75
+    from kd_tree_nn_amd import _lib
+    z = _lib.IcpSums()
+    z.n, z.sum_d2 = 0, 0.0
+    mo = _lib.IcpMoments()
+    _lib.check(_lib.lib().kdnn_moments(ctypes.byref(z), ctypes.byref(mo)), "kdnn_moments")
+    assert mo.n == 0 and list(mo.H) == [0.0] * 9 and mo.mse == 0.0
+    assert _lib.lib().kdnn_moments(None, ctypes.byref(mo)) == _lib.KDNN_EINVAL
+
+
+def _ctypes_sums(d):
+    from kd_tree_nn_amd import _lib
+    s = _lib.IcpSums()
+    s.n = int(d["n"])
+    s.c[:] = list(np.asarray(d["c"], np.float64))
+    s.sum_s[:] = list(d["sum_s"])
+    s.sum_m[:] = list(d["sum_m"])
+    s.sum_sm[:] = list(np.asarray(d["sum_sm"]).ravel())
+    s.sum_d2 = float(d["E"])
+    return s
+
