@@ -466,12 +466,12 @@ kdnn_status voxel_downsample(const float *xyz_dev, int64_t n, double leaf, float
 const char *kdnn_last_error(void);
 
 /* Kernel timing, a profiling aid.  After kdnn_timing_begin(cap), each of the
- * calling thread's next `cap` correspondence launches (icp_correspond_reduce,
- * icp_correspond_reduce_async and each iteration of icp_align) has its search
- * kernel's dispatch stamp a pair of HIP events with its start and end time
- * (hipExtLaunchKernel; the traversal-order sort before it and the reduction
- * after it fall outside; the two-pass schedule spans both passes); later
- * launches are not timed.  kdnn_timing_end waits for the recorded events,
+ * calling thread's next `cap` search launches (nn_query, nn_query_radius,
+ * icp_correspond_reduce, icp_correspond_reduce_async and each iteration of
+ * icp_align) has its search kernel's dispatch stamp a pair of HIP events with
+ * its start and end time (hipExtLaunchKernel; the traversal-order sort before
+ * it and the reduction after it fall outside; the two-pass schedule spans
+ * both passes); later launches are not timed.  kdnn_timing_end waits for the recorded events,
  * writes the launch count to *count_out (optional) and, when ms_out is not
  * null, the search kernel's duration in milliseconds of launch k to
  * ms_out[k] (cap_out entries available, at least the count), and ends timing.

@@ -713,7 +713,7 @@ static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t 
         }
     }
     hipError_t e = launch_nn(tree->dev, q, m, perm, idx, d2, cn, cp, stats, schedule_of(flags),
-                             bound2, twopass, s);
+                             bound2, twopass, s, stats ? nullptr : g_timing.next());
     if (e != hipSuccess) return hip_fail(e, "nn_query: launch");
     return KDNN_OK;
 }

@@ -164,9 +164,11 @@ struct Schedule {
     uint32_t budget = 0;  // 0 = default two-pass budget / automatic choice
     bool top_lds = false;
 };
+// timing: null, or two events the search kernel(s) stamp with their start and end.
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     const Schedule &sc, float bound2, void *twopass, hipStream_t s);
+                     const Schedule &sc, float bound2, void *twopass, hipStream_t s,
+                     const hipEvent_t *timing = nullptr);
 hipError_t launch_transform(const float *in, float *out, int64_t n, const double *R,
                             const double *t, hipStream_t s);
 // Correspondence search + per-work-group partials, then the one-group

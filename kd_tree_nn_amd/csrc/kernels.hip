@@ -2466,8 +2466,26 @@ static WavePlan wave_plan(K kernel, int slot, int32_t depth, int64_t m, float bo
     return p;
 }
 
+template <typename T>
+struct same_type {
+    using type = T;
+};
+
+// Launch through hipExtLaunchKernel: a non-null e0 / e1 is stamped by the
+// dispatch itself at its start / end (no marker packets between kernels);
+// with both null it is a plain launch.
+template <typename... P>
+static hipError_t launch_k(void (*k)(P...), dim3 grid, uint32_t block, size_t lds, hipStream_t s,
+                           hipEvent_t e0, hipEvent_t e1, typename same_type<P>::type... args)
+{
+    void *pa[] = {static_cast<void *>(&args)...};
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(k), grid, dim3(block), pa, lds, s, e0,
+                              e1, 0);
+}
+
 template <int G, int CH = kLeafChunk>
-static void launch_nn_g(NnArgs a, bool stats, float bound2, hipStream_t s)
+static hipError_t launch_nn_g(NnArgs a, bool stats, float bound2, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1)
 {
     int64_t blocks = (a.m + kWG / G - 1) / (kWG / G);  // G lanes per query
     if (G == 1) {
@@ -2483,16 +2501,14 @@ static void launch_nn_g(NnArgs a, bool stats, float bound2, hipStream_t s)
     }
     if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
     const size_t lds = G == 1 && CH == kLeafChunkSmall ? lbs_bytes(a.tree.depth) : 0;
-    if (stats) {
-        nn_kernel<G, true, CH><<<dim3(uint32_t(blocks)), kWG, lds, s>>>(a);
-    } else if (G == 1 && KDNN_QLDS && a.wq < kQFull &&
-               blocks <= resident_groups(nn_kernel<1, false, CH, true>,
-                                         CH == kLeafChunk ? 4 : 5, a.tree.depth)) {
+    const dim3 grid{uint32_t(blocks)};
+    if (stats) return launch_k(nn_kernel<G, true, CH>, grid, kWG, lds, s, e0, e1, a);
+    if (G == 1 && KDNN_QLDS && a.wq < kQFull &&
+        blocks <= resident_groups(nn_kernel<1, false, CH, true>, CH == kLeafChunk ? 4 : 5,
+                                  a.tree.depth))
         // a one-round launch, still resident at once with the larger LDS
-        nn_kernel<1, false, CH, true><<<dim3(uint32_t(blocks)), kWG, lds, s>>>(a);
-    } else {
-        nn_kernel<G, false, CH><<<dim3(uint32_t(blocks)), kWG, lds, s>>>(a);
-    }
+        return launch_k(nn_kernel<1, false, CH, true>, grid, kWG, lds, s, e0, e1, a);
+    return launch_k(nn_kernel<G, false, CH>, grid, kWG, lds, s, e0, e1, a);
 }
 
 // Persistent LDS launch shape for this device: one work-group per CU and
@@ -2534,16 +2550,22 @@ static void allow_lds(K kernel, size_t bytes)
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
 }
 
-static void launch_nn_two_pass(const NnArgs &a, bool stats, void *twopass, hipStream_t s)
+static hipError_t launch_nn_two_pass(const NnArgs &a, bool stats, void *twopass, hipStream_t s,
+                                     hipEvent_t e0, hipEvent_t e1)
 {
     const TwoPass tp = carve_twopass(twopass, a.m);
+    hipError_t e;
     if (stats) {
-        nn_pass1_kernel<true><<<dim3(uint32_t(tp.nb1)), kWG, 0, s>>>(a, tp);
-        nn_pass2_kernel<true><<<dim3(kPass2Blocks), kWG, 0, s>>>(a, tp);
+        e = launch_k(nn_pass1_kernel<true>, dim3(uint32_t(tp.nb1)), kWG, 0, s, e0, nullptr, a, tp);
+        if (e == hipSuccess)
+            e = launch_k(nn_pass2_kernel<true>, dim3(kPass2Blocks), kWG, 0, s, nullptr, e1, a, tp);
     } else {
-        nn_pass1_kernel<false><<<dim3(uint32_t(tp.nb1)), kWG, 0, s>>>(a, tp);
-        nn_pass2_kernel<false><<<dim3(kPass2Blocks), kWG, 0, s>>>(a, tp);
+        e = launch_k(nn_pass1_kernel<false>, dim3(uint32_t(tp.nb1)), kWG, 0, s, e0, nullptr, a,
+                     tp);
+        if (e == hipSuccess)
+            e = launch_k(nn_pass2_kernel<false>, dim3(kPass2Blocks), kWG, 0, s, nullptr, e1, a, tp);
     }
+    return e;
 }
 
 // The start key of a search under the squared-distance bound bound2: no bound
@@ -2560,8 +2582,11 @@ static uint64_t host_bound_key(float bound2)
 
 hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
                      int32_t *idx, float *d2, uint32_t *cnt_nodes, uint32_t *cnt_pts, bool stats,
-                     const Schedule &sc, float bound2, void *twopass, hipStream_t s)
+                     const Schedule &sc, float bound2, void *twopass, hipStream_t s,
+                     const hipEvent_t *timing)
 {
+    const hipEvent_t e0 = timing ? timing[0] : nullptr, e1 = timing ? timing[1] : nullptr;
+    hipError_t e;
     NnArgs a{};
     a.tree = tree_view(t);
     a.init = host_bound_key(bound2);
@@ -2577,28 +2602,30 @@ hipError_t launch_nn(const DeviceTree &t, const float *q, int64_t m, const int32
     if (sc.lanes == 0 && sc.top_lds && persist_shape(a.tree, m, ps)) {
         if (stats) {
             allow_lds(nn_persist_kernel<true>, ps.lds_bytes);
-            nn_persist_kernel<true><<<ps.blocks, kPWG, ps.lds_bytes, s>>>(a, ps.lds_first);
+            e = launch_k(nn_persist_kernel<true>, dim3(ps.blocks), kPWG, ps.lds_bytes, s, e0, e1,
+                         a, ps.lds_first);
         } else {
             allow_lds(nn_persist_kernel<false>, ps.lds_bytes);
-            nn_persist_kernel<false><<<ps.blocks, kPWG, ps.lds_bytes, s>>>(a, ps.lds_first);
+            e = launch_k(nn_persist_kernel<false>, dim3(ps.blocks), kPWG, ps.lds_bytes, s, e0, e1,
+                         a, ps.lds_first);
         }
     } else if (sc.lanes == 0 && sc.budget != 0 && twopass) {
-        launch_nn_two_pass(a, stats, twopass, s);
+        e = launch_nn_two_pass(a, stats, twopass, s, e0, e1);
     } else {
         switch (sc.lanes) {
-        case 2: launch_nn_g<2>(a, stats, bound2, s); break;
-        case 4: launch_nn_g<4>(a, stats, bound2, s); break;
-        case 8: launch_nn_g<8>(a, stats, bound2, s); break;
-        case 16: launch_nn_g<16>(a, stats, bound2, s); break;
+        case 2: e = launch_nn_g<2>(a, stats, bound2, s, e0, e1); break;
+        case 4: e = launch_nn_g<4>(a, stats, bound2, s, e0, e1); break;
+        case 8: e = launch_nn_g<8>(a, stats, bound2, s, e0, e1); break;
+        case 16: e = launch_nn_g<16>(a, stats, bound2, s, e0, e1); break;
         default:
             if (t.max_leaf <= kLeafChunkSmall)
-                launch_nn_g<1, kLeafChunkSmall>(a, stats, bound2, s);
+                e = launch_nn_g<1, kLeafChunkSmall>(a, stats, bound2, s, e0, e1);
             else
-                launch_nn_g<1>(a, stats, bound2, s);
+                e = launch_nn_g<1>(a, stats, bound2, s, e0, e1);
             break;
         }
     }
-    return hipGetLastError();
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 hipError_t launch_transform(const float *in, float *out, int64_t n, const double *R,
@@ -2610,23 +2637,6 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
                                                              R[4], R[5], R[6], R[7], R[8], t[0],
                                                              t[1], t[2]);
     return hipGetLastError();
-}
-
-template <typename T>
-struct same_type {
-    using type = T;
-};
-
-// Launch through hipExtLaunchKernel: a non-null e0 / e1 is stamped by the
-// dispatch itself at its start / end (no marker packets between kernels);
-// with both null it is a plain launch.
-template <typename... P>
-static hipError_t launch_k(void (*k)(P...), dim3 grid, uint32_t block, size_t lds, hipStream_t s,
-                           hipEvent_t e0, hipEvent_t e1, typename same_type<P>::type... args)
-{
-    void *pa[] = {static_cast<void *>(&args)...};
-    return hipExtLaunchKernel(reinterpret_cast<const void *>(k), grid, dim3(block), pa, lds, s, e0,
-                              e1, 0);
 }
 
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
