@@ -395,6 +395,27 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
                       uint32_t flags, const kdnn_icp_reject *reject, void *ws_dev,
                       size_t ws_bytes, hipStream_t stream);
 
+/* icp_align for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation:
+ * the same registration, arguments and results as icp_align, with no
+ * workspace argument.  Its workspace is a library-owned device array of
+ * KDNN_NOALLOC_SCRATCH_BYTES per device (a module global: every device the
+ * library runs on holds its copy until the process ends), so the call makes
+ * no allocation of any kind.  Limit: n <= KDNN_NOALLOC_MAX_POINTS source
+ * points (larger n is EINVAL); the tree must live on the current device.
+ * Every call on a device shares that device's array and finds in it what the
+ * last call left (no part of it needs to start at zero: each iteration
+ * writes every word it reads); the library serialises calls on one device
+ * with a lock, since two overlapping calls would race on the array.
+ * Synchronises stream.  Errors: EINVAL, EDEVICE, EDEGENERATE (as icp_align). */
+#define KDNN_NOALLOC_MAX_POINTS 262144
+#define KDNN_NOALLOC_SCRATCH_BYTES (12u << 20)
+kdnn_status icp_align_noalloc(const kdnn_tree *tree, const float *src_dev, int64_t n,
+                              const double *R0_host, const double *t0_host, int32_t max_iter,
+                              double eps, double *R_out, double *t_out, double *E_hist,
+                              double *Rt_hist, int32_t *iters_done, uint32_t flags,
+                              const kdnn_icp_reject *reject, hipStream_t stream);
+
 /* Bytes of device workspace icp_align_batch needs for B pairs of n[p] source
  * points (partial sums, and each pair's loop state and record, ~54 KB).
  * 0 if B < 1, n is NULL or some n[p] < 1. */

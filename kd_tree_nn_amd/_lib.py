@@ -20,6 +20,8 @@ KDNN_ICP_SORT = 4
 KDNN_ICP_HOST_LOOP = 8
 KDNN_ICP_DEVICE_LOOP = 16
 KDNN_SUMS_DOUBLES = 17
+KDNN_NOALLOC_MAX_POINTS = 262144
+KDNN_NOALLOC_SCRATCH_BYTES = 12 << 20
 KDNN_LANES_SHIFT = 8
 KDNN_BUDGET_SHIFT = 16
 KDNN_TOP_LDS = 1 << 24
@@ -101,6 +103,9 @@ SIGNATURES = {
     "icp_align": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, c_i32, ctypes.c_double, c_dp, c_dp,
                           c_dp, c_dp, ctypes.POINTER(c_i32), c_u32, ctypes.POINTER(IcpReject),
                           c_vp, c_sz, c_vp]),
+    "icp_align_noalloc": (c_i32, [c_vp, c_vp, c_i64, c_dp, c_dp, c_i32, ctypes.c_double, c_dp,
+                                  c_dp, c_dp, c_dp, ctypes.POINTER(c_i32), c_u32,
+                                  ctypes.POINTER(IcpReject), c_vp]),
     "icp_batch_workspace_bytes": (c_sz, [c_i32, ctypes.POINTER(c_i64)]),
     "icp_align_batch": (c_i32, [c_i32, c_vp, c_vp, ctypes.POINTER(c_i64), c_dp, c_dp, c_i32,
                                 ctypes.c_double, c_dp, c_dp, c_dp, ctypes.POINTER(c_i32),

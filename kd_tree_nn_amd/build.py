@@ -20,7 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkdnn.so")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "voxel.hip", "roofline.hip", "builder.cpp", "procrustes.cpp", "capi.cpp"]
+SOURCES = ["kernels.hip", "voxel.hip", "roofline.hip", "noalloc.hip", "builder.cpp",
+           "procrustes.cpp", "capi.cpp"]
 
 
 def hipcc() -> str:

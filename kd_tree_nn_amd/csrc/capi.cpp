@@ -963,6 +963,37 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
     KDNN_GUARD_END
 }
 
+kdnn_status icp_align_noalloc(const kdnn_tree *tree, const float *src_dev, int64_t n,
+                              const double *R0_host, const double *t0_host, int32_t max_iter,
+                              double eps, double *R_out, double *t_out, double *E_hist,
+                              double *Rt_hist, int32_t *iters_done, uint32_t flags,
+                              const kdnn_icp_reject *reject, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    if (!tree) return fail(KDNN_EINVAL, "icp_align_noalloc: null tree");
+    if (n > KDNN_NOALLOC_MAX_POINTS)
+        return fail(KDNN_EINVAL, "icp_align_noalloc: n = " + std::to_string(n) + " exceeds " +
+                                     std::to_string(KDNN_NOALLOC_MAX_POINTS) +
+                                     " (the scratch limit; use icp_align with a workspace)");
+    const size_t need = icp_ws_bytes(n);
+    if (need > size_t(KDNN_NOALLOC_SCRATCH_BYTES))
+        return fail(KDNN_EINVAL, "icp_align_noalloc: workspace larger than the scratch");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "icp_align_noalloc: hipGetDevice");
+    if (tree->device != dev)
+        return fail(KDNN_EINVAL, "icp_align_noalloc: the tree lives on another device");
+    void *ptr = nullptr;
+    std::mutex *call_mu = nullptr;
+    if ((e = noalloc_scratch(dev, &ptr, &call_mu)) != hipSuccess)
+        return hip_fail(e, "icp_align_noalloc: scratch address");
+    std::lock_guard<std::mutex> lock(*call_mu);
+    return icp_align(tree, src_dev, n, R0_host, t0_host, max_iter, eps, R_out, t_out, E_hist,
+                     Rt_hist, iters_done, flags, reject, ptr, size_t(KDNN_NOALLOC_SCRATCH_BYTES),
+                     stream);
+    KDNN_GUARD_END
+}
+
 size_t voxel_downsample_workspace_bytes(int64_t n) { return voxel_ws_bytes(n); }
 
 kdnn_status voxel_downsample(const float *xyz_dev, int64_t n, double leaf, float *out_dev,

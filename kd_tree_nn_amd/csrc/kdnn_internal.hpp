@@ -149,6 +149,11 @@ struct IcpWorkspace {
 size_t icp_ws_bytes(int64_t n);
 IcpWorkspace carve_icp_workspace(void *ws, int64_t n);
 
+// icp_align_noalloc's device scratch (noalloc.hip): the address of the
+// current device's copy (found on the first call per device; `device` must
+// be current) and the lock that keeps calls on that device from overlapping.
+hipError_t noalloc_scratch(int device, void **ptr, std::mutex **call_mu);
+
 // Kernel launchers (return the hipError_t of the launch).
 // Morton-order the points moved by (R, t) (R == nullptr: not moved): on
 // return *perm points at the int32 permutation (traversal slot -> point).

@@ -364,3 +364,18 @@ def _ctypes_sums(d):
     s.sum_d2 = float(d["E"])
     return s
 
+
+def test_noalloc_limits_consistent(kdnn):
+    """The allocation-free registration's scratch holds the ICP workspace of
+    its largest input; the binding's constants are the header's."""
+    from kd_tree_nn_amd import _lib
+    text = open(os.path.join(ROOT, "include", "kdnn.h")).read()
+    mx = int(re.search(r"#define KDNN_NOALLOC_MAX_POINTS (\d+)", text).group(1))
+    sh = int(re.search(r"#define KDNN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text).group(1))
+    sb = int(re.search(r"#define KDNN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text).group(2))
+    assert (mx, sh << sb) == (_lib.KDNN_NOALLOC_MAX_POINTS, _lib.KDNN_NOALLOC_SCRATCH_BYTES)
+    L = _lib.lib()
+    assert L.icp_workspace_bytes(mx) <= _lib.KDNN_NOALLOC_SCRATCH_BYTES
+    # argument errors come back before any device work
+    assert L.icp_align_noalloc(None, None, 10, None, None, 1, 0.0, None, None, None, None, None,
+                               0, None, None) == _lib.KDNN_EINVAL
