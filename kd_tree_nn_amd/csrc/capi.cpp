@@ -4,6 +4,7 @@
 // host, repeat; §4.6 convergence rule).  No exception crosses the ABI.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cmath>
@@ -1127,10 +1128,25 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         return batch_on_device(B, trees, src_dev, n, R, t, max_iter, eps, R_out, t_out, E_hist,
                                iters_done, status_out, reject, ws_dev, total, part, stream);
 
-    // Each pair's 17 sums go to its loop-state slot of the workspace (unused
-    // by this path) and come back with one copy per iteration into ordinary
-    // host memory; on every return the stream is drained first, since a copy
-    // of the current iteration may still be in flight.
+    // Each pair's reduction writes its 17 sums into its tree's pinned slot,
+    // then the launch's sequence number into the slot's completion word, which
+    // the host polls (the slots belong to the trees: nothing is allocated).
+    // The users of those slots are serialised by the trees' locks, taken in
+    // address order.  When one tree serves several pairs of the batch, its
+    // single slot cannot: then every pair's sums go to its loop-state slot of
+    // the workspace (unused by this path) and come back with one copy per
+    // iteration.  On every return the stream is drained first (the Staging
+    // destructor runs before the locks are released), since a launch of the
+    // current iteration may still be writing.
+    std::vector<kdnn_tree *> uniq;
+    for (int32_t p = 0; p < B; ++p) uniq.push_back(const_cast<kdnn_tree *>(trees[p]));
+    std::sort(uniq.begin(), uniq.end());
+    uniq.erase(std::unique(uniq.begin(), uniq.end()), uniq.end());
+    const bool shared_tree = int32_t(uniq.size()) != B;
+    std::vector<std::unique_lock<std::mutex>> locks;
+    for (kdnn_tree *u : uniq) locks.emplace_back(u->icp_mu);
+    uint64_t seq0 = 0;
+    for (kdnn_tree *u : uniq) seq0 = u->seq > seq0 ? u->seq : seq0;
     const size_t sb = (sizeof(IcpLoopState) + 255) & ~size_t(255);
     static_assert(sizeof(IcpLoopState) >= KDNN_SUMS_DOUBLES * sizeof(double),
                   "a loop-state slot holds one pair's sums");
@@ -1140,9 +1156,13 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         ~Staging() { (void)hipStreamSynchronize(s); }
     } pin;
     pin.s = stream;
-    pin.h.assign(size_t(B) * (sb / sizeof(double)), 0.0);
+    if (shared_tree) pin.h.assign(size_t(B) * (sb / sizeof(double)), 0.0);
     auto dev_sums = [&](int32_t p) {
-        return reinterpret_cast<double *>(batch_loop_state(ws_dev, total, p));
+        return shared_tree ? reinterpret_cast<double *>(batch_loop_state(ws_dev, total, p))
+                           : trees[p]->d_pinned;
+    };
+    auto host_sums = [&](int32_t p) -> const double * {
+        return shared_tree ? pin.h.data() + size_t(p) * (sb / sizeof(double)) : trees[p]->h_pinned;
     };
 
     const float bound2 = reject ? bound_of(reject->max_dist) : INFINITY;
@@ -1156,25 +1176,39 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
         for (int32_t p = 0; p < B; ++p)
             if (!done[p]) active.push_back(p);
         if (active.empty()) break;
+        // one sequence number for every tree of the batch (all of them locked)
+        const uint64_t seq = seq0 + uint64_t(k) + 1;
+        for (kdnn_tree *u : uniq) u->seq = seq;
         for (size_t c0 = 0; c0 < active.size(); c0 += size_t(batch_max_pairs())) {
             jobs.clear();
             for (size_t c = c0; c < active.size() && c < c0 + size_t(batch_max_pairs()); ++c) {
                 const int32_t p = active[c];
+                uint64_t *done_word =
+                    shared_tree ? nullptr
+                                : reinterpret_cast<uint64_t *>(trees[p]->d_pinned + kDoneWord);
                 jobs.push_back(BatchJob{&trees[p]->dev, src_dev[p], n[p], &R[9 * size_t(p)],
-                                        &t[3 * size_t(p)], part[p], dev_sums(p), nullptr});
+                                        &t[3 * size_t(p)], part[p], dev_sums(p), done_word});
             }
-            e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream);
+            e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream,
+                                 seq);
             if (e != hipSuccess) return hip_fail(e, "icp_align_batch: launch");
         }
-        // every pair's slot, active or not (one strided copy), then wait
-        if ((e = hipMemcpy2DAsync(pin.h.data(), sb, dev_sums(0), sb,
-                                  KDNN_SUMS_DOUBLES * sizeof(double), size_t(B),
-                                  hipMemcpyDeviceToHost, stream)) != hipSuccess ||
-            (e = hipStreamSynchronize(stream)) != hipSuccess)
-            return hip_fail(e, "icp_align_batch: read back the sums");
+        if (shared_tree) {
+            // every pair's slot, active or not (one copy), then wait
+            if ((e = hipMemcpyAsync(pin.h.data(), dev_sums(0), size_t(B) * sb,
+                                    hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+                (e = hipStreamSynchronize(stream)) != hipSuccess)
+                return hip_fail(e, "icp_align_batch: read back the sums");
+        } else {
+            for (const int32_t p : active)
+                if ((e = wait_word(reinterpret_cast<const volatile uint64_t *>(
+                                       trees[p]->h_pinned + kDoneWord),
+                                   seq, stream)) != hipSuccess)
+                    return hip_fail(e, "icp_align_batch: wait for the sums");
+        }
         for (const int32_t p : active) {
             kdnn_icp_sums sums;
-            to_sums(pin.h.data() + size_t(p) * (sb / sizeof(double)), trees[p]->dev.center, &sums);
+            to_sums(host_sums(p), trees[p]->dev.center, &sums);
             if (E_hist) E_hist[size_t(p) * max_iter + k] = sums.sum_d2;
             std::string err;
             double Rn[9], tn[3];
