@@ -5,20 +5,26 @@ Workload (seeded, synthetic): the Scene pair -- 100k-point target sampled on a
 ground disk, 20 boxes and 10 spheres (density ~ 1/r^2, 1 cm noise); source = an
 independent 100k resample moved by 10 degrees of yaw and 0.5 m; leaf 16.
 
-One step = one ICP registration of 30 iterations (transform, exact NN of all
-100k source points, fp64 reduction, host SVD, per iteration) with the tree
-already built and both clouds resident in device memory.  The tree build and
-upload are timed separately.  value = NN queries/s over the timed steps
-(30 x 100k queries per step); icp_iters_per_s is the same clock.
+One step = one ICP registration of 30 iterations as the library runs it by
+default: per iteration the fused kernel (transform, exact NN of all 100k
+source points, fp64 reduction to 17 sums), a 136-byte readback, the SVD solve
+with the det sign fix and the convergence check on the host -- with the tree
+already built and both clouds resident in device memory.  value = NN
+queries/s over the timed steps (30 x 100k queries per step); icp_iters_per_s
+is the same clock.  The same registrations with the iterations kept on the
+device (KDNN_ICP_DEVICE_LOOP) are reported beside it.
 
-Also reported: the fused correspondence kernel's duration (HIP events around
-each launch, on the stream it is launched on) and its roofline against the
-algorithmic bytes counted by the instrumented traversal; HBM traffic from the
-committed rocprofv3 counter summary when it was taken on the current kernel
-source; standalone nn_query rates with and without the Morton ordering; and
-the CPU oracle on the host (one thread, a bounded sample).
+Also reported: the fused kernel's duration (the library's event pair stamped
+by the kernel's own dispatch, on the stream it is launched on) and its
+roofline -- the algorithmic bytes of the search (node records, leaf points,
+index, query, source and match, counted by the instrumented traversal) against
+the random-gather ceiling of the memory level holding the tree, measured by
+the library's micro-benchmark, with the 8 TB/s HBM peak as context; HBM
+traffic from the committed rocprofv3 counter summary when it was taken on the
+current kernel source; the other workloads' nn_query rooflines; the CPU
+oracle on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only SECTION]
     python bench.py --profile-pass    # short run for rocprofv3 counter passes
 """
 
@@ -36,6 +42,10 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "kd_tree_nn_amd", "csrc", "kernels.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "icp_fused_kernel_scene100k_traffic.txt")
 COPY_MIB = 512
+ITERS = 30
+QUERY_WORKLOADS = ("stress_1M_leaf8", "stress_1M_leaf16", "skewed_500k_leaf8",
+                   "skewed_500k_leaf16")
+SECTIONS = ("scene", "reject", "sweep", "lidar", "voxel") + QUERY_WORKLOADS
 
 
 def kernel_source_hash():
@@ -70,61 +80,82 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench "
-             "-- python3 -u bench.py --steps 5 --warmup 1 --no-cpu-baseline --headline-only")
+def pct(a):
+    import numpy as np
+    a = np.asarray(a, dtype=np.float64)
+    return {"median": float(np.median(a)), "p25": float(np.percentile(a, 25)),
+            "p75": float(np.percentile(a, 75)), "mean": float(a.mean()), "n": int(len(a))}
+
+
+# --------------------------------------------------------------- profiles/
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_{only} "
+             "-o bench -- python3 -u bench.py --steps 20 --warmup 3 --no-cpu-baseline "
+             "--only {only} --json-out gpurun_out/trace_{only}/bench.json")
 PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} "
            "-o pmc -- python3 -u bench.py --profile-pass")
 
 
-def summarize(trace_dir, fetch_dir, write_dir):
-    """Write the short rocprofv3 summaries under profiles/ from the CSV output of
-    the trace run and the two counter passes (commands in TRACE_CMD, PMC_CMD)."""
+def _rows(path):
     import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
 
-    import numpy as np
 
-    def rows(path):
-        with open(path) as f:
-            return list(csv.DictReader(f))
+def _agent(d):
+    try:
+        for r in _rows(os.path.join(d, [f for f in os.listdir(d) if f.endswith("agent_info.csv")][0])):
+            if r.get("Agent_Type", "").upper() == "GPU":
+                return (f'{r.get("Name", "?")}, {r.get("Cu_Count", "?")} CUs, '
+                        f'{r.get("Num_Xcc", "?")} XCDs, {r.get("Max_Engine_Clk_Fcompute", "?")} MHz')
+    except (OSError, IndexError):
+        pass
+    return "?"
 
-    def agent(d):
-        try:
-            for r in rows(os.path.join(d, [f for f in os.listdir(d) if f.endswith("agent_info.csv")][0])):
-                if r.get("Agent_Type", "").upper() == "GPU":
-                    return (f'{r.get("Name", "?")}, {r.get("Cu_Count", "?")} CUs, '
-                            f'{r.get("Num_Xcc", "?")} XCDs, {r.get("Max_Engine_Clk_Fcompute", "?")} MHz')
-        except (OSError, IndexError):
-            pass
-        return "?"
 
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    stats = rows(os.path.join(trace_dir, "bench_kernel_stats.csv"))
-    out = [f"# rocprofv3 kernel statistics: bench.py on the Scene 100k x 100k ICP workload",
-           f"# command: {TRACE_CMD}",
-           f"# device: {agent(trace_dir)}",
+def summarize_trace(trace_dir, only, out_name):
+    """profiles/<out_name>: rocprofv3 kernel statistics of `bench.py --only
+    <only>` (TRACE_CMD) and that same run's bench line, from which its
+    roofline figures are computed."""
+    stats = _rows(os.path.join(trace_dir, "bench_kernel_stats.csv"))
+    out = [f"# rocprofv3 kernel statistics of bench.py --only {only}",
+           f"# command: {TRACE_CMD.format(only=only)}",
+           f"# device: {_agent(trace_dir)}",
            f"# kernels.hip code sha256[:16] (comments, whitespace dropped): {kernel_source_hash()}",
            "",
-           f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}"]
-    for r in stats[:14]:
-        out.append(f"{r['Name'][:64]:64s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+           f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}"]
+    for r in stats[:24]:
+        out.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
                    f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
                    f"{float(r['Percentage']):6.2f}")
-    with open(os.path.join(ROOT, "profiles", "icp_fused_kernel_scene100k_trace.txt"), "w") as f:
+    try:
+        with open(os.path.join(trace_dir, "bench.json")) as f:
+            line = json.load(f)
+        out += ["", "# the same run's bench line:", json.dumps(line, indent=1, sort_keys=True)]
+    except OSError:
+        pass
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
         f.write("\n".join(out) + "\n")
+    print("\n".join(out[:34]))
+
+
+def summarize(fetch_dir, write_dir):
+    """profiles/ traffic summary of the fused kernel from the two counter
+    passes (PMC_CMD, FETCH_SIZE then WRITE_SIZE), each scaled by what the same
+    counter reads for device copies of a known size in the same program."""
+    import numpy as np
 
     def counter(d):
         per = {}
-        for r in rows(os.path.join(d, "pmc_counter_collection.csv")):
-            per.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+        for r in _rows(os.path.join(d, "pmc_counter_collection.csv")):
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return per
 
     copy_kib = COPY_MIB * 1024
     res = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = counter(d)
-        fused = [v for k, vs in per.items() if "icp_fused_kernel" in k for _, v in vs]
-        copies = [v for k, vs in per.items() if "copyBuffer" in k for _, v in vs
-                  if v > 0.25 * copy_kib]
+        fused = [v for k, vs in per.items() if "icp_fused_kernel" in k for v in vs]
+        copies = [v for k, vs in per.items() if "copyBuffer" in k for v in vs if v > 0.25 * copy_kib]
         factor = copy_kib / float(np.mean(copies))
         res[name] = (float(np.mean(fused)), len(fused), copies, factor)
     traffic = sum(v * 1024 * fac for v, _, _, fac in res.values())
@@ -132,7 +163,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
            "# two rocprofv3 counter passes, each over the same short program:",
            "#   " + PMC_CMD.format(c="FETCH_SIZE", d="fetch"),
            "#   " + PMC_CMD.format(c="WRITE_SIZE", d="write"),
-           f"# device: {agent(fetch_dir)}",
+           f"# device: {_agent(fetch_dir)}",
            "# calibration: three device copies of a known size in the same program;",
            "# factor = copied KiB / counter KiB of those dispatches",
            ""]
@@ -165,17 +196,14 @@ PMC_SETS = {
 def summarize_counters(root):
     """profiles/ summary of the three counter passes (PMC_SETS) over
     `bench.py --profile-pass`, per dispatch of the fused kernel."""
-    import csv
-
     import numpy as np
     val = {}
     for name in PMC_SETS:
         per = {}
-        with open(os.path.join(root, f"pmc_{name}", "pmc_counter_collection.csv")) as f:
-            for r in csv.DictReader(f):
-                if "icp_fused_kernel" in r["Kernel_Name"]:
-                    per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
-                    per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for r in _rows(os.path.join(root, f"pmc_{name}", "pmc_counter_collection.csv")):
+            if "icp_fused_kernel" in r["Kernel_Name"]:
+                per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+                per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
         for c, d in per.items():
             val[c] = float(np.mean(list(d.values())))
     waves = val["SQ_WAVES"]
@@ -209,86 +237,186 @@ def summarize_counters(root):
     print("\n".join(out))
 
 
-def roofline_micro(torch, kdnn, work_bytes, n, nodes_avg, pts_avg, kern_ms):
-    """The library's micro-benchmarks at three working-set sizes: the fused
-    kernel's own (box array + points + index map: one XCD's L2), 64 MiB (the
-    Infinity Cache) and 512 MiB (HBM).  Random-gather GB/s for records of 16 B
-    (a point), 48 B (a child-pair box load) and 256 B (a leaf chunk), 2^20
-    lanes x 16 records, best of three seeds; dependent-load latency per hop
-    for 64 lanes chasing a random cycle of 64-byte records.  Then the fused
-    kernel's floor at its own level: its box-pair, leaf and per-point bytes
-    each at the L2 rate for that record shape."""
-    sizes = {"l2_working_set": int(work_bytes), "infinity_cache": 64 << 20, "hbm": 512 << 20}
+# ------------------------------------------------------------ measurement
+class Gpu:
+    """torch, the library, the launch stream and a calibrated spin length."""
+
+    def __init__(self):
+        import torch
+
+        import kd_tree_nn_amd as kdnn
+        assert torch.cuda.is_available(), "bench needs a HIP device"
+        torch.cuda.set_device(0)
+        self.torch, self.kdnn = torch, kdnn
+        self.stream = torch.cuda.current_stream()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1 << 20)
+        c0.record(self.stream)
+        torch.cuda._sleep(1 << 24)
+        c1.record(self.stream)
+        torch.cuda.synchronize()
+        # a spin kernel of ~25 ms queued before a batch of launches keeps the GPU
+        # from running dry while the host enqueues them
+        self.spin = int((1 << 24) * 25.0 / max(c0.elapsed_time(c1), 1e-3))
+
+    def dev(self, a):
+        import numpy as np
+        return self.torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+    def events(self, k):
+        E = self.torch.cuda.Event
+        return [(E(enable_timing=True), E(enable_timing=True)) for _ in range(k)]
+
+
+def gather_ceilings(g, size_bytes):
+    """The library's micro-benchmarks at one working-set size: random-gather
+    GB/s for records of 16 B (a point), 48 B (a child-pair box run) and 256 B
+    (a leaf chunk), 2^20 lanes x 16 records, best of three seeds; and the
+    dependent-load latency of 64 lanes chasing a random cycle of 64-B records."""
+    torch, kdnn = g.torch, g.kdnn
+    size = max(int(size_bytes) - int(size_bytes) % 4096, 1 << 16)
     lanes, rounds = 1 << 20, 16
-    out = {}
-    for lvl, size in sizes.items():
-        size -= size % 4096
-        buf = torch.empty(size // 4, dtype=torch.int32, device="cuda")
-        e = {"mib": round(size / 2 ** 20, 2)}
-        for words in (1, 3, 16):
-            kdnn.gather_bench(buf, words, lanes, rounds)
-            ms = min(kdnn.gather_bench(buf, words, lanes, rounds, seed=s_) for s_ in (1, 2, 3))
-            e[f"gather_gbs_{16 * words}B"] = round(lanes * rounds * words * 16 / (ms * 1e-3) / 1e9, 1)
-        nrec = size // 64
-        perm = torch.randperm(nrec, device="cuda", dtype=torch.int64)
-        nxt = torch.zeros(nrec * 16, dtype=torch.int32, device="cuda")
-        nxt[perm * 16] = torch.roll(perm, -1).to(torch.int32)
-        steps = 4000
-        kdnn.chase_bench(nxt, 1, 200)
-        e["latency_ns"] = round(kdnn.chase_bench(nxt, 1, steps) * 1e6 / steps, 1)
-        out[lvl] = e
-        del buf, perm, nxt
-    l2 = out["l2_working_set"]
-    t_min = n * (24 * nodes_avg / l2["gather_gbs_48B"] + 16 * pts_avg / l2["gather_gbs_256B"]
-                 + 32 / l2["gather_gbs_16B"]) / 1e9
-    out["fused_kernel_at_l2"] = {
-        "floor_us": round(t_min * 1e6, 2), "measured_us": round(kern_ms * 1e3, 2),
-        "frac": round(t_min / (kern_ms * 1e-3), 4),
-        "note": "floor = box-pair bytes at the 48 B rate + leaf bytes at the 256 B rate + "
-                "source/match bytes at the 16 B rate, all for this working set"}
-    return out
+    buf = torch.empty(size // 4, dtype=torch.int32, device="cuda")
+    e = {"mib": round(size / 2 ** 20, 2)}
+    for words in (1, 3, 16):
+        kdnn.gather_bench(buf, words, lanes, rounds)
+        ms = min(kdnn.gather_bench(buf, words, lanes, rounds, seed=s_) for s_ in (1, 2, 3))
+        e[f"gather_gbs_{16 * words}B"] = round(lanes * rounds * words * 16 / (ms * 1e-3) / 1e9, 1)
+    nrec = size // 64
+    perm = torch.randperm(nrec, device="cuda", dtype=torch.int64)
+    nxt = torch.zeros(nrec * 16, dtype=torch.int32, device="cuda")
+    nxt[perm * 16] = torch.roll(perm, -1).to(torch.int32)
+    steps = 4000
+    kdnn.chase_bench(nxt, 1, 200)
+    e["latency_ns"] = round(kdnn.chase_bench(nxt, 1, steps) * 1e6 / steps, 1)
+    return e
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--kernel-reps", type=int, default=10)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--headline-only", action="store_true",
-                    help="skip the rejection, leaf/axis sweep, LiDAR batch and voxel sections "
-                         "(the kernel trace of the Scene workload alone)")
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="only: 30 fused launches of the Scene ICP iterations, then a "
-                         f"{COPY_MIB} MiB device copy (calibration for HBM counters)")
-    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write the profiles/ summaries from rocprofv3 CSV output and exit")
-    ap.add_argument("--summarize-counters", metavar="OUT_DIR",
-                    help="write the profiles/ counter summary from gpurun_out/pmc_<set> and exit")
-    args = ap.parse_args()
-    if args.summarize_counters:
-        summarize_counters(args.summarize_counters)
-        return
-    if args.summarize:
-        summarize(*args.summarize)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
-        sys.exit(2)
+def level_of(bytes_, l2_bytes):
+    return "l2" if bytes_ <= l2_bytes else ("infinity_cache" if bytes_ <= (256 << 20) else "hbm")
 
+
+def search_roofline(n, nodes_avg, pts_avg, per_query_fixed, kern_s, ceil, level, what):
+    """Roofline of one search launch of n queries.
+
+    Algorithmic bytes per query, as the path's byte model counts them: 32 B
+    per node record visited, 12 B per leaf point scanned, plus the fixed
+    per-query bytes (index read, query, and -- fused -- original source and
+    matched point, or -- nn_query -- the two outputs).  Peak: the measured
+    random-gather bandwidth of the level holding the tree, for the record
+    shapes the search reads (node bytes at the 48-B child-pair-run rate, leaf
+    bytes at the 256-B leaf-chunk rate, fixed bytes at the 16-B rate),
+    combined as the byte-weighted harmonic mean; frac = achieved / peak, i.e.
+    the time those bytes take at the measured rates over the kernel time."""
+    b_nodes, b_pts = 32.0 * nodes_avg, 12.0 * pts_avg
+    per_query = b_nodes + b_pts + per_query_fixed
+    bytes_launch = n * per_query
+    achieved = bytes_launch / kern_s / 1e9
+    t_floor = n * (b_nodes / ceil["gather_gbs_48B"] + b_pts / ceil["gather_gbs_256B"]
+                   + per_query_fixed / ceil["gather_gbs_16B"]) / 1e9
+    peak = bytes_launch / t_floor / 1e9
+    return {
+        "bound": level, "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "GB/s",
+        "frac": round(achieved / peak, 4),
+        "hbm_context": {"peak": HBM_PEAK_GBS, "frac": round(achieved / HBM_PEAK_GBS, 4)},
+        "bytes_per_launch": round(bytes_launch), "bytes_per_query": round(per_query, 2),
+        "nodes_per_query": round(nodes_avg, 3), "points_per_query": round(pts_avg, 3),
+        "fixed_bytes_per_query": per_query_fixed,
+        "kernel_us": round(kern_s * 1e6, 3), "floor_us": round(t_floor * 1e6, 3),
+        "ceilings": ceil,
+        "byte_model": f"{what}: 32 B x node records + 12 B x leaf points + "
+                      f"{per_query_fixed} B per query; node and point counts from the "
+                      "instrumented single-lane traversal of the same queries",
+    }
+
+
+def time_fused(g, tree, src, ws, Rts, reps):
+    """The fused kernel at every iteration's transform, `reps` times: its own
+    duration (the library's event pair stamped by the search kernel's
+    dispatch) and the whole call (torch events: search + one-group reduction)."""
     import numpy as np
-    import torch
+    kdnn, torch = g.kdnn, g.torch
+    sums = torch.zeros(kdnn.KDNN_SUMS_DOUBLES, dtype=torch.float64, device="cuda")
+    tree.correspond_reduce_async(src, Rts[0][0], Rts[0][1], sums, ws)   # order, if any
+    evs = g.events(reps * len(Rts))
+    for r in range(reps):
+        torch.cuda._sleep(g.spin)
+        for k, (R, t) in enumerate(Rts):
+            e0, e1 = evs[r * len(Rts) + k]
+            e0.record(g.stream)
+            tree.correspond_reduce_async(src, R, t, sums, ws, flags=kdnn.KDNN_ICP_REUSE_ORDER)
+            e1.record(g.stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    kdnn.timing_begin(reps * len(Rts))
+    for r in range(reps):
+        torch.cuda._sleep(g.spin)
+        for R, t in Rts:
+            tree.correspond_reduce_async(src, R, t, sums, ws, flags=kdnn.KDNN_ICP_REUSE_ORDER)
+    torch.cuda.synchronize()
+    kern_ms = kdnn.timing_end().astype(np.float64)
+    assert len(kern_ms) == reps * len(Rts)
+    return kern_ms, call_ms
 
-    import kd_tree_nn_amd as kdnn
+
+def time_query(g, tr, q, sort, reps=100, warm=10):
+    """nn_query: whole calls (torch events on the launch stream: the Morton
+    ordering, when applied, and the search) and the search kernel alone (the
+    library's event pair), ms."""
+    import numpy as np
+    torch, kdnn = g.torch, g.kdnn
+    qws = tr.query_workspace(len(q))
+    out = (torch.empty(len(q), dtype=torch.int32, device="cuda"),
+           torch.empty(len(q), dtype=torch.float32, device="cuda"))
+    for _ in range(warm):
+        tr.query(q, sort=sort, out=out, workspace=qws)
+    evs = g.events(reps)
+    torch.cuda._sleep(g.spin)
+    for e0, e1 in evs:
+        e0.record(g.stream)
+        tr.query(q, sort=sort, out=out, workspace=qws)
+        e1.record(g.stream)
+    torch.cuda.synchronize()
+    call = np.array([a.elapsed_time(b) for a, b in evs])
+    kdnn.timing_begin(reps)
+    torch.cuda._sleep(g.spin)
+    for _ in range(reps):
+        tr.query(q, sort=sort, out=out, workspace=qws)
+    torch.cuda.synchronize()
+    kern = kdnn.timing_end().astype(np.float64)
+    return call, kern
+
+
+def query_counts(tr, q):
+    _, _, cn, cp = tr.query_stats(q)
+    return float(cn.double().mean()), float(cp.double().mean())
+
+
+def timed_steps(g, fn, steps):
+    """`steps` calls of fn, each timed on the host (every registration
+    synchronises), bracketed by device synchronisations: (total s, per-step s)."""
+    import numpy as np
+    g.torch.cuda.synchronize()
+    per = []
+    r = None
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        a = time.perf_counter()
+        r = fn()
+        per.append(time.perf_counter() - a)
+    g.torch.cuda.synchronize()
+    return time.perf_counter() - t0, np.array(per), r
+
+
+def ms_stats(per_s):
+    return {k: round(v * 1e3, 4) for k, v in pct(per_s).items() if k != "n"}
+
+
+# ------------------------------------------------------------------ scene
+def bench_scene(g, args, result):
+    import numpy as np
+    kdnn, torch = g.kdnn, g.torch
     import synth
-
-    assert torch.cuda.is_available(), "bench needs a HIP device"
-    torch.cuda.set_device(0)
-    ITERS = 30
-
     log("generating Scene workload")
     p = synth.scene()
     n = len(p.source)
@@ -296,302 +424,87 @@ def main():
     t0 = time.perf_counter()
     tree = kdnn.Tree(p.target, p.leaf_size)
     build_wall_ms = (time.perf_counter() - t0) * 1e3
-    info = tree.info
-    src = torch.from_numpy(p.source).cuda()
+    # a second build of the same tree: its upload excludes the runtime's
+    # one-time start-up, which the first device allocation pays
+    tree2 = kdnn.Tree(p.target, p.leaf_size)
+    info, info2 = tree.info, tree2.info
+    del tree2
+    src = g.dev(p.source)
     ws = tree.icp_workspace(n)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    sums = torch.zeros(kdnn.KDNN_SUMS_DOUBLES, dtype=torch.float64, device="cuda")
 
-    if args.profile_pass:
-        g = tree.icp(src, max_iter=ITERS, workspace=ws)
-        Rt = g["Rt_hist"]
-        for k in range(ITERS):
-            tree.correspond_reduce_async(src, Rt[k, :9], Rt[k, 9:], sums, ws)
-        a = torch.empty(COPY_MIB << 18, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        a.fill_(1.0)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log("profile pass done: icp", ITERS, "iterations +", ITERS, "fused launches +",
-            f"3 copies of {COPY_MIB} MiB")
-        return
-
-    # ---------------------------------------------------------------- headline
     log(f"warmup {args.warmup} registrations")
     for _ in range(args.warmup):
-        g = tree.icp(src, max_iter=ITERS, workspace=ws)
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} registrations x {ITERS} iterations")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        g = tree.icp(src, max_iter=ITERS, workspace=ws)
-    torch.cuda.synchronize()
-    T = time.perf_counter() - t0
-    assert g["iters"] == ITERS
+        tree.icp(src, max_iter=ITERS, workspace=ws)
+    log(f"timing {args.steps} registrations x {ITERS} iterations (host solve per iteration)")
+    T, per, r = timed_steps(g, lambda: tree.icp(src, max_iter=ITERS, workspace=ws), args.steps)
+    assert r["iters"] == ITERS
     value = args.steps * ITERS * n / T
-    iters_per_s = args.steps * ITERS / T
-    log(f"{value / 1e9:.3f} G queries/s, {iters_per_s:.0f} ICP iterations/s")
-    # the same registrations with the iterations kept on the device
+    log(f"{value / 1e9:.3f} G queries/s, {args.steps * ITERS / T:.0f} ICP iterations/s")
     for _ in range(max(args.warmup, 1)):
-        gh = tree.icp(src, max_iter=ITERS, workspace=ws, device_loop=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        gh = tree.icp(src, max_iter=ITERS, workspace=ws, device_loop=True)
-    torch.cuda.synchronize()
-    T_host = time.perf_counter() - t0
-    assert gh["iters"] == ITERS
-    log(f"device loop: {args.steps * ITERS / T_host:.0f} ICP iterations/s")
+        tree.icp(src, max_iter=ITERS, workspace=ws, device_loop=True)
+    Td, perd, rd = timed_steps(
+        g, lambda: tree.icp(src, max_iter=ITERS, workspace=ws, device_loop=True), args.steps)
+    assert rd["iters"] == ITERS
+    log(f"device loop: {args.steps * ITERS / Td:.0f} ICP iterations/s")
 
-    rej, sweep, lid, vox = None, None, None, None
-    if not args.headline_only:
-        # ---------------------------------- the same registration with rejection
-        # (article §4.4: max_dist fused into the search, then 3-sigma residual
-        # rejection and a second solve per iteration)
-        REJ = {"max_dist": 1.0, "reject_k": 3.0}
-        for _ in range(2):
-            tree.icp(src, max_iter=ITERS, workspace=ws, **REJ)
-        torch.cuda.synchronize()
-        rsteps = max(args.steps // 2, 1)
-        t0 = time.perf_counter()
-        for _ in range(rsteps):
-            gr = tree.icp(src, max_iter=ITERS, workspace=ws, **REJ)
-        torch.cuda.synchronize()
-        Tr = time.perf_counter() - t0
-        rej = {"max_dist_m": REJ["max_dist"], "reject_k": REJ["reject_k"], "steps": rsteps,
-               "icp_iters_per_s": round(rsteps * ITERS / Tr, 1),
-               "icp_iter_us": round(Tr / (rsteps * ITERS) * 1e6, 2),
-               "queries_per_s": round(rsteps * ITERS * n / Tr)}
-        log(f"with rejection: {rej['icp_iters_per_s']:.0f} ICP iterations/s")
-
-        # ------------------ builder variants: leaf size and split-axis rule sweep
-        # (article §4.1 leaf table, §4.2 max-variance vs round-robin axis)
-        log("leaf / axis sweep on the Scene target")
-        q_it0 = src
-        sweep = []
-        for rr in (False, True):
-            for leaf in (1, 4, 8, 16, 32, 64):
-                tr = kdnn.Tree(p.target, leaf, round_robin=rr)
-                inf_ = tr.info
-                out_ = (torch.empty(n, dtype=torch.int32, device="cuda"),
-                        torch.empty(n, dtype=torch.float32, device="cuda"))
-                qw = tr.query_workspace(n)
-                tr.query(q_it0, out=out_, workspace=qw)
-                ts = []
-                for _ in range(10):
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    tr.query(q_it0, out=out_, workspace=qw)
-                    e1.record(stream)
-                    ts.append((e0, e1))
-                _, _, cn_, cp_ = tr.query_stats(q_it0)
-                torch.cuda.synchronize()
-                iw = tr.icp_workspace(n)
-                tr.icp(src, max_iter=ITERS, workspace=iw)
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for _ in range(3):
-                    tr.icp(src, max_iter=ITERS, workspace=iw)
-                torch.cuda.synchronize()
-                icp_us = (time.perf_counter() - t0) / (3 * ITERS) * 1e6
-                sweep.append({
-                    "axis": "round_robin" if rr else "max_variance", "leaf": leaf,
-                    "depth": inf_["depth"], "host_build_ms": round(inf_["build_ms"], 2),
-                    "device_mb": round(inf_["device_bytes"] / 2**20, 2),
-                    "nn_query_us": round(float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3, 1),
-                    "nodes_per_query": round(float(cn_.float().mean()), 2),
-                    "points_per_query": round(float(cp_.float().mean()), 2),
-                    "icp_iter_us": round(icp_us, 1)})
-                del tr
-        log("sweep:", [(r["axis"][0], r["leaf"], r["nn_query_us"]) for r in sweep])
-
-        # ----------------------- LiDAR frame pairs: batched vs one after another
-        # (article §3.4: consecutive frames in flight together)
-        log("LiDAR: 16 frame pairs, 30 iterations each")
-        lp = synth.lidar_pairs()
-        ltrees = [kdnn.Tree(q.target, q.leaf_size) for q in lp]
-        lsrc = [torch.from_numpy(np.ascontiguousarray(q.source)).cuda() for q in lp]
-        bws = kdnn.icp_batch_workspace([len(x) for x in lsrc])
-        lws = [t_.icp_workspace(len(x)) for t_, x in zip(ltrees, lsrc)]
-
-        def run_batch():
-            return kdnn.icp_batch(ltrees, lsrc, max_iter=ITERS, workspace=bws)
-
-        def run_seq():
-            return [t_.icp(x, max_iter=ITERS, workspace=w_, sort=False)
-                    for t_, x, w_ in zip(ltrees, lsrc, lws)]
-
-        lid = {"pairs": len(lp), "points_per_frame": int(np.mean([len(x) for x in lsrc])),
-               "iterations": ITERS}
-        for name, fn in (("batched", run_batch), ("sequential", run_seq)):
-            fn()
-            torch.cuda.synchronize()
-            reps = 5
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                fn()
-            torch.cuda.synchronize()
-            T_ = (time.perf_counter() - t0) / reps
-            q_ = sum(len(x) for x in lsrc) * ITERS
-            lid[name] = {"ms_per_16_pairs": round(T_ * 1e3, 3), "pairs_per_s": round(len(lp) / T_, 1),
-                         "icp_iters_per_s": round(len(lp) * ITERS / T_, 1),
-                         "queries_per_s": round(q_ / T_)}
-        lid["speedup"] = round(lid["sequential"]["ms_per_16_pairs"] / lid["batched"]["ms_per_16_pairs"], 2)
-        log(f"LiDAR batched {lid['batched']['pairs_per_s']} pairs/s, "
-            f"sequential {lid['sequential']['pairs_per_s']} pairs/s")
-
-        # ------------------------------- voxel-grid down-sampling (article §4.3)
-        # ~1M points: the first 8 LiDAR frames stacked (each in its own sensor
-        # frame), filtered at 0.2 m (the article's outdoor range 0.2-0.5 m)
-        vox_in = torch.cat(lsrc[:8]).contiguous()
-        vws = torch.empty(int(kdnn._lib.lib().voxel_downsample_workspace_bytes(len(vox_in))),
-                          dtype=torch.uint8, device="cuda")
-        vox = {"input_points": int(len(vox_in)), "leaf_m": 0.2}
-        vout = kdnn.voxel_downsample(vox_in, 0.2, workspace=vws)
-        torch.cuda.synchronize()
-        reps = 10
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            vout = kdnn.voxel_downsample(vox_in, 0.2, workspace=vws)
-        torch.cuda.synchronize()
-        Tv = (time.perf_counter() - t0) / reps
-        vox.update({"voxels": int(len(vout)), "ms": round(Tv * 1e3, 3),
-                    "points_per_s": round(len(vox_in) / Tv),
-                    "note": "wall time of the synchronous call (two host round trips included)"})
-        log(f"voxel filter: {vox['input_points']} -> {vox['voxels']} in {vox['ms']} ms")
-
-    # ------------------------------------------- fused kernel: events per launch
-    # The library launches on torch's current stream.  Its timing facility
-    # records a HIP event pair around the search kernel of each launch; torch
-    # events around each call time the whole call (search kernel + the
-    # one-group reduction).  A spin kernel queued ahead of every 30 launches
-    # keeps the GPU from running dry while the host enqueues them, so that the
-    # events time the kernels and not the host.
-    Rt = g["Rt_hist"]
-    tree.correspond_reduce_async(src, Rt[0, :9], Rt[0, 9:], sums, ws)   # order, if any
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(1 << 20)
-    c0.record(stream)
-    torch.cuda._sleep(1 << 24)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    spin_cycles = int((1 << 24) * 25.0 / max(c0.elapsed_time(c1), 1e-3))   # ~25 ms
+    Rt = r["Rt_hist"]
     Rts = [(Rt[k, :9].copy(), Rt[k, 9:].copy()) for k in range(ITERS)]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.kernel_reps * ITERS)]
-    # pass 1: whole calls (torch events); pass 2: the search kernel alone
-    # (library events, which add their own markers between the two kernels)
-    for r in range(args.kernel_reps):
-        torch.cuda._sleep(spin_cycles)
-        for k in range(ITERS):
-            e0, e1 = evs[r * ITERS + k]
-            e0.record(stream)
-            tree.correspond_reduce_async(src, Rts[k][0], Rts[k][1], sums, ws,
-                                         flags=kdnn.KDNN_ICP_REUSE_ORDER)
-            e1.record(stream)
-    torch.cuda.synchronize()
-    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    kdnn.timing_begin(args.kernel_reps * ITERS)
-    for r in range(args.kernel_reps):
-        torch.cuda._sleep(spin_cycles)
-        for k in range(ITERS):
-            tree.correspond_reduce_async(src, Rts[k][0], Rts[k][1], sums, ws,
-                                         flags=kdnn.KDNN_ICP_REUSE_ORDER)
-    torch.cuda.synchronize()
-    kern_ms = kdnn.timing_end().astype(np.float64)
-    assert len(kern_ms) == args.kernel_reps * ITERS
-    kern_avg_ms = float(kern_ms.mean())
-    log(f"fused kernel: mean {kern_avg_ms * 1e3:.1f} us, median {np.median(kern_ms) * 1e3:.1f} us;"
-        f" whole call mean {call_ms.mean() * 1e3:.1f} us")
+    kern_ms, call_ms = time_fused(g, tree, src, ws, Rts, args.kernel_reps)
+    kern_s = float(kern_ms.mean()) * 1e-3
+    log(f"fused kernel: mean {kern_s * 1e6:.1f} us, median {np.median(kern_ms) * 1e3:.1f} us; "
+        f"whole call mean {call_ms.mean() * 1e3:.1f} us")
 
-    # host rigid solve alone (what each iteration does between two launches)
+    # host SVD solve alone, through the C ABI from Python (an upper bound)
     sd = tree.correspond_reduce(src, Rt[0, :9], Rt[0, 9:], workspace=ws)
     t0 = time.perf_counter()
-    for _ in range(200):
+    for _ in range(500):
         kdnn.procrustes(sd)
-    solve_us = (time.perf_counter() - t0) / 200 * 1e6
+    solve_us = (time.perf_counter() - t0) / 500 * 1e6
 
-    # algorithmic bytes of one launch, per iteration's transform
-    nodes_tot, pts_tot = [], []
-    for k in range(ITERS):
-        q = kdnn.transform(src, Rt[k, :9], Rt[k, 9:])
-        _, _, cn, cp = tree.query_stats(q)
-        nodes_tot.append(int(cn.sum()))
-        pts_tot.append(int(cp.sum()))
-    nodes_avg = float(np.mean(nodes_tot)) / n
-    pts_avg = float(np.mean(pts_tot)) / n
-    # per source point: the box of every node record the search reads (24 B),
-    # every leaf point scanned (16 B: x, y, z, original index), the source point
-    # (12 B), its matched target point and that point's slot (16 + 4 B), and its
-    # slot in the traversal order when ordered (4 B).  The 136 B of partial sums
-    # each work-group writes are left out (< 0.1%).
-    per_query = (24 * nodes_avg + 16 * pts_avg + 12 + 20
-                 + (4 if info["auto_sort_icp"] else 0))
-    bytes_launch = n * per_query
-    achieved = bytes_launch / (kern_avg_ms * 1e-3) / 1e9
-    # one descent to a leaf and nothing else: the root box, both children's
-    # boxes at each of D levels, one leaf's points, the source and its match
-    descent_lb = 24 * (2 * info["depth"] + 1) + 16 * (n / 2 ** info["depth"]) + 32
+    # node records and leaf points per query: the instrumented traversal of
+    # every iteration's queries
+    cnts = [query_counts(tree, kdnn.transform(src, R, t)) for R, t in Rts]
+    nodes_avg = float(np.mean([c[0] for c in cnts]))
+    pts_avg = float(np.mean([c[1] for c in cnts]))
+    work = 24 * 2 ** (info["depth"] + 1) + 16 * (len(p.target) + 16) + 4 * len(p.target)
+    ceil = gather_ceilings(g, work)
+    # fused: index read 4 + query 12 + original source 12 + matched point 12
+    roof = search_roofline(n, nodes_avg, pts_avg, 4 + 12 + 12 + 12, kern_s, ceil,
+                           level_of(work, info["l2_bytes"]), "fused correspondence kernel")
+    traffic, traffic_src = committed_traffic()
+    roof.update({
+        "traffic": None if traffic is None else round(traffic),
+        "traffic_source": traffic_src,
+        "kernel": "icp_fused_kernel<1, 16>",
+        "kernel_time_source": "mean of the library's dispatch-stamped event pairs over "
+                              f"{len(kern_ms)} launches (the 30 iterations' transforms x "
+                              f"{args.kernel_reps})",
+        "kernels_hip_sha256_16": kernel_source_hash(),
+        "working_set_bytes": work,
+        "single_descent_bytes_per_query": round(32 * (info["depth"] + 1)
+                                                + 12 * (n / 2 ** info["depth"]) + 40, 1),
+    })
+    log(f"roofline: {roof['achieved']} of {roof['peak']} GB/s at {roof['bound']} "
+        f"-> frac {roof['frac']}")
 
-    # ------------------------------------------------------ standalone nn_query
-    def time_query(tr, q, sort, reps=100, warm=10):
-        """Device time of nn_query (events on the launch stream): median, p25, p75 in ms."""
-        qws = tr.query_workspace(len(q))
-        out = (torch.empty(len(q), dtype=torch.int32, device="cuda"),
-               torch.empty(len(q), dtype=torch.float32, device="cuda"))
-        for _ in range(warm):
-            tr.query(q, sort=sort, out=out, workspace=qws)
-        evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(reps)]
-        torch.cuda._sleep(spin_cycles)
-        for e0, e1 in evs_:
-            e0.record(stream)
-            tr.query(q, sort=sort, out=out, workspace=qws)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        t_ = np.array([a.elapsed_time(b) for a, b in evs_])
-        return float(np.median(t_)), float(np.percentile(t_, 25)), float(np.percentile(t_, 75))
-
-    def nn_entry(m_, ms):
-        return {"ms": round(ms[0], 4), "p25_ms": round(ms[1], 4), "p75_ms": round(ms[2], 4),
-                "queries_per_s": round(m_ / (ms[0] * 1e-3))}
-
-    q0 = src
-    qc = kdnn.transform(src, g["R"], g["t"])
+    # standalone nn_query on the iteration-0 and the converged queries
     nnq = {"automatic_order": "morton" if info["auto_sort"] else "unsorted",
            "runs": "median and quartiles of 100 launches after 10 warm-ups"}
-    for name, q in (("iteration0", q0), ("converged", qc)):
+    qc = kdnn.transform(src, r["R"], r["t"])
+    for name, q in (("iteration0", src), ("converged", qc)):
         for sort in (True, False):
-            nnq[f"{name}_{'morton' if sort else 'unsorted'}"] = nn_entry(
-                len(q), time_query(tree, q, sort))
+            call, kern = time_query(g, tree, q, sort)
+            c = pct(call)
+            km = float(np.median(kern))
+            nnq[f"{name}_{'morton' if sort else 'unsorted'}"] = {
+                "call_us": round(c["median"] * 1e3, 2), "call_p25_us": round(c["p25"] * 1e3, 2),
+                "call_p75_us": round(c["p75"] * 1e3, 2), "search_kernel_us": round(km * 1e3, 2),
+                "order_us": round((c["median"] - km) * 1e3, 2) if sort else 0.0,
+                "queries_per_s": round(len(q) / (c["median"] * 1e-3))}
     log("nn_query:", nnq)
 
-    # the other query workloads (one nn_query pass each, the library's automatic order)
-    other = {}
-    if not args.headline_only:
-        for wname, gen, leaf in (("stress_1M_leaf8", synth.stress, 8),
-                                 ("stress_1M_leaf16", synth.stress, 16),
-                                 ("skewed_500k_leaf8", synth.skewed, 8),
-                                 ("skewed_500k_leaf16", synth.skewed, 16)):
-            pw = gen()
-            tw = kdnn.Tree(pw.target, leaf)
-            qw = torch.from_numpy(np.ascontiguousarray(pw.source)).cuda()
-            other[wname] = dict(nn_entry(len(qw), time_query(tw, qw, None, reps=20, warm=3)),
-                                automatic_order="morton" if tw.info["auto_sort"] else "unsorted",
-                                build_ms=round(tw.info["build_ms"], 1))
-            del tw, qw
-        log("other workloads:", other)
-    micro = None
-    if not args.headline_only:
-        work = 24 * 2 ** (info["depth"] + 1) + 16 * (len(p.target) + 16) + 4 * len(p.target)
-        micro = roofline_micro(torch, kdnn, work, n, nodes_avg, pts_avg, kern_avg_ms)
-        log("roofline micro-benchmarks:", micro)
-    traffic, traffic_src = committed_traffic()
-
-    result = {
+    result.update({
         "metric": METRIC,
         "value": round(value),
         "unit": "queries/s",
@@ -602,121 +515,453 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 distances, f64 transform+reduction",
+        "dtype": "f32 distances, f64 transform+reduction+solve",
         "data": "synthetic",
         "config": {
             "workload": "scene-100k-icp30",
             "target_points": len(p.target), "source_points": n, "leaf_size": p.leaf_size,
             "icp_iterations_per_step": ITERS, "tree_depth": info["depth"],
-            "step": "one 30-iteration ICP registration, tree and clouds resident",
+            "step": "one 30-iteration ICP registration (icp_align default: host SVD solve "
+                    "and convergence check per iteration), tree and clouds resident",
         },
-        "icp_iters_per_s": round(iters_per_s, 1),
-        "icp_with_rejection": rej,
-        "lidar_pairs": lid,
-        "leaf_axis_sweep": sweep,
-        "voxel_downsample": vox,
+        "icp_iters_per_s": round(args.steps * ITERS / T, 1),
         "icp_iter_us": round(T / (args.steps * ITERS) * 1e6, 2),
+        "registration_ms": ms_stats(per),
+        "icp_device_loop": {
+            "icp_iters_per_s": round(args.steps * ITERS / Td, 1),
+            "icp_iter_us": round(Td / (args.steps * ITERS) * 1e6, 2),
+            "queries_per_s": round(args.steps * ITERS * n / Td),
+            "registration_ms": ms_stats(perd),
+            "speedup_vs_host_solve": round(T / Td, 3),
+            "R_diff_vs_host_loop": float(np.linalg.norm(rd["R"] - r["R"])),
+            "note": "KDNN_ICP_DEVICE_LOOP: the iterations stay on the device (a one-group "
+                    "kernel reduces, solves with Horn's quaternion form and applies the "
+                    "convergence rule); the host enqueues all 30 and waits once"},
         "build": {"host_build_ms": round(info["build_ms"], 3),
-                  "upload_ms": round(info["upload_ms"], 3),
+                  "upload_ms_first_tree": round(info["upload_ms"], 3),
+                  "upload_ms": round(info2["upload_ms"], 3),
                   "wall_ms": round(build_wall_ms, 3),
-                  "registration_incl_build_ms": round(build_wall_ms + T / args.steps * 1e3, 3)},
-        "fused_kernel": {"name": "icp_fused_kernel", "mean_us": round(kern_avg_ms * 1e3, 2),
-                         "median_us": round(float(np.median(kern_ms)) * 1e3, 2),
-                         "p25_us": round(float(np.percentile(kern_ms, 25)) * 1e3, 2),
-                         "p75_us": round(float(np.percentile(kern_ms, 75)) * 1e3, 2),
+                  "note": "upload_ms: a second build of the same tree (the first device "
+                          "allocation also pays the runtime's start-up)"},
+        "fused_kernel": {"name": "icp_fused_kernel<1, 16>",
+                         **{f"{k}_us": round(v * 1e3, 3) for k, v in pct(kern_ms).items()
+                            if k != "n"},
                          "launches": len(kern_ms),
-                         "queries_per_s": round(n / (kern_avg_ms * 1e-3)),
+                         "queries_per_s": round(n / kern_s),
+                         "call_mean_us": round(float(call_ms.mean()) * 1e3, 2),
                          "timing": "event pair stamped by the search kernel's dispatch "
                                    "(library timing facility, hipExtLaunchKernel)"},
-        "icp_host_loop": {"icp_iters_per_s": round(args.steps * ITERS / T_host, 1),
-                          "icp_iter_us": round(T_host / (args.steps * ITERS) * 1e6, 2),
-                          "queries_per_s": round(args.steps * ITERS * n / T_host),
-                          "R_diff_vs_device_loop": float(np.linalg.norm(gh["R"] - g["R"]))},
         "icp_iteration_breakdown_us": {
-            "iteration": round(T / (args.steps * ITERS) * 1e6, 2),
-            "of_which_fused_kernel": round(kern_avg_ms * 1e3, 2),
-            "device_loop_rest": round(T / (args.steps * ITERS) * 1e6 - kern_avg_ms * 1e3, 2),
-            "host_loop_iteration": round(T_host / (args.steps * ITERS) * 1e6, 2),
-            "host_loop_correspondence_call_events": round(float(call_ms.mean()) * 1e3, 2),
-            "host_solve_through_python": round(solve_us, 2),
-            "note": "device loop (the headline): per iteration the fused kernel, then one "
-                    "work-group that sums the partials, solves and leaves the next transform "
-                    "on the device; device_loop_rest = that step kernel and the two launch "
-                    "gaps.  Host loop: host_loop_correspondence_call_events = the search "
-                    "kernel, the one-group reduction into pinned memory and the gap between "
-                    "them; the rest of its iteration is the readback wait, host solve and "
-                    "next launch.  host_solve_through_python times kdnn_procrustes called "
-                    "from Python (ctypes marshalling included): an upper bound of the C++ call"},
+            "host_loop_iteration": round(T / (args.steps * ITERS) * 1e6, 2),
+            "device_loop_iteration": round(Td / (args.steps * ITERS) * 1e6, 2),
+            "fused_kernel": round(kern_s * 1e6, 2),
+            "correspondence_call_events": round(float(call_ms.mean()) * 1e3, 2),
+            "host_svd_solve_through_python": round(solve_us, 2),
+            "note": "host loop: the search kernel, the one-group reduction into pinned "
+                    "memory (correspondence_call_events covers both and the gap between "
+                    "them), then the host's wait, SVD solve and next launch; device loop: the "
+                    "search kernel and a one-group step kernel per iteration"},
         "nn_query": nnq,
-        "other_workloads_nn_query": other,
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if traffic is None else round(traffic),
-            "traffic_source": traffic_src,
-            "kernel": "icp_fused_kernel<1>",
-            "kernels_hip_sha256_16": kernel_source_hash(),
-            "bytes_per_launch": round(bytes_launch),
-            "bytes_per_query": round(per_query, 1),
-            "nodes_per_query": round(nodes_avg, 2), "points_per_query": round(pts_avg, 2),
-            "single_descent_bytes_per_query": round(descent_lb, 1),
-            "tree_device_bytes": info["device_bytes"], "l2_bytes": info["l2_bytes"],
-            "note": "the tree fits one XCD's L2: algorithmic gather bytes vs HBM peak; "
-                    "traffic = HBM bytes the counters saw per launch",
-            "measured_levels": micro,
-        },
-    }
+        "roofline": roof,
+    })
+    return p, tree, src, ws, r
 
-    if not args.no_cpu_baseline:
-        import oracle
-        log("cpu baseline: oracle ICP registrations (30 iterations each), 1 thread, >= 10 s")
-        regs, Tc = 0, 0.0
-        while Tc < 10.0 and regs < 6:
+
+def bench_reject(g, p, tree, src, ws, args):
+    """Scene ICP with max_dist 1 m fused into the search and the 3-sigma
+    residual rejection with a second solve per iteration (article §4.4)."""
+    rej = {"max_dist_m": 1.0, "reject_k": 3.0}
+    for name, kw in (("host_loop", {}), ("device_loop", {"device_loop": True})):
+        for _ in range(2):
+            tree.icp(src, max_iter=ITERS, workspace=ws, max_dist=1.0, reject_k=3.0, **kw)
+        steps = max(args.steps // 2, 1)
+        Tr, _, _ = timed_steps(g, lambda: tree.icp(src, max_iter=ITERS, workspace=ws,
+                                                   max_dist=1.0, reject_k=3.0, **kw), steps)
+        rej[name] = {"steps": steps, "icp_iters_per_s": round(steps * ITERS / Tr, 1),
+                     "icp_iter_us": round(Tr / (steps * ITERS) * 1e6, 2),
+                     "queries_per_s": round(steps * ITERS * len(p.source) / Tr)}
+    log("with rejection:", rej)
+    return rej
+
+
+def bench_sweep(g, p, src):
+    """Builder variants: leaf size and split-axis rule (article §4.1, §4.2)."""
+    import numpy as np
+    kdnn = g.kdnn
+    n = len(p.source)
+    sweep = []
+    for rr in (False, True):
+        for leaf in (1, 4, 8, 16, 32, 64):
+            tr = kdnn.Tree(p.target, leaf, round_robin=rr)
+            inf_ = tr.info
+            call, _ = time_query(g, tr, src, None, reps=10, warm=2)
+            cn, cp = query_counts(tr, src)
+            iw = tr.icp_workspace(n)
+            tr.icp(src, max_iter=ITERS, workspace=iw)
+            Ti, _, _ = timed_steps(g, lambda: tr.icp(src, max_iter=ITERS, workspace=iw), 3)
+            sweep.append({
+                "axis": "round_robin" if rr else "max_variance", "leaf": leaf,
+                "depth": inf_["depth"], "host_build_ms": round(inf_["build_ms"], 2),
+                "device_mb": round(inf_["device_bytes"] / 2 ** 20, 2),
+                "nn_query_us": round(float(np.median(call)) * 1e3, 1),
+                "nodes_per_query": round(cn, 2), "points_per_query": round(cp, 2),
+                "icp_iter_us": round(Ti / (3 * ITERS) * 1e6, 1)})
+            del tr
+    log("sweep:", [(s["axis"][0], s["leaf"], s["nn_query_us"]) for s in sweep])
+    return sweep
+
+
+def bench_lidar(g):
+    """16 LiDAR frame pairs x 30 iterations: batched (device loop, the default;
+    and a host solve per iteration) vs one registration after another."""
+    import numpy as np
+    kdnn = g.kdnn
+    import synth
+    log("LiDAR: 16 frame pairs, 30 iterations each")
+    lp = synth.lidar_pairs()
+    ltrees = [kdnn.Tree(q.target, q.leaf_size) for q in lp]
+    lsrc = [g.dev(q.source) for q in lp]
+    bws = kdnn.icp_batch_workspace([len(x) for x in lsrc])
+    lws = [t_.icp_workspace(len(x)) for t_, x in zip(ltrees, lsrc)]
+    runs = {
+        "batched": lambda: kdnn.icp_batch(ltrees, lsrc, max_iter=ITERS, workspace=bws),
+        "batched_host_solve": lambda: kdnn.icp_batch(ltrees, lsrc, max_iter=ITERS, workspace=bws,
+                                                     device_loop=False),
+        "sequential": lambda: [t_.icp(x, max_iter=ITERS, workspace=w_, sort=False)
+                               for t_, x, w_ in zip(ltrees, lsrc, lws)],
+        "sequential_device_loop": lambda: [t_.icp(x, max_iter=ITERS, workspace=w_, sort=False,
+                                                  device_loop=True)
+                                           for t_, x, w_ in zip(ltrees, lsrc, lws)],
+    }
+    lid = {"pairs": len(lp), "points_per_frame": int(np.mean([len(x) for x in lsrc])),
+           "iterations": ITERS}
+    q_ = sum(len(x) for x in lsrc) * ITERS
+    for name, fn in runs.items():
+        fn()
+        _, per, _ = timed_steps(g, fn, 5)
+        med = float(np.median(per))
+        lid[name] = {"ms_per_16_pairs": round(med * 1e3, 3), "pairs_per_s": round(len(lp) / med, 1),
+                     "icp_iters_per_s": round(len(lp) * ITERS / med, 1),
+                     "queries_per_s": round(q_ / med), "runs": "median of 5"}
+    lid["speedup_batched_vs_sequential"] = round(lid["sequential"]["ms_per_16_pairs"]
+                                                 / lid["batched"]["ms_per_16_pairs"], 2)
+    log("LiDAR:", {k: v["ms_per_16_pairs"] for k, v in lid.items() if isinstance(v, dict)})
+    return lid, lp, lsrc
+
+
+def bench_voxel(g, lsrc):
+    """Voxel-grid down-sampling (article §4.3): the first 8 LiDAR frames stacked
+    (~1.05M points, each in its own sensor frame), 0.2 m voxels."""
+    import numpy as np
+    kdnn, torch = g.kdnn, g.torch
+    vox_in = torch.cat(lsrc[:8]).contiguous()
+    vws = torch.empty(int(kdnn._lib.lib().voxel_downsample_workspace_bytes(len(vox_in))),
+                      dtype=torch.uint8, device="cuda")
+    vout = kdnn.voxel_downsample(vox_in, 0.2, workspace=vws)
+    reps = 20
+    evs = g.events(reps)
+    walls = []
+    for e0, e1 in evs:
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        e0.record(g.stream)
+        vout = kdnn.voxel_downsample(vox_in, 0.2, workspace=vws)
+        e1.record(g.stream)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - a)
+    span = np.array([a.elapsed_time(b) for a, b in evs])
+    n, m = len(vox_in), len(vout)
+    # the filter's minimum traffic: every point read once, every voxel written
+    # once (centroid 12 B + count 4 B)
+    b_min = 12 * n + 16 * m
+    t = float(np.median(span)) * 1e-3
+    vox = {"input_points": int(n), "leaf_m": 0.2, "voxels": int(m),
+           "wall_ms": round(float(np.median(walls)) * 1e3, 4),
+           "device_span_ms": round(t * 1e3, 4),
+           "points_per_s": round(n / float(np.median(walls))),
+           "hbm_roofline": {"bound": "hbm", "bytes_min": b_min,
+                            "achieved": round(b_min / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(b_min / t / 1e9 / HBM_PEAK_GBS, 5)},
+           "note": "median of 20 calls; device_span = events around the synchronous call (its "
+                   "kernels and the two host round trips between them); bytes_min = one read "
+                   "of every point and one write per voxel"}
+    log(f"voxel filter: {n} -> {m} in {vox['wall_ms']} ms wall, {vox['device_span_ms']} ms span")
+    return vox
+
+
+def bench_query_workload(g, name):
+    """One nn_query pass of a Stress or Skewed configuration in the library's
+    automatic order, with its roofline at the level holding its tree."""
+    import numpy as np
+    kdnn = g.kdnn
+    import synth
+    gen, leaf = {"stress_1M_leaf8": (synth.stress, 8), "stress_1M_leaf16": (synth.stress, 16),
+                 "skewed_500k_leaf8": (synth.skewed, 8),
+                 "skewed_500k_leaf16": (synth.skewed, 16)}[name]
+    pw = gen()
+    tw = kdnn.Tree(pw.target, leaf)
+    inf_ = tw.info
+    qw = g.dev(pw.source)
+    m = len(qw)
+    call, kern = time_query(g, tw, qw, None, reps=20, warm=3)
+    cn, cp = query_counts(tw, qw)
+    sorted_ = bool(inf_["auto_sort"])
+    work = 24 * 2 ** (inf_["depth"] + 1) + 16 * (len(pw.target) + 16)
+    ceil = gather_ceilings(g, work)
+    km = float(np.median(kern))
+    # index read 4 + query 12 + outputs 8 (+ the traversal-order slot 4 when ordered)
+    roof = search_roofline(m, cn, cp, 4 + 12 + 8 + (4 if sorted_ else 0), km * 1e-3, ceil,
+                           level_of(work, inf_["l2_bytes"]), "nn_query search kernel")
+    c = pct(call)
+    out = {"queries": m, "target_points": len(pw.target), "leaf": leaf, "depth": inf_["depth"],
+           "automatic_order": "morton" if sorted_ else "unsorted",
+           "call_us": round(c["median"] * 1e3, 2), "call_p25_us": round(c["p25"] * 1e3, 2),
+           "call_p75_us": round(c["p75"] * 1e3, 2), "search_kernel_us": round(km * 1e3, 2),
+           "order_us": round((c["median"] - km) * 1e3, 2) if sorted_ else 0.0,
+           "queries_per_s": round(m / (c["median"] * 1e-3)),
+           "host_build_ms": round(inf_["build_ms"], 1),
+           "working_set_bytes": work, "roofline": roof,
+           "runs": "median and quartiles of 20 calls after 3 warm-ups"}
+    log(name, {k: out[k] for k in ("call_us", "search_kernel_us")}, "frac", roof["frac"])
+    return out, pw
+
+
+# -------------------------------------------------------------- CPU oracle
+def cpu_threads():
+    """Host threads for the oracle: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when the environment sets it (the host's share)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(cap))) if cap.isdigit() else n
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "?"
+
+
+class ThreadedSearch:
+    """The oracle's KD search of a query set split into chunks over host threads
+    (the C query keeps no global state; ctypes releases the GIL)."""
+
+    def __init__(self, tree, pool, threads):
+        self.tree, self.pool, self.k = tree, pool, threads
+
+    def query(self, q):
+        import numpy as np
+        parts = list(self.pool.map(self.tree.query, np.array_split(q, self.k * 4)))
+        return np.concatenate([a for a, _ in parts]), np.concatenate([b for _, b in parts])
+
+
+def cpu_baseline(scene_p, workloads, lidar_pairs):
+    """The oracle, as it stands, on the host: the first two of the article's
+    three baselines (§6: brute force, CPU KD-tree; the GPU is the third)."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+    import synth
+    th = cpu_threads()
+    n = len(scene_p.source)
+    res = {}
+    with cf.ThreadPoolExecutor(th) as pool:
+        otree = oracle.KDTree(scene_p.target, scene_p.leaf_size)
+        par = ThreadedSearch(otree, pool, th)
+        log(f"cpu: oracle Scene ICP, 1 thread and {th} threads")
+        t1 = []
+        for _ in range(3):
             t0 = time.perf_counter()
-            o = oracle.icp(p.target, p.source, ITERS, leaf_size=p.leaf_size)
-            Tc += time.perf_counter() - t0
-            regs += 1
+            oracle.icp(scene_p.target, scene_p.source, ITERS, tree=otree)
+            t1.append(time.perf_counter() - t0)
+        tn = []
+        o = None
+        for _ in range(3):
+            t0 = time.perf_counter()
+            o = oracle.icp(scene_p.target, scene_p.source, ITERS, tree=par)
+            tn.append(time.perf_counter() - t0)
+        m1, mn = float(np.median(t1)), float(np.median(tn))
+        res["scene_icp"] = {"threads": th, "s_per_registration_all_threads": round(mn, 3),
+                            "s_per_registration_1_thread": round(m1, 3),
+                            "queries_per_s_all_threads": round(ITERS * n / mn),
+                            "queries_per_s_1_thread": round(ITERS * n / m1),
+                            "icp_iters_per_s_all_threads": round(ITERS / mn, 2),
+                            "icp_iters_per_s_1_thread": round(ITERS / m1, 2),
+                            "runs": "median of 3 registrations each"}
+        log("cpu: brute force")
+        tiny = synth.tiny()
+        tb = []
+        for _ in range(10):
+            t0 = time.perf_counter()
+            oracle.icp(tiny.target, tiny.source, tiny.iters, nn="brute")
+            tb.append(time.perf_counter() - t0)
+        res["tiny_brute_force_icp"] = {"iterations": tiny.iters, "s": round(float(np.median(tb)), 4),
+                                       "threads": 1, "runs": "median of 10"}
+        T_ = scene_p.target
+        tsb = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(pool.map(lambda c: oracle.brute_nn(T_, c), np.array_split(scene_p.source, th * 4)))
+            tsb.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        oracle.brute_nn(T_, scene_p.source[:5000])
+        t_one = (time.perf_counter() - t0) * n / 5000
+        res["scene_brute_force_iteration"] = {
+            "pairs": n * len(T_), "s_all_threads": round(float(np.median(tsb)), 3),
+            "threads": th, "s_1_thread_estimated": round(t_one, 2),
+            "runs": f"median of 3 on {th} threads; 1 thread timed on 5,000 queries and scaled"}
+        for name, pw, leaf in workloads:
+            log(f"cpu: oracle KD {name}")
+            t0 = time.perf_counter()
+            ot = oracle.KDTree(pw.target, leaf)
+            tbuild = time.perf_counter() - t0
+            ps = ThreadedSearch(ot, pool, th)
+            tq = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                ps.query(pw.source)
+                tq.append(time.perf_counter() - t0)
+            res[name] = {"queries": len(pw.source), "threads": th,
+                         "s_query_all_threads": round(float(np.median(tq)), 3),
+                         "queries_per_s_all_threads": round(len(pw.source) / float(np.median(tq))),
+                         "oracle_build_s": round(tbuild, 2), "runs": "median of 3 passes"}
+            del ot
+        if lidar_pairs:
+            log("cpu: oracle KD ICP of the 16 LiDAR pairs")
+            t0 = time.perf_counter()
+            for q in lidar_pairs:
+                ot = oracle.KDTree(q.target, q.leaf_size)
+                oracle.icp(q.target, q.source, ITERS, tree=ThreadedSearch(ot, pool, th))
+            tl = time.perf_counter() - t0
+            res["lidar_16_pairs_icp"] = {"s": round(tl, 2), "threads": th,
+                                         "pairs_per_s": round(len(lidar_pairs) / tl, 3),
+                                         "runs": "one pass over the 16 pairs (tree builds included)"}
+    return res, th, o
+
+
+# ------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=SECTIONS, default=None,
+                    help="run one section (for a profiled run of that workload)")
+    ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="only: 30 fused launches of the Scene ICP iterations, then a "
+                         f"{COPY_MIB} MiB device copy (calibration for HBM counters)")
+    ap.add_argument("--summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ traffic summary from rocprofv3 CSV output")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "ONLY", "OUT_NAME"),
+                    help="write a profiles/ kernel-trace summary of a `--only` run")
+    ap.add_argument("--summarize-counters", metavar="OUT_DIR",
+                    help="write the profiles/ counter summary from gpurun_out/pmc_<set> and exit")
+    args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.summarize:
+        summarize(*args.summarize)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+
+    g = Gpu()
+
+    if args.profile_pass:
+        import synth
+        p = synth.scene()
+        tree = g.kdnn.Tree(p.target, p.leaf_size)
+        src = g.dev(p.source)
+        ws = tree.icp_workspace(len(p.source))
+        r = tree.icp(src, max_iter=ITERS, workspace=ws)
+        sums = g.torch.zeros(g.kdnn.KDNN_SUMS_DOUBLES, dtype=g.torch.float64, device="cuda")
+        for k in range(ITERS):
+            tree.correspond_reduce_async(src, r["Rt_hist"][k, :9], r["Rt_hist"][k, 9:], sums, ws)
+        a = g.torch.empty(COPY_MIB << 18, dtype=g.torch.float32, device="cuda")
+        b = g.torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(3):
+            b.copy_(a)
+        g.torch.cuda.synchronize()
+        log("profile pass done: icp", ITERS, "iterations +", ITERS, "fused launches +",
+            f"3 copies of {COPY_MIB} MiB")
+        return
+
+    def want(s):
+        return args.only is None or args.only == s
+
+    result = {} if args.only in (None, "scene") else {"only": args.only}
+    scene_p = tree = src = ws = r_gpu = None
+    if want("scene"):
+        scene_p, tree, src, ws, r_gpu = bench_scene(g, args, result)
+    elif want("reject") or want("sweep"):
+        import synth
+        scene_p = synth.scene()
+        tree = g.kdnn.Tree(scene_p.target, scene_p.leaf_size)
+        src = g.dev(scene_p.source)
+        ws = tree.icp_workspace(len(scene_p.source))
+    if want("reject"):
+        result["icp_with_rejection"] = bench_reject(g, scene_p, tree, src, ws, args)
+    if want("sweep"):
+        result["leaf_axis_sweep"] = bench_sweep(g, scene_p, src)
+    lpairs = lsrc = None
+    if want("lidar"):
+        result["lidar_pairs"], lpairs, lsrc = bench_lidar(g)
+    if want("voxel"):
+        if lsrc is None:
+            import synth
+            lsrc = [g.dev(q.source) for q in synth.lidar_pairs()[:8]]
+        result["voxel_downsample"] = bench_voxel(g, lsrc)
+    other, cpu_workloads = {}, []
+    for name in QUERY_WORKLOADS:
+        if want(name):
+            other[name], pw = bench_query_workload(g, name)
+            cpu_workloads.append((name, pw, other[name]["leaf"]))
+    if other:
+        result["other_workloads_nn_query"] = other
+
+    if not args.no_cpu_baseline and args.only is None:
+        res, th, o = cpu_baseline(scene_p, cpu_workloads, lpairs)
+        sc = res["scene_icp"]
         result["cpu_baseline"] = {
-            "value": round(regs * ITERS * n / Tc), "unit": "queries/s", "cores": 1,
+            "value": sc["queries_per_s_all_threads"], "unit": "queries/s", "cores": th,
             "kind": "oracle",
-            "sample": f"{regs} full Scene registrations (30 ICP iterations x 100k queries each) "
-                      "with the oracle's C KD-tree search and numpy fp64 reduction/Horn "
-                      f"solve, {Tc:.2f} s wall",
-            "icp_iters_per_s": round(regs * ITERS / Tc, 2),
-            "R_diff_vs_gpu": float(np.linalg.norm(o["R"] - g["R"])),
+            "sample": f"3 full Scene registrations (30 ICP iterations x 100k queries) with the "
+                      f"oracle's C KD-tree search split over {th} host threads and its numpy "
+                      f"fp64 reduction and Horn solve; median "
+                      f"{sc['s_per_registration_all_threads']} s per registration",
+            "icp_iters_per_s": sc["icp_iters_per_s_all_threads"],
+            "value_1_thread": sc["queries_per_s_1_thread"],
+            "host": {"cpu_model": cpu_model(), "nproc": os.cpu_count(),
+                     "affinity_cpus": len(os.sched_getaffinity(0)),
+                     "omp_num_threads": os.environ.get("OMP_NUM_THREADS")},
+            "R_diff_vs_gpu": float(np.linalg.norm(o["R"] - r_gpu["R"])),
         }
-        log(f"cpu baseline {regs * ITERS * n / Tc / 1e6:.2f} M queries/s")
-        # context: the oracle's KD-tree query of one iteration's queries on every
-        # host core (threads over query chunks; the C query holds no global
-        # state and ctypes releases the GIL), and its brute force on a sample
-        import concurrent.futures as cf
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
-        otree = oracle.KDTree(p.target, p.leaf_size)
-        chunks = np.array_split(p.source, threads * 4)
-        t0 = time.perf_counter()
-        otree.query(p.source)
-        Tq1 = time.perf_counter() - t0
-        with cf.ThreadPoolExecutor(threads) as ex:
-            list(ex.map(otree.query, chunks[:threads]))  # warm
-            t0 = time.perf_counter()
-            list(ex.map(otree.query, chunks))
-            Tq = time.perf_counter() - t0
-        ns = 2000
-        t0 = time.perf_counter()
-        oracle.brute_nn(p.target, p.source[:ns])
-        Tb = time.perf_counter() - t0
-        result["cpu_context"] = {
-            "oracle_kd_nn_queries_per_s_all_cores": round(n / Tq),
-            "threads": threads,
-            "oracle_kd_nn_queries_per_s_1_thread": round(n / Tq1),
-            "brute_force_pairs_per_s_1_thread": round(ns * len(p.target) / Tb),
-            "brute_force_one_scene_iteration_s": round(Tb * n / ns, 1),
-            "note": "context only: the oracle's own KD search of one Scene iteration's "
-                    "100k queries split over host threads; brute force timed on 2,000 "
-                    "queries and scaled to 100k x 100k pairs"}
-        log(f"cpu context: {n / Tq / 1e6:.2f} M queries/s on {threads} threads, brute force "
-            f"{Tb * n / ns:.1f} s per Scene iteration")
-    print(json.dumps(result), flush=True)
+        result["cpu_context"] = res
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
 
 
 if __name__ == "__main__":
