@@ -193,15 +193,16 @@ PMC_SETS = {
 }
 
 
-def summarize_counters(root):
+def summarize_counters(root, kernel="icp_fused_kernel", out_name=None, title=None, cmd=None):
     """profiles/ summary of the three counter passes (PMC_SETS) over
-    `bench.py --profile-pass`, per dispatch of the fused kernel."""
+    `bench.py --profile-pass` (or the command given), per dispatch of the
+    kernels whose name contains `kernel`."""
     import numpy as np
     val = {}
     for name in PMC_SETS:
         per = {}
         for r in _rows(os.path.join(root, f"pmc_{name}", "pmc_counter_collection.csv")):
-            if "icp_fused_kernel" in r["Kernel_Name"]:
+            if kernel in r["Kernel_Name"]:
                 per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
                 per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
         for c, d in per.items():
@@ -220,9 +221,11 @@ def summarize_counters(root):
         ("address unit busy (TA busy / (CUs x GPU-active cycles per XCD))",
          val["TA_TA_BUSY_sum"] / (256 * val["GRBM_GUI_ACTIVE"] / 8)),
     ]
-    out = ["# rocprofv3 counters of icp_fused_kernel<1>, Scene 100k x 100k, mean per dispatch",
+    cmd = cmd or "python3 -u bench.py --profile-pass"
+    out = [f"# rocprofv3 counters of {title or 'icp_fused_kernel<1>, Scene 100k x 100k'}, "
+           "mean per dispatch",
            "# three passes, each: timeout -s KILL 120 rocprofv3 --pmc <set> --output-format csv "
-           "-d gpurun_out/pmc_<name> -o pmc -- python3 -u bench.py --profile-pass",
+           f"-d {root}/pmc_<name> -o pmc -- {cmd}",
            f"# kernels.hip code sha256[:16] (comments, whitespace dropped): {kernel_source_hash()}", ""]
     for name, cs in PMC_SETS.items():
         out.append(f"# set {name}: {cs}")
@@ -232,7 +235,8 @@ def summarize_counters(root):
     out.append("")
     for k, v in derived:
         out.append(f"{k:64s} {v:10.4g}")
-    with open(os.path.join(ROOT, "profiles", "icp_fused_kernel_scene100k_counters.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", out_name or "icp_fused_kernel_scene100k_counters.txt"),
+              "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
 
@@ -865,9 +869,18 @@ def main():
                     help="write a profiles/ kernel-trace summary of a `--only` run")
     ap.add_argument("--summarize-counters", metavar="OUT_DIR",
                     help="write the profiles/ counter summary from gpurun_out/pmc_<set> and exit")
+    ap.add_argument("--counters-of", nargs=4, metavar=("OUT_DIR", "KERNEL", "OUT_NAME", "ONLY"),
+                    help="the same for the kernels named KERNEL of `bench.py --only ONLY "
+                         "--steps 2 --warmup 1 --no-cpu-baseline`")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
+        return
+    if args.counters_of:
+        d, kern, name, only = args.counters_of
+        summarize_counters(d, kern, name, f"{kern} in bench.py --only {only}",
+                           f"python3 -u bench.py --only {only} --steps 2 --warmup 1 "
+                           "--no-cpu-baseline")
         return
     if args.summarize:
         summarize(*args.summarize)
