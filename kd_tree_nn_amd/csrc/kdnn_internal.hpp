@@ -212,6 +212,7 @@ struct VoxelWorkspace {
     float *bbox_part;       // [7][kVoxBlocks]: min xyz, max xyz, finite count
     float *bbox;            // [8]: min xyz, max xyz, finite count (as float bits), pad
     uint32_t *nvox;         // [1]
+    float *sorted;          // [n][3] the finite points' coordinates in sorted order
 };
 size_t voxel_ws_bytes(int64_t n);
 VoxelWorkspace carve_voxel_workspace(void *ws, int64_t n);
