@@ -300,38 +300,63 @@ def level_of(bytes_, l2_bytes):
     return "l2" if bytes_ <= l2_bytes else ("infinity_cache" if bytes_ <= (256 << 20) else "hbm")
 
 
-def search_roofline(n, nodes_avg, pts_avg, per_query_fixed, kern_s, ceil, level, what):
+def search_roofline(n, nodes_avg, pts_avg, per_query_fixed, kern_s, ceil, level, what,
+                    replay_s, replay_info):
     """Roofline of one search launch of n queries.
 
     Algorithmic bytes per query, as the path's byte model counts them: 32 B
     per node record visited, 12 B per leaf point scanned, plus the fixed
     per-query bytes (index read, query, and -- fused -- original source and
-    matched point, or -- nn_query -- the two outputs).  Peak: the measured
-    random-gather bandwidth of the level holding the tree, for the record
-    shapes the search reads (node bytes at the 48-B child-pair-run rate, leaf
-    bytes at the 256-B leaf-chunk rate, fixed bytes at the 16-B rate),
-    combined as the byte-weighted harmonic mean; frac = achieved / peak, i.e.
-    the time those bytes take at the measured rates over the kernel time."""
+    matched point, or -- nn_query -- the two outputs).
+
+    Peak: the replay ceiling (kdnn_replay_bench) -- the time the memory system
+    takes to deliver exactly the records this launch's queries visit, in the
+    launch's own work-groups, waves and XCDs, step by step across each wave's
+    queries, with the dependencies removed -- plus the fixed bytes at the
+    measured 16-B random-gather rate; peak = bytes / that time and frac =
+    achieved / peak = that time / kernel time.  A uniform random gather over
+    the working set (`random_gather`, context) misses what the tree's hot top
+    levels and neighbouring queries get from L1 and L2, and under-rates
+    launches whose queries share records (its fraction exceeds 1 there)."""
     b_nodes, b_pts = 32.0 * nodes_avg, 12.0 * pts_avg
     per_query = b_nodes + b_pts + per_query_fixed
     bytes_launch = n * per_query
     achieved = bytes_launch / kern_s / 1e9
-    t_floor = n * (b_nodes / ceil["gather_gbs_48B"] + b_pts / ceil["gather_gbs_256B"]
-                   + per_query_fixed / ceil["gather_gbs_16B"]) / 1e9
+    t_fixed = n * per_query_fixed / ceil["gather_gbs_16B"] / 1e9
+    t_gather = n * (b_nodes / ceil["gather_gbs_48B"] + b_pts / ceil["gather_gbs_256B"]) / 1e9 \
+        + t_fixed
+    t_floor = replay_s + t_fixed
     peak = bytes_launch / t_floor / 1e9
+    g_peak = bytes_launch / t_gather / 1e9
+    ri = replay_info
     return {
         "bound": level, "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "GB/s",
         "frac": round(achieved / peak, 4),
+        "peak_source": "replay of the launch's own record stream without dependencies "
+                       "(kdnn_replay_bench) + fixed bytes at the 16-B random-gather rate",
         "hbm_context": {"peak": HBM_PEAK_GBS, "frac": round(achieved / HBM_PEAK_GBS, 4)},
         "bytes_per_launch": round(bytes_launch), "bytes_per_query": round(per_query, 2),
         "nodes_per_query": round(nodes_avg, 3), "points_per_query": round(pts_avg, 3),
         "fixed_bytes_per_query": per_query_fixed,
         "kernel_us": round(kern_s * 1e6, 3), "floor_us": round(t_floor * 1e6, 3),
-        "ceilings": ceil,
+        "replay": {"us": round(replay_s * 1e6, 3), "bytes_loaded": ri["bytes"],
+                   "gbs_loaded": round(ri["bytes"] / replay_s / 1e9, 1),
+                   "visits": ri["visits"], "truncated_queries": ri["truncated"],
+                   "launch": {"blocks": ri["blocks"], "queries_per_wave": ri["queries_per_wave"],
+                              "spread": bool(ri["spread"])}},
+        "random_gather": {"peak": round(g_peak, 1), "frac": round(achieved / g_peak, 4),
+                          "floor_us": round(t_gather * 1e6, 3), "ceilings": ceil},
         "byte_model": f"{what}: 32 B x node records + 12 B x leaf points + "
                       f"{per_query_fixed} B per query; node and point counts from the "
                       "instrumented single-lane traversal of the same queries",
     }
+
+
+def replay_time(tree, q, icp, reps):
+    """Median replay time (s) of the launch over queries q, and what it replayed."""
+    import numpy as np
+    ms, info = tree.replay_bench(q, icp=icp, reps=reps)
+    return float(np.median(ms)) * 1e-3, info
 
 
 def time_fused(g, tree, src, ws, Rts, reps):
@@ -468,14 +493,24 @@ def bench_scene(g, args, result):
 
     # node records and leaf points per query: the instrumented traversal of
     # every iteration's queries
-    cnts = [query_counts(tree, kdnn.transform(src, R, t)) for R, t in Rts]
+    # every iteration's queries, and the replay of each in the fused kernel's
+    # launch shape
+    cnts, reps_s = [], []
+    for R, t in Rts:
+        qk = kdnn.transform(src, R, t)
+        cnts.append(query_counts(tree, qk))
+        rs, rinfo = replay_time(tree, qk, True, 5)
+        reps_s.append(rs)
     nodes_avg = float(np.mean([c[0] for c in cnts]))
     pts_avg = float(np.mean([c[1] for c in cnts]))
     work = 24 * 2 ** (info["depth"] + 1) + 16 * (len(p.target) + 16) + 4 * len(p.target)
     ceil = gather_ceilings(g, work)
     # fused: index read 4 + query 12 + original source 12 + matched point 12
     roof = search_roofline(n, nodes_avg, pts_avg, 4 + 12 + 12 + 12, kern_s, ceil,
-                           level_of(work, info["l2_bytes"]), "fused correspondence kernel")
+                           level_of(work, info["l2_bytes"]), "fused correspondence kernel",
+                           float(np.mean(reps_s)), rinfo)
+    roof["replay"]["note"] = ("mean over the 30 iterations' queries of the median of 5 "
+                              "replays each; bytes and launch of the last")
     traffic, traffic_src = committed_traffic()
     roof.update({
         "traffic": None if traffic is None else round(traffic),
@@ -746,8 +781,10 @@ def bench_query_workload(g, name):
     ceil = gather_ceilings(g, work)
     km = float(np.median(kern))
     # index read 4 + query 12 + outputs 8 (+ the traversal-order slot 4 when ordered)
+    rs, rinfo = replay_time(tw, qw, False, 20)
     roof = search_roofline(m, cn, cp, 4 + 12 + 8 + (4 if sorted_ else 0), km * 1e-3, ceil,
-                           level_of(work, inf_["l2_bytes"]), "nn_query search kernel")
+                           level_of(work, inf_["l2_bytes"]), "nn_query search kernel", rs, rinfo)
+    roof["replay"]["note"] = "median of 20 replays in nn_query's launch shape and order"
     c = pct(call)
     out = {"queries": m, "target_points": len(pw.target), "leaf": leaf, "depth": inf_["depth"],
            "automatic_order": "morton" if sorted_ else "unsorted",

@@ -48,8 +48,9 @@
 extern "C" {
 #endif
 
-#define KDNN_VERSION 4  /* 4: kdnn_moments; icp_align solves on the host unless
-                           KDNN_ICP_DEVICE_LOOP; kdnn_procrustes takes the SVD route */
+#define KDNN_VERSION 5  /* 4: kdnn_moments; icp_align solves on the host unless
+                           KDNN_ICP_DEVICE_LOOP; kdnn_procrustes takes the SVD route.
+                           5: kdnn_replay_bench */
 
 typedef enum kdnn_status {
     KDNN_OK = 0,
@@ -530,6 +531,49 @@ kdnn_status kdnn_gather_bench(const void *buf_dev, int64_t n_records, int32_t wo
                               hipStream_t stream);
 kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_t waves,
                              int32_t steps, uint32_t *sink_dev, float *ms_out, hipStream_t stream);
+
+/* Replay ceiling of one search launch, a measurement aid like the two above:
+ * the time the memory system takes to deliver exactly the records a search
+ * launch's queries visit, in that launch's work-groups, waves and XCDs, with
+ * the dependencies between them removed.  A search kernel's time over this
+ * time is how far its dependent chains and instruction stream keep it from
+ * the memory system's own limit for that access stream.
+ *   1. The instrumented single-lane search (the one nn_query_stats counts)
+ *      records each query's visits: the root's box (32 B), each internal
+ *      node's run of child boxes (48 B), each leaf (its points, loaded in
+ *      chunks as the search loads them); at most KDNN_REPLAY_CAP per query.
+ *   2. The rows are laid out per wave in the launch shape of the production
+ *      kernel: nn_query's one-lane-per-query kernel, or with KDNN_REPLAY_ICP
+ *      the fused ICP kernel's (work-groups, queries per wave, spread of
+ *      positions over each XCD's segment, order).
+ *   3. A kernel in that shape loads each wave's visits with its 64 lanes,
+ *      dealt round-robin, two in flight per lane; timed `reps` times.
+ *   q_dev  : m query points (x, y, z fp32, device), already transformed.
+ *   flags  : KDNN_QUERY_SORT / KDNN_QUERY_NO_SORT (default: the tree's
+ *            automatic choice for nn_query, or for the ICP entry points
+ *            with KDNN_REPLAY_ICP), KDNN_REPLAY_ICP.
+ *   ws_dev : kdnn_replay_workspace_bytes(tree, m, flags) bytes of device
+ *            memory (about 4 KB per query), caller-owned.
+ *   ms_out : host, reps floats: each replay's kernel time (events).
+ *   info   : host: what was replayed (below).
+ * Synchronous (returns after the replays).  Errors: EINVAL (m < 1, reps < 1,
+ * null pointers, unknown flag, small workspace), EDEVICE. */
+#define KDNN_REPLAY_ICP 4u
+#define KDNN_REPLAY_CAP 512
+typedef struct kdnn_replay_info {
+    int64_t visits;        /* root, box-run and leaf visits replayed */
+    int64_t bytes;         /* bytes one replay loads */
+    int64_t node_records;  /* node records the visits stand for (sum of nn_query_stats' nodes) */
+    int64_t leaf_points;   /* leaf points they stand for (sum of nn_query_stats' points) */
+    int64_t truncated;     /* queries with more than KDNN_REPLAY_CAP visits (tail not replayed) */
+    int64_t blocks;        /* work-groups of the launch shape */
+    int32_t queries_per_wave;
+    int32_t spread;        /* 1: positions spread over each XCD's segment */
+} kdnn_replay_info;
+size_t kdnn_replay_workspace_bytes(const kdnn_tree *tree, int64_t m, uint32_t flags);
+kdnn_status kdnn_replay_bench(const kdnn_tree *tree, const float *q_dev, int64_t m, uint32_t flags,
+                              int32_t reps, void *ws_dev, size_t ws_bytes, float *ms_out,
+                              kdnn_replay_info *info, hipStream_t stream);
 
 /* KDNN_VERSION of the built library. */
 int32_t kdnn_version(void);

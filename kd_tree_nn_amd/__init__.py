@@ -195,6 +195,26 @@ class Tree:
             | _lib.lanes_flag(lanes, budget, top_lds), _ptr(ws), ws.numel() if ws is not None else 0, _stream()), "nn_query_stats")
         return idx, d2, cn, cp
 
+    def replay_bench(self, q, icp: bool = False, sort=None, reps: int = 10):
+        """Replay ceiling of a search launch over the queries q
+        (kdnn_replay_bench): each replay's kernel time in ms (numpy array of
+        `reps`) and what was replayed (dict of kdnn_replay_info's fields).
+        icp=True takes the fused ICP kernel's launch shape, else nn_query's."""
+        torch = _torch()
+        q = _dev_points(q, "queries")
+        m = q.shape[0]
+        flags = (_lib.KDNN_REPLAY_ICP if icp else 0) | _lib.sort_flag(
+            sort, KDNN_QUERY_SORT, KDNN_QUERY_NO_SORT)
+        nbytes = int(_lib.lib().kdnn_replay_workspace_bytes(self._h, m, flags))
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        ms = (ctypes.c_float * int(reps))()
+        info = _lib.ReplayInfo()
+        _lib.check(_lib.lib().kdnn_replay_bench(self._h, _ptr(q), m, flags, int(reps), _ptr(ws),
+                                                nbytes, ms, ctypes.byref(info), _stream()),
+                   "kdnn_replay_bench")
+        out = {f: getattr(info, f) for f, _ in _lib.ReplayInfo._fields_}
+        return np.array(ms[:], dtype=np.float64), out
+
     # ------------------------------------------------------------------ ICP
     def icp_workspace(self, n: int):
         torch = _torch()

@@ -20,6 +20,8 @@ KDNN_ICP_SORT = 4
 KDNN_ICP_HOST_LOOP = 8
 KDNN_ICP_DEVICE_LOOP = 16
 KDNN_SUMS_DOUBLES = 17
+KDNN_REPLAY_ICP = 4
+KDNN_REPLAY_CAP = 512
 KDNN_NOALLOC_MAX_POINTS = 262144
 KDNN_NOALLOC_SCRATCH_BYTES = 12 << 20
 KDNN_LANES_SHIFT = 8
@@ -70,6 +72,12 @@ class IcpMoments(ctypes.Structure):
                 ("H", ctypes.c_double * 9), ("E", ctypes.c_double), ("mse", ctypes.c_double)]
 
 
+class ReplayInfo(ctypes.Structure):
+    _fields_ = [("visits", c_i64), ("bytes", c_i64), ("node_records", c_i64),
+                ("leaf_points", c_i64), ("truncated", c_i64), ("blocks", c_i64),
+                ("queries_per_wave", c_i32), ("spread", c_i32)]
+
+
 def loop_flag(device_loop):
     """ICP loop flag: None = the entry point's default, True = iterations on the
     device (KDNN_ICP_DEVICE_LOOP), False = a host solve per iteration."""
@@ -118,6 +126,9 @@ SIGNATURES = {
     "kdnn_gather_bench": (c_i32, [c_vp, c_i64, c_i32, c_i64, c_i32, c_u32, c_vp, c_fp, c_vp]),
     "kdnn_chase_bench": (c_i32, [c_vp, c_i64, c_i32, c_i32, c_vp, c_fp, c_vp]),
     "kdnn_timing_end": (c_i32, [c_fp, c_i32, ctypes.POINTER(c_i32)]),
+    "kdnn_replay_workspace_bytes": (c_sz, [c_vp, c_i64, c_u32]),
+    "kdnn_replay_bench": (c_i32, [c_vp, c_vp, c_i64, c_u32, c_i32, c_vp, c_sz, c_fp,
+                                  ctypes.POINTER(ReplayInfo), c_vp]),
     "kdnn_last_error": (ctypes.c_char_p, []),
     "kdnn_version": (c_i32, []),
 }

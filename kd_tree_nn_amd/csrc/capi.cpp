@@ -502,6 +502,53 @@ kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_
     KDNN_GUARD_END
 }
 
+size_t kdnn_replay_workspace_bytes(const kdnn_tree *tree, int64_t m, uint32_t flags)
+{
+    if (!tree || m < 1) return 0;
+    try {
+        const size_t q = (query_ws_bytes(m) + 255) & ~size_t(255);
+        return q + replay_ws_bytes(tree->dev, m, (flags & KDNN_REPLAY_ICP) != 0);
+    } catch (...) {
+        return 0;
+    }
+}
+
+kdnn_status kdnn_replay_bench(const kdnn_tree *tree, const float *q_dev, int64_t m, uint32_t flags,
+                              int32_t reps, void *ws_dev, size_t ws_bytes, float *ms_out,
+                              kdnn_replay_info *info, hipStream_t stream)
+{
+    KDNN_GUARD_BEGIN
+    if (!tree) return fail(KDNN_EINVAL, "kdnn_replay_bench: null tree");
+    if (m < 1) return fail(KDNN_EINVAL, "kdnn_replay_bench: m must be >= 1");
+    kdnn_status st = check_points(q_dev, m, "kdnn_replay_bench: queries");
+    if (st != KDNN_OK) return st;
+    if (reps < 1 || !ms_out || !info)
+        return fail(KDNN_EINVAL, "kdnn_replay_bench: reps < 1 or null ms_out / info");
+    if (flags & ~(KDNN_QUERY_NO_SORT | KDNN_QUERY_SORT | KDNN_REPLAY_ICP))
+        return fail(KDNN_EINVAL, "kdnn_replay_bench: unknown flag");
+    if ((flags & KDNN_QUERY_SORT) && (flags & KDNN_QUERY_NO_SORT))
+        return fail(KDNN_EINVAL, "kdnn_replay_bench: KDNN_QUERY_SORT and KDNN_QUERY_NO_SORT together");
+    const bool icp = (flags & KDNN_REPLAY_ICP) != 0;
+    const size_t need = kdnn_replay_workspace_bytes(tree, m, flags);
+    if (need == 0) return fail(KDNN_EINVAL, "kdnn_replay_bench: workspace size unavailable");
+    if ((st = check_ws(ws_dev, ws_bytes, need)) != KDNN_OK) return st;
+    const bool sort = (flags & KDNN_QUERY_SORT) ||
+                      (!(flags & KDNN_QUERY_NO_SORT) && (icp ? tree->auto_sort_icp : tree->auto_sort));
+    const QueryWorkspace qw = carve_query_workspace(ws_dev, m);
+    const int32_t *perm = nullptr;
+    hipError_t e = hipSuccess;
+    if (sort && (e = launch_morton_order(tree->dev, q_dev, m, nullptr, qw.sort, &perm, stream)) !=
+                    hipSuccess)
+        return hip_fail(e, "kdnn_replay_bench: order launch");
+    void *rws = static_cast<char *>(ws_dev) + ((query_ws_bytes(m) + 255) & ~size_t(255));
+    *info = kdnn_replay_info{};
+    if ((e = launch_replay(tree->dev, q_dev, m, perm, icp, rws, reps, ms_out, info, stream)) !=
+        hipSuccess)
+        return hip_fail(e, "kdnn_replay_bench");
+    return KDNN_OK;
+    KDNN_GUARD_END
+}
+
 int32_t kdnn_version(void) { return KDNN_VERSION; }
 
 kdnn_status kdtree_layout(int64_t n, const kdnn_build_params *params, int32_t *depth_out,

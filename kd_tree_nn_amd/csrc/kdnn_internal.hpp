@@ -254,6 +254,15 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
 
 // Residual rejection of the pairs the last fused launch stored (keep_matches):
 // sums of the pairs with r^2 <= kk * mean r^2 under (R, t).
+// Replay ceiling of a search launch (kdnn_replay_bench): workspace bytes and
+// the launch (trace, pack, `reps` timed replays into ms_out[0 .. reps)).
+// icp: the fused ICP kernel's launch shape, else nn_query's.
+using ReplayTally = kdnn_replay_info;
+size_t replay_ws_bytes(const DeviceTree &t, int64_t m, bool icp);
+hipError_t launch_replay(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
+                         bool icp, void *ws, int32_t reps, float *ms_out, ReplayTally *tally,
+                         hipStream_t s);
+
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
                              const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,
                              double *stat_out, uint8_t *kept, hipStream_t s,

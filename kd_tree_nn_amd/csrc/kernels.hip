@@ -590,6 +590,7 @@ struct WaveTask {
     uint32_t i;      // node being processed (kDone: task finished)
     uint32_t pend;   // pending second children, per path level
     uint32_t cn, cp;
+    uint32_t nt;     // instrumented search: visits recorded so far (trace_visit)
 };
 
 // A finished task publishes its best (and counts) to the owner's slot.
@@ -607,6 +608,17 @@ __device__ __forceinline__ void task_finish(WaveTask &w, unsigned long long *oke
         }
         w.owner = kNoOwner;
     }
+}
+
+// The instrumented search's visit stream, one row per query: 0 for the root's
+// box, an internal node i for the run of its two children's boxes, a leaf
+// node for that leaf's points.  Visits beyond the row's tcap entries are
+// counted, not stored.
+__device__ __forceinline__ void trace_visit(WaveTask &w, uint32_t *trow, uint32_t tcap,
+                                            uint32_t e)
+{
+    if (trow && w.nt < tcap) trow[w.nt] = e;
+    ++w.nt;
 }
 
 // Hand-over round: idle lanes take the shallowest pending subtree of busy
@@ -703,12 +715,17 @@ __device__ __forceinline__ float *lbs_array()
 // and each step reads its task's from there, instead of every task carrying
 // them in registers: a hand-over moves the owner only, and the loop carries
 // three registers fewer (which the compiler otherwise merges by copies).
+// trow / tcap / tcnt (STATS only, each lane its own query's): the row its
+// visits are recorded in (trace_visit), its capacity, and where the number of
+// visits goes (null: none recorded).
 template <bool STATS, bool BALANCE = true, int CH = kLeafChunk, bool QL = false>
 __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
                                             float oqz, uint64_t init, float *lbs,
                                             unsigned long long *okey, uint32_t *ocn,
                                             uint32_t *ocp, uint32_t *xfer, uint32_t quorum = 64u,
-                                            float4 *qpool = nullptr, uint32_t wq = 64u)
+                                            float4 *qpool = nullptr, uint32_t wq = 64u,
+                                            uint32_t *trow = nullptr, uint32_t tcap = 0u,
+                                            uint32_t *tcnt = nullptr)
 {
     const uint32_t p1_idle = wq < KDNN_P1_Q_SPLIT ? KDNN_P1_MIN_IDLE : KDNN_P1_MIN_IDLE_FULL;
     okey[threadIdx.x] = init;
@@ -727,10 +744,14 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
     w.pend = 0u;
     w.cn = 0u;
     w.cp = 0u;
+    w.nt = 0u;
     if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
         const float4 A = t.nodes[2];
         const float4 B = t.nodes[3];
-        if (STATS) ++w.cn;
+        if constexpr (STATS) {
+            ++w.cn;
+            trace_visit(w, trow, tcap, 0u);
+        }
         w.i = enters(box_lb(oqx, oqy, oqz, A, B), key_dist(w.key)) ? 1u : kDone;
     }
     for (;;) {
@@ -756,7 +777,10 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                 const float4 B0 = make_float4(P1.x, P1.y, 0.0f, 0.0f);
                 const float4 A1 = make_float4(P1.z, P1.w, P2.x, P2.y);
                 const float4 B1 = make_float4(P2.z, P2.w, 0.0f, 0.0f);
-                if (STATS) w.cn += 2;
+                if constexpr (STATS) {
+                    w.cn += 2;
+                    trace_visit(w, trow, tcap, i);
+                }
                 float qx = w.qx, qy = w.qy, qz = w.qz;
                 if constexpr (QL) {
                     const float4 q = qpool[w.owner];
@@ -811,7 +835,10 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                 }
                 k0 += CH;
             } while (k0 < uint32_t(end));
-            if (STATS) w.cp += uint32_t(end - begin);
+            if constexpr (STATS) {
+                w.cp += uint32_t(end - begin);
+                trace_visit(w, trow, tcap, w.i);
+            }
             const uint64_t seen = atomicMin(&okey[w.owner], (unsigned long long)key);
             w.key = seen < key ? seen : key;
             w.i = pair_next(w.i, w.pend, lbs, key_dist(w.key));
@@ -820,6 +847,9 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
         if (__ballot(w.owner != kNoOwner) == 0) break;
         if (BALANCE) task_handover<QL>(w, lbs, okey, xfer);
     }
+    // without hand-overs (STATS) the lane did all of its own query's visits
+    if constexpr (STATS)
+        if (tcnt) *tcnt = w.nt;
 }
 
 struct NnArgs {
@@ -835,6 +865,9 @@ struct NnArgs {
     uint32_t *cnt_pts;
     bool spread;  // one-lane-per-query kernel: spread_pos
     uint32_t wq;  // one-lane-per-query kernel: queries per wave (1..64)
+    uint32_t *trace;   // instrumented one-lane kernel: [m][tcap] visit rows, or null
+    uint32_t *tcount;  // [m] visits of each query (may exceed tcap)
+    uint32_t tcap;
 };
 
 // Cooperative search of one query by G >= 2 lanes.
@@ -877,12 +910,15 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             const float qx = own ? a.q[3 * i] : 0.0f;
             const float qy = own ? a.q[3 * i + 1] : 0.0f;
             const float qz = own ? a.q[3 * i + 2] : 0.0f;
-            // the instrumented kernel counts the single-lane search of each query
+            // the instrumented kernel counts (and may record) the single-lane
+            // search of each query
+            const bool tr = STATS && own && a.trace;
             wave_search<STATS, !STATS, CH, QL>(a.tree, own, qx, qy, qz, a.init,
                                                lbs + threadIdx.x, okey, ocn, ocp,
                                                xfer + (threadIdx.x & ~63u),
                                                wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u, qpool,
-                                               wq);
+                                               wq, tr ? a.trace + size_t(i) * a.tcap : nullptr,
+                                               a.tcap, tr ? a.tcount + i : nullptr);
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
@@ -2719,6 +2755,323 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
                                    nullptr, done, seq, s);
     }
     return hipGetLastError();
+}
+
+// ------------------------------------------------- replay ceiling of a search
+//
+// A measurement aid (kdnn_replay_bench), not part of any search.  The
+// ceiling a search launch is compared against is the time the memory system
+// takes to deliver the very records that launch's queries visit, in the same
+// work-groups, waves and XCDs, with every dependency removed:
+//   1. the instrumented single-lane search records each query's visits
+//      (trace_visit: the root box, each child-pair box run, each leaf);
+//   2. replay_pack_kernel walks the production launch's shape (blocks, queries
+//      per wave, spread positions, order) and lays out each wave's queries'
+//      rows step-major in one segment per (sweep, work-group, wave): every
+//      query's first visit, then every query's second, ... -- so lanes side
+//      by side replay the same step of neighbouring queries, which load the
+//      same or nearby records as they do in the search (one query's own
+//      visits dealt to adjacent lanes would miss that coherence), while the
+//      segment stays dense (no lane idles on a short row); it adds up the
+//      visits, bytes and truncated rows;
+//   3. replay_kernel, in the same shape, has each wave load its segment's
+//      records with its 64 lanes dealt the visits round-robin, two in
+//      flight per lane: the root (2 x 16 B), a box run (3 x 16 B) or a leaf
+//      (its chunks of CH x 16 B from one base, as the search loads them).
+struct ReplayArgs {
+    TreeView tree;
+    int64_t m;
+    const int32_t *perm;
+    bool spread;
+    uint32_t wq;
+    uint32_t tcap;
+    const uint32_t *rows;    // [m][tcap]
+    const uint32_t *rcount;  // [m]
+    uint32_t *packed;        // [segments][64 * tcap]
+    uint32_t *seg_total;     // [segments]
+    unsigned long long *tally;  // [4]: visits, bytes, node records, leaf points
+    unsigned long long *truncated;
+    uint32_t *sink;
+};
+
+// Bytes the replay loads for visit e (and, for the tally, node records and
+// leaf points it stands for).
+template <int CH>
+__device__ __forceinline__ void replay_cost(const TreeView &t, uint32_t e, uint32_t &bytes,
+                                            uint32_t &recs, uint32_t &pts)
+{
+    if (e == 0u) {
+        bytes = 32u;
+        recs = 1u;
+        pts = 0u;
+    } else if (e < t.first_leaf) {
+        bytes = 48u;
+        recs = 2u;
+        pts = 0u;
+    } else {
+        int32_t begin, last, end;
+        leaf_range(t, e, begin, last, end);
+        const uint32_t chunks = end > begin ? uint32_t((end - begin + CH - 1) / CH) : 1u;
+        bytes = chunks * uint32_t(CH) * 16u;
+        recs = 0u;
+        pts = uint32_t(end - begin);
+    }
+}
+
+template <int CH>
+__global__ __launch_bounds__(kWG) void replay_pack_kernel(ReplayArgs a)
+{
+    const uint32_t nb = gridDim.x;
+    const uint32_t blk = xcd_remap(blockIdx.x, nb);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint32_t wq = a.wq;
+    const int64_t QB = int64_t(kWG / 64) * wq;
+    int64_t sweep = 0;
+    for (int64_t base = int64_t(blk) * QB; base < a.m; base += int64_t(nb) * QB, ++sweep) {
+        const int64_t seg = (sweep * nb + blockIdx.x) * (kWG / 64) + wv;
+        const int64_t k = base + int64_t(wv) * wq + lane;
+        const bool own = uint32_t(lane) < wq && k < a.m;
+        const int64_t pos = own ? spread_pos(a.spread, wq, k, blk, base, nb, a.m) : k;
+        const int64_t i = own ? (a.perm ? int64_t(a.perm[pos]) : pos) : 0;
+        const uint32_t full = own ? a.rcount[i] : 0u;
+        const uint32_t len = full < a.tcap ? full : a.tcap;
+        uint32_t *const dst = a.packed + size_t(seg) * 64u * a.tcap;
+        const uint32_t *const src = a.rows + size_t(i) * a.tcap;
+        const uint64_t below = (uint64_t(1) << lane) - 1u;
+        // step j of the rows that have one, in lane order, after all of step j - 1
+        uint32_t total = 0u;
+        unsigned long long b = 0, r = 0, p = 0;
+        for (uint32_t j = 0;; ++j) {
+            const uint64_t act = __ballot(j < len);
+            if (act == 0) break;
+            if (j < len) {
+                const uint32_t e = src[j];
+                dst[total + uint32_t(__popcll(act & below))] = e;
+                uint32_t eb, er, ep;
+                replay_cost<CH>(a.tree, e, eb, er, ep);
+                b += eb;
+                r += er;
+                p += ep;
+            }
+            total += uint32_t(__popcll(act));
+        }
+        if (len) {
+            atomicAdd(&a.tally[0], (unsigned long long)len);
+            atomicAdd(&a.tally[1], b);
+            atomicAdd(&a.tally[2], r);
+            atomicAdd(&a.tally[3], p);
+        }
+        if (full > a.tcap) atomicAdd(a.truncated, 1ull);
+        if (lane == 0) a.seg_total[seg] = total;
+    }
+}
+
+// XOR of the words of the record(s) visit e stands for (loads kept alive).
+template <int CH>
+__device__ __forceinline__ uint32_t replay_load(const TreeView &t, uint32_t e)
+{
+    uint32_t x = 0u;
+    if (e == 0u) {
+        const float4 A = t.nodes[2], B = t.nodes[3];
+        x = __float_as_uint(A.x) ^ __float_as_uint(A.y) ^ __float_as_uint(A.z) ^
+            __float_as_uint(A.w) ^ __float_as_uint(B.x) ^ __float_as_uint(B.y);
+    } else if (e < t.first_leaf) {
+        const float4 *const pb = t.boxes + 3 * size_t(e);
+        const float4 P0 = pb[0], P1 = pb[1], P2 = pb[2];
+        x = __float_as_uint(P0.x) ^ __float_as_uint(P0.w) ^ __float_as_uint(P1.y) ^
+            __float_as_uint(P1.z) ^ __float_as_uint(P2.x) ^ __float_as_uint(P2.w);
+    } else {
+        int32_t begin, last, end;
+        leaf_range(t, e, begin, last, end);
+        uint32_t k0 = uint32_t(begin);
+        do {
+            const float4 *pc = t.pts + k0;
+            float4 p[CH];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) p[c] = pc[c];
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                x ^= __float_as_uint(p[c].x) ^ __float_as_uint(p[c].y) ^
+                     __float_as_uint(p[c].z) ^ __float_as_uint(p[c].w);
+            k0 += CH;
+        } while (k0 < uint32_t(end));
+    }
+    return x;
+}
+
+template <int CH>
+__global__ __launch_bounds__(kWG) void replay_kernel(ReplayArgs a)
+{
+    const uint32_t nb = gridDim.x;
+    const uint32_t blk = xcd_remap(blockIdx.x, nb);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t QB = int64_t(kWG / 64) * a.wq;
+    uint32_t acc = 0u;
+    int64_t sweep = 0;
+    for (int64_t base = int64_t(blk) * QB; base < a.m; base += int64_t(nb) * QB, ++sweep) {
+        const int64_t seg = (sweep * nb + blockIdx.x) * (kWG / 64) + wv;
+        const uint32_t T = a.seg_total[seg];
+        const uint32_t *const E = a.packed + size_t(seg) * 64u * a.tcap;
+        for (uint32_t j = uint32_t(lane); j < T; j += 128u) {
+            const uint32_t e0 = E[j];
+            const uint32_t e1 = j + 64u < T ? E[j + 64u] : kDone;
+            acc ^= replay_load<CH>(a.tree, e0);
+            if (e1 != kDone) acc ^= replay_load<CH>(a.tree, e1);
+        }
+    }
+    if (acc == 0x5eed5eedu) a.sink[0] = acc;  // keeps the loads; practically never taken
+}
+
+constexpr uint32_t kReplayCap = 512;  // visits recorded per query
+
+struct ReplayPlan {
+    int64_t blocks, segments;
+    uint32_t wq;
+    bool spread, small;
+};
+
+// The launch shape of the production kernel the replay stands in for: the
+// fused ICP kernel (icp) or nn_query's one-lane-per-query kernel.
+static ReplayPlan replay_plan(const DeviceTree &t, int64_t m, bool icp, bool ordered)
+{
+    ReplayPlan p{};
+    p.small = t.max_leaf <= kLeafChunkSmall;
+    WavePlan wp;
+    if (icp) {
+        void (*k1)(IcpArgs) = p.small ? icp_fused_kernel<1, kLeafChunkSmall> : icp_fused_kernel<1>;
+        p.spread = spread_wanted(k1, p.small ? 3 : 1, t.depth, m, ordered);
+        wp = wave_plan(k1, p.small ? 3 : 1, t.depth, m, INFINITY, KDNN_Q_TARGET_ICP);
+        if (wp.blocks > kIcpMaxBlocks) wp.blocks = kIcpMaxBlocks;
+    } else if (p.small) {
+        p.spread = spread_wanted(nn_kernel<1, false, kLeafChunkSmall>, 2, t.depth, m, ordered);
+        wp = wave_plan(nn_kernel<1, false, kLeafChunkSmall>, 2, t.depth, m, INFINITY,
+                       KDNN_Q_TARGET_NN);
+    } else {
+        p.spread = spread_wanted(nn_kernel<1, false>, 0, t.depth, m, ordered);
+        wp = wave_plan(nn_kernel<1, false>, 0, t.depth, m, INFINITY, KDNN_Q_TARGET_NN);
+    }
+    if (wp.blocks > (int64_t(1) << 20)) wp.blocks = int64_t(1) << 20;
+    p.blocks = wp.blocks;
+    p.wq = wp.q;
+    const int64_t per_sweep = p.blocks * int64_t(kWG / 64) * wp.q;
+    p.segments = (m + per_sweep - 1) / per_sweep * p.blocks * (kWG / 64);
+    return p;
+}
+
+struct ReplayWorkspace {
+    uint32_t *rows, *rcount, *packed, *seg_total, *sink;
+    int32_t *idx;
+    float *d2;
+    unsigned long long *tally;  // [5]: tally[0..3], truncated
+};
+
+static ReplayWorkspace carve_replay(void *ws, int64_t m, const ReplayPlan &p)
+{
+    char *c = static_cast<char *>(ws);
+    ReplayWorkspace w{};
+    w.tally = reinterpret_cast<unsigned long long *>(c);
+    c += 256;
+    w.sink = reinterpret_cast<uint32_t *>(c);
+    c += 256;
+    w.rcount = reinterpret_cast<uint32_t *>(c);
+    c += align256(size_t(m) * 4);
+    w.idx = reinterpret_cast<int32_t *>(c);
+    c += align256(size_t(m) * 4);
+    w.d2 = reinterpret_cast<float *>(c);
+    c += align256(size_t(m) * 4);
+    w.seg_total = reinterpret_cast<uint32_t *>(c);
+    c += align256(size_t(p.segments) * 4);
+    w.rows = reinterpret_cast<uint32_t *>(c);
+    c += align256(size_t(m) * kReplayCap * 4);
+    w.packed = reinterpret_cast<uint32_t *>(c);
+    return w;
+}
+
+size_t replay_ws_bytes(const DeviceTree &t, int64_t m, bool icp)
+{
+    // the segment count does not depend on the order (spread only permutes)
+    const ReplayPlan p = replay_plan(t, m, icp, false);
+    return 512 + 3 * align256(size_t(m) * 4) + align256(size_t(p.segments) * 4) +
+           align256(size_t(m) * kReplayCap * 4) +
+           align256(size_t(p.segments) * 64 * kReplayCap * 4);
+}
+
+hipError_t launch_replay(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
+                         bool icp, void *ws, int32_t reps, float *ms_out, ReplayTally *tally,
+                         hipStream_t s)
+{
+    const ReplayPlan p = replay_plan(t, m, icp, perm != nullptr);
+    const ReplayWorkspace w = carve_replay(ws, m, p);
+    hipError_t e = hipMemsetAsync(w.tally, 0, 5 * sizeof(unsigned long long), s);
+    if (e != hipSuccess) return e;
+    // 1. the visit rows, from the instrumented search
+    NnArgs na{};
+    na.tree = tree_view(t);
+    na.init = host_bound_key(INFINITY);
+    na.q = q;
+    na.m = m;
+    na.idx = w.idx;
+    na.d2 = w.d2;
+    na.trace = w.rows;
+    na.tcount = w.rcount;
+    na.tcap = kReplayCap;
+    const WavePlan fw = full_wave_plan(m);
+    na.wq = fw.q;
+    const size_t lds = p.small ? lbs_bytes(t.depth) : 0;
+    e = p.small ? launch_k(nn_kernel<1, true, kLeafChunkSmall>, dim3(uint32_t(fw.blocks)), kWG, lds,
+                           s, nullptr, nullptr, na)
+                : launch_k(nn_kernel<1, true>, dim3(uint32_t(fw.blocks)), kWG, 0, s, nullptr,
+                           nullptr, na);
+    if (e != hipSuccess) return e;
+    // 2. the segments, in the production launch's shape
+    ReplayArgs a{};
+    a.tree = na.tree;
+    a.m = m;
+    a.perm = perm;
+    a.spread = p.spread;
+    a.wq = p.wq;
+    a.tcap = kReplayCap;
+    a.rows = w.rows;
+    a.rcount = w.rcount;
+    a.packed = w.packed;
+    a.seg_total = w.seg_total;
+    a.tally = w.tally;
+    a.truncated = w.tally + 4;
+    a.sink = w.sink;
+    const dim3 grid{uint32_t(p.blocks)};
+    if (p.small)
+        replay_pack_kernel<kLeafChunkSmall><<<grid, kWG, 0, s>>>(a);
+    else
+        replay_pack_kernel<kLeafChunk><<<grid, kWG, 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    unsigned long long h[5];
+    if ((e = hipMemcpyAsync(h, w.tally, sizeof h, hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+        return e;
+    tally->visits = int64_t(h[0]);
+    tally->bytes = int64_t(h[1]);
+    tally->node_records = int64_t(h[2]);
+    tally->leaf_points = int64_t(h[3]);
+    tally->truncated = int64_t(h[4]);
+    tally->blocks = p.blocks;
+    tally->queries_per_wave = int32_t(p.wq);
+    tally->spread = p.spread ? 1 : 0;
+    // 3. the timed replays
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if ((e = hipEventCreate(&e0)) != hipSuccess) return e;
+    if ((e = hipEventCreate(&e1)) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return e;
+    }
+    for (int32_t r = 0; r < reps && e == hipSuccess; ++r) {
+        e = p.small ? launch_k(replay_kernel<kLeafChunkSmall>, grid, kWG, 0, s, e0, e1, a)
+                    : launch_k(replay_kernel<kLeafChunk>, grid, kWG, 0, s, e0, e1, a);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms_out[r], e0, e1);
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return e;
 }
 
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,

@@ -39,7 +39,7 @@ def test_header_symbols_exported(kdnn):
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdnn.h but not exported"
     assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
-    assert kdnn.version() == 4
+    assert kdnn.version() == 5
 
 
 @pytest.mark.parametrize("n,leaf,D", [(1, 16, 0), (16, 16, 0), (17, 16, 1), (1024, 8, 7),
