@@ -352,6 +352,66 @@ def test_device_loop_matches_host_loop(torch, kdnn):
             say("  bit-identical:", bool(np.array_equal(d["Rt_hist"], h["Rt_hist"])))
 
 
+def _step_by_step(kdnn, tree, src, iters, sort, max_dist=None, eps=0.0):
+    """icp_align's host loop spelled out through the C ABI: one
+    icp_correspond_reduce per iteration (the transform as kernel arguments),
+    kdnn_procrustes on its sums, the convergence rule in Python."""
+    from kd_tree_nn_amd import _lib
+    first = _lib.KDNN_ICP_SORT if sort else _lib.KDNN_ICP_NO_SORT
+    R, t = np.eye(3), np.zeros(3)
+    ws = tree.icp_workspace(src.shape[0])
+    E, hist = [], []
+    prev, small = 0.0, 0
+    for k in range(iters):
+        hist.append(np.concatenate([R.ravel(), t]))
+        flags = first if k == 0 else first | _lib.KDNN_ICP_REUSE_ORDER
+        sums = tree.correspond_reduce(src, R, t, flags=flags, workspace=ws, max_dist=max_dist)
+        E.append(sums["E"])
+        R, t = kdnn.procrustes(sums)
+        mse = sums["E"] / sums["n"]
+        if eps > 0.0 and k > 0:
+            small = small + 1 if abs(mse - prev) < eps else 0
+            if small >= 2:
+                break
+        prev = mse
+    return R, t, np.array(E), np.array(hist)
+
+
+def test_host_loop_matches_step_by_step(torch, kdnn):
+    """icp_align's host loop (sums into the tree's pinned slot, completion
+    word, host SVD, next launch) must follow, bit for bit, the same loop made
+    of separate icp_correspond_reduce and kdnn_procrustes calls -- including
+    where the convergence rule stops it."""
+    for name, p, leaf in [("tiny", synth.tiny(), 8), ("scene", scene(), 16),
+                          ("lidar 5", lidar()[5], 16)]:
+        tree = kdnn.Tree(p.target, leaf)
+        src = dev(torch, p.source)
+        auto = bool(tree.info["auto_sort_icp"])
+        for kw in ({}, {"sort": True}, {"sort": False}, {"max_dist": 1.0}, {"eps": 1e-7}):
+            say("host loop vs step by step", name, kw)
+            sort = kw.get("sort", auto)
+            g = tree.icp(src, max_iter=p.iters, **kw)
+            R, t, E, hist = _step_by_step(kdnn, tree, src, p.iters, sort, kw.get("max_dist"),
+                                          kw.get("eps", 0.0))
+            assert g["iters"] == len(E), (name, kw, g["iters"], len(E))
+            np.testing.assert_array_equal(g["E"][:len(E)], E)
+            np.testing.assert_array_equal(g["Rt_hist"][:len(E)], hist)
+            np.testing.assert_array_equal(g["R"], R)
+            np.testing.assert_array_equal(g["t"], t)
+    # a failed solve: the call reports it, and the tree's slot and the stream
+    # are left ready for the next call
+    p = synth.tiny()
+    tree = kdnn.Tree(p.target, 8)
+    src = dev(torch, p.source)
+    say("host loop, degenerate first iteration")
+    with pytest.raises(kdnn.KdnnError, match="EDEGENERATE"):
+        tree.icp(src, max_iter=5, R0=synth.rot_z(0.0), t0=[100.0, 0.0, 0.0], max_dist=0.01)
+    g = tree.icp(src, max_iter=p.iters)
+    o = oracle.icp(p.target, p.source, p.iters, nn="brute")
+    assert g["iters"] == p.iters
+    assert np.linalg.norm(g["R"] - o["R"]) <= R_TOL and np.max(np.abs(g["t"] - o["t"])) <= T_TOL
+
+
 def test_device_loop_eps_and_limits(torch, kdnn):
     """Convergence stop at every phase of the 4-iteration chunks, the host
     fallback beyond the record's 512 iterations, and a degenerate first
