@@ -122,11 +122,44 @@ def summarize_trace(trace_dir, only, out_name):
            f"# device: {_agent(trace_dir)}",
            f"# kernels.hip code sha256[:16] (comments, whitespace dropped): {kernel_source_hash()}",
            "",
+           "# (torch's spin_kernel, which bench.py queues ahead of timed regions so that the",
+           "#  host's launches run ahead of the device, is left out; time% is of the rest)",
+           "",
            f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}"]
+    stats = [r for r in stats if "spin_kernel" not in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in stats) or 1.0
     for r in stats[:24]:
+        r["Percentage"] = 100.0 * float(r["TotalDurationNs"]) / total
         out.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
                    f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
                    f"{float(r['Percentage']):6.2f}")
+    # the bench's event-timed batches: the dispatches queued behind a spin
+    # kernel, up to the next spin kernel or the first idle gap of 200 us (the
+    # batch's closing synchronisation) -- the launches whose event pairs give
+    # the bench line's kernel times (under the profiler those events read higher)
+    try:
+        trace = sorted(_rows(os.path.join(trace_dir, "bench_kernel_trace.csv")),
+                       key=lambda r: int(r["Start_Timestamp"]))
+        per, last_end = {}, None
+        for r in trace:
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            if "spin_kernel" in r["Kernel_Name"]:
+                last_end = t1
+                continue
+            if last_end is not None and t0 - last_end < 200000:
+                per.setdefault(r["Kernel_Name"], []).append((t1 - t0) / 1e3)
+                last_end = t1
+            else:
+                last_end = None
+        if per:
+            out += ["", "# dispatches queued behind a spin kernel (the event-timed batches):",
+                    f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'median':>9s}"]
+            for name, ds in sorted(per.items(), key=lambda kv: -sum(kv[1]))[:8]:
+                ds = sorted(ds)
+                out.append(f"{name[:72]:72s} {len(ds):6d} {sum(ds) / len(ds):9.2f} "
+                           f"{ds[len(ds) // 2]:9.2f}")
+    except (OSError, KeyError, ValueError):
+        pass
     try:
         with open(os.path.join(trace_dir, "bench.json")) as f:
             line = json.load(f)
