@@ -532,6 +532,18 @@ constexpr uint32_t kNoOwner = 0xFFFFFFFFu;
 #ifndef KDNN_DONATE_DEEPEST
 #define KDNN_DONATE_DEEPEST 0
 #endif
+// Give pending subtrees away only once the task's query has a candidate (0:
+// never gate), in launches whose waves start about half idle:
+// KDNN_DONATE_GATE_Q <= queries per wave < KDNN_P1_Q_SPLIT.  There the idle
+// lanes would otherwise take far subtrees during the first descents and
+// search them with nothing to prune.  Measured against no gate: Scene fused
+// kernel (33 per wave) 36.2 -> 35.6 us, its nn_query search 30.8 -> 29.9 us;
+// fuller waves lost (Stress 1M leaf 8, 64 per wave: 213 -> 219 us; the LiDAR
+// batch, 43 per wave: 7.93 -> 8.03 ms) and so did a 1,024-point launch of 8
+// per wave, so those stay ungated.
+#ifndef KDNN_DONATE_GATE_Q
+#define KDNN_DONATE_GATE_Q 24
+#endif
 #ifndef KDNN_P1_HANDOVER
 #define KDNN_P1_HANDOVER 1
 #endif
@@ -624,10 +636,11 @@ __device__ __forceinline__ void trace_visit(WaveTask &w, uint32_t *trow, uint32_
 // Hand-over round: idle lanes take the shallowest pending subtree of busy
 // lanes, paired by rank.  Every lane of the wave must call it together.
 // xfer: this wave's 64-entry LDS table (donor rank -> donor lane).
+// need_cand: only tasks whose best key holds a candidate give work away.
 template <bool QL = false>
 __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
                                               const unsigned long long *okey, uint32_t *xfer,
-                                              uint32_t min_idle = 1u)
+                                              uint32_t min_idle = 1u, bool need_cand = false)
 {
     const uint32_t lane = threadIdx.x & 63u;
     const uint64_t below = (uint64_t(1) << lane) - 1u;
@@ -635,7 +648,8 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
     const uint64_t idle_m = __ballot(idle);
     if (idle_m == 0 || uint32_t(__popcll(idle_m)) < min_idle) return;
     const uint32_t dep = idle ? 0u : 31u - uint32_t(__clz(int(w.i)));
-    const uint32_t avail = idle ? 0u : (w.pend & ((1u << dep) - 1u));
+    const bool hold = idle || (need_cand && uint32_t(w.key) == 0xFFFFFFFFu);
+    const uint32_t avail = hold ? 0u : (w.pend & ((1u << dep) - 1u));
     const uint64_t don_m = __ballot(avail != 0u);
     if (don_m == 0) return;
     const uint32_t nidle = uint32_t(__popcll(idle_m)), ndon = uint32_t(__popcll(don_m));
@@ -728,6 +742,8 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                                             uint32_t *tcnt = nullptr)
 {
     const uint32_t p1_idle = wq < KDNN_P1_Q_SPLIT ? KDNN_P1_MIN_IDLE : KDNN_P1_MIN_IDLE_FULL;
+    const bool need_cand = KDNN_DONATE_GATE_Q > 0 && wq >= uint32_t(KDNN_DONATE_GATE_Q) &&
+                           wq < uint32_t(KDNN_P1_Q_SPLIT);
     okey[threadIdx.x] = init;
     if constexpr (QL) qpool[threadIdx.x] = make_float4(oqx, oqy, oqz, 0.0f);
     if (STATS) {
@@ -804,7 +820,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
             }
             task_finish<STATS>(w, okey, ocn, ocp);
             if (BALANCE && KDNN_P1_HANDOVER)
-                task_handover<QL>(w, lbs, okey, xfer, p1_idle);
+                task_handover<QL>(w, lbs, okey, xfer, p1_idle, need_cand);
         }
         // Phase 2: leaves, then share the improved best of the query.
         if (w.i != kDone && w.i >= t.first_leaf) {
@@ -845,7 +861,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
         }
         task_finish<STATS>(w, okey, ocn, ocp);
         if (__ballot(w.owner != kNoOwner) == 0) break;
-        if (BALANCE) task_handover<QL>(w, lbs, okey, xfer);
+        if (BALANCE) task_handover<QL>(w, lbs, okey, xfer, 1u, need_cand);
     }
     // without hand-overs (STATS) the lane did all of its own query's visits
     if constexpr (STATS)
