@@ -216,7 +216,7 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
                         const double *t, double *sums_dev, int32_t *idx, float *d2,
                         uint32_t flags, const kdnn_icp_reject *rej, const IcpWorkspace &w,
                         hipStream_t s, uint64_t *done = nullptr, uint64_t seq = 0,
-                        const IcpLoop *loop = nullptr)
+                        const IcpLoop *loop = nullptr, int hint_mode = 0)
 {
     const float bound2 = rej ? bound_of(rej->max_dist) : INFINITY;
     const bool keep = rej && rej->reject_k > 0.0;
@@ -233,7 +233,7 @@ kdnn_status icp_enqueue(const kdnn_tree *tree, const float *src, int64_t n, cons
     }
     if (e != hipSuccess) return hip_fail(e, "icp: order launch");
     e = launch_icp_fused(tree->dev, src, n, perm, R, t, w, sums_dev, idx, d2, schedule_of(flags),
-                         bound2, keep, s, g_timing.next(), done, seq, loop);
+                         bound2, keep, s, g_timing.next(), done, seq, loop, hint_mode);
     if (e != hipSuccess) return hip_fail(e, "icp: fused kernel launch");
     return KDNN_OK;
 }
@@ -279,7 +279,7 @@ kdnn_status icp_align_on_device(kdnn_tree *mt, const float *src_dev, int64_t n, 
         const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
         L.mode = reject_k > 0.0 ? 1 : 0;
         const kdnn_status st = icp_enqueue(mt, src_dev, n, R, t, nullptr, nullptr, nullptr, f,
-                                           reject, w, stream, nullptr, 0, &L);
+                                           reject, w, stream, nullptr, 0, &L, k == 0 ? 1 : 2);
         if (st != KDNN_OK) return st;
         if (reject_k > 0.0) {
             // residuals under the first solve, then the solve of the kept pairs
@@ -966,7 +966,8 @@ kdnn_status icp_align(const kdnn_tree *tree, const float *src_dev, int64_t n, co
         const uint32_t f = k == 0 ? flags : (flags | KDNN_ICP_REUSE_ORDER);
         const uint64_t seq = ++mt->seq;
         st = icp_enqueue(tree, src_dev, n, R, t, mt->d_pinned, nullptr, nullptr, f, reject, w,
-                         stream, reinterpret_cast<uint64_t *>(mt->d_pinned + kDoneWord), seq);
+                         stream, reinterpret_cast<uint64_t *>(mt->d_pinned + kDoneWord), seq,
+                         nullptr, k == 0 ? 1 : 2);
         if (st != KDNN_OK) return st;
         hipError_t e = wait_sums(mt, seq, stream);
         if (e != hipSuccess) return hip_fail(e, "icp_align: wait for the sums");

@@ -144,6 +144,8 @@ struct IcpWorkspace {
     double *stat;       // residual statistics of the rejection step
     double *sums;       // KDNN_SUMS_DOUBLES
     IcpLoopState *loop; // device-side ICP loop state
+    uint32_t *hint;     // [n] heap index of the leaf that held each source point's
+                        // last match (0: none), written by the fused kernel
     int32_t max_blocks;
 };
 size_t icp_ws_bytes(int64_t n);
@@ -183,12 +185,17 @@ hipError_t launch_transform(const float *in, float *out, int64_t n, const double
 // loop: null, or one iteration of a device-side loop (one lane per query
 // schedule only): the search takes its transform from loop->state (R, tv
 // unused) and the step kernel replaces the reduction (sums_out unused).
+// hint_mode (one lane per query schedule; other schedules ignore it): 0
+// none, 1 record each source point's match leaf in ws.hint, 2 also start each
+// search from the leaf recorded there by the previous launch over the same
+// source (an ICP iteration after the first).
 hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, const int32_t *perm,
                             const double *R, const double *tv, const IcpWorkspace &ws,
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
                             float bound2, bool keep_matches, hipStream_t s,
                             const hipEvent_t *timing = nullptr, uint64_t *done = nullptr,
-                            uint64_t seq = 0, const IcpLoop *loop = nullptr);
+                            uint64_t seq = 0, const IcpLoop *loop = nullptr,
+                            int hint_mode = 0);
 // Start a device-side ICP loop: state <- (R0, t0), counters cleared; the
 // output record's transform <- (R0, t0), no iterations, no failure.
 hipError_t launch_icp_loop_init(IcpLoopState *state, IcpLoopOut *out, const double *R0,

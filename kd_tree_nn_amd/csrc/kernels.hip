@@ -218,6 +218,15 @@ __device__ __forceinline__ void leaf_range(const TreeView &t, uint32_t i, int32_
     last = end > begin ? end - 1 : begin;  // a valid slot even for an empty leaf
 }
 
+// The leaf (heap index) whose range holds leaf-order slot s < n: leaf j starts
+// at floor(j n / 2^D), so j is the largest with floor(j n / 2^D) <= s, i.e.
+// ceil((s + 1) 2^D / n) - 1.
+__device__ __forceinline__ uint32_t leaf_of_slot(const TreeView &t, uint32_t s)
+{
+    const uint64_t num = (uint64_t(s + 1u) << t.depth) - 1u;
+    return t.first_leaf + uint32_t(num / uint64_t(t.n));
+}
+
 // Load C points (slots first, first + S, ...; clamped to `last`), then rank
 // them.  Clamped repeats of the last point carry its own key and never
 // replace it.
@@ -698,6 +707,56 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
     }
 }
 
+// Warm start of a task at `leaf` (a heap index in [2^D, 2^(D+1)); the ICP
+// loop passes the leaf that held the query's match in the previous
+// iteration, usually at or next to the new one).  The subtrees beside the
+// leaf's path -- the sibling of its ancestor at every depth 1 .. D -- cover
+// the rest of the tree, so the task begins as if it had descended to the leaf:
+// each sibling is pending under the distance bound of its box (lbs, one
+// level per path depth), and the walk continues exactly as after a descent,
+// visiting the pending subtrees deepest first and only while their bound
+// lets them in.  The result is the same as from the root; the descent's chain
+// of dependent loads is replaced by independent loads of the sibling boxes
+// (kWarmBatch levels at a time) and the first leaf's scan gives a close bound
+// at once.
+constexpr int kWarmBatch = 4;
+__device__ __forceinline__ void warm_start(const TreeView &t, uint32_t leaf, float qx, float qy,
+                                           float qz, float *lbs, WaveTask &w)
+{
+    const uint32_t D = uint32_t(t.depth);
+    const float best = key_dist(w.key);
+    uint32_t pend = 0u;
+    for (int d0 = int(D) - 1; d0 >= 0; d0 -= kWarmBatch) {
+        float4 P[kWarmBatch][2];
+#pragma unroll
+        for (int u = 0; u < kWarmBatch; ++u) {
+            // depth of the sibling's parent (past the root: the root again, unused)
+            const uint32_t d = uint32_t(d0 - u < 0 ? 0 : d0 - u);
+            const uint32_t parent = leaf >> (D - d);
+            const uint32_t odd = ((leaf >> (D - d - 1u)) & 1u) ^ 1u;  // the sibling's side
+            const float4 *pb = t.boxes + 3 * size_t(parent) + odd;
+            P[u][0] = pb[0];
+            P[u][1] = pb[1];
+        }
+#pragma unroll
+        for (int u = 0; u < kWarmBatch; ++u) {
+            const int d = d0 - u;
+            if (d >= 0) {
+                const bool odd = (((leaf >> (D - uint32_t(d) - 1u)) & 1u) ^ 1u) != 0u;
+                const float4 A = odd ? make_float4(P[u][0].z, P[u][0].w, P[u][1].x, P[u][1].y)
+                                     : P[u][0];
+                const float4 B = odd ? make_float4(P[u][1].z, P[u][1].w, 0.0f, 0.0f)
+                                     : make_float4(P[u][1].x, P[u][1].y, 0.0f, 0.0f);
+                const float lb = box_lb(qx, qy, qz, A, B);
+                lbs[d * kWG] = lb;
+                pend |= enters(lb, best) ? (1u << d) : 0u;
+            }
+        }
+    }
+    w.pend = pend;
+    w.i = leaf;
+}
+
 // The pending-bound array of a balanced-search work-group (one float per path
 // level and lane): a static array of kDevMaxDepth levels, or (DYN) dynamic LDS
 // of lbs_bytes(D) sized to the tree, which leaves room for more resident
@@ -732,6 +791,8 @@ __device__ __forceinline__ float *lbs_array()
 // trow / tcap / tcnt (STATS only, each lane its own query's): the row its
 // visits are recorded in (trace_visit), its capacity, and where the number of
 // visits goes (null: none recorded).
+// hint (this lane's own query; 0: none): a leaf to start from instead of the
+// root (warm_start).
 template <bool STATS, bool BALANCE = true, int CH = kLeafChunk, bool QL = false>
 __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
                                             float oqz, uint64_t init, float *lbs,
@@ -739,7 +800,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                                             uint32_t *ocp, uint32_t *xfer, uint32_t quorum = 64u,
                                             float4 *qpool = nullptr, uint32_t wq = 64u,
                                             uint32_t *trow = nullptr, uint32_t tcap = 0u,
-                                            uint32_t *tcnt = nullptr)
+                                            uint32_t *tcnt = nullptr, uint32_t hint = 0u)
 {
     const uint32_t p1_idle = wq < KDNN_P1_Q_SPLIT ? KDNN_P1_MIN_IDLE : KDNN_P1_MIN_IDLE_FULL;
     const bool need_cand = KDNN_DONATE_GATE_Q > 0 && wq >= uint32_t(KDNN_DONATE_GATE_Q) &&
@@ -761,7 +822,9 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
     w.cn = 0u;
     w.cp = 0u;
     w.nt = 0u;
-    if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
+    if (!STATS && own && hint != 0u && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
+        warm_start(t, hint, oqx, oqy, oqz, lbs, w);
+    } else if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
         const float4 A = t.nodes[2];
         const float4 B = t.nodes[3];
         if constexpr (STATS) {
@@ -1197,6 +1260,11 @@ struct IcpArgs {
     uint32_t wq;        // one-lane-per-query kernel: queries per wave (1..64)
     const double *rt_dev;  // one-lane-per-query kernel, device loop: (R, t) here, not in R / t
     const uint32_t *stop;  // the same: nonzero = the loop has stopped, do nothing
+    // one-lane-per-query kernel: per source point, the heap index of the leaf
+    // that held its match (0: none) -- written after the search when non-null,
+    // and read before it as a warm start (wave_search hint) when hint_in
+    uint32_t *hint;
+    bool hint_in;
 };
 
 __device__ __forceinline__ float rigid_row(double r0, double r1, double r2, double tr, double x,
@@ -1599,11 +1667,14 @@ icp_fused_kernel(IcpArgs a)
                 else
                     icp_query(a, i, X, Y, Z, qx, qy, qz);
             }
+            // the leaf of the point's previous match, checked to be a leaf
+            uint32_t hint = own && a.hint_in ? a.hint[i] : 0u;
+            hint = hint >= a.tree.first_leaf && hint < 2u * a.tree.first_leaf ? hint : 0u;
             wave_search<false, true, CH, KDNN_QLDS>(a.tree, own, qx, qy, qz, a.init,
                                                     lbs + threadIdx.x, okey, nullptr, nullptr,
                                                     xfer + (threadIdx.x & ~63u),
                                                     wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u,
-                                                    qpool, wq);
+                                                    qpool, wq, nullptr, 0u, nullptr, hint);
             double acc[kS];
 #pragma unroll
             for (int c = 0; c < kS; ++c) acc[c] = 0.0;
@@ -1613,6 +1684,9 @@ icp_fused_kernel(IcpArgs a)
                 // the source point again (cheaper than keeping it in registers)
                 const double X = a.src[3 * i], Y = a.src[3 * i + 1], Z = a.src[3 * i + 2];
                 icp_accumulate(a, i, X, Y, Z, b, acc);
+                if (a.hint)
+                    a.hint[i] = b.idx >= 0 ? leaf_of_slot(a.tree, uint32_t(a.tree.slot_of[b.idx]))
+                                           : 0u;
             }
             double v;
             const int cw = wave_scatter_sums(acc, v);
@@ -2301,7 +2375,7 @@ size_t icp_ws_bytes(int64_t n)
     return sort_workspace_bytes(n) + align256(size_t(kS) * kIcpMaxBlocks * 8) +
            align256(size_t(kS) * kPass2Blocks * 8) + align256(size_t(kS) * 8) +
            align256(nn * 4) + align256(nn * 8) + twopass_bytes(n) + 2 * align256(nn * 4) + 256 +
-           align256(sizeof(IcpLoopState));
+           align256(sizeof(IcpLoopState)) + align256(nn * 4);
 }
 
 IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
@@ -2329,6 +2403,8 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n)
     w.stat = reinterpret_cast<double *>(p);
     p += 256;
     w.loop = reinterpret_cast<IcpLoopState *>(p);
+    p += align256(sizeof(IcpLoopState));
+    w.hint = reinterpret_cast<uint32_t *>(p);
     w.max_blocks = kIcpMaxBlocks;
     return w;
 }
@@ -2696,7 +2772,7 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
                             double *sums_out, int32_t *idx, float *d2, const Schedule &sc,
                             float bound2, bool keep_matches, hipStream_t s,
                             const hipEvent_t *timing, uint64_t *done, uint64_t seq,
-                            const IcpLoop *loop)
+                            const IcpLoop *loop, int hint_mode)
 {
     if (loop && (sc.lanes > 1 || sc.top_lds || sc.budget != 0))
         return hipErrorInvalidValue;  // the device loop runs the one-lane-per-query kernel only
@@ -2760,6 +2836,10 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         case 8: k = icp_fused_kernel<8>; break;
         case 16: k = icp_fused_kernel<16>; break;
         default: k = k1; break;
+        }
+        if (sc.lanes <= 1 && hint_mode > 0) {  // the one-lane kernel keeps the match leaves
+            a.hint = ws.hint;
+            a.hint_in = hint_mode > 1;
         }
         e = launch_k(k, grid, kWG, sc.lanes <= 1 && small ? lbs_bytes(t.depth) : 0, s, e0, e1,
                      a);
