@@ -158,6 +158,35 @@ def summarize_trace(trace_dir, only, out_name):
                 ds = sorted(ds)
                 out.append(f"{name[:72]:72s} {len(ds):6d} {sum(ds) / len(ds):9.2f} "
                            f"{ds[len(ds) // 2]:9.2f}")
+        # the fused launches of ICP registrations (runs of fused launches with
+        # only their reductions or step kernels between them, not behind a
+        # spin kernel, cut at every loop start): iteration 0 searches from the
+        # root, iterations 1.. start at the leaf of the previous match
+        runs, cur, spun = [], [], False
+        for r in trace:
+            name = r["Kernel_Name"]
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            if "icp_fused_kernel" in name:
+                cur.append(d)
+            elif "reduce_partials" in name or "icp_loop_step" in name:
+                continue
+            else:
+                if cur and not spun:
+                    runs.append(cur)
+                cur, spun = [], "spin_kernel" in name
+        if cur and not spun:
+            runs.append(cur)
+        it0 = [x for run in runs if len(run) % ITERS == 0 for x in run[0::ITERS]]
+        warm = [x for run in runs if len(run) % ITERS == 0
+                for j, x in enumerate(run) if j % ITERS]
+        if it0 and warm:
+            out += ["", f"# icp_fused_kernel inside {len(it0)} ICP registrations of {ITERS} "
+                        "iterations (runs of fused launches with only their reductions or "
+                        "step kernels between them):",
+                    f"iteration 0 (from the root): {len(it0)} launches, avg "
+                    f"{sum(it0) / len(it0):.2f} us",
+                    f"iterations 1..{ITERS - 1} (warm start): {len(warm)} launches, avg "
+                    f"{sum(warm) / len(warm):.2f} us, median {sorted(warm)[len(warm) // 2]:.2f} us"]
     except (OSError, KeyError, ValueError):
         pass
     try:
@@ -385,10 +414,11 @@ def search_roofline(n, nodes_avg, pts_avg, per_query_fixed, kern_s, ceil, level,
     }
 
 
-def replay_time(tree, q, icp, reps):
-    """Median replay time (s) of the launch over queries q, and what it replayed."""
+def replay_time(tree, q, icp, reps, prev=None):
+    """Median replay time (s) of the launch over queries q (warm-started from
+    the previous iteration's queries `prev` when given), and what it replayed."""
     import numpy as np
-    ms, info = tree.replay_bench(q, icp=icp, reps=reps)
+    ms, info = tree.replay_bench(q, icp=icp, reps=reps, prev=prev)
     return float(np.median(ms)) * 1e-3, info
 
 
@@ -524,39 +554,71 @@ def bench_scene(g, args, result):
         kdnn.procrustes(sd)
     solve_us = (time.perf_counter() - t0) / 500 * 1e6
 
-    # node records and leaf points per query: the instrumented traversal of
-    # every iteration's queries
-    # every iteration's queries, and the replay of each in the fused kernel's
-    # launch shape
-    cnts, reps_s = [], []
-    for R, t in Rts:
-        qk = kdnn.transform(src, R, t)
-        cnts.append(query_counts(tree, qk))
-        rs, rinfo = replay_time(tree, qk, True, 5)
-        reps_s.append(rs)
-    nodes_avg = float(np.mean([c[0] for c in cnts]))
-    pts_avg = float(np.mean([c[1] for c in cnts]))
+    # the fused kernel as the ICP loop runs it: the library's event pairs around
+    # every fused launch of `kernel_reps` registrations.  Iteration 0 searches
+    # from the root; iterations 1..29 start at the leaf of each point's
+    # previous match (warm start).
+    kdnn.timing_begin(ITERS * args.kernel_reps)
+    for _ in range(args.kernel_reps):
+        tree.icp(src, max_iter=ITERS, workspace=ws)
+    torch.cuda.synchronize()
+    loop_ms = kdnn.timing_end().astype(np.float64).reshape(args.kernel_reps, ITERS)
+    warm_s = float(loop_ms[:, 1:].mean()) * 1e-3
+    log(f"fused kernel in the ICP loop: iteration 0 {loop_ms[:, 0].mean() * 1e3:.1f} us, "
+        f"iterations 1..{ITERS - 1} {warm_s * 1e6:.1f} us")
+
+    # node records and leaf points per query and the replay ceiling, both for
+    # the instrumented single-lane search of each iteration's queries in the
+    # fused kernel's launch shape: warm-started from the previous iteration's
+    # queries (iterations 1..29; node records then include the sibling boxes),
+    # and from the root (all 30, the cold entry point above)
+    qs = [kdnn.transform(src, R, t) for R, t in Rts]
+    wcnt, wrep, ccnt, crep = [], [], [], []
+    for k in range(ITERS):
+        ccnt.append(query_counts(tree, qs[k]))
+        rs, rinfo_c = replay_time(tree, qs[k], True, 5)
+        crep.append(rs)
+        if k > 0:
+            rs, rinfo_w = replay_time(tree, qs[k], True, 5, prev=qs[k - 1])
+            wrep.append(rs)
+            wcnt.append((rinfo_w["node_records"] / n, rinfo_w["leaf_points"] / n))
     work = 24 * 2 ** (info["depth"] + 1) + 16 * (len(p.target) + 16) + 4 * len(p.target)
     ceil = gather_ceilings(g, work)
+    level = level_of(work, info["l2_bytes"])
     # fused: index read 4 + query 12 + original source 12 + matched point 12
-    roof = search_roofline(n, nodes_avg, pts_avg, 4 + 12 + 12 + 12, kern_s, ceil,
-                           level_of(work, info["l2_bytes"]), "fused correspondence kernel",
-                           float(np.mean(reps_s)), rinfo)
-    roof["replay"]["note"] = ("mean over the 30 iterations' queries of the median of 5 "
-                              "replays each; bytes and launch of the last")
+    # (+ the warm start's leaf read and write, 4 + 4)
+    roof = search_roofline(n, float(np.mean([c[0] for c in wcnt])),
+                           float(np.mean([c[1] for c in wcnt])), 4 + 12 + 12 + 12 + 8, warm_s,
+                           ceil, level, "fused correspondence kernel, warm-started",
+                           float(np.mean(wrep)), rinfo_w)
+    roof["replay"]["note"] = (f"mean over iterations 1..{ITERS - 1} of the median of 5 replays "
+                              "each, every search starting at the leaf of its query's match in "
+                              "the previous iteration; bytes and launch of the last")
+    cold = search_roofline(n, float(np.mean([c[0] for c in ccnt])),
+                           float(np.mean([c[1] for c in ccnt])), 4 + 12 + 12 + 12, kern_s, ceil,
+                           level, "fused correspondence kernel, searches from the root",
+                           float(np.mean(crep)), rinfo_c)
     traffic, traffic_src = committed_traffic()
     roof.update({
         "traffic": None if traffic is None else round(traffic),
         "traffic_source": traffic_src,
         "kernel": "icp_fused_kernel<1, 16>",
-        "kernel_time_source": "mean of the library's dispatch-stamped event pairs over "
-                              f"{len(kern_ms)} launches (the 30 iterations' transforms x "
-                              f"{args.kernel_reps})",
+        "kernel_time_source": "mean of the library's dispatch-stamped event pairs over the "
+                              f"warm-started launches (iterations 1..{ITERS - 1}) of "
+                              f"{args.kernel_reps} registrations",
+        "kernel_us_iteration0": round(float(loop_ms[:, 0].mean()) * 1e3, 3),
         "kernels_hip_sha256_16": kernel_source_hash(),
         "working_set_bytes": work,
         "single_descent_bytes_per_query": round(32 * (info["depth"] + 1)
                                                 + 12 * (n / 2 ** info["depth"]) + 40, 1),
+        "cold_start": {k: cold[k] for k in ("achieved", "peak", "frac", "kernel_us", "floor_us",
+                                            "bytes_per_query", "nodes_per_query",
+                                            "points_per_query", "replay", "random_gather",
+                                            "byte_model")},
     })
+    roof["cold_start"]["kernel_time_source"] = (
+        f"icp_correspond_reduce_async at the 30 iterations' transforms x {args.kernel_reps}, "
+        "the library's event pairs (no warm start)")
     log(f"roofline: {roof['achieved']} of {roof['peak']} GB/s at {roof['bound']} "
         f"-> frac {roof['frac']}")
 
@@ -616,16 +678,28 @@ def bench_scene(g, args, result):
                   "note": "upload_ms: a second build of the same tree (the first device "
                           "allocation also pays the runtime's start-up)"},
         "fused_kernel": {"name": "icp_fused_kernel<1, 16>",
-                         **{f"{k}_us": round(v * 1e3, 3) for k, v in pct(kern_ms).items()
-                            if k != "n"},
-                         "launches": len(kern_ms),
-                         "queries_per_s": round(n / kern_s),
-                         "call_mean_us": round(float(call_ms.mean()) * 1e3, 2),
+                         "in_icp_loop": {
+                             "iteration0_mean_us": round(float(loop_ms[:, 0].mean()) * 1e3, 3),
+                             **{f"warm_{k}_us": round(v * 1e3, 3)
+                                for k, v in pct(loop_ms[:, 1:].ravel()).items() if k != "n"},
+                             "launches": int(loop_ms.size),
+                             "note": "every fused launch of the host-loop registrations; "
+                                     "iterations after the first start each search at the "
+                                     "leaf of its point's previous match"},
+                         "cold_entry_point": {
+                             **{f"{k}_us": round(v * 1e3, 3) for k, v in pct(kern_ms).items()
+                                if k != "n"},
+                             "launches": len(kern_ms),
+                             "queries_per_s": round(n / kern_s),
+                             "call_mean_us": round(float(call_ms.mean()) * 1e3, 2),
+                             "note": "icp_correspond_reduce_async at the 30 iterations' "
+                                     "transforms: searches from the root"},
                          "timing": "event pair stamped by the search kernel's dispatch "
                                    "(library timing facility, hipExtLaunchKernel)"},
         "icp_iteration_breakdown_us": {
             "host_loop_iteration": round(T / (args.steps * ITERS) * 1e6, 2),
             "device_loop_iteration": round(Td / (args.steps * ITERS) * 1e6, 2),
+            "fused_kernel_in_loop_warm": round(warm_s * 1e6, 2),
             "fused_kernel": round(kern_s * 1e6, 2),
             "correspondence_call_events": round(float(call_ms.mean()) * 1e3, 2),
             "host_svd_solve_through_python": round(solve_us, 2),

@@ -542,6 +542,10 @@ kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_
  *      records each query's visits: the root's box (32 B), each internal
  *      node's run of child boxes (48 B), each leaf (its points, loaded in
  *      chunks as the search loads them); at most KDNN_REPLAY_CAP per query.
+ *      With q_prev_dev (the previous ICP iteration's queries, m points) each
+ *      search starts as icp_align's do after the first iteration: at the
+ *      leaf of that query's nearest neighbour, with the box of every sibling
+ *      subtree along the leaf's path (32 B each) in place of the descent.
  *   2. The rows are laid out per wave in the launch shape of the production
  *      kernel: nn_query's one-lane-per-query kernel, or with KDNN_REPLAY_ICP
  *      the fused ICP kernel's (work-groups, queries per wave, spread of
@@ -563,7 +567,8 @@ kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_
 typedef struct kdnn_replay_info {
     int64_t visits;        /* root, box-run and leaf visits replayed */
     int64_t bytes;         /* bytes one replay loads */
-    int64_t node_records;  /* node records the visits stand for (sum of nn_query_stats' nodes) */
+    int64_t node_records;  /* node records the visits stand for (cold start: the sum of
+                              nn_query_stats' node counts; each warm-start sibling box: 1) */
     int64_t leaf_points;   /* leaf points they stand for (sum of nn_query_stats' points) */
     int64_t truncated;     /* queries with more than KDNN_REPLAY_CAP visits (tail not replayed) */
     int64_t blocks;        /* work-groups of the launch shape */
@@ -571,9 +576,10 @@ typedef struct kdnn_replay_info {
     int32_t spread;        /* 1: positions spread over each XCD's segment */
 } kdnn_replay_info;
 size_t kdnn_replay_workspace_bytes(const kdnn_tree *tree, int64_t m, uint32_t flags);
-kdnn_status kdnn_replay_bench(const kdnn_tree *tree, const float *q_dev, int64_t m, uint32_t flags,
-                              int32_t reps, void *ws_dev, size_t ws_bytes, float *ms_out,
-                              kdnn_replay_info *info, hipStream_t stream);
+kdnn_status kdnn_replay_bench(const kdnn_tree *tree, const float *q_dev, const float *q_prev_dev,
+                              int64_t m, uint32_t flags, int32_t reps, void *ws_dev,
+                              size_t ws_bytes, float *ms_out, kdnn_replay_info *info,
+                              hipStream_t stream);
 
 /* KDNN_VERSION of the built library. */
 int32_t kdnn_version(void);

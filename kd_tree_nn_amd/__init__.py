@@ -195,23 +195,28 @@ class Tree:
             | _lib.lanes_flag(lanes, budget, top_lds), _ptr(ws), ws.numel() if ws is not None else 0, _stream()), "nn_query_stats")
         return idx, d2, cn, cp
 
-    def replay_bench(self, q, icp: bool = False, sort=None, reps: int = 10):
+    def replay_bench(self, q, icp: bool = False, sort=None, reps: int = 10, prev=None):
         """Replay ceiling of a search launch over the queries q
         (kdnn_replay_bench): each replay's kernel time in ms (numpy array of
         `reps`) and what was replayed (dict of kdnn_replay_info's fields).
-        icp=True takes the fused ICP kernel's launch shape, else nn_query's."""
+        icp=True takes the fused ICP kernel's launch shape, else nn_query's;
+        prev: the previous ICP iteration's queries (warm-started searches)."""
         torch = _torch()
         q = _dev_points(q, "queries")
         m = q.shape[0]
+        if prev is not None:
+            prev = _dev_points(prev, "prev")
+            if prev.shape[0] != m:
+                raise ValueError("prev must have as many points as q")
         flags = (_lib.KDNN_REPLAY_ICP if icp else 0) | _lib.sort_flag(
             sort, KDNN_QUERY_SORT, KDNN_QUERY_NO_SORT)
         nbytes = int(_lib.lib().kdnn_replay_workspace_bytes(self._h, m, flags))
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
         ms = (ctypes.c_float * int(reps))()
         info = _lib.ReplayInfo()
-        _lib.check(_lib.lib().kdnn_replay_bench(self._h, _ptr(q), m, flags, int(reps), _ptr(ws),
-                                                nbytes, ms, ctypes.byref(info), _stream()),
-                   "kdnn_replay_bench")
+        _lib.check(_lib.lib().kdnn_replay_bench(self._h, _ptr(q), _ptr(prev), m, flags, int(reps),
+                                                _ptr(ws), nbytes, ms, ctypes.byref(info),
+                                                _stream()), "kdnn_replay_bench")
         out = {f: getattr(info, f) for f, _ in _lib.ReplayInfo._fields_}
         return np.array(ms[:], dtype=np.float64), out
 

@@ -127,7 +127,7 @@ SIGNATURES = {
     "kdnn_chase_bench": (c_i32, [c_vp, c_i64, c_i32, c_i32, c_vp, c_fp, c_vp]),
     "kdnn_timing_end": (c_i32, [c_fp, c_i32, ctypes.POINTER(c_i32)]),
     "kdnn_replay_workspace_bytes": (c_sz, [c_vp, c_i64, c_u32]),
-    "kdnn_replay_bench": (c_i32, [c_vp, c_vp, c_i64, c_u32, c_i32, c_vp, c_sz, c_fp,
+    "kdnn_replay_bench": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_u32, c_i32, c_vp, c_sz, c_fp,
                                   ctypes.POINTER(ReplayInfo), c_vp]),
     "kdnn_last_error": (ctypes.c_char_p, []),
     "kdnn_version": (c_i32, []),

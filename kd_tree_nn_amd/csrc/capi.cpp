@@ -371,6 +371,8 @@ kdnn_status batch_on_device(int32_t B, const kdnn_tree *const *trees, const floa
                            &t[3 * size_t(p)], part[p], nullptr, nullptr};
                 J.st = batch_loop_state(ws_dev, total, p);
                 J.out = batch_loop_out(ws_dev, total, B, p);
+                J.hint = batch_hint(ws_dev, total, B, n, p);
+                J.hint_in = k > 0;
                 jobs.push_back(J);
             }
             if ((e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total,
@@ -513,15 +515,19 @@ size_t kdnn_replay_workspace_bytes(const kdnn_tree *tree, int64_t m, uint32_t fl
     }
 }
 
-kdnn_status kdnn_replay_bench(const kdnn_tree *tree, const float *q_dev, int64_t m, uint32_t flags,
-                              int32_t reps, void *ws_dev, size_t ws_bytes, float *ms_out,
-                              kdnn_replay_info *info, hipStream_t stream)
+kdnn_status kdnn_replay_bench(const kdnn_tree *tree, const float *q_dev, const float *q_prev_dev,
+                              int64_t m, uint32_t flags, int32_t reps, void *ws_dev,
+                              size_t ws_bytes, float *ms_out, kdnn_replay_info *info,
+                              hipStream_t stream)
 {
     KDNN_GUARD_BEGIN
     if (!tree) return fail(KDNN_EINVAL, "kdnn_replay_bench: null tree");
     if (m < 1) return fail(KDNN_EINVAL, "kdnn_replay_bench: m must be >= 1");
     kdnn_status st = check_points(q_dev, m, "kdnn_replay_bench: queries");
     if (st != KDNN_OK) return st;
+    if (q_prev_dev && (st = check_points(q_prev_dev, m, "kdnn_replay_bench: previous queries")) !=
+                          KDNN_OK)
+        return st;
     if (reps < 1 || !ms_out || !info)
         return fail(KDNN_EINVAL, "kdnn_replay_bench: reps < 1 or null ms_out / info");
     if (flags & ~(KDNN_QUERY_NO_SORT | KDNN_QUERY_SORT | KDNN_REPLAY_ICP))
@@ -542,8 +548,8 @@ kdnn_status kdnn_replay_bench(const kdnn_tree *tree, const float *q_dev, int64_t
         return hip_fail(e, "kdnn_replay_bench: order launch");
     void *rws = static_cast<char *>(ws_dev) + ((query_ws_bytes(m) + 255) & ~size_t(255));
     *info = kdnn_replay_info{};
-    if ((e = launch_replay(tree->dev, q_dev, m, perm, icp, rws, reps, ms_out, info, stream)) !=
-        hipSuccess)
+    if ((e = launch_replay(tree->dev, q_dev, m, perm, icp, q_prev_dev, rws, reps, ms_out, info,
+                           stream)) != hipSuccess)
         return hip_fail(e, "kdnn_replay_bench");
     return KDNN_OK;
     KDNN_GUARD_END
@@ -1234,8 +1240,11 @@ kdnn_status icp_align_batch(int32_t B, const kdnn_tree *const *trees, const floa
                 uint64_t *done_word =
                     shared_tree ? nullptr
                                 : reinterpret_cast<uint64_t *>(trees[p]->d_pinned + kDoneWord);
-                jobs.push_back(BatchJob{&trees[p]->dev, src_dev[p], n[p], &R[9 * size_t(p)],
-                                        &t[3 * size_t(p)], part[p], dev_sums(p), done_word});
+                BatchJob J{&trees[p]->dev, src_dev[p], n[p], &R[9 * size_t(p)],
+                           &t[3 * size_t(p)], part[p], dev_sums(p), done_word};
+                J.hint = batch_hint(ws_dev, total, B, n, p);
+                J.hint_in = k > 0;
+                jobs.push_back(J);
             }
             e = launch_icp_batch(int32_t(jobs.size()), jobs.data(), bound2, ws_dev, total, stream,
                                  seq);

@@ -245,11 +245,15 @@ struct BatchJob {
     uint64_t *done;   // null, or a device-visible word the reduction sets to seq
     IcpLoopState *st = nullptr;  // device loop: the pair's state (R, t unused), else null
     IcpLoopOut *out = nullptr;   // device loop: the pair's record
+    uint32_t *hint = nullptr;    // [n] the pair's match leaves (warm start), or null
+    bool hint_in = false;        // start the searches from them (an iteration after the first)
 };
 int batch_max_pairs();
 int32_t batch_groups(int64_t n);  // work-groups (partial columns) of an n-point pair
-// Workspace: the partial columns, then B loop states, then B loop records.
+// Workspace: the partial columns, then B loop states, then B loop records,
+// then each pair's match leaves (n[p] words, 256-byte aligned).
 size_t icp_batch_ws_bytes(int32_t B, const int64_t *n);
+uint32_t *batch_hint(void *ws, int32_t total, int32_t B, const int64_t *n, int32_t p);
 size_t batch_loop_bytes(int32_t B);
 IcpLoopState *batch_loop_state(void *ws, int32_t total, int32_t p);
 IcpLoopOut *batch_loop_out(void *ws, int32_t total, int32_t B, int32_t p);
@@ -263,12 +267,14 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
 // sums of the pairs with r^2 <= kk * mean r^2 under (R, t).
 // Replay ceiling of a search launch (kdnn_replay_bench): workspace bytes and
 // the launch (trace, pack, `reps` timed replays into ms_out[0 .. reps)).
-// icp: the fused ICP kernel's launch shape, else nn_query's.
+// icp: the fused ICP kernel's launch shape, else nn_query's.  q_prev: null,
+// or the previous ICP iteration's queries (each search then starts at the
+// leaf of that query's nearest neighbour, as the ICP loop's searches do).
 using ReplayTally = kdnn_replay_info;
 size_t replay_ws_bytes(const DeviceTree &t, int64_t m, bool icp);
 hipError_t launch_replay(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
-                         bool icp, void *ws, int32_t reps, float *ms_out, ReplayTally *tally,
-                         hipStream_t s);
+                         bool icp, const float *q_prev, void *ws, int32_t reps, float *ms_out,
+                         ReplayTally *tally, hipStream_t s);
 
 hipError_t launch_icp_reject(const DeviceTree &t, const float *src, int64_t n, const double *R,
                              const double *tv, double kk, const IcpWorkspace &ws, double *sums_out,

@@ -633,8 +633,10 @@ __device__ __forceinline__ void task_finish(WaveTask &w, unsigned long long *oke
 
 // The instrumented search's visit stream, one row per query: 0 for the root's
 // box, an internal node i for the run of its two children's boxes, a leaf
-// node for that leaf's points.  Visits beyond the row's tcap entries are
+// node for that leaf's points, kSiblingVisit | v for the box of node v alone
+// (a warm start's sibling boxes).  Visits beyond the row's tcap entries are
 // counted, not stored.
+constexpr uint32_t kSiblingVisit = 0x80000000u;
 __device__ __forceinline__ void trace_visit(WaveTask &w, uint32_t *trow, uint32_t tcap,
                                             uint32_t e)
 {
@@ -719,9 +721,18 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
 // of dependent loads is replaced by independent loads of the sibling boxes
 // (kWarmBatch levels at a time) and the first leaf's scan gives a close bound
 // at once.
-constexpr int kWarmBatch = 4;
+// STATS: each sibling box counts as one node record (and is traced).
+// (Scene, warm searches of the ICP loop: batches of 4 and 7 levels measured
+// alike, 29.6 / 29.8 us; all 13 levels at once 30.8 us, its 128 registers
+// costing the whole kernel more than the saved round trips.)
+#ifndef KDNN_WARM_BATCH
+#define KDNN_WARM_BATCH 4
+#endif
+constexpr int kWarmBatch = KDNN_WARM_BATCH;
+template <bool STATS>
 __device__ __forceinline__ void warm_start(const TreeView &t, uint32_t leaf, float qx, float qy,
-                                           float qz, float *lbs, WaveTask &w)
+                                           float qz, float *lbs, WaveTask &w, uint32_t *trow,
+                                           uint32_t tcap)
 {
     const uint32_t D = uint32_t(t.depth);
     const float best = key_dist(w.key);
@@ -750,6 +761,10 @@ __device__ __forceinline__ void warm_start(const TreeView &t, uint32_t leaf, flo
                 const float lb = box_lb(qx, qy, qz, A, B);
                 lbs[d * kWG] = lb;
                 pend |= enters(lb, best) ? (1u << d) : 0u;
+                if constexpr (STATS) {
+                    ++w.cn;
+                    trace_visit(w, trow, tcap, kSiblingVisit | ((leaf >> (D - uint32_t(d) - 1u)) ^ 1u));
+                }
             }
         }
     }
@@ -822,8 +837,8 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
     w.cn = 0u;
     w.cp = 0u;
     w.nt = 0u;
-    if (!STATS && own && hint != 0u && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
-        warm_start(t, hint, oqx, oqy, oqz, lbs, w);
+    if (own && hint != 0u && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
+        warm_start<STATS>(t, hint, oqx, oqy, oqz, lbs, w, trow, tcap);
     } else if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
         const float4 A = t.nodes[2];
         const float4 B = t.nodes[3];
@@ -947,6 +962,7 @@ struct NnArgs {
     uint32_t *trace;   // instrumented one-lane kernel: [m][tcap] visit rows, or null
     uint32_t *tcount;  // [m] visits of each query (may exceed tcap)
     uint32_t tcap;
+    const uint32_t *hint;  // instrumented one-lane kernel: [m] warm-start leaves (0: none), or null
 };
 
 // Cooperative search of one query by G >= 2 lanes.
@@ -992,12 +1008,14 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
             // the instrumented kernel counts (and may record) the single-lane
             // search of each query
             const bool tr = STATS && own && a.trace;
+            uint32_t hint = STATS && own && a.hint ? a.hint[i] : 0u;
+            hint = hint >= a.tree.first_leaf && hint < 2u * a.tree.first_leaf ? hint : 0u;
             wave_search<STATS, !STATS, CH, QL>(a.tree, own, qx, qy, qz, a.init,
                                                lbs + threadIdx.x, okey, ocn, ocp,
                                                xfer + (threadIdx.x & ~63u),
                                                wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u, qpool,
                                                wq, tr ? a.trace + size_t(i) * a.tcap : nullptr,
-                                               a.tcap, tr ? a.tcount + i : nullptr);
+                                               a.tcap, tr ? a.tcount + i : nullptr, hint);
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
@@ -1849,6 +1867,8 @@ struct BatchPair {
     uint64_t *done;   // null, or a word set to the launch's sequence number after the sums
     IcpLoopState *st; // device loop: the pair's state ((R, t) from here), else null
     IcpLoopOut *out;  // device loop: the pair's record
+    uint32_t *hint;   // null, or per source point the leaf of its match (written after the
+    bool hint_in;     // search; read before it as a warm start when hint_in)
 };
 
 struct BatchArgs {
@@ -1898,12 +1918,16 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
             qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
         }
     }
+    uint32_t hint = own && P.hint_in ? P.hint[i] : 0u;
+    hint = hint >= P.tree.first_leaf && hint < 2u * P.tree.first_leaf ? hint : 0u;
     wave_search<false, true, CH>(P.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
                                  nullptr, nullptr, xfer + (threadIdx.x & ~63u),
-                                 KDNN_BATCH_QUORUM);
+                                 KDNN_BATCH_QUORUM, nullptr, 64u, nullptr, 0u, nullptr, hint);
     if (own) {
         Best b;
         finish(okey[threadIdx.x], 0u, b);
+        if (P.hint)
+            P.hint[i] = b.idx >= 0 ? leaf_of_slot(P.tree, uint32_t(P.tree.slot_of[b.idx])) : 0u;
         if (b.idx >= 0) {
             const float4 mp = P.tree.pts[P.tree.slot_of[b.idx]];
             const double s0 = X - P.c[0], s1 = Y - P.c[1], s2 = Z - P.c[2];
@@ -2896,7 +2920,7 @@ template <int CH>
 __device__ __forceinline__ void replay_cost(const TreeView &t, uint32_t e, uint32_t &bytes,
                                             uint32_t &recs, uint32_t &pts)
 {
-    if (e == 0u) {
+    if (e == 0u || (e & kSiblingVisit)) {
         bytes = 32u;
         recs = 1u;
         pts = 0u;
@@ -2971,6 +2995,13 @@ __device__ __forceinline__ uint32_t replay_load(const TreeView &t, uint32_t e)
         const float4 A = t.nodes[2], B = t.nodes[3];
         x = __float_as_uint(A.x) ^ __float_as_uint(A.y) ^ __float_as_uint(A.z) ^
             __float_as_uint(A.w) ^ __float_as_uint(B.x) ^ __float_as_uint(B.y);
+    } else if (e & kSiblingVisit) {
+        // the half of its parent's box run that holds node v's box, as warm_start loads it
+        const uint32_t v = e & ~kSiblingVisit;
+        const float4 *const pb = t.boxes + 3 * size_t(v >> 1) + (v & 1u);
+        const float4 P0 = pb[0], P1 = pb[1];
+        x = __float_as_uint(P0.x) ^ __float_as_uint(P0.w) ^ __float_as_uint(P1.y) ^
+            __float_as_uint(P1.z);
     } else if (e < t.first_leaf) {
         const float4 *const pb = t.boxes + 3 * size_t(e);
         const float4 P0 = pb[0], P1 = pb[1], P2 = pb[2];
@@ -3055,7 +3086,7 @@ static ReplayPlan replay_plan(const DeviceTree &t, int64_t m, bool icp, bool ord
 }
 
 struct ReplayWorkspace {
-    uint32_t *rows, *rcount, *packed, *seg_total, *sink;
+    uint32_t *rows, *rcount, *packed, *seg_total, *sink, *hint;
     int32_t *idx;
     float *d2;
     unsigned long long *tally;  // [5]: tally[0..3], truncated
@@ -3077,6 +3108,8 @@ static ReplayWorkspace carve_replay(void *ws, int64_t m, const ReplayPlan &p)
     c += align256(size_t(m) * 4);
     w.seg_total = reinterpret_cast<uint32_t *>(c);
     c += align256(size_t(p.segments) * 4);
+    w.hint = reinterpret_cast<uint32_t *>(c);
+    c += align256(size_t(m) * 4);
     w.rows = reinterpret_cast<uint32_t *>(c);
     c += align256(size_t(m) * kReplayCap * 4);
     w.packed = reinterpret_cast<uint32_t *>(c);
@@ -3087,19 +3120,43 @@ size_t replay_ws_bytes(const DeviceTree &t, int64_t m, bool icp)
 {
     // the segment count does not depend on the order (spread only permutes)
     const ReplayPlan p = replay_plan(t, m, icp, false);
-    return 512 + 3 * align256(size_t(m) * 4) + align256(size_t(p.segments) * 4) +
+    return 512 + 4 * align256(size_t(m) * 4) + align256(size_t(p.segments) * 4) +
            align256(size_t(m) * kReplayCap * 4) +
            align256(size_t(p.segments) * 64 * kReplayCap * 4);
 }
 
+// Warm-start leaves from matches: the leaf holding each original index's
+// point (0 where there is no match), as the fused kernel records them.
+__global__ __launch_bounds__(256) void hint_of_match_kernel(TreeView t, const int32_t *idx,
+                                                            int64_t m, uint32_t *hint)
+{
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < m;
+         i += int64_t(gridDim.x) * 256) {
+        const int32_t k = idx[i];
+        hint[i] = k >= 0 ? leaf_of_slot(t, uint32_t(t.slot_of[k])) : 0u;
+    }
+}
+
 hipError_t launch_replay(const DeviceTree &t, const float *q, int64_t m, const int32_t *perm,
-                         bool icp, void *ws, int32_t reps, float *ms_out, ReplayTally *tally,
-                         hipStream_t s)
+                         bool icp, const float *q_prev, void *ws, int32_t reps, float *ms_out,
+                         ReplayTally *tally, hipStream_t s)
 {
     const ReplayPlan p = replay_plan(t, m, icp, perm != nullptr);
     const ReplayWorkspace w = carve_replay(ws, m, p);
     hipError_t e = hipMemsetAsync(w.tally, 0, 5 * sizeof(unsigned long long), s);
     if (e != hipSuccess) return e;
+    if (q_prev) {
+        // the ICP loop's warm start: each search begins at the leaf of the
+        // point's match in the previous iteration, i.e. of q_prev's nearest
+        // neighbour
+        e = launch_nn(t, q_prev, m, nullptr, w.idx, w.d2, nullptr, nullptr, false, Schedule{},
+                      INFINITY, nullptr, s, nullptr);
+        if (e != hipSuccess) return e;
+        int64_t hb = (m + 255) / 256;
+        hint_of_match_kernel<<<dim3(uint32_t(hb < 65536 ? hb : 65536)), 256, 0, s>>>(
+            tree_view(t), w.idx, m, w.hint);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     // 1. the visit rows, from the instrumented search
     NnArgs na{};
     na.tree = tree_view(t);
@@ -3111,6 +3168,7 @@ hipError_t launch_replay(const DeviceTree &t, const float *q, int64_t m, const i
     na.trace = w.rows;
     na.tcount = w.rcount;
     na.tcap = kReplayCap;
+    na.hint = q_prev ? w.hint : nullptr;
     const WavePlan fw = full_wave_plan(m);
     na.wq = fw.q;
     const size_t lds = p.small ? lbs_bytes(t.depth) : 0;
@@ -3212,7 +3270,16 @@ size_t icp_batch_ws_bytes(int32_t B, const int64_t *n)
 {
     int64_t total = 0;
     for (int32_t p = 0; p < B; ++p) total += batch_groups(n[p]);
-    return align256(size_t(kS) * size_t(total) * 8) + batch_loop_bytes(B);
+    size_t hints = 0;
+    for (int32_t p = 0; p < B; ++p) hints += align256(size_t(n[p]) * 4);
+    return align256(size_t(kS) * size_t(total) * 8) + batch_loop_bytes(B) + hints;
+}
+
+uint32_t *batch_hint(void *ws, int32_t total, int32_t B, const int64_t *n, int32_t p)
+{
+    size_t off = align256(size_t(kS) * size_t(total) * 8) + batch_loop_bytes(B);
+    for (int32_t q = 0; q < p; ++q) off += align256(size_t(n[q]) * 4);
+    return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + off);
 }
 
 size_t batch_loop_bytes(int32_t B)
@@ -3295,6 +3362,8 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
         P.done = J.done;
         P.st = J.st;
         P.out = J.out;
+        P.hint = J.hint;
+        P.hint_in = J.hint_in;
         const int kx = (kNumXcd - p + B - 1) / B;
         const int64_t per_xcd = (P.nb + kx - 1) / kx;
         slots = per_xcd > slots ? per_xcd : slots;

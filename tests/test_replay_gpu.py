@@ -134,13 +134,46 @@ def test_replay_argument_checks(torch, kdnn):
         (0, 0, 4, need),                                      # no queries
     ]
     for m, flags, reps, nbytes in bad:
-        st = L.kdnn_replay_bench(tree._h, qd.data_ptr(), m, flags, reps, ws.data_ptr(), nbytes,
-                                 ms, ctypes.byref(info), None)
+        st = L.kdnn_replay_bench(tree._h, qd.data_ptr(), None, m, flags, reps, ws.data_ptr(),
+                                 nbytes, ms, ctypes.byref(info), None)
         assert st == _lib.KDNN_EINVAL, (m, flags, reps, nbytes)
-    st = L.kdnn_replay_bench(tree._h, qd.data_ptr(), 500, 0, 4, ws.data_ptr(), need, None,
+    st = L.kdnn_replay_bench(tree._h, qd.data_ptr(), None, 500, 0, 4, ws.data_ptr(), need, None,
                              ctypes.byref(info), None)
     assert st == _lib.KDNN_EINVAL
-    # and a good call on the same buffers
-    st = L.kdnn_replay_bench(tree._h, qd.data_ptr(), 500, 0, 4, ws.data_ptr(), need, ms,
+    st = L.kdnn_replay_bench(tree._h, qd.data_ptr(), qd.data_ptr() + 2, 500, 0, 4,
+                             ws.data_ptr(), need, ms, ctypes.byref(info), None)
+    assert st == _lib.KDNN_EINVAL  # misaligned previous queries
+    # and good calls on the same buffers, cold and warm
+    st = L.kdnn_replay_bench(tree._h, qd.data_ptr(), None, 500, 0, 4, ws.data_ptr(), need, ms,
                              ctypes.byref(info), None)
     assert st == _lib.KDNN_OK and info.visits > 0
+    st = L.kdnn_replay_bench(tree._h, qd.data_ptr(), qd.data_ptr(), 500, 0, 4, ws.data_ptr(),
+                             need, ms, ctypes.byref(info), None)
+    assert st == _lib.KDNN_OK and info.visits > 0
+
+
+@pytest.mark.parametrize("name", ["tiny_leaf8", "uniform_ragged_leaf16", "scene_leaf16"])
+def test_replay_warm_start_tallies(torch, kdnn, name):
+    """Warm-started replay (the previous iteration's queries given): every
+    searched query records the D sibling boxes beside its start leaf (one node
+    record each) and at least one leaf; bytes follow from the tallies; with
+    the queries themselves as the previous iteration every search starts at
+    its own answer's leaf, so it scans no more points than from the root."""
+    tgt, q, leaf = _case(name)
+    say("replay warm start", name, "queries", len(q))
+    tree = kdnn.Tree(tgt, leaf)
+    qd = dev(torch, q)
+    _, _, cn, cp = tree.query_stats(qd)
+    ms, info = tree.replay_bench(qd, icp=True, reps=2, prev=qd)
+    assert np.all(ms > 0.0) and info["truncated"] == 0
+    D = tree.info["depth"]
+    finite = int(np.isfinite(q).all(axis=1).sum())
+    siblings = finite * D
+    pairs2 = info["node_records"] - siblings
+    assert pairs2 >= 0 and pairs2 % 2 == 0
+    pairs = pairs2 // 2
+    leaves = info["visits"] - siblings - pairs
+    assert leaves >= finite
+    chunk = 8 if tree.info["max_leaf"] <= 8 else 16
+    assert info["bytes"] == 32 * siblings + 48 * pairs + 16 * chunk * leaves
+    assert info["leaf_points"] <= int(cp.cpu().numpy().astype(np.int64).sum())
