@@ -772,6 +772,95 @@ __device__ __forceinline__ void warm_start(const TreeView &t, uint32_t leaf, flo
     w.i = leaf;
 }
 
+// The same with the start leaf scanned here too: its points are loaded with
+// the first sibling boxes (one round trip for both), its best key bounds the
+// siblings, which are pending only while it lets them in, and the task goes on
+// at the next pending subtree -- already holding a candidate.  okey_own: the
+// query's best key in LDS (this lane's own slot).
+#ifndef KDNN_WARM_LEAF
+#define KDNN_WARM_LEAF 1
+#endif
+template <bool STATS, int CH>
+__device__ __forceinline__ void warm_start_leaf(const TreeView &t, uint32_t leaf, float qx,
+                                                float qy, float qz, float *lbs, WaveTask &w,
+                                                uint32_t *trow, uint32_t tcap,
+                                                unsigned long long *okey_own)
+{
+    const uint32_t D = uint32_t(t.depth);
+    int32_t begin, last, end;
+    leaf_range(t, leaf, begin, last, end);
+    float4 p[CH];
+    const float4 *pc = t.pts + begin;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) p[c] = pc[c];
+    float4 P[kWarmBatch][2];
+    auto load_batch = [&](int d0) {
+#pragma unroll
+        for (int u = 0; u < kWarmBatch; ++u) {
+            const uint32_t d = uint32_t(d0 - u < 0 ? 0 : d0 - u);
+            const uint32_t parent = leaf >> (D - d);
+            const uint32_t odd = ((leaf >> (D - d - 1u)) & 1u) ^ 1u;
+            const float4 *pb = t.boxes + 3 * size_t(parent) + odd;
+            P[u][0] = pb[0];
+            P[u][1] = pb[1];
+        }
+    };
+    uint32_t pend = 0u;
+    auto bound_batch = [&](int d0, float best) {
+#pragma unroll
+        for (int u = 0; u < kWarmBatch; ++u) {
+            const int d = d0 - u;
+            if (d >= 0) {
+                const bool odd = (((leaf >> (D - uint32_t(d) - 1u)) & 1u) ^ 1u) != 0u;
+                const float4 A = odd ? make_float4(P[u][0].z, P[u][0].w, P[u][1].x, P[u][1].y)
+                                     : P[u][0];
+                const float4 B = odd ? make_float4(P[u][1].z, P[u][1].w, 0.0f, 0.0f)
+                                     : make_float4(P[u][1].x, P[u][1].y, 0.0f, 0.0f);
+                const float lb = box_lb(qx, qy, qz, A, B);
+                lbs[d * kWG] = lb;
+                pend |= enters(lb, best) ? (1u << d) : 0u;
+                if constexpr (STATS) {
+                    ++w.cn;
+                    trace_visit(w, trow, tcap,
+                                kSiblingVisit | ((leaf >> (D - uint32_t(d) - 1u)) ^ 1u));
+                }
+            }
+        }
+    };
+    load_batch(int(D) - 1);
+    uint64_t key = w.key;
+    for (uint32_t k0 = uint32_t(begin);;) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const float dx = p[c].x - qx;
+            const float dy = p[c].y - qy;
+            const float dz = p[c].z - qz;
+            const float dd = (dx * dx + dy * dy) + dz * dz;
+            const uint64_t k = nn_key(dd, __float_as_uint(p[c].w));
+            key = k < key ? k : key;
+        }
+        k0 += CH;
+        if (k0 >= uint32_t(end)) break;
+        pc = t.pts + k0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) p[c] = pc[c];
+    }
+    if constexpr (STATS) {
+        w.cp += uint32_t(end - begin);
+        trace_visit(w, trow, tcap, leaf);
+    }
+    const float best = key_dist(key);
+    bound_batch(int(D) - 1, best);
+    for (int d0 = int(D) - 1 - kWarmBatch; d0 >= 0; d0 -= kWarmBatch) {
+        load_batch(d0);
+        bound_batch(d0, best);
+    }
+    const uint64_t seen = atomicMin(okey_own, (unsigned long long)key);
+    w.key = seen < key ? seen : key;
+    w.pend = pend;
+    w.i = pair_next(leaf, w.pend, lbs, key_dist(w.key));
+}
+
 // The pending-bound array of a balanced-search work-group (one float per path
 // level and lane): a static array of kDevMaxDepth levels, or (DYN) dynamic LDS
 // of lbs_bytes(D) sized to the tree, which leaves room for more resident
@@ -838,7 +927,11 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
     w.cp = 0u;
     w.nt = 0u;
     if (own && hint != 0u && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
-        warm_start<STATS>(t, hint, oqx, oqy, oqz, lbs, w, trow, tcap);
+        if (KDNN_WARM_LEAF)
+            warm_start_leaf<STATS, CH>(t, hint, oqx, oqy, oqz, lbs, w, trow, tcap,
+                                       &okey[threadIdx.x]);
+        else
+            warm_start<STATS>(t, hint, oqx, oqy, oqz, lbs, w, trow, tcap);
     } else if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
         const float4 A = t.nodes[2];
         const float4 B = t.nodes[3];
