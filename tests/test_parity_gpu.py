@@ -412,6 +412,35 @@ def test_host_loop_matches_step_by_step(torch, kdnn):
     assert np.linalg.norm(g["R"] - o["R"]) <= R_TOL and np.max(np.abs(g["t"] - o["t"])) <= T_TOL
 
 
+def test_warm_start_ties_and_gaps(torch, kdnn):
+    """Iterations after the first start each search at the leaf of the point's
+    previous match.  On a lattice target with sources at cell centres (8 target
+    points at exactly the same distance, lowest index wins), with NaN sources
+    (no match, no warm start) and far outliers, every iterate must still equal
+    the loop of separate root-start calls bit for bit, under max_dist too."""
+    g = np.stack(np.meshgrid(*(np.arange(12, dtype=np.float32),) * 3, indexing="ij"), -1)
+    tgt = g.reshape(-1, 3)
+    rng = np.random.Generator(np.random.PCG64(17))
+    tgt = tgt[rng.permutation(len(tgt))]                  # ties between unrelated indices
+    src = (g[:-1, :-1, :-1] + 0.5).reshape(-1, 3).astype(np.float32)
+    src = np.concatenate([src, np.full((3, 3), np.nan, np.float32),
+                          np.array([[60.0, 5.0, 5.0], [-40.0, -40.0, 3.0]], np.float32)])
+    for leaf in (1, 8, 16):
+        tree = kdnn.Tree(tgt, leaf)
+        sd = dev(torch, src)
+        auto = bool(tree.info["auto_sort_icp"])
+        for kw in ({}, {"max_dist": 0.9}, {"sort": True}):
+            say("warm start ties and gaps, leaf", leaf, kw)
+            gi = tree.icp(sd, max_iter=6, R0=synth.rot_z(0.0), t0=[0.0, 0.0, 0.0], **kw)
+            R, t, E, hist = _step_by_step(kdnn, tree, sd, 6, kw.get("sort", auto),
+                                          kw.get("max_dist"))
+            assert gi["iters"] == len(E) == 6
+            np.testing.assert_array_equal(gi["E"], E)
+            np.testing.assert_array_equal(gi["Rt_hist"], hist)
+            np.testing.assert_array_equal(gi["R"], R)
+            np.testing.assert_array_equal(gi["t"], t)
+
+
 def test_device_loop_eps_and_limits(torch, kdnn):
     """Convergence stop at every phase of the 4-iteration chunks, the host
     fallback beyond the record's 512 iterations, and a degenerate first
