@@ -289,7 +289,9 @@ typedef struct {
     double reject_k;
 } kdnn_icp_reject;
 
-/* Bytes of device workspace the ICP entry points need for n source points. */
+/* Bytes of device workspace the ICP entry points need for n source points
+ * (traversal order, partial sums, rejection state, device-loop state, and
+ * each source point's match leaf for icp_align's next iteration). */
 size_t icp_workspace_bytes(int64_t n);
 
 /* One ICP correspondence step fused into one kernel (article §2.1, §3.3):
@@ -376,6 +378,11 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  *                  n_k count them; with reject_k > 0 each iteration solves,
  *                  rejects by residual (icp_reject_reduce) and solves again.
  * The traversal order is computed once, from the source moved by (R0, t0).
+ * With one lane per query (no schedule flag or KDNN_LANES(1)) every
+ * iteration after the first starts each point's search at the leaf that held
+ * its match in the previous iteration (kept in ws), with the rest of the tree
+ * still searched as far as the bound requires: the same pairs as a search
+ * from the root, in fewer dependent steps.
  * Default (and KDNN_ICP_HOST_LOOP): the article's loop (§3.3) -- each
  * iteration's 17 sums come back to the host (a pinned readback), which solves
  * with kdnn_procrustes (SVD, det sign fix) and applies the convergence rule
@@ -418,7 +425,8 @@ kdnn_status icp_align_noalloc(const kdnn_tree *tree, const float *src_dev, int64
                               const kdnn_icp_reject *reject, hipStream_t stream);
 
 /* Bytes of device workspace icp_align_batch needs for B pairs of n[p] source
- * points (partial sums, and each pair's loop state and record, ~54 KB).
+ * points (partial sums, each pair's loop state and record, ~54 KB, and each
+ * point's match leaf, 4 B, for the searches of the next iteration).
  * 0 if B < 1, n is NULL or some n[p] < 1. */
 size_t icp_batch_workspace_bytes(int32_t B, const int64_t *n);
 
