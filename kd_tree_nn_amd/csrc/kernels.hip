@@ -1740,7 +1740,10 @@ static void launch_icp_loop_step(const double *p, int32_t np, const IcpLoop &L,
 #ifndef KDNN_FUSED_WPE
 #define KDNN_FUSED_WPE 5
 #endif
-template <int G, int CH = kLeafChunk>
+// WARM (one lane per query): the instance that starts searches from a.hint
+// (hint_in); the other one searches from the root and has the warm start's
+// registers to spare (only its own hints are written).
+template <int G, int CH = kLeafChunk, bool WARM = false>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(
     G == 1 && CH == kLeafChunk && KDNN_QLDS ? 4 : KDNN_FUSED_WPE))) void
 icp_fused_kernel(IcpArgs a)
@@ -1779,7 +1782,7 @@ icp_fused_kernel(IcpArgs a)
                     icp_query(a, i, X, Y, Z, qx, qy, qz);
             }
             // the leaf of the point's previous match, checked to be a leaf
-            uint32_t hint = own && a.hint_in ? a.hint[i] : 0u;
+            uint32_t hint = WARM && own && a.hint_in ? a.hint[i] : 0u;
             hint = hint >= a.tree.first_leaf && hint < 2u * a.tree.first_leaf ? hint : 0u;
             wave_search<false, true, CH, KDNN_QLDS>(a.tree, own, qx, qy, qz, a.init,
                                                     lbs + threadIdx.x, okey, nullptr, nullptr,
@@ -1978,7 +1981,7 @@ struct BatchArgs {
 #ifndef KDNN_BATCH_QUORUM
 #define KDNN_BATCH_QUORUM KDNN_LEAF_QUORUM_FULL
 #endif
-template <int CH>
+template <int CH, bool WARM = false>  // WARM: as icp_fused_kernel's
 __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
 {
     __shared__ double red[(kWG / 64) * kS];
@@ -2011,7 +2014,7 @@ __global__ __launch_bounds__(kWG) void icp_batch_kernel(BatchArgs a)
             qz = rigid_row(P.R[6], P.R[7], P.R[8], P.t[2], X, Y, Z);
         }
     }
-    uint32_t hint = own && P.hint_in ? P.hint[i] : 0u;
+    uint32_t hint = WARM && own && P.hint_in ? P.hint[i] : 0u;
     hint = hint >= P.tree.first_leaf && hint < 2u * P.tree.first_leaf ? hint : 0u;
     wave_search<false, true, CH>(P.tree, own, qx, qy, qz, a.init, lbs + threadIdx.x, okey,
                                  nullptr, nullptr, xfer + (threadIdx.x & ~63u),
@@ -2957,6 +2960,9 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
         if (sc.lanes <= 1 && hint_mode > 0) {  // the one-lane kernel keeps the match leaves
             a.hint = ws.hint;
             a.hint_in = hint_mode > 1;
+            if (a.hint_in)
+                k = small ? icp_fused_kernel<1, kLeafChunkSmall, true>
+                          : icp_fused_kernel<1, kLeafChunk, true>;
         }
         e = launch_k(k, grid, kWG, sc.lanes <= 1 && small ? lbs_bytes(t.depth) : 0, s, e0, e1,
                      a);
@@ -3461,12 +3467,12 @@ hipError_t launch_icp_batch(int32_t B, const BatchJob *jobs, float bound2, void 
         const int64_t per_xcd = (P.nb + kx - 1) / kx;
         slots = per_xcd > slots ? per_xcd : slots;
     }
-    if (max_leaf <= kLeafChunkSmall)
-        icp_batch_kernel<kLeafChunkSmall><<<dim3(uint32_t(slots * kNumXcd)), kWG, lbs_bytes(depth),
-                                            s>>>(a);
-    else
-        icp_batch_kernel<kLeafChunk><<<dim3(uint32_t(slots * kNumXcd)), kWG, lbs_bytes(depth),
-                                       s>>>(a);
+    const bool warm = B > 0 && jobs[0].hint_in;  // every pair of a launch is at one iteration
+    void (*kb)(BatchArgs) =
+        max_leaf <= kLeafChunkSmall
+            ? (warm ? icp_batch_kernel<kLeafChunkSmall, true> : icp_batch_kernel<kLeafChunkSmall>)
+            : (warm ? icp_batch_kernel<kLeafChunk, true> : icp_batch_kernel<kLeafChunk>);
+    kb<<<dim3(uint32_t(slots * kNumXcd)), kWG, lbs_bytes(depth), s>>>(a);
     batch_reduce_kernel<<<dim3(uint32_t(B)), kWG, 0, s>>>(a);
     return hipGetLastError();
 }
