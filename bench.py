@@ -594,8 +594,9 @@ def bench_scene(g, args, result):
     # node records and leaf points per query and the replay ceiling, both for
     # the instrumented single-lane search of each iteration's queries in the
     # fused kernel's launch shape: warm-started from the previous iteration's
-    # queries (iterations 1..29; node records then include the sibling boxes),
-    # and from the root (all 30, the cold entry point above)
+    # queries (iterations 1..29; node records then include two for the start
+    # leaf's 64-byte plane record), and from the root (all 30, the cold entry
+    # point above)
     qs = [kdnn.transform(src, R, t) for R, t in Rts]
     wcnt, wrep, ccnt, crep = [], [], [], []
     for k in range(ITERS):

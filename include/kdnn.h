@@ -88,7 +88,8 @@ typedef struct kdnn_tree_info {
     double center[3];       /* bbox centre; the shift applied in kdnn_icp_sums */
     double build_ms;        /* host build time (excluding the upload) */
     double upload_ms;       /* device allocation + host-to-device copy */
-    int64_t device_bytes;   /* device memory held by the tree */
+    int64_t device_bytes;   /* device memory held by the tree (node records, child box
+                               runs, points, slot map, 64-byte plane record per leaf) */
     int64_t l2_bytes;       /* L2 cache size of the tree's device */
     int32_t auto_sort;      /* 1: nn_query's automatic choice applies the Morton ordering */
     int32_t auto_sort_icp;  /* 1: the ICP entry points' automatic choice applies it */
@@ -382,7 +383,9 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  * iteration after the first starts each point's search at the leaf that held
  * its match in the previous iteration (kept in ws), with the rest of the tree
  * still searched as far as the bound requires: the same pairs as a search
- * from the root, in fewer dependent steps.
+ * from the root, in fewer dependent steps.  The subtrees beside that leaf's
+ * path are bounded by their ancestors' split planes, read from the leaf's
+ * 64-byte plane record (kept with the tree: 64 bytes per leaf).
  * Default (and KDNN_ICP_HOST_LOOP): the article's loop (§3.3) -- each
  * iteration's 17 sums come back to the host (a pinned readback), which solves
  * with kdnn_procrustes (SVD, det sign fix) and applies the convergence rule
@@ -552,8 +555,10 @@ kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_
  *      chunks as the search loads them); at most KDNN_REPLAY_CAP per query.
  *      With q_prev_dev (the previous ICP iteration's queries, m points) each
  *      search starts as icp_align's do after the first iteration: at the
- *      leaf of that query's nearest neighbour, with the box of every sibling
- *      subtree along the leaf's path (32 B each) in place of the descent.
+ *      leaf of that query's nearest neighbour, with that leaf's plane record
+ *      (64 B: the split planes of its deepest 14 ancestors) and, in trees
+ *      deeper than 14 levels, the box of each sibling subtree above those
+ *      (32 B each) in place of the descent.
  *   2. The rows are laid out per wave in the launch shape of the production
  *      kernel: nn_query's one-lane-per-query kernel, or with KDNN_REPLAY_ICP
  *      the fused ICP kernel's (work-groups, queries per wave, spread of
@@ -576,7 +581,8 @@ typedef struct kdnn_replay_info {
     int64_t visits;        /* root, box-run and leaf visits replayed */
     int64_t bytes;         /* bytes one replay loads */
     int64_t node_records;  /* node records the visits stand for (cold start: the sum of
-                              nn_query_stats' node counts; each warm-start sibling box: 1) */
+                              nn_query_stats' node counts; a warm start's plane record: 2,
+                              each sibling box it loads: 1) */
     int64_t leaf_points;   /* leaf points they stand for (sum of nn_query_stats' points) */
     int64_t truncated;     /* queries with more than KDNN_REPLAY_CAP visits (tail not replayed) */
     int64_t blocks;        /* work-groups of the launch shape */

@@ -104,6 +104,7 @@ void free_tree(kdnn_tree *t)
     if (t->d_boxes) (void)hipFree(t->d_boxes);
     if (t->d_points) (void)hipFree(t->d_points);
     if (t->d_slot_of) (void)hipFree(t->d_slot_of);
+    if (t->d_paths) (void)hipFree(t->d_paths);
     if (t->h_pinned) (void)hipHostFree(t->h_pinned);
     if (t->h_loop) (void)hipHostFree(t->h_loop);
     if (t->d_loop) (void)hipFree(t->d_loop);
@@ -629,10 +630,27 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         std::memcpy(&boxes[6 * r], &ht.nodes[r * kNodeWords], 6 * sizeof(float));
     const size_t bb = boxes.size() * sizeof(float);
     const size_t ob = size_t(n) * sizeof(int32_t);
+    // Each leaf's plane record (warm starts): the split axis and value of its
+    // ancestors at depths D-1, D-2, .. (at most kPathLevels of them).
+    const size_t leaves = size_t(1) << ht.depth;
+    std::vector<uint32_t> paths(leaves * kPathWords, 0u);
+    for (size_t j = 0; j < leaves; ++j) {
+        uint32_t *rec = &paths[j * kPathWords];
+        const size_t leaf = leaves + j;
+        for (int k = 0; k < kPathLevels && k < ht.depth; ++k) {
+            const float *w = &ht.nodes[(leaf >> (k + 1)) * kNodeWords];
+            uint32_t ax;
+            std::memcpy(&ax, &w[7], 4);
+            rec[0] |= (ax & 3u) << (2 * k);
+            std::memcpy(&rec[1 + k], &w[6], 4);
+        }
+    }
+    const size_t rb = paths.size() * sizeof(uint32_t);
     if ((e = hipMalloc(&t->d_nodes, nb)) != hipSuccess ||
         (e = hipMalloc(&t->d_boxes, bb)) != hipSuccess ||
         (e = hipMalloc(&t->d_points, pb + pad_bytes)) != hipSuccess ||
-        (e = hipMalloc(&t->d_slot_of, ob)) != hipSuccess) {
+        (e = hipMalloc(&t->d_slot_of, ob)) != hipSuccess ||
+        (e = hipMalloc(&t->d_paths, rb)) != hipSuccess) {
         free_tree(t);
         return fail(KDNN_ENOMEM, std::string("kdtree_build: hipMalloc: ") + hipGetErrorString(e));
     }
@@ -666,7 +684,8 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         (e = hipMemcpy(t->d_points, ht.points.data(), pb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(static_cast<char *>(t->d_points) + pb, pad.data(), pad_bytes,
                        hipMemcpyHostToDevice)) != hipSuccess ||
-        (e = hipMemcpy(t->d_slot_of, slot_of.data(), ob, hipMemcpyHostToDevice)) != hipSuccess) {
+        (e = hipMemcpy(t->d_slot_of, slot_of.data(), ob, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(t->d_paths, paths.data(), rb, hipMemcpyHostToDevice)) != hipSuccess) {
         free_tree(t);
         return hip_fail(e, "kdtree_build: upload");
     }
@@ -677,6 +696,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     d.boxes = t->d_boxes;
     d.points = t->d_points;
     d.slot_of = t->d_slot_of;
+    d.paths = t->d_paths;
     d.first_leaf = uint32_t(1) << ht.depth;
     d.depth = ht.depth;
     d.max_leaf = ht.max_leaf;
@@ -702,7 +722,7 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
     }
     I.build_ms = build_ms;
     I.upload_ms = upload_ms;
-    I.device_bytes = int64_t(nb + bb + pb + pad_bytes + ob);
+    I.device_bytes = int64_t(nb + bb + pb + pad_bytes + ob + rb);
     int l2 = 0;
     if ((e = hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, t->device)) != hipSuccess) {
         free_tree(t);

@@ -28,6 +28,11 @@ namespace kdnn {
 // so a leaf is one contiguous run read with 16-byte loads.
 constexpr int kNodeWords = 8;
 constexpr int kMaxDepth = 28;
+// Per-leaf plane record: the split planes of the leaf's deepest kPathLevels
+// ancestors in one 64-byte record (16 words: word 0 the ancestors' split axes,
+// two bits each, deepest first; words 1 .. kPathLevels their split values).
+constexpr int kPathLevels = 14;
+constexpr int kPathWords = 16;
 constexpr int kMaxLeafSize = 1024;
 
 struct HostTree {
@@ -70,6 +75,7 @@ struct DeviceTree {
     const void *boxes = nullptr;   // 6 floats per node slot: lo.xyz, hi.xyz (pairs 48 B)
     const void *points = nullptr;  // float4 array, 1 per point
     const void *slot_of = nullptr; // n int32: leaf-order slot of each original index
+    const void *paths = nullptr;   // kPathWords words per leaf: its plane record
     uint32_t first_leaf = 1;       // 2^D
     int32_t depth = 0;             // D
     int32_t max_leaf = 0;          // points in the largest leaf
@@ -292,6 +298,7 @@ struct kdnn_tree {
     void *d_boxes = nullptr;
     void *d_points = nullptr;
     void *d_slot_of = nullptr;
+    void *d_paths = nullptr;
     kdnn_tree_info info{};
     double *h_pinned = nullptr;  // host readback slot for the ICP sums (32 doubles;
                                  // the last word: completion sequence number)

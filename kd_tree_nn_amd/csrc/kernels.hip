@@ -143,6 +143,7 @@ struct TreeView {
     const float4 *__restrict__ boxes;     // children of i: boxes[3i .. 3i+2] (48 B)
     const float4 *__restrict__ pts;
     const int32_t *__restrict__ slot_of;  // original index -> leaf-order slot
+    const uint4 *__restrict__ paths;      // per leaf: 64-byte plane record (kPathWords)
     uint32_t first_leaf;  // 2^D
     int32_t depth;        // D
     int64_t n;
@@ -633,10 +634,11 @@ __device__ __forceinline__ void task_finish(WaveTask &w, unsigned long long *oke
 
 // The instrumented search's visit stream, one row per query: 0 for the root's
 // box, an internal node i for the run of its two children's boxes, a leaf
-// node for that leaf's points, kSiblingVisit | v for the box of node v alone
-// (a warm start's sibling boxes).  Visits beyond the row's tcap entries are
-// counted, not stored.
+// node for that leaf's points, kPlaneVisit | leaf for that leaf's plane
+// record and kSiblingVisit | v for the box of node v alone (both read by a
+// warm start).  Visits beyond the row's tcap entries are counted, not stored.
 constexpr uint32_t kSiblingVisit = 0x80000000u;
+constexpr uint32_t kPlaneVisit = 0x40000000u;
 __device__ __forceinline__ void trace_visit(WaveTask &w, uint32_t *trow, uint32_t tcap,
                                             uint32_t e)
 {
@@ -712,79 +714,41 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
 // Warm start of a task at `leaf` (a heap index in [2^D, 2^(D+1)); the ICP
 // loop passes the leaf that held the query's match in the previous
 // iteration, usually at or next to the new one).  The subtrees beside the
-// leaf's path -- the sibling of its ancestor at every depth 1 .. D -- cover
-// the rest of the tree, so the task begins as if it had descended to the leaf:
-// each sibling is pending under the distance bound of its box (lbs, one
-// level per path depth), and the walk continues exactly as after a descent,
-// visiting the pending subtrees deepest first and only while their bound
-// lets them in.  The result is the same as from the root; the descent's chain
-// of dependent loads is replaced by independent loads of the sibling boxes
-// (kWarmBatch levels at a time) and the first leaf's scan gives a close bound
-// at once.
-// STATS: each sibling box counts as one node record (and is traced).
-// (Scene, warm searches of the ICP loop: batches of 4 and 7 levels measured
-// alike, 29.6 / 29.8 us; all 13 levels at once 30.8 us, its 128 registers
-// costing the whole kernel more than the saved round trips.)
+// leaf's path -- the sibling of its ancestor at every depth 0 .. D-1 -- cover
+// the rest of the tree, so the task begins as if it had descended to the
+// leaf: it scans the leaf, each sibling is pending under a lower bound of its
+// distance (lbs, one level per ancestor depth) while that bound lets it in,
+// and the walk goes on exactly as after a descent, visiting pending subtrees
+// deepest first.  The result is the same as from the root.
+//
+// The bounds come from the ancestors' split planes.  The sibling below the
+// depth-d ancestor lies wholly on the far side of that ancestor's plane (left
+// points <= split <= right points), so the squared gap between the query and
+// the plane, when the query is on the leaf's side, bounds every point of it
+// from below; computed as fl(gap)^2 it is also no larger than the rounded
+// squared distance of any such point (each rounding step is monotone), so
+// pruning with it drops no point that could tie or win.  The planes of the
+// deepest kPathLevels ancestors sit in the leaf's 64-byte plane record, one
+// cache line loaded in the same round trip as the leaf's points; the
+// siblings' boxes would take a line each, and a scattered gather costs about
+// a line fetch per lane whatever its width (Scene, warm searches of the ICP
+// loop: 25.1 -> 24.2 us; the 131k LiDAR frames 24.9 -> 22.3 us; the same
+// planes read from the 32-byte node records, a line each, measured no faster
+// than the boxes).  Shallower levels (trees deeper than kPathLevels) load
+// their sibling boxes, kWarmBatch at a time: those sit near the root, shared
+// by the wave's lanes.  A plane is a looser bound than the box, so a sibling
+// may be entered that its box would have kept out; its children's boxes are
+// tested as usual.
+// STATS: the plane record counts as two node records (64 bytes; traced as one
+// kPlaneVisit entry for the leaf), each sibling box as one.
 #ifndef KDNN_WARM_BATCH
 #define KDNN_WARM_BATCH 4
 #endif
 constexpr int kWarmBatch = KDNN_WARM_BATCH;
-template <bool STATS>
+template <bool STATS, int CH>
 __device__ __forceinline__ void warm_start(const TreeView &t, uint32_t leaf, float qx, float qy,
                                            float qz, float *lbs, WaveTask &w, uint32_t *trow,
-                                           uint32_t tcap)
-{
-    const uint32_t D = uint32_t(t.depth);
-    const float best = key_dist(w.key);
-    uint32_t pend = 0u;
-    for (int d0 = int(D) - 1; d0 >= 0; d0 -= kWarmBatch) {
-        float4 P[kWarmBatch][2];
-#pragma unroll
-        for (int u = 0; u < kWarmBatch; ++u) {
-            // depth of the sibling's parent (past the root: the root again, unused)
-            const uint32_t d = uint32_t(d0 - u < 0 ? 0 : d0 - u);
-            const uint32_t parent = leaf >> (D - d);
-            const uint32_t odd = ((leaf >> (D - d - 1u)) & 1u) ^ 1u;  // the sibling's side
-            const float4 *pb = t.boxes + 3 * size_t(parent) + odd;
-            P[u][0] = pb[0];
-            P[u][1] = pb[1];
-        }
-#pragma unroll
-        for (int u = 0; u < kWarmBatch; ++u) {
-            const int d = d0 - u;
-            if (d >= 0) {
-                const bool odd = (((leaf >> (D - uint32_t(d) - 1u)) & 1u) ^ 1u) != 0u;
-                const float4 A = odd ? make_float4(P[u][0].z, P[u][0].w, P[u][1].x, P[u][1].y)
-                                     : P[u][0];
-                const float4 B = odd ? make_float4(P[u][1].z, P[u][1].w, 0.0f, 0.0f)
-                                     : make_float4(P[u][1].x, P[u][1].y, 0.0f, 0.0f);
-                const float lb = box_lb(qx, qy, qz, A, B);
-                lbs[d * kWG] = lb;
-                pend |= enters(lb, best) ? (1u << d) : 0u;
-                if constexpr (STATS) {
-                    ++w.cn;
-                    trace_visit(w, trow, tcap, kSiblingVisit | ((leaf >> (D - uint32_t(d) - 1u)) ^ 1u));
-                }
-            }
-        }
-    }
-    w.pend = pend;
-    w.i = leaf;
-}
-
-// The same with the start leaf scanned here too: its points are loaded with
-// the first sibling boxes (one round trip for both), its best key bounds the
-// siblings, which are pending only while it lets them in, and the task goes on
-// at the next pending subtree -- already holding a candidate.  okey_own: the
-// query's best key in LDS (this lane's own slot).
-#ifndef KDNN_WARM_LEAF
-#define KDNN_WARM_LEAF 1
-#endif
-template <bool STATS, int CH>
-__device__ __forceinline__ void warm_start_leaf(const TreeView &t, uint32_t leaf, float qx,
-                                                float qy, float qz, float *lbs, WaveTask &w,
-                                                uint32_t *trow, uint32_t tcap,
-                                                unsigned long long *okey_own)
+                                           uint32_t tcap, unsigned long long *okey_own)
 {
     const uint32_t D = uint32_t(t.depth);
     int32_t begin, last, end;
@@ -793,41 +757,10 @@ __device__ __forceinline__ void warm_start_leaf(const TreeView &t, uint32_t leaf
     const float4 *pc = t.pts + begin;
 #pragma unroll
     for (int c = 0; c < CH; ++c) p[c] = pc[c];
-    float4 P[kWarmBatch][2];
-    auto load_batch = [&](int d0) {
+    const uint4 *const pr = t.paths + 4 * size_t(leaf - t.first_leaf);
+    uint4 R[kPathWords / 4];
 #pragma unroll
-        for (int u = 0; u < kWarmBatch; ++u) {
-            const uint32_t d = uint32_t(d0 - u < 0 ? 0 : d0 - u);
-            const uint32_t parent = leaf >> (D - d);
-            const uint32_t odd = ((leaf >> (D - d - 1u)) & 1u) ^ 1u;
-            const float4 *pb = t.boxes + 3 * size_t(parent) + odd;
-            P[u][0] = pb[0];
-            P[u][1] = pb[1];
-        }
-    };
-    uint32_t pend = 0u;
-    auto bound_batch = [&](int d0, float best) {
-#pragma unroll
-        for (int u = 0; u < kWarmBatch; ++u) {
-            const int d = d0 - u;
-            if (d >= 0) {
-                const bool odd = (((leaf >> (D - uint32_t(d) - 1u)) & 1u) ^ 1u) != 0u;
-                const float4 A = odd ? make_float4(P[u][0].z, P[u][0].w, P[u][1].x, P[u][1].y)
-                                     : P[u][0];
-                const float4 B = odd ? make_float4(P[u][1].z, P[u][1].w, 0.0f, 0.0f)
-                                     : make_float4(P[u][1].x, P[u][1].y, 0.0f, 0.0f);
-                const float lb = box_lb(qx, qy, qz, A, B);
-                lbs[d * kWG] = lb;
-                pend |= enters(lb, best) ? (1u << d) : 0u;
-                if constexpr (STATS) {
-                    ++w.cn;
-                    trace_visit(w, trow, tcap,
-                                kSiblingVisit | ((leaf >> (D - uint32_t(d) - 1u)) ^ 1u));
-                }
-            }
-        }
-    };
-    load_batch(int(D) - 1);
+    for (int v = 0; v < kPathWords / 4; ++v) R[v] = pr[v];
     uint64_t key = w.key;
     for (uint32_t k0 = uint32_t(begin);;) {
 #pragma unroll
@@ -848,12 +781,62 @@ __device__ __forceinline__ void warm_start_leaf(const TreeView &t, uint32_t leaf
     if constexpr (STATS) {
         w.cp += uint32_t(end - begin);
         trace_visit(w, trow, tcap, leaf);
+        w.cn += 2;
+        trace_visit(w, trow, tcap, kPlaneVisit | leaf);
     }
     const float best = key_dist(key);
-    bound_batch(int(D) - 1, best);
-    for (int d0 = int(D) - 1 - kWarmBatch; d0 >= 0; d0 -= kWarmBatch) {
-        load_batch(d0);
-        bound_batch(d0, best);
+    uint32_t pend = 0u;
+    const uint32_t axes = R[0].x;
+#pragma unroll
+    for (int k = 0; k < kPathLevels; ++k) {
+        // the ancestor at depth d = D-1-k: record word 1+k
+        const int d = int(D) - 1 - k;
+        if (d >= 0) {
+            const uint4 Rv = R[(k + 1) / 4];
+            const uint32_t wv = (k + 1) % 4 == 0 ? Rv.x : (k + 1) % 4 == 1 ? Rv.y
+                                : (k + 1) % 4 == 2 ? Rv.z : Rv.w;
+            const float split = __uint_as_float(wv);
+            const uint32_t ax = (axes >> (2 * k)) & 3u;
+            const float qa = ax == 0u ? qx : (ax == 1u ? qy : qz);
+            // the leaf's side of the plane: right child of its depth-d ancestor
+            const bool right = ((leaf >> k) & 1u) != 0u;
+            const float gap = right ? qa - split : split - qa;
+            const float lb = gap > 0.0f ? gap * gap : 0.0f;
+            lbs[d * kWG] = lb;
+            pend |= enters(lb, best) ? (1u << d) : 0u;
+        }
+    }
+    // levels above the record: their sibling boxes
+    for (int d0 = int(D) - 1 - kPathLevels; d0 >= 0; d0 -= kWarmBatch) {
+        float4 P[kWarmBatch][2];
+#pragma unroll
+        for (int u = 0; u < kWarmBatch; ++u) {
+            const uint32_t d = uint32_t(d0 - u < 0 ? 0 : d0 - u);
+            const uint32_t parent = leaf >> (D - d);
+            const uint32_t odd = ((leaf >> (D - d - 1u)) & 1u) ^ 1u;
+            const float4 *pb = t.boxes + 3 * size_t(parent) + odd;
+            P[u][0] = pb[0];
+            P[u][1] = pb[1];
+        }
+#pragma unroll
+        for (int u = 0; u < kWarmBatch; ++u) {
+            const int d = d0 - u;
+            if (d >= 0) {
+                const bool odd = (((leaf >> (D - uint32_t(d) - 1u)) & 1u) ^ 1u) != 0u;
+                const float4 A = odd ? make_float4(P[u][0].z, P[u][0].w, P[u][1].x, P[u][1].y)
+                                     : P[u][0];
+                const float4 B = odd ? make_float4(P[u][1].z, P[u][1].w, 0.0f, 0.0f)
+                                     : make_float4(P[u][1].x, P[u][1].y, 0.0f, 0.0f);
+                const float lb = box_lb(qx, qy, qz, A, B);
+                lbs[d * kWG] = lb;
+                pend |= enters(lb, best) ? (1u << d) : 0u;
+                if constexpr (STATS) {
+                    ++w.cn;
+                    trace_visit(w, trow, tcap,
+                                kSiblingVisit | ((leaf >> (D - uint32_t(d) - 1u)) ^ 1u));
+                }
+            }
+        }
     }
     const uint64_t seen = atomicMin(okey_own, (unsigned long long)key);
     w.key = seen < key ? seen : key;
@@ -927,11 +910,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
     w.cp = 0u;
     w.nt = 0u;
     if (own && hint != 0u && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
-        if (KDNN_WARM_LEAF)
-            warm_start_leaf<STATS, CH>(t, hint, oqx, oqy, oqz, lbs, w, trow, tcap,
-                                       &okey[threadIdx.x]);
-        else
-            warm_start<STATS>(t, hint, oqx, oqy, oqz, lbs, w, trow, tcap);
+        warm_start<STATS, CH>(t, hint, oqx, oqy, oqz, lbs, w, trow, tcap, &okey[threadIdx.x]);
     } else if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
         const float4 A = t.nodes[2];
         const float4 B = t.nodes[3];
@@ -2537,6 +2516,7 @@ static TreeView tree_view(const DeviceTree &t)
     v.nodes = static_cast<const float4 *>(t.nodes);
     v.boxes = static_cast<const float4 *>(t.boxes);
     v.slot_of = static_cast<const int32_t *>(t.slot_of);
+    v.paths = static_cast<const uint4 *>(t.paths);
     v.pts = static_cast<const float4 *>(t.points);
     v.first_leaf = t.first_leaf;
     v.depth = t.depth;
@@ -3023,6 +3003,10 @@ __device__ __forceinline__ void replay_cost(const TreeView &t, uint32_t e, uint3
         bytes = 32u;
         recs = 1u;
         pts = 0u;
+    } else if (e & kPlaneVisit) {
+        bytes = 16u * uint32_t(kPathWords / 4);
+        recs = 2u;
+        pts = 0u;
     } else if (e < t.first_leaf) {
         bytes = 48u;
         recs = 2u;
@@ -3101,6 +3085,14 @@ __device__ __forceinline__ uint32_t replay_load(const TreeView &t, uint32_t e)
         const float4 P0 = pb[0], P1 = pb[1];
         x = __float_as_uint(P0.x) ^ __float_as_uint(P0.w) ^ __float_as_uint(P1.y) ^
             __float_as_uint(P1.z);
+    } else if (e & kPlaneVisit) {
+        // the leaf's plane record, as warm_start loads it
+        const uint4 *const pr = t.paths + 4 * size_t((e & ~kPlaneVisit) - t.first_leaf);
+#pragma unroll
+        for (int v = 0; v < kPathWords / 4; ++v) {
+            const uint4 r = pr[v];
+            x ^= r.x ^ r.y ^ r.z ^ r.w;
+        }
     } else if (e < t.first_leaf) {
         const float4 *const pb = t.boxes + 3 * size_t(e);
         const float4 P0 = pb[0], P1 = pb[1], P2 = pb[2];

@@ -417,20 +417,27 @@ def test_warm_start_ties_and_gaps(torch, kdnn):
     previous match.  On a lattice target with sources at cell centres (8 target
     points at exactly the same distance, lowest index wins), with NaN sources
     (no match, no warm start) and far outliers, every iterate must still equal
-    the loop of separate root-start calls bit for bit, under max_dist too."""
-    g = np.stack(np.meshgrid(*(np.arange(12, dtype=np.float32),) * 3, indexing="ij"), -1)
-    tgt = g.reshape(-1, 3)
-    rng = np.random.Generator(np.random.PCG64(17))
-    tgt = tgt[rng.permutation(len(tgt))]                  # ties between unrelated indices
-    src = (g[:-1, :-1, :-1] + 0.5).reshape(-1, 3).astype(np.float32)
-    src = np.concatenate([src, np.full((3, 3), np.nan, np.float32),
-                          np.array([[60.0, 5.0, 5.0], [-40.0, -40.0, 3.0]], np.float32)])
-    for leaf in (1, 8, 16):
+    the loop of separate root-start calls bit for bit, under max_dist too.
+    Lattice coordinates put many points exactly on split planes (on both
+    sides of them), the case the plane bounds of the warm start must get
+    right; the 26^3 lattice with one point per leaf is deeper (D = 15) than
+    the 14 levels of a leaf's plane record, so its searches also bound the
+    subtree below the root by its box."""
+    for side, leaf in ((12, 1), (12, 8), (12, 16), (26, 1)):
+        g = np.stack(np.meshgrid(*(np.arange(side, dtype=np.float32),) * 3, indexing="ij"), -1)
+        tgt = g.reshape(-1, 3)
+        rng = np.random.Generator(np.random.PCG64(17))
+        tgt = tgt[rng.permutation(len(tgt))]                  # ties between unrelated indices
+        src = (g[:-1, :-1, :-1] + 0.5).reshape(-1, 3).astype(np.float32)
+        src = np.concatenate([src, np.full((3, 3), np.nan, np.float32),
+                              np.array([[60.0, 5.0, 5.0], [-40.0, -40.0, 3.0]], np.float32)])
         tree = kdnn.Tree(tgt, leaf)
+        if side == 26:
+            assert tree.info["depth"] > 14
         sd = dev(torch, src)
         auto = bool(tree.info["auto_sort_icp"])
         for kw in ({}, {"max_dist": 0.9}, {"sort": True}):
-            say("warm start ties and gaps, leaf", leaf, kw)
+            say("warm start ties and gaps, lattice", side, "leaf", leaf, kw)
             gi = tree.icp(sd, max_iter=6, R0=synth.rot_z(0.0), t0=[0.0, 0.0, 0.0], **kw)
             R, t, E, hist = _step_by_step(kdnn, tree, sd, 6, kw.get("sort", auto),
                                           kw.get("max_dist"))

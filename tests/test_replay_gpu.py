@@ -155,25 +155,49 @@ def test_replay_argument_checks(torch, kdnn):
 @pytest.mark.parametrize("name", ["tiny_leaf8", "uniform_ragged_leaf16", "scene_leaf16"])
 def test_replay_warm_start_tallies(torch, kdnn, name):
     """Warm-started replay (the previous iteration's queries given): every
-    searched query records the D sibling boxes beside its start leaf (one node
-    record each) and at least one leaf; bytes follow from the tallies; with
-    the queries themselves as the previous iteration every search starts at
-    its own answer's leaf, so it scans no more points than from the root."""
+    searched query records its start leaf's 64-byte plane record (two node
+    records), the sibling boxes above the record's 14 levels (none in these
+    trees) and at least one leaf -- its start leaf, with the queries
+    themselves as the previous iteration their own answer's leaf; bytes
+    follow from the tallies.  (A plane bounds its sibling more loosely than
+    the sibling's box, so a warm search may scan a leaf the search from the
+    root skips: no comparison of point counts holds in general.)"""
     tgt, q, leaf = _case(name)
     say("replay warm start", name, "queries", len(q))
     tree = kdnn.Tree(tgt, leaf)
     qd = dev(torch, q)
-    _, _, cn, cp = tree.query_stats(qd)
     ms, info = tree.replay_bench(qd, icp=True, reps=2, prev=qd)
     assert np.all(ms > 0.0) and info["truncated"] == 0
     D = tree.info["depth"]
+    assert D <= 14
     finite = int(np.isfinite(q).all(axis=1).sum())
-    siblings = finite * D
-    pairs2 = info["node_records"] - siblings
+    pairs2 = info["node_records"] - 2 * finite
     assert pairs2 >= 0 and pairs2 % 2 == 0
     pairs = pairs2 // 2
-    leaves = info["visits"] - siblings - pairs
+    leaves = info["visits"] - finite - pairs
     assert leaves >= finite
     chunk = 8 if tree.info["max_leaf"] <= 8 else 16
-    assert info["bytes"] == 32 * siblings + 48 * pairs + 16 * chunk * leaves
-    assert info["leaf_points"] <= int(cp.cpu().numpy().astype(np.int64).sum())
+    assert info["bytes"] == 64 * finite + 48 * pairs + 16 * chunk * leaves
+    assert info["leaf_points"] >= finite * tree.info["min_leaf"]
+
+
+def test_replay_warm_start_deep_tree(torch, kdnn):
+    """A tree deeper than the plane record (leaf size 1, 2^15 leaves): every
+    warm search also loads the D - 14 sibling boxes nearest the root, one
+    node record and 32 bytes each."""
+    tgt, q = _uniform(5, 20_000, 3_000)
+    say("replay warm start, deep tree, 20000 points leaf 1, 3000 queries")
+    tree = kdnn.Tree(tgt, 1)
+    D = tree.info["depth"]
+    assert D > 14
+    qd = dev(torch, q)
+    ms, info = tree.replay_bench(qd, icp=True, reps=2, prev=qd)
+    assert np.all(ms > 0.0) and info["truncated"] == 0
+    m = len(q)
+    top = D - 14
+    pairs2 = info["node_records"] - (2 + top) * m
+    assert pairs2 >= 0 and pairs2 % 2 == 0
+    pairs = pairs2 // 2
+    leaves = info["visits"] - (1 + top) * m - pairs
+    assert leaves >= m
+    assert info["bytes"] == (64 + 32 * top) * m + 48 * pairs + 16 * 8 * leaves
