@@ -209,7 +209,11 @@ size_t nn_query_workspace_bytes(int64_t m);
 /* Exact nearest neighbour of every query (article §2.2 search with
  * backtracking and split-plane pruning; §3.2 one query per GPU lane;
  * §5.3 queries Morton-ordered so that neighbouring lanes walk the same
- * branches).
+ * branches).  Each search first locates the leaf whose cell holds its query
+ * by the ancestors' split planes, scans it, and then visits the rest of the
+ * tree as far as the best distance requires: the subtrees beside that leaf's
+ * path are bounded by their split planes (the leaf's plane record), nodes
+ * below them by their boxes.
  *   q_dev      : m x 3 fp32 queries (device).
  *   idx_dev    : m int32 out, original target index of each nearest point.
  *   dist2_dev  : m fp32 out, its squared distance.
@@ -236,7 +240,10 @@ kdnn_status nn_query_radius(const kdnn_tree *tree, const float *q_dev, int64_t m
                             size_t ws_bytes, hipStream_t stream);
 
 /* Instrumented nn_query: same results, and per query the number of tree node
- * records loaded and of leaf points scanned (uint32 each, may be NULL).  With
+ * records loaded and of leaf points scanned (uint32 each, may be NULL).  Node
+ * records: one per split plane read by the point location (D), two for the
+ * start leaf's 64-byte plane record, one per sibling box above that record's
+ * 14 levels (D - 14 when D > 14), two per child-pair run.  With
  * the default schedule the counts are those of the exact single-lane search
  * of that query (lanes do not share work in this mode, so the counts do not
  * depend on which queries share a wavefront; the balanced search of nn_query
@@ -550,9 +557,11 @@ kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_
  * time is how far its dependent chains and instruction stream keep it from
  * the memory system's own limit for that access stream.
  *   1. The instrumented single-lane search (the one nn_query_stats counts)
- *      records each query's visits: the root's box (32 B), each internal
- *      node's run of child boxes (48 B), each leaf (its points, loaded in
- *      chunks as the search loads them); at most KDNN_REPLAY_CAP per query.
+ *      records each query's visits: the split plane of each node on its
+ *      point location's path (8 B), its start leaf's plane record (64 B),
+ *      each internal node's run of child boxes (48 B), each leaf (its points,
+ *      loaded in chunks as the search loads them); at most KDNN_REPLAY_CAP
+ *      per query.
  *      With q_prev_dev (the previous ICP iteration's queries, m points) each
  *      search starts as icp_align's do after the first iteration: at the
  *      leaf of that query's nearest neighbour, with that leaf's plane record

@@ -636,9 +636,12 @@ __device__ __forceinline__ void task_finish(WaveTask &w, unsigned long long *oke
 // box, an internal node i for the run of its two children's boxes, a leaf
 // node for that leaf's points, kPlaneVisit | leaf for that leaf's plane
 // record and kSiblingVisit | v for the box of node v alone (both read by a
-// warm start).  Visits beyond the row's tcap entries are counted, not stored.
+// warm start), kLocateVisit | i for node i's split plane (read by the point
+// location of a search from the root).  Visits beyond the row's tcap entries
+// are counted, not stored.
 constexpr uint32_t kSiblingVisit = 0x80000000u;
 constexpr uint32_t kPlaneVisit = 0x40000000u;
+constexpr uint32_t kLocateVisit = 0x20000000u;
 __device__ __forceinline__ void trace_visit(WaveTask &w, uint32_t *trow, uint32_t tcap,
                                             uint32_t e)
 {
@@ -709,6 +712,40 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
         w.key = okey[town];
         w.i = enters(tlb, key_dist(w.key)) ? tv : kDone;
     }
+}
+
+// Point location: the leaf whose cell holds the query, found by the split
+// planes of its ancestors (node i's split value and axis, the last 8 bytes of
+// its 32-byte record), one dependent 8-byte load per level -- the top levels
+// shared by the wave's lanes and cached.  A search without a start leaf of
+// its own (the first ICP iteration, nn_query) starts there as a warm start
+// would (below): the same exact answer as a descent from the root, whose
+// child-pair runs (three 16-byte loads per level, each lane's own lines below
+// the top) and box-bounded backtracking it replaces.  Measured (search
+// kernels, MI355X): nn_query Scene 30.2 -> 26.5 us, Stress 1M leaf 8 213 ->
+// 148 us, Skewed 500k leaf 16 168 -> 157 us; the first ICP iteration's fused
+// kernel, Scene 33.3 -> 30.4 us, the 131k LiDAR frames ~47 -> ~39 us.
+// STATS: each plane read counts as one node record (traced kLocateVisit | i).
+#ifndef KDNN_COLD_LOCATE
+#define KDNN_COLD_LOCATE 1
+#endif
+template <bool STATS>
+__device__ __forceinline__ uint32_t locate_leaf(const TreeView &t, float qx, float qy, float qz,
+                                                WaveTask &w, uint32_t *trow, uint32_t tcap)
+{
+    const float2 *const sa = reinterpret_cast<const float2 *>(t.nodes) + 3;
+    uint32_t i = 1u;
+    while (i < t.first_leaf) {
+        const float2 S = sa[4 * size_t(i)];
+        if constexpr (STATS) {
+            ++w.cn;
+            trace_visit(w, trow, tcap, kLocateVisit | i);
+        }
+        const uint32_t ax = __float_as_uint(S.y);
+        const float qa = ax == 0u ? qx : (ax == 1u ? qy : qz);
+        i = 2u * i + (qa > S.x ? 1u : 0u);  // left points <= split
+    }
+    return i;
 }
 
 // Warm start of a task at `leaf` (a heap index in [2^D, 2^(D+1)); the ICP
@@ -909,9 +946,13 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
     w.cn = 0u;
     w.cp = 0u;
     w.nt = 0u;
-    if (own && hint != 0u && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
-        warm_start<STATS, CH>(t, hint, oqx, oqy, oqz, lbs, w, trow, tcap, &okey[threadIdx.x]);
-    } else if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
+    const bool searched = own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz);
+    uint32_t start = searched ? hint : 0u;
+    if (KDNN_COLD_LOCATE && searched && start == 0u)
+        start = locate_leaf<STATS>(t, oqx, oqy, oqz, w, trow, tcap);
+    if (start != 0u) {
+        warm_start<STATS, CH>(t, start, oqx, oqy, oqz, lbs, w, trow, tcap, &okey[threadIdx.x]);
+    } else if (searched) {
         const float4 A = t.nodes[2];
         const float4 B = t.nodes[3];
         if constexpr (STATS) {
@@ -3007,6 +3048,10 @@ __device__ __forceinline__ void replay_cost(const TreeView &t, uint32_t e, uint3
         bytes = 16u * uint32_t(kPathWords / 4);
         recs = 2u;
         pts = 0u;
+    } else if (e & kLocateVisit) {
+        bytes = 8u;
+        recs = 1u;
+        pts = 0u;
     } else if (e < t.first_leaf) {
         bytes = 48u;
         recs = 2u;
@@ -3085,6 +3130,10 @@ __device__ __forceinline__ uint32_t replay_load(const TreeView &t, uint32_t e)
         const float4 P0 = pb[0], P1 = pb[1];
         x = __float_as_uint(P0.x) ^ __float_as_uint(P0.w) ^ __float_as_uint(P1.y) ^
             __float_as_uint(P1.z);
+    } else if (e & kLocateVisit) {
+        // node i's split value and axis, as locate_leaf loads them
+        const float2 S = reinterpret_cast<const float2 *>(t.nodes)[4 * size_t(e & ~kLocateVisit) + 3];
+        x = __float_as_uint(S.x) ^ __float_as_uint(S.y);
     } else if (e & kPlaneVisit) {
         // the leaf's plane record, as warm_start loads it
         const uint4 *const pr = t.paths + 4 * size_t((e & ~kPlaneVisit) - t.first_leaf);
