@@ -212,7 +212,7 @@ size_t nn_query_workspace_bytes(int64_t m);
  * branches).  Each search first locates the leaf whose cell holds its query
  * by the ancestors' split planes, scans it, and then visits the rest of the
  * tree as far as the best distance requires: the subtrees beside that leaf's
- * path are bounded by their split planes (the leaf's plane record), nodes
+ * path are bounded along their parents' split axes (the leaf's plane record), nodes
  * below them by their boxes.
  *   q_dev      : m x 3 fp32 queries (device).
  *   idx_dev    : m int32 out, original target index of each nearest point.
@@ -391,8 +391,9 @@ kdnn_status kdnn_procrustes(const kdnn_icp_sums *sums, double *R_out, double *t_
  * its match in the previous iteration (kept in ws), with the rest of the tree
  * still searched as far as the bound requires: the same pairs as a search
  * from the root, in fewer dependent steps.  The subtrees beside that leaf's
- * path are bounded by their ancestors' split planes, read from the leaf's
- * 64-byte plane record (kept with the tree: 64 bytes per leaf).
+ * path are bounded along their parents' split axes by the near faces of
+ * their boxes, read from the leaf's 64-byte plane record (kept with the tree:
+ * 64 bytes per leaf).
  * Default (and KDNN_ICP_HOST_LOOP): the article's loop (§3.3) -- each
  * iteration's 17 sums come back to the host (a pinned readback), which solves
  * with kdnn_procrustes (SVD, det sign fix) and applies the convergence rule
@@ -565,7 +566,8 @@ kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_
  *      With q_prev_dev (the previous ICP iteration's queries, m points) each
  *      search starts as icp_align's do after the first iteration: at the
  *      leaf of that query's nearest neighbour, with that leaf's plane record
- *      (64 B: the split planes of its deepest 14 ancestors) and, in trees
+ *      (64 B: the split axes of its deepest 14 ancestors and the near faces
+ *      of their off-path children's boxes along them) and, in trees
  *      deeper than 14 levels, the box of each sibling subtree above those
  *      (32 B each) in place of the descent.
  *   2. The rows are laid out per wave in the launch shape of the production

@@ -630,8 +630,10 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
         std::memcpy(&boxes[6 * r], &ht.nodes[r * kNodeWords], 6 * sizeof(float));
     const size_t bb = boxes.size() * sizeof(float);
     const size_t ob = size_t(n) * sizeof(int32_t);
-    // Each leaf's plane record (warm starts): the split axis and value of its
-    // ancestors at depths D-1, D-2, .. (at most kPathLevels of them).
+    // Each leaf's plane record (warm starts): for its ancestors at depths D-1,
+    // D-2, .. (at most kPathLevels of them) the split axis and the near face,
+    // along that axis, of the box of the child off the leaf's path (its lo
+    // for a right child, its hi for a left one; at or beyond the split).
     const size_t leaves = size_t(1) << ht.depth;
     std::vector<uint32_t> paths(leaves * kPathWords, 0u);
     for (size_t j = 0; j < leaves; ++j) {
@@ -641,8 +643,12 @@ kdnn_status kdtree_build(const float *xyz_host, int64_t n, const kdnn_build_para
             const float *w = &ht.nodes[(leaf >> (k + 1)) * kNodeWords];
             uint32_t ax;
             std::memcpy(&ax, &w[7], 4);
-            rec[0] |= (ax & 3u) << (2 * k);
-            std::memcpy(&rec[1 + k], &w[6], 4);
+            ax &= 3u;
+            const size_t sib = (leaf >> k) ^ 1u;
+            const float *sb = &ht.nodes[sib * kNodeWords];
+            const float face = (sib & 1u) ? sb[ax] : sb[3 + ax];
+            rec[0] |= ax << (2 * k);
+            std::memcpy(&rec[1 + k], &face, 4);
         }
     }
     const size_t rb = paths.size() * sizeof(uint32_t);

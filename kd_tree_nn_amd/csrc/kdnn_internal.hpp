@@ -28,9 +28,10 @@ namespace kdnn {
 // so a leaf is one contiguous run read with 16-byte loads.
 constexpr int kNodeWords = 8;
 constexpr int kMaxDepth = 28;
-// Per-leaf plane record: the split planes of the leaf's deepest kPathLevels
-// ancestors in one 64-byte record (16 words: word 0 the ancestors' split axes,
-// two bits each, deepest first; words 1 .. kPathLevels their split values).
+// Per-leaf plane record: for the leaf's deepest kPathLevels ancestors, in one
+// 64-byte record (16 words): word 0 their split axes, two bits each, deepest
+// first; words 1 .. kPathLevels the near face, along that axis, of the box of
+// each one's child off the leaf's path (at or beyond the split).
 constexpr int kPathLevels = 14;
 constexpr int kPathWords = 16;
 constexpr int kMaxLeafSize = 1024;

@@ -760,22 +760,26 @@ __device__ __forceinline__ uint32_t locate_leaf(const TreeView &t, float qx, flo
 //
 // The bounds come from the ancestors' split planes.  The sibling below the
 // depth-d ancestor lies wholly on the far side of that ancestor's plane (left
-// points <= split <= right points), so the squared gap between the query and
-// the plane, when the query is on the leaf's side, bounds every point of it
-// from below; computed as fl(gap)^2 it is also no larger than the rounded
-// squared distance of any such point (each rounding step is monotone), so
-// pruning with it drops no point that could tie or win.  The planes of the
-// deepest kPathLevels ancestors sit in the leaf's 64-byte plane record, one
-// cache line loaded in the same round trip as the leaf's points; the
-// siblings' boxes would take a line each, and a scattered gather costs about
-// a line fetch per lane whatever its width (Scene, warm searches of the ICP
-// loop: 25.1 -> 24.2 us; the 131k LiDAR frames 24.9 -> 22.3 us; the same
-// planes read from the 32-byte node records, a line each, measured no faster
-// than the boxes).  Shallower levels (trees deeper than kPathLevels) load
-// their sibling boxes, kWarmBatch at a time: those sit near the root, shared
-// by the wave's lanes.  A plane is a looser bound than the box, so a sibling
-// may be entered that its box would have kept out; its children's boxes are
-// tested as usual.
+// points <= split <= right points), and its box's near face along the split
+// axis lies at or beyond the plane: the squared gap between the query and
+// that face, when the query is on the leaf's side of it, bounds every point
+// of the sibling from below; computed as fl(gap)^2 it is also no larger than
+// the rounded squared distance of any such point (each rounding step is
+// monotone), so pruning with it drops no point that could tie or win.  (An
+// empty sibling's face is at infinity: never entered.)  The faces of the
+// deepest kPathLevels ancestors' siblings sit in the leaf's 64-byte plane
+// record, one cache line loaded in the same round trip as the leaf's points;
+// the siblings' boxes would take a line each, and a scattered gather costs
+// about a line fetch per lane whatever its width (Scene, warm searches of the
+// ICP loop: 25.1 -> 24.2 us with the split values themselves; the 131k LiDAR
+// frames 24.9 -> 22.3 us; the same planes read from the 32-byte node records,
+// a line each, measured no faster than the boxes).  The face prunes more than
+// the split: Scene (host simulation) 0.71 siblings entered per query with the
+// splits, 0.63 with the faces, 0.60 with the whole boxes.  Shallower levels
+// (trees deeper than kPathLevels) load their sibling boxes, kWarmBatch at a
+// time: those sit near the root, shared by the wave's lanes.  A one-axis
+// bound is looser than the box, so a sibling may be entered that its box
+// would have kept out; its children's boxes are tested as usual.
 // STATS: the plane record counts as two node records (64 bytes; traced as one
 // kPlaneVisit entry for the leaf), each sibling box as one.
 #ifndef KDNN_WARM_BATCH
@@ -832,12 +836,13 @@ __device__ __forceinline__ void warm_start(const TreeView &t, uint32_t leaf, flo
             const uint4 Rv = R[(k + 1) / 4];
             const uint32_t wv = (k + 1) % 4 == 0 ? Rv.x : (k + 1) % 4 == 1 ? Rv.y
                                 : (k + 1) % 4 == 2 ? Rv.z : Rv.w;
-            const float split = __uint_as_float(wv);
+            const float face = __uint_as_float(wv);
             const uint32_t ax = (axes >> (2 * k)) & 3u;
             const float qa = ax == 0u ? qx : (ax == 1u ? qy : qz);
-            // the leaf's side of the plane: right child of its depth-d ancestor
+            // the leaf's side: right child of its depth-d ancestor (the
+            // sibling's points then lie at or below its face, else at or above)
             const bool right = ((leaf >> k) & 1u) != 0u;
-            const float gap = right ? qa - split : split - qa;
+            const float gap = right ? qa - face : face - qa;
             const float lb = gap > 0.0f ? gap * gap : 0.0f;
             lbs[d * kWG] = lb;
             pend |= enters(lb, best) ? (1u << d) : 0u;
