@@ -448,6 +448,45 @@ def test_warm_start_ties_and_gaps(torch, kdnn):
             np.testing.assert_array_equal(gi["t"], t)
 
 
+@pytest.mark.parametrize("leaf", [1, 3, 16])
+def test_warm_start_adversarial(torch, kdnn, leaf):
+    """Warm-started iterations on the adversarial clouds (exact ties on grids,
+    heavy duplication, coplanar and collinear targets, tight clusters with far
+    queries, trees with empty leaves): the host loop, whose iterations after
+    the first start at each point's previous leaf, must equal the loop of
+    separate calls bit for bit; a degenerate registration must fail the same
+    way in both."""
+    compared = 0
+    for name, T, Q in adversarial_clouds():
+        if len(Q) < 3:
+            continue
+        tree = kdnn.Tree(T, leaf)
+        sd = dev(torch, Q)
+        auto = bool(tree.info["auto_sort_icp"])
+        say("warm start adversarial", name, "leaf", leaf, len(T), len(Q))
+        status = []
+        try:
+            gi = tree.icp(sd, max_iter=5, R0=synth.rot_z(0.0), t0=[0.0, 0.0, 0.0])
+            status.append(None)
+        except kdnn.KdnnError as err:
+            status.append(err.status)
+        try:
+            R, t, E, hist = _step_by_step(kdnn, tree, sd, 5, auto)
+            status.append(None)
+        except kdnn.KdnnError as err:
+            status.append(err.status)
+        assert status[0] == status[1], (name, status)
+        if status[0] is not None:
+            continue
+        assert gi["iters"] == len(E), name
+        np.testing.assert_array_equal(gi["E"], E, err_msg=name)
+        np.testing.assert_array_equal(gi["Rt_hist"], hist, err_msg=name)
+        np.testing.assert_array_equal(gi["R"], R, err_msg=name)
+        np.testing.assert_array_equal(gi["t"], t, err_msg=name)
+        compared += 1
+    assert compared >= 5  # the grid, duplicate, planar, cluster and coarse sets at least
+
+
 def test_device_loop_eps_and_limits(torch, kdnn):
     """Convergence stop at every phase of the 4-iteration chunks, the host
     fallback beyond the record's 512 iterations, and a degenerate first
