@@ -573,10 +573,13 @@ constexpr uint32_t kNoOwner = 0xFFFFFFFFu;
 #ifndef KDNN_QLDS
 #define KDNN_QLDS 1  // query coordinates in LDS (wave_search QL) where the kernel allows
 #endif
-// Idle lanes that trigger a hand-over inside the internal-node phase: 16 when
+// Idle lanes that trigger a hand-over inside the internal-node phase: 8 when
 // a wave starts with many idle lanes (fewer than KDNN_P1_Q_SPLIT queries per
 // wave), 24 when it starts (nearly) full.  Measured: Scene ICP (33 per wave)
-// best at 16; the 131k LiDAR frame's fused kernel (43 per wave) 39.9 -> 38.2 us
+// with searches from the root best at 14-20; since the searches start at a
+// leaf (warm start, point location), 8: warm fused kernel 24.4 -> 23.5 us
+// (mean of three A/B pairs; 16, 12, 4 and 24+ measured too), nn_query 26.1 ->
+// 25.4 us.  The 131k LiDAR frame's fused kernel (43 per wave) 39.9 -> 38.2 us
 // at 24, Skewed 500k (64 per wave) -2.5%, uniform Stress 1M -1.5%.
 #ifndef KDNN_P1_MIN_IDLE_FULL
 #define KDNN_P1_MIN_IDLE_FULL 24
@@ -585,7 +588,7 @@ constexpr uint32_t kNoOwner = 0xFFFFFFFFu;
 #define KDNN_P1_Q_SPLIT 40
 #endif
 #ifndef KDNN_P1_MIN_IDLE
-#define KDNN_P1_MIN_IDLE 16
+#define KDNN_P1_MIN_IDLE 8
 #endif
 
 // Position of the r-th (0-based) set bit of m (m has more than r set bits).
