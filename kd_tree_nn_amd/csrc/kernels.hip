@@ -729,9 +729,6 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
 // 148 us, Skewed 500k leaf 16 168 -> 157 us; the first ICP iteration's fused
 // kernel, Scene 33.3 -> 30.4 us, the 131k LiDAR frames ~47 -> ~39 us.
 // STATS: each plane read counts as one node record (traced kLocateVisit | i).
-#ifndef KDNN_COLD_LOCATE
-#define KDNN_COLD_LOCATE 1
-#endif
 template <bool STATS>
 __device__ __forceinline__ uint32_t locate_leaf(const TreeView &t, float qx, float qy, float qz,
                                                 WaveTask &w, uint32_t *trow, uint32_t tcap)
@@ -923,8 +920,9 @@ __device__ __forceinline__ float *lbs_array()
 // trow / tcap / tcnt (STATS only, each lane its own query's): the row its
 // visits are recorded in (trace_visit), its capacity, and where the number of
 // visits goes (null: none recorded).
-// hint (this lane's own query; 0: none): a leaf to start from instead of the
-// root (warm_start).
+// hint (this lane's own query; 0: none): the leaf to start from (warm_start);
+// without one the search starts at the leaf whose cell holds the query
+// (locate_leaf).
 template <bool STATS, bool BALANCE = true, int CH = kLeafChunk, bool QL = false>
 __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float oqx, float oqy,
                                             float oqz, uint64_t init, float *lbs,
@@ -954,20 +952,11 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
     w.cn = 0u;
     w.cp = 0u;
     w.nt = 0u;
-    const bool searched = own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz);
-    uint32_t start = searched ? hint : 0u;
-    if (KDNN_COLD_LOCATE && searched && start == 0u)
-        start = locate_leaf<STATS>(t, oqx, oqy, oqz, w, trow, tcap);
-    if (start != 0u) {
+    if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
+        // the start leaf: the hint, else the query's own leaf
+        const uint32_t start =
+            hint != 0u ? hint : locate_leaf<STATS>(t, oqx, oqy, oqz, w, trow, tcap);
         warm_start<STATS, CH>(t, start, oqx, oqy, oqz, lbs, w, trow, tcap, &okey[threadIdx.x]);
-    } else if (searched) {
-        const float4 A = t.nodes[2];
-        const float4 B = t.nodes[3];
-        if constexpr (STATS) {
-            ++w.cn;
-            trace_visit(w, trow, tcap, 0u);
-        }
-        w.i = enters(box_lb(oqx, oqy, oqz, A, B), key_dist(w.key)) ? 1u : kDone;
     }
     for (;;) {
         // Phase 1: internal nodes, as in the single-lane pair search; lanes
