@@ -183,7 +183,7 @@ def summarize_trace(trace_dir, only, out_name):
             out += ["", f"# icp_fused_kernel inside {len(it0)} ICP registrations of {ITERS} "
                         "iterations (runs of fused launches with only their reductions or "
                         "step kernels between them):",
-                    f"iteration 0 (from the root): {len(it0)} launches, avg "
+                    f"iteration 0 (no start leaf: point location): {len(it0)} launches, avg "
                     f"{sum(it0) / len(it0):.2f} us",
                     f"iterations 1..{ITERS - 1} (warm start): {len(warm)} launches, avg "
                     f"{sum(warm) / len(warm):.2f} us, median {sorted(warm)[len(warm) // 2]:.2f} us"]
@@ -579,9 +579,9 @@ def bench_scene(g, args, result):
     solve_us = (time.perf_counter() - t0) / 500 * 1e6
 
     # the fused kernel as the ICP loop runs it: the library's event pairs around
-    # every fused launch of `kernel_reps` registrations.  Iteration 0 searches
-    # from the root; iterations 1..29 start at the leaf of each point's
-    # previous match (warm start).
+    # every fused launch of `kernel_reps` registrations.  Iteration 0 starts
+    # each search at the leaf holding its query (point location); iterations
+    # 1..29 start at the leaf of each point's previous match (warm start).
     kdnn.timing_begin(ITERS * args.kernel_reps)
     for _ in range(args.kernel_reps):
         tree.icp(src, max_iter=ITERS, workspace=ws)
@@ -595,8 +595,8 @@ def bench_scene(g, args, result):
     # the instrumented single-lane search of each iteration's queries in the
     # fused kernel's launch shape: warm-started from the previous iteration's
     # queries (iterations 1..29; node records then include two for the start
-    # leaf's 64-byte plane record), and from the root (all 30, the cold entry
-    # point above)
+    # leaf's 64-byte plane record), and with no start leaf (all 30, the cold
+    # entry point above: point location, then the walk)
     qs = [kdnn.transform(src, R, t) for R, t in Rts]
     wcnt, wrep, ccnt, crep = [], [], [], []
     for k in range(ITERS):
@@ -621,7 +621,7 @@ def bench_scene(g, args, result):
                               "the previous iteration; bytes and launch of the last")
     cold = search_roofline(n, float(np.mean([c[0] for c in ccnt])),
                            float(np.mean([c[1] for c in ccnt])), 4 + 12 + 12 + 12, kern_s, ceil,
-                           level, "fused correspondence kernel, searches from the root",
+                           level, "fused correspondence kernel, no start leaf (point location, then the walk)",
                            float(np.mean(crep)), rinfo_c)
     traffic, traffic_src = committed_traffic()
     roof.update({
@@ -718,7 +718,7 @@ def bench_scene(g, args, result):
                              "queries_per_s": round(n / kern_s),
                              "call_mean_us": round(float(call_ms.mean()) * 1e3, 2),
                              "note": "icp_correspond_reduce_async at the 30 iterations' "
-                                     "transforms: searches from the root"},
+                                     "transforms: no start leaf (point location, then the walk)"},
                          "timing": "event pair stamped by the search kernel's dispatch "
                                    "(library timing facility, hipExtLaunchKernel)"},
         "icp_iteration_breakdown_us": {
