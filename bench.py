@@ -257,8 +257,9 @@ def summarize(fetch_dir, write_dir):
             f"traffic_bytes_per_launch={traffic:.0f}",
             f"kernels_hip_sha256_16={kernel_source_hash()}",
             "",
-            "# context: the cold entry point (icp_correspond_reduce_async, searches from the "
-            f"root): fetch {cold['FETCH_SIZE']:.0f}, write {cold['WRITE_SIZE']:.0f} bytes per launch"]
+            "# context: the cold entry point (icp_correspond_reduce_async, no start leaf: point "
+            f"location, then the walk): fetch {cold['FETCH_SIZE']:.0f}, write "
+            f"{cold['WRITE_SIZE']:.0f} bytes per launch"]
     with open(TRAFFIC_SUMMARY, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
