@@ -60,6 +60,9 @@ def _case(name):
     if name == "scene_leaf16":
         p = synth.scene()
         return p.target, p.source, 16
+    if name == "uniform_leaf1_deep":  # depth 15: one level above the plane record
+        tgt, q = _uniform(9, 20_000, 4_000)
+        return tgt, q, 1
     raise KeyError(name)
 
 
@@ -68,6 +71,7 @@ def _case(name):
     ("uniform_ragged_leaf16", False, False), ("uniform_ragged_leaf16", False, True),
     ("uniform_ragged_leaf16", True, None),
     ("scene_leaf16", True, False), ("scene_leaf16", True, True), ("scene_leaf16", False, None),
+    ("uniform_leaf1_deep", False, None), ("uniform_leaf1_deep", True, None),
 ])
 def test_replay_tallies_match_instrumented_counts(torch, kdnn, name, icp, sort):
     tgt, q, leaf = _case(name)
