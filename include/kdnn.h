@@ -179,7 +179,10 @@ kdnn_status kdtree_build_host(const float *xyz_host, int64_t n, const kdnn_build
  * tree's node records and points take more than 4 times the device's L2
  * cache (kdnn_tree_info.auto_sort).  The ordering costs a sort on every
  * call, and the search gains L2 locality from it only for trees well beyond
- * the L2.  Results never depend on the order. */
+ * the L2.  The ordering key is the top 8 bits of the queries' 30-bit Morton
+ * code in the tree's bounding box (one radix pass; the ICP entry points,
+ * which sort once per registration, take 16).  Results never depend on the
+ * order. */
 
 /* Search schedule (nn_query, nn_query_stats and the ICP entry points).
  * Default: one lane owns each query, and the 64 lanes of a wavefront share

@@ -547,8 +547,9 @@ kdnn_status kdnn_replay_bench(const kdnn_tree *tree, const float *q_dev, const f
     const QueryWorkspace qw = carve_query_workspace(ws_dev, m);
     const int32_t *perm = nullptr;
     hipError_t e = hipSuccess;
-    if (sort && (e = launch_morton_order(tree->dev, q_dev, m, nullptr, qw.sort, &perm, stream)) !=
-                    hipSuccess)
+    if (sort && (e = launch_morton_order(tree->dev, q_dev, m, nullptr,
+                                         icp ? kKeyBitsIcp : kKeyBitsQuery, qw.sort, &perm,
+                                         stream)) != hipSuccess)
         return hip_fail(e, "kdnn_replay_bench: order launch");
     void *rws = static_cast<char *>(ws_dev) + ((query_ws_bytes(m) + 255) & ~size_t(255));
     *info = kdnn_replay_info{};
@@ -791,7 +792,7 @@ static kdnn_status nn_query_impl(const kdnn_tree *tree, const float *q, int64_t 
         const QueryWorkspace w = carve_query_workspace(ws, m);
         twopass = w.twopass;
         if (sort) {
-            hipError_t e = launch_morton_order(tree->dev, q, m, nullptr, w.sort, &perm, s);
+            hipError_t e = launch_morton_order(tree->dev, q, m, nullptr, kKeyBitsQuery, w.sort, &perm, s);
             if (e != hipSuccess) return hip_fail(e, "nn_query: order launch");
         }
     }

@@ -34,6 +34,11 @@ constexpr int kMaxDepth = 28;
 // each one's child off the leaf's path (at or beyond the split).
 constexpr int kPathLevels = 14;
 constexpr int kPathWords = 16;
+// Morton prefix (of the 30-bit code) that orders the queries: nn_query pays
+// the sort on every call and takes one 8-bit radix pass; the ICP entry points
+// sort once per registration for 30 searches and take two.
+constexpr int kKeyBitsQuery = 8;
+constexpr int kKeyBitsIcp = 16;
 constexpr int kMaxLeafSize = 1024;
 
 struct HostTree {
@@ -164,10 +169,12 @@ IcpWorkspace carve_icp_workspace(void *ws, int64_t n);
 hipError_t noalloc_scratch(int device, void **ptr, std::mutex **call_mu);
 
 // Kernel launchers (return the hipError_t of the launch).
-// Morton-order the points moved by (R, t) (R == nullptr: not moved): on
-// return *perm points at the int32 permutation (traversal slot -> point).
+// Morton-order the points moved by (R, t) (R == nullptr: not moved) by the
+// top key_bits (8 or 16) bits of their code: on return *perm points at the
+// int32 permutation (traversal slot -> point).
 hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
-                               const SortWorkspace &ws, const int32_t **perm, hipStream_t s);
+                               int key_bits, const SortWorkspace &ws, const int32_t **perm,
+                               hipStream_t s);
 // Same, for the ICP entry points (sort buffers carved from the ICP workspace).
 hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                             const IcpWorkspace &ws, const int32_t **perm, hipStream_t s);

@@ -42,7 +42,6 @@ constexpr int kLeafChunkSmall = 8;                // the same for trees whose le
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
 constexpr int kSortTile = kSortThreads * kSortItems;  // keys per radix tile
-constexpr int kKeyBits = 16;                      // Morton prefix used for ordering
 constexpr int kIcpMaxBlocks = 4096;
 constexpr int kNumXcd = 8;
 constexpr int kS = KDNN_SUMS_DOUBLES;
@@ -2244,17 +2243,21 @@ __global__ __launch_bounds__(256) void transform_kernel(const float *in, float *
 
 // ------------------------------------------------------- Morton ordering
 //
-// Queries are ordered by the top kKeyBits bits of their 30-bit Morton code
-// in the target's bounding box (10 bits per axis, clamped), so that the 64
-// lanes of a wave start from neighbouring points and walk mostly the same
-// branches.  Stable LSD radix sort, two 8-bit passes; the permutation is a
-// deterministic function of the input.
+// Queries are ordered by the top key_bits bits of their 30-bit Morton code
+// in the target's bounding box (10 bits per axis, clamped), so that each
+// XCD's segment of the order is one region of space (its L2 holds that part
+// of the tree).  Stable LSD radix sort, one 8-bit pass per 8 key bits; the
+// permutation is a deterministic function of the input.  nn_query takes 8
+// bits (one pass: Stress 1M leaf 8 / 16 call 186 / 193 -> 175 / 187 us; the
+// search is 9-11% slower on the coarser order, the sort half as long), the
+// ICP entry points 16 (two passes, paid once for 30 searches).
 
 struct OrderArgs {
     const float *pts;
     int64_t m;
     float R[12];  // row-major R then t; used when moved != 0
     int32_t moved;
+    int32_t key_shift;  // 30 - key bits
     float lo[3];
     float inv[3];
 };
@@ -2291,7 +2294,7 @@ __device__ __forceinline__ uint32_t order_key(const OrderArgs &a, int64_t i)
     const uint32_t code = (spread10(quant10(x, a.lo[0], a.inv[0])) << 2) |
                           (spread10(quant10(y, a.lo[1], a.inv[1])) << 1) |
                           spread10(quant10(z, a.lo[2], a.inv[2]));
-    return code >> (30 - kKeyBits);
+    return code >> a.key_shift;
 }
 
 template <bool FROM_POINTS>
@@ -2562,12 +2565,14 @@ static TreeView tree_view(const DeviceTree &t)
     return v;
 }
 
-static OrderArgs make_order_args(const DeviceTree &t, const float *pts, int64_t m, const float *R12)
+static OrderArgs make_order_args(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
+                                 int key_bits)
 {
     OrderArgs oa{};
     oa.pts = pts;
     oa.m = m;
     oa.moved = R12 ? 1 : 0;
+    oa.key_shift = 30 - key_bits;
     for (int k = 0; k < 12; ++k) oa.R[k] = R12 ? R12[k] : 0.0f;
     for (int k = 0; k < 3; ++k) {
         oa.lo[k] = t.box_lo[k];
@@ -2577,13 +2582,19 @@ static OrderArgs make_order_args(const DeviceTree &t, const float *pts, int64_t 
 }
 
 static hipError_t morton_order_impl(const DeviceTree &t, const float *pts, int64_t m,
-                                    const float *R12, const SortWorkspace &ws, uint32_t *zero_me,
-                                    const int32_t **perm, hipStream_t s)
+                                    const float *R12, int key_bits, const SortWorkspace &ws,
+                                    uint32_t *zero_me, const int32_t **perm, hipStream_t s)
 {
-    const OrderArgs oa = make_order_args(t, pts, m, R12);
+    const OrderArgs oa = make_order_args(t, pts, m, R12, key_bits);
     const int32_t nt = ws.ntiles;
     radix_hist_kernel<true><<<nt, kSortThreads, 0, s>>>(oa, nullptr, 0, ws.hist, nt);
     radix_scan_kernel<<<256, kSortThreads, 0, s>>>(ws.hist, nt, ws.totals, zero_me);
+    if (key_bits <= 8) {  // one pass: the permutation straight out of it
+        radix_scatter_kernel<true, false><<<nt, kSortThreads, 0, s>>>(
+            oa, nullptr, nullptr, 0, ws.hist, ws.totals, nt, nullptr, ws.vals_a);
+        *perm = ws.vals_a;
+        return hipGetLastError();
+    }
     radix_scatter_kernel<true, true><<<nt, kSortThreads, 0, s>>>(
         oa, nullptr, nullptr, 0, ws.hist, ws.totals, nt, ws.keys_b, ws.vals_b);
     radix_hist_kernel<false><<<nt, kSortThreads, 0, s>>>(oa, ws.keys_b, 8, ws.hist, nt);
@@ -2617,15 +2628,16 @@ hipError_t launch_scan_row(uint32_t *row, int32_t len, uint32_t *total, hipStrea
 }
 
 hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
-                               const SortWorkspace &ws, const int32_t **perm, hipStream_t s)
+                               int key_bits, const SortWorkspace &ws, const int32_t **perm,
+                               hipStream_t s)
 {
-    return morton_order_impl(t, pts, m, R12, ws, nullptr, perm, s);
+    return morton_order_impl(t, pts, m, R12, key_bits, ws, nullptr, perm, s);
 }
 
 hipError_t launch_icp_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                             const IcpWorkspace &ws, const int32_t **perm, hipStream_t s)
 {
-    return morton_order_impl(t, pts, m, R12, ws.sort, nullptr, perm, s);
+    return morton_order_impl(t, pts, m, R12, kKeyBitsIcp, ws.sort, nullptr, perm, s);
 }
 
 // Dynamic LDS of the balanced search kernels: the pending bound of every path
