@@ -1098,43 +1098,18 @@ kdnn_status voxel_downsample(const float *xyz_dev, int64_t n, double leaf, float
         return fail(KDNN_EINVAL, "voxel_downsample: misaligned counts");
     if ((st = check_ws(ws_dev, ws_bytes, voxel_ws_bytes(n))) != KDNN_OK) return st;
     const VoxelWorkspace w = carve_voxel_workspace(ws_dev, n);
-    hipError_t e = launch_voxel_bbox(xyz_dev, n, w, stream);
+    hipError_t e = launch_voxel_filter(xyz_dev, n, leaf, w, out_dev, counts_dev, stream);
     if (e != hipSuccess) return hip_fail(e, "voxel_downsample: launch");
-    float bb[7];
-    if ((e = hipMemcpyAsync(bb, w.bbox, sizeof bb, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
-        (e = hipStreamSynchronize(stream)) != hipSuccess)
-        return hip_fail(e, "voxel_downsample: bbox readback");
-    uint32_t n_finite;
-    std::memcpy(&n_finite, &bb[6], 4);
-    if (n_finite == 0) return KDNN_OK;
-    // the grid spanned by the occupied voxels: floor and the division by a
-    // positive leaf are monotone, so its corners are the voxels of min / max
-    int64_t vmin[3];
-    uint32_t dims[3];
-    double cells = 1.0;
-    for (int a = 0; a < 3; ++a) {
-        const double lo = std::floor(double(bb[a]) / leaf), hi = std::floor(double(bb[3 + a]) / leaf);
-        if (!(std::fabs(lo) < 4.0e18 && std::fabs(hi) < 4.0e18))
-            return fail(KDNN_EINVAL, "voxel_downsample: leaf too small for the coordinates");
-        const double d = hi - lo + 1.0;
-        cells *= d;
-        if (!(cells < 4294967295.0))
-            return fail(KDNN_EINVAL, "voxel_downsample: the voxel grid over the cloud's extent "
-                                     "needs 2^32 cells or more (leaf too small)");
-        vmin[a] = int64_t(lo);
-        dims[a] = uint32_t(d);
-    }
-    const uint32_t sentinel = uint32_t(cells);  // one past the last key
-    int bits = 0;
-    while (bits < 32 && (uint64_t(sentinel) >> bits) != 0) ++bits;
-    const int passes = (bits + 7) / 8;
-    e = launch_voxel_filter(xyz_dev, n, leaf, vmin, dims, sentinel, passes, int64_t(n_finite), w,
-                            out_dev, counts_dev, stream);
-    if (e != hipSuccess) return hip_fail(e, "voxel_downsample: launch");
-    uint32_t m = 0;
-    if ((e = hipMemcpyAsync(&m, w.nvox, 4, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+    VoxGrid g{};
+    if ((e = hipMemcpyAsync(&g, w.grid, sizeof g, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
         (e = hipStreamSynchronize(stream)) != hipSuccess)
         return hip_fail(e, "voxel_downsample: synchronize");
+    if (g.err == kVoxErrRange)
+        return fail(KDNN_EINVAL, "voxel_downsample: leaf too small for the coordinates");
+    if (g.err == kVoxErrCells)
+        return fail(KDNN_EINVAL, "voxel_downsample: the voxel grid over the cloud's extent "
+                                 "needs 2^32 cells or more (leaf too small)");
+    const uint32_t m = g.n_finite == 0 ? 0u : g.nvox;
     *m_out = int64_t(m);
     return KDNN_OK;
     KDNN_GUARD_END

@@ -214,36 +214,40 @@ hipError_t launch_icp_fused(const DeviceTree &t, const float *src, int64_t n, co
 // output record's transform <- (R0, t0), no iterations, no failure.
 hipError_t launch_icp_loop_init(IcpLoopState *state, IcpLoopOut *out, const double *R0,
                                 const double *t0, hipStream_t s);
-// One stable LSD radix pass (8-bit digit at `shift`) of (key, value) pairs;
-// hist: 256 x radix_tiles(m) words, totals: 256 words.
-int32_t radix_tiles(int64_t m);
-hipError_t launch_radix_pass(const uint32_t *keys_in, const int32_t *vals_in, int shift,
-                             uint32_t *keys_out, int32_t *vals_out, int64_t m, uint32_t *hist,
-                             uint32_t *totals, hipStream_t s);
-// In-place exclusive scan of row[0..len); *total = the sum.  One work-group.
-hipError_t launch_scan_row(uint32_t *row, int32_t len, uint32_t *total, hipStream_t s);
-
 // Voxel-grid filter (voxel.hip).
+// The key grid of one call, computed on the device from the cloud's bounding
+// box: voxel v = floor(p / leaf) - vmin, key = vx + dims[0] (vy + dims[1] vz);
+// non-finite points take `sentinel` (the dims product, one past the last key).
+struct VoxGrid {
+    int64_t vmin[3];
+    uint32_t dims[3];
+    uint32_t sentinel;
+    uint32_t n_finite;  // finite points
+    int32_t passes;     // radix passes the keys need; 0: nothing to sort
+    int32_t err;        // kVoxOk, kVoxErrRange or kVoxErrCells
+    uint32_t nvox;      // voxels: the sum of the segment heads
+    uint32_t nbig;      // voxels summed by a whole wave (their list: vals_a)
+};
+constexpr int32_t kVoxOk = 0;
+constexpr int32_t kVoxErrRange = 1;  // |floor(p / leaf)| >= 4e18 for a bounding-box corner
+constexpr int32_t kVoxErrCells = 2;  // the grid over the extent needs 2^32 cells or more
 struct VoxelWorkspace {
     uint32_t *keys_a, *keys_b;
     int32_t *vals_a, *vals_b;
-    uint32_t *hist, *totals;
-    uint32_t *tile_heads;   // [tiles]
-    int32_t *starts;        // [n] first sorted position of each voxel
-    float *bbox_part;       // [7][kVoxBlocks]: min xyz, max xyz, finite count
-    float *bbox;            // [8]: min xyz, max xyz, finite count (as float bits), pad
-    uint32_t *nvox;         // [1]
-    float *sorted;          // [n][3] the finite points' coordinates in sorted order
+    uint32_t *hist, *totals;  // [digits][tiles] tile counts, [digits] digit totals
+    uint32_t *tile_heads;     // [tiles]
+    int32_t *starts;          // [n] first sorted position of each voxel
+    uint32_t *bbox_part;      // [7][blocks]: min xyz, max xyz (fp32 bits), finite count
+    VoxGrid *grid;
+    float4 *sorted;           // [n] the points' coordinates (x, y, z, 0) in sorted order
 };
 size_t voxel_ws_bytes(int64_t n);
 VoxelWorkspace carve_voxel_workspace(void *ws, int64_t n);
-hipError_t launch_voxel_bbox(const float *xyz, int64_t n, const VoxelWorkspace &w, hipStream_t s);
-// key grid: voxel v = floor(p / leaf) - vmin, key = vx + dims[0] (vy + dims[1] vz);
-// non-finite points get key `sentinel` (= dims product); passes = radix passes.
-hipError_t launch_voxel_filter(const float *xyz, int64_t n, double leaf, const int64_t *vmin,
-                               const uint32_t *dims, uint32_t sentinel, int passes,
-                               int64_t n_finite, const VoxelWorkspace &w, float *out,
-                               int32_t *counts, hipStream_t s);
+// Every launch of the filter, none waiting on the host.  When the stream
+// gets past them, *w.grid holds the grid, its error code and the voxel count,
+// and out / counts their first nvox rows (none when err != kVoxOk).
+hipError_t launch_voxel_filter(const float *xyz, int64_t n, double leaf, const VoxelWorkspace &w,
+                               float *out, int32_t *counts, hipStream_t s);
 
 // Batched correspondence steps: up to batch_max_pairs() (tree, source) pairs
 // per launch, one pair per group of XCDs.  ws: icp_batch_ws_bytes layout

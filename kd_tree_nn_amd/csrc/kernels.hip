@@ -2605,28 +2605,6 @@ static hipError_t morton_order_impl(const DeviceTree &t, const float *pts, int64
     return hipGetLastError();
 }
 
-int32_t radix_tiles(int64_t m) { return sort_tiles(m); }
-
-hipError_t launch_radix_pass(const uint32_t *keys_in, const int32_t *vals_in, int shift,
-                             uint32_t *keys_out, int32_t *vals_out, int64_t m, uint32_t *hist,
-                             uint32_t *totals, hipStream_t s)
-{
-    OrderArgs oa{};
-    oa.m = m;
-    const int32_t nt = sort_tiles(m);
-    radix_hist_kernel<false><<<nt, kSortThreads, 0, s>>>(oa, keys_in, shift, hist, nt);
-    radix_scan_kernel<<<256, kSortThreads, 0, s>>>(hist, nt, totals, nullptr);
-    radix_scatter_kernel<false, true><<<nt, kSortThreads, 0, s>>>(
-        oa, keys_in, vals_in, shift, hist, totals, nt, keys_out, vals_out);
-    return hipGetLastError();
-}
-
-hipError_t launch_scan_row(uint32_t *row, int32_t len, uint32_t *total, hipStream_t s)
-{
-    radix_scan_kernel<<<1, kSortThreads, 0, s>>>(row, len, total, nullptr);
-    return hipGetLastError();
-}
-
 hipError_t launch_morton_order(const DeviceTree &t, const float *pts, int64_t m, const float *R12,
                                int key_bits, const SortWorkspace &ws, const int32_t **perm,
                                hipStream_t s)

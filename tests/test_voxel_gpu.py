@@ -67,3 +67,39 @@ def test_idempotent_on_gpu(torch, kdnn):
     c2, n2 = kdnn.voxel_downsample(c.contiguous(), 0.3, return_counts=True)
     assert torch.equal(c.view(torch.int32), c2.view(torch.int32))
     assert bool((n2 == 1).all())
+
+
+def test_large_voxels(torch, kdnn):
+    """Voxels of more points than one lane sums (a wave sums them, in windows
+    of 256 points): 8 LiDAR frames at 0.5 m and 1 m (up to ~1,800 and ~6,100
+    points per voxel), and voxels of 64, 65, 255-257, 513 and 5,000 points."""
+    P = np.concatenate([p.source for p in lidar()[:8]]).astype(np.float32)
+    for leaf in (0.5, 1.0):
+        c = check_voxels(kdnn, torch, P, leaf, f"8 lidar frames, leaf {leaf}")
+        assert len(c) > 0
+    rng = np.random.Generator(np.random.PCG64(11))
+    sizes = [64, 65, 255, 256, 257, 513, 5000]
+    parts = [rng.uniform(0.05, 0.95, (m, 3)) + [4.0 * k, 0.0, 0.0] for k, m in enumerate(sizes)]
+    parts.append(rng.uniform(-60.0, 60.0, (30_000, 3)))
+    Q = np.concatenate(parts).astype(np.float32)
+    Q = Q[rng.permutation(len(Q))]
+    _, en = oracle.voxel_downsample(Q, 1.0)
+    assert set(sizes) <= set(en.tolist())
+    check_voxels(kdnn, torch, Q, 1.0, "voxels at the one-lane and window limits")
+
+
+def test_errors_then_a_good_call(torch, kdnn):
+    """The grid's range checks run on the device: each error is reported after
+    the call, and the next call on the same workspace is unaffected."""
+    P = np.array([[0.5, 0.5, 0.5], [0.25, 0.75, 0.5], [1.0, 0.0, 0.0], [-0.5, 0.0, 0.0]],
+                 np.float32)
+    ec, en = oracle.voxel_downsample(P, 1.0)
+    ws = torch.empty(int(kdnn._lib.lib().voxel_downsample_workspace_bytes(len(P))),
+                     dtype=torch.uint8, device="cuda")
+    for bad, leaf, what in [([[1e30, 0, 0], [0, 0, 0]], 1e-10, "too small for the coordinates"),
+                            ([[0, 0, 0], [100, 100, 100]], 1e-4, "2\\^32 cells")]:
+        with pytest.raises(kdnn.KdnnError, match=what):
+            kdnn.voxel_downsample(dev(torch, bad), leaf, workspace=ws)
+        c, n = kdnn.voxel_downsample(dev(torch, P), 1.0, return_counts=True, workspace=ws)
+        assert np.array_equal(c.cpu().numpy().view(np.uint32), ec.view(np.uint32))
+        assert np.array_equal(n.cpu().numpy(), en)
