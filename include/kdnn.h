@@ -213,7 +213,8 @@ size_t nn_query_workspace_bytes(int64_t m);
  * backtracking and split-plane pruning; §3.2 one query per GPU lane;
  * §5.3 queries Morton-ordered so that neighbouring lanes walk the same
  * branches).  Each search first locates the leaf whose cell holds its query
- * by the ancestors' split planes, scans it, and then visits the rest of the
+ * by the ancestors' split planes (the top 8 levels' from a copy each
+ * work-group keeps in LDS), scans it, and then visits the rest of the
  * tree as far as the best distance requires: the subtrees beside that leaf's
  * path are bounded along their parents' split axes (the leaf's plane record), nodes
  * below them by their boxes.
@@ -244,7 +245,9 @@ kdnn_status nn_query_radius(const kdnn_tree *tree, const float *q_dev, int64_t m
 
 /* Instrumented nn_query: same results, and per query the number of tree node
  * records loaded and of leaf points scanned (uint32 each, may be NULL).  Node
- * records: one per split plane read by the point location (D), two for the
+ * records: one per split plane the point location reads from memory (D - 8
+ * when D > 8: the top 8 levels' planes come from the work-group's LDS copy
+ * and count none), two for the
  * start leaf's 64-byte plane record, one per sibling box above that record's
  * 14 levels (D - 14 when D > 14), two per child-pair run.  With
  * the default schedule the counts are those of the exact single-lane search
@@ -562,7 +565,8 @@ kdnn_status kdnn_chase_bench(const uint32_t *next_dev, int64_t n_records, int32_
  * the memory system's own limit for that access stream.
  *   1. The instrumented single-lane search (the one nn_query_stats counts)
  *      records each query's visits: the split plane of each node on its
- *      point location's path (8 B), its start leaf's plane record (64 B),
+ *      point location's path below the top 8 levels (8 B; those come from
+ *      LDS), its start leaf's plane record (64 B),
  *      each internal node's run of child boxes (48 B), each leaf (its points,
  *      loaded in chunks as the search loads them); at most KDNN_REPLAY_CAP
  *      per query.

@@ -36,6 +36,9 @@ constexpr int kWG = KDNN_WG;                      // traversal work-group size
 #ifndef KDNN_Q_TARGET_ICP
 #define KDNN_Q_TARGET_ICP 43
 #endif
+#ifndef KDNN_TOP_LOC_LEVELS
+#define KDNN_TOP_LOC_LEVELS 8
+#endif
 constexpr uint32_t kQFull = 64;
 constexpr int kLeafChunk = 16;                    // leaf points loaded per batch (one lane)
 constexpr int kLeafChunkSmall = 8;                // the same for trees whose leaves hold <= 8
@@ -718,8 +721,9 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
 
 // Point location: the leaf whose cell holds the query, found by the split
 // planes of its ancestors (node i's split value and axis, the last 8 bytes of
-// its 32-byte record), one dependent 8-byte load per level -- the top levels
-// shared by the wave's lanes and cached.  A search without a start leaf of
+// its 32-byte record), one dependent 8-byte load per level -- the levels
+// below the LDS copy (next) shared by the wave's lanes and cached.  A search
+// without a start leaf of
 // its own (the first ICP iteration, nn_query) starts there as a warm start
 // would (below): the same exact answer as a descent from the root, whose
 // child-pair runs (three 16-byte loads per level, each lane's own lines below
@@ -727,13 +731,42 @@ __device__ __forceinline__ void task_handover(WaveTask &w, const float *lbs,
 // kernels, MI355X): nn_query Scene 30.2 -> 26.5 us, Stress 1M leaf 8 213 ->
 // 148 us, Skewed 500k leaf 16 168 -> 157 us; the first ICP iteration's fused
 // kernel, Scene 33.3 -> 30.4 us, the 131k LiDAR frames ~47 -> ~39 us.
-// STATS: each plane read counts as one node record (traced kLocateVisit | i).
+// The planes of the top KDNN_TOP_LOC_LEVELS levels are read from a copy each
+// work-group keeps in LDS (top; null: none), staged once per launch
+// (stage_top_planes): every lane's first dependent loads become LDS reads
+// (Scene nn_query search 26.3 -> 25.5 us, Stress 1M leaf 8 156 -> 152 us,
+// Skewed 500k leaf 16 156 -> 154 us; 10 levels: no better).
+// STATS: each plane read from memory counts as one node record (traced
+// kLocateVisit | i); the LDS reads are not memory records.
+constexpr uint32_t kTopLocEnd = 1u << KDNN_TOP_LOC_LEVELS;  // nodes [1, kTopLocEnd)
+
+// A work-group's copy of the top levels' (split, axis) pairs, entry i for
+// node i (entry 0 unused); all threads call it together.
+__device__ __forceinline__ void stage_top_planes(const TreeView &t, float2 *top)
+{
+    const float2 *const sa = reinterpret_cast<const float2 *>(t.nodes) + 3;
+    const uint32_t lim = t.first_leaf < kTopLocEnd ? t.first_leaf : kTopLocEnd;
+    for (uint32_t j = threadIdx.x; j < lim; j += kWG)
+        if (j >= 1u) top[j] = sa[4 * size_t(j)];
+    __syncthreads();
+}
+
 template <bool STATS>
 __device__ __forceinline__ uint32_t locate_leaf(const TreeView &t, float qx, float qy, float qz,
-                                                WaveTask &w, uint32_t *trow, uint32_t tcap)
+                                                WaveTask &w, uint32_t *trow, uint32_t tcap,
+                                                const float2 *top = nullptr)
 {
     const float2 *const sa = reinterpret_cast<const float2 *>(t.nodes) + 3;
     uint32_t i = 1u;
+    if (top) {
+        const uint32_t lim = t.first_leaf < kTopLocEnd ? t.first_leaf : kTopLocEnd;
+        while (i < lim) {
+            const float2 S = top[i];
+            const uint32_t ax = __float_as_uint(S.y);
+            const float qa = ax == 0u ? qx : (ax == 1u ? qy : qz);
+            i = 2u * i + (qa > S.x ? 1u : 0u);
+        }
+    }
     while (i < t.first_leaf) {
         const float2 S = sa[4 * size_t(i)];
         if constexpr (STATS) {
@@ -929,7 +962,8 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
                                             uint32_t *ocp, uint32_t *xfer, uint32_t quorum = 64u,
                                             float4 *qpool = nullptr, uint32_t wq = 64u,
                                             uint32_t *trow = nullptr, uint32_t tcap = 0u,
-                                            uint32_t *tcnt = nullptr, uint32_t hint = 0u)
+                                            uint32_t *tcnt = nullptr, uint32_t hint = 0u,
+                                            const float2 *top = nullptr)
 {
     const uint32_t p1_idle = wq < KDNN_P1_Q_SPLIT ? KDNN_P1_MIN_IDLE : KDNN_P1_MIN_IDLE_FULL;
     const bool need_cand = KDNN_DONATE_GATE_Q > 0 && wq >= uint32_t(KDNN_DONATE_GATE_Q) &&
@@ -954,7 +988,7 @@ __device__ __forceinline__ void wave_search(const TreeView &t, bool own, float o
     if (own && isfinite(oqx) && isfinite(oqy) && isfinite(oqz)) {
         // the start leaf: the hint, else the query's own leaf
         const uint32_t start =
-            hint != 0u ? hint : locate_leaf<STATS>(t, oqx, oqy, oqz, w, trow, tcap);
+            hint != 0u ? hint : locate_leaf<STATS>(t, oqx, oqy, oqz, w, trow, tcap, top);
         warm_start<STATS, CH>(t, start, oqx, oqy, oqz, lbs, w, trow, tcap, &okey[threadIdx.x]);
     }
     for (;;) {
@@ -1103,6 +1137,11 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
         __shared__ uint32_t ocn[STATS ? kWG : 1], ocp[STATS ? kWG : 1];
         __shared__ uint32_t xfer[kWG];
         __shared__ float4 qpool[QL ? kWG : 1];
+        // the top planes for point location, in LDS (the instrumented kernel
+        // too: its counts and records are the memory loads of the search)
+        constexpr bool kTop = KDNN_TOP_LOC_LEVELS > 0;
+        __shared__ float2 top[kTop ? kTopLocEnd : 1];
+        if constexpr (kTop) stage_top_planes(a.tree, top);
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         const uint32_t wq = a.wq;
         const int64_t QB = int64_t(kWG / 64) * wq;
@@ -1124,7 +1163,8 @@ __global__ __launch_bounds__(kWG) void nn_kernel(NnArgs a)
                                                xfer + (threadIdx.x & ~63u),
                                                wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u, qpool,
                                                wq, tr ? a.trace + size_t(i) * a.tcap : nullptr,
-                                               a.tcap, tr ? a.tcount + i : nullptr, hint);
+                                               a.tcap, tr ? a.tcount + i : nullptr, hint,
+                                               kTop ? top : nullptr);
             if (own) {
                 Best b;
                 finish(okey[threadIdx.x], 0u, b);
@@ -1776,8 +1816,11 @@ icp_fused_kernel(IcpArgs a)
         __shared__ unsigned long long okey[kWG];
         __shared__ uint32_t xfer[kWG];
         __shared__ float4 qpool[KDNN_QLDS ? kWG : 1];
+        constexpr bool kTop = !WARM && KDNN_TOP_LOC_LEVELS > 0;  // searches all locate
+        __shared__ float2 top[kTop ? kTopLocEnd : 1];
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         if (a.stop && *a.stop) return;  // device loop already stopped (uniform)
+        if constexpr (kTop) stage_top_planes(a.tree, top);
         if (lane == 63) {
 #pragma unroll
             for (int c = 0; c < kS; ++c) red[wv * kS + c] = 0.0;
@@ -1804,7 +1847,8 @@ icp_fused_kernel(IcpArgs a)
                                                     lbs + threadIdx.x, okey, nullptr, nullptr,
                                                     xfer + (threadIdx.x & ~63u),
                                                     wq == kQFull ? KDNN_LEAF_QUORUM_FULL : 64u,
-                                                    qpool, wq, nullptr, 0u, nullptr, hint);
+                                                    qpool, wq, nullptr, 0u, nullptr, hint,
+                                                    kTop ? top : nullptr);
             double acc[kS];
 #pragma unroll
             for (int c = 0; c < kS; ++c) acc[c] = 0.0;

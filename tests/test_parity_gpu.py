@@ -197,7 +197,9 @@ def test_query_stats_consistent(torch, kdnn):
     for sched in SCHED:
         si, sd, cn, cp = tree.query_stats(q, **sched)
         assert torch.equal(idx, si) and torch.equal(d2.view(torch.int32), sd.view(torch.int32))
-        assert int(cn.min()) >= D + 1 and int(cp.min()) >= 1
+        # at least the location planes below the 8 levels kept in LDS and the
+        # start leaf's plane record (two records)
+        assert int(cn.min()) >= D - min(D, 8) + 2 and int(cp.min()) >= 1
         # a search never loads a node twice, except the greedy descent a second
         # pass repeats; a pruning search loads far fewer than all of them
         assert int(cn.max()) <= 2 ** (D + 1) + 2 * (D + 1)

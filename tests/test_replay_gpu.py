@@ -18,6 +18,10 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
+# point location reads the split planes of the top 8 levels from a work-group
+# copy in LDS: they are no memory records
+TOP_LOC_LEVELS = 8
+
 
 def say(*a):
     print("[gpu-case]", *a, file=sys.stderr, flush=True)
@@ -87,21 +91,23 @@ def test_replay_tallies_match_instrumented_counts(torch, kdnn, name, icp, sort):
     assert info["node_records"] == int(cn.sum())
     assert info["leaf_points"] == int(cp.sum())
     assert 1 <= info["queries_per_wave"] <= 64 and info["blocks"] >= 1
-    # visits of each searched query: the D split planes of its point location
-    # (8 B, one record each), its leaf's plane record (64 B, two records), the
-    # sibling boxes above the record's 14 levels (32 B, one record each), one
-    # box run per internal node entered (48 B, two records), one per leaf
-    # scanned (whole chunks)
+    # visits of each searched query: the split planes of its point location
+    # below the top TOP_LOC_LEVELS levels (8 B, one record each; the top ones
+    # come from LDS), its leaf's plane record (64 B, two records), the sibling
+    # boxes above the record's 14 levels (32 B, one record each), one box run
+    # per internal node entered (48 B, two records), one per leaf scanned
+    # (whole chunks)
     finite = int(np.isfinite(q).all(axis=1).sum())
     D = tree.info["depth"]
+    loc = D - min(D, TOP_LOC_LEVELS)
     top = max(0, D - 14)
-    pairs2 = int(cn.sum()) - finite * (D + 2 + top)
+    pairs2 = int(cn.sum()) - finite * (loc + 2 + top)
     assert pairs2 >= 0 and pairs2 % 2 == 0
     pairs = pairs2 // 2
-    leaves = info["visits"] - finite * (D + 1 + top) - pairs
+    leaves = info["visits"] - finite * (loc + 1 + top) - pairs
     assert leaves >= finite  # every searched query scans at least one leaf
     chunk = 8 if tree.info["max_leaf"] <= 8 else 16
-    assert info["bytes"] == finite * (8 * D + 64 + 32 * top) + 48 * pairs + 16 * chunk * leaves
+    assert info["bytes"] == finite * (8 * loc + 64 + 32 * top) + 48 * pairs + 16 * chunk * leaves
 
 
 def test_replay_truncates_long_rows(torch, kdnn):
