@@ -145,6 +145,33 @@ def test_ragged_query_counts(torch, kdnn, m):
             assert_nn_equal(idx, d2, oi, od, f"m={m} sort={sort} {sched}")
 
 
+@pytest.mark.parametrize("n", [1000, 2000, 4000, 8000])
+def test_depth_around_the_lds_planes(torch, kdnn, n):
+    """Point location reads the top 8 levels' planes from LDS and the rest
+    from memory: trees of depth 7-10 (all planes in LDS, exactly the LDS
+    levels, one and two levels below them), searches without a start leaf
+    (nn_query, the instrumented search, the fused correspondence kernel)."""
+    rng = np.random.Generator(np.random.PCG64(n))
+    T = rng.normal(size=(n, 3)).astype(np.float32)
+    Q = (rng.normal(size=(3001, 3)) * 1.1).astype(np.float32)
+    tree = kdnn.Tree(T, 8)
+    D = tree.info["depth"]
+    say("depth around the LDS planes", n, "depth", D)
+    assert D == {1000: 7, 2000: 8, 4000: 9, 8000: 10}[n]
+    oi, od = oracle.brute_nn(T, Q)
+    for sort in (True, False):
+        idx, d2 = tree.query(dev(torch, Q), sort=sort)
+        assert_nn_equal(idx, d2, oi, od, f"n={n} sort={sort}")
+    si, sd, cn, _ = tree.query_stats(dev(torch, Q))
+    assert_nn_equal(si, sd, oi, od, f"n={n} stats")
+    assert int(cn.min()) >= D - min(D, 8) + 2
+    R, t = synth.rotation_about(synth.random_unit(rng), 0.2), rng.normal(size=3) * 0.1
+    oi, od, red = _pairs_oracle(T, Q, R, t)
+    res = tree.correspond_reduce(dev(torch, Q), R, t, return_pairs=True)
+    assert_nn_equal(res["idx"], res["d2"], oi, od, f"n={n} correspond_reduce")
+    check_sums(res, red, bbox_diag(T), f"n={n} correspond_reduce sums")
+
+
 def test_nonfinite_and_empty(torch, kdnn):
     say("nonfinite / empty")
     rng = np.random.Generator(np.random.PCG64(3))
