@@ -226,7 +226,7 @@ struct VoxGrid {
     int32_t passes;     // radix passes the keys need; 0: nothing to sort
     int32_t err;        // kVoxOk, kVoxErrRange or kVoxErrCells
     uint32_t nvox;      // voxels: the sum of the segment heads
-    uint32_t nbig;      // voxels summed by a whole wave (their list: vals_a)
+    uint32_t nbig;      // voxels summed by a whole wave (their list: in vals_a)
 };
 constexpr int32_t kVoxOk = 0;
 constexpr int32_t kVoxErrRange = 1;  // |floor(p / leaf)| >= 4e18 for a bounding-box corner

@@ -478,8 +478,9 @@ __global__ __launch_bounds__(kVoxThreads) void voxel_starts_kernel(const uint32_
 //     would keep one chain per lane, but every load instruction of the wave
 //     would touch 64 cache lines; a wave that stages one segment in coalesced
 //     windows and runs its x, y and z chains in three lanes is ~10x faster on
-//     them.  Their indices go to a list (any order: each result depends on its
-//     voxel alone).
+//     them.  They go to a list as (voxel, segment start, segment end), in any
+//     order (each result depends on its voxel alone); at over 64 points each,
+//     the 16-byte entries fit in n int32 of workspace.
 constexpr int kVoxSmall = 64;
 constexpr int kVoxWin = 256;  // points per staged window
 
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(kVoxThreads) void voxel_centroid_kernel(const float
                                                                      const int32_t *starts,
                                                                      VoxGrid *grid, float *out,
                                                                      int32_t *counts,
-                                                                     int32_t *big)
+                                                                     int4 *big)
 {
     constexpr int kChunk = 32;
     const int lane = threadIdx.x & 63;
@@ -505,7 +506,8 @@ __global__ __launch_bounds__(kVoxThreads) void voxel_centroid_kernel(const float
             if (lane == 0) at = atomicAdd(&grid->nbig, uint32_t(__popcll(bal)));
             at = uint32_t(__shfl(int(at), 0, 64));
             if (large)
-                big[at + uint32_t(__popcll(bal & ((uint64_t(1) << lane) - 1u)))] = int32_t(v);
+                big[at + uint32_t(__popcll(bal & ((uint64_t(1) << lane) - 1u)))] =
+                    make_int4(int32_t(v), int32_t(s), int32_t(e), 0);
         }
         if (!own || large) continue;
         double sx = 0.0, sy = 0.0, sz = 0.0;
@@ -536,21 +538,17 @@ __global__ __launch_bounds__(kVoxThreads) void voxel_centroid_kernel(const float
 // by all lanes); lane c < 3 then adds row c in order, while the loads of the
 // next window are in flight.
 __global__ __launch_bounds__(64) void voxel_big_kernel(const float4 *sorted,
-                                                       const int32_t *starts,
-                                                       const VoxGrid *grid, const int32_t *big,
+                                                       const VoxGrid *grid, const int4 *big,
                                                        float *out, int32_t *counts)
 {
     constexpr int kPer = kVoxWin / 64;  // points per lane and window
     __shared__ double row[3][kVoxWin];
     const int lane = threadIdx.x;
-    const int64_t m = int64_t(grid->nvox);
-    const int64_t n_finite = int64_t(grid->n_finite);
     const uint32_t nbig = grid->nbig;
     const double *mine = row[lane < 3 ? lane : 0];
     for (uint32_t i = blockIdx.x; i < nbig; i += gridDim.x) {
-        const int64_t v = big[i];
-        const int64_t s = starts[v];
-        const int64_t e = v + 1 < m ? int64_t(starts[v + 1]) : n_finite;
+        const int4 job = big[i];
+        const int64_t v = job.x, s = job.y, e = job.z;
         float4 q[kPer];
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
@@ -677,9 +675,10 @@ hipError_t launch_voxel_filter(const float *xyz, int64_t n, double leaf, const V
     voxel_heads_kernel<<<nt, kVoxThreads, 0, s>>>(w.keys_a, w.keys_b, n, w.grid, w.tile_heads);
     voxel_starts_kernel<<<nt, kVoxThreads, 0, s>>>(w.keys_a, w.keys_b, n, w.grid, w.tile_heads,
                                                     w.starts);
+    int4 *const big = reinterpret_cast<int4 *>(w.vals_a);  // free once the sort is done
     voxel_centroid_kernel<<<grid_of(n, kVoxThreads, 4096), kVoxThreads, 0, s>>>(
-        w.sorted, w.starts, w.grid, out, counts, w.vals_a);
-    voxel_big_kernel<<<2048, 64, 0, s>>>(w.sorted, w.starts, w.grid, w.vals_a, out, counts);
+        w.sorted, w.starts, w.grid, out, counts, big);
+    voxel_big_kernel<<<2048, 64, 0, s>>>(w.sorted, w.grid, big, out, counts);
     return hipGetLastError();
 }
 
